@@ -1,0 +1,483 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+Each test names what it pins: closed forms, library routines (torch's bf16
+conversion and scaled-dot-product attention, Python's complex arithmetic),
+brute-force loops on tiny inputs, planted answers, and the storage table the
+TokenDance notes print.  A plausible mistake in the oracle (a dropped term,
+a wrong sign or index, a transposed operand, a wrong tie rule) fails one.
+"""
+
+import cmath
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------- bf16 format
+
+def _torch_bf16_bits(x32):
+    return torch.from_numpy(np.asarray(x32, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_bf16_rounding_matches_torch_on_fp32_inputs():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal(200000).astype(np.float32) * np.float32(3.0)
+    # exact ties: low 16 bits = 0x8000, both parities of the kept lsb
+    ties = (rng.integers(0, 2**31, 20000, dtype=np.uint32) & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    tiny = (rng.integers(1, 2**23, 2000, dtype=np.uint32)).view(np.float32)  # fp32 subnormals
+    big = np.float32([3.3e38, -3.3e38, 3.4e38, 1e-40, -1e-45, 0.0, -0.0])
+    allx = np.concatenate([x, ties.view(np.float32), tiny, big])
+    allx = allx[np.isfinite(allx)]
+    np.testing.assert_array_equal(O.f64_to_bf16(allx.astype(np.float64)), _torch_bf16_bits(allx))
+
+
+def test_bf16_rounding_hand_values():
+    cases = {
+        1.0: 0x3F80,
+        1.0 + 2.0**-8: 0x3F80,            # tie -> even (down)
+        1.0 + 3 * 2.0**-8: 0x3F82,        # tie -> even (up)
+        1.0 + 2.0**-8 + 2.0**-40: 0x3F81,  # above the tie only in fp64: one rounding
+        -2.5: 0xC020,
+        2.0**-126: 0x0080,
+        2.0**-133: 0x0001,                # smallest bf16 subnormal
+        2.0**-134: 0x0000,                # tie at half the smallest subnormal -> even (0)
+        3 * 2.0**-134: 0x0002,            # 1.5 quanta -> even (2)
+        2.0**128: 0x7F80,
+    }
+    got = O.f64_to_bf16(np.array(list(cases.keys())))
+    assert [int(v) for v in got] == list(cases.values())
+
+
+def test_bf16_widen_round_trip_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = O.bf16_to_f64(bits)
+    ok = ~np.isnan(vals)
+    np.testing.assert_array_equal(O.f64_to_bf16(vals[ok]), bits[ok])
+    assert O.bf16_to_f64(np.array([0x3F80, 0xC000], np.uint16)).tolist() == [1.0, -2.0]
+
+
+# ------------------------------------------------------------------------ RoPE
+
+def test_rope_inv_freq_closed_form():
+    f = O.rope_inv_freq(128, 1e6)
+    assert f.shape == (64,)
+    assert f[0] == 1.0
+    assert math.isclose(f[32], 1e-3, rel_tol=1e-14)       # 1e6 ** (-64/128)
+    assert math.isclose(f[63], 1e6 ** (-126 / 128), rel_tol=1e-14)
+    assert math.isclose(O.rope_inv_freq(64, 1e4)[16], 1e-2, rel_tol=1e-14)
+
+
+def test_rope_single_pair_closed_form():
+    # D = 2: one pair at frequency 1, so (1, 0) at position p -> (cos p, sin p)
+    for p in (1, 2, -3, 1000):
+        out = O.rope_rotate(np.array([1.0, 0.0]), p, 1e4)
+        assert np.allclose(out, [math.cos(p), math.sin(p)], rtol=0, atol=1e-15)
+    out = O.rope_rotate(np.array([0.0, 1.0]), 1, 1e4)
+    assert np.allclose(out, [-math.sin(1), math.cos(1)], atol=1e-15)
+
+
+def test_rope_matches_complex_multiplication():
+    rng = np.random.default_rng(2)
+    D, theta = 64, 1e4
+    x = rng.standard_normal((5, D))
+    pos = np.array([0, 1, 17, 4096, -250])
+    got = O.rope_rotate(x, pos, theta)
+    for r in range(5):
+        for e in range(D // 2):
+            ang = pos[r] * theta ** (-2.0 * e / D)
+            z = complex(x[r, e], x[r, e + D // 2]) * cmath.exp(1j * ang)
+            assert abs(got[r, e] - z.real) < 1e-12
+            assert abs(got[r, e + D // 2] - z.imag) < 1e-12
+
+
+def test_rope_shift_composition_and_inverse():
+    # RoPE(x, p + delta) = R(delta) RoPE(x, p); R(-delta) R(delta) = I
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((7, 4, 128))
+    p = rng.integers(0, 8192, size=7)
+    d = rng.integers(-6000, 6000, size=7)
+    a = O.rope_rotate(O.rope_rotate(x, p[:, None], 1e6), d[:, None], 1e6)
+    b = O.rope_rotate(x, (p + d)[:, None], 1e6)
+    assert np.max(np.abs(a - b)) <= 1e-12 * np.max(np.abs(b)) * 100
+    back = O.rope_rotate(O.rope_rotate(x, d[:, None], 1e6), -d[:, None], 1e6)
+    assert np.max(np.abs(back - x)) < 1e-12
+    # each (e, e + D/2) pair keeps its norm
+    y = O.rope_rotate(x, d[:, None], 1e6)
+    n0 = x[..., :64] ** 2 + x[..., 64:] ** 2
+    n1 = y[..., :64] ** 2 + y[..., 64:] ** 2
+    assert np.max(np.abs(n0 - n1)) < 1e-12
+
+
+# ------------------------------------------------------------------- rerotate
+
+def _layout(lens, src, dst):
+    bs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return bs, np.asarray(src, np.int32), np.asarray(dst, np.int32)
+
+
+def test_rerotate_moves_rope_to_agent_offsets_fp32():
+    # Cached K = RoPE(raw, src); re-rotated copy must equal RoPE(raw, dst) up
+    # to the fp32 storage rounding of the cached K.
+    rng = np.random.default_rng(4)
+    lens = [16, 32, 16]
+    bs, src, dst = _layout(lens, [0, 16, 48], [[100, 10, 3000], [5, 7000, 64]])
+    T = bs[-1]
+    raw = rng.standard_normal((2, T, 3, 64))
+    bt = O.block_of_token(bs)
+    kc = O.rope_rotate(raw, src[bt][None, :, None], 1e4).astype(np.float32)
+    out = O.rerotate(kc, bs, src, dst, 1e4)
+    assert out.shape == (2, 2, T, 3, 64) and out.dtype == np.float32
+    for i in range(2):
+        want = O.rope_rotate(raw, dst[i][bt][None, :, None], 1e4)
+        assert np.max(np.abs(out[i] - want)) < 2e-5
+
+
+def test_rerotate_brute_force_loops_bf16():
+    rng = np.random.default_rng(5)
+    bs, src, dst = _layout([16, 16], [0, 16], [[40, 7], [16, 0]])
+    kc = O.f64_to_bf16(rng.standard_normal((1, 32, 2, 8)))
+    out = O.rerotate(kc, bs, src, dst, 1e4)
+    x = O.bf16_to_f64(kc)
+    for i in range(2):
+        for t in range(32):
+            b = 0 if t < 16 else 1
+            delta = int(dst[i][b]) - int(src[b])
+            for h in range(2):
+                for e in range(4):
+                    ang = delta * (1e4 ** (-2.0 * e / 8))
+                    z = complex(x[0, t, h, e], x[0, t, h, e + 4]) * cmath.exp(1j * ang)
+                    assert out[i, 0, t, h, e] == O.f64_to_bf16(np.array([z.real]))[0]
+                    assert out[i, 0, t, h, e + 4] == O.f64_to_bf16(np.array([z.imag]))[0]
+
+
+@pytest.mark.parametrize("dt", [np.uint16, np.float32])
+def test_rerotate_zero_shift_is_bitwise_copy(dt):
+    rng = np.random.default_rng(6)
+    bs, src, dst = _layout([32, 16], [0, 32], [[0, 32], [0, 32]])
+    x = rng.standard_normal((2, 48, 2, 64))
+    kc = O.narrow(x, dt)
+    out = O.rerotate(kc, bs, src, dst, 1e6)
+    for i in range(2):
+        np.testing.assert_array_equal(out[i].view(np.uint8), kc.view(np.uint8))
+
+
+def test_rerotate_there_and_back_bf16():
+    rng = np.random.default_rng(7)
+    bs, src, dst = _layout([64], [0], [[5000]])
+    kc = O.f64_to_bf16(rng.standard_normal((1, 64, 4, 128)))
+    fwd = O.rerotate(kc, bs, src, dst, 1e6)[0]
+    back = O.rerotate(fwd, bs, np.int32([5000]), np.int32([[0]]), 1e6)[0]
+    a, b = O.bf16_to_f64(back), O.bf16_to_f64(kc)
+    assert np.all(np.abs(a - b) <= 2e-2 + 1e-2 * np.abs(b))
+
+
+# ------------------------------------------------------------------ deviation
+
+def test_deviation_brute_force():
+    rng = np.random.default_rng(8)
+    N, T, H, D = 3, 5, 2, 8
+    r = O.f64_to_bf16(rng.standard_normal((N, T, H, D)))
+    x = O.f64_to_bf16(O.bf16_to_f64(r) + 0.1 * rng.standard_normal((N, T, H, D)))
+    d, s, a = O.deviation(r, x)
+    R, X = O.bf16_to_f64(r), O.bf16_to_f64(x)
+    for i in range(N):
+        for t in range(T):
+            tot = 0.0
+            for h in range(H):
+                ss = 0.0
+                for e in range(D):
+                    ss += (X[i, t, h, e] - R[i, t, h, e]) ** 2
+                tot += math.sqrt(ss)
+            assert abs(d[i, t] - tot) < 1e-13
+    for t in range(T):
+        assert abs(s[t] - sum(d[i, t] for i in range(N))) < 1e-13
+    for i in range(N):
+        assert abs(a[i] - sum(d[i, t] for t in range(T))) < 1e-13
+
+
+def test_deviation_closed_forms():
+    N, T, H, D = 2, 4, 3, 16
+    r = np.zeros((N, T, H, D), np.float32)
+    x = r.copy()
+    d, s, a = O.deviation(r, x)
+    assert not d.any() and not s.any() and not a.any()
+    x[1, 2, 1, :] = 0.5           # one head shifted by c on every dim: d = |c| sqrt(D)
+    x[0, 3, :, 0] = -3.0          # every head shifted by c on one dim: d = H |c|
+    d, s, a = O.deviation(r, x)
+    assert d[1, 2] == 0.5 * 4.0 and d[0, 3] == 9.0
+    assert d.sum() == 11.0 and s[2] == 2.0 and a[0] == 9.0
+
+
+# -------------------------------------------------------------- select/master
+
+def test_topk_count_is_exact_ceiling():
+    for T in range(1, 20001):
+        want = min(max(math.ceil(Fraction(15 * T, 100)), 1), T)
+        assert O.topk_count(15, T) == want
+    assert O.topk_count(15, 192) == 29
+    assert O.topk_count(0, 10) == 1 and O.topk_count(100, 10) == 10
+
+
+def test_select_ties_and_order():
+    s = np.float32([1.0, 2.0, 2.0, 0.0, 2.0])
+    assert O.select_important(s, 1).tolist() == [1]
+    assert O.select_important(s, 2).tolist() == [1, 2]
+    assert O.select_important(s, 4).tolist() == [0, 1, 2, 4]
+    assert O.select_important(s, 5).tolist() == [0, 1, 2, 3, 4]
+
+
+def test_select_brute_force_against_full_sort():
+    rng = np.random.default_rng(9)
+    for trial in range(50):
+        T = int(rng.integers(1, 60))
+        s = rng.integers(0, 6, T).astype(np.float32)  # many ties
+        k = int(rng.integers(1, T + 1))
+        # independent: numpy lexsort on (index, -score)
+        order = np.lexsort((np.arange(T), -s.astype(np.float64)))
+        assert O.select_important(s, k).tolist() == sorted(order[:k].tolist())
+
+
+def test_select_planted_set_through_deviation():
+    rng = np.random.default_rng(10)
+    N, T, H, D = 4, 200, 2, 16
+    planted = np.sort(rng.choice(T, 30, replace=False))
+    r = O.f64_to_bf16(rng.standard_normal((N, T, H, D)))
+    x = r.copy()
+    x[:, planted] = O.f64_to_bf16(O.bf16_to_f64(r[:, planted]) + 0.3 * rng.standard_normal((N, 30, H, D)))
+    _, s, _ = O.deviation(r, x)
+    assert O.select_important(s.astype(np.float32), 30).tolist() == planted.tolist()
+
+
+def test_select_single_agent_is_per_request_topk():
+    rng = np.random.default_rng(11)
+    r = rng.standard_normal((1, 50, 2, 8)).astype(np.float32)
+    x = (r + rng.standard_normal(r.shape) * 0.1).astype(np.float32)
+    d, s, _ = O.deviation(r, x)
+    assert np.array_equal(s, d[0])
+    want = sorted(np.argsort(-d[0].astype(np.float32), kind="stable")[:8].tolist())
+    assert O.select_important(s.astype(np.float32), 8).tolist() == want
+
+
+def test_master_planted_and_ties():
+    from workload import CONFIGS, make_layout, reuse_stand_in, recomputed_k, noise_tokens, to_numpy_bits
+    cfg = CONFIGS["tiny"]
+    lay = make_layout(cfg)
+    kr = reuse_stand_in(cfg, lay)
+    toks = noise_tokens(cfg, lay)
+    toks = [toks[0]] * cfg.n_agents  # same tokens for all agents
+    for planted in range(cfg.n_agents):
+        sig = [0.2] * cfg.n_agents
+        sig[planted] = 0.1
+        kx = recomputed_k(cfg, lay, kr, tokens=toks, sigmas=sig)
+        _, _, a = O.deviation(to_numpy_bits(kr), to_numpy_bits(kx))
+        assert O.choose_master(a.astype(np.float32)) == planted
+    assert O.choose_master(np.float32([3, 1, 1, 2])) == 1
+
+
+# --------------------------------------------------------------------- encode
+
+def _tiny_caches(master=1, frac=(0.1, 0.2)):
+    from workload import CONFIGS, make_layout, cached_kv, agent_caches, mirror_blocks, to_numpy_bits
+    cfg = CONFIGS["tiny"].scaled(n_layers=2, mirror_frac=frac)
+    lay = make_layout(cfg)
+    kc, vc = cached_kv(cfg, lay)
+    ak, av = agent_caches(cfg, lay, kc, vc, master)
+    return cfg, lay, to_numpy_bits(kc), to_numpy_bits(vc), to_numpy_bits(ak), to_numpy_bits(av), mirror_blocks(cfg, lay)
+
+
+def test_encode_recovers_planted_blocks_and_round_trips():
+    cfg, lay, kc, vc, ak, av, blocks = _tiny_caches(master=1)
+    off, idx, dk, dv = O.diff_encode(ak, av, 1)
+    L = cfg.n_layers
+    for i in range(cfg.n_agents):
+        for l in range(L):
+            row = idx[off[i * L + l]:off[i * L + l + 1]]
+            want = [] if i == 1 else blocks[i].tolist()
+            assert row.tolist() == want
+        k, v = O.decode_mirror(kc, vc, off, idx, dk, dv, i)
+        np.testing.assert_array_equal(k.view(np.uint8), ak[i].view(np.uint8))
+        np.testing.assert_array_equal(v.view(np.uint8), av[i].view(np.uint8))
+
+
+def test_encode_zero_and_all_blocks():
+    rng = np.random.default_rng(12)
+    N, L, T, H, D = 3, 2, 64, 2, 8
+    base = O.f64_to_bf16(rng.standard_normal((L, T, H, D)))
+    same = np.stack([base] * N)
+    off, idx, dk, dv = O.diff_encode(same, same.copy(), 0)
+    assert off.tolist() == [0] * (N * L + 1) and idx.size == 0 and dk.shape[0] == 0
+    other = same.copy()
+    other[2] = O.f64_to_bf16(O.bf16_to_f64(base) + 1.0)
+    off, idx, dk, dv = O.diff_encode(other, same.copy(), 0)
+    assert idx.tolist() == [0, 1, 2, 3] * L
+    assert off.tolist() == [0, 0, 0, 0, 0, 4, 8]
+
+
+def test_encode_counts_any_bit_in_k_or_v():
+    N, L, T, H, D = 2, 1, 48, 1, 4
+    k = np.zeros((N, L, T, H, D), np.float32)
+    v = np.zeros_like(k)
+    k[1, 0, 17, 0, 3] = -0.0        # sign bit only: a different stored value
+    v[1, 0, 47, 0, 0] = 1e-30
+    off, idx, dk, dv = O.diff_encode(k, v, 0)
+    assert idx.tolist() == [1, 2]
+    k2, v2 = O.decode_mirror(k[0], v[0], off, idx, dk, dv, 1)
+    np.testing.assert_array_equal(k2.view(np.uint32), k[1].view(np.uint32))
+
+
+# ------------------------------------------------------------------ attention
+
+def test_attend_brute_force_loops():
+    rng = np.random.default_rng(13)
+    Hq, Hkv, D, n = 4, 2, 8, 6
+    q = rng.standard_normal((Hq, D))
+    k = rng.standard_normal((n, Hkv, D))
+    v = rng.standard_normal((n, Hkv, D))
+    got = O.attend(q, k, v, 0.3)
+    for hq in range(Hq):
+        h = hq // 2
+        z = [sum(q[hq, e] * k[j, h, e] for e in range(D)) * 0.3 for j in range(n)]
+        w = [math.exp(zz) for zz in z]
+        for e in range(D):
+            want = sum(w[j] * v[j, h, e] for j in range(n)) / sum(w)
+            assert abs(got[hq, e] - want) < 1e-12
+
+
+def test_attend_single_and_identical_keys():
+    rng = np.random.default_rng(14)
+    q = rng.standard_normal((4, 16))
+    k1 = rng.standard_normal((1, 2, 16))
+    v1 = rng.standard_normal((1, 2, 16))
+    out = O.attend(q, k1, v1, 0.25)
+    assert np.allclose(out[:2], v1[0, 0]) and np.allclose(out[2:], v1[0, 1])
+    kk = np.repeat(k1, 5, axis=0)
+    vv = rng.standard_normal((5, 2, 16))
+    out = O.attend(q, kk, vv, 0.25)
+    assert np.allclose(out[0], vv[:, 0].mean(0), atol=1e-14)
+    assert np.allclose(out[3], vv[:, 1].mean(0), atol=1e-14)
+
+
+def test_restore_attn_matches_torch_sdpa_without_shift_or_diff():
+    # Delta = 0, no diff, no private keys: plain GQA attention over the Master.
+    rng = np.random.default_rng(15)
+    N, L, T, Hkv, Hq, D = 2, 2, 32, 2, 6, 16
+    mk = O.f64_to_bf16(rng.standard_normal((L, T, Hkv, D)))
+    mv = O.f64_to_bf16(rng.standard_normal((L, T, Hkv, D)))
+    q = O.f64_to_bf16(rng.standard_normal((N, L, Hq, D)))
+    bs, src, dst = _layout([16, 16], [0, 16], [[0, 16], [0, 16]])
+    off = np.zeros(N * L + 1, np.int64)
+    empty = np.zeros((0, 16, Hkv, D), np.uint16)
+    got = O.restore_attn(q, np.zeros(N + 1, np.int32), np.zeros((L, 0, Hkv, D), np.uint16),
+                         np.zeros((L, 0, Hkv, D), np.uint16), mk, mv, off, np.zeros(0, np.int32),
+                         empty, empty, bs, src, dst, 1e6, 1 / 4.0)
+    K = torch.from_numpy(O.bf16_to_f64(mk))
+    V = torch.from_numpy(O.bf16_to_f64(mv))
+    Q = torch.from_numpy(O.bf16_to_f64(q))
+    for i in range(N):
+        for l in range(L):
+            qq = Q[i, l][:, None, :]                                        # [Hq][1][D]
+            kk = K[l].permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)  # [Hq][T][D]
+            vv = V[l].permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)
+            ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, scale=0.25)[:, 0]
+            np.testing.assert_array_equal(got[i, l], O.f64_to_bf16(ref.numpy()))
+
+
+def test_restore_attn_shift_invariance_and_private_order():
+    # q and the shared keys built from raw vectors at real positions: adding
+    # one constant to every position leaves the output unchanged.
+    rng = np.random.default_rng(16)
+    T, Hkv, Hq, D = 32, 1, 2, 32
+    bs, src, _ = _layout([16, 16], [0, 16], [[0, 0]])
+    raw_k = rng.standard_normal((T, Hkv, D))
+    mv = rng.standard_normal((1, T, Hkv, D)).astype(np.float32)
+    bt = O.block_of_token(bs)
+    mk = O.rope_rotate(raw_k, src[bt][:, None], 1e4)[None].astype(np.float32)
+    raw_q = rng.standard_normal((Hq, D))
+    outs = []
+    for c in (0, 137, 5000):
+        dst = np.int32([[300 + c, 50 + c]])
+        qpos = 400 + c
+        q = O.rope_rotate(raw_q, qpos, 1e4)[None, None].astype(np.float32)
+        off = np.zeros(2, np.int64)
+        empty = np.zeros((0, 16, Hkv, D), np.float32)
+        outs.append(O.restore_attn(q, np.int32([0, 0]), np.zeros((1, 0, Hkv, D), np.float32),
+                                   np.zeros((1, 0, Hkv, D), np.float32), mk, mv, off,
+                                   np.zeros(0, np.int32), empty, empty, bs, src, dst, 1e4, 0.2))
+    assert np.max(np.abs(outs[0] - outs[1])) < 1e-5
+    assert np.max(np.abs(outs[0] - outs[2])) < 1e-5
+
+
+def test_fused_equals_dense_and_decoded_mirror():
+    cfg, lay, kc, vc, ak, av, _ = _tiny_caches(master=0)
+    from workload import queries, private_kv, to_numpy_bits
+    q = to_numpy_bits(queries(cfg.scaled(n_layers=2)))
+    pk, pv = private_kv(cfg, lay)
+    pk, pv = to_numpy_bits(pk), to_numpy_bits(pv)
+    off, idx, dk, dv = O.diff_encode(ak, av, 0)
+    args = (lay.blk_start, lay.src_pos, lay.dst_pos, cfg.theta)
+    scale = 1 / math.sqrt(cfg.head_dim)
+    fused = O.restore_attn(q, lay.priv_off, pk, pv, kc, vc, off, idx, dk, dv, *args, scale)
+    kd, vd = O.restore_dense(kc, vc, off, idx, dk, dv, *args)
+    dense = O.decode_attn_dense(q, lay.priv_off, pk, pv, kd, vd, scale)
+    assert np.max(np.abs(fused - dense)) < 1e-5  # fp32: only the K rounding differs
+    # the dense cache equals the re-rotation of each agent's full cache
+    for i in range(cfg.n_agents):
+        rot = O.rerotate(ak[i], lay.blk_start, lay.src_pos, lay.dst_pos[i:i + 1], cfg.theta)[0]
+        np.testing.assert_array_equal(kd[i], rot)
+        np.testing.assert_array_equal(vd[i], av[i])
+
+
+# ---------------------------------------------------------------- compression
+
+def test_compression_matches_printed_table():
+    with open(os.path.join(GOLDEN, "compression_table.json")) as f:
+        g = json.load(f)
+    N = g["n_agents"]
+    for row in g["rows"]:
+        caches = O.caches_for_group(N, row["per_mirror_ratio"])
+        assert round(caches, 1) == row["caches_for_10"]
+        assert round(N / round(caches, 1), 1) == row["reduction_for_10"]
+        assert round(100 / row["per_mirror_ratio"], 1) == row["mirror_pct_of_master"]
+    # 7B row from block counts: 53.2 changed blocks per Mirror per layer out of
+    # 596 blocks (within the 500-700 the table gives) is the 11.2x per Mirror.
+    counts = np.array([[0] * 5] + [[53, 53, 53, 53, 54]] * (N - 1))
+    res = O.compression(counts, master=0, n_tokens=596 * 16, kv_heads=4, head_dim=128, elem_bytes=2)
+    assert round(res["per_mirror_ratio_mean"], 1) == 11.2
+    assert round(res["caches_equivalent"], 1) == 1.8
+
+
+def test_compression_closed_form():
+    counts = np.array([[0, 0], [3, 1], [2, 2]])
+    res = O.compression(counts, master=0, n_tokens=64, kv_heads=2, head_dim=8, elem_bytes=2,
+                        priv_len=[5, 6, 7])
+    blk = 16 * 2 * 8 * 2 * 2
+    dense_one = 2 * 64 * 2 * 8 * 2 * 2
+    m1 = (3 * (blk + 4) + 4) + (1 * (blk + 4) + 4)
+    m2 = 2 * ((2 * (blk + 4)) + 4)
+    assert res["per_mirror_ratio"][1] == dense_one / m1
+    assert res["stored_shared_bytes"] == dense_one + m1 + m2
+    assert res["group_ratio"] == 3 * dense_one / (dense_one + m1 + m2)
+    priv = 18 * 2 * 2 * 8 * 2 * 2
+    assert res["footprint_ratio"] == (3 * dense_one + priv) / (dense_one + m1 + m2 + priv)
+
+
+def test_attend_large_logits_stay_finite():
+    # logits near 1000 overflow exp() unless the row maximum is subtracted;
+    # the softmax is then a one-hot on the largest logit.
+    q = np.zeros((2, 4))
+    q[:, 0] = 1000.0
+    k = np.zeros((3, 1, 4))
+    k[:, 0, 0] = [1.0, 0.98, 0.5]
+    v = np.arange(12, dtype=np.float64).reshape(3, 1, 4)
+    out = O.attend(q, k, v, 1.0)
+    assert np.all(np.isfinite(out))
+    assert np.allclose(out[0], v[0, 0]) and np.allclose(out[1], v[0, 0])
