@@ -1,0 +1,292 @@
+"""Benchmark of one collective-reuse round on one MI355X.
+
+A step is one pass of the whole hot path over one synthetic round held in
+HBM: batched RoPE re-rotation of the shared K for all agents and layers,
+the check-layer deviation pass with important-position selection and Master
+choice, the Master-Mirror diff encode, and the fused restore + decode
+attention of every agent and layer.  The dense restore-then-attend
+comparator is timed on the same round outside the step.
+
+Prints ONE JSON line (see the fields below).  Default workload: the
+Qwen2.5-14B-shaped full round (10 agents, 48 layers, 8 KV heads x 128,
+40 query heads, bf16, 4K-8K-token contexts).
+"""
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="qwen14b_round")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    return ap.parse_args()
+
+
+def stage_bytes(cfg, lay, nnz_total, k):
+    """Algorithmic HBM bytes of each stage (what the method must move)."""
+    N, L, T, H, D, Hq = cfg.n_agents, cfg.n_layers, lay.n_tokens, cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads
+    eb = cfg.elem_bytes
+    kt = H * D * eb
+    kv = 2 * kt
+    ptot = int(lay.priv_len.sum())
+    blk = 16 * kv
+    diff_bytes = nnz_total * (blk + 4)
+    return {
+        "rerotate": L * T * kt + N * L * T * kt,
+        "select": 2 * N * T * kt + 4 * N * T + 4 * T + 4 * k + 4 * N,
+        # read every agent's cache once, write diff values + indices and the Master copy
+        "encode": N * L * T * kv + diff_bytes + L * T * kv + 4 * (N * L + 1),
+        # Master once, private histories, diff records, q and out
+        "restore_attn": L * T * kv + L * ptot * kv + diff_bytes + 2 * N * L * Hq * D * eb,
+        # dense restore (read Master + diffs, write N dense caches) + attention over them
+        "dense": (L * T * kv + diff_bytes + N * L * T * kv) + (L * ptot * kv + N * L * T * kv)
+                 + 2 * N * L * Hq * D * eb,
+    }
+
+
+def compression(counts, master, T, H, D, eb, priv_len, L):
+    """Storage of the shared region: dense N copies vs Master + diff rows."""
+    import numpy as np
+
+    counts = np.asarray(counts, dtype=np.int64)
+    N = counts.shape[0]
+    dense_one = L * T * H * D * 2 * eb
+    row = counts * (16 * H * D * 2 * eb + 4) + 4
+    mirror = row.sum(axis=1)
+    per = [dense_one / float(mirror[i]) for i in range(N) if i != master]
+    stored = dense_one + sum(int(mirror[i]) for i in range(N) if i != master)
+    priv = int(np.sum(priv_len)) * L * H * D * 2 * eb
+    return {
+        "per_mirror_ratio_mean": float(np.mean(per)) if per else None,
+        "group_ratio": N * dense_one / float(stored),
+        "dense_shared_GB": N * dense_one / 1e9,
+        "master_plus_diff_GB": stored / 1e9,
+        "footprint_with_private_ratio": (N * dense_one + priv) / float(stored + priv),
+        "dense_total_GB": (N * dense_one + priv) / 1e9,
+        "stored_total_GB": (stored + priv) / 1e9,
+    }
+
+
+def cpu_baseline(cfg, lay, pct):
+    """The oracle on a bounded sample: layer 0 of the same round (drawn on the
+    host), all agents; the round's layers are iid, so the whole-round time is
+    the one-layer time x L (select runs once per round)."""
+    import numpy as np
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+    from workload import (cached_kv, agent_caches, queries, private_kv, recomputed_k,
+                          to_numpy_bits, from_numpy_bits)
+
+    c1 = cfg.scaled(n_layers=1)
+    kc, vc = cached_kv(c1, lay)
+    q = queries(c1)
+    pk, pv = private_kv(c1, lay)
+    hk, hv, hq, hpk, hpv = (to_numpy_bits(x) for x in (kc, vc, q, pk, pv))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        kr = O.rerotate(hk, lay.blk_start, lay.src_pos, lay.dst_pos, cfg.theta)
+        t1 = time.perf_counter()
+        kx = to_numpy_bits(recomputed_k(c1, lay, from_numpy_bits(kr[:, 0])))
+        t2 = time.perf_counter()
+        _, s, a = O.deviation(kr[:, 0], kx)
+        k = O.topk_count(pct, lay.n_tokens)
+        O.select_important(s.astype(np.float32), k)
+        m = O.choose_master(a.astype(np.float32))
+        t3 = time.perf_counter()
+        ak, av = agent_caches(c1, lay, kc, vc, m)
+        hak, hav = to_numpy_bits(ak), to_numpy_bits(av)
+        t4 = time.perf_counter()
+        off, idx, dk, dv = O.diff_encode(hak, hav, m)
+        t5 = time.perf_counter()
+        O.restore_attn(hq, lay.priv_off, hpk, hpv, hk, hv, off, idx, dk, dv, lay.blk_start,
+                       lay.src_pos, lay.dst_pos, cfg.theta, 1.0 / math.sqrt(cfg.head_dim))
+        t6 = time.perf_counter()
+    L = cfg.n_layers
+    per_round = (t1 - t0) * L + (t3 - t2) + (t5 - t4) * L + (t6 - t5) * L
+    return {
+        "value": cfg.n_agents * lay.n_tokens / per_round,
+        "unit": "agent-tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"layer 0 of the {cfg.name} round on the host (all {cfg.n_agents} agents, "
+                   f"{lay.n_tokens} shared tokens); per-layer stages x {L} layers + one select; "
+                   f"measured {t6 - t0 - (t2 - t1) - (t4 - t3):.1f} s of oracle time"),
+        "stage_s_per_layer": {"rerotate": t1 - t0, "select_once": t3 - t2, "encode": t5 - t4,
+                              "restore_attn": t6 - t5},
+        "cpu": platform.processor() or platform.machine(),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the collective reuse path here runs on a single "
+              "MI355X (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from collective_kv_cache_amd import tdx
+    from workload import (CONFIGS, make_layout, cached_kv, agent_caches, queries, private_kv,
+                          recomputed_k)
+
+    dev = "cuda"
+    cfg = CONFIGS[args.config]
+    lay = make_layout(cfg)
+    N, L, T, H, Hq, D = cfg.n_agents, cfg.n_layers, lay.n_tokens, cfg.n_kv_heads, cfg.n_q_heads, cfg.head_dim
+    shape = tdx.Shape(L, H, Hq, D, cfg.torch_dtype, cfg.theta)
+    shape1 = shape.with_layers(L)
+    dl = tdx.RoundLayout(lay.blk_start, lay.src_pos, lay.dst_pos, dev)
+    k = tdx.topk_count(cfg.pct, T)
+    max_priv = int(lay.priv_len.max())
+
+    # ---- inputs, drawn directly in HBM
+    kc, vc = cached_kv(cfg, lay, device=dev)
+    q = queries(cfg, device=dev)
+    pk, pv = private_kv(cfg, lay, device=dev)
+    po = torch.as_tensor(lay.priv_off, device=dev)
+    kr = torch.empty((N, L, T, H, D), dtype=cfg.torch_dtype, device=dev)
+    tdx.rerotate(shape, dl, kc, out=kr)
+    kx = recomputed_k(cfg, lay, kr[:, cfg.check_layer].contiguous())
+    sel = tdx.select_important(shape1, dl, kr, kx, k, check_layer=cfg.check_layer)
+    master = int(sel["master"].item())
+    ak, av = agent_caches(cfg, lay, kc, vc, master)
+    nb = T // 16
+    cap = int(math.ceil(0.35 * (N - 1) * L * nb))  # the Mirrors differ in at most 20% of blocks
+    ds = tdx.diff_encode(shape, dl, sel["master"], ak, av, cap_blocks=cap, check=True)
+    out = tdx.restore_attn(shape, dl, q, po, pk, pv, max_priv, ds.master_k, ds.master_v, ds)
+    ws_sel = torch.empty(max(tdx.select_workspace(shape1, dl), 16), dtype=torch.uint8, device=dev)
+    ws_enc = torch.empty(max(tdx.encode_workspace(shape, dl), 16), dtype=torch.uint8, device=dev)
+    ws_att = torch.empty(max(tdx.restore_attn_workspace(shape, dl, max_priv), 16), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    nnz = ds.nnz()
+    counts = np.diff(ds.off.cpu().numpy().astype(np.int64)).reshape(N, L)
+
+    stages = ["rerotate", "select", "encode", "restore_attn"]
+
+    def step(ev=None):
+        def mark(j):
+            if ev is not None:
+                ev[j].record()
+        mark(0)
+        tdx.rerotate(shape, dl, kc, out=kr)
+        mark(1)
+        tdx.select_important(shape1, dl, kr, kx, k, check_layer=cfg.check_layer, out=sel, ws=ws_sel)
+        mark(2)
+        tdx.diff_encode(shape, dl, sel["master"], ak, av, out=ds, check=False, ws=ws_enc)
+        mark(3)
+        tdx.restore_attn(shape, dl, q, po, pk, pv, max_priv, ds.master_k, ds.master_v, ds, out=out, ws=ws_att)
+        mark(4)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for s in range(args.steps):
+        step(evs[s])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    stage_ms = {name: float(np.mean([evs[s][j].elapsed_time(evs[s][j + 1]) for s in range(args.steps)]))
+                for j, name in enumerate(stages)}
+    if ds.nnz() != nnz or nnz > cap:
+        raise RuntimeError("diff encode changed between steps or overflowed")
+
+    # ---- dense comparator on the same round (outside the step)
+    dense = None
+    if not args.no_dense:
+        kd = torch.empty((N, L, T, H, D), dtype=cfg.torch_dtype, device=dev)
+        vd = torch.empty_like(kd)
+        outd = torch.empty_like(out)
+        ws_d = torch.empty(max(tdx.decode_attn_dense_workspace(shape, dl, max_priv), 16), dtype=torch.uint8, device=dev)
+
+        def dense_step():
+            tdx.restore_dense(shape, dl, ds.master_k, ds.master_v, ds, kd, vd)
+            tdx.decode_attn_dense(shape, dl, q, po, pk, pv, max_priv, kd, vd, out=outd, ws=ws_d)
+
+        for _ in range(max(1, args.warmup)):
+            dense_step()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            dense_step()
+        e1.record()
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / args.steps
+        diff = (outd.float() - out.float()).abs().max().item()
+        dense = {"ms": dense_ms, "fused_ms": stage_ms["restore_attn"],
+                 "speedup_fused_vs_dense": dense_ms / stage_ms["restore_attn"],
+                 "max_abs_fused_minus_dense": diff}
+        del kd, vd
+
+    byts = stage_bytes(cfg, lay, nnz, k)
+    stage_rep = {}
+    for name in stages:
+        gbs = byts[name] / (stage_ms[name] * 1e-3) / 1e9
+        stage_rep[name] = {"ms": round(stage_ms[name], 4), "alg_GB": round(byts[name] / 1e9, 4),
+                           "GBps": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    if dense is not None:
+        gbs = byts["dense"] / (dense["ms"] * 1e-3) / 1e9
+        dense.update({"alg_GB": round(byts["dense"] / 1e9, 3), "GBps": round(gbs, 1)})
+    dom = max(stages, key=lambda n: stage_ms[n])
+    reuse_ms = stage_ms["rerotate"] + stage_ms["select"]
+    agent_tokens = N * T
+    res = {
+        "metric": "collective reuse agent-tokens/s; fused restore-attn GB/s (% of HBM peak)",
+        "value": agent_tokens / (ms_step * 1e-3),
+        "unit": "agent-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) K/V/q, generated in HBM)",
+        "config": {"workload": cfg.name, "n_agents": N, "n_layers": L, "n_kv_heads": H,
+                   "n_q_heads": Hq, "head_dim": D, "shared_tokens": T,
+                   "private_tokens_total": int(lay.priv_len.sum()), "select_k": k,
+                   "diff_blocks": nnz, "master": master, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(stage_rep[dom]["GBps"], 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(stage_rep[dom]["GBps"] / HBM_PEAK_GBS, 4), "traffic": None},
+        "fused_restore_attn": {"GBps": stage_rep["restore_attn"]["GBps"],
+                               "frac_hbm_peak": stage_rep["restore_attn"]["frac_hbm_peak"]},
+        "collective_reuse_agent_tokens_per_s": agent_tokens / (reuse_ms * 1e-3),
+        "stages": stage_rep,
+        "dense_comparator": dense,
+        "compression": compression(counts, master, T, H, D, cfg.elem_bytes, lay.priv_len, L),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, lay, cfg.pct)
+        res["gpu_vs_oracle"] = res["value"] / res["cpu_baseline"]["value"]
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,323 @@
+// C ABI entry points: argument checks, dispatch to the HIP launchers,
+// error reporting.  No C++ exception crosses this boundary.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return TDX_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(TDX_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQ(cond, code, ...)                 \
+  do {                                       \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+#define REQ_PTR(p) REQ((p) != nullptr && aligned16(p), TDX_EINVAL, "%s is null or not 16-byte aligned", #p)
+#define REQ_PTR4(p) \
+  REQ((p) != nullptr && (reinterpret_cast<uintptr_t>(p) & 3u) == 0, TDX_EINVAL, "%s is null or not 4-byte aligned", #p)
+
+// Shape checks common to all calls.
+int check_shape(const tdx_shape* s, tdx::Dims* d) {
+  REQ(s != nullptr, TDX_EINVAL, "shape is null");
+  REQ(s->dtype == TDX_F32 || s->dtype == TDX_BF16, TDX_EINVAL, "dtype %d is not TDX_F32/TDX_BF16", s->dtype);
+  REQ(s->n_layers >= 1, TDX_EINVAL, "n_layers %d < 1", s->n_layers);
+  REQ(s->n_kv_heads >= 1 && s->n_q_heads >= 1, TDX_EINVAL, "head counts must be >= 1");
+  REQ(s->n_q_heads % s->n_kv_heads == 0, TDX_EINVAL, "n_q_heads %d is not a multiple of n_kv_heads %d",
+      s->n_q_heads, s->n_kv_heads);
+  REQ(s->head_dim == 64 || s->head_dim == 128, TDX_EUNSUPPORTED, "head_dim %d not in {64, 128}", s->head_dim);
+  REQ(s->rope_theta > 1.0, TDX_EINVAL, "rope_theta must be > 1");
+  REQ(s->n_kv_heads <= 16, TDX_EUNSUPPORTED, "n_kv_heads %d > 16", s->n_kv_heads);
+  d->L = s->n_layers;
+  d->Hkv = s->n_kv_heads;
+  d->Hq = s->n_q_heads;
+  d->D = s->head_dim;
+  d->dtype = s->dtype;
+  d->theta = s->rope_theta;
+  return TDX_OK;
+}
+
+int check_layout(const tdx_layout* lay, tdx::Dims* d, bool need_pos) {
+  REQ(lay != nullptr, TDX_EINVAL, "layout is null");
+  REQ(lay->n_agents >= 1, TDX_EINVAL, "n_agents %d < 1", lay->n_agents);
+  REQ(lay->n_blocks >= 1, TDX_EINVAL, "n_blocks %d < 1", lay->n_blocks);
+  REQ(lay->n_tokens >= 1, TDX_EINVAL, "n_tokens %d < 1", lay->n_tokens);
+  REQ(lay->n_agents <= 1024, TDX_EUNSUPPORTED, "n_agents %d > 1024", lay->n_agents);
+  REQ(lay->n_blocks <= 4096, TDX_EUNSUPPORTED, "n_blocks %d > 4096", lay->n_blocks);
+  if (need_pos) {
+    REQ_PTR4(lay->blk_start);
+    REQ_PTR4(lay->src_pos);
+    REQ_PTR4(lay->dst_pos);
+  }
+  d->N = lay->n_agents;
+  d->B = lay->n_blocks;
+  d->T = lay->n_tokens;
+  return TDX_OK;
+}
+
+#define GUARD_BEGIN try {
+#define GUARD_END                                                   \
+  }                                                                 \
+  catch (...) {                                                     \
+    return fail(TDX_EINTERNAL, "unexpected exception in %s", __func__); \
+  }
+
+}  // namespace
+
+extern "C" {
+
+int tdx_version(void) { return TDX_VERSION; }
+
+const char* tdx_strerror(int code) {
+  switch (code) {
+    case TDX_OK: return "success";
+    case TDX_EINVAL: return "invalid argument";
+    case TDX_EUNSUPPORTED: return "unsupported shape";
+    case TDX_EHIP: return "HIP runtime error";
+    case TDX_EINTERNAL: return "internal error";
+    case TDX_EWORKSPACE: return "workspace missing or too small";
+    default: return "unknown error code";
+  }
+}
+
+const char* tdx_last_error(void) { return g_last_error.c_str(); }
+
+int32_t tdx_topk_count(int32_t pct, int32_t n_tokens) {
+  if (n_tokens < 1 || pct < 0 || pct > 100) return 0;
+  int64_t k = ((int64_t)pct * n_tokens + 99) / 100;
+  if (k < 1) k = 1;
+  if (k > n_tokens) k = n_tokens;
+  return (int32_t)k;
+}
+
+int tdx_rerotate(const tdx_shape* shape, const tdx_layout* layout, const void* k_cached,
+                 void* k_out, void* stream) {
+  GUARD_BEGIN
+  tdx::Dims d{};
+  int rc;
+  if ((rc = check_shape(shape, &d)) != TDX_OK) return rc;
+  if ((rc = check_layout(layout, &d, true)) != TDX_OK) return rc;
+  REQ_PTR(k_cached);
+  REQ_PTR(k_out);
+  hipError_t e = tdx::launch_rerotate(d, *layout, k_cached, k_out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tdx_rerotate launch");
+  return ok();
+  GUARD_END
+}
+
+size_t tdx_select_workspace(const tdx_shape* shape, const tdx_layout* layout) {
+  tdx::Dims d{};
+  if (check_shape(shape, &d) != TDX_OK || check_layout(layout, &d, false) != TDX_OK) return 0;
+  return tdx::select_ws_bytes(d);
+}
+
+int tdx_select_important(const tdx_shape* shape, const tdx_layout* layout, int32_t check_layer,
+                         const void* k_reuse, const void* k_recomp, int32_t k, float* dev,
+                         float* score, float* agent_dev, int32_t* selected, int32_t* master,
+                         void* ws, size_t ws_bytes, void* stream) {
+  GUARD_BEGIN
+  tdx::Dims d{};
+  int rc;
+  if ((rc = check_shape(shape, &d)) != TDX_OK) return rc;
+  if ((rc = check_layout(layout, &d, false)) != TDX_OK) return rc;
+  REQ(check_layer >= 0 && check_layer < d.L, TDX_EINVAL, "check_layer %d outside [0, %d)", check_layer, d.L);
+  REQ(k >= 1 && k <= d.T, TDX_EINVAL, "k %d outside [1, %d]", k, d.T);
+  REQ_PTR(k_reuse);
+  REQ_PTR(k_recomp);
+  REQ_PTR4(dev);
+  REQ_PTR4(score);
+  REQ_PTR4(agent_dev);
+  REQ_PTR4(selected);
+  REQ_PTR4(master);
+  const size_t need = tdx::select_ws_bytes(d);
+  REQ(ws != nullptr && aligned16(ws) && ws_bytes >= need, TDX_EWORKSPACE,
+      "workspace needs %zu bytes (16-byte aligned), got %zu", need, ws_bytes);
+  hipError_t e = tdx::launch_select(d, *layout, check_layer, k_reuse, k_recomp, k, dev, score,
+                                    agent_dev, selected, master, ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tdx_select_important launch");
+  return ok();
+  GUARD_END
+}
+
+size_t tdx_diff_encode_workspace(const tdx_shape* shape, const tdx_layout* layout) {
+  tdx::Dims d{};
+  if (check_shape(shape, &d) != TDX_OK || check_layout(layout, &d, false) != TDX_OK) return 0;
+  return tdx::encode_ws_bytes(d);
+}
+
+int tdx_diff_encode(const tdx_shape* shape, const tdx_layout* layout, const int32_t* master,
+                    const void* agents_k, const void* agents_v, int64_t cap_blocks,
+                    int32_t* diff_off, int32_t* diff_idx, void* diff_k, void* diff_v,
+                    int64_t* nnz, void* master_k_out, void* master_v_out, void* ws,
+                    size_t ws_bytes, void* stream) {
+  GUARD_BEGIN
+  tdx::Dims d{};
+  int rc;
+  if ((rc = check_shape(shape, &d)) != TDX_OK) return rc;
+  if ((rc = check_layout(layout, &d, false)) != TDX_OK) return rc;
+  REQ(d.T % TDX_DIFF_BLOCK == 0, TDX_EINVAL, "n_tokens %d is not a multiple of 16", d.T);
+  REQ(cap_blocks >= 0, TDX_EINVAL, "cap_blocks < 0");
+  REQ((int64_t)d.N * d.L <= INT32_MAX, TDX_EUNSUPPORTED, "too many CSR rows");
+  REQ_PTR4(master);
+  REQ_PTR(agents_k);
+  REQ_PTR(agents_v);
+  REQ_PTR4(diff_off);
+  REQ((reinterpret_cast<uintptr_t>(nnz) & 7u) == 0 && nnz != nullptr, TDX_EINVAL, "nnz is null or not 8-byte aligned");
+  if (cap_blocks > 0) {
+    REQ_PTR4(diff_idx);
+    REQ_PTR(diff_k);
+    REQ_PTR(diff_v);
+  }
+  REQ((master_k_out == nullptr) == (master_v_out == nullptr), TDX_EINVAL,
+      "master_k_out and master_v_out must both be set or both be NULL");
+  if (master_k_out != nullptr) {
+    REQ_PTR(master_k_out);
+    REQ_PTR(master_v_out);
+  }
+  const size_t need = tdx::encode_ws_bytes(d);
+  REQ(ws != nullptr && aligned16(ws) && ws_bytes >= need, TDX_EWORKSPACE,
+      "workspace needs %zu bytes (16-byte aligned), got %zu", need, ws_bytes);
+  hipError_t e = tdx::launch_encode(d, master, agents_k, agents_v, cap_blocks, diff_off, diff_idx,
+                                    diff_k, diff_v, nnz, master_k_out, master_v_out, ws,
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tdx_diff_encode launch");
+  return ok();
+  GUARD_END
+}
+
+size_t tdx_restore_attn_workspace(const tdx_shape* shape, const tdx_layout* layout, int32_t max_priv) {
+  tdx::Dims d{};
+  if (check_shape(shape, &d) != TDX_OK || check_layout(layout, &d, false) != TDX_OK || max_priv < 0) return 0;
+  return tdx::restore_attn_ws_bytes(d, max_priv);
+}
+
+int tdx_restore_attn(const tdx_shape* shape, const tdx_layout* layout, const void* q,
+                     const int32_t* priv_off, const void* priv_k, const void* priv_v,
+                     int32_t max_priv, const void* master_k, const void* master_v,
+                     const int32_t* diff_off, const int32_t* diff_idx, const void* diff_k,
+                     const void* diff_v, float scale, void* out, void* ws, size_t ws_bytes,
+                     void* stream) {
+  GUARD_BEGIN
+  tdx::Dims d{};
+  int rc;
+  if ((rc = check_shape(shape, &d)) != TDX_OK) return rc;
+  if ((rc = check_layout(layout, &d, true)) != TDX_OK) return rc;
+  REQ(d.T % TDX_DIFF_BLOCK == 0, TDX_EINVAL, "n_tokens %d is not a multiple of 16", d.T);
+  REQ(d.Hq / d.Hkv <= 16, TDX_EUNSUPPORTED, "more than 16 query heads per KV head");
+  REQ(max_priv >= 0, TDX_EINVAL, "max_priv < 0");
+  REQ(scale > 0.0f, TDX_EINVAL, "scale must be > 0");
+  REQ_PTR(q);
+  REQ_PTR4(priv_off);
+  if (max_priv > 0) {
+    REQ_PTR(priv_k);
+    REQ_PTR(priv_v);
+  }
+  REQ_PTR(master_k);
+  REQ_PTR(master_v);
+  REQ_PTR4(diff_off);
+  // diff arrays may be empty (all rows empty) but must then still be valid
+  // pointers to zero-length storage; they are only read through diff_off.
+  REQ(diff_idx != nullptr && diff_k != nullptr && diff_v != nullptr, TDX_EINVAL, "diff arrays are null");
+  REQ(aligned16(diff_k) && aligned16(diff_v), TDX_EINVAL, "diff_k/diff_v not 16-byte aligned");
+  REQ_PTR(out);
+  const size_t need = tdx::restore_attn_ws_bytes(d, max_priv);
+  REQ(ws != nullptr && aligned16(ws) && ws_bytes >= need, TDX_EWORKSPACE,
+      "workspace needs %zu bytes (16-byte aligned), got %zu", need, ws_bytes);
+  hipError_t e = tdx::launch_restore_attn(d, *layout, q, priv_off, priv_k, priv_v, max_priv,
+                                          master_k, master_v, diff_off, diff_idx, diff_k, diff_v,
+                                          scale, out, ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tdx_restore_attn launch");
+  return ok();
+  GUARD_END
+}
+
+int tdx_restore_dense(const tdx_shape* shape, const tdx_layout* layout, const void* master_k,
+                      const void* master_v, const int32_t* diff_off, const int32_t* diff_idx,
+                      const void* diff_k, const void* diff_v, void* k_dense, void* v_dense,
+                      void* stream) {
+  GUARD_BEGIN
+  tdx::Dims d{};
+  int rc;
+  if ((rc = check_shape(shape, &d)) != TDX_OK) return rc;
+  if ((rc = check_layout(layout, &d, true)) != TDX_OK) return rc;
+  REQ(d.T % TDX_DIFF_BLOCK == 0, TDX_EINVAL, "n_tokens %d is not a multiple of 16", d.T);
+  REQ_PTR(master_k);
+  REQ_PTR(master_v);
+  REQ_PTR4(diff_off);
+  REQ(diff_idx != nullptr && diff_k != nullptr && diff_v != nullptr, TDX_EINVAL, "diff arrays are null");
+  REQ(aligned16(diff_k) && aligned16(diff_v), TDX_EINVAL, "diff_k/diff_v not 16-byte aligned");
+  REQ_PTR(k_dense);
+  REQ_PTR(v_dense);
+  hipError_t e = tdx::launch_restore_dense(d, *layout, master_k, master_v, diff_off, diff_idx,
+                                           diff_k, diff_v, k_dense, v_dense,
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tdx_restore_dense launch");
+  return ok();
+  GUARD_END
+}
+
+size_t tdx_decode_attn_dense_workspace(const tdx_shape* shape, const tdx_layout* layout,
+                                       int32_t max_priv) {
+  tdx::Dims d{};
+  if (check_shape(shape, &d) != TDX_OK || check_layout(layout, &d, false) != TDX_OK || max_priv < 0) return 0;
+  return tdx::dense_attn_ws_bytes(d, max_priv);
+}
+
+int tdx_decode_attn_dense(const tdx_shape* shape, const tdx_layout* layout, const void* q,
+                          const int32_t* priv_off, const void* priv_k, const void* priv_v,
+                          int32_t max_priv, const void* k_dense, const void* v_dense, float scale,
+                          void* out, void* ws, size_t ws_bytes, void* stream) {
+  GUARD_BEGIN
+  tdx::Dims d{};
+  int rc;
+  if ((rc = check_shape(shape, &d)) != TDX_OK) return rc;
+  if ((rc = check_layout(layout, &d, false)) != TDX_OK) return rc;
+  REQ(d.T % TDX_DIFF_BLOCK == 0, TDX_EINVAL, "n_tokens %d is not a multiple of 16", d.T);
+  REQ(d.Hq / d.Hkv <= 16, TDX_EUNSUPPORTED, "more than 16 query heads per KV head");
+  REQ(max_priv >= 0, TDX_EINVAL, "max_priv < 0");
+  REQ(scale > 0.0f, TDX_EINVAL, "scale must be > 0");
+  REQ_PTR(q);
+  REQ_PTR4(priv_off);
+  if (max_priv > 0) {
+    REQ_PTR(priv_k);
+    REQ_PTR(priv_v);
+  }
+  REQ_PTR(k_dense);
+  REQ_PTR(v_dense);
+  REQ_PTR(out);
+  const size_t need = tdx::dense_attn_ws_bytes(d, max_priv);
+  REQ(ws != nullptr && aligned16(ws) && ws_bytes >= need, TDX_EWORKSPACE,
+      "workspace needs %zu bytes (16-byte aligned), got %zu", need, ws_bytes);
+  hipError_t e = tdx::launch_dense_attn(d, q, priv_off, priv_k, priv_v, max_priv, k_dense, v_dense,
+                                        scale, out, ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tdx_decode_attn_dense launch");
+  return ok();
+  GUARD_END
+}
+
+}  // extern "C"

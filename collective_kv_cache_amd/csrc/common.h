@@ -1,0 +1,136 @@
+// Device helpers shared by the tdx HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/tdx.h"
+
+namespace tdx {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kBlock = TDX_DIFF_BLOCK;  // 16-token diff block
+
+// ---- element formats -------------------------------------------------------
+// A 16-byte vector holds 8 bf16 or 4 fp32 values.  bf16 is kept as raw bits.
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest, ties to even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+template <typename E>
+struct Fmt;
+
+template <>
+struct Fmt<uint16_t> {  // bf16 bits
+  static constexpr int VEC = 8;
+  __device__ static __forceinline__ void unpack(const u32x4& v, float* x) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = bf16_lo(v[k]);
+      x[2 * k + 1] = bf16_hi(v[k]);
+    }
+  }
+  __device__ static __forceinline__ u32x4 pack(const float* x) {
+    u32x4 v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = pack_bf16(x[2 * k], x[2 * k + 1]);
+    return v;
+  }
+};
+
+template <>
+struct Fmt<float> {
+  static constexpr int VEC = 4;
+  __device__ static __forceinline__ void unpack(const u32x4& v, float* x) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = __uint_as_float(v[k]);
+  }
+  __device__ static __forceinline__ u32x4 pack(const float* x) {
+    u32x4 v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = __float_as_uint(x[k]);
+    return v;
+  }
+};
+
+template <typename E>
+__device__ __forceinline__ u32x4 ld16(const E* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+template <typename E>
+__device__ __forceinline__ void st16(E* p, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+// Streaming store: the written data is not re-read by this kernel.
+template <typename E>
+__device__ __forceinline__ void st16_nt(E* p, const u32x4& v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
+// RoPE inverse frequency theta^(-2e/D) in double precision.
+__device__ __forceinline__ double rope_inv_freq(double theta, int e, int D) {
+  return pow(theta, -2.0 * (double)e / (double)D);
+}
+
+}  // namespace tdx
+
+// ---- internal launchers (implemented per kernel file, called by api.hip) ----
+// Each returns hipSuccess or the launch error.  Arguments are already checked.
+namespace tdx {
+
+struct Dims {
+  int N, B, T, L, Hkv, Hq, D;
+  int dtype;
+  double theta;
+};
+
+hipError_t launch_rerotate(const Dims& d, const tdx_layout& lay, const void* kc, void* out,
+                           hipStream_t s);
+
+size_t select_ws_bytes(const Dims& d);
+hipError_t launch_select(const Dims& d, const tdx_layout& lay, int check_layer,
+                         const void* k_reuse, const void* k_recomp, int k, float* dev,
+                         float* score, float* agent_dev, int32_t* selected, int32_t* master,
+                         void* ws, hipStream_t s);
+
+size_t encode_ws_bytes(const Dims& d);
+hipError_t launch_encode(const Dims& d, const int32_t* master, const void* ak, const void* av,
+                         int64_t cap, int32_t* diff_off, int32_t* diff_idx, void* diff_k,
+                         void* diff_v, int64_t* nnz, void* mk_out, void* mv_out, void* ws,
+                         hipStream_t s);
+
+size_t restore_attn_ws_bytes(const Dims& d, int max_priv);
+hipError_t launch_restore_attn(const Dims& d, const tdx_layout& lay, const void* q,
+                               const int32_t* priv_off, const void* pk, const void* pv,
+                               int max_priv, const void* mk, const void* mv,
+                               const int32_t* diff_off, const int32_t* diff_idx,
+                               const void* dk, const void* dv, float scale, void* out, void* ws,
+                               hipStream_t s);
+
+hipError_t launch_restore_dense(const Dims& d, const tdx_layout& lay, const void* mk,
+                                const void* mv, const int32_t* diff_off,
+                                const int32_t* diff_idx, const void* dk, const void* dv,
+                                void* kd, void* vd, hipStream_t s);
+
+size_t dense_attn_ws_bytes(const Dims& d, int max_priv);
+hipError_t launch_dense_attn(const Dims& d, const void* q, const int32_t* priv_off,
+                             const void* pk, const void* pv, int max_priv, const void* kd,
+                             const void* vd, float scale, void* out, void* ws, hipStream_t s);
+
+}  // namespace tdx

@@ -1,0 +1,242 @@
+// a4: Master-Mirror block-sparse diff encode.
+//
+// TokenDance notes, Figure 8 and §2b (blog §4.3): the least-deviation agent
+// (the Master) keeps its full cache; every other agent (a Mirror) stores only
+// the 16-token blocks that differ from the Master, as block-sparse
+// (indices, values), one record per Mirror per layer.
+//
+// Kernels (all deterministic, no atomics on the data path):
+//  flag_kernel    one workgroup per (block beta, layer l): the Master block's
+//                 K and V sit in registers (16-byte chunks per lane); every
+//                 Mirror block is streamed once and compared bit for bit; a
+//                 workgroup-wide OR decides the flag.  Optionally writes the
+//                 dense Master copy from the same registers.
+//  rows_kernel    one workgroup per CSR row (agent, layer): count of flagged
+//                 blocks and each block's rank inside its row.
+//  offsets_kernel one workgroup: exclusive scan of the row counts -> row
+//                 offsets and the true total nnz.
+//  copy_kernel    one workgroup per (row, 8-block chunk): writes the ascending
+//                 block indices and copies the Mirror's K/V blocks; entries at
+//                 or past the capacity are skipped.
+#include "common.h"
+
+namespace tdx {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kCopyChunk = 8;
+constexpr int kScanThreads = 1024;
+
+// KC = 16-byte chunks per thread per tensor for one 16-token block.
+template <int KC>
+__global__ __launch_bounds__(kThreads) void flag_kernel(
+    const u32x4* __restrict__ ak, const u32x4* __restrict__ av,
+    const int32_t* __restrict__ master_p, int N, int L, int nb, int chunks,
+    uint8_t* __restrict__ flags, u32x4* __restrict__ mk_out, u32x4* __restrict__ mv_out) {
+  const int beta = blockIdx.x;
+  const int l = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int m = master_p[0];
+  if (m < 0 || m >= N) {  // invalid Master: no reads; offsets_kernel reports nnz = -1
+    for (int i = tid; i < N; i += kThreads) flags[((size_t)i * L + l) * nb + beta] = 0;
+    return;
+  }
+  // chunk offset of (agent a, layer l, block beta): ((a*L + l)*nb + beta)*chunks
+  const size_t layer_chunks = (size_t)nb * chunks;
+  const size_t mbase = ((size_t)m * L + l) * layer_chunks + (size_t)beta * chunks;
+  u32x4 mkr[KC], mvr[KC];
+#pragma unroll
+  for (int j = 0; j < KC; ++j) {
+    const int c = tid + j * kThreads;
+    if (c < chunks) {
+      mkr[j] = ak[mbase + c];
+      mvr[j] = av[mbase + c];
+    }
+  }
+  if (mk_out != nullptr) {
+    const size_t obase = (size_t)l * layer_chunks + (size_t)beta * chunks;
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      const int c = tid + j * kThreads;
+      if (c < chunks) {
+        __builtin_nontemporal_store(mkr[j], mk_out + obase + c);
+        __builtin_nontemporal_store(mvr[j], mv_out + obase + c);
+      }
+    }
+  }
+  for (int i = 0; i < N; ++i) {
+    if (i == m) {
+      if (tid == 0) flags[((size_t)i * L + l) * nb + beta] = 0;
+      continue;
+    }
+    const size_t base = ((size_t)i * L + l) * layer_chunks + (size_t)beta * chunks;
+    uint32_t acc = 0;
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      const int c = tid + j * kThreads;
+      if (c < chunks) {
+        const u32x4 xk = ak[base + c] ^ mkr[j];
+        const u32x4 xv = av[base + c] ^ mvr[j];
+        acc |= xk[0] | xk[1] | xk[2] | xk[3] | xv[0] | xv[1] | xv[2] | xv[3];
+      }
+    }
+    const int any = __syncthreads_or(acc != 0);
+    if (tid == 0) flags[((size_t)i * L + l) * nb + beta] = any ? 1 : 0;
+  }
+}
+
+__device__ __forceinline__ int lanemask_count(uint64_t m, int lane) {
+  return __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+}
+
+// In-row exclusive ranks of the flagged blocks and the row count.
+__global__ __launch_bounds__(kThreads) void rows_kernel(const uint8_t* __restrict__ flags, int nb,
+                                                        int32_t* __restrict__ rank,
+                                                        int32_t* __restrict__ count) {
+  constexpr int W = kThreads / kWave;
+  __shared__ int wcnt[W];
+  const size_t r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  int carry = 0;
+  for (int base = 0; base < nb; base += kThreads) {
+    const int beta = base + tid;
+    const bool f = beta < nb && flags[r * nb + beta] != 0;
+    const uint64_t m = __ballot(f);
+    if (lane == 0) wcnt[wave] = __popcll(m);
+    __syncthreads();
+    int pre = carry, all = carry;
+    for (int w = 0; w < W; ++w) {
+      if (w < wave) pre += wcnt[w];
+      all += wcnt[w];
+    }
+    if (beta < nb) rank[r * nb + beta] = pre + lanemask_count(m, lane);
+    carry = all;
+    __syncthreads();
+  }
+  if (tid == 0) count[r] = carry;
+}
+
+__global__ __launch_bounds__(kScanThreads) void offsets_kernel(const int32_t* __restrict__ count,
+                                                               int rows, int32_t* __restrict__ off,
+                                                               int64_t* __restrict__ nnz,
+                                                               const int32_t* __restrict__ master_p,
+                                                               int N) {
+  constexpr int W = kScanThreads / kWave;
+  __shared__ long long wsum[W];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  long long carry = 0;
+  for (int base = 0; base < rows; base += kScanThreads) {
+    const int r = base + tid;
+    long long v = r < rows ? count[r] : 0;
+    // inclusive wave scan
+    long long x = v;
+    for (int o = 1; o < kWave; o <<= 1) {
+      const long long y = __shfl_up(x, o, kWave);
+      if (lane >= o) x += y;
+    }
+    if (lane == kWave - 1) wsum[wave] = x;
+    __syncthreads();
+    long long pre = carry, all = carry;
+    for (int w = 0; w < W; ++w) {
+      if (w < wave) pre += wsum[w];
+      all += wsum[w];
+    }
+    if (r < rows) off[r] = (int32_t)(pre + x - v);
+    carry = all;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    off[rows] = (int32_t)carry;
+    const int m = master_p[0];
+    nnz[0] = (m < 0 || m >= N) ? -1 : carry;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void copy_kernel(
+    const u32x4* __restrict__ ak, const u32x4* __restrict__ av, const uint8_t* __restrict__ flags,
+    const int32_t* __restrict__ rank, const int32_t* __restrict__ off, int nb, int chunks,
+    int64_t cap, int32_t* __restrict__ diff_idx, u32x4* __restrict__ dk, u32x4* __restrict__ dv) {
+  const size_t r = blockIdx.y;
+  const int b0 = blockIdx.x * kCopyChunk;
+  const int tid = threadIdx.x;
+  const int64_t row_off = off[r];
+  for (int beta = b0; beta < min(b0 + kCopyChunk, nb); ++beta) {
+    if (!flags[r * nb + beta]) continue;  // uniform
+    const int64_t slot = row_off + rank[r * nb + beta];
+    if (slot >= cap) continue;
+    if (tid == 0) diff_idx[slot] = beta;
+    const size_t src = (r * nb + beta) * (size_t)chunks;
+    const size_t dst = (size_t)slot * chunks;
+    for (int c = tid; c < chunks; c += kThreads) {
+      __builtin_nontemporal_store(ak[src + c], dk + dst + c);
+      __builtin_nontemporal_store(av[src + c], dv + dst + c);
+    }
+  }
+}
+
+struct WsLayout {
+  size_t flags, rank, count, total;
+};
+
+WsLayout ws_layout(const Dims& d) {
+  const size_t rows = (size_t)d.N * d.L;
+  const size_t nb = (size_t)(d.T / kBlock);
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  WsLayout w;
+  w.flags = 0;
+  w.rank = up(rows * nb);
+  w.count = w.rank + up(rows * nb * 4);
+  w.total = w.count + up(rows * 4);
+  return w;
+}
+
+}  // namespace
+
+size_t encode_ws_bytes(const Dims& d) { return ws_layout(d).total; }
+
+hipError_t launch_encode(const Dims& d, const int32_t* master, const void* ak, const void* av,
+                         int64_t cap, int32_t* diff_off, int32_t* diff_idx, void* diff_k,
+                         void* diff_v, int64_t* nnz, void* mk_out, void* mv_out, void* ws,
+                         hipStream_t s) {
+  const int nb = d.T / kBlock;
+  const int eb = d.dtype == TDX_BF16 ? 2 : 4;
+  const int chunks = kBlock * d.Hkv * d.D * eb / 16;  // 16-byte chunks per block per tensor
+  const int rows = d.N * d.L;
+  const WsLayout w = ws_layout(d);
+  uint8_t* flags = static_cast<uint8_t*>(ws) + w.flags;
+  int32_t* rank = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + w.rank);
+  int32_t* count = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + w.count);
+  const u32x4* k4 = static_cast<const u32x4*>(ak);
+  const u32x4* v4 = static_cast<const u32x4*>(av);
+  u32x4* mk4 = static_cast<u32x4*>(mk_out);
+  u32x4* mv4 = static_cast<u32x4*>(mv_out);
+  {
+    const int kc = (chunks + kThreads - 1) / kThreads;
+    dim3 grid(nb, d.L);
+#define TDX_FLAG(KC)                                                                         \
+  hipLaunchKernelGGL(flag_kernel<KC>, grid, dim3(kThreads), 0, s, k4, v4, master, d.N, d.L, \
+                     nb, chunks, flags, mk4, mv4)
+    if (kc <= 1) TDX_FLAG(1);
+    else if (kc <= 2) TDX_FLAG(2);
+    else if (kc <= 4) TDX_FLAG(4);
+    else if (kc <= 8) TDX_FLAG(8);
+    else if (kc <= 16) TDX_FLAG(16);
+    else return hipErrorInvalidValue;
+#undef TDX_FLAG
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(rows_kernel, dim3(rows), dim3(kThreads), 0, s, flags, nb, rank, count);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(kScanThreads), 0, s, count, rows, diff_off, nnz,
+                     master, d.N);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 cgrid((nb + kCopyChunk - 1) / kCopyChunk, rows);
+  hipLaunchKernelGGL(copy_kernel, cgrid, dim3(kThreads), 0, s, k4, v4, flags, rank, diff_off, nb,
+                     chunks, cap, diff_idx, static_cast<u32x4*>(diff_k),
+                     static_cast<u32x4*>(diff_v));
+  return hipGetLastError();
+}
+
+}  // namespace tdx

@@ -1,0 +1,152 @@
+// a1: batched RoPE delta re-rotation of the cached shared K to all N agents.
+//
+// TokenDance notes, Summary "Method" and Figure 7 (path T3): the K of the
+// shared blocks is corrected to every agent's absolute offsets by one
+// group-wide RoPE pass instead of one pass per agent; Deep Analysis §0: the
+// position difference of a block is fixed by one rotation R(Delta).
+//
+// Design (gfx950): the pass reads each cached K tile once and writes N
+// rotated copies, so it is bound by HBM writes.  A workgroup owns a tile of
+// up to 16 canonical tokens that lies inside one shared block, for a group of
+// layers.  It evaluates cos/sin(Delta(i,b) * theta^(-2e/D)) for up to 64
+// agents in double precision into LDS once, then streams: every lane holds the
+// 16-byte chunk at dims [e0, e0+VEC) and its rotate-half partner at
+// [e0+D/2, e0+D/2+VEC) in registers and emits both rotated chunks for every
+// agent with 16-byte non-temporal stores.
+#include "common.h"
+
+namespace tdx {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTileTok = 16;
+constexpr int kAgentChunk = 64;
+constexpr int kItems = 4;  // (token, head) rows held per lane at once
+constexpr int kMaxBlocksLds = 4096;
+
+template <typename E, int D>
+__global__ __launch_bounds__(kThreads) void rerotate_kernel(
+    const E* __restrict__ kc, E* __restrict__ out, const int32_t* __restrict__ blk_start,
+    const int32_t* __restrict__ src_pos, const int32_t* __restrict__ dst_pos, int N, int B,
+    int T, int L, int Hkv, int lpg, double theta) {
+  constexpr int VEC = Fmt<E>::VEC;
+  constexpr int HALF = D / 2;
+  constexpr int G = HALF / VEC;       // lanes per (token, head) row
+  constexpr int RPP = kThreads / G;   // rows covered by the workgroup per item
+  __shared__ float2 tab[kAgentChunk * HALF];
+  __shared__ double invf[HALF];
+  __shared__ int32_t sblk[kMaxBlocksLds + 1];
+
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * kTileTok;
+  const int t1 = min(t0 + kTileTok, T);
+  const int l0 = blockIdx.y * lpg;
+  const int l1 = min(l0 + lpg, L);
+  if (t0 >= T || l0 >= L) return;  // uniform over the workgroup
+
+  for (int b = tid; b <= B; b += kThreads) sblk[b] = blk_start[b];
+  for (int e = tid; e < HALF; e += kThreads) invf[e] = rope_inv_freq(theta, e, D);
+  __syncthreads();
+
+  // first block containing t0: largest b with sblk[b] <= t0 (skips empty blocks)
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (sblk[mid] <= t0) lo = mid; else hi = mid - 1;
+  }
+
+  const int e0 = (tid % G) * VEC;
+  const int row_base = tid / G;
+  const size_t rowD = (size_t)Hkv * D;
+
+  for (int b = lo; b < B && sblk[b] < t1; ++b) {
+    const int ta = max(t0, sblk[b]);
+    const int tb = min(t1, sblk[b + 1]);
+    if (ta >= tb) continue;
+    const int nrows = (tb - ta) * Hkv;
+    const int sp = src_pos[b];
+    for (int a0 = 0; a0 < N; a0 += kAgentChunk) {
+      const int na = min(kAgentChunk, N - a0);
+      __syncthreads();  // previous users of tab are done
+      for (int x = tid; x < na * HALF; x += kThreads) {
+        const int a = x / HALF, e = x % HALF;
+        const double delta = (double)(dst_pos[(size_t)(a0 + a) * B + b] - sp);
+        double sn, cs;
+        sincos(delta * invf[e], &sn, &cs);
+        tab[x] = make_float2((float)cs, (float)sn);
+      }
+      __syncthreads();
+      for (int l = l0; l < l1; ++l) {
+        const E* src = kc + ((size_t)l * T + ta) * rowD;
+        for (int rb = 0; rb < nrows; rb += RPP * kItems) {
+          u32x4 xl[kItems], xh[kItems];
+#pragma unroll
+          for (int k = 0; k < kItems; ++k) {
+            const int r = rb + row_base + k * RPP;
+            if (r < nrows) {
+              xl[k] = ld16(src + (size_t)r * D + e0);
+              xh[k] = ld16(src + (size_t)r * D + HALF + e0);
+            }
+          }
+          for (int a = 0; a < na; ++a) {
+            float cs[VEC], sn[VEC];
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+              const float2 v = tab[a * HALF + e0 + j];
+              cs[j] = v.x;
+              sn[j] = v.y;
+            }
+            E* dst = out + ((size_t)(a0 + a) * L + l) * (size_t)T * rowD + (size_t)ta * rowD;
+#pragma unroll
+            for (int k = 0; k < kItems; ++k) {
+              const int r = rb + row_base + k * RPP;
+              if (r < nrows) {
+                float x[VEC], y[VEC], ox[VEC], oy[VEC];
+                Fmt<E>::unpack(xl[k], x);
+                Fmt<E>::unpack(xh[k], y);
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) {
+                  ox[j] = x[j] * cs[j] - y[j] * sn[j];
+                  oy[j] = y[j] * cs[j] + x[j] * sn[j];
+                }
+                st16_nt(dst + (size_t)r * D + e0, Fmt<E>::pack(ox));
+                st16_nt(dst + (size_t)r * D + HALF + e0, Fmt<E>::pack(oy));
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+template <typename E, int D>
+hipError_t launch_t(const Dims& d, const tdx_layout& lay, const void* kc, void* out,
+                    hipStream_t s) {
+  const int tiles = (d.T + kTileTok - 1) / kTileTok;
+  // enough workgroups to fill 256 CUs several times over, >= 1 layer each
+  int groups = (2048 + tiles - 1) / tiles;
+  groups = groups < 1 ? 1 : (groups > d.L ? d.L : groups);
+  const int lpg = (d.L + groups - 1) / groups;
+  groups = (d.L + lpg - 1) / lpg;
+  dim3 grid(tiles, groups);
+  hipLaunchKernelGGL((rerotate_kernel<E, D>), grid, dim3(kThreads), 0, s,
+                     static_cast<const E*>(kc), static_cast<E*>(out), lay.blk_start,
+                     lay.src_pos, lay.dst_pos, d.N, d.B, d.T, d.L, d.Hkv, lpg, d.theta);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rerotate(const Dims& d, const tdx_layout& lay, const void* kc, void* out,
+                           hipStream_t s) {
+  if (d.B > kMaxBlocksLds) return hipErrorInvalidValue;
+  if (d.dtype == TDX_BF16) {
+    return d.D == 128 ? launch_t<uint16_t, 128>(d, lay, kc, out, s)
+                      : launch_t<uint16_t, 64>(d, lay, kc, out, s);
+  }
+  return d.D == 128 ? launch_t<float, 128>(d, lay, kc, out, s)
+                    : launch_t<float, 64>(d, lay, kc, out, s);
+}
+
+}  // namespace tdx

@@ -1,0 +1,369 @@
+"""Python binding of libtdx (ctypes).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libtdx.so.  PyTorch provides device memory and the current stream.  When the
+library is missing, loading fails with an error; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtdx.so")
+
+TDX_OK = 0
+TDX_EINVAL = -1
+TDX_EUNSUPPORTED = -2
+TDX_EHIP = -3
+TDX_EINTERNAL = -4
+TDX_EWORKSPACE = -5
+TDX_F32 = 0
+TDX_BF16 = 1
+DIFF_BLOCK = 16
+
+
+class TdxError(RuntimeError):
+    def __init__(self, code: int, what: str, detail: str):
+        super().__init__(f"{what} failed ({code}: {detail})")
+        self.code = code
+
+
+class CShape(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("n_q_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("rope_theta", ctypes.c_double)]
+
+
+class CLayout(ctypes.Structure):
+    _fields_ = [("n_agents", ctypes.c_int32), ("n_blocks", ctypes.c_int32),
+                ("n_tokens", ctypes.c_int32), ("blk_start", ctypes.c_void_p),
+                ("src_pos", ctypes.c_void_p), ("dst_pos", ctypes.c_void_p)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_F = ctypes.c_float
+_PS = ctypes.POINTER(CShape)
+_PL = ctypes.POINTER(CLayout)
+
+_SIGS = {
+    "tdx_version": (ctypes.c_int, []),
+    "tdx_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "tdx_last_error": (ctypes.c_char_p, []),
+    "tdx_topk_count": (_I32, [_I32, _I32]),
+    "tdx_rerotate": (ctypes.c_int, [_PS, _PL, _P, _P, _P]),
+    "tdx_select_workspace": (_SZ, [_PS, _PL]),
+    "tdx_select_important": (ctypes.c_int, [_PS, _PL, _I32, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "tdx_diff_encode_workspace": (_SZ, [_PS, _PL]),
+    "tdx_diff_encode": (ctypes.c_int, [_PS, _PL, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "tdx_restore_attn_workspace": (_SZ, [_PS, _PL, _I32]),
+    "tdx_restore_attn": (ctypes.c_int, [_PS, _PL, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _F, _P, _P, _SZ, _P]),
+    "tdx_restore_dense": (ctypes.c_int, [_PS, _PL, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "tdx_decode_attn_dense_workspace": (_SZ, [_PS, _PL, _I32]),
+    "tdx_decode_attn_dense": (ctypes.c_int, [_PS, _PL, _P, _P, _P, _P, _I32, _P, _P, _F, _P, _P, _SZ, _P]),
+}
+
+EXPORTED = tuple(_SIGS)
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libtdx.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m collective_kv_cache_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def _check(rc: int, what: str):
+    if rc != TDX_OK:
+        raise TdxError(rc, what, lib().tdx_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if device is not None and _norm(t.device) != _norm(device):
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _norm(d) -> torch.device:
+    d = torch.device(d)
+    if d.type == "cuda" and d.index is None:
+        return torch.device("cuda", torch.cuda.current_device())
+    return d
+
+
+@dataclass(frozen=True)
+class Shape:
+    n_layers: int
+    n_kv_heads: int
+    n_q_heads: int
+    head_dim: int
+    dtype: torch.dtype  # torch.bfloat16 or torch.float32
+    rope_theta: float
+
+    def c(self) -> CShape:
+        code = {torch.bfloat16: TDX_BF16, torch.float32: TDX_F32}.get(self.dtype, -1)
+        return CShape(self.n_layers, self.n_kv_heads, self.n_q_heads, self.head_dim, code,
+                      float(self.rope_theta))
+
+    def with_layers(self, n: int) -> "Shape":
+        return Shape(n, self.n_kv_heads, self.n_q_heads, self.head_dim, self.dtype, self.rope_theta)
+
+
+class RoundLayout:
+    """Device copy of a round's geometry (int32 tensors) plus host scalars."""
+
+    def __init__(self, blk_start, src_pos, dst_pos, device):
+        bs = np.asarray(blk_start, dtype=np.int32)
+        sp = np.asarray(src_pos, dtype=np.int32)
+        dp = np.asarray(dst_pos, dtype=np.int32)
+        self.n_agents, self.n_blocks = dp.shape
+        self.n_tokens = int(bs[-1])
+        self.device = _norm(device)
+        self.blk_start = torch.as_tensor(bs, device=self.device)
+        self.src_pos = torch.as_tensor(sp, device=self.device)
+        self.dst_pos = torch.as_tensor(dp.reshape(-1), device=self.device)
+        self._c = CLayout(self.n_agents, self.n_blocks, self.n_tokens,
+                          self.blk_start.data_ptr(), self.src_pos.data_ptr(), self.dst_pos.data_ptr())
+
+    def c(self) -> CLayout:
+        return self._c
+
+
+def version() -> int:
+    return lib().tdx_version()
+
+
+def topk_count(pct: int, n_tokens: int) -> int:
+    return int(lib().tdx_topk_count(int(pct), int(n_tokens)))
+
+
+def strerror(code: int) -> str:
+    return lib().tdx_strerror(code).decode()
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def rerotate(shape: Shape, lay: RoundLayout, k_cached: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """a1: [L][T][Hkv][D] -> [N][L][T][Hkv][D] re-rotated to every agent's offsets."""
+    L, T, H, D = shape.n_layers, lay.n_tokens, shape.n_kv_heads, shape.head_dim
+    _need(k_cached, "k_cached", shape.dtype, (L, T, H, D), lay.device)
+    if out is None:
+        out = torch.empty((lay.n_agents, L, T, H, D), dtype=shape.dtype, device=lay.device)
+    _need(out, "out", shape.dtype, (lay.n_agents, L, T, H, D), lay.device)
+    s, l = shape.c(), lay.c()
+    _check(lib().tdx_rerotate(ctypes.byref(s), ctypes.byref(l), _ptr(k_cached), _ptr(out), _stream()),
+           "tdx_rerotate")
+    return out
+
+
+def select_workspace(shape: Shape, lay: RoundLayout) -> int:
+    s, l = shape.c(), lay.c()
+    return int(lib().tdx_select_workspace(ctypes.byref(s), ctypes.byref(l)))
+
+
+def select_important(shape: Shape, lay: RoundLayout, k_reuse: torch.Tensor, k_recomp: torch.Tensor,
+                     k: int, check_layer: int = 0, out: Optional[dict] = None, ws=None) -> dict:
+    """a2 + a3: returns dict(dev, score, agent_dev, selected, master) on the device."""
+    N, L, T, H, D = lay.n_agents, shape.n_layers, lay.n_tokens, shape.n_kv_heads, shape.head_dim
+    dev_ = lay.device
+    _need(k_reuse, "k_reuse", shape.dtype, (N, L, T, H, D), dev_)
+    _need(k_recomp, "k_recomp", shape.dtype, (N, T, H, D), dev_)
+    if out is None:
+        out = dict(
+            dev=torch.empty((N, T), dtype=torch.float32, device=dev_),
+            score=torch.empty((T,), dtype=torch.float32, device=dev_),
+            agent_dev=torch.empty((N,), dtype=torch.float32, device=dev_),
+            selected=torch.empty((max(int(k), 1),), dtype=torch.int32, device=dev_),
+            master=torch.empty((1,), dtype=torch.int32, device=dev_),
+        )
+    if ws is None:
+        ws = _ws(select_workspace(shape, lay), dev_)
+    s, l = shape.c(), lay.c()
+    _check(lib().tdx_select_important(
+        ctypes.byref(s), ctypes.byref(l), int(check_layer), _ptr(k_reuse), _ptr(k_recomp), int(k),
+        _ptr(out["dev"]), _ptr(out["score"]), _ptr(out["agent_dev"]), _ptr(out["selected"]),
+        _ptr(out["master"]), _ptr(ws), ws.numel(), _stream()), "tdx_select_important")
+    return out
+
+
+def encode_workspace(shape: Shape, lay: RoundLayout) -> int:
+    s, l = shape.c(), lay.c()
+    return int(lib().tdx_diff_encode_workspace(ctypes.byref(s), ctypes.byref(l)))
+
+
+class DiffSet:
+    """CSR diff record of every (agent, layer) row plus the dense Master."""
+
+    def __init__(self, off, idx, k, v, nnz, master_k, master_v, cap):
+        self.off, self.idx, self.k, self.v = off, idx, k, v
+        self.nnz_dev = nnz
+        self.master_k, self.master_v = master_k, master_v
+        self.cap = cap
+
+    def nnz(self) -> int:
+        return int(self.nnz_dev.item())
+
+
+def diff_encode(shape: Shape, lay: RoundLayout, master: torch.Tensor, agents_k: torch.Tensor,
+                agents_v: torch.Tensor, cap_blocks: Optional[int] = None, master_copy: bool = True,
+                check: bool = True, out: Optional[DiffSet] = None, ws=None) -> DiffSet:
+    """a4: Master-Mirror block-sparse encode.  With ``check`` the stream is
+    synchronised and an overflow of ``cap_blocks`` raises."""
+    N, L, T, H, D = lay.n_agents, shape.n_layers, lay.n_tokens, shape.n_kv_heads, shape.head_dim
+    dev_ = lay.device
+    _need(master, "master", torch.int32, (1,), dev_)
+    _need(agents_k, "agents_k", shape.dtype, (N, L, T, H, D), dev_)
+    _need(agents_v, "agents_v", shape.dtype, (N, L, T, H, D), dev_)
+    if out is None:
+        nb = T // DIFF_BLOCK
+        cap = (N - 1) * L * nb if cap_blocks is None else int(cap_blocks)
+        out = DiffSet(
+            torch.empty((N * L + 1,), dtype=torch.int32, device=dev_),
+            torch.empty((max(cap, 1),), dtype=torch.int32, device=dev_),
+            torch.empty((max(cap, 1), DIFF_BLOCK, H, D), dtype=shape.dtype, device=dev_),
+            torch.empty((max(cap, 1), DIFF_BLOCK, H, D), dtype=shape.dtype, device=dev_),
+            torch.empty((1,), dtype=torch.int64, device=dev_),
+            torch.empty((L, T, H, D), dtype=shape.dtype, device=dev_) if master_copy else None,
+            torch.empty((L, T, H, D), dtype=shape.dtype, device=dev_) if master_copy else None,
+            cap)
+    if ws is None:
+        ws = _ws(encode_workspace(shape, lay), dev_)
+    s, l = shape.c(), lay.c()
+    _check(lib().tdx_diff_encode(
+        ctypes.byref(s), ctypes.byref(l), _ptr(master), _ptr(agents_k), _ptr(agents_v), int(out.cap),
+        _ptr(out.off), _ptr(out.idx), _ptr(out.k), _ptr(out.v), _ptr(out.nnz_dev),
+        _ptr(out.master_k), _ptr(out.master_v), _ptr(ws), ws.numel(), _stream()), "tdx_diff_encode")
+    if check:
+        n = out.nnz()
+        if n < 0:
+            raise TdxError(TDX_EINVAL, "tdx_diff_encode", "the Master index is outside [0, N)")
+        if n > out.cap:
+            raise TdxError(TDX_EINVAL, "tdx_diff_encode", f"{n} diff blocks exceed capacity {out.cap}")
+    return out
+
+
+def restore_attn_workspace(shape: Shape, lay: RoundLayout, max_priv: int) -> int:
+    s, l = shape.c(), lay.c()
+    return int(lib().tdx_restore_attn_workspace(ctypes.byref(s), ctypes.byref(l), int(max_priv)))
+
+
+def restore_attn(shape: Shape, lay: RoundLayout, q: torch.Tensor, priv_off: torch.Tensor,
+                 priv_k: torch.Tensor, priv_v: torch.Tensor, max_priv: int,
+                 master_k: torch.Tensor, master_v: torch.Tensor, diff: DiffSet,
+                 scale: Optional[float] = None, out: Optional[torch.Tensor] = None, ws=None):
+    """a5: fused restore + decode attention -> [N][L][Hq][D]."""
+    N, L, T, H, Hq, D = (lay.n_agents, shape.n_layers, lay.n_tokens, shape.n_kv_heads,
+                         shape.n_q_heads, shape.head_dim)
+    dev_ = lay.device
+    _need(q, "q", shape.dtype, (N, L, Hq, D), dev_)
+    _need(priv_off, "priv_off", torch.int32, (N + 1,), dev_)
+    _need(priv_k, "priv_k", shape.dtype, None, dev_)
+    _need(priv_v, "priv_v", shape.dtype, tuple(priv_k.shape), dev_)
+    if priv_k.dim() != 4 or priv_k.shape[0] != L or tuple(priv_k.shape[2:]) != (H, D):
+        raise ValueError("priv_k must be [L][P_total][Hkv][D]")
+    _need(master_k, "master_k", shape.dtype, (L, T, H, D), dev_)
+    _need(master_v, "master_v", shape.dtype, (L, T, H, D), dev_)
+    if out is None:
+        out = torch.empty((N, L, Hq, D), dtype=shape.dtype, device=dev_)
+    _need(out, "out", shape.dtype, (N, L, Hq, D), dev_)
+    if ws is None:
+        ws = _ws(restore_attn_workspace(shape, lay, max_priv), dev_)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    s, l = shape.c(), lay.c()
+    _check(lib().tdx_restore_attn(
+        ctypes.byref(s), ctypes.byref(l), _ptr(q), _ptr(priv_off), _ptr(priv_k), _ptr(priv_v),
+        int(max_priv), _ptr(master_k), _ptr(master_v), _ptr(diff.off), _ptr(diff.idx),
+        _ptr(diff.k), _ptr(diff.v), scale, _ptr(out), _ptr(ws), ws.numel(), _stream()),
+        "tdx_restore_attn")
+    return out
+
+
+def restore_dense(shape: Shape, lay: RoundLayout, master_k: torch.Tensor, master_v: torch.Tensor,
+                  diff: DiffSet, k_dense: Optional[torch.Tensor] = None,
+                  v_dense: Optional[torch.Tensor] = None):
+    """a6 first half: every agent's dense cache, K rotated to its offsets."""
+    N, L, T, H, D = lay.n_agents, shape.n_layers, lay.n_tokens, shape.n_kv_heads, shape.head_dim
+    dev_ = lay.device
+    _need(master_k, "master_k", shape.dtype, (L, T, H, D), dev_)
+    _need(master_v, "master_v", shape.dtype, (L, T, H, D), dev_)
+    if k_dense is None:
+        k_dense = torch.empty((N, L, T, H, D), dtype=shape.dtype, device=dev_)
+    if v_dense is None:
+        v_dense = torch.empty((N, L, T, H, D), dtype=shape.dtype, device=dev_)
+    _need(k_dense, "k_dense", shape.dtype, (N, L, T, H, D), dev_)
+    _need(v_dense, "v_dense", shape.dtype, (N, L, T, H, D), dev_)
+    s, l = shape.c(), lay.c()
+    _check(lib().tdx_restore_dense(
+        ctypes.byref(s), ctypes.byref(l), _ptr(master_k), _ptr(master_v), _ptr(diff.off),
+        _ptr(diff.idx), _ptr(diff.k), _ptr(diff.v), _ptr(k_dense), _ptr(v_dense), _stream()),
+        "tdx_restore_dense")
+    return k_dense, v_dense
+
+
+def decode_attn_dense_workspace(shape: Shape, lay: RoundLayout, max_priv: int) -> int:
+    s, l = shape.c(), lay.c()
+    return int(lib().tdx_decode_attn_dense_workspace(ctypes.byref(s), ctypes.byref(l), int(max_priv)))
+
+
+def decode_attn_dense(shape: Shape, lay: RoundLayout, q: torch.Tensor, priv_off: torch.Tensor,
+                      priv_k: torch.Tensor, priv_v: torch.Tensor, max_priv: int,
+                      k_dense: torch.Tensor, v_dense: torch.Tensor, scale: Optional[float] = None,
+                      out: Optional[torch.Tensor] = None, ws=None):
+    """a6 second half: plain decode attention over [private; dense shared]."""
+    N, L, T, H, Hq, D = (lay.n_agents, shape.n_layers, lay.n_tokens, shape.n_kv_heads,
+                         shape.n_q_heads, shape.head_dim)
+    dev_ = lay.device
+    _need(q, "q", shape.dtype, (N, L, Hq, D), dev_)
+    _need(priv_off, "priv_off", torch.int32, (N + 1,), dev_)
+    _need(k_dense, "k_dense", shape.dtype, (N, L, T, H, D), dev_)
+    _need(v_dense, "v_dense", shape.dtype, (N, L, T, H, D), dev_)
+    if out is None:
+        out = torch.empty((N, L, Hq, D), dtype=shape.dtype, device=dev_)
+    _need(out, "out", shape.dtype, (N, L, Hq, D), dev_)
+    if ws is None:
+        ws = _ws(decode_attn_dense_workspace(shape, lay, max_priv), dev_)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    s, l = shape.c(), lay.c()
+    _check(lib().tdx_decode_attn_dense(
+        ctypes.byref(s), ctypes.byref(l), _ptr(q), _ptr(priv_off), _ptr(priv_k), _ptr(priv_v),
+        int(max_priv), _ptr(k_dense), _ptr(v_dense), scale, _ptr(out), _ptr(ws), ws.numel(),
+        _stream()), "tdx_decode_attn_dense")
+    return out

@@ -1,0 +1,216 @@
+/*
+ * tdx.h - C ABI of the collective KV-cache reuse kernels for AMD MI355X (gfx950).
+ *
+ * The operations follow the TokenDance pages' statement of the problem.  In
+ * one synchronous multi-agent round every agent i's prompt is its private
+ * history followed by the same shared output blocks in an agent-specific
+ * order (TokenDance deep-dive notes, Summary "Motivation", Figure 1), so one
+ * shared block sits at a different absolute offset in every prompt.  The
+ * library provides:
+ *
+ *   tdx_rerotate          one batched RoPE correction of the cached shared K
+ *                         to all N agents' offsets (notes, Summary "Method",
+ *                         Figure 7 path T3, Deep Analysis §0).
+ *   tdx_select_important  one check-layer key-difference pass over the group,
+ *                         one important-position set and the least-deviation
+ *                         Master (notes, Summary "Method", §3c A2/A3).
+ *   tdx_diff_encode       Master-Mirror block-sparse diff: per Mirror and
+ *                         layer, the indices and K/V values of the 16-token
+ *                         blocks that differ from the Master (notes, Figure 8,
+ *                         §2b; blog §4.3).
+ *   tdx_restore_attn      fused restore: diff blocks merged into Master tiles
+ *                         and RoPE recovered inside the decode-attention
+ *                         kernel, no dense Mirror written (notes §3d, §4
+ *                         "Fused Diff Restore"; blog §4.4).
+ *   tdx_restore_dense +   the dense comparator: materialise every agent's
+ *   tdx_decode_attn_dense cache, then attend (notes §3d, §7b).
+ *
+ * Conventions shared by every call
+ *  - Tensor arguments are DEVICE pointers to dense row-major arrays owned by
+ *    the caller; the library allocates and frees nothing and keeps no state
+ *    apart from a thread-local error string.  Scratch memory is passed as
+ *    (ws, ws_bytes), sized by the matching tdx_*_workspace() query.
+ *  - Element type of K, V, q and outputs is shape->dtype (fp32 or bf16 bit
+ *    patterns).  All tensor pointers must be 16-byte aligned.
+ *  - RoPE is the rotate-half form: dims (e, e + D/2) form a pair rotated by
+ *    angle p * theta^(-2e/D).  Cos/sin of each shift are evaluated in double
+ *    precision and applied in fp32.
+ *  - stream is a hipStream_t passed as void* (NULL = default stream).  Every
+ *    call only enqueues work; results are valid after the stream completes.
+ *  - All argument checks run before anything is enqueued: a call that
+ *    returns an error has had no effect.  Launch failures return TDX_EHIP.
+ *    tdx_last_error() gives the calling thread's last error message.
+ */
+#ifndef TDX_H
+#define TDX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TDX_VERSION 10000 /* 1.0.0 */
+#define TDX_DIFF_BLOCK 16 /* tokens per diff block (notes §3c A4: 16/32-token pages) */
+
+enum {
+  TDX_OK = 0,
+  TDX_EINVAL = -1,       /* bad argument: null/unaligned pointer, bad size or shape */
+  TDX_EUNSUPPORTED = -2, /* shape outside what the kernels are built for */
+  TDX_EHIP = -3,         /* a HIP runtime call or kernel launch failed */
+  TDX_EINTERNAL = -4,    /* unexpected internal failure */
+  TDX_EWORKSPACE = -5    /* ws is null or ws_bytes below the workspace query */
+};
+
+typedef enum { TDX_F32 = 0, TDX_BF16 = 1 } tdx_dtype;
+
+/* Model-side shape.  n_layers is the layer count of the K/V arrays passed to
+ * the call; head_dim is 64 or 128; n_q_heads is a multiple of n_kv_heads
+ * (query head hq reads KV head hq / (n_q_heads / n_kv_heads)). */
+typedef struct {
+  int32_t n_layers;
+  int32_t n_kv_heads;
+  int32_t n_q_heads;
+  int32_t head_dim;
+  int32_t dtype;     /* tdx_dtype */
+  double rope_theta; /* RoPE base theta > 1 */
+} tdx_shape;
+
+/* Round geometry.  Shared tokens are kept in canonical order: block b covers
+ * canonical tokens [blk_start[b], blk_start[b+1]).  src_pos[b] is the absolute
+ * position the cached K of block b was rotated at; dst_pos[i*B + b] is the
+ * absolute position of block b's first token in agent i's prompt.  Agent i
+ * needs its block b shifted by Delta(i,b) = dst_pos[i*B+b] - src_pos[b].
+ * The three arrays are DEVICE int32 arrays; n_tokens == blk_start[B]. */
+typedef struct {
+  int32_t n_agents; /* N >= 1 */
+  int32_t n_blocks; /* B >= 1 */
+  int32_t n_tokens; /* T >= 1 */
+  const int32_t *blk_start; /* [B+1], non-decreasing, blk_start[0] = 0 */
+  const int32_t *src_pos;   /* [B] */
+  const int32_t *dst_pos;   /* [N*B] */
+} tdx_layout;
+
+/* ---- a1: batched RoPE delta re-rotation ---------------------------------
+ * k_out[i][l][t][h][:] = round(R(Delta(i, b(t))) . k_cached[l][t][h][:]) for
+ * every agent i, layer l < n_layers, canonical token t, KV head h: one
+ * launch for the whole group (notes, Summary "Method"; Figure 7 T3).  V is
+ * never rotated.  A block with Delta = 0 is copied bit for bit.
+ *   k_cached  [L][T][Hkv][D]      read once
+ *   k_out     [N][L][T][Hkv][D]   written, tokens in canonical order
+ * Block lengths may be any non-negative integers.  Returns TDX_OK or an
+ * error; no workspace. */
+int tdx_rerotate(const tdx_shape *shape, const tdx_layout *layout,
+                 const void *k_cached, void *k_out, void *stream);
+
+/* ---- a2 + a3: check-layer key difference, one important set, Master -----
+ * At the check layer (notes, Summary "Method"; CacheBlend-style deviation):
+ *   dev[i][t]    = sum_h || k_recomp[i][t][h] - k_reuse[i][check][t][h] ||_2
+ *   score[t]     = sum_i dev[i][t]            (fp32, from double sums)
+ *   agent_dev[i] = sum_t dev[i][t]            (fp32, from double sums)
+ *   selected[0..k) = the k largest score[t], ties to the lower t, ascending
+ *   master[0]    = argmin_i agent_dev[i] (fp32 values), ties to the lower i
+ * The one set is reused by every later layer and never recomputed (notes
+ * §3c A3); the least-deviation agent keeps the full cache (§3c A2).
+ *   k_reuse   [N][L][T][Hkv][D]  re-rotated K (e.g. tdx_rerotate output);
+ *             the slice at layer check_layer is read
+ *   k_recomp  [N][T][Hkv][D]     recomputed K at the check layer
+ *   k         1 <= k <= T (tdx_topk_count gives ceil(pct * T / 100))
+ *   dev [N][T], score [T], agent_dev [N] (fp32); selected [k], master [1]
+ *   (int32) - all device, all written.
+ * Deterministic: every reduction runs in a fixed order. */
+int tdx_select_important(const tdx_shape *shape, const tdx_layout *layout,
+                         int32_t check_layer, const void *k_reuse,
+                         const void *k_recomp, int32_t k, float *dev,
+                         float *score, float *agent_dev, int32_t *selected,
+                         int32_t *master, void *ws, size_t ws_bytes,
+                         void *stream);
+size_t tdx_select_workspace(const tdx_shape *shape, const tdx_layout *layout);
+/* ceil(pct * n_tokens / 100) in integer arithmetic, clamped to [1, n_tokens];
+ * returns 0 when n_tokens < 1 or pct is outside [0, 100]. */
+int32_t tdx_topk_count(int32_t pct, int32_t n_tokens);
+
+/* ---- a4: Master-Mirror block-sparse diff encode ---------------------------
+ * For every agent i != *master and layer l, the 16-token blocks beta of its
+ * canonical-frame cache whose K or V differs from the Master's in any stored
+ * bit (all heads, all dims) are recorded as one CSR row r = i*L + l (notes,
+ * Figure 8: Diff = block-sparse (indices, values); §2b one record per Mirror
+ * per layer).  The values are the Mirror's own K/V (a replacement, so
+ * decoding is lossless).  The Master's rows are empty.
+ *   master      [1] device int32 (e.g. tdx_select_important output)
+ *   agents_k/v  [N][L][T][Hkv][D] canonical-frame caches; T % 16 == 0
+ *   cap_blocks  capacity of diff_idx / diff_k / diff_v in blocks (>= 0)
+ *   diff_off    [N*L+1] int32, row offsets (always written in full)
+ *   diff_idx    [cap] int32, ascending block indices within each row
+ *   diff_k/v    [cap][16][Hkv][D]
+ *   nnz         [1] int64: the true total; when it exceeds cap_blocks the
+ *               entries at positions >= cap_blocks are not written, which the
+ *               caller detects by reading nnz (a device-side condition).
+ *               nnz = -1 (and every row empty) when *master is not in [0, N).
+ *   master_k_out/master_v_out  [L][T][Hkv][D] dense copy of the Master, or
+ *               NULL to skip. */
+int tdx_diff_encode(const tdx_shape *shape, const tdx_layout *layout,
+                    const int32_t *master, const void *agents_k,
+                    const void *agents_v, int64_t cap_blocks, int32_t *diff_off,
+                    int32_t *diff_idx, void *diff_k, void *diff_v,
+                    int64_t *nnz, void *master_k_out, void *master_v_out,
+                    void *ws, size_t ws_bytes, void *stream);
+size_t tdx_diff_encode_workspace(const tdx_shape *shape, const tdx_layout *layout);
+
+/* ---- a5: fused restore + decode attention --------------------------------
+ * out[i][l][hq] = sum_j softmax_j(scale * q[i][l][hq] . key_j) val_j over
+ * agent i's private keys followed by its shared keys, where the shared key of
+ * canonical token t is R(Delta(i, b(t))) applied to K~_i[l][t], and K~_i / V~_i
+ * are the Master patched with agent i's diff rows.  The patch and the RoPE
+ * recovery happen tile by tile inside the attention kernel; no dense Mirror
+ * is written (notes §3d "dense materialization zero times", §4; blog §4.4).
+ *   q          [N][L][Hq][D]
+ *   priv_off   [N+1] device int32 offsets into the private arrays
+ *   priv_k/v   [L][P_total][Hkv][D], agent i owns rows priv_off[i]..priv_off[i+1]
+ *   max_priv   host scalar >= max_i (priv_off[i+1] - priv_off[i])
+ *   master_k/v [L][T][Hkv][D]; T % 16 == 0
+ *   diff_off / diff_idx / diff_k / diff_v  as written by tdx_diff_encode
+ *   scale      softmax scale (> 0), usually 1/sqrt(D)
+ *   out        [N][L][Hq][D] */
+int tdx_restore_attn(const tdx_shape *shape, const tdx_layout *layout,
+                     const void *q, const int32_t *priv_off,
+                     const void *priv_k, const void *priv_v, int32_t max_priv,
+                     const void *master_k, const void *master_v,
+                     const int32_t *diff_off, const int32_t *diff_idx,
+                     const void *diff_k, const void *diff_v, float scale,
+                     void *out, void *ws, size_t ws_bytes, void *stream);
+size_t tdx_restore_attn_workspace(const tdx_shape *shape, const tdx_layout *layout,
+                                  int32_t max_priv);
+
+/* ---- a6: dense comparator --------------------------------------------------
+ * tdx_restore_dense writes every agent's full cache:
+ *   k_dense[i][l][t] = round(R(Delta(i, b(t))) K~_i[l][t]), v_dense[i][l][t] = V~_i[l][t]
+ * ([N][L][T][Hkv][D] each; inputs as for tdx_restore_attn).
+ * tdx_decode_attn_dense then runs plain decode attention of agent i over its
+ * private keys followed by k_dense[i] / v_dense[i] (outputs as tdx_restore_attn).
+ * Together they are the dense restore-then-attend path the fused restore is
+ * measured against (notes §3d, §7b). */
+int tdx_restore_dense(const tdx_shape *shape, const tdx_layout *layout,
+                      const void *master_k, const void *master_v,
+                      const int32_t *diff_off, const int32_t *diff_idx,
+                      const void *diff_k, const void *diff_v, void *k_dense,
+                      void *v_dense, void *stream);
+int tdx_decode_attn_dense(const tdx_shape *shape, const tdx_layout *layout,
+                          const void *q, const int32_t *priv_off,
+                          const void *priv_k, const void *priv_v,
+                          int32_t max_priv, const void *k_dense,
+                          const void *v_dense, float scale, void *out,
+                          void *ws, size_t ws_bytes, void *stream);
+size_t tdx_decode_attn_dense_workspace(const tdx_shape *shape, const tdx_layout *layout,
+                                       int32_t max_priv);
+
+/* ---- utilities -------------------------------------------------------------*/
+const char *tdx_strerror(int code); /* static text for a return code */
+const char *tdx_last_error(void);   /* detail of the calling thread's last error */
+int tdx_version(void);              /* TDX_VERSION */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TDX_H */

@@ -156,6 +156,18 @@ def rerotate(kc: np.ndarray, blk_start, src_pos, dst_pos, theta: float) -> np.nd
     return np.stack(out)
 
 
+def rerotate_tokens(rows: np.ndarray, tokens, agent: int, blk_start, src_pos, dst_pos,
+                    theta: float) -> np.ndarray:
+    """The same definition evaluated for chosen canonical tokens only.
+
+    rows: [n][Hkv][D] stored cached-K rows of ``tokens`` (any layer); returns
+    agent ``agent``'s re-rotated rows in the storage format.
+    """
+    delta = shift(src_pos, dst_pos)[agent]
+    p = delta[block_of_token(blk_start)[np.asarray(tokens, dtype=np.int64)]]
+    return narrow(rope_rotate(widen(rows), p[:, None], theta), rows.dtype)
+
+
 # ---------------------------------------------------------------------------
 # a2: check-layer key difference (notes, Summary "Method"; Figure 7)
 # ---------------------------------------------------------------------------

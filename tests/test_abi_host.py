@@ -1,0 +1,150 @@
+"""C-ABI host checks (no GPU): the library loads, exports every declared
+symbol, and rejects bad arguments before anything reaches the HIP runtime."""
+
+import ctypes
+import math
+import os
+import re
+from fractions import Fraction
+
+import pytest
+
+from collective_kv_cache_amd import tdx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tdx.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(tdx.LIB_PATH), reason="libtdx.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tdx_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(tdx.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported():
+    l = ctypes.CDLL(tdx.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(l, name), name
+
+
+def test_version_and_strerror():
+    assert tdx.version() == 10000
+    assert tdx.strerror(0) == "success"
+    assert tdx.strerror(-1) == "invalid argument"
+    assert tdx.strerror(-5).startswith("workspace")
+    assert tdx.strerror(123) == "unknown error code"
+
+
+def test_topk_count_is_integer_ceiling():
+    for T in (1, 2, 7, 100, 192, 3744, 5536, 20000):
+        for pct in (0, 1, 15, 50, 99, 100):
+            want = min(max(math.ceil(Fraction(pct * T, 100)), 1), T)
+            assert tdx.topk_count(pct, T) == want
+    assert tdx.topk_count(15, 0) == 0 and tdx.topk_count(-1, 10) == 0 and tdx.topk_count(101, 10) == 0
+
+
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: calls fail validation first
+
+
+def _shape(**kw):
+    d = dict(n_layers=2, n_kv_heads=4, n_q_heads=28, head_dim=128, dtype=tdx.TDX_BF16, rope_theta=1e6)
+    d.update(kw)
+    return tdx.CShape(**d)
+
+
+def _layout(**kw):
+    d = dict(n_agents=3, n_blocks=2, n_tokens=64, blk_start=0x20000, src_pos=0x30000, dst_pos=0x40000)
+    d.update(kw)
+    return tdx.CLayout(**d)
+
+
+def _rerotate(shape, lay, kc=FAKE, out=FAKE):
+    return tdx.lib().tdx_rerotate(ctypes.byref(shape) if shape is not None else None,
+                                  ctypes.byref(lay) if lay is not None else None, kc, out, None)
+
+
+@pytest.mark.parametrize("shape_kw,lay_kw,code", [
+    (dict(dtype=7), {}, tdx.TDX_EINVAL),
+    (dict(head_dim=96), {}, tdx.TDX_EUNSUPPORTED),
+    (dict(n_q_heads=30), {}, tdx.TDX_EINVAL),
+    (dict(n_layers=0), {}, tdx.TDX_EINVAL),
+    (dict(rope_theta=1.0), {}, tdx.TDX_EINVAL),
+    (dict(n_kv_heads=32, n_q_heads=32), {}, tdx.TDX_EUNSUPPORTED),
+    ({}, dict(n_agents=0), tdx.TDX_EINVAL),
+    ({}, dict(n_tokens=0), tdx.TDX_EINVAL),
+    ({}, dict(n_agents=2000), tdx.TDX_EUNSUPPORTED),
+    ({}, dict(blk_start=0), tdx.TDX_EINVAL),
+    ({}, dict(dst_pos=0x40002), tdx.TDX_EINVAL),
+])
+def test_rerotate_rejects_bad_arguments(shape_kw, lay_kw, code):
+    assert _rerotate(_shape(**shape_kw), _layout(**lay_kw)) == code
+    assert tdx.lib().tdx_last_error().decode() != ""
+
+
+def test_rerotate_rejects_null_and_unaligned_tensors():
+    assert _rerotate(None, _layout()) == tdx.TDX_EINVAL
+    assert _rerotate(_shape(), None) == tdx.TDX_EINVAL
+    assert _rerotate(_shape(), _layout(), kc=None) == tdx.TDX_EINVAL
+    assert _rerotate(_shape(), _layout(), out=ctypes.c_void_p(0x10008)) == tdx.TDX_EINVAL
+    assert "k_out" in tdx.lib().tdx_last_error().decode()
+
+
+def _select(k=5, check_layer=0, ws_bytes=1 << 20, ws=FAKE):
+    s, l = _shape(), _layout()
+    return tdx.lib().tdx_select_important(ctypes.byref(s), ctypes.byref(l), check_layer, FAKE, FAKE, k,
+                                          FAKE, FAKE, FAKE, FAKE, FAKE, ws, ws_bytes, None)
+
+
+def test_select_rejects_bad_arguments():
+    assert _select(k=0) == tdx.TDX_EINVAL
+    assert _select(k=65) == tdx.TDX_EINVAL
+    assert _select(check_layer=2) == tdx.TDX_EINVAL
+    assert _select(ws_bytes=0) == tdx.TDX_EWORKSPACE
+    assert _select(ws=None) == tdx.TDX_EWORKSPACE
+
+
+def test_workspace_queries_are_positive_and_grow():
+    s, l = _shape(), _layout()
+    a = tdx.lib().tdx_select_workspace(ctypes.byref(s), ctypes.byref(l))
+    b = tdx.lib().tdx_diff_encode_workspace(ctypes.byref(s), ctypes.byref(l))
+    c = tdx.lib().tdx_restore_attn_workspace(ctypes.byref(s), ctypes.byref(l), 100)
+    assert a > 0 and b > 0 and c > 0
+    l2 = _layout(n_agents=30)
+    assert tdx.lib().tdx_diff_encode_workspace(ctypes.byref(s), ctypes.byref(l2)) > b
+    bad = _shape(head_dim=96)
+    assert tdx.lib().tdx_select_workspace(ctypes.byref(bad), ctypes.byref(l)) == 0
+
+
+def _encode(T=64, cap=10, nnz=FAKE, mk=FAKE, mv=FAKE, ws_bytes=1 << 30):
+    s, l = _shape(), _layout(n_tokens=T)
+    return tdx.lib().tdx_diff_encode(ctypes.byref(s), ctypes.byref(l), FAKE, FAKE, FAKE, cap, FAKE, FAKE,
+                                     FAKE, FAKE, nnz, mk, mv, FAKE, ws_bytes, None)
+
+
+def test_encode_rejects_bad_arguments():
+    assert _encode(T=60) == tdx.TDX_EINVAL           # not a multiple of 16
+    assert _encode(cap=-1) == tdx.TDX_EINVAL
+    assert _encode(nnz=ctypes.c_void_p(0x10004)) == tdx.TDX_EINVAL
+    assert _encode(mv=None) == tdx.TDX_EINVAL        # one Master output without the other
+    assert _encode(ws_bytes=0) == tdx.TDX_EWORKSPACE
+
+
+def _restore(T=64, scale=0.1, max_priv=10, ws_bytes=1 << 30, hq=28):
+    s, l = _shape(n_q_heads=hq), _layout(n_tokens=T)
+    return tdx.lib().tdx_restore_attn(ctypes.byref(s), ctypes.byref(l), FAKE, FAKE, FAKE, FAKE, max_priv,
+                                      FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(scale), FAKE,
+                                      FAKE, ws_bytes, None)
+
+
+def test_restore_rejects_bad_arguments():
+    assert _restore(T=40) == tdx.TDX_EINVAL
+    assert _restore(scale=0.0) == tdx.TDX_EINVAL
+    assert _restore(max_priv=-1) == tdx.TDX_EINVAL
+    assert _restore(ws_bytes=0) == tdx.TDX_EWORKSPACE
+    assert _restore(hq=4 * 17) == tdx.TDX_EUNSUPPORTED  # 17 query heads per KV head

@@ -1,0 +1,113 @@
+"""a2 + a3 parity: tdx_select_important against the oracle (GPU).
+
+Stage-wise on identical inputs: both sides read the same reused K (an
+independent N(0,1) draw) and the same synthetic recomputed K.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from collective_kv_cache_amd import tdx
+from workload import CONFIGS, make_layout, reuse_stand_in, recomputed_k, to_numpy_bits
+
+from gpu_common import (DEV, assert_master, assert_scores, assert_selection, dlayout, host,
+                        shape_of)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(cfg, lay, kr, kx, k, shape=None, kr5=None, check_layer=0):
+    """kr: [N][T][Hkv][D] reused K at the check layer (host); kr5 optionally the
+    full [N][L][T][Hkv][D] array the GPU reads from."""
+    shape = shape_of(cfg, 1) if shape is None else shape
+    kr_dev = (kr.unsqueeze(1) if kr5 is None else kr5).to(DEV).contiguous()
+    out = tdx.select_important(shape, dlayout(lay), kr_dev, kx.to(DEV), k, check_layer=check_layer)
+    torch.cuda.synchronize()
+    d, s, a = O.deviation(to_numpy_bits(kr), to_numpy_bits(kx))
+    s32, a32 = s.astype(np.float32), a.astype(np.float32)
+    assert_scores(host(out["dev"]), d.astype(np.float32), "dev")
+    assert_scores(host(out["score"]), s32, "score")
+    assert_scores(host(out["agent_dev"]), a32, "agent_dev")
+    sel = host(out["selected"])
+    assert_selection(sel, s32, k)
+    m = int(host(out["master"])[0])
+    assert_master(m, a32)
+    return sel, m, O.select_important(s32, k), O.choose_master(a32)
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen7b_check", "qwen7b_round", "qwen14b_round", "qwen7b_scaleout"])
+def test_select_matches_oracle(name):
+    cfg = CONFIGS[name]
+    lay = make_layout(cfg)
+    kr = reuse_stand_in(cfg, lay)
+    kx = recomputed_k(cfg, lay, kr)
+    k = O.topk_count(cfg.pct, lay.n_tokens)
+    assert k == tdx.topk_count(cfg.pct, lay.n_tokens)
+    sel, m, sel_ref, m_ref = _check(cfg, lay, kr, kx, k)
+    # no ties inside the band on these inputs: the sets agree exactly
+    assert sel.tolist() == sel_ref.tolist()
+    assert m == m_ref
+
+
+def test_select_all_ties_takes_lowest_tokens():
+    cfg = CONFIGS["qwen7b_check"]
+    lay = make_layout(cfg)
+    kr = reuse_stand_in(cfg, lay)
+    k = 37
+    sel, m, _, _ = _check(cfg, lay, kr, kr.clone(), k)
+    assert sel.tolist() == list(range(k))  # every score is 0: ties to the lower t
+    assert m == 0
+
+
+@pytest.mark.parametrize("k_mode", ["one", "all"])
+def test_select_extreme_k(k_mode):
+    cfg = CONFIGS["tiny"]
+    lay = make_layout(cfg)
+    kr = reuse_stand_in(cfg, lay)
+    kx = recomputed_k(cfg, lay, kr)
+    k = 1 if k_mode == "one" else lay.n_tokens
+    sel, _, sel_ref, _ = _check(cfg, lay, kr, kx, k)
+    assert sel.tolist() == sel_ref.tolist()
+
+
+def test_select_single_agent_and_planted_master():
+    cfg = CONFIGS["qwen7b_check"].scaled(n_agents=1)
+    lay = make_layout(cfg)
+    kr = reuse_stand_in(cfg, lay)
+    kx = recomputed_k(cfg, lay, kr)
+    _check(cfg, lay, kr, kx, 100)
+    # planted Master: every agent noisy on the same tokens, agent 6 at half sigma
+    cfg = CONFIGS["qwen7b_check"]
+    lay = make_layout(cfg)
+    kr = reuse_stand_in(cfg, lay)
+    tok = [np.arange(0, lay.n_tokens, 7)] * cfg.n_agents
+    sig = [0.1] * cfg.n_agents
+    sig[6] = 0.05
+    kx = recomputed_k(cfg, lay, kr, tokens=tok, sigmas=sig)
+    _, m, _, m_ref = _check(cfg, lay, kr, kx, 50)
+    assert m == 6 and m_ref == 6
+
+
+def test_select_reads_the_check_layer_of_a_multilayer_reuse_tensor():
+    cfg = CONFIGS["tiny"].scaled(n_layers=3)
+    lay = make_layout(cfg)
+    kr = reuse_stand_in(cfg, lay)
+    kx = recomputed_k(cfg, lay, kr)
+    kr5 = torch.randn((cfg.n_agents, 3, lay.n_tokens, cfg.n_kv_heads, cfg.head_dim))
+    kr5[:, 2] = kr
+    _check(cfg, lay, kr, kx, 29, shape=shape_of(cfg, 3), kr5=kr5, check_layer=2)
+
+
+def test_select_deterministic():
+    cfg = CONFIGS["qwen7b_scaleout"]
+    lay = make_layout(cfg)
+    kr = reuse_stand_in(cfg, lay, device=DEV).unsqueeze(1).contiguous()
+    kx = recomputed_k(cfg, lay, kr[:, 0])
+    k = tdx.topk_count(15, lay.n_tokens)
+    a = tdx.select_important(shape_of(cfg, 1), dlayout(lay), kr, kx, k)
+    b = tdx.select_important(shape_of(cfg, 1), dlayout(lay), kr, kx, k)
+    torch.cuda.synchronize()
+    for key in a:
+        assert torch.equal(a[key].view(torch.int32), b[key].view(torch.int32)), key

@@ -159,6 +159,18 @@ def test_rerotate_brute_force_loops_bf16():
                     assert out[i, 0, t, h, e + 4] == O.f64_to_bf16(np.array([z.imag]))[0]
 
 
+def test_rerotate_tokens_is_the_same_definition():
+    rng = np.random.default_rng(17)
+    bs, src, dst = _layout([16, 48, 32], [0, 16, 64], [[7, 900, 40], [0, 16, 64], [123, 5, 3000]])
+    kc = O.f64_to_bf16(rng.standard_normal((2, 96, 2, 16)))
+    full = O.rerotate(kc, bs, src, dst, 1e4)
+    toks = np.array([0, 15, 16, 63, 64, 95])
+    for i in range(3):
+        for l in range(2):
+            np.testing.assert_array_equal(O.rerotate_tokens(kc[l, toks], toks, i, bs, src, dst, 1e4),
+                                          full[i, l, toks])
+
+
 @pytest.mark.parametrize("dt", [np.uint16, np.float32])
 def test_rerotate_zero_shift_is_bitwise_copy(dt):
     rng = np.random.default_rng(6)

@@ -21,4 +21,5 @@ from .synth import (  # noqa: F401
     mirror_blocks,
     agent_caches,
     to_numpy_bits,
+    from_numpy_bits,
 )

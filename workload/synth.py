@@ -360,3 +360,13 @@ def to_numpy_bits(x: torch.Tensor) -> np.ndarray:
     if x.dtype == torch.float32:
         return x.numpy()
     raise TypeError(x.dtype)
+
+
+def from_numpy_bits(a: np.ndarray) -> torch.Tensor:
+    """Inverse of ``to_numpy_bits``: uint16 bit patterns -> bf16, float32 as is."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    if a.dtype == np.float32:
+        return torch.from_numpy(a)
+    raise TypeError(a.dtype)
