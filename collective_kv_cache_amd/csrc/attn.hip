@@ -6,22 +6,32 @@
 // dense comparator (restore every agent's cache, then attend) is what the
 // fused path is measured against (notes §3d, §7b).
 //
-// Split-K decode attention, one workgroup per (agent i, key split, layer l,
-// KV head h), 4 waves.  Agent i's keys are its private history followed by
-// the shared tokens; they are walked in 16-token tiles (a shared tile is
-// exactly one 16-token diff block).  Per tile a wave:
-//   * loads the K rows straight into MFMA A-operand registers: for a shared
-//     tile in the fused path each lane takes its token's row from the diff
-//     record when the block is in agent i's diff row, else from the Master;
-//   * stages V in wave-private LDS;
-//   * computes S^T = K Q'^T with v_mfma_f32_16x16x32_bf16, where Q' is the
-//     GQA query group of KV head h.  RoPE is recovered on the query side:
-//     q . R(Delta) k = (R(-Delta) q) . k, so a shared tile of block b uses
-//     Q' = R(-Delta(i,b)) q (cos/sin from a double-precision table), and one
-//     Master tile layout serves every agent;
-//   * runs an online softmax per query row (rows live in lanes) and
-//     accumulates O^T += V^T P^T with v_mfma_f32_16x16x16_bf16.
-// The four waves combine in LDS; a merge kernel combines the splits.
+// Fused path = two kernels writing split-K partials, then one merge:
+//
+//  shared_kernel  one workgroup per (agent group, shared split, layer, KV
+//                 head).  Each 16-token Master tile (= one diff block) is
+//                 staged ONCE in LDS (ping-pong buffers: the next tile's
+//                 loads are in flight while this one is used) and serves the
+//                 query rows of every agent of the group: the agents' GQA
+//                 query groups are stacked into 16-row MFMA tiles, two per
+//                 wave.  RoPE is recovered on the query side,
+//                 q . R(Delta) k = (R(-Delta) q) . k, with Q' = R(-Delta(i,b))
+//                 per row from a double-precision cos/sin table, so one
+//                 canonical Master tile serves all agents.  Rows of an agent
+//                 whose diff record holds the tile are masked here.
+//  agent_kernel   one workgroup per (agent, split, layer, KV head): the
+//                 agent's private history followed by its own diff blocks
+//                 (the "patch": K/V straight from the diff record, Q' rotated
+//                 by the block's Delta).  4 waves stride over 16-token tiles;
+//                 the next tile's loads are issued before the current tile is
+//                 used; V goes through wave-private LDS.
+//  merge_kernel   combines the partials of every (agent, layer, query head).
+//
+// Per tile: S^T = K Q'^T with v_mfma_f32_16x16x32_bf16 (K rows in the A
+// operand, query rows in B, so each lane ends up holding 4 logits of ONE
+// query row), online softmax with rows in lanes, O^T += V^T P^T with
+// v_mfma_f32_16x16x16_bf16.  The dense comparator's attention is agent_kernel
+// reading the materialised caches instead of diff records.
 // Operands are bf16 (fp32 K/V/q are rounded to bf16 for the MFMA); softmax,
 // accumulation and the merge run in fp32.
 #include "common.h"
@@ -35,14 +45,16 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kTile = 16;
-constexpr int kTilesPerSplit = 64;  // 16 per wave
+constexpr int kTilesPerSplit = 64;  // agent_kernel: 16 tiles per wave
+constexpr int kShThreads = 256;     // shared_kernel: 4 waves, one 16-row tile each
+constexpr int kShWaves = kShThreads / kWave;
+constexpr int kRowsPerGroup = 16 * kShWaves;
+constexpr int kMaxSharedTiles = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
 enum Mode { FUSED = 0, DENSE = 1 };
 
 // ---- bf16 operand helpers ---------------------------------------------------
-
-__device__ __forceinline__ uint32_t bf16_bits(float f) { return f32_to_bf16(f); }
 
 // 8 consecutive elements -> 8 floats
 template <typename E>
@@ -57,7 +69,7 @@ __device__ __forceinline__ void load8<float>(const float* p, float* x) {
   Fmt<float>::unpack(ld16(p + 4), x + 4);
 }
 
-// 8 consecutive elements as packed bf16 (4 dwords), no float round trip for bf16
+// 8 consecutive elements as packed bf16 (4 dwords); bf16 input is passed through
 template <typename E>
 __device__ __forceinline__ u32x4 load8_bf16(const E* p);
 template <>
@@ -88,9 +100,24 @@ __device__ __forceinline__ f32x4 mfma16(const i16x4& a, const i16x4& b, f32x4 c)
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
+// Order this wave's LDS writes before its later LDS reads of other lanes'
+// data.  A wave's LDS operations execute in order, so only compiler ordering
+// is needed; the fence is restricted to LDS so that outstanding global loads
+// (the next tile's prefetch) are not waited for.
 __device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// Largest b in [0, B) with blk[b] <= t (the block holding token t; skips
+// empty blocks).  blk is an LDS copy of blk_start.
+__device__ __forceinline__ int block_of(const int32_t* blk, int B, int t) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (blk[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
 }
 
 // ---- RoPE table: tab[(i*B + b)*HALF + e] = (cos, sin)(Delta(i,b) * theta^(-2e/D))
@@ -113,91 +140,335 @@ __global__ __launch_bounds__(256) void rope_table_kernel(const int32_t* __restri
   }
 }
 
-// ---- split attention ----------------------------------------------------------
+// ---- rotated queries: qrot[((i*L + l)*B + b)*Hq + hq][D] = bf16(R(-Delta(i,b)) q[i][l][hq])
+// RoPE recovery on the query side: q . R(Delta) k = (R(-Delta) q) . k, so the
+// canonical Master/diff key rows can be used as they are stored.  One thread
+// per (agent, layer, block, query head, 8 lower-half dims).
+
+template <typename E, int D>
+__global__ __launch_bounds__(256) void qrot_kernel(const E* __restrict__ q, const float2* __restrict__ tab,
+                                                   int N, int L, int B, int Hq,
+                                                   uint16_t* __restrict__ qrot) {
+  constexpr int HALF = D / 2;
+  constexpr int C = HALF / 8;  // 8-dim chunks of the lower half
+  const size_t n = (size_t)N * L * B * Hq * C;
+  for (size_t x = blockIdx.x * (size_t)blockDim.x + threadIdx.x; x < n;
+       x += (size_t)gridDim.x * blockDim.x) {
+    const int c = (int)(x % C);
+    size_t r = x / C;
+    const int hq = (int)(r % Hq);
+    r /= Hq;
+    const int b = (int)(r % B);
+    r /= B;
+    const int l = (int)(r % L);
+    const int i = (int)(r / L);
+    const E* qr = q + (((size_t)i * L + l) * Hq + hq) * D;
+    float lo[8], hi[8], olo[8], ohi[8];
+    load8<E>(qr + 8 * c, lo);
+    load8<E>(qr + HALF + 8 * c, hi);
+    const float2* cs = tab + ((size_t)i * B + b) * HALF + 8 * c;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      // R(-phi): (x, y) -> (x cos + y sin, y cos - x sin)
+      olo[j] = lo[j] * cs[j].x + hi[j] * cs[j].y;
+      ohi[j] = hi[j] * cs[j].x - lo[j] * cs[j].y;
+    }
+    uint16_t* o = qrot + ((((size_t)i * L + l) * B + b) * Hq + hq) * D;
+    st16(o + 8 * c, Fmt<uint16_t>::pack(olo));
+    st16(o + HALF + 8 * c, Fmt<uint16_t>::pack(ohi));
+  }
+}
+
+// ---- shared state ----------------------------------------------------------------
 
 struct AttnArgs {
-  const void* q;          // [N][L][Hq][D]
-  const int32_t* priv_off;
-  const void* pk;         // [L][Ptot][Hkv][D]
+  const void* q;             // [N][L][Hq][D]
+  const int32_t* priv_off;   // [N+1]
+  const void* pk;            // [L][Ptot][Hkv][D]
   const void* pv;
-  const void* sk;         // fused: master [L][T][Hkv][D]; dense: k_dense [N][L][T][Hkv][D]
+  const void* sk;            // fused: Master [L][T][Hkv][D]; dense: [N][L][T][Hkv][D]
   const void* sv;
-  const int32_t* diff_off;  // fused only
+  const int32_t* diff_off;   // fused: [N*L+1]
   const int32_t* diff_idx;
-  const void* dk;         // [nnz][16][Hkv][D]
+  const void* dk;            // [nnz][16][Hkv][D]
   const void* dv;
-  const int32_t* blk_start;  // fused only
-  const float2* tab;         // fused only [N][B][D/2]
-  float* part;               // [N][L][Hq][S][D+4]
-  int N, L, T, B, Hkv, Hq, S;
+  const int32_t* blk_start;  // [B+1]
+  const float2* tab;         // fused: [N][B][D/2] cos/sin of each shift
+  uint16_t* qrot;            // fused: [N][L][B][Hq][D] bf16 rotated queries
+  float* part;               // [N][L][Hq][S][D+4]: m, l, -, -, O[D]
+  int N, L, T, B, Hkv, Hq;
+  int SP;                    // agent-kernel record slots
+  int SG;                    // shared-kernel record slots (after SP)
+  int S;                     // SP + SG
+  int AGS, NAG, TPG;         // shared kernel: agents per group, groups, tiles per split
+  int n_sh_wg;               // shared kernel: real workgroups (grid is padded to 8)
   float scale_log2;
 };
 
 template <int D>
-struct WaveState {
+struct RowState {
   static constexpr int DT = D / 16;
-  f32x4 o[DT];  // O^T tile dt: dims dt*16 + 4q + j, row = lane % 16
-  float m;      // running max (log2 domain), row-uniform
+  f32x4 o[DT];  // O^T tile dt: dims dt*16 + 4*q4 + j of row lane%16
+  float m;      // running max (log2 domain), uniform over the row's 4 lanes
   float l;      // lane-partial running sum
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m = -INFINITY;
+    l = 0.f;
+  }
 };
 
-// Online-softmax update and PV for one tile.  z: 4 logits (log2 domain) of
-// the lane's row at tokens 4q..4q+3 (-inf when masked).  vt: wave-private
-// V tile in LDS, [16][D + 8] bf16.
+// Gather the PV A operand of one tile from row-major LDS V [16][VS]:
+// va[dt][j] = V[token 4*q4 + j][dim 16*dt + c16].
 template <int D>
-__device__ __forceinline__ void softmax_pv(WaveState<D>& st, float z[4], const uint16_t* vt,
-                                           int lane) {
+__device__ __forceinline__ void gather_v(const uint16_t* vt, int VS, int q4, int c16, i16x4* va) {
   constexpr int DT = D / 16;
-  constexpr int VS = D + 8;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) va[dt][j] = (short)vt[(4 * q4 + j) * VS + dt * 16 + c16];
+}
+
+// Online softmax + PV for one tile.  z: the 4 logits (log2 domain) of the
+// lane's row at tokens 4*q4 .. 4*q4+3 (-inf = masked).  While a row has no
+// valid key, mnew = -inf: 0 is used as the reference so every exp2 is of -inf
+// (-> 0) and nothing turns into NaN; the path stays wave-uniform around the
+// MFMAs.
+template <int D>
+__device__ __forceinline__ void softmax_pv(RowState<D>& st, const float z[4], const i16x4* va) {
+  constexpr int DT = D / 16;
   float tmax = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
   tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
   const float mnew = fmaxf(st.m, tmax);
-  // while a row has seen no valid key, mnew = -inf: use 0 as the reference so
-  // that every exp2 below is of -inf (-> 0) and nothing turns into NaN; the
-  // path stays uniform across the wave around the MFMAs
   const float mref = (mnew == -INFINITY) ? 0.0f : mnew;
-  const float alpha = exp2f(st.m - mref);  // st.m = -inf -> 0
+  const float alpha = exp2f(st.m - mref);
   st.m = mnew;
   i16x4 pb;
   float psum = 0.0f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float p = exp2f(z[j] - mref);  // masked -> 0
-    const uint32_t b = bf16_bits(p);
+    const uint32_t b = f32_to_bf16(exp2f(z[j] - mref));
     pb[j] = (short)b;
-    psum += __uint_as_float(b << 16);
+    psum += __uint_as_float(b << 16);  // the sum uses the same rounded weights
   }
   st.l = st.l * alpha + psum;
-  const int q = lane / 16, c = lane % 16;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
     st.o[dt] *= alpha;
-    i16x4 va;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) va[j] = (short)vt[(4 * q + j) * VS + dt * 16 + c];
-    st.o[dt] = mfma16(va, pb, st.o[dt]);
+    st.o[dt] = mfma16(va[dt], pb, st.o[dt]);
   }
 }
 
-template <typename E, int D, int MODE>
-__global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a) {
-  constexpr int KD = D / 32;       // 32-dim k-steps of the QK MFMA
+// Write a row's partial record (m, l, O unnormalised).
+template <int D>
+__device__ __forceinline__ void write_record(float* rec, const RowState<D>& st, float lsum, int q4,
+                                             int c16) {
+  constexpr int DT = D / 16;
+  if (q4 == 0) {
+    rec[0] = st.m;
+    rec[1] = lsum;
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    *reinterpret_cast<f32x4*>(rec + 4 + dt * 16 + 4 * q4) = st.o[dt];
+}
+
+// ---- shared_kernel: Master tiles staged once, all agents' query rows ------------
+
+template <typename E, int D>
+__global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(3))) void shared_kernel(AttnArgs a) {
+  constexpr int KD = D / 32;
   constexpr int DT = D / 16;
   constexpr int HALF = D / 2;
-  constexpr int VS = D + 8;        // padded LDS row stride (bf16)
+  constexpr int VS = D + 8;  // padded LDS row stride (bf16)
+  constexpr int CH = D / 8;  // 8-element chunks per row
+  constexpr int NCH = 2 * kTile * CH;  // staged chunks per tile (K then V)
+  constexpr int CPT = (NCH + kShThreads - 1) / kShThreads;
   extern __shared__ __align__(16) unsigned char smem[];
-  // layout: [kWaves][16][VS] bf16 V tiles | combine area aliases it afterwards | blk_start
-  uint16_t* vtile_all = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* kbuf = reinterpret_cast<uint16_t*>(smem);  // [2][16][VS]
+  uint16_t* vbuf = kbuf + 2 * kTile * VS;              // [2][16][VS]
+  int32_t* sblk = reinterpret_cast<int32_t*>(vbuf + 2 * kTile * VS);  // [B+1]
+  uint8_t* dflag = reinterpret_cast<uint8_t*>(sblk + a.B + 1);        // [AGS][TPG]
+
+  // Hardware deals workgroups round-robin to the 8 XCDs; give each XCD a
+  // contiguous run of logical ids so that the agent groups sharing a Master
+  // tile run on the same XCD (one L2) at the same time.
+  const int nwg = gridDim.x;  // a multiple of 8
+  const int w = blockIdx.x;
+  const int logical = (w % 8) * (nwg / 8) + w / 8;
+  if (logical >= a.n_sh_wg) return;
+  const int ag = logical % a.NAG;
+  const int rest = logical / a.NAG;
+  const int gs = rest % a.SG;
+  const int lh = rest / a.SG;
+  const int l = lh / a.Hkv, h = lh % a.Hkv;
+  const int g = a.Hq / a.Hkv;
+  const int a0 = ag * a.AGS;
+  const int na = min(a.AGS, a.N - a0);
+  const int nrows = na * g;
+  const int nb = a.T / kTile;
+  const int b0 = gs * a.TPG;
+  const int b1 = min(b0 + a.TPG, nb);
+  if (b0 >= b1) return;  // uniform
+  const int ntl = b1 - b0;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform per wave
+  const int q4 = lane / 16, c16 = lane % 16;
+
+  for (int x = tid; x <= a.B; x += kShThreads) sblk[x] = a.blk_start[x];
+  for (int x = tid; x < a.AGS * a.TPG; x += kShThreads) dflag[x] = 0;
+  __syncthreads();
+  // flag (agent, tile) pairs whose block is in the agent's diff row: those
+  // rows take the tile from the agent's own record (agent_kernel)
+  for (int al = wave; al < na; al += kShWaves) {
+    const int r = (a0 + al) * a.L + l;
+    const int e1 = a.diff_off[r + 1];
+    for (int e = a.diff_off[r] + lane; e < e1; e += kWave) {
+      const int beta = a.diff_idx[e];
+      if (beta >= b0 && beta < b1) dflag[al * a.TPG + (beta - b0)] = 1;
+    }
+  }
+
+  // this wave's 16 query rows (row = agent-major, then the GQA group)
+  const bool has_rows = wave * 16 < nrows;  // wave-uniform
+  const int row = wave * 16 + c16;
+  const bool valid = row < nrows;
+  const int agent = a0 + (valid ? row / g : 0);
+  const int hq = h * g + (valid ? row % g : 0);
+  u32x4 qr[KD];  // rotated query operand for block bq
+#pragma unroll
+  for (int k = 0; k < KD; ++k) qr[k] = u32x4{0, 0, 0, 0};
+  int bq = -1;
+  RowState<D> st;
+  st.init();
+
+  const size_t rowHD = (size_t)a.Hkv * D;
+  const E* mk = static_cast<const E*>(a.sk) + (size_t)l * a.T * rowHD + (size_t)h * D;
+  const E* mv = static_cast<const E*>(a.sv) + (size_t)l * a.T * rowHD + (size_t)h * D;
+  auto stage_load = [&](int beta, u32x4* r) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * kShThreads;
+      if (idx < NCH) {
+        const int tensor = idx / (kTile * CH);
+        const int rem = idx % (kTile * CH);
+        const E* src = (tensor ? mv : mk) + (size_t)(beta * kTile + rem / CH) * rowHD + (rem % CH) * 8;
+        r[c] = load8_bf16<E>(src);
+      }
+    }
+  };
+  auto stage_store = [&](int buf, const u32x4* r) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * kShThreads;
+      if (idx < NCH) {
+        const int tensor = idx / (kTile * CH);
+        const int rem = idx % (kTile * CH);
+        uint16_t* dst = (tensor ? vbuf : kbuf) + (buf * kTile + rem / CH) * VS + (rem % CH) * 8;
+        *reinterpret_cast<u32x4*>(dst) = r[c];
+      }
+    }
+  };
+  auto compute = [&](int buf, int n) {
+    if (!has_rows) return;  // wave-uniform
+    const int beta = b0 + n;
+    const uint16_t* kt = kbuf + buf * kTile * VS;
+    const uint16_t* vt = vbuf + buf * kTile * VS;
+    u32x4 kop[KD];
+#pragma unroll
+    for (int k = 0; k < KD; ++k) kop[k] = *reinterpret_cast<const u32x4*>(kt + c16 * VS + 32 * k + 8 * q4);
+    const int t0 = beta * kTile;
+    float z[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    for (int b = block_of(sblk, a.B, t0); b < a.B && sblk[b] < t0 + kTile; ++b) {
+      if (sblk[b + 1] <= t0) continue;  // empty block
+      if (b != bq) {
+        const uint16_t* qs = a.qrot + ((((size_t)agent * a.L + l) * a.B + b) * a.Hq + hq) * D;
+#pragma unroll
+        for (int k = 0; k < KD; ++k) qr[k] = valid ? ld16(qs + 32 * k + 8 * q4) : u32x4{0, 0, 0, 0};
+        bq = b;
+      }
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KD; ++k) acc = mfma32(kop[k], qr[k], acc);
+      const int bs = sblk[b], be = sblk[b + 1];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tt = t0 + 4 * q4 + j;
+        if (tt >= bs && tt < be) z[j] = acc[j] * a.scale_log2;
+      }
+    }
+    if (!valid || dflag[(agent - a0) * a.TPG + n]) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) z[j] = -INFINITY;
+    }
+    i16x4 va[DT];
+    gather_v<D>(vt, VS, q4, c16, va);
+    softmax_pv<D>(st, z, va);
+  };
+
+  // Two register sets keep the Master tile n+2 in flight while tile n is
+  // used and tile n+1 (loaded one step earlier) goes into the other LDS buffer.
+  // Loads past the last tile re-read the last tile (unconditional issue keeps
+  // the compiler's wait counting on one path).
+  u32x4 sA[CPT], sB[CPT];
+  stage_load(b0, sA);
+  stage_store(0, sA);
+  stage_load(b0 + min(1, ntl - 1), sB);
+  __syncthreads();  // tile 0 staged, diff flags complete
+  for (int n = 0;;) {
+    stage_load(b0 + min(n + 2, ntl - 1), sA);
+    compute(0, n);
+    if (++n >= ntl) break;
+    stage_store(1, sB);
+    __syncthreads();
+    stage_load(b0 + min(n + 2, ntl - 1), sB);
+    compute(1, n);
+    if (++n >= ntl) break;
+    stage_store(0, sA);
+    __syncthreads();
+  }
+
+  if (has_rows) {
+    float lsum = st.l;
+    lsum += __shfl_xor(lsum, 16, kWave);
+    lsum += __shfl_xor(lsum, 32, kWave);
+    if (valid) {
+      float* dst = a.part + ((((size_t)agent * a.L + l) * a.Hq + hq) * a.S + a.SP + gs) * (D + 4);
+      write_record<D>(dst, st, lsum, q4, c16);
+    }
+  }
+}
+
+// ---- agent_kernel: private history + own diff blocks (or dense shared) ---------
+
+template <typename E, int D>
+struct TileIn {
+  u32x4 k[D / 32];
+  u32x4 v[D / 32];
+  u32x4 q[D / 32];  // diff tiles: query rotated for the tile's first shared block
+};
+
+template <typename E, int D, int MODE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void agent_kernel(AttnArgs a) {
+  constexpr int KD = D / 32;
+  constexpr int DT = D / 16;
+  constexpr int HALF = D / 2;
+  constexpr int VS = D + 8;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* vtile_all = reinterpret_cast<uint16_t*>(smem);  // [kWaves][16][VS]
   const size_t vbytes = (size_t)kWaves * kTile * VS * 2;
-  const size_t cbytes = (size_t)kWaves * 16 * (D + 4) * 4;
-  int32_t* sblk = reinterpret_cast<int32_t*>(smem + (vbytes > cbytes ? vbytes : cbytes));
+  const size_t cbytes = (size_t)kWaves * 16 * (D + 2) * 4;
+  int2* tinfo = reinterpret_cast<int2*>(smem + (vbytes > cbytes ? vbytes : cbytes));  // [64]
+  int32_t* sblk = reinterpret_cast<int32_t*>(tinfo + kTilesPerSplit);                 // [B+1]
 
   const int i = blockIdx.x;
   const int s = blockIdx.y;
   const int l = blockIdx.z / a.Hkv;
   const int h = blockIdx.z % a.Hkv;
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform per wave
   const int q4 = lane / 16, c16 = lane % 16;
   const int g = a.Hq / a.Hkv;
 
@@ -205,176 +476,160 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a) {
   const int p0 = a.priv_off[i];
   const int P = a.priv_off[i + 1] - p0;
   const int ntp = (P + kTile - 1) / kTile;
-  const int nts = a.T / kTile;
-  const int ntiles = ntp + nts;
+  int e0 = 0, nx;
+  if (MODE == FUSED) {
+    const int r = i * a.L + l;
+    e0 = a.diff_off[r];
+    nx = a.diff_off[r + 1] - e0;
+  } else {
+    nx = a.T / kTile;
+  }
+  const int ntiles = ntp + nx;
   const int tbeg = s * kTilesPerSplit;
-  if (tbeg >= ntiles) return;  // uniform: this agent has fewer splits
+  if (tbeg >= ntiles) return;  // uniform: this agent needs fewer splits
   const int tend = min(tbeg + kTilesPerSplit, ntiles);
 
   if (MODE == FUSED) {
     for (int b = tid; b <= a.B; b += kThreads) sblk[b] = a.blk_start[b];
   }
-
-  const E* qrow = static_cast<const E*>(a.q) + (((size_t)i * a.L + l) * a.Hq + (size_t)h * g) * D;
-  // query operand: row c16 (valid when < g), dims 8*q4 + 32k .. +7
-  float qf[KD][8];
-  u32x4 qb[KD], qr[KD];
+  // rows >= g of the 16-row query tile repeat row g-1; their results are never used
+  const int qrow_i = min(c16, g - 1);
+  const E* qrow = static_cast<const E*>(a.q) + (((size_t)i * a.L + l) * a.Hq + (size_t)h * g + qrow_i) * D;
+  u32x4 qplain[KD];  // the query as given, for private (and dense) tiles
 #pragma unroll
-  for (int k = 0; k < KD; ++k) {
-    if (c16 < g) {
-      load8<E>(qrow + (size_t)c16 * D + 32 * k + 8 * q4, qf[k]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) qf[k][j] = 0.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) qb[k][j] = pack_bf16(qf[k][2 * j], qf[k][2 * j + 1]);
-    qr[k] = qb[k];
-  }
+  for (int k = 0; k < KD; ++k) qplain[k] = load8_bf16<E>(qrow + 32 * k + 8 * q4);
   __syncthreads();  // sblk ready
+  if (MODE == FUSED) {
+    // per diff tile of this split: (diff block beta, first shared block), so
+    // that issuing a tile's loads needs no dependent global read
+    for (int u = tbeg + tid; u < tend; u += kThreads) {
+      if (u >= ntp) {
+        const int beta = a.diff_idx[e0 + u - ntp];
+        tinfo[u - tbeg] = make_int2(beta, block_of(sblk, a.B, beta * kTile));
+      }
+    }
+    __syncthreads();
+  }
 
-  WaveState<D> st;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  st.m = -INFINITY;
-  st.l = 0.0f;
-
+  RowState<D> st;
+  st.init();
   uint16_t* vt = vtile_all + (size_t)wave * kTile * VS;
   const size_t rowHD = (size_t)a.Hkv * D;
   const E* pk = static_cast<const E*>(a.pk) + ((size_t)l * ptot + p0) * rowHD + (size_t)h * D;
   const E* pv = static_cast<const E*>(a.pv) + ((size_t)l * ptot + p0) * rowHD + (size_t)h * D;
 
-  // fused: cursor into agent i's diff row at layer l
-  int dcur = 0, dend = 0;
-  int bcur = -1;  // block whose rotation qr holds
-  if (MODE == FUSED) {
-    const int r = i * a.L + l;
-    dcur = a.diff_off[r];
-    dend = a.diff_off[r + 1];
-    // first entry >= the first shared diff block this wave can visit
-    int first = tbeg + wave - ntp;
-    if (first < 0) first = 0;
-    int lo = dcur, hi = dend;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (a.diff_idx[mid] < first) lo = mid + 1; else hi = mid;
+  // Loads of one tile into registers.  Every address is valid: rows past the
+  // end of the private history re-read its last row and are masked out of
+  // the softmax (weight 0 times a finite value), so no lane branches around a
+  // load and nothing consumes the loads before the tile is processed.
+  auto issue = [&](int u, TileIn<E, D>& t) {
+    const E* kr;
+    const E* vr;
+    if (u < ntp) {
+      const int p = min(u * kTile + c16, P - 1);
+      kr = pk + (size_t)p * rowHD;
+      vr = pv + (size_t)p * rowHD;
+#pragma unroll
+      for (int k = 0; k < KD; ++k) t.q[k] = qplain[k];  // defined on every path (no stale copies)
+    } else if (MODE == FUSED) {
+      const size_t o = ((size_t)(e0 + u - ntp) * kTile + c16) * rowHD + (size_t)h * D;
+      kr = static_cast<const E*>(a.dk) + o;
+      vr = static_cast<const E*>(a.dv) + o;
+      // the rotated query of the tile's first shared block travels with the
+      // tile, so processing the tile issues no global loads of its own
+      const int b = tinfo[u - tbeg].y;
+      const uint16_t* qs = a.qrot + ((((size_t)i * a.L + l) * a.B + b) * a.Hq + (size_t)h * g + qrow_i) * D;
+#pragma unroll
+      for (int k = 0; k < KD; ++k) t.q[k] = ld16(qs + 32 * k + 8 * q4);
+    } else {
+      const size_t o = (((size_t)i * a.L + l) * a.T + (size_t)(u - ntp) * kTile + c16) * rowHD +
+                       (size_t)h * D;
+      kr = static_cast<const E*>(a.sk) + o;
+      vr = static_cast<const E*>(a.sv) + o;
+#pragma unroll
+      for (int k = 0; k < KD; ++k) t.q[k] = qplain[k];
     }
-    dcur = lo;
-  }
+#pragma unroll
+    for (int k = 0; k < KD; ++k) {
+      t.k[k] = load8_bf16<E>(kr + 32 * k + 8 * q4);
+      t.v[k] = load8_bf16<E>(vr + 32 * k + 8 * q4);
+    }
+  };
 
-  for (int tile = tbeg + wave; tile < tend; tile += kWaves) {
-    u32x4 kop[KD];
-    const E* vsrc;
+  // each wave walks a contiguous run of tiles (consecutive diff blocks tend
+  // to share a shared block, so the rotated query is reused)
+  const int span = (tend - tbeg + kWaves - 1) / kWaves;
+  const int ubeg = tbeg + wave * span;
+  const int uend = min(ubeg + span, tend);
+  auto process = [&](const TileIn<E, D>& cur, int u) {
+#pragma unroll
+    for (int k = 0; k < KD; ++k) *reinterpret_cast<u32x4*>(vt + c16 * VS + 32 * k + 8 * q4) = cur.v[k];
     float z[4];
-    if (tile < ntp) {
-      // ---- private tile
-      const int p = tile * kTile + c16;
-      const bool ok = p < P;
-      const E* krow = pk + (size_t)(ok ? p : 0) * rowHD;
-      vsrc = pv + (size_t)(ok ? p : 0) * rowHD;
-#pragma unroll
-      for (int k = 0; k < KD; ++k) kop[k] = ok ? load8_bf16<E>(krow + 32 * k + 8 * q4) : u32x4{0, 0, 0, 0};
-      // V -> LDS
-#pragma unroll
-      for (int k = 0; k < KD; ++k) {
-        const u32x4 v = ok ? load8_bf16<E>(vsrc + 32 * k + 8 * q4) : u32x4{0, 0, 0, 0};
-        *reinterpret_cast<u32x4*>(vt + c16 * VS + 32 * k + 8 * q4) = v;
-      }
+    if (u < ntp || MODE == DENSE) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < KD; ++k) acc = mfma32(kop[k], qb[k], acc);
+      for (int k = 0; k < KD; ++k) acc = mfma32(cur.k[k], qplain[k], acc);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        z[j] = (tile * kTile + 4 * q4 + j < P) ? acc[j] * a.scale_log2 : -INFINITY;
+        z[j] = (u >= ntp || u * kTile + 4 * q4 + j < P) ? acc[j] * a.scale_log2 : -INFINITY;
     } else {
-      // ---- shared tile = diff block beta
-      const int beta = tile - ntp;
-      const int t = beta * kTile + c16;
-      const E* krow;
-      const E* vrow;
-      if (MODE == FUSED) {
-        while (dcur < dend && a.diff_idx[dcur] < beta) ++dcur;
-        const bool hit = dcur < dend && a.diff_idx[dcur] == beta;
-        if (hit) {
-          const size_t o = ((size_t)dcur * kTile + c16) * rowHD + (size_t)h * D;
-          krow = static_cast<const E*>(a.dk) + o;
-          vrow = static_cast<const E*>(a.dv) + o;
-        } else {
-          const size_t o = ((size_t)l * a.T + t) * rowHD + (size_t)h * D;
-          krow = static_cast<const E*>(a.sk) + o;
-          vrow = static_cast<const E*>(a.sv) + o;
+      // the agent's own block: RoPE recovered through Q' = R(-Delta(i,b)) q
+      const int2 ti = tinfo[u - tbeg];
+      const int t0 = ti.x * kTile;
+      const int bfirst = ti.y;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) z[j] = -INFINITY;
+      for (int b = bfirst; b < a.B && sblk[b] < t0 + kTile; ++b) {
+        if (sblk[b + 1] <= t0) continue;  // empty block
+        u32x4 qr[KD];
+        if (b == bfirst) {
+#pragma unroll
+          for (int k = 0; k < KD; ++k) qr[k] = cur.q[k];
+        } else {  // a tile straddling shared blocks (block starts not 16-aligned)
+          const uint16_t* qs = a.qrot + ((((size_t)i * a.L + l) * a.B + b) * a.Hq + (size_t)h * g + qrow_i) * D;
+#pragma unroll
+          for (int k = 0; k < KD; ++k) qr[k] = ld16(qs + 32 * k + 8 * q4);
         }
-      } else {
-        const size_t o = (((size_t)i * a.L + l) * a.T + t) * rowHD + (size_t)h * D;
-        krow = static_cast<const E*>(a.sk) + o;
-        vrow = static_cast<const E*>(a.sv) + o;
-      }
-#pragma unroll
-      for (int k = 0; k < KD; ++k) kop[k] = load8_bf16<E>(krow + 32 * k + 8 * q4);
-#pragma unroll
-      for (int k = 0; k < KD; ++k)
-        *reinterpret_cast<u32x4*>(vt + c16 * VS + 32 * k + 8 * q4) = load8_bf16<E>(vrow + 32 * k + 8 * q4);
-      if (MODE == DENSE) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < KD; ++k) acc = mfma32(kop[k], qb[k], acc);
+        for (int k = 0; k < KD; ++k) acc = mfma32(cur.k[k], qr[k], acc);
+        const int bs = sblk[b], be = sblk[b + 1];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) z[j] = acc[j] * a.scale_log2;
-      } else {
-        // blocks covering tokens [16 beta, 16 beta + 16): usually one
-        const int t0 = beta * kTile;
-        int lo = 0, hi = a.B - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (sblk[mid] <= t0) lo = mid; else hi = mid - 1;
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) z[j] = -INFINITY;
-        for (int b = lo; b < a.B && sblk[b] < t0 + kTile; ++b) {
-          if (sblk[b + 1] <= t0) continue;  // empty block
-          if (b != bcur) {
-            // Q' = R(-Delta(i,b)) q on the lane's pairs (k, k + KD/2)
-            const float2* tb = a.tab + ((size_t)i * a.B + b) * HALF;
-#pragma unroll
-            for (int k = 0; k < KD / 2; ++k) {
-              float lo_o[8], hi_o[8];
-#pragma unroll
-              for (int j = 0; j < 8; ++j) {
-                const float2 cs = tb[32 * k + 8 * q4 + j];
-                const float x = qf[k][j], y = qf[k + KD / 2][j];
-                lo_o[j] = x * cs.x + y * cs.y;
-                hi_o[j] = y * cs.x - x * cs.y;
-              }
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                qr[k][j] = pack_bf16(lo_o[2 * j], lo_o[2 * j + 1]);
-                qr[k + KD / 2][j] = pack_bf16(hi_o[2 * j], hi_o[2 * j + 1]);
-              }
-            }
-            bcur = b;
-          }
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int k = 0; k < KD; ++k) acc = mfma32(kop[k], qr[k], acc);
-          const int bs = sblk[b], be = sblk[b + 1];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int tt = t0 + 4 * q4 + j;
-            if (tt >= bs && tt < be) z[j] = acc[j] * a.scale_log2;
-          }
+        for (int j = 0; j < 4; ++j) {
+          const int tt = t0 + 4 * q4 + j;
+          if (tt >= bs && tt < be) z[j] = acc[j] * a.scale_log2;
         }
       }
     }
     wave_sync();  // V tile visible to the whole wave
-    softmax_pv<D>(st, z, vt, lane);
-    wave_sync();  // done reading before the next tile overwrites it
+    i16x4 va[DT];
+    gather_v<D>(vt, VS, q4, c16, va);
+    softmax_pv<D>(st, z, va);
+    wave_sync();  // reads done before the next tile overwrites the V tile
+  };
+
+  // Two fixed register sets: the next tile's loads are in flight while the
+  // current one is used.  The next loads are issued unconditionally (the last
+  // step re-reads its own tile) so that the compiler's wait counting sees one
+  // path and waits only for the older set.
+  if (ubeg < uend) {
+    TileIn<E, D> ta, tb;
+    issue(ubeg, ta);
+    for (int u = ubeg;;) {
+      issue(min(u + 1, uend - 1), tb);
+      process(ta, u);
+      if (++u >= uend) break;
+      issue(min(u + 1, uend - 1), ta);
+      process(tb, u);
+      if (++u >= uend) break;
+    }
   }
 
   // ---- combine the four waves (LDS aliases the V tiles)
   __syncthreads();
-  float* cm = reinterpret_cast<float*>(smem);   // [kWaves][16] max
-  float* cl = cm + kWaves * 16;                  // [kWaves][16] sum
-  float* co = cl + kWaves * 16;                  // [kWaves][16][D]
+  float* cm = reinterpret_cast<float*>(smem);  // [kWaves][16] max
+  float* cl = cm + kWaves * 16;                 // [kWaves][16] sum
+  float* co = cl + kWaves * 16;                 // [kWaves][16][D]
   float lsum = st.l;
   lsum += __shfl_xor(lsum, 16, kWave);
   lsum += __shfl_xor(lsum, 32, kWave);
@@ -384,8 +639,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a) {
   }
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) co[((size_t)wave * 16 + c16) * D + dt * 16 + 4 * q4 + j] = st.o[dt][j];
+    *reinterpret_cast<f32x4*>(co + ((size_t)wave * 16 + c16) * D + dt * 16 + 4 * q4) = st.o[dt];
   __syncthreads();
   const size_t rec = D + 4;
   for (int x = tid; x < g * D; x += kThreads) {
@@ -409,26 +663,31 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a) {
   }
 }
 
-// One wave per output row (agent, layer, query head): combine the splits.
-template <typename E, int D>
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part,
-                                                   const int32_t* __restrict__ priv_off, int N,
-                                                   int L, int Hq, int T, int S, E* __restrict__ out) {
+// One wave per output row (agent, layer, query head): combine the agent
+// kernel's splits [0, nsp) and the shared kernel's splits [SP, SP + SG).
+template <typename E, int D, int MODE>
+__global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, E* __restrict__ out) {
   const int lane = threadIdx.x % kWave;
   const size_t row = (size_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-  if (row >= (size_t)N * L * Hq) return;
-  const int i = (int)(row / ((size_t)L * Hq));
-  const int P = priv_off[i + 1] - priv_off[i];
-  const int ntiles = (P + kTile - 1) / kTile + T / kTile;
-  const int ns = min((ntiles + kTilesPerSplit - 1) / kTilesPerSplit, S);  // S bounds the record
+  if (row >= (size_t)a.N * a.L * a.Hq) return;
+  const int i = (int)(row / ((size_t)a.L * a.Hq));
+  const int l = (int)((row / a.Hq) % a.L);
+  const int P = a.priv_off[i + 1] - a.priv_off[i];
+  const int nx = (MODE == FUSED) ? a.diff_off[i * a.L + l + 1] - a.diff_off[i * a.L + l] : a.T / kTile;
+  const int nt = (P + kTile - 1) / kTile + nx;
+  const int nsp = min((nt + kTilesPerSplit - 1) / kTilesPerSplit, a.SP);
   const size_t rec = D + 4;
-  const float* pr = part + row * S * rec;
+  const float* pr = a.part + row * a.S * rec;
   float mm = -INFINITY;
-  for (int s = 0; s < ns; ++s) mm = fmaxf(mm, pr[s * rec]);
+  for (int s = 0; s < a.S; ++s) {
+    if (s >= nsp && s < a.SP) continue;
+    mm = fmaxf(mm, pr[s * rec]);
+  }
   constexpr int PER = D / kWave;
   float o[PER] = {};
   float ls = 0.f;
-  for (int s = 0; s < ns; ++s) {
+  for (int s = 0; s < a.S; ++s) {
+    if (s >= nsp && s < a.SP) continue;
     const float ms = pr[s * rec];
     const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - mm);
     ls += f * pr[s * rec + 1];
@@ -534,54 +793,90 @@ __global__ __launch_bounds__(kThreads) void restore_dense_kernel(
 
 // ---- host-side planning ------------------------------------------------------------
 
-int max_splits(const Dims& d, int max_priv) {
-  const int nt = (max_priv + kTile - 1) / kTile + d.T / kTile;
-  return (nt + kTilesPerSplit - 1) / kTilesPerSplit;
-}
-
-struct AttnWs {
-  size_t part, tab, total;
+struct Plan {
+  int SP, SG, AGS, NAG, TPG, n_sh_wg;
+  size_t part_bytes, tab_off, qrot_off, total;
 };
 
-AttnWs attn_ws(const Dims& d, int max_priv, bool fused) {
+Plan make_plan(const Dims& d, int max_priv, bool fused) {
+  Plan p{};
+  const int nb = d.T / kTile;
+  p.SP = ((max_priv + kTile - 1) / kTile + nb + kTilesPerSplit - 1) / kTilesPerSplit;
+  if (p.SP < 1) p.SP = 1;
+  if (fused) {
+    const int g = d.Hq / d.Hkv;
+    p.AGS = kRowsPerGroup / g;
+    if (p.AGS > d.N) p.AGS = d.N;
+    if (p.AGS < 1) p.AGS = 1;
+    p.NAG = (d.N + p.AGS - 1) / p.AGS;
+    const long base = (long)p.NAG * d.L * d.Hkv;
+    long sg = (2048 + base - 1) / base;  // aim at ~2048 workgroups
+    if (sg < 1) sg = 1;
+    if (sg > nb) sg = nb;
+    p.TPG = (int)((nb + sg - 1) / sg);
+    if (p.TPG > kMaxSharedTiles) p.TPG = kMaxSharedTiles;
+    p.SG = (nb + p.TPG - 1) / p.TPG;
+    p.n_sh_wg = p.NAG * p.SG * d.L * d.Hkv;
+  }
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  AttnWs w;
-  w.part = 0;
-  const size_t nrec = (size_t)d.N * d.L * d.Hq * max_splits(d, max_priv);
-  w.tab = up(nrec * (d.D + 4) * 4);
-  w.total = w.tab + (fused ? up((size_t)d.N * d.B * (d.D / 2) * 8) : 0);
-  return w;
+  p.part_bytes = (size_t)d.N * d.L * d.Hq * (p.SP + p.SG) * (d.D + 4) * 4;
+  p.tab_off = up(p.part_bytes);
+  p.qrot_off = p.tab_off + (fused ? up((size_t)d.N * d.B * (d.D / 2) * 8) : 0);
+  p.total = p.qrot_off + (fused ? up((size_t)d.N * d.L * d.B * d.Hq * d.D * 2) : 0);
+  return p;
 }
 
-size_t attn_lds_bytes(int D, int B, bool fused) {
+size_t agent_lds(int D, int B, bool fused) {
   const size_t vbytes = (size_t)kWaves * kTile * (D + 8) * 2;
-  const size_t cbytes = (size_t)kWaves * 16 * (D + 4) * 4 + 2 * kWaves * 16 * 4;
-  return (vbytes > cbytes ? vbytes : cbytes) + (fused ? (size_t)(B + 1) * 4 : 0);
+  const size_t cbytes = (size_t)kWaves * 16 * (D + 2) * 4;
+  return (vbytes > cbytes ? vbytes : cbytes) + (size_t)kTilesPerSplit * 8 + (fused ? (size_t)(B + 1) * 4 : 0);
+}
+
+size_t shared_lds(int D, int B, const Plan& p) {
+  return (size_t)4 * kTile * (D + 8) * 2 + (size_t)(B + 1) * 4 + (size_t)p.AGS * p.TPG;
 }
 
 template <typename E, int D, int MODE>
-hipError_t launch_attn_t(const Dims& d, AttnArgs a, int max_priv, E* out, hipStream_t s) {
-  a.S = max_splits(d, max_priv);
-  const size_t lds = attn_lds_bytes(D, d.B, MODE == FUSED);
-  if (lds > 160 * 1024) return hipErrorInvalidValue;
-  dim3 grid(d.N, a.S, d.L * d.Hkv);
-  hipLaunchKernelGGL((attn_split_kernel<E, D, MODE>), grid, dim3(kThreads), lds, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+hipError_t launch_attn_t(const Dims& d, AttnArgs a, const Plan& p, E* out, hipStream_t s) {
+  a.SP = p.SP;
+  a.SG = p.SG;
+  a.S = p.SP + p.SG;
+  a.AGS = p.AGS;
+  a.NAG = p.NAG;
+  a.TPG = p.TPG;
+  a.n_sh_wg = p.n_sh_wg;
+  hipError_t e;
+  if (MODE == FUSED) {
+    const size_t nq = (size_t)d.N * d.L * d.B * d.Hq * (D / 16);
+    const int qblocks = (int)((nq + 255) / 256 < 8192 ? (nq + 255) / 256 : 8192);
+    hipLaunchKernelGGL((qrot_kernel<E, D>), dim3(qblocks), dim3(256), 0, s,
+                       static_cast<const E*>(a.q), a.tab, d.N, d.L, d.B, d.Hq, a.qrot);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const size_t lds = shared_lds(D, d.B, p);
+    if (lds > 64 * 1024) return hipErrorInvalidValue;
+    const int grid = (p.n_sh_wg + 7) / 8 * 8;
+    hipLaunchKernelGGL((shared_kernel<E, D>), dim3(grid), dim3(kShThreads), lds, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const size_t lds = agent_lds(D, d.B, MODE == FUSED);
+  if (lds > 64 * 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((agent_kernel<E, D, MODE>), dim3(d.N, p.SP, d.L * d.Hkv), dim3(kThreads), lds,
+                     s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t rows = (size_t)d.N * d.L * d.Hq;
   const int rpb = 256 / kWave;
-  hipLaunchKernelGGL((merge_kernel<E, D>), dim3((rows + rpb - 1) / rpb), dim3(256), 0, s, a.part,
-                     a.priv_off, d.N, d.L, d.Hq, d.T, a.S, out);
+  hipLaunchKernelGGL((merge_kernel<E, D, MODE>), dim3((rows + rpb - 1) / rpb), dim3(256), 0, s, a,
+                     out);
   return hipGetLastError();
 }
 
 template <int MODE>
-hipError_t dispatch_attn(const Dims& d, AttnArgs a, int max_priv, void* out, hipStream_t s) {
+hipError_t dispatch_attn(const Dims& d, AttnArgs a, const Plan& p, void* out, hipStream_t s) {
   if (d.dtype == TDX_BF16)
-    return d.D == 128 ? launch_attn_t<uint16_t, 128, MODE>(d, a, max_priv, static_cast<uint16_t*>(out), s)
-                      : launch_attn_t<uint16_t, 64, MODE>(d, a, max_priv, static_cast<uint16_t*>(out), s);
-  return d.D == 128 ? launch_attn_t<float, 128, MODE>(d, a, max_priv, static_cast<float*>(out), s)
-                    : launch_attn_t<float, 64, MODE>(d, a, max_priv, static_cast<float*>(out), s);
+    return d.D == 128 ? launch_attn_t<uint16_t, 128, MODE>(d, a, p, static_cast<uint16_t*>(out), s)
+                      : launch_attn_t<uint16_t, 64, MODE>(d, a, p, static_cast<uint16_t*>(out), s);
+  return d.D == 128 ? launch_attn_t<float, 128, MODE>(d, a, p, static_cast<float*>(out), s)
+                    : launch_attn_t<float, 64, MODE>(d, a, p, static_cast<float*>(out), s);
 }
 
 AttnArgs common_args(const Dims& d, const void* q, const int32_t* priv_off, const void* pk,
@@ -604,15 +899,15 @@ AttnArgs common_args(const Dims& d, const void* q, const int32_t* priv_off, cons
 
 }  // namespace
 
-size_t restore_attn_ws_bytes(const Dims& d, int max_priv) { return attn_ws(d, max_priv, true).total; }
-size_t dense_attn_ws_bytes(const Dims& d, int max_priv) { return attn_ws(d, max_priv, false).total; }
+size_t restore_attn_ws_bytes(const Dims& d, int max_priv) { return make_plan(d, max_priv, true).total; }
+size_t dense_attn_ws_bytes(const Dims& d, int max_priv) { return make_plan(d, max_priv, false).total; }
 
 hipError_t launch_restore_attn(const Dims& d, const tdx_layout& lay, const void* q,
                                const int32_t* priv_off, const void* pk, const void* pv,
                                int max_priv, const void* mk, const void* mv,
                                const int32_t* diff_off, const int32_t* diff_idx, const void* dk,
                                const void* dv, float scale, void* out, void* ws, hipStream_t s) {
-  const AttnWs w = attn_ws(d, max_priv, true);
+  const Plan p = make_plan(d, max_priv, true);
   AttnArgs a = common_args(d, q, priv_off, pk, pv, scale, ws);
   a.sk = mk;
   a.sv = mv;
@@ -621,15 +916,16 @@ hipError_t launch_restore_attn(const Dims& d, const tdx_layout& lay, const void*
   a.dk = dk;
   a.dv = dv;
   a.blk_start = lay.blk_start;
-  float2* tab = reinterpret_cast<float2*>(static_cast<unsigned char*>(ws) + w.tab);
+  float2* tab = reinterpret_cast<float2*>(static_cast<unsigned char*>(ws) + p.tab_off);
   a.tab = tab;
+  a.qrot = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(ws) + p.qrot_off);
   const size_t n = (size_t)d.N * d.B * (d.D / 2);
   const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
   hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(256), 0, s, lay.src_pos, lay.dst_pos,
                      d.N, d.B, d.D, d.theta, tab);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return dispatch_attn<FUSED>(d, a, max_priv, out, s);
+  return dispatch_attn<FUSED>(d, a, p, out, s);
 }
 
 hipError_t launch_restore_dense(const Dims& d, const tdx_layout& lay, const void* mk,
@@ -655,10 +951,11 @@ hipError_t launch_restore_dense(const Dims& d, const tdx_layout& lay, const void
 hipError_t launch_dense_attn(const Dims& d, const void* q, const int32_t* priv_off,
                              const void* pk, const void* pv, int max_priv, const void* kd,
                              const void* vd, float scale, void* out, void* ws, hipStream_t s) {
+  const Plan p = make_plan(d, max_priv, false);
   AttnArgs a = common_args(d, q, priv_off, pk, pv, scale, ws);
   a.sk = kd;
   a.sv = vd;
-  return dispatch_attn<DENSE>(d, a, max_priv, out, s);
+  return dispatch_attn<DENSE>(d, a, p, out, s);
 }
 
 }  // namespace tdx

@@ -24,21 +24,28 @@ namespace tdx {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kFlagThreads = 1024;
 constexpr int kCopyChunk = 8;
 constexpr int kScanThreads = 1024;
 
-// KC = 16-byte chunks per thread per tensor for one 16-token block.
+// KC = 16-byte chunks per thread per tensor for one 16-token block.  The
+// Master block stays in registers; each thread ORs the XOR of every Mirror
+// chunk into one bit per agent (64 agents per pass), so consecutive Mirrors'
+// loads overlap; one workgroup-wide OR per pass decides the flags.
 template <int KC>
-__global__ __launch_bounds__(kThreads) void flag_kernel(
+__global__ __launch_bounds__(kFlagThreads) void flag_kernel(
     const u32x4* __restrict__ ak, const u32x4* __restrict__ av,
     const int32_t* __restrict__ master_p, int N, int L, int nb, int chunks,
     uint8_t* __restrict__ flags, u32x4* __restrict__ mk_out, u32x4* __restrict__ mv_out) {
+  constexpr int W = kFlagThreads / kWave;
+  __shared__ unsigned long long wmask[W];
   const int beta = blockIdx.x;
   const int l = blockIdx.y;
   const int tid = threadIdx.x;
+  const int lane = tid % kWave, wave = tid / kWave;
   const int m = master_p[0];
   if (m < 0 || m >= N) {  // invalid Master: no reads; offsets_kernel reports nnz = -1
-    for (int i = tid; i < N; i += kThreads) flags[((size_t)i * L + l) * nb + beta] = 0;
+    for (int i = tid; i < N; i += kFlagThreads) flags[((size_t)i * L + l) * nb + beta] = 0;
     return;
   }
   // chunk offset of (agent a, layer l, block beta): ((a*L + l)*nb + beta)*chunks
@@ -47,7 +54,7 @@ __global__ __launch_bounds__(kThreads) void flag_kernel(
   u32x4 mkr[KC], mvr[KC];
 #pragma unroll
   for (int j = 0; j < KC; ++j) {
-    const int c = tid + j * kThreads;
+    const int c = tid + j * kFlagThreads;
     if (c < chunks) {
       mkr[j] = ak[mbase + c];
       mvr[j] = av[mbase + c];
@@ -57,31 +64,42 @@ __global__ __launch_bounds__(kThreads) void flag_kernel(
     const size_t obase = (size_t)l * layer_chunks + (size_t)beta * chunks;
 #pragma unroll
     for (int j = 0; j < KC; ++j) {
-      const int c = tid + j * kThreads;
+      const int c = tid + j * kFlagThreads;
       if (c < chunks) {
         __builtin_nontemporal_store(mkr[j], mk_out + obase + c);
         __builtin_nontemporal_store(mvr[j], mv_out + obase + c);
       }
     }
   }
-  for (int i = 0; i < N; ++i) {
-    if (i == m) {
-      if (tid == 0) flags[((size_t)i * L + l) * nb + beta] = 0;
-      continue;
-    }
-    const size_t base = ((size_t)i * L + l) * layer_chunks + (size_t)beta * chunks;
-    uint32_t acc = 0;
+  for (int i0 = 0; i0 < N; i0 += 64) {
+    const int iend = min(i0 + 64, N);
+    unsigned long long bits = 0;
+#pragma unroll 2
+    for (int i = i0; i < iend; ++i) {
+      if (i == m) continue;  // uniform
+      const size_t base = ((size_t)i * L + l) * layer_chunks + (size_t)beta * chunks;
+      uint32_t acc = 0;
 #pragma unroll
-    for (int j = 0; j < KC; ++j) {
-      const int c = tid + j * kThreads;
-      if (c < chunks) {
-        const u32x4 xk = ak[base + c] ^ mkr[j];
-        const u32x4 xv = av[base + c] ^ mvr[j];
-        acc |= xk[0] | xk[1] | xk[2] | xk[3] | xv[0] | xv[1] | xv[2] | xv[3];
+      for (int j = 0; j < KC; ++j) {
+        const int c = tid + j * kFlagThreads;
+        if (c < chunks) {
+          const u32x4 xk = ak[base + c] ^ mkr[j];
+          const u32x4 xv = av[base + c] ^ mvr[j];
+          acc |= xk[0] | xk[1] | xk[2] | xk[3] | xv[0] | xv[1] | xv[2] | xv[3];
+        }
       }
+      bits |= (unsigned long long)(acc != 0) << (i - i0);
     }
-    const int any = __syncthreads_or(acc != 0);
-    if (tid == 0) flags[((size_t)i * L + l) * nb + beta] = any ? 1 : 0;
+    // OR over the workgroup
+    for (int o = kWave / 2; o > 0; o >>= 1) bits |= __shfl_xor(bits, o, kWave);
+    if (lane == 0) wmask[wave] = bits;
+    __syncthreads();
+    if (tid < iend - i0) {
+      unsigned long long all = 0;
+      for (int w = 0; w < W; ++w) all |= wmask[w];
+      flags[((size_t)(i0 + tid) * L + l) * nb + beta] = (uint8_t)((all >> tid) & 1ull);
+    }
+    __syncthreads();
   }
 }
 
@@ -211,10 +229,10 @@ hipError_t launch_encode(const Dims& d, const int32_t* master, const void* ak, c
   u32x4* mk4 = static_cast<u32x4*>(mk_out);
   u32x4* mv4 = static_cast<u32x4*>(mv_out);
   {
-    const int kc = (chunks + kThreads - 1) / kThreads;
+    const int kc = (chunks + kFlagThreads - 1) / kFlagThreads;
     dim3 grid(nb, d.L);
-#define TDX_FLAG(KC)                                                                         \
-  hipLaunchKernelGGL(flag_kernel<KC>, grid, dim3(kThreads), 0, s, k4, v4, master, d.N, d.L, \
+#define TDX_FLAG(KC)                                                                             \
+  hipLaunchKernelGGL(flag_kernel<KC>, grid, dim3(kFlagThreads), 0, s, k4, v4, master, d.N, d.L, \
                      nb, chunks, flags, mk4, mv4)
     if (kc <= 1) TDX_FLAG(1);
     else if (kc <= 2) TDX_FLAG(2);

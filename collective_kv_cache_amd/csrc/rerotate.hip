@@ -8,7 +8,7 @@
 // Design (gfx950): the pass reads each cached K tile once and writes N
 // rotated copies, so it is bound by HBM writes.  A workgroup owns a tile of
 // up to 16 canonical tokens that lies inside one shared block, for a group of
-// layers.  It evaluates cos/sin(Delta(i,b) * theta^(-2e/D)) for up to 64
+// layers.  It evaluates cos/sin(Delta(i,b) * theta^(-2e/D)) for up to 32
 // agents in double precision into LDS once, then streams: every lane holds the
 // 16-byte chunk at dims [e0, e0+VEC) and its rotate-half partner at
 // [e0+D/2, e0+D/2+VEC) in registers and emits both rotated chunks for every
@@ -20,10 +20,25 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTileTok = 16;
-constexpr int kAgentChunk = 64;
-constexpr int kItems = 4;  // (token, head) rows held per lane at once
-constexpr int kMaxBlocksLds = 4096;
+constexpr int kAgentChunk = 32;  // agents whose cos/sin sit in LDS at once
+constexpr int kItems = 2;        // (token, head) rows per lane per batch
 
+#ifndef TDX_RR_NT_STORES
+#define TDX_RR_NT_STORES 1
+#endif
+
+template <typename E>
+__device__ __forceinline__ void st_out(E* p, const u32x4& v) {
+#if TDX_RR_NT_STORES
+  st16_nt(p, v);
+#else
+  st16(p, v);
+#endif
+}
+
+// One workgroup: canonical tokens [t0, t0+16) for layers [l0, l0+lpg).  The
+// (layer, batch) steps run in sequence and the next step's input is loaded
+// while the current one is written out for every agent.
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void rerotate_kernel(
     const E* __restrict__ kc, E* __restrict__ out, const int32_t* __restrict__ blk_start,
@@ -33,9 +48,10 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(
   constexpr int HALF = D / 2;
   constexpr int G = HALF / VEC;       // lanes per (token, head) row
   constexpr int RPP = kThreads / G;   // rows covered by the workgroup per item
-  __shared__ float2 tab[kAgentChunk * HALF];
-  __shared__ double invf[HALF];
-  __shared__ int32_t sblk[kMaxBlocksLds + 1];
+  extern __shared__ __align__(16) unsigned char smem[];
+  float2* tab = reinterpret_cast<float2*>(smem);                      // [kAgentChunk][HALF]
+  double* invf = reinterpret_cast<double*>(tab + kAgentChunk * HALF);  // [HALF]
+  int32_t* sblk = reinterpret_cast<int32_t*>(invf + HALF);            // [B+1]
 
   const int tid = threadIdx.x;
   const int t0 = blockIdx.x * kTileTok;
@@ -64,6 +80,8 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(
     const int tb = min(t1, sblk[b + 1]);
     if (ta >= tb) continue;
     const int nrows = (tb - ta) * Hkv;
+    const int nbatch = (nrows + RPP * kItems - 1) / (RPP * kItems);
+    const int nsteps = (l1 - l0) * nbatch;
     const int sp = src_pos[b];
     for (int a0 = 0; a0 < N; a0 += kAgentChunk) {
       const int na = min(kAgentChunk, N - a0);
@@ -76,44 +94,56 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(
         tab[x] = make_float2((float)cs, (float)sn);
       }
       __syncthreads();
-      for (int l = l0; l < l1; ++l) {
+      // step = (layer, batch of rows)
+      u32x4 xl[kItems], xh[kItems], nl[kItems], nh[kItems];
+      auto load_step = [&](int step, u32x4* lo_, u32x4* hi_) {
+        const int l = l0 + step / nbatch;
+        const int rb = (step % nbatch) * RPP * kItems;
         const E* src = kc + ((size_t)l * T + ta) * rowD;
-        for (int rb = 0; rb < nrows; rb += RPP * kItems) {
-          u32x4 xl[kItems], xh[kItems];
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) {
+          const int r = rb + row_base + k * RPP;
+          if (r < nrows) {
+            lo_[k] = ld16(src + (size_t)r * D + e0);
+            hi_[k] = ld16(src + (size_t)r * D + HALF + e0);
+          }
+        }
+      };
+      load_step(0, xl, xh);
+      for (int step = 0; step < nsteps; ++step) {
+        if (step + 1 < nsteps) load_step(step + 1, nl, nh);  // in flight during the stores
+        const int l = l0 + step / nbatch;
+        const int rb = (step % nbatch) * RPP * kItems;
+        for (int a = 0; a < na; ++a) {
+          float cs[VEC], sn[VEC];
+#pragma unroll
+          for (int j = 0; j < VEC; ++j) {
+            const float2 v = tab[a * HALF + e0 + j];
+            cs[j] = v.x;
+            sn[j] = v.y;
+          }
+          E* dst = out + ((size_t)(a0 + a) * L + l) * (size_t)T * rowD + (size_t)ta * rowD;
 #pragma unroll
           for (int k = 0; k < kItems; ++k) {
             const int r = rb + row_base + k * RPP;
             if (r < nrows) {
-              xl[k] = ld16(src + (size_t)r * D + e0);
-              xh[k] = ld16(src + (size_t)r * D + HALF + e0);
-            }
-          }
-          for (int a = 0; a < na; ++a) {
-            float cs[VEC], sn[VEC];
+              float x[VEC], y[VEC], ox[VEC], oy[VEC];
+              Fmt<E>::unpack(xl[k], x);
+              Fmt<E>::unpack(xh[k], y);
 #pragma unroll
-            for (int j = 0; j < VEC; ++j) {
-              const float2 v = tab[a * HALF + e0 + j];
-              cs[j] = v.x;
-              sn[j] = v.y;
-            }
-            E* dst = out + ((size_t)(a0 + a) * L + l) * (size_t)T * rowD + (size_t)ta * rowD;
-#pragma unroll
-            for (int k = 0; k < kItems; ++k) {
-              const int r = rb + row_base + k * RPP;
-              if (r < nrows) {
-                float x[VEC], y[VEC], ox[VEC], oy[VEC];
-                Fmt<E>::unpack(xl[k], x);
-                Fmt<E>::unpack(xh[k], y);
-#pragma unroll
-                for (int j = 0; j < VEC; ++j) {
-                  ox[j] = x[j] * cs[j] - y[j] * sn[j];
-                  oy[j] = y[j] * cs[j] + x[j] * sn[j];
-                }
-                st16_nt(dst + (size_t)r * D + e0, Fmt<E>::pack(ox));
-                st16_nt(dst + (size_t)r * D + HALF + e0, Fmt<E>::pack(oy));
+              for (int j = 0; j < VEC; ++j) {
+                ox[j] = x[j] * cs[j] - y[j] * sn[j];
+                oy[j] = y[j] * cs[j] + x[j] * sn[j];
               }
+              st_out(dst + (size_t)r * D + e0, Fmt<E>::pack(ox));
+              st_out(dst + (size_t)r * D + HALF + e0, Fmt<E>::pack(oy));
             }
           }
+        }
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) {
+          xl[k] = nl[k];
+          xh[k] = nh[k];
         }
       }
     }
@@ -130,7 +160,8 @@ hipError_t launch_t(const Dims& d, const tdx_layout& lay, const void* kc, void* 
   const int lpg = (d.L + groups - 1) / groups;
   groups = (d.L + lpg - 1) / lpg;
   dim3 grid(tiles, groups);
-  hipLaunchKernelGGL((rerotate_kernel<E, D>), grid, dim3(kThreads), 0, s,
+  const size_t lds = (size_t)kAgentChunk * (D / 2) * 8 + (D / 2) * 8 + (size_t)(d.B + 1) * 4;
+  hipLaunchKernelGGL((rerotate_kernel<E, D>), grid, dim3(kThreads), lds, s,
                      static_cast<const E*>(kc), static_cast<E*>(out), lay.blk_start,
                      lay.src_pos, lay.dst_pos, d.N, d.B, d.T, d.L, d.Hkv, lpg, d.theta);
   return hipGetLastError();
@@ -140,7 +171,6 @@ hipError_t launch_t(const Dims& d, const tdx_layout& lay, const void* kc, void* 
 
 hipError_t launch_rerotate(const Dims& d, const tdx_layout& lay, const void* kc, void* out,
                            hipStream_t s) {
-  if (d.B > kMaxBlocksLds) return hipErrorInvalidValue;
   if (d.dtype == TDX_BF16) {
     return d.D == 128 ? launch_t<uint16_t, 128>(d, lay, kc, out, s)
                       : launch_t<uint16_t, 64>(d, lay, kc, out, s);
