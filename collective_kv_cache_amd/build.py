@@ -24,6 +24,9 @@ FLAGS = [
     "-Wno-unused-function",
     # keep hipcc from forming packed fp32 arithmetic (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the online-softmax rescale then
+    # multiplies them in place instead of copying them out of and back into AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

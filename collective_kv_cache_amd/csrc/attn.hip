@@ -45,7 +45,16 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kTile = 16;
-constexpr int kTilesPerSplit = 64;  // agent_kernel: 16 tiles per wave
+#ifndef TDX_AG_TPS
+#define TDX_AG_TPS 128
+#endif
+#ifndef TDX_AG_NW
+#define TDX_AG_NW 4
+#endif
+#ifndef TDX_AG_PD
+#define TDX_AG_PD 3
+#endif
+constexpr int kTilesPerSplit = TDX_AG_TPS;  // agent_kernel: tiles per workgroup
 constexpr int kShThreads = 256;     // shared_kernel: 4 waves, one 16-row tile each
 constexpr int kShWaves = kShThreads / kWave;
 constexpr int kRowsPerGroup = 16 * kShWaves;
@@ -94,6 +103,13 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
 
 __device__ __forceinline__ f32x4 mfma32(const u32x4& a, const u32x4& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// (lo, hi) -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ f32x4 mfma16(const i16x4& a, const i16x4& b, f32x4 c) {
@@ -195,6 +211,7 @@ struct AttnArgs {
   const int32_t* blk_start;  // [B+1]
   const float2* tab;         // fused: [N][B][D/2] cos/sin of each shift
   uint16_t* qrot;            // fused: [N][L][B][Hq][D] bf16 rotated queries
+  uint16_t* qplain;          // [N][L][Hq][D] bf16 queries
   float* part;               // [N][L][Hq][S][D+4]: m, l, -, -, O[D]
   int N, L, T, B, Hkv, Hq;
   int SP;                    // agent-kernel record slots
@@ -219,15 +236,25 @@ struct RowState {
   }
 };
 
-// Gather the PV A operand of one tile from row-major LDS V [16][VS]:
+// LDS transpose read (ds_read_b64_tr_b16, gfx950).  Every lane supplies the
+// address of 4 consecutive 16-bit elements; within each 16-lane group G, lane
+// 16G + i receives element i%4 of the rows addressed by lanes 16G + 4j + i/4,
+// j = 0..3.  If lane s addresses row 4*(s/16) + (s%16)/4 at column c0 + 4*(s%4),
+// lane l gets [row 4*(l/16) + j][column c0 + l%16] for j = 0..3: the B
+// operand layout of v_mfma_f32_16x16x16_bf16 with tokens as the reduction index.
+__device__ __forceinline__ i16x4 ld_tr16(const void* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+// The PV operand of one tile from row-major LDS V [16][VS] (bf16):
 // va[dt][j] = V[token 4*q4 + j][dim 16*dt + c16].
 template <int D>
 __device__ __forceinline__ void gather_v(const uint16_t* vt, int VS, int q4, int c16, i16x4* va) {
   constexpr int DT = D / 16;
+  const uint16_t* base = vt + (4 * q4 + (c16 >> 2)) * VS + 4 * (c16 & 3);
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) va[dt][j] = (short)vt[(4 * q4 + j) * VS + dt * 16 + c16];
+  for (int dt = 0; dt < DT; ++dt) va[dt] = ld_tr16(base + 16 * dt);
 }
 
 // Online softmax + PV for one tile.  z: the 4 logits (log2 domain) of the
@@ -243,22 +270,31 @@ __device__ __forceinline__ void softmax_pv(RowState<D>& st, const float z[4], co
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
   const float mnew = fmaxf(st.m, tmax);
   const float mref = (mnew == -INFINITY) ? 0.0f : mnew;
-  const float alpha = exp2f(st.m - mref);
+  // O and l are rescaled only when some row's maximum grew; otherwise every
+  // lane's factor is exactly 1 (or 0 * 0 for a row with no key yet) and the
+  // wave skips the multiplies as a whole
+  float alpha = 1.0f;
+  const bool grow = __builtin_amdgcn_ballot_w64(mnew > st.m) != 0;
+  if (grow) alpha = __builtin_amdgcn_exp2f(st.m - mref);
   st.m = mnew;
+  // weights in (0, 1]: v_exp_f32, then one v_cvt_pk_bf16_f32 (round to
+  // nearest even) per pair; the sum uses the same rounded weights
+  const uint32_t w01 = cvt_pk_bf16(__builtin_amdgcn_exp2f(z[0] - mref), __builtin_amdgcn_exp2f(z[1] - mref));
+  const uint32_t w23 = cvt_pk_bf16(__builtin_amdgcn_exp2f(z[2] - mref), __builtin_amdgcn_exp2f(z[3] - mref));
+  const float psum = (__uint_as_float(w01 << 16) + __uint_as_float(w01 & 0xffff0000u)) +
+                     (__uint_as_float(w23 << 16) + __uint_as_float(w23 & 0xffff0000u));
   i16x4 pb;
-  float psum = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t b = f32_to_bf16(exp2f(z[j] - mref));
-    pb[j] = (short)b;
-    psum += __uint_as_float(b << 16);  // the sum uses the same rounded weights
-  }
+  pb[0] = (short)(w01 & 0xffffu);
+  pb[1] = (short)(w01 >> 16);
+  pb[2] = (short)(w23 & 0xffffu);
+  pb[3] = (short)(w23 >> 16);
   st.l = st.l * alpha + psum;
+  if (grow) {
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    st.o[dt] *= alpha;
-    st.o[dt] = mfma16(va[dt], pb, st.o[dt]);
+    for (int dt = 0; dt < DT; ++dt) st.o[dt] *= alpha;
   }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) st.o[dt] = mfma16(va[dt], pb, st.o[dt]);
 }
 
 // Write a row's partial record (m, l, O unnormalised).
@@ -442,25 +478,48 @@ __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(3)))
 }
 
 // ---- agent_kernel: private history + own diff blocks (or dense shared) ---------
+//
+// Each wave walks a contiguous run of 16-token tiles through a PD-stage
+// register pipeline: while tile u is used, the K rows, V rows and the 16-row
+// bf16 query operand of tiles u+1 .. u+PD-1 are in flight in VGPRs (the query
+// is the plain one for private/dense tiles and the one rotated by -Delta of
+// the tile's shared block for diff tiles).  K and the query feed the MFMA
+// straight from registers; V is written to a wave-private bf16 LDS tile and
+// read back transposed (ds_read_b64_tr_b16) as the PV operand.  The register
+// file holds far more bytes in flight per CU than LDS slots could.
 
 template <typename E, int D>
-struct TileIn {
-  u32x4 k[D / 32];
-  u32x4 v[D / 32];
-  u32x4 q[D / 32];  // diff tiles: query rotated for the tile's first shared block
+struct Stage {
+  static constexpr int KD = D / 32;                       // 16-byte bf16 chunks of K/Q per lane
+  static constexpr int KL = KD * (int)sizeof(E) / 2;       // K loads per lane
+  static constexpr int NV = kTile * D * (int)sizeof(E) / 16 / kWave;  // V loads per lane
+  u32x4 k[KL];
+  u32x4 v[NV];
+  u32x4 q[KD];
 };
 
-template <typename E, int D, int MODE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void agent_kernel(AttnArgs a) {
-  constexpr int KD = D / 32;
+// V tile of one wave in LDS: [16 rows][D] bf16, 16-byte chunk ch of row t
+// stored at chunk position ch ^ (t % (D/8)) so that row-wise writes and the
+// transposed reads spread over the banks.
+template <int D>
+__device__ __forceinline__ int vlds_off(int t, int ch) {
+  constexpr int C = D / 8;
+  return (t * C + (ch ^ (t % C))) * 16;
+}
+
+template <typename E, int D, int MODE, int NW, int PD>
+__global__ __launch_bounds__(NW * kWave) void agent_kernel(AttnArgs a) {
+  using St = Stage<E, D>;
+  constexpr int KD = St::KD;
   constexpr int DT = D / 16;
-  constexpr int HALF = D / 2;
-  constexpr int VS = D + 8;
+  constexpr int NT = NW * kWave;
+  constexpr int RB = D * (int)sizeof(E);  // K/V row bytes of one head
+  constexpr int CPR = RB / 16;            // 16-byte chunks per K/V row
+  constexpr int VB = kTile * D * 2;       // bf16 V tile bytes
   extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t* vtile_all = reinterpret_cast<uint16_t*>(smem);  // [kWaves][16][VS]
-  const size_t vbytes = (size_t)kWaves * kTile * VS * 2;
-  const size_t cbytes = (size_t)kWaves * 16 * (D + 2) * 4;
-  int2* tinfo = reinterpret_cast<int2*>(smem + (vbytes > cbytes ? vbytes : cbytes));  // [64]
+  const size_t vbytes = (size_t)NW * VB;
+  const size_t cbytes = (size_t)NW * 16 * (D + 2) * 4;
+  int2* tinfo = reinterpret_cast<int2*>(smem + (vbytes > cbytes ? vbytes : cbytes));  // [TPS]
   int32_t* sblk = reinterpret_cast<int32_t*>(tinfo + kTilesPerSplit);                 // [B+1]
 
   const int i = blockIdx.x;
@@ -490,19 +549,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int tend = min(tbeg + kTilesPerSplit, ntiles);
 
   if (MODE == FUSED) {
-    for (int b = tid; b <= a.B; b += kThreads) sblk[b] = a.blk_start[b];
+    for (int b = tid; b <= a.B; b += NT) sblk[b] = a.blk_start[b];
   }
-  // rows >= g of the 16-row query tile repeat row g-1; their results are never used
-  const int qrow_i = min(c16, g - 1);
-  const E* qrow = static_cast<const E*>(a.q) + (((size_t)i * a.L + l) * a.Hq + (size_t)h * g + qrow_i) * D;
-  u32x4 qplain[KD];  // the query as given, for private (and dense) tiles
-#pragma unroll
-  for (int k = 0; k < KD; ++k) qplain[k] = load8_bf16<E>(qrow + 32 * k + 8 * q4);
   __syncthreads();  // sblk ready
   if (MODE == FUSED) {
-    // per diff tile of this split: (diff block beta, first shared block), so
-    // that issuing a tile's loads needs no dependent global read
-    for (int u = tbeg + tid; u < tend; u += kThreads) {
+    // per diff tile of this split: (diff block beta, first shared block)
+    for (int u = tbeg + tid; u < tend; u += NT) {
       if (u >= ntp) {
         const int beta = a.diff_idx[e0 + u - ntp];
         tinfo[u - tbeg] = make_int2(beta, block_of(sblk, a.B, beta * kTile));
@@ -513,123 +565,159 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
   RowState<D> st;
   st.init();
-  uint16_t* vt = vtile_all + (size_t)wave * kTile * VS;
   const size_t rowHD = (size_t)a.Hkv * D;
-  const E* pk = static_cast<const E*>(a.pk) + ((size_t)l * ptot + p0) * rowHD + (size_t)h * D;
-  const E* pv = static_cast<const E*>(a.pv) + ((size_t)l * ptot + p0) * rowHD + (size_t)h * D;
+  const size_t rowbytes = rowHD * sizeof(E);
+  const unsigned char* pkb = reinterpret_cast<const unsigned char*>(
+      static_cast<const E*>(a.pk) + ((size_t)l * ptot + p0) * rowHD + (size_t)h * D);
+  const unsigned char* pvb = reinterpret_cast<const unsigned char*>(
+      static_cast<const E*>(a.pv) + ((size_t)l * ptot + p0) * rowHD + (size_t)h * D);
+  // bf16 query rows of this (agent, layer, KV head): plain, and per shared block rotated
+  const uint16_t* qplain = a.qplain + (((size_t)i * a.L + l) * a.Hq + (size_t)h * g) * D;
+  unsigned char* vl = smem + (size_t)wave * VB;  // this wave's V tile
 
-  // Loads of one tile into registers.  Every address is valid: rows past the
-  // end of the private history re-read its last row and are masked out of
-  // the softmax (weight 0 times a finite value), so no lane branches around a
-  // load and nothing consumes the loads before the tile is processed.
-  auto issue = [&](int u, TileIn<E, D>& t) {
-    const E* kr;
-    const E* vr;
+  const int qrow = min(c16, g - 1);  // query rows >= g repeat row g-1 (unused columns)
+
+  // Issue the loads of tile u into stage S (the same count on every path).
+  auto load = [&](int u, St& S) {
+    const unsigned char* kb;
+    const unsigned char* vb;
+    const uint16_t* qb = qplain;
+    int rmax = kTile - 1;  // rows past the end of a partial tile re-read its last row
     if (u < ntp) {
-      const int p = min(u * kTile + c16, P - 1);
-      kr = pk + (size_t)p * rowHD;
-      vr = pv + (size_t)p * rowHD;
-#pragma unroll
-      for (int k = 0; k < KD; ++k) t.q[k] = qplain[k];  // defined on every path (no stale copies)
+      kb = pkb + (size_t)u * kTile * rowbytes;
+      vb = pvb + (size_t)u * kTile * rowbytes;
+      rmax = min(kTile - 1, P - 1 - u * kTile);
     } else if (MODE == FUSED) {
-      const size_t o = ((size_t)(e0 + u - ntp) * kTile + c16) * rowHD + (size_t)h * D;
-      kr = static_cast<const E*>(a.dk) + o;
-      vr = static_cast<const E*>(a.dv) + o;
-      // the rotated query of the tile's first shared block travels with the
-      // tile, so processing the tile issues no global loads of its own
+      const size_t o = ((size_t)(e0 + u - ntp) * kTile * rowHD + (size_t)h * D) * sizeof(E);
+      kb = static_cast<const unsigned char*>(a.dk) + o;
+      vb = static_cast<const unsigned char*>(a.dv) + o;
       const int b = tinfo[u - tbeg].y;
-      const uint16_t* qs = a.qrot + ((((size_t)i * a.L + l) * a.B + b) * a.Hq + (size_t)h * g + qrow_i) * D;
-#pragma unroll
-      for (int k = 0; k < KD; ++k) t.q[k] = ld16(qs + 32 * k + 8 * q4);
+      qb = a.qrot + ((((size_t)i * a.L + l) * a.B + b) * a.Hq + (size_t)h * g) * D;
     } else {
-      const size_t o = (((size_t)i * a.L + l) * a.T + (size_t)(u - ntp) * kTile + c16) * rowHD +
-                       (size_t)h * D;
-      kr = static_cast<const E*>(a.sk) + o;
-      vr = static_cast<const E*>(a.sv) + o;
+      const size_t o = ((((size_t)i * a.L + l) * a.T + (size_t)(u - ntp) * kTile) * rowHD + (size_t)h * D) * sizeof(E);
+      kb = static_cast<const unsigned char*>(a.sk) + o;
+      vb = static_cast<const unsigned char*>(a.sv) + o;
+    }
+    // K: row c16, elements 32k + 8*q4 .. +7
+    const unsigned char* kr = kb + (size_t)min(c16, rmax) * rowbytes;
 #pragma unroll
-      for (int k = 0; k < KD; ++k) t.q[k] = qplain[k];
+    for (int k = 0; k < St::KL; ++k)
+      S.k[k] = *reinterpret_cast<const u32x4*>(kr + (sizeof(E) == 2 ? (32 * k + 8 * q4) * 2
+                                                                    : (32 * (k / 2) + 8 * q4 + 4 * (k % 2)) * 4));
+    // V: 16-byte chunk p = 64 v + lane of the tile = row p / CPR, chunk p % CPR
+#pragma unroll
+    for (int v = 0; v < St::NV; ++v) {
+      const int p = v * kWave + lane;
+      S.v[v] = *reinterpret_cast<const u32x4*>(vb + (size_t)min(p / CPR, rmax) * rowbytes + (p % CPR) * 16);
     }
 #pragma unroll
-    for (int k = 0; k < KD; ++k) {
-      t.k[k] = load8_bf16<E>(kr + 32 * k + 8 * q4);
-      t.v[k] = load8_bf16<E>(vr + 32 * k + 8 * q4);
-    }
+    for (int k = 0; k < KD; ++k) S.q[k] = ld16(qb + (size_t)qrow * D + 32 * k + 8 * q4);
   };
 
-  // each wave walks a contiguous run of tiles (consecutive diff blocks tend
-  // to share a shared block, so the rotated query is reused)
-  const int span = (tend - tbeg + kWaves - 1) / kWaves;
-  const int ubeg = tbeg + wave * span;
-  const int uend = min(ubeg + span, tend);
-  auto process = [&](const TileIn<E, D>& cur, int u) {
+  // live = false: a pipeline fill/drain step; every score is masked, so the
+  // stage contents (zeros, or a re-read of the last tile) add nothing
+  auto process = [&](St& S, int u, bool live) {
+    // V rows -> bf16 LDS tile (a wave's LDS operations run in order, so the
+    // previous tile's transposed reads have completed before these writes)
 #pragma unroll
-    for (int k = 0; k < KD; ++k) *reinterpret_cast<u32x4*>(vt + c16 * VS + 32 * k + 8 * q4) = cur.v[k];
+    for (int v = 0; v < St::NV; ++v) {
+      const int p = v * kWave + lane;
+      if constexpr (sizeof(E) == 2) {
+        *reinterpret_cast<u32x4*>(vl + vlds_off<D>(p / CPR, p % CPR)) = S.v[v];
+      } else {
+        const int t = p / CPR, c4 = p % CPR;  // fp32 chunk = dims 4*c4 .. +3
+        uint2 w;
+        w.x = pack_bf16(__uint_as_float(S.v[v][0]), __uint_as_float(S.v[v][1]));
+        w.y = pack_bf16(__uint_as_float(S.v[v][2]), __uint_as_float(S.v[v][3]));
+        *reinterpret_cast<uint2*>(vl + vlds_off<D>(t, c4 / 2) + (c4 % 2) * 8) = w;
+      }
+    }
+    wave_sync();
+    u32x4 kop[KD];
+#pragma unroll
+    for (int k = 0; k < KD; ++k) {
+      if constexpr (sizeof(E) == 2) {
+        kop[k] = S.k[k];
+      } else {
+        kop[k] = u32x4{pack_bf16(__uint_as_float(S.k[2 * k][0]), __uint_as_float(S.k[2 * k][1])),
+                       pack_bf16(__uint_as_float(S.k[2 * k][2]), __uint_as_float(S.k[2 * k][3])),
+                       pack_bf16(__uint_as_float(S.k[2 * k + 1][0]), __uint_as_float(S.k[2 * k + 1][1])),
+                       pack_bf16(__uint_as_float(S.k[2 * k + 1][2]), __uint_as_float(S.k[2 * k + 1][3]))};
+      }
+    }
     float z[4];
     if (u < ntp || MODE == DENSE) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < KD; ++k) acc = mfma32(cur.k[k], qplain[k], acc);
+      for (int k = 0; k < KD; ++k) acc = mfma32(kop[k], S.q[k], acc);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        z[j] = (u >= ntp || u * kTile + 4 * q4 + j < P) ? acc[j] * a.scale_log2 : -INFINITY;
+        z[j] = live && (u >= ntp || u * kTile + 4 * q4 + j < P) ? acc[j] * a.scale_log2 : -INFINITY;
     } else {
       // the agent's own block: RoPE recovered through Q' = R(-Delta(i,b)) q
       const int2 ti = tinfo[u - tbeg];
       const int t0 = ti.x * kTile;
-      const int bfirst = ti.y;
 #pragma unroll
       for (int j = 0; j < 4; ++j) z[j] = -INFINITY;
-      for (int b = bfirst; b < a.B && sblk[b] < t0 + kTile; ++b) {
+      for (int b = ti.y; b < a.B && sblk[b] < t0 + kTile; ++b) {
         if (sblk[b + 1] <= t0) continue;  // empty block
         u32x4 qr[KD];
-        if (b == bfirst) {
+        if (b == ti.y) {
 #pragma unroll
-          for (int k = 0; k < KD; ++k) qr[k] = cur.q[k];
+          for (int k = 0; k < KD; ++k) qr[k] = S.q[k];
         } else {  // a tile straddling shared blocks (block starts not 16-aligned)
-          const uint16_t* qs = a.qrot + ((((size_t)i * a.L + l) * a.B + b) * a.Hq + (size_t)h * g + qrow_i) * D;
+          const uint16_t* qs = a.qrot + ((((size_t)i * a.L + l) * a.B + b) * a.Hq + (size_t)h * g + qrow) * D;
 #pragma unroll
           for (int k = 0; k < KD; ++k) qr[k] = ld16(qs + 32 * k + 8 * q4);
         }
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < KD; ++k) acc = mfma32(cur.k[k], qr[k], acc);
+        for (int k = 0; k < KD; ++k) acc = mfma32(kop[k], qr[k], acc);
         const int bs = sblk[b], be = sblk[b + 1];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int tt = t0 + 4 * q4 + j;
-          if (tt >= bs && tt < be) z[j] = acc[j] * a.scale_log2;
+          if (live && tt >= bs && tt < be) z[j] = acc[j] * a.scale_log2;
         }
       }
     }
-    wave_sync();  // V tile visible to the whole wave
+    // PV operand: va[dt][j] = V[token 4*q4 + j][dim 16*dt + c16]; this lane
+    // addresses row 4*q4 + c16/4, dims 16*dt + 4*(c16%4)
     i16x4 va[DT];
-    gather_v<D>(vt, VS, q4, c16, va);
+    const int vrow = 4 * q4 + (c16 >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      va[dt] = ld_tr16(vl + vlds_off<D>(vrow, 2 * dt + ((c16 & 3) >> 1)) + (c16 & 1) * 8);
     softmax_pv<D>(st, z, va);
-    wave_sync();  // reads done before the next tile overwrites the V tile
   };
 
-  // Two fixed register sets: the next tile's loads are in flight while the
-  // current one is used.  The next loads are issued unconditionally (the last
-  // step re-reads its own tile) so that the compiler's wait counting sees one
-  // path and waits only for the older set.
+  // each wave walks a contiguous run of tiles; PD-1 tiles are always in
+  // flight.  Step k of the unrolled body always loads into S[(k+PD-1) % PD]
+  // and uses S[k], with no branch around either: the pipeline fills in the
+  // first pass (masked steps over zeroed stages) and drains in the last one
+  // (masked steps over re-reads of the last tile).  Every stage then lives in
+  // the same registers on every pass and the hardware wait before a stage is
+  // used leaves the PD-1 younger tiles in flight.
+  const int span = (tend - tbeg + NW - 1) / NW;
+  const int ubeg = tbeg + wave * span;
+  const int uend = min(ubeg + span, tend);
   if (ubeg < uend) {
-    TileIn<E, D> ta, tb;
-    issue(ubeg, ta);
-    for (int u = ubeg;;) {
-      issue(min(u + 1, uend - 1), tb);
-      process(ta, u);
-      if (++u >= uend) break;
-      issue(min(u + 1, uend - 1), ta);
-      process(tb, u);
-      if (++u >= uend) break;
+    St S[PD] = {};  // zeros for the fill steps
+    for (int u0 = ubeg - (PD - 1); u0 < uend; u0 += PD) {
+#pragma unroll
+      for (int k = 0; k < PD; ++k) {
+        const int u = u0 + k;  // tile used in this step (wave-uniform)
+        load(min(u + PD - 1, uend - 1), S[(k + PD - 1) % PD]);
+        process(S[k], min(max(u, ubeg), uend - 1), u >= ubeg && u < uend);
+      }
     }
   }
 
-  // ---- combine the four waves (LDS aliases the V tiles)
+  // ---- combine the waves (LDS aliases the V tiles)
   __syncthreads();
-  float* cm = reinterpret_cast<float*>(smem);  // [kWaves][16] max
-  float* cl = cm + kWaves * 16;                 // [kWaves][16] sum
-  float* co = cl + kWaves * 16;                 // [kWaves][16][D]
+  float* cm = reinterpret_cast<float*>(smem);  // [NW][16] max
+  float* cl = cm + NW * 16;                     // [NW][16] sum
+  float* co = cl + NW * 16;                     // [NW][16][D]
   float lsum = st.l;
   lsum += __shfl_xor(lsum, 16, kWave);
   lsum += __shfl_xor(lsum, 32, kWave);
@@ -642,13 +730,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     *reinterpret_cast<f32x4*>(co + ((size_t)wave * 16 + c16) * D + dt * 16 + 4 * q4) = st.o[dt];
   __syncthreads();
   const size_t rec = D + 4;
-  for (int x = tid; x < g * D; x += kThreads) {
+  for (int x = tid; x < g * D; x += NT) {
     const int r = x / D, d = x % D;
     float mm = -INFINITY;
-    for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, cm[w * 16 + r]);
+    for (int w = 0; w < NW; ++w) mm = fmaxf(mm, cm[w * 16 + r]);
     float o = 0.f, ls = 0.f;
     if (mm != -INFINITY) {
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float f = exp2f(cm[w * 16 + r] - mm);
         o += f * co[((size_t)w * 16 + r) * D + d];
         ls += f * cl[w * 16 + r];
@@ -661,6 +749,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       dst[1] = ls;
     }
   }
+}
+
+// bf16 copy of the queries (the MFMA operand form): qplain[i][l][hq][D]
+template <typename E, int D>
+__global__ __launch_bounds__(256) void qplain_kernel(const E* __restrict__ q, size_t n8,
+                                                     uint16_t* __restrict__ out) {
+  for (size_t x = blockIdx.x * (size_t)blockDim.x + threadIdx.x; x < n8; x += (size_t)gridDim.x * blockDim.x)
+    st16(out + 8 * x, load8_bf16<E>(q + 8 * x));
 }
 
 // One wave per output row (agent, layer, query head): combine the agent
@@ -795,7 +891,7 @@ __global__ __launch_bounds__(kThreads) void restore_dense_kernel(
 
 struct Plan {
   int SP, SG, AGS, NAG, TPG, n_sh_wg;
-  size_t part_bytes, tab_off, qrot_off, total;
+  size_t part_bytes, tab_off, qrot_off, qplain_off, total;
 };
 
 Plan make_plan(const Dims& d, int max_priv, bool fused) {
@@ -822,15 +918,25 @@ Plan make_plan(const Dims& d, int max_priv, bool fused) {
   p.part_bytes = (size_t)d.N * d.L * d.Hq * (p.SP + p.SG) * (d.D + 4) * 4;
   p.tab_off = up(p.part_bytes);
   p.qrot_off = p.tab_off + (fused ? up((size_t)d.N * d.B * (d.D / 2) * 8) : 0);
-  p.total = p.qrot_off + (fused ? up((size_t)d.N * d.L * d.B * d.Hq * d.D * 2) : 0);
+  p.qplain_off = p.qrot_off + (fused ? up((size_t)d.N * d.L * d.B * d.Hq * d.D * 2) : 0);
+  p.total = p.qplain_off + up((size_t)d.N * d.L * d.Hq * d.D * 2);
   return p;
 }
 
-size_t agent_lds(int D, int B, bool fused) {
-  const size_t vbytes = (size_t)kWaves * kTile * (D + 8) * 2;
-  const size_t cbytes = (size_t)kWaves * 16 * (D + 2) * 4;
+template <int D, int NW>
+size_t agent_lds(int B, bool fused) {
+  const size_t vbytes = (size_t)NW * kTile * D * 2;
+  const size_t cbytes = (size_t)NW * 16 * (D + 2) * 4;
   return (vbytes > cbytes ? vbytes : cbytes) + (size_t)kTilesPerSplit * 8 + (fused ? (size_t)(B + 1) * 4 : 0);
 }
+
+// waves per workgroup / register stages of agent_kernel: PD stages keep PD-1
+// tiles in flight per wave; fp32 rows of 128 dims take twice the registers
+template <typename E, int D>
+struct AgentCfg {
+  static constexpr int NW = TDX_AG_NW;
+  static constexpr int PD = (sizeof(E) == 4 && D == 128) ? 2 : TDX_AG_PD;
+};
 
 size_t shared_lds(int D, int B, const Plan& p) {
   return (size_t)4 * kTile * (D + 8) * 2 + (size_t)(B + 1) * 4 + (size_t)p.AGS * p.TPG;
@@ -858,9 +964,17 @@ hipError_t launch_attn_t(const Dims& d, AttnArgs a, const Plan& p, E* out, hipSt
     hipLaunchKernelGGL((shared_kernel<E, D>), dim3(grid), dim3(kShThreads), lds, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  const size_t lds = agent_lds(D, d.B, MODE == FUSED);
-  if (lds > 64 * 1024) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((agent_kernel<E, D, MODE>), dim3(d.N, p.SP, d.L * d.Hkv), dim3(kThreads), lds,
+  {
+    const size_t nq = (size_t)d.N * d.L * d.Hq * D / 8;
+    const int qblocks = (int)((nq + 255) / 256 < 4096 ? (nq + 255) / 256 : 4096);
+    hipLaunchKernelGGL((qplain_kernel<E, D>), dim3(qblocks), dim3(256), 0, s, static_cast<const E*>(a.q), nq,
+                       a.qplain);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  constexpr int NW = AgentCfg<E, D>::NW, PD = AgentCfg<E, D>::PD;
+  const size_t lds = agent_lds<D, NW>(d.B, MODE == FUSED);
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((agent_kernel<E, D, MODE, NW, PD>), dim3(d.N, p.SP, d.L * d.Hkv), dim3(NW * kWave), lds,
                      s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t rows = (size_t)d.N * d.L * d.Hq;
@@ -919,6 +1033,7 @@ hipError_t launch_restore_attn(const Dims& d, const tdx_layout& lay, const void*
   float2* tab = reinterpret_cast<float2*>(static_cast<unsigned char*>(ws) + p.tab_off);
   a.tab = tab;
   a.qrot = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(ws) + p.qrot_off);
+  a.qplain = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(ws) + p.qplain_off);
   const size_t n = (size_t)d.N * d.B * (d.D / 2);
   const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
   hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(256), 0, s, lay.src_pos, lay.dst_pos,
@@ -955,6 +1070,7 @@ hipError_t launch_dense_attn(const Dims& d, const void* q, const int32_t* priv_o
   AttnArgs a = common_args(d, q, priv_off, pk, pv, scale, ws);
   a.sk = kd;
   a.sv = vd;
+  a.qplain = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(ws) + p.qplain_off);
   return dispatch_attn<DENSE>(d, a, p, out, s);
 }
 
