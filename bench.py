@@ -50,8 +50,9 @@ def stage_bytes(cfg, lay, nnz_total, k):
     return {
         "rerotate": L * T * kt + N * L * T * kt,
         "select": 2 * N * T * kt + 4 * N * T + 4 * T + 4 * k + 4 * N,
-        # read every agent's cache once, write diff values + indices and the Master copy
-        "encode": N * L * T * kv + diff_bytes + L * T * kv + 4 * (N * L + 1),
+        # read every agent's cache once, write diff values + indices (the Master
+        # stays in place)
+        "encode": N * L * T * kv + diff_bytes + 4 * (N * L + 1),
         # Master once, private histories, diff records, q and out
         "restore_attn": L * T * kv + L * ptot * kv + diff_bytes + 2 * N * L * Hq * D * eb,
         # dense restore (read Master + diffs, write N dense caches) + attention over them
@@ -170,8 +171,9 @@ def main():
     ak, av = agent_caches(cfg, lay, kc, vc, master)
     nb = T // 16
     cap = int(math.ceil(0.35 * (N - 1) * L * nb))  # the Mirrors differ in at most 20% of blocks
-    ds = tdx.diff_encode(shape, dl, sel["master"], ak, av, cap_blocks=cap, check=True)
-    out = tdx.restore_attn(shape, dl, q, po, pk, pv, max_priv, ds.master_k, ds.master_v, ds)
+    # the Master keeps its own cache: no dense copy, restore reads it in place
+    ds = tdx.diff_encode(shape, dl, sel["master"], ak, av, cap_blocks=cap, check=True, master_copy=False)
+    out = tdx.restore_attn(shape, dl, q, po, pk, pv, max_priv, ak, av, ds, master_sel=sel["master"])
     ws_sel = torch.empty(max(tdx.select_workspace(shape1, dl), 16), dtype=torch.uint8, device=dev)
     ws_enc = torch.empty(max(tdx.encode_workspace(shape, dl), 16), dtype=torch.uint8, device=dev)
     ws_att = torch.empty(max(tdx.restore_attn_workspace(shape, dl, max_priv), 16), dtype=torch.uint8, device=dev)
@@ -192,7 +194,8 @@ def main():
         mark(2)
         tdx.diff_encode(shape, dl, sel["master"], ak, av, out=ds, check=False, ws=ws_enc)
         mark(3)
-        tdx.restore_attn(shape, dl, q, po, pk, pv, max_priv, ds.master_k, ds.master_v, ds, out=out, ws=ws_att)
+        tdx.restore_attn(shape, dl, q, po, pk, pv, max_priv, ak, av, ds, out=out, ws=ws_att,
+                         master_sel=sel["master"])
         mark(4)
 
     for _ in range(args.warmup):
@@ -223,7 +226,7 @@ def main():
         ws_d = torch.empty(max(tdx.decode_attn_dense_workspace(shape, dl, max_priv), 16), dtype=torch.uint8, device=dev)
 
         def dense_step():
-            tdx.restore_dense(shape, dl, ds.master_k, ds.master_v, ds, kd, vd)
+            tdx.restore_dense(shape, dl, ak, av, ds, kd, vd, master_sel=sel["master"])
             tdx.decode_attn_dense(shape, dl, q, po, pk, pv, max_priv, kd, vd, out=outd, ws=ws_d)
 
         for _ in range(max(1, args.warmup)):

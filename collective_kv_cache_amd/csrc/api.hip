@@ -32,6 +32,7 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 #define REQ(cond, code, ...)                 \
   do {                                       \
@@ -219,6 +220,7 @@ size_t tdx_restore_attn_workspace(const tdx_shape* shape, const tdx_layout* layo
 int tdx_restore_attn(const tdx_shape* shape, const tdx_layout* layout, const void* q,
                      const int32_t* priv_off, const void* priv_k, const void* priv_v,
                      int32_t max_priv, const void* master_k, const void* master_v,
+                     const int32_t* master_sel, int64_t master_stride,
                      const int32_t* diff_off, const int32_t* diff_idx, const void* diff_k,
                      const void* diff_v, float scale, void* out, void* ws, size_t ws_bytes,
                      void* stream) {
@@ -239,6 +241,9 @@ int tdx_restore_attn(const tdx_shape* shape, const tdx_layout* layout, const voi
   }
   REQ_PTR(master_k);
   REQ_PTR(master_v);
+  REQ(master_sel == nullptr || aligned4(master_sel), TDX_EINVAL, "master_sel not 4-byte aligned");
+  REQ(master_sel == nullptr || (master_stride >= 0 && master_stride % (d.dtype == TDX_BF16 ? 8 : 4) == 0),
+      TDX_EINVAL, "master_stride %lld is negative or breaks 16-byte alignment", (long long)master_stride);
   REQ_PTR4(diff_off);
   // diff arrays may be empty (all rows empty) but must then still be valid
   // pointers to zero-length storage; they are only read through diff_off.
@@ -248,16 +253,18 @@ int tdx_restore_attn(const tdx_shape* shape, const tdx_layout* layout, const voi
   const size_t need = tdx::restore_attn_ws_bytes(d, max_priv);
   REQ(ws != nullptr && aligned16(ws) && ws_bytes >= need, TDX_EWORKSPACE,
       "workspace needs %zu bytes (16-byte aligned), got %zu", need, ws_bytes);
-  hipError_t e = tdx::launch_restore_attn(d, *layout, q, priv_off, priv_k, priv_v, max_priv,
-                                          master_k, master_v, diff_off, diff_idx, diff_k, diff_v,
-                                          scale, out, ws, static_cast<hipStream_t>(stream));
+  const tdx::MasterRef mref{master_k, master_v, master_sel, master_sel ? master_stride : 0};
+  hipError_t e = tdx::launch_restore_attn(d, *layout, q, priv_off, priv_k, priv_v, max_priv, mref,
+                                          diff_off, diff_idx, diff_k, diff_v, scale, out, ws,
+                                          static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "tdx_restore_attn launch");
   return ok();
   GUARD_END
 }
 
 int tdx_restore_dense(const tdx_shape* shape, const tdx_layout* layout, const void* master_k,
-                      const void* master_v, const int32_t* diff_off, const int32_t* diff_idx,
+                      const void* master_v, const int32_t* master_sel, int64_t master_stride,
+                      const int32_t* diff_off, const int32_t* diff_idx,
                       const void* diff_k, const void* diff_v, void* k_dense, void* v_dense,
                       void* stream) {
   GUARD_BEGIN
@@ -268,14 +275,17 @@ int tdx_restore_dense(const tdx_shape* shape, const tdx_layout* layout, const vo
   REQ(d.T % TDX_DIFF_BLOCK == 0, TDX_EINVAL, "n_tokens %d is not a multiple of 16", d.T);
   REQ_PTR(master_k);
   REQ_PTR(master_v);
+  REQ(master_sel == nullptr || aligned4(master_sel), TDX_EINVAL, "master_sel not 4-byte aligned");
+  REQ(master_sel == nullptr || (master_stride >= 0 && master_stride % (d.dtype == TDX_BF16 ? 8 : 4) == 0),
+      TDX_EINVAL, "master_stride %lld is negative or breaks 16-byte alignment", (long long)master_stride);
   REQ_PTR4(diff_off);
   REQ(diff_idx != nullptr && diff_k != nullptr && diff_v != nullptr, TDX_EINVAL, "diff arrays are null");
   REQ(aligned16(diff_k) && aligned16(diff_v), TDX_EINVAL, "diff_k/diff_v not 16-byte aligned");
   REQ_PTR(k_dense);
   REQ_PTR(v_dense);
-  hipError_t e = tdx::launch_restore_dense(d, *layout, master_k, master_v, diff_off, diff_idx,
-                                           diff_k, diff_v, k_dense, v_dense,
-                                           static_cast<hipStream_t>(stream));
+  const tdx::MasterRef mref{master_k, master_v, master_sel, master_sel ? master_stride : 0};
+  hipError_t e = tdx::launch_restore_dense(d, *layout, mref, diff_off, diff_idx, diff_k, diff_v,
+                                           k_dense, v_dense, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "tdx_restore_dense launch");
   return ok();
   GUARD_END

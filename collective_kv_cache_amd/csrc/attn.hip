@@ -125,6 +125,14 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
+// Element offset of the Master's cache: (*sel clamped to [0, N)) * stride,
+// 0 without a selector.
+__device__ __forceinline__ size_t master_offset(const int32_t* sel, long long stride, int N) {
+  if (sel == nullptr) return 0;
+  const int m = min(max(sel[0], 0), N - 1);
+  return (size_t)m * (size_t)stride;
+}
+
 // Largest b in [0, B) with blk[b] <= t (the block holding token t; skips
 // empty blocks).  blk is an LDS copy of blk_start.
 __device__ __forceinline__ int block_of(const int32_t* blk, int B, int t) {
@@ -203,6 +211,8 @@ struct AttnArgs {
   const void* pk;            // [L][Ptot][Hkv][D]
   const void* pv;
   const void* sk;            // fused: Master [L][T][Hkv][D]; dense: [N][L][T][Hkv][D]
+  const int32_t* msel;       // fused: Master at sk/sv + (*msel) * mstride (null: + 0)
+  long long mstride;
   const void* sv;
   const int32_t* diff_off;   // fused: [N*L+1]
   const int32_t* diff_idx;
@@ -381,8 +391,9 @@ __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(3)))
   st.init();
 
   const size_t rowHD = (size_t)a.Hkv * D;
-  const E* mk = static_cast<const E*>(a.sk) + (size_t)l * a.T * rowHD + (size_t)h * D;
-  const E* mv = static_cast<const E*>(a.sv) + (size_t)l * a.T * rowHD + (size_t)h * D;
+  const size_t moff = master_offset(a.msel, a.mstride, a.N);
+  const E* mk = static_cast<const E*>(a.sk) + moff + (size_t)l * a.T * rowHD + (size_t)h * D;
+  const E* mv = static_cast<const E*>(a.sv) + moff + (size_t)l * a.T * rowHD + (size_t)h * D;
   auto stage_load = [&](int beta, u32x4* r) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
@@ -811,7 +822,8 @@ constexpr int kMaxTileBlocks = kTile;  // a 16-token tile touches at most 16 blo
 
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void restore_dense_kernel(
-    const E* __restrict__ mk, const E* __restrict__ mv, const int32_t* __restrict__ diff_off,
+    const E* __restrict__ mk, const E* __restrict__ mv, const int32_t* __restrict__ msel,
+    long long mstride, const int32_t* __restrict__ diff_off,
     const int32_t* __restrict__ diff_idx, const E* __restrict__ dk, const E* __restrict__ dv,
     const int32_t* __restrict__ blk_start, const int32_t* __restrict__ src_pos,
     const int32_t* __restrict__ dst_pos, int N, int B, int T, int L, int Hkv, double theta,
@@ -827,6 +839,9 @@ __global__ __launch_bounds__(kThreads) void restore_dense_kernel(
   const int i = blockIdx.y;
   const int tid = threadIdx.x;
   const int t0 = beta * kTile;
+  const size_t moff = master_offset(msel, mstride, N);
+  mk += moff;
+  mv += moff;
   if (tid == 0) {
     int lo = 0, hi = B - 1;
     while (lo < hi) {
@@ -1018,13 +1033,15 @@ size_t dense_attn_ws_bytes(const Dims& d, int max_priv) { return make_plan(d, ma
 
 hipError_t launch_restore_attn(const Dims& d, const tdx_layout& lay, const void* q,
                                const int32_t* priv_off, const void* pk, const void* pv,
-                               int max_priv, const void* mk, const void* mv,
+                               int max_priv, const MasterRef& master,
                                const int32_t* diff_off, const int32_t* diff_idx, const void* dk,
                                const void* dv, float scale, void* out, void* ws, hipStream_t s) {
   const Plan p = make_plan(d, max_priv, true);
   AttnArgs a = common_args(d, q, priv_off, pk, pv, scale, ws);
-  a.sk = mk;
-  a.sv = mv;
+  a.sk = master.k;
+  a.sv = master.v;
+  a.msel = master.sel;
+  a.mstride = master.stride;
   a.diff_off = diff_off;
   a.diff_idx = diff_idx;
   a.dk = dk;
@@ -1043,14 +1060,14 @@ hipError_t launch_restore_attn(const Dims& d, const tdx_layout& lay, const void*
   return dispatch_attn<FUSED>(d, a, p, out, s);
 }
 
-hipError_t launch_restore_dense(const Dims& d, const tdx_layout& lay, const void* mk,
-                                const void* mv, const int32_t* diff_off,
-                                const int32_t* diff_idx, const void* dk, const void* dv,
-                                void* kd, void* vd, hipStream_t s) {
+hipError_t launch_restore_dense(const Dims& d, const tdx_layout& lay, const MasterRef& master,
+                                const int32_t* diff_off, const int32_t* diff_idx, const void* dk,
+                                const void* dv, void* kd, void* vd, hipStream_t s) {
   dim3 grid(d.T / kTile, d.N);
 #define TDX_RD(E, DD)                                                                          \
   hipLaunchKernelGGL((restore_dense_kernel<E, DD>), grid, dim3(kThreads), 0, s,               \
-                     static_cast<const E*>(mk), static_cast<const E*>(mv), diff_off, diff_idx, \
+                     static_cast<const E*>(master.k), static_cast<const E*>(master.v),         \
+                     master.sel, (long long)master.stride, diff_off, diff_idx,                 \
                      static_cast<const E*>(dk), static_cast<const E*>(dv), lay.blk_start,      \
                      lay.src_pos, lay.dst_pos, d.N, d.B, d.T, d.L, d.Hkv, d.theta,             \
                      static_cast<E*>(kd), static_cast<E*>(vd))

@@ -116,15 +116,24 @@ hipError_t launch_encode(const Dims& d, const int32_t* master, const void* ak, c
                          hipStream_t s);
 
 size_t restore_attn_ws_bytes(const Dims& d, int max_priv);
+// The Master's cache: k/v + m * stride elements, m = *sel clamped to [0, N)
+// (m = 0 when sel is null).
+struct MasterRef {
+  const void* k;
+  const void* v;
+  const int32_t* sel;
+  int64_t stride;
+};
+
 hipError_t launch_restore_attn(const Dims& d, const tdx_layout& lay, const void* q,
                                const int32_t* priv_off, const void* pk, const void* pv,
-                               int max_priv, const void* mk, const void* mv,
+                               int max_priv, const MasterRef& master,
                                const int32_t* diff_off, const int32_t* diff_idx,
                                const void* dk, const void* dv, float scale, void* out, void* ws,
                                hipStream_t s);
 
-hipError_t launch_restore_dense(const Dims& d, const tdx_layout& lay, const void* mk,
-                                const void* mv, const int32_t* diff_off,
+hipError_t launch_restore_dense(const Dims& d, const tdx_layout& lay, const MasterRef& master,
+                                const int32_t* diff_off,
                                 const int32_t* diff_idx, const void* dk, const void* dv,
                                 void* kd, void* vd, hipStream_t s);
 

@@ -6,13 +6,14 @@
 // (indices, values), one record per Mirror per layer.
 //
 // Kernels (all deterministic, no atomics on the data path):
-//  flag_kernel    one workgroup per (block beta, layer l): the Master block's
-//                 K and V sit in registers (16-byte chunks per lane); every
-//                 Mirror block is streamed once and compared bit for bit; a
-//                 workgroup-wide OR decides the flag.  Optionally writes the
+//  flag_kernel    one workgroup per (block beta, layer l, chunk slice): the
+//                 Master block's K and V sit in registers (16-byte chunks per
+//                 lane); every Mirror block is streamed once through a register
+//                 pipeline and compared bit for bit.  Optionally writes the
 //                 dense Master copy from the same registers.
-//  rows_kernel    one workgroup per CSR row (agent, layer): count of flagged
-//                 blocks and each block's rank inside its row.
+//  rows_kernel    one workgroup per CSR row (agent, layer): OR of the slices'
+//                 flags, count of flagged blocks and each block's rank inside
+//                 its row.
 //  offsets_kernel one workgroup: exclusive scan of the row counts -> row
 //                 offsets and the true total nnz.
 //  copy_kernel    one workgroup per (row, 8-block chunk): writes the ascending
@@ -27,88 +28,107 @@ constexpr int kThreads = 256;
 constexpr int kFlagThreads = 1024;
 constexpr int kCopyChunk = 8;
 constexpr int kScanThreads = 1024;
+constexpr int kMaxAgents = 1024;
 
-// KC = 16-byte chunks per thread per tensor for one 16-token block.  The
-// Master block stays in registers; each thread ORs the XOR of every Mirror
-// chunk into one bit per agent (64 agents per pass), so consecutive Mirrors'
-// loads overlap; one workgroup-wide OR per pass decides the flags.
-template <int KC>
+// One workgroup per (block beta, layer l, chunk slice cs): the slice's
+// 16-byte chunks of the Master block sit in registers (KC per thread and
+// tensor) and the Mirrors' blocks stream through a PD-stage register
+// pipeline: while Mirror j is compared, Mirrors j+1 .. j+PD-1 are in flight.
+// The unrolled body has no branch around a load, so the wait before each
+// compare leaves the younger Mirrors' loads outstanding.  A wave that sees a
+// difference marks the Mirror in LDS; the marks become the slice's flags.
+template <int KC, int PD>
 __global__ __launch_bounds__(kFlagThreads) void flag_kernel(
     const u32x4* __restrict__ ak, const u32x4* __restrict__ av,
     const int32_t* __restrict__ master_p, int N, int L, int nb, int chunks,
     uint8_t* __restrict__ flags, u32x4* __restrict__ mk_out, u32x4* __restrict__ mv_out) {
-  constexpr int W = kFlagThreads / kWave;
-  __shared__ unsigned long long wmask[W];
+  __shared__ uint8_t mark[kMaxAgents];
   const int beta = blockIdx.x;
   const int l = blockIdx.y;
+  const int cs = blockIdx.z;
   const int tid = threadIdx.x;
-  const int lane = tid % kWave, wave = tid / kWave;
+  const int lane = tid % kWave;
   const int m = master_p[0];
+  uint8_t* fl = flags + (size_t)cs * N * L * nb;
   if (m < 0 || m >= N) {  // invalid Master: no reads; offsets_kernel reports nnz = -1
-    for (int i = tid; i < N; i += kFlagThreads) flags[((size_t)i * L + l) * nb + beta] = 0;
+    for (int i = tid; i < N; i += kFlagThreads) fl[((size_t)i * L + l) * nb + beta] = 0;
     return;
   }
+  for (int i = tid; i < N; i += kFlagThreads) mark[i] = 0;
+  // this thread's chunks c0 + tid + 1024 j of the slice; lanes past the block
+  // end re-read its last chunk (the compare then sees equal data)
+  const int c0 = cs * KC * kFlagThreads;
+  int cidx[KC];
+#pragma unroll
+  for (int j = 0; j < KC; ++j) cidx[j] = min(c0 + tid + j * kFlagThreads, chunks - 1);
   // chunk offset of (agent a, layer l, block beta): ((a*L + l)*nb + beta)*chunks
   const size_t layer_chunks = (size_t)nb * chunks;
   const size_t mbase = ((size_t)m * L + l) * layer_chunks + (size_t)beta * chunks;
   u32x4 mkr[KC], mvr[KC];
 #pragma unroll
   for (int j = 0; j < KC; ++j) {
-    const int c = tid + j * kFlagThreads;
-    if (c < chunks) {
-      mkr[j] = ak[mbase + c];
-      mvr[j] = av[mbase + c];
-    }
+    mkr[j] = ak[mbase + cidx[j]];
+    mvr[j] = av[mbase + cidx[j]];
   }
   if (mk_out != nullptr) {
     const size_t obase = (size_t)l * layer_chunks + (size_t)beta * chunks;
 #pragma unroll
     for (int j = 0; j < KC; ++j) {
-      const int c = tid + j * kFlagThreads;
+      const int c = c0 + tid + j * kFlagThreads;
       if (c < chunks) {
         __builtin_nontemporal_store(mkr[j], mk_out + obase + c);
         __builtin_nontemporal_store(mvr[j], mv_out + obase + c);
       }
     }
   }
-  for (int i0 = 0; i0 < N; i0 += 64) {
-    const int iend = min(i0 + 64, N);
-    unsigned long long bits = 0;
-#pragma unroll 2
-    for (int i = i0; i < iend; ++i) {
-      if (i == m) continue;  // uniform
-      const size_t base = ((size_t)i * L + l) * layer_chunks + (size_t)beta * chunks;
+  __syncthreads();  // marks cleared
+  const int nm = N - 1;  // Mirror j is agent j + (j >= m)
+  if (nm > 0) {
+    struct Blk {
+      u32x4 k[KC], v[KC];
+    };
+    Blk S[PD] = {};
+    auto load = [&](int j, Blk& B) {
+      const int a = j + (j >= m);
+      const size_t base = ((size_t)a * L + l) * layer_chunks + (size_t)beta * chunks;
+#pragma unroll
+      for (int q = 0; q < KC; ++q) {
+        B.k[q] = ak[base + cidx[q]];
+        B.v[q] = av[base + cidx[q]];
+      }
+    };
+    auto compare = [&](const Blk& B, int j, bool live) {
       uint32_t acc = 0;
 #pragma unroll
-      for (int j = 0; j < KC; ++j) {
-        const int c = tid + j * kFlagThreads;
-        if (c < chunks) {
-          const u32x4 xk = ak[base + c] ^ mkr[j];
-          const u32x4 xv = av[base + c] ^ mvr[j];
-          acc |= xk[0] | xk[1] | xk[2] | xk[3] | xv[0] | xv[1] | xv[2] | xv[3];
-        }
+      for (int q = 0; q < KC; ++q) {
+        const u32x4 xk = B.k[q] ^ mkr[q];
+        const u32x4 xv = B.v[q] ^ mvr[q];
+        acc |= xk[0] | xk[1] | xk[2] | xk[3] | xv[0] | xv[1] | xv[2] | xv[3];
       }
-      bits |= (unsigned long long)(acc != 0) << (i - i0);
+      if (__builtin_amdgcn_ballot_w64(live && acc != 0) != 0 && lane == 0) mark[j + (j >= m)] = 1;
+    };
+    for (int j0 = -(PD - 1); j0 < nm; j0 += PD) {
+#pragma unroll
+      for (int k = 0; k < PD; ++k) {
+        const int j = j0 + k;  // Mirror compared in this step (wave-uniform)
+        load(min(j + PD - 1, nm - 1), S[(k + PD - 1) % PD]);
+        compare(S[k], j, j >= 0 && j < nm);
+      }
     }
-    // OR over the workgroup
-    for (int o = kWave / 2; o > 0; o >>= 1) bits |= __shfl_xor(bits, o, kWave);
-    if (lane == 0) wmask[wave] = bits;
-    __syncthreads();
-    if (tid < iend - i0) {
-      unsigned long long all = 0;
-      for (int w = 0; w < W; ++w) all |= wmask[w];
-      flags[((size_t)(i0 + tid) * L + l) * nb + beta] = (uint8_t)((all >> tid) & 1ull);
-    }
-    __syncthreads();
   }
+  __syncthreads();
+  for (int i = tid; i < N; i += kFlagThreads) fl[((size_t)i * L + l) * nb + beta] = mark[i];
 }
 
 __device__ __forceinline__ int lanemask_count(uint64_t m, int lane) {
   return __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
 }
 
-// In-row exclusive ranks of the flagged blocks and the row count.
-__global__ __launch_bounds__(kThreads) void rows_kernel(const uint8_t* __restrict__ flags, int nb,
+// In-row exclusive ranks of the flagged blocks and the row count.  With
+// several chunk slices the block flag is the OR of the slices' flags; it is
+// stored back into slice 0 for copy_kernel.
+__global__ __launch_bounds__(kThreads) void rows_kernel(uint8_t* __restrict__ flags, int nb,
+                                                        int nslices, size_t slice_stride,
                                                         int32_t* __restrict__ rank,
                                                         int32_t* __restrict__ count) {
   constexpr int W = kThreads / kWave;
@@ -118,7 +138,11 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(const uint8_t* __restric
   int carry = 0;
   for (int base = 0; base < nb; base += kThreads) {
     const int beta = base + tid;
-    const bool f = beta < nb && flags[r * nb + beta] != 0;
+    bool f = false;
+    if (beta < nb) {
+      for (int c = 0; c < nslices; ++c) f |= flags[c * slice_stride + r * nb + beta] != 0;
+      if (nslices > 1) flags[r * nb + beta] = f ? 1 : 0;
+    }
     const uint64_t m = __ballot(f);
     if (lane == 0) wcnt[wave] = __popcll(m);
     __syncthreads();
@@ -196,13 +220,22 @@ struct WsLayout {
   size_t flags, rank, count, total;
 };
 
+int block_chunks(const Dims& d) {  // 16-byte chunks per block per tensor
+  return kBlock * d.Hkv * d.D * (d.dtype == TDX_BF16 ? 2 : 4) / 16;
+}
+int flag_kc(const Dims& d) { return block_chunks(d) <= kFlagThreads ? 1 : 2; }
+int flag_slices(const Dims& d) {
+  const int per = flag_kc(d) * kFlagThreads;
+  return (block_chunks(d) + per - 1) / per;
+}
+
 WsLayout ws_layout(const Dims& d) {
   const size_t rows = (size_t)d.N * d.L;
   const size_t nb = (size_t)(d.T / kBlock);
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   WsLayout w;
   w.flags = 0;
-  w.rank = up(rows * nb);
+  w.rank = up(rows * nb * flag_slices(d));
   w.count = w.rank + up(rows * nb * 4);
   w.total = w.count + up(rows * 4);
   return w;
@@ -217,8 +250,7 @@ hipError_t launch_encode(const Dims& d, const int32_t* master, const void* ak, c
                          void* diff_v, int64_t* nnz, void* mk_out, void* mv_out, void* ws,
                          hipStream_t s) {
   const int nb = d.T / kBlock;
-  const int eb = d.dtype == TDX_BF16 ? 2 : 4;
-  const int chunks = kBlock * d.Hkv * d.D * eb / 16;  // 16-byte chunks per block per tensor
+  const int chunks = block_chunks(d);
   const int rows = d.N * d.L;
   const WsLayout w = ws_layout(d);
   uint8_t* flags = static_cast<uint8_t*>(ws) + w.flags;
@@ -229,21 +261,18 @@ hipError_t launch_encode(const Dims& d, const int32_t* master, const void* ak, c
   u32x4* mk4 = static_cast<u32x4*>(mk_out);
   u32x4* mv4 = static_cast<u32x4*>(mv_out);
   {
-    const int kc = (chunks + kFlagThreads - 1) / kFlagThreads;
-    dim3 grid(nb, d.L);
-#define TDX_FLAG(KC)                                                                             \
-  hipLaunchKernelGGL(flag_kernel<KC>, grid, dim3(kFlagThreads), 0, s, k4, v4, master, d.N, d.L, \
-                     nb, chunks, flags, mk4, mv4)
-    if (kc <= 1) TDX_FLAG(1);
-    else if (kc <= 2) TDX_FLAG(2);
-    else if (kc <= 4) TDX_FLAG(4);
-    else if (kc <= 8) TDX_FLAG(8);
-    else if (kc <= 16) TDX_FLAG(16);
-    else return hipErrorInvalidValue;
-#undef TDX_FLAG
+    const int ns = flag_slices(d);
+    dim3 grid(nb, d.L, ns);
+    if (flag_kc(d) == 1)
+      hipLaunchKernelGGL((flag_kernel<1, 8>), grid, dim3(kFlagThreads), 0, s, k4, v4, master, d.N, d.L, nb,
+                         chunks, flags, mk4, mv4);
+    else
+      hipLaunchKernelGGL((flag_kernel<2, 4>), grid, dim3(kFlagThreads), 0, s, k4, v4, master, d.N, d.L, nb,
+                         chunks, flags, mk4, mv4);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(rows_kernel, dim3(rows), dim3(kThreads), 0, s, flags, nb, rank, count);
+    hipLaunchKernelGGL(rows_kernel, dim3(rows), dim3(kThreads), 0, s, flags, nb, ns, (size_t)rows * nb, rank,
+                       count);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(kScanThreads), 0, s, count, rows, diff_off, nnz,

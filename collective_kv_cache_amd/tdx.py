@@ -67,8 +67,9 @@ _SIGS = {
     "tdx_diff_encode_workspace": (_SZ, [_PS, _PL]),
     "tdx_diff_encode": (ctypes.c_int, [_PS, _PL, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "tdx_restore_attn_workspace": (_SZ, [_PS, _PL, _I32]),
-    "tdx_restore_attn": (ctypes.c_int, [_PS, _PL, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _F, _P, _P, _SZ, _P]),
-    "tdx_restore_dense": (ctypes.c_int, [_PS, _PL, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "tdx_restore_attn": (ctypes.c_int, [_PS, _PL, _P, _P, _P, _P, _I32, _P, _P, _P, _I64, _P, _P, _P, _P, _F, _P,
+                                        _P, _SZ, _P]),
+    "tdx_restore_dense": (ctypes.c_int, [_PS, _PL, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "tdx_decode_attn_dense_workspace": (_SZ, [_PS, _PL, _I32]),
     "tdx_decode_attn_dense": (ctypes.c_int, [_PS, _PL, _P, _P, _P, _P, _I32, _P, _P, _F, _P, _P, _SZ, _P]),
 }
@@ -285,11 +286,30 @@ def restore_attn_workspace(shape: Shape, lay: RoundLayout, max_priv: int) -> int
     return int(lib().tdx_restore_attn_workspace(ctypes.byref(s), ctypes.byref(l), int(max_priv)))
 
 
+def _master_args(shape: Shape, lay: RoundLayout, master_k, master_v, master_sel):
+    """(k, v, sel, stride): master_k/v are either the Master's own cache
+    [L][T][Hkv][D] (master_sel None) or every agent's cache [N][L][T][Hkv][D]
+    with the device int32 [1] ``master_sel`` naming the Master (read in place)."""
+    N, L, T, H, D = lay.n_agents, shape.n_layers, lay.n_tokens, shape.n_kv_heads, shape.head_dim
+    dev_ = lay.device
+    if master_sel is None:
+        _need(master_k, "master_k", shape.dtype, (L, T, H, D), dev_)
+        _need(master_v, "master_v", shape.dtype, (L, T, H, D), dev_)
+        return master_k, master_v, None, 0
+    _need(master_sel, "master_sel", torch.int32, (1,), dev_)
+    _need(master_k, "master_k", shape.dtype, (N, L, T, H, D), dev_)
+    _need(master_v, "master_v", shape.dtype, (N, L, T, H, D), dev_)
+    return master_k, master_v, master_sel, L * T * H * D
+
+
 def restore_attn(shape: Shape, lay: RoundLayout, q: torch.Tensor, priv_off: torch.Tensor,
                  priv_k: torch.Tensor, priv_v: torch.Tensor, max_priv: int,
                  master_k: torch.Tensor, master_v: torch.Tensor, diff: DiffSet,
-                 scale: Optional[float] = None, out: Optional[torch.Tensor] = None, ws=None):
-    """a5: fused restore + decode attention -> [N][L][Hq][D]."""
+                 scale: Optional[float] = None, out: Optional[torch.Tensor] = None, ws=None,
+                 master_sel: Optional[torch.Tensor] = None):
+    """a5: fused restore + decode attention -> [N][L][Hq][D].  The Master is
+    ``master_k``/``master_v`` ([L][T][Hkv][D]), or, with ``master_sel``, entry
+    ``master_sel[0]`` of the [N][L][T][Hkv][D] agent caches, read in place."""
     N, L, T, H, Hq, D = (lay.n_agents, shape.n_layers, lay.n_tokens, shape.n_kv_heads,
                          shape.n_q_heads, shape.head_dim)
     dev_ = lay.device
@@ -299,8 +319,7 @@ def restore_attn(shape: Shape, lay: RoundLayout, q: torch.Tensor, priv_off: torc
     _need(priv_v, "priv_v", shape.dtype, tuple(priv_k.shape), dev_)
     if priv_k.dim() != 4 or priv_k.shape[0] != L or tuple(priv_k.shape[2:]) != (H, D):
         raise ValueError("priv_k must be [L][P_total][Hkv][D]")
-    _need(master_k, "master_k", shape.dtype, (L, T, H, D), dev_)
-    _need(master_v, "master_v", shape.dtype, (L, T, H, D), dev_)
+    mk, mv, msel, mstride = _master_args(shape, lay, master_k, master_v, master_sel)
     if out is None:
         out = torch.empty((N, L, Hq, D), dtype=shape.dtype, device=dev_)
     _need(out, "out", shape.dtype, (N, L, Hq, D), dev_)
@@ -310,7 +329,7 @@ def restore_attn(shape: Shape, lay: RoundLayout, q: torch.Tensor, priv_off: torc
     s, l = shape.c(), lay.c()
     _check(lib().tdx_restore_attn(
         ctypes.byref(s), ctypes.byref(l), _ptr(q), _ptr(priv_off), _ptr(priv_k), _ptr(priv_v),
-        int(max_priv), _ptr(master_k), _ptr(master_v), _ptr(diff.off), _ptr(diff.idx),
+        int(max_priv), _ptr(mk), _ptr(mv), _ptr(msel), mstride, _ptr(diff.off), _ptr(diff.idx),
         _ptr(diff.k), _ptr(diff.v), scale, _ptr(out), _ptr(ws), ws.numel(), _stream()),
         "tdx_restore_attn")
     return out
@@ -318,12 +337,12 @@ def restore_attn(shape: Shape, lay: RoundLayout, q: torch.Tensor, priv_off: torc
 
 def restore_dense(shape: Shape, lay: RoundLayout, master_k: torch.Tensor, master_v: torch.Tensor,
                   diff: DiffSet, k_dense: Optional[torch.Tensor] = None,
-                  v_dense: Optional[torch.Tensor] = None):
-    """a6 first half: every agent's dense cache, K rotated to its offsets."""
+                  v_dense: Optional[torch.Tensor] = None, master_sel: Optional[torch.Tensor] = None):
+    """a6 first half: every agent's dense cache, K rotated to its offsets
+    (Master given as for :func:`restore_attn`)."""
     N, L, T, H, D = lay.n_agents, shape.n_layers, lay.n_tokens, shape.n_kv_heads, shape.head_dim
     dev_ = lay.device
-    _need(master_k, "master_k", shape.dtype, (L, T, H, D), dev_)
-    _need(master_v, "master_v", shape.dtype, (L, T, H, D), dev_)
+    mk, mv, msel, mstride = _master_args(shape, lay, master_k, master_v, master_sel)
     if k_dense is None:
         k_dense = torch.empty((N, L, T, H, D), dtype=shape.dtype, device=dev_)
     if v_dense is None:
@@ -332,7 +351,7 @@ def restore_dense(shape: Shape, lay: RoundLayout, master_k: torch.Tensor, master
     _need(v_dense, "v_dense", shape.dtype, (N, L, T, H, D), dev_)
     s, l = shape.c(), lay.c()
     _check(lib().tdx_restore_dense(
-        ctypes.byref(s), ctypes.byref(l), _ptr(master_k), _ptr(master_v), _ptr(diff.off),
+        ctypes.byref(s), ctypes.byref(l), _ptr(mk), _ptr(mv), _ptr(msel), mstride, _ptr(diff.off),
         _ptr(diff.idx), _ptr(diff.k), _ptr(diff.v), _ptr(k_dense), _ptr(v_dense), _stream()),
         "tdx_restore_dense")
     return k_dense, v_dense

@@ -169,7 +169,14 @@ size_t tdx_diff_encode_workspace(const tdx_shape *shape, const tdx_layout *layou
  *   priv_off   [N+1] device int32 offsets into the private arrays
  *   priv_k/v   [L][P_total][Hkv][D], agent i owns rows priv_off[i]..priv_off[i+1]
  *   max_priv   host scalar >= max_i (priv_off[i+1] - priv_off[i])
- *   master_k/v [L][T][Hkv][D]; T % 16 == 0
+ *   master_k/v the Master's cache, [L][T][Hkv][D] (T % 16 == 0), found at
+ *              master_k + m * master_stride elements (same for v), where
+ *              m = *master_sel (device int32, clamped to [0, N)) or m = 0 when
+ *              master_sel is NULL.  Pass the dense copy written by
+ *              tdx_diff_encode with master_sel = NULL, or read the Master in
+ *              place: master_k = agents_k, master_sel = the Master chosen by
+ *              tdx_select_important, master_stride = L*T*Hkv*D (the Master
+ *              keeps its own cache, notes Figure 8).
  *   diff_off / diff_idx / diff_k / diff_v  as written by tdx_diff_encode
  *   scale      softmax scale (> 0), usually 1/sqrt(D)
  *   out        [N][L][Hq][D] */
@@ -177,6 +184,7 @@ int tdx_restore_attn(const tdx_shape *shape, const tdx_layout *layout,
                      const void *q, const int32_t *priv_off,
                      const void *priv_k, const void *priv_v, int32_t max_priv,
                      const void *master_k, const void *master_v,
+                     const int32_t *master_sel, int64_t master_stride,
                      const int32_t *diff_off, const int32_t *diff_idx,
                      const void *diff_k, const void *diff_v, float scale,
                      void *out, void *ws, size_t ws_bytes, void *stream);
@@ -193,6 +201,7 @@ size_t tdx_restore_attn_workspace(const tdx_shape *shape, const tdx_layout *layo
  * measured against (notes §3d, §7b). */
 int tdx_restore_dense(const tdx_shape *shape, const tdx_layout *layout,
                       const void *master_k, const void *master_v,
+                      const int32_t *master_sel, int64_t master_stride,
                       const int32_t *diff_off, const int32_t *diff_idx,
                       const void *diff_k, const void *diff_v, void *k_dense,
                       void *v_dense, void *stream);

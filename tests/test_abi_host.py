@@ -135,11 +135,17 @@ def test_encode_rejects_bad_arguments():
     assert _encode(ws_bytes=0) == tdx.TDX_EWORKSPACE
 
 
-def _restore(T=64, scale=0.1, max_priv=10, ws_bytes=1 << 30, hq=28):
+def _restore(T=64, scale=0.1, max_priv=10, ws_bytes=1 << 30, hq=28, msel=None, mstride=0):
     s, l = _shape(n_q_heads=hq), _layout(n_tokens=T)
     return tdx.lib().tdx_restore_attn(ctypes.byref(s), ctypes.byref(l), FAKE, FAKE, FAKE, FAKE, max_priv,
-                                      FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(scale), FAKE,
-                                      FAKE, ws_bytes, None)
+                                      FAKE, FAKE, msel, mstride, FAKE, FAKE, FAKE, FAKE,
+                                      ctypes.c_float(scale), FAKE, FAKE, ws_bytes, None)
+
+
+def _restore_dense(msel=None, mstride=0):
+    s, l = _shape(), _layout(n_tokens=64)
+    return tdx.lib().tdx_restore_dense(ctypes.byref(s), ctypes.byref(l), FAKE, FAKE, msel, mstride, FAKE,
+                                       FAKE, FAKE, FAKE, FAKE, FAKE, None)
 
 
 def test_restore_rejects_bad_arguments():
@@ -148,3 +154,9 @@ def test_restore_rejects_bad_arguments():
     assert _restore(max_priv=-1) == tdx.TDX_EINVAL
     assert _restore(ws_bytes=0) == tdx.TDX_EWORKSPACE
     assert _restore(hq=4 * 17) == tdx.TDX_EUNSUPPORTED  # 17 query heads per KV head
+    # the Master selector: aligned pointer, stride >= 0 keeping 16-byte alignment (bf16: % 8)
+    assert _restore(msel=ctypes.c_void_p(0x10002)) == tdx.TDX_EINVAL
+    assert _restore(msel=FAKE, mstride=-8) == tdx.TDX_EINVAL
+    assert _restore(msel=FAKE, mstride=12) == tdx.TDX_EINVAL
+    assert _restore_dense(msel=FAKE, mstride=12) == tdx.TDX_EINVAL
+    assert _restore_dense(msel=ctypes.c_void_p(0x10001)) == tdx.TDX_EINVAL

@@ -172,3 +172,46 @@ def test_attention_deterministic():
     b = r.gpu_fused(ds)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny", {}),
+    ("qwen7b_round", dict(n_layers=2, n_agents=4)),
+])
+def test_master_read_in_place_matches_copy(name, kw):
+    # the Master taken straight from the agents' caches through the device-side
+    # selector gives exactly what the dense Master copy gives
+    cfg = CONFIGS[name].scaled(**kw)
+    lay = make_layout(cfg)
+    r = Round(cfg, lay, master=2)
+    d = r.dev
+    ds = r.gpu_encode()
+    m = torch.tensor([2], dtype=torch.int32, device=DEV)
+    ds_nc = tdx.diff_encode(r.shape, r.dl, m, d["ak"], d["av"], master_copy=False)
+    assert ds_nc.master_k is None and ds_nc.nnz() == ds.nnz()
+    copy = host(r.gpu_fused(ds))
+    inplace = host(tdx.restore_attn(r.shape, r.dl, d["q"], d["po"], d["pk"], d["pv"], r.max_priv,
+                                    d["ak"], d["av"], ds_nc, master_sel=m))
+    np.testing.assert_array_equal(inplace, copy)
+    kd0, vd0 = tdx.restore_dense(r.shape, r.dl, ds.master_k, ds.master_v, ds)
+    kd1, vd1 = tdx.restore_dense(r.shape, r.dl, d["ak"], d["av"], ds_nc, master_sel=m)
+    np.testing.assert_array_equal(host(kd1), host(kd0))
+    np.testing.assert_array_equal(host(vd1), host(vd0))
+
+
+def test_master_selector_is_clamped():
+    # a selector outside [0, N) reads the nearest agent instead of faulting
+    cfg = CONFIGS["tiny"].scaled(n_layers=1)
+    lay = make_layout(cfg)
+    r = Round(cfg, lay, master=0)
+    d = r.dev
+    ds = r.gpu_encode()
+    N = cfg.n_agents
+
+    def run(sel):
+        m = torch.tensor([sel], dtype=torch.int32, device=DEV)
+        return host(tdx.restore_attn(r.shape, r.dl, d["q"], d["po"], d["pk"], d["pv"], r.max_priv,
+                                     d["ak"], d["av"], ds, master_sel=m))
+
+    np.testing.assert_array_equal(run(-7), run(0))
+    np.testing.assert_array_equal(run(N + 3), run(N - 1))
