@@ -105,13 +105,6 @@ __device__ __forceinline__ f32x4 mfma32(const u32x4& a, const u32x4& b, f32x4 c)
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
-// (lo, hi) -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
-}
-
 __device__ __forceinline__ f32x4 mfma16(const i16x4& a, const i16x4& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
@@ -289,8 +282,8 @@ __device__ __forceinline__ void softmax_pv(RowState<D>& st, const float z[4], co
   st.m = mnew;
   // weights in (0, 1]: v_exp_f32, then one v_cvt_pk_bf16_f32 (round to
   // nearest even) per pair; the sum uses the same rounded weights
-  const uint32_t w01 = cvt_pk_bf16(__builtin_amdgcn_exp2f(z[0] - mref), __builtin_amdgcn_exp2f(z[1] - mref));
-  const uint32_t w23 = cvt_pk_bf16(__builtin_amdgcn_exp2f(z[2] - mref), __builtin_amdgcn_exp2f(z[3] - mref));
+  const uint32_t w01 = pack_bf16(__builtin_amdgcn_exp2f(z[0] - mref), __builtin_amdgcn_exp2f(z[1] - mref));
+  const uint32_t w23 = pack_bf16(__builtin_amdgcn_exp2f(z[2] - mref), __builtin_amdgcn_exp2f(z[3] - mref));
   const float psum = (__uint_as_float(w01 << 16) + __uint_as_float(w01 & 0xffff0000u)) +
                      (__uint_as_float(w23 << 16) + __uint_as_float(w23 & 0xffff0000u));
   i16x4 pb;

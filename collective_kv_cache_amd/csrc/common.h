@@ -21,17 +21,18 @@ constexpr int kBlock = TDX_DIFF_BLOCK;  // 16-token diff block
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// fp32 -> bf16 bits, round to nearest, ties to even (NaN stays a quiet NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// (lo, hi) fp32 -> packed bf16 bits with one v_cvt_pk_bf16_f32: round to
+// nearest, ties to even, denormals kept, NaN -> quiet NaN with the upper
+// payload bits (the same bits as ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) for
+// non-NaN u and (u >> 16) | 0x40 for NaN; checked on gfx950 for all 2^32 inputs).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
-}
+// fp32 -> bf16 bits (as pack_bf16)
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16(f, 0.0f) & 0xFFFFu; }
 
 template <typename E>
 struct Fmt;

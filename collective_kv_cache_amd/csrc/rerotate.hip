@@ -23,6 +23,9 @@ constexpr int kTileTok = 16;
 constexpr int kAgentChunk = 32;  // agents whose cos/sin sit in LDS at once
 constexpr int kItems = 2;        // (token, head) rows per lane per batch
 
+#ifndef TDX_RR_TARGET_WG
+#define TDX_RR_TARGET_WG 16384
+#endif
 #ifndef TDX_RR_NT_STORES
 #define TDX_RR_NT_STORES 1
 #endif
@@ -155,7 +158,7 @@ hipError_t launch_t(const Dims& d, const tdx_layout& lay, const void* kc, void* 
                     hipStream_t s) {
   const int tiles = (d.T + kTileTok - 1) / kTileTok;
   // enough workgroups to fill 256 CUs several times over, >= 1 layer each
-  int groups = (2048 + tiles - 1) / tiles;
+  int groups = (TDX_RR_TARGET_WG + tiles - 1) / tiles;
   groups = groups < 1 ? 1 : (groups > d.L ? d.L : groups);
   const int lpg = (d.L + groups - 1) / groups;
   groups = (d.L + lpg - 1) / lpg;
