@@ -35,7 +35,43 @@ def parse():
     ap.add_argument("--config", default="qwen14b_round")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
     return ap.parse_args()
+
+
+CSRC = os.path.join(ROOT, "collective_kv_cache_amd", "csrc")
+# C-ABI entry point of each stage (one call per step; its kernels run back to back)
+ENTRY = {"rerotate": "tdx_rerotate", "select": "tdx_select_important", "encode": "tdx_diff_encode",
+         "restore_attn": "tdx_restore_attn"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_hash() -> str:
+    """sha256 over the HIP sources, to tell whether recorded counters still
+    describe the kernels being run."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(entry: str, workload: str):
+    """HBM bytes per call of `entry` from the rocprofv3 FETCH_SIZE/WRITE_SIZE
+    runs recorded in profiles/traffic.json, or None when absent or taken on
+    other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    r = rec.get(entry)
+    if not r or r.get("workload") != workload or r.get("src_sha256") != source_hash():
+        return None
+    return int(r["fetch_bytes"]) + int(r["write_bytes"])
 
 
 def stage_bytes(cfg, lay, nnz_total, k):
@@ -84,17 +120,18 @@ def compression(counts, master, T, H, D, eb, priv_len, L):
     }
 
 
-def cpu_baseline(cfg, lay, pct):
-    """The oracle on a bounded sample: layer 0 of the same round (drawn on the
-    host), all agents; the round's layers are iid, so the whole-round time is
-    the one-layer time x L (select runs once per round)."""
+def cpu_baseline(cfg, lay, pct, n_sample=8):
+    """The oracle on a bounded sample: the first ``n_sample`` layers of the same
+    round (drawn on the host), all agents; the round's layers are iid, so the
+    whole-round time is the per-layer time x L (select runs once per round)."""
     import numpy as np
     import oracle as O
     from threadpoolctl import threadpool_limits
     from workload import (cached_kv, agent_caches, queries, private_kv, recomputed_k,
                           to_numpy_bits, from_numpy_bits)
 
-    c1 = cfg.scaled(n_layers=1)
+    ns = min(n_sample, cfg.n_layers)
+    c1 = cfg.scaled(n_layers=ns)
     kc, vc = cached_kv(c1, lay)
     q = queries(c1)
     pk, pv = private_kv(c1, lay)
@@ -119,17 +156,19 @@ def cpu_baseline(cfg, lay, pct):
                        lay.src_pos, lay.dst_pos, cfg.theta, 1.0 / math.sqrt(cfg.head_dim))
         t6 = time.perf_counter()
     L = cfg.n_layers
-    per_round = (t1 - t0) * L + (t3 - t2) + (t5 - t4) * L + (t6 - t5) * L
+    f = L / ns
+    per_round = ((t1 - t0) + (t5 - t4) + (t6 - t5)) * f + (t3 - t2)
     return {
         "value": cfg.n_agents * lay.n_tokens / per_round,
         "unit": "agent-tokens/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"layer 0 of the {cfg.name} round on the host (all {cfg.n_agents} agents, "
-                   f"{lay.n_tokens} shared tokens); per-layer stages x {L} layers + one select; "
-                   f"measured {t6 - t0 - (t2 - t1) - (t4 - t3):.1f} s of oracle time"),
-        "stage_s_per_layer": {"rerotate": t1 - t0, "select_once": t3 - t2, "encode": t5 - t4,
-                              "restore_attn": t6 - t5},
+        "sample": (f"layers 0..{ns - 1} of the {cfg.name} round on the host (all {cfg.n_agents} "
+                   f"agents, {lay.n_tokens} shared tokens, the same private histories), one thread; "
+                   f"per-layer stages x {L}/{ns} + one select; measured "
+                   f"{t6 - t0 - (t2 - t1) - (t4 - t3):.1f} s of oracle time"),
+        "stage_s_per_layer": {"rerotate": (t1 - t0) / ns, "select_once": t3 - t2,
+                              "encode": (t5 - t4) / ns, "restore_attn": (t6 - t5) / ns},
         "cpu": platform.processor() or platform.machine(),
     }
 
@@ -198,6 +237,15 @@ def main():
                          master_sel=sel["master"])
         mark(4)
 
+    if args.calib_copy:
+        # a plain copy of known size (1 GiB read + 1 GiB written) for scaling
+        # the FETCH_SIZE / WRITE_SIZE counters of a rocprofv3 --pmc run
+        csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cdst = torch.empty_like(csrc)
+        for _ in range(3):
+            cdst.copy_(csrc)
+        torch.cuda.synchronize()
+        del csrc, cdst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -274,9 +322,12 @@ def main():
                    "n_q_heads": Hq, "head_dim": D, "shared_tokens": T,
                    "private_tokens_total": int(lay.priv_len.sum()), "select_k": k,
                    "diff_blocks": nnz, "master": master, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(stage_rep[dom]["GBps"], 1),
+        "roofline": {"bound": "hbm", "kernel": ENTRY[dom], "stage": dom,
+                     "achieved": round(stage_rep[dom]["GBps"], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(stage_rep[dom]["GBps"] / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(stage_rep[dom]["GBps"] / HBM_PEAK_GBS, 4),
+                     "alg_bytes": int(byts[dom]),
+                     "traffic": recorded_traffic(ENTRY[dom], cfg.name)},
         "fused_restore_attn": {"GBps": stage_rep["restore_attn"]["GBps"],
                                "frac_hbm_peak": stage_rep["restore_attn"]["frac_hbm_peak"]},
         "collective_reuse_agent_tokens_per_s": agent_tokens / (reuse_ms * 1e-3),
