@@ -8,9 +8,9 @@
 // Kernels:
 //  deviation_kernel  one wave per canonical token: for each agent the lanes
 //                    stream the (reused, recomputed) K rows with 16-byte loads,
-//                    square-sum in double, reduce each head with xor shuffles,
-//                    take the per-head norm and add the heads.  The wave sums
-//                    its token over agents in index order (score) and writes
+//                    square-sum in fp32, sum each head's lanes with DPP, take
+//                    the per-head norm and add the heads.  The wave sums its
+//                    token over agents in index order (score) and writes
 //                    per-workgroup agent partials for the Master total.
 //  select_kernel     one 1024-thread workgroup: fixed-order agent totals and
 //                    argmin, 4-pass 8-bit radix select of the k-th largest
@@ -23,86 +23,104 @@ namespace {
 
 constexpr int kDevThreads = 256;
 constexpr int kDevWaves = kDevThreads / kWave;
-constexpr int kTokPerWave = 2;
-constexpr int kTokPerWg = kDevWaves * kTokPerWave;
-constexpr int kAgentUnroll = 4;
+constexpr int kTokPerWg = kDevWaves;  // one token per wave
 constexpr int kSelThreads = 1024;
 constexpr int kMaxAgents = 1024;
+constexpr int kSelLdsKeys = 12288;  // scores kept in LDS up to this many tokens
 
 __device__ __forceinline__ double wave_sum_xor(double v, int width) {
   for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
 }
 
+// DPP lane moves within a 16-lane row (VALU, no LDS round trip)
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of G lanes (G = 8, 16 or 32), result in every lane
+// of the group; a fixed butterfly, so the order of the additions is fixed.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror: groups of 8
+  if constexpr (G >= 16) v += dpp<0x140>(v);  // row_mirror: groups of 16
+  if constexpr (G >= 32) v += __shfl_xor(v, 16, kWave);
+  return v;
+}
+
+// One wave per canonical token t: for every agent, the lanes stream the
+// (reused, recomputed) K rows with 16-byte loads (all agents of a group of
+// AU in flight together), square-sum each lane's elements in fp32,
+// sum each head's lanes with DPP, take the head norms and add the heads.
 // KCH = 16-byte chunks per lane per row (row = Hkv * D elements).
-template <typename E, int D, int KCH>
+template <typename E, int D, int KCH, int AU>
 __global__ __launch_bounds__(kDevThreads) void deviation_kernel(
     const E* __restrict__ kr, const E* __restrict__ kx, int N, int T, int Hkv,
     size_t kr_agent_stride, float* __restrict__ dev, float* __restrict__ score,
     double* __restrict__ part) {
   constexpr int VEC = Fmt<E>::VEC;
   constexpr int G = D / VEC;  // lanes per head
+  static_assert(G == 8 || G == 16 || G == 32, "lanes per head");
   extern __shared__ double wsum_dyn[];  // [kDevWaves][N] per-wave agent sums
   const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int rowE = Hkv * D;
   const int cpr = rowE / VEC;  // chunks per row
   double* wsum = wsum_dyn + (size_t)wave * N;
-
   for (int i = lane; i < N; i += kWave) wsum[i] = 0.0;
   __syncthreads();
 
-  for (int j = 0; j < kTokPerWave; ++j) {
-    const int t = blockIdx.x * kTokPerWg + wave * kTokPerWave + j;
-    if (t >= T) break;  // uniform within the wave
-    double s_t = 0.0;
-    for (int i0 = 0; i0 < N; i0 += kAgentUnroll) {
-      u32x4 a[kAgentUnroll][KCH], b[kAgentUnroll][KCH];
+  const int t = blockIdx.x * kTokPerWg + wave;
+  const bool live = t < T;  // uniform within the wave
+  const int tc = live ? t : T - 1;
+  double s_t = 0.0;
+  for (int i0 = 0; i0 < N; i0 += AU) {
+    u32x4 a[AU][KCH], b[AU][KCH];
 #pragma unroll
-      for (int u = 0; u < kAgentUnroll; ++u) {
-        const int i = i0 + u;
+    for (int u = 0; u < AU; ++u) {
+      const int i = min(i0 + u, N - 1);  // past N: re-read the last agent (unused)
 #pragma unroll
-        for (int k = 0; k < KCH; ++k) {
-          const int c = lane + k * kWave;
-          if (i < N && c < cpr) {
-            a[u][k] = ld16(kr + (size_t)i * kr_agent_stride + (size_t)t * rowE + c * VEC);
-            b[u][k] = ld16(kx + ((size_t)i * T + t) * rowE + c * VEC);
-          }
+      for (int k = 0; k < KCH; ++k) {
+        const int c = min(lane + k * kWave, cpr - 1);
+        a[u][k] = ld16(kr + (size_t)i * kr_agent_stride + (size_t)tc * rowE + c * VEC);
+        b[u][k] = ld16(kx + ((size_t)i * T + tc) * rowE + c * VEC);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < AU; ++u) {
+      const int i = i0 + u;
+      float d_it = 0.0f;
+#pragma unroll
+      for (int k = 0; k < KCH; ++k) {
+        float x[VEC], y[VEC];
+        Fmt<E>::unpack(a[u][k], x);
+        Fmt<E>::unpack(b[u][k], y);
+        float ss = 0.0f;
+#pragma unroll
+        for (int q = 0; q < VEC; ++q) {
+          const float df = y[q] - x[q];
+          ss = fmaf(df, df, ss);
+        }
+        const float nh = sqrtf(group_sum<G>(ss));  // this lane's head norm
+        // add the norms of the heads covered by chunk k (one lane per head)
+#pragma unroll
+        for (int hl = 0; hl < kWave; hl += G) {
+          if (hl + k * kWave < cpr) d_it += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(nh), hl));
         }
       }
-#pragma unroll
-      for (int u = 0; u < kAgentUnroll; ++u) {
-        const int i = i0 + u;
-        if (i >= N) break;
-        double d_it = 0.0;
-#pragma unroll
-        for (int k = 0; k < KCH; ++k) {
-          const int c = lane + k * kWave;
-          double ss = 0.0;
-          if (c < cpr) {
-            float x[VEC], y[VEC];
-            Fmt<E>::unpack(a[u][k], x);
-            Fmt<E>::unpack(b[u][k], y);
-#pragma unroll
-            for (int q = 0; q < VEC; ++q) {
-              const double df = (double)y[q] - (double)x[q];
-              ss = fma(df, df, ss);
-            }
-          }
-          ss = wave_sum_xor(ss, G);  // every lane of a head holds the head's sum
-          const bool leader = (lane % G) == 0 && c < cpr;
-          d_it += leader ? sqrt(ss) : 0.0;
-        }
-        d_it = wave_sum_xor(d_it, kWave);  // add the heads
-        s_t += d_it;
-        if (lane == 0) {
-          dev[(size_t)i * T + t] = (float)d_it;
-          wsum[i] += d_it;
+      if (i < N) {  // uniform
+        s_t += (double)d_it;
+        if (lane == 0 && live) {
+          dev[(size_t)i * T + t] = d_it;
+          wsum[i] += (double)d_it;
         }
       }
     }
-    if (lane == 0) score[t] = (float)s_t;
   }
+  if (lane == 0 && live) score[t] = (float)s_t;
   __syncthreads();
   for (int i = threadIdx.x; i < N; i += kDevThreads) {
     double acc = 0.0;
@@ -124,23 +142,42 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     int k, float* __restrict__ agent_dev, int32_t* __restrict__ selected,
     int32_t* __restrict__ master) {
   constexpr int W = kSelThreads / kWave;
+  extern __shared__ uint32_t s_key_dyn[];  // [T] score bits, when they fit
   __shared__ float s_adev[kMaxAgents];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t s_prefix, s_need;
   __shared__ int s_wcnt[2][W];
+  __shared__ double s_at[kSelThreads];  // [S][N] slice sums
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
+  // the scores (>= 0, so their fp32 bit patterns order like the values) are
+  // read from LDS when the launch gave room for them, else from global memory
+  const bool in_lds = T <= kSelLdsKeys;
+  const uint32_t* key = in_lds ? s_key_dyn : reinterpret_cast<const uint32_t*>(score);
+  if (in_lds)
+    for (int t = tid; t < T; t += kSelThreads) s_key_dyn[t] = __float_as_uint(score[t]);
 
-  // ---- agent totals (fixed order: lane-strided partials, xor tree) and Master
-  for (int i = wave; i < N; i += W) {
-    double acc = 0.0;
-    for (int p = lane; p < nparts; p += kWave) acc += part[(size_t)p * N + i];
-    acc = wave_sum_xor(acc, kWave);
-    if (lane == 0) {
-      const float a = (float)acc;
-      agent_dev[i] = a;
-      s_adev[i] = a;
+  // ---- agent totals and Master.  Thread (slice j, agent i) = tid sums the
+  // partials p = j, j + S, ... of agent i (S = 1024 / N slices, consecutive
+  // threads read consecutive agents); agent i then adds its S slice sums in
+  // slice order, so the order of every addition is fixed.
+  {
+    const int S = kSelThreads / N;  // N <= 1024
+    const int i = tid % N, j = tid / N;
+    if (j < S) {
+      double acc = 0.0;
+#pragma unroll 4
+      for (int p = j; p < nparts; p += S) acc += part[(size_t)p * N + i];
+      s_at[j * N + i] = acc;
+    }
+    __syncthreads();
+    for (int a = tid; a < N; a += kSelThreads) {
+      double tot = 0.0;
+      for (int q = 0; q < S; ++q) tot += s_at[q * N + a];
+      const float v = (float)tot;
+      agent_dev[a] = v;
+      s_adev[a] = v;
     }
   }
   __syncthreads();
@@ -151,36 +188,37 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     master[0] = best;
   }
 
-  // ---- radix select of the k-th largest key (scores are >= 0, so the fp32
-  // bit pattern orders like the value)
+  // ---- radix select of the k-th largest key, 8 bits per pass from the top
   uint32_t prefix = 0, mask = 0, need = (uint32_t)k;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     for (int x = tid; x < 256; x += kSelThreads) hist[x] = 0;
     __syncthreads();
     for (int t = tid; t < T; t += kSelThreads) {
-      const uint32_t u = __float_as_uint(score[t]);
+      const uint32_t u = key[t];
       if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (wave == 0) {
-      // lane owns digits 4*lane .. 4*lane+3; suffix sums from the top digit
+      // lane owns digits 4*lane .. 4*lane+3; keys above this lane's digits =
+      // exclusive suffix sum over the higher lanes (shuffle scan, 6 steps)
       uint32_t h[4], own = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         h[q] = hist[4 * lane + q];
         own += h[q];
       }
-      // keys whose digit belongs to a higher lane (exclusive suffix sum)
-      uint32_t above = 0;
-      for (int src = kWave - 1; src > 0; --src) {
-        const uint32_t v = __shfl(own, src, kWave);
-        if (src > lane) above += v;
+      uint32_t incl = own;  // inclusive suffix sum: lanes >= lane
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t v = __shfl_down(incl, o, kWave);
+        if (lane + o < kWave) incl += v;
       }
-      // digit d crosses when above + sum_{q > d} h[q] < need <= ... + h[d]
-      uint32_t run = above;
+      uint32_t run = incl - own;  // lanes > lane
+      // digit d crosses when run + sum_{q > d} h[q] < need <= ... + h[d]
       int found = -1;
       uint32_t need_in = 0;
+#pragma unroll
       for (int q = 3; q >= 0; --q) {
         if (found < 0 && run < need && need <= run + h[q]) {
           found = 4 * lane + q;
@@ -188,20 +226,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         }
         run += h[q];
       }
-      const uint64_t m = __ballot(found >= 0);
-      const int src = __ffsll((unsigned long long)m) - 1;
-      const int digit = __shfl(found, src, kWave);
-      const uint32_t nin = __shfl(need_in, src, kWave);
-      if (lane == 0) {
-        s_prefix = prefix | ((uint32_t)digit << shift);
-        s_need = nin;
+      if (found >= 0) {  // exactly one lane
+        s_prefix = prefix | ((uint32_t)found << shift);
+        s_need = need_in;
       }
     }
     __syncthreads();
     prefix = s_prefix;
     need = s_need;
     mask |= 255u << shift;
-    __syncthreads();
   }
 
   // ---- ordered compaction: every key > thr, and the first `need` keys == thr
@@ -210,7 +243,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   for (int base = 0; base < T; base += kSelThreads) {
     const int t = base + tid;
     const bool valid = t < T;
-    const uint32_t u = valid ? __float_as_uint(score[t]) : 0u;
+    const uint32_t u = valid ? key[t] : 0u;
     const bool gt = valid && u > thr;
     const bool eq = valid && u == thr;
     int tot_eq, tot_sel;
@@ -244,9 +277,22 @@ hipError_t launch_dev(const Dims& d, int check_layer, const void* kr, const void
   const size_t rowE = (size_t)d.Hkv * d.D;
   const size_t stride = (size_t)d.L * d.T * rowE;
   const E* krl = static_cast<const E*>(kr) + (size_t)check_layer * d.T * rowE;
-  hipLaunchKernelGGL((deviation_kernel<E, D, KCH>), dim3(nparts), dim3(kDevThreads),
-                     kDevWaves * d.N * sizeof(double), s, krl,
-                     static_cast<const E*>(kx), d.N, d.T, d.Hkv, stride, dev, score, part);
+  // agents in flight per wave: the group size that wastes the fewest re-reads
+  // of the last agent (ties to the larger group)
+  int best = 8;
+  for (int au : {8, 5, 4}) {
+    const int waste = (d.N + au - 1) / au * au - d.N;
+    const int bw = (d.N + best - 1) / best * best - d.N;
+    if (waste < bw) best = au;
+  }
+#define TDX_DEV(AU)                                                                      \
+  hipLaunchKernelGGL((deviation_kernel<E, D, KCH, AU>), dim3(nparts), dim3(kDevThreads), \
+                     kDevWaves * d.N * sizeof(double), s, krl, static_cast<const E*>(kx), d.N, \
+                     d.T, d.Hkv, stride, dev, score, part)
+  if (best == 8) TDX_DEV(8);
+  else if (best == 5) TDX_DEV(5);
+  else TDX_DEV(4);
+#undef TDX_DEV
   return hipGetLastError();
 }
 
@@ -288,7 +334,8 @@ hipError_t launch_select(const Dims& d, const tdx_layout& lay, int check_layer,
     e = d.D == 128 ? launch_dev_d<float, 128>(d, check_layer, k_reuse, k_recomp, dev, score, part, nparts, s)
                    : launch_dev_d<float, 64>(d, check_layer, k_reuse, k_recomp, dev, score, part, nparts, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(select_kernel, dim3(1), dim3(kSelThreads), 0, s, score, part, nparts, d.N,
+  const size_t lds = d.T <= kSelLdsKeys ? (size_t)d.T * sizeof(uint32_t) : 0;
+  hipLaunchKernelGGL(select_kernel, dim3(1), dim3(kSelThreads), lds, s, score, part, nparts, d.N,
                      d.T, k, agent_dev, selected, master);
   return hipGetLastError();
 }
