@@ -484,13 +484,15 @@ __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(3)))
 // ---- agent_kernel: private history + own diff blocks (or dense shared) ---------
 //
 // Each wave walks a contiguous run of 16-token tiles through a PD-stage
-// register pipeline: while tile u is used, the K rows, V rows and the 16-row
-// bf16 query operand of tiles u+1 .. u+PD-1 are in flight in VGPRs (the query
-// is the plain one for private/dense tiles and the one rotated by -Delta of
-// the tile's shared block for diff tiles).  K and the query feed the MFMA
-// straight from registers; V is written to a wave-private bf16 LDS tile and
-// read back transposed (ds_read_b64_tr_b16) as the PV operand.  The register
-// file holds far more bytes in flight per CU than LDS slots could.
+// register pipeline: while tile u is used, the K and V rows of tiles
+// u+1 .. u+PD-1 are in flight in VGPRs.  The query operand is the agent's
+// plain query, loaded once: the agent's own diff blocks are canonical keys, so
+// their rows are rotated to the agent's offsets in registers, each lane by the
+// shift of the shared block that holds its row (K' = R(Delta(i,b)) K, rounded
+// to bf16 like a materialised cache; cos/sin from the round's table, kept in
+// LDS when it fits).  K feeds the MFMA straight from registers; V is written
+// to a wave-private bf16 LDS tile and read back transposed
+// (ds_read_b64_tr_b16) as the PV operand.
 
 template <typename E, int D>
 struct Stage {
@@ -499,7 +501,6 @@ struct Stage {
   static constexpr int NV = kTile * D * (int)sizeof(E) / 16 / kWave;  // V loads per lane
   u32x4 k[KL];
   u32x4 v[NV];
-  u32x4 q[KD];
 };
 
 // V tile of one wave in LDS: [16 rows][D] bf16, 16-byte chunk ch of row t
@@ -511,11 +512,20 @@ __device__ __forceinline__ int vlds_off(int t, int ch) {
   return (t * C + (ch ^ (t % C))) * 16;
 }
 
-template <typename E, int D, int MODE, int NW, int PD>
-__global__ __launch_bounds__(NW * kWave) void agent_kernel(AttnArgs a) {
+constexpr int kMaxLdsTabBlocks = 64;  // cos/sin table of up to 64 shared blocks in LDS
+
+// TAB_LDS: the agent's cos/sin table sits in LDS (B <= kMaxLdsTabBlocks),
+// else diff tiles read it from the workspace.
+#ifndef TDX_AG_WPE
+#define TDX_AG_WPE 2
+#endif
+template <typename E, int D, int MODE, int NW, int PD, bool TAB_LDS>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(TDX_AG_WPE))) void agent_kernel(
+    AttnArgs a) {
   using St = Stage<E, D>;
   constexpr int KD = St::KD;
   constexpr int DT = D / 16;
+  constexpr int HALF = D / 2;
   constexpr int NT = NW * kWave;
   constexpr int RB = D * (int)sizeof(E);  // K/V row bytes of one head
   constexpr int CPR = RB / 16;            // 16-byte chunks per K/V row
@@ -523,8 +533,9 @@ __global__ __launch_bounds__(NW * kWave) void agent_kernel(AttnArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const size_t vbytes = (size_t)NW * VB;
   const size_t cbytes = (size_t)NW * 16 * (D + 2) * 4;
-  int2* tinfo = reinterpret_cast<int2*>(smem + (vbytes > cbytes ? vbytes : cbytes));  // [TPS]
-  int32_t* sblk = reinterpret_cast<int32_t*>(tinfo + kTilesPerSplit);                 // [B+1]
+  int32_t* tbeta = reinterpret_cast<int32_t*>(smem + (vbytes > cbytes ? vbytes : cbytes));  // [TPS]
+  int32_t* sblk = tbeta + kTilesPerSplit;                                                    // [B+1]
+  float2* stab = reinterpret_cast<float2*>(sblk + ((a.B + 2) & ~1));                        // [B][HALF]
 
   const int i = blockIdx.x;
   const int s = blockIdx.y;
@@ -552,20 +563,23 @@ __global__ __launch_bounds__(NW * kWave) void agent_kernel(AttnArgs a) {
   if (tbeg >= ntiles) return;  // uniform: this agent needs fewer splits
   const int tend = min(tbeg + kTilesPerSplit, ntiles);
 
+  // the agent's plain query rows (bf16): row min(c16, g-1), elements 32k + 8*q4
+  const int qrow = min(c16, g - 1);  // rows >= g repeat row g-1 (unused columns)
+  const uint16_t* qp = a.qplain + (((size_t)i * a.L + l) * a.Hq + (size_t)h * g + qrow) * D;
+  u32x4 qop[KD];
+#pragma unroll
+  for (int k = 0; k < KD; ++k) qop[k] = ld16(qp + 32 * k + 8 * q4);
+
   if (MODE == FUSED) {
     for (int b = tid; b <= a.B; b += NT) sblk[b] = a.blk_start[b];
-  }
-  __syncthreads();  // sblk ready
-  if (MODE == FUSED) {
-    // per diff tile of this split: (diff block beta, first shared block)
-    for (int u = tbeg + tid; u < tend; u += NT) {
-      if (u >= ntp) {
-        const int beta = a.diff_idx[e0 + u - ntp];
-        tinfo[u - tbeg] = make_int2(beta, block_of(sblk, a.B, beta * kTile));
-      }
+    for (int u = tbeg + ntp + tid - ntp; u < tend; u += NT)
+      if (u >= ntp) tbeta[u - tbeg] = a.diff_idx[e0 + u - ntp];
+    if (TAB_LDS) {
+      const float2* gt = a.tab + (size_t)i * a.B * HALF;
+      for (int x = tid; x < a.B * HALF; x += NT) stab[x] = gt[x];
     }
-    __syncthreads();
   }
+  __syncthreads();
 
   RowState<D> st;
   st.init();
@@ -575,17 +589,13 @@ __global__ __launch_bounds__(NW * kWave) void agent_kernel(AttnArgs a) {
       static_cast<const E*>(a.pk) + ((size_t)l * ptot + p0) * rowHD + (size_t)h * D);
   const unsigned char* pvb = reinterpret_cast<const unsigned char*>(
       static_cast<const E*>(a.pv) + ((size_t)l * ptot + p0) * rowHD + (size_t)h * D);
-  // bf16 query rows of this (agent, layer, KV head): plain, and per shared block rotated
-  const uint16_t* qplain = a.qplain + (((size_t)i * a.L + l) * a.Hq + (size_t)h * g) * D;
   unsigned char* vl = smem + (size_t)wave * VB;  // this wave's V tile
-
-  const int qrow = min(c16, g - 1);  // query rows >= g repeat row g-1 (unused columns)
+  const float2* tabrow = TAB_LDS ? stab : a.tab + (size_t)i * a.B * HALF;
 
   // Issue the loads of tile u into stage S (the same count on every path).
   auto load = [&](int u, St& S) {
     const unsigned char* kb;
     const unsigned char* vb;
-    const uint16_t* qb = qplain;
     int rmax = kTile - 1;  // rows past the end of a partial tile re-read its last row
     if (u < ntp) {
       kb = pkb + (size_t)u * kTile * rowbytes;
@@ -595,8 +605,6 @@ __global__ __launch_bounds__(NW * kWave) void agent_kernel(AttnArgs a) {
       const size_t o = ((size_t)(e0 + u - ntp) * kTile * rowHD + (size_t)h * D) * sizeof(E);
       kb = static_cast<const unsigned char*>(a.dk) + o;
       vb = static_cast<const unsigned char*>(a.dv) + o;
-      const int b = tinfo[u - tbeg].y;
-      qb = a.qrot + ((((size_t)i * a.L + l) * a.B + b) * a.Hq + (size_t)h * g) * D;
     } else {
       const size_t o = ((((size_t)i * a.L + l) * a.T + (size_t)(u - ntp) * kTile) * rowHD + (size_t)h * D) * sizeof(E);
       kb = static_cast<const unsigned char*>(a.sk) + o;
@@ -614,8 +622,6 @@ __global__ __launch_bounds__(NW * kWave) void agent_kernel(AttnArgs a) {
       const int p = v * kWave + lane;
       S.v[v] = *reinterpret_cast<const u32x4*>(vb + (size_t)min(p / CPR, rmax) * rowbytes + (p % CPR) * 16);
     }
-#pragma unroll
-    for (int k = 0; k < KD; ++k) S.q[k] = ld16(qb + (size_t)qrow * D + 32 * k + 8 * q4);
   };
 
   // live = false: a pipeline fill/drain step; every score is masked, so the
@@ -637,54 +643,40 @@ __global__ __launch_bounds__(NW * kWave) void agent_kernel(AttnArgs a) {
       }
     }
     wave_sync();
-    u32x4 kop[KD];
+    // K chunks as floats: x[k][j] = K[row c16][32k + 8*q4 + j]
+    float x[KD][8];
 #pragma unroll
     for (int k = 0; k < KD; ++k) {
       if constexpr (sizeof(E) == 2) {
-        kop[k] = S.k[k];
+        Fmt<uint16_t>::unpack(S.k[k], x[k]);
       } else {
-        kop[k] = u32x4{pack_bf16(__uint_as_float(S.k[2 * k][0]), __uint_as_float(S.k[2 * k][1])),
-                       pack_bf16(__uint_as_float(S.k[2 * k][2]), __uint_as_float(S.k[2 * k][3])),
-                       pack_bf16(__uint_as_float(S.k[2 * k + 1][0]), __uint_as_float(S.k[2 * k + 1][1])),
-                       pack_bf16(__uint_as_float(S.k[2 * k + 1][2]), __uint_as_float(S.k[2 * k + 1][3]))};
+        Fmt<float>::unpack(S.k[2 * k], x[k]);
+        Fmt<float>::unpack(S.k[2 * k + 1], x[k] + 4);
       }
     }
+    if (MODE == FUSED && u >= ntp) {
+      // the agent's own block: rotate this lane's key row by the shift of the
+      // shared block holding it; pairs (e, e + D/2) are chunks k and k + KD/2
+      const int t = tbeta[u - tbeg] * kTile + c16;
+      const int b = block_of(sblk, a.B, t);
+      const float2* cs = tabrow + (size_t)b * HALF;
+#pragma unroll
+      for (int k = 0; k < KD / 2; ++k)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float2 c = cs[32 * k + 8 * q4 + j];
+          const float lo = x[k][j], hi = x[k + KD / 2][j];
+          x[k][j] = lo * c.x - hi * c.y;
+          x[k + KD / 2][j] = hi * c.x + lo * c.y;
+        }
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < KD; ++k) acc = mfma32(Fmt<uint16_t>::pack(x[k]), qop[k], acc);
     float z[4];
-    if (u < ntp || MODE == DENSE) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < KD; ++k) acc = mfma32(kop[k], S.q[k], acc);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        z[j] = live && (u >= ntp || u * kTile + 4 * q4 + j < P) ? acc[j] * a.scale_log2 : -INFINITY;
-    } else {
-      // the agent's own block: RoPE recovered through Q' = R(-Delta(i,b)) q
-      const int2 ti = tinfo[u - tbeg];
-      const int t0 = ti.x * kTile;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) z[j] = -INFINITY;
-      for (int b = ti.y; b < a.B && sblk[b] < t0 + kTile; ++b) {
-        if (sblk[b + 1] <= t0) continue;  // empty block
-        u32x4 qr[KD];
-        if (b == ti.y) {
-#pragma unroll
-          for (int k = 0; k < KD; ++k) qr[k] = S.q[k];
-        } else {  // a tile straddling shared blocks (block starts not 16-aligned)
-          const uint16_t* qs = a.qrot + ((((size_t)i * a.L + l) * a.B + b) * a.Hq + (size_t)h * g + qrow) * D;
-#pragma unroll
-          for (int k = 0; k < KD; ++k) qr[k] = ld16(qs + 32 * k + 8 * q4);
-        }
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k = 0; k < KD; ++k) acc = mfma32(kop[k], qr[k], acc);
-        const int bs = sblk[b], be = sblk[b + 1];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int tt = t0 + 4 * q4 + j;
-          if (live && tt >= bs && tt < be) z[j] = acc[j] * a.scale_log2;
-        }
-      }
-    }
+    for (int j = 0; j < 4; ++j)
+      z[j] = live && (u >= ntp || u * kTile + 4 * q4 + j < P) ? acc[j] * a.scale_log2 : -INFINITY;
     // PV operand: va[dt][j] = V[token 4*q4 + j][dim 16*dt + c16]; this lane
     // addresses row 4*q4 + c16/4, dims 16*dt + 4*(c16%4)
     i16x4 va[DT];
@@ -932,10 +924,11 @@ Plan make_plan(const Dims& d, int max_priv, bool fused) {
 }
 
 template <int D, int NW>
-size_t agent_lds(int B, bool fused) {
+size_t agent_lds(int B, bool fused, bool tab_lds) {
   const size_t vbytes = (size_t)NW * kTile * D * 2;
   const size_t cbytes = (size_t)NW * 16 * (D + 2) * 4;
-  return (vbytes > cbytes ? vbytes : cbytes) + (size_t)kTilesPerSplit * 8 + (fused ? (size_t)(B + 1) * 4 : 0);
+  return (vbytes > cbytes ? vbytes : cbytes) + (size_t)kTilesPerSplit * 4 + (size_t)((B + 2) & ~1) * 4 +
+         (fused && tab_lds ? (size_t)B * (D / 2) * 8 : 0);
 }
 
 // waves per workgroup / register stages of agent_kernel: PD stages keep PD-1
@@ -980,10 +973,14 @@ hipError_t launch_attn_t(const Dims& d, AttnArgs a, const Plan& p, E* out, hipSt
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   constexpr int NW = AgentCfg<E, D>::NW, PD = AgentCfg<E, D>::PD;
-  const size_t lds = agent_lds<D, NW>(d.B, MODE == FUSED);
+  const bool tab_lds = d.B <= kMaxLdsTabBlocks;
+  const size_t lds = agent_lds<D, NW>(d.B, MODE == FUSED, tab_lds);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((agent_kernel<E, D, MODE, NW, PD>), dim3(d.N, p.SP, d.L * d.Hkv), dim3(NW * kWave), lds,
-                     s, a);
+  const dim3 agrid(d.N, p.SP, d.L * d.Hkv);
+  if (tab_lds)
+    hipLaunchKernelGGL((agent_kernel<E, D, MODE, NW, PD, true>), agrid, dim3(NW * kWave), lds, s, a);
+  else
+    hipLaunchKernelGGL((agent_kernel<E, D, MODE, NW, PD, false>), agrid, dim3(NW * kWave), lds, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t rows = (size_t)d.N * d.L * d.Hq;
   const int rpb = 256 / kWave;

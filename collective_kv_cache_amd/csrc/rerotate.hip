@@ -46,7 +46,7 @@ template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void rerotate_kernel(
     const E* __restrict__ kc, E* __restrict__ out, const int32_t* __restrict__ blk_start,
     const int32_t* __restrict__ src_pos, const int32_t* __restrict__ dst_pos, int N, int B,
-    int T, int L, int Hkv, int lpg, double theta) {
+    int T, int L, int Hkv, int lpg, int apg, double theta) {
   constexpr int VEC = Fmt<E>::VEC;
   constexpr int HALF = D / 2;
   constexpr int G = HALF / VEC;       // lanes per (token, head) row
@@ -61,7 +61,9 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(
   const int t1 = min(t0 + kTileTok, T);
   const int l0 = blockIdx.y * lpg;
   const int l1 = min(l0 + lpg, L);
-  if (t0 >= T || l0 >= L) return;  // uniform over the workgroup
+  const int ab = blockIdx.z * apg;  // this workgroup's agents [ab, ae)
+  const int ae = min(ab + apg, N);
+  if (t0 >= T || l0 >= L || ab >= ae) return;  // uniform over the workgroup
 
   for (int b = tid; b <= B; b += kThreads) sblk[b] = blk_start[b];
   for (int e = tid; e < HALF; e += kThreads) invf[e] = rope_inv_freq(theta, e, D);
@@ -86,8 +88,8 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(
     const int nbatch = (nrows + RPP * kItems - 1) / (RPP * kItems);
     const int nsteps = (l1 - l0) * nbatch;
     const int sp = src_pos[b];
-    for (int a0 = 0; a0 < N; a0 += kAgentChunk) {
-      const int na = min(kAgentChunk, N - a0);
+    for (int a0 = ab; a0 < ae; a0 += kAgentChunk) {
+      const int na = min(kAgentChunk, ae - a0);
       __syncthreads();  // previous users of tab are done
       for (int x = tid; x < na * HALF; x += kThreads) {
         const int a = x / HALF, e = x % HALF;
@@ -157,16 +159,21 @@ template <typename E, int D>
 hipError_t launch_t(const Dims& d, const tdx_layout& lay, const void* kc, void* out,
                     hipStream_t s) {
   const int tiles = (d.T + kTileTok - 1) / kTileTok;
-  // enough workgroups to fill 256 CUs several times over, >= 1 layer each
+  // enough workgroups to fill 256 CUs several times over: layers split
+  // first (>= 1 layer each), then agents
   int groups = (TDX_RR_TARGET_WG + tiles - 1) / tiles;
   groups = groups < 1 ? 1 : (groups > d.L ? d.L : groups);
   const int lpg = (d.L + groups - 1) / groups;
   groups = (d.L + lpg - 1) / lpg;
-  dim3 grid(tiles, groups);
+  int asplit = (2048 + tiles * groups - 1) / (tiles * groups);  // only for small rounds
+  asplit = asplit < 1 ? 1 : (asplit > d.N ? d.N : asplit);
+  const int apg = (d.N + asplit - 1) / asplit;
+  asplit = (d.N + apg - 1) / apg;
+  dim3 grid(tiles, groups, asplit);
   const size_t lds = (size_t)kAgentChunk * (D / 2) * 8 + (D / 2) * 8 + (size_t)(d.B + 1) * 4;
   hipLaunchKernelGGL((rerotate_kernel<E, D>), grid, dim3(kThreads), lds, s,
                      static_cast<const E*>(kc), static_cast<E*>(out), lay.blk_start,
-                     lay.src_pos, lay.dst_pos, d.N, d.B, d.T, d.L, d.Hkv, lpg, d.theta);
+                     lay.src_pos, lay.dst_pos, d.N, d.B, d.T, d.L, d.Hkv, lpg, apg, d.theta);
   return hipGetLastError();
 }
 
