@@ -315,16 +315,46 @@ __device__ __forceinline__ void write_record(float* rec, const RowState<D>& st, 
 }
 
 // ---- shared_kernel: Master tiles staged once, all agents' query rows ------------
+//
+// One workgroup per (agent group, Master split, layer, KV head).  The split's
+// tiles are taken shared block by shared block: the wave's 16 rotated query
+// rows R(-Delta(i,b)) q are loaded once per block, and the block's tiles
+// stream through a PD-stage register pipeline (each thread's chunks of the
+// tile's K and V rows), the tile in use sitting in one of two LDS buffers.
+// Step n: issue the loads of tile n+PD-1, use tile n, store tile n+1 into the
+// other buffer, barrier.  No branch surrounds a load or a use inside a
+// block, so the wait before a stage leaves the younger tiles in flight; fill
+// and drain steps run masked.  A tile that straddles two shared blocks is
+// used once for each, with the other block's rows masked.
+
+#ifndef TDX_SH_PD
+#define TDX_SH_PD 4
+#endif
+#ifndef TDX_SH_TARGET_WG
+#define TDX_SH_TARGET_WG 1024
+#endif
 
 template <typename E, int D>
-__global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(3))) void shared_kernel(AttnArgs a) {
+struct ShStage {
+  static constexpr int CH = D / 8;                         // 8-element chunks per row
+  static constexpr int CPT = 2 * kTile * CH / kShThreads;  // chunks per thread (K then V)
+  static constexpr int LPC = (int)sizeof(E) / 2;           // 16-byte loads per chunk
+  u32x4 kv[CPT * LPC];
+};
+
+#ifndef TDX_SH_WPE
+#define TDX_SH_WPE 3
+#endif
+template <typename E, int D, int PD>
+__global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(TDX_SH_WPE))) void shared_kernel(AttnArgs a) {
+  using St = ShStage<E, D>;
   constexpr int KD = D / 32;
   constexpr int DT = D / 16;
-  constexpr int HALF = D / 2;
   constexpr int VS = D + 8;  // padded LDS row stride (bf16)
-  constexpr int CH = D / 8;  // 8-element chunks per row
-  constexpr int NCH = 2 * kTile * CH;  // staged chunks per tile (K then V)
-  constexpr int CPT = (NCH + kShThreads - 1) / kShThreads;
+  constexpr int CH = St::CH;
+  constexpr int CPT = St::CPT;
+  constexpr int LPC = St::LPC;
+  static_assert(2 * kTile * CH % kShThreads == 0, "tile chunks per thread");
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* kbuf = reinterpret_cast<uint16_t*>(smem);  // [2][16][VS]
   uint16_t* vbuf = kbuf + 2 * kTile * VS;              // [2][16][VS]
@@ -351,16 +381,19 @@ __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(3)))
   const int b0 = gs * a.TPG;
   const int b1 = min(b0 + a.TPG, nb);
   if (b0 >= b1) return;  // uniform
-  const int ntl = b1 - b0;
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform per wave
   const int q4 = lane / 16, c16 = lane % 16;
 
   for (int x = tid; x <= a.B; x += kShThreads) sblk[x] = a.blk_start[x];
   for (int x = tid; x < a.AGS * a.TPG; x += kShThreads) dflag[x] = 0;
+  // zeroed tile buffers: the first fill steps read them under a full mask
+  for (int x = tid; x < 4 * kTile * VS / 8; x += kShThreads)
+    reinterpret_cast<u32x4*>(kbuf)[x] = u32x4{0, 0, 0, 0};
   __syncthreads();
   // flag (agent, tile) pairs whose block is in the agent's diff row: those
-  // rows take the tile from the agent's own record (agent_kernel)
+  // rows take the tile from the agent's own record (agent_kernel); read after
+  // the pipeline's first barrier
   for (int al = wave; al < na; al += kShWaves) {
     const int r = (a0 + al) * a.L + l;
     const int e1 = a.diff_off[r + 1];
@@ -370,16 +403,13 @@ __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(3)))
     }
   }
 
-  // this wave's 16 query rows (row = agent-major, then the GQA group)
+  // this wave's 16 query rows (row = agent-major, then the GQA group); rows
+  // past the group load row 0's data and are masked
   const bool has_rows = wave * 16 < nrows;  // wave-uniform
   const int row = wave * 16 + c16;
   const bool valid = row < nrows;
   const int agent = a0 + (valid ? row / g : 0);
   const int hq = h * g + (valid ? row % g : 0);
-  u32x4 qr[KD];  // rotated query operand for block bq
-#pragma unroll
-  for (int k = 0; k < KD; ++k) qr[k] = u32x4{0, 0, 0, 0};
-  int bq = -1;
   RowState<D> st;
   st.init();
 
@@ -387,87 +417,87 @@ __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(3)))
   const size_t moff = master_offset(a.msel, a.mstride, a.N);
   const E* mk = static_cast<const E*>(a.sk) + moff + (size_t)l * a.T * rowHD + (size_t)h * D;
   const E* mv = static_cast<const E*>(a.sv) + moff + (size_t)l * a.T * rowHD + (size_t)h * D;
-  auto stage_load = [&](int beta, u32x4* r) {
+  const uint16_t* qbase = a.qrot + (((size_t)agent * a.L + l) * a.B) * a.Hq * D + (size_t)hq * D;
+  const size_t qblk = (size_t)a.Hq * D;  // qrot stride between shared blocks
+
+  auto load = [&](int tile, St& S) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int idx = tid + c * kShThreads;
-      if (idx < NCH) {
-        const int tensor = idx / (kTile * CH);
-        const int rem = idx % (kTile * CH);
-        const E* src = (tensor ? mv : mk) + (size_t)(beta * kTile + rem / CH) * rowHD + (rem % CH) * 8;
-        r[c] = load8_bf16<E>(src);
-      }
+      const int tensor = idx / (kTile * CH);
+      const int rem = idx % (kTile * CH);
+      const E* src = (tensor ? mv : mk) + (size_t)(tile * kTile + rem / CH) * rowHD + (rem % CH) * 8;
+#pragma unroll
+      for (int p = 0; p < LPC; ++p) S.kv[c * LPC + p] = ld16(src + p * (8 / LPC));
     }
   };
-  auto stage_store = [&](int buf, const u32x4* r) {
+  auto store = [&](const St& S, int buf) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int idx = tid + c * kShThreads;
-      if (idx < NCH) {
-        const int tensor = idx / (kTile * CH);
-        const int rem = idx % (kTile * CH);
-        uint16_t* dst = (tensor ? vbuf : kbuf) + (buf * kTile + rem / CH) * VS + (rem % CH) * 8;
-        *reinterpret_cast<u32x4*>(dst) = r[c];
+      const int tensor = idx / (kTile * CH);
+      const int rem = idx % (kTile * CH);
+      uint16_t* dst = (tensor ? vbuf : kbuf) + (buf * kTile + rem / CH) * VS + (rem % CH) * 8;
+      u32x4 v;
+      if constexpr (sizeof(E) == 2) {
+        v = S.kv[c];
+      } else {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          v[2 * p] = pack_bf16(__uint_as_float(S.kv[2 * c + p][0]), __uint_as_float(S.kv[2 * c + p][1]));
+          v[2 * p + 1] = pack_bf16(__uint_as_float(S.kv[2 * c + p][2]), __uint_as_float(S.kv[2 * c + p][3]));
+        }
       }
+      *reinterpret_cast<u32x4*>(dst) = v;
     }
   };
-  auto compute = [&](int buf, int n) {
-    if (!has_rows) return;  // wave-uniform
-    const int beta = b0 + n;
-    const uint16_t* kt = kbuf + buf * kTile * VS;
-    const uint16_t* vt = vbuf + buf * kTile * VS;
-    u32x4 kop[KD];
+
+  // shared blocks that intersect this split's tiles, one after the other
+  for (int b = block_of(sblk, a.B, b0 * kTile); b < a.B && sblk[b] < b1 * kTile; ++b) {
+    const int bs = sblk[b], be = sblk[b + 1];
+    const int ta = max(b0, bs / kTile), tb = min(b1, (be + kTile - 1) / kTile);
+    if (be <= bs || ta >= tb) continue;  // empty block (uniform)
+    const int nt = tb - ta;
+    u32x4 qr[KD];  // rotated query rows for block b
+    {
+      const uint16_t* qs = qbase + (size_t)b * qblk;
 #pragma unroll
-    for (int k = 0; k < KD; ++k) kop[k] = *reinterpret_cast<const u32x4*>(kt + c16 * VS + 32 * k + 8 * q4);
-    const int t0 = beta * kTile;
-    float z[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    for (int b = block_of(sblk, a.B, t0); b < a.B && sblk[b] < t0 + kTile; ++b) {
-      if (sblk[b + 1] <= t0) continue;  // empty block
-      if (b != bq) {
-        const uint16_t* qs = a.qrot + ((((size_t)agent * a.L + l) * a.B + b) * a.Hq + hq) * D;
+      for (int k = 0; k < KD; ++k) qr[k] = ld16(qs + 32 * k + 8 * q4);
+    }
+    // use tile ta + n (buffer buf)
+    auto compute = [&](int n, bool live, int buf) {
+      if (!has_rows) return;  // wave-uniform; no loads or barriers inside
+      const uint16_t* kt = kbuf + buf * kTile * VS;
+      const uint16_t* vt = vbuf + buf * kTile * VS;
+      u32x4 kop[KD];
 #pragma unroll
-        for (int k = 0; k < KD; ++k) qr[k] = valid ? ld16(qs + 32 * k + 8 * q4) : u32x4{0, 0, 0, 0};
-        bq = b;
-      }
+      for (int k = 0; k < KD; ++k) kop[k] = *reinterpret_cast<const u32x4*>(kt + c16 * VS + 32 * k + 8 * q4);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < KD; ++k) acc = mfma32(kop[k], qr[k], acc);
-      const int bs = sblk[b], be = sblk[b + 1];
+      const int tile = ta + min(max(n, 0), nt - 1);
+      const bool on = live && valid && !dflag[(agent - a0) * a.TPG + (tile - b0)];
+      float z[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int tt = t0 + 4 * q4 + j;
-        if (tt >= bs && tt < be) z[j] = acc[j] * a.scale_log2;
+        const int tt = tile * kTile + 4 * q4 + j;
+        z[j] = (on && tt >= bs && tt < be) ? acc[j] * a.scale_log2 : -INFINITY;
+      }
+      i16x4 va[DT];
+      gather_v<D>(vt, VS, q4, c16, va);
+      softmax_pv<D>(st, z, va);
+    };
+    St S[PD] = {};
+    for (int n0 = -(PD - 1); n0 < nt; n0 += PD) {
+#pragma unroll
+      for (int k = 0; k < PD; ++k) {
+        const int n = n0 + k;  // tile ta + n used in this step (workgroup-uniform)
+        load(ta + min(n + PD - 1, nt - 1), S[(k + PD - 1) % PD]);
+        compute(n, n >= 0 && n < nt, n & 1);
+        store(S[(k + 1) % PD], (n + 1) & 1);
+        __syncthreads();
       }
     }
-    if (!valid || dflag[(agent - a0) * a.TPG + n]) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) z[j] = -INFINITY;
-    }
-    i16x4 va[DT];
-    gather_v<D>(vt, VS, q4, c16, va);
-    softmax_pv<D>(st, z, va);
-  };
-
-  // Two register sets keep the Master tile n+2 in flight while tile n is
-  // used and tile n+1 (loaded one step earlier) goes into the other LDS buffer.
-  // Loads past the last tile re-read the last tile (unconditional issue keeps
-  // the compiler's wait counting on one path).
-  u32x4 sA[CPT], sB[CPT];
-  stage_load(b0, sA);
-  stage_store(0, sA);
-  stage_load(b0 + min(1, ntl - 1), sB);
-  __syncthreads();  // tile 0 staged, diff flags complete
-  for (int n = 0;;) {
-    stage_load(b0 + min(n + 2, ntl - 1), sA);
-    compute(0, n);
-    if (++n >= ntl) break;
-    stage_store(1, sB);
-    __syncthreads();
-    stage_load(b0 + min(n + 2, ntl - 1), sB);
-    compute(1, n);
-    if (++n >= ntl) break;
-    stage_store(0, sA);
-    __syncthreads();
   }
 
   if (has_rows) {
@@ -906,7 +936,7 @@ Plan make_plan(const Dims& d, int max_priv, bool fused) {
     if (p.AGS < 1) p.AGS = 1;
     p.NAG = (d.N + p.AGS - 1) / p.AGS;
     const long base = (long)p.NAG * d.L * d.Hkv;
-    long sg = (2048 + base - 1) / base;  // aim at ~2048 workgroups
+    long sg = (TDX_SH_TARGET_WG + base - 1) / base;  // aim at this many workgroups
     if (sg < 1) sg = 1;
     if (sg > nb) sg = nb;
     p.TPG = (int)((nb + sg - 1) / sg);
@@ -962,7 +992,7 @@ hipError_t launch_attn_t(const Dims& d, AttnArgs a, const Plan& p, E* out, hipSt
     const size_t lds = shared_lds(D, d.B, p);
     if (lds > 64 * 1024) return hipErrorInvalidValue;
     const int grid = (p.n_sh_wg + 7) / 8 * 8;
-    hipLaunchKernelGGL((shared_kernel<E, D>), dim3(grid), dim3(kShThreads), lds, s, a);
+    hipLaunchKernelGGL((shared_kernel<E, D, TDX_SH_PD>), dim3(grid), dim3(kShThreads), lds, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   {
