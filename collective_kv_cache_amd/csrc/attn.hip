@@ -342,6 +342,20 @@ struct ShStage {
   u32x4 kv[CPT * LPC];
 };
 
+// Master tiles are read by every agent group of a (layer, head, split); a
+// plain load lets the groups that run together on one XCD share its L2 lines.
+#ifndef TDX_SH_NT
+#define TDX_SH_NT 0
+#endif
+template <typename E>
+__device__ __forceinline__ u32x4 sh_ld(const E* p) {
+#if TDX_SH_NT
+  return ld16_nt(p);
+#else
+  return ld16(p);
+#endif
+}
+
 #ifndef TDX_SH_WPE
 #define TDX_SH_WPE 3
 #endif
@@ -428,7 +442,7 @@ __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(TDX_
       const int rem = idx % (kTile * CH);
       const E* src = (tensor ? mv : mk) + (size_t)(tile * kTile + rem / CH) * rowHD + (rem % CH) * 8;
 #pragma unroll
-      for (int p = 0; p < LPC; ++p) S.kv[c * LPC + p] = ld16(src + p * (8 / LPC));
+      for (int p = 0; p < LPC; ++p) S.kv[c * LPC + p] = sh_ld(src + p * (8 / LPC));
     }
   };
   auto store = [&](const St& S, int buf) {
@@ -542,6 +556,29 @@ __device__ __forceinline__ int vlds_off(int t, int ch) {
   return (t * C + (ch ^ (t % C))) * 16;
 }
 
+#ifndef TDX_AG_NTK
+#define TDX_AG_NTK 0
+#endif
+#ifndef TDX_AG_NTV
+#define TDX_AG_NTV 1
+#endif
+template <typename E>
+__device__ __forceinline__ u32x4 ag_ldk(const E* p) {
+#if TDX_AG_NTK
+  return ld16_nt(p);
+#else
+  return ld16(p);
+#endif
+}
+template <typename E>
+__device__ __forceinline__ u32x4 ag_ldv(const E* p) {
+#if TDX_AG_NTV
+  return ld16_nt(p);
+#else
+  return ld16(p);
+#endif
+}
+
 constexpr int kMaxLdsTabBlocks = 64;  // cos/sin table of up to 64 shared blocks in LDS
 
 // TAB_LDS: the agent's cos/sin table sits in LDS (B <= kMaxLdsTabBlocks),
@@ -644,13 +681,12 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(TDX_
     const unsigned char* kr = kb + (size_t)min(c16, rmax) * rowbytes;
 #pragma unroll
     for (int k = 0; k < St::KL; ++k)
-      S.k[k] = *reinterpret_cast<const u32x4*>(kr + (sizeof(E) == 2 ? (32 * k + 8 * q4) * 2
-                                                                    : (32 * (k / 2) + 8 * q4 + 4 * (k % 2)) * 4));
+      S.k[k] = ag_ldk(kr + (sizeof(E) == 2 ? (32 * k + 8 * q4) * 2 : (32 * (k / 2) + 8 * q4 + 4 * (k % 2)) * 4));
     // V: 16-byte chunk p = 64 v + lane of the tile = row p / CPR, chunk p % CPR
 #pragma unroll
     for (int v = 0; v < St::NV; ++v) {
       const int p = v * kWave + lane;
-      S.v[v] = *reinterpret_cast<const u32x4*>(vb + (size_t)min(p / CPR, rmax) * rowbytes + (p % CPR) * 16);
+      S.v[v] = ag_ldv(vb + (size_t)min(p / CPR, rmax) * rowbytes + (p % CPR) * 16);
     }
   };
 

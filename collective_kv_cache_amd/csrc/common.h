@@ -78,6 +78,19 @@ template <typename E>
 __device__ __forceinline__ void st16(E* p, const u32x4& v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }
+// Streaming load: data this kernel reads once (non-temporal hint, so the
+// stream does not displace lines that are reused from the caches).
+#ifndef TDX_NT_LOADS
+#define TDX_NT_LOADS 1
+#endif
+template <typename E>
+__device__ __forceinline__ u32x4 ld16_nt(const E* p) {
+#if TDX_NT_LOADS
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#else
+  return *reinterpret_cast<const u32x4*>(p);
+#endif
+}
 // Streaming store: the written data is not re-read by this kernel.
 template <typename E>
 __device__ __forceinline__ void st16_nt(E* p, const u32x4& v) {

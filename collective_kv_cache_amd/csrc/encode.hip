@@ -67,8 +67,8 @@ __global__ __launch_bounds__(kFlagThreads) void flag_kernel(
   u32x4 mkr[KC], mvr[KC];
 #pragma unroll
   for (int j = 0; j < KC; ++j) {
-    mkr[j] = ak[mbase + cidx[j]];
-    mvr[j] = av[mbase + cidx[j]];
+    mkr[j] = ld16_nt(ak + mbase + cidx[j]);
+    mvr[j] = ld16_nt(av + mbase + cidx[j]);
   }
   if (mk_out != nullptr) {
     const size_t obase = (size_t)l * layer_chunks + (size_t)beta * chunks;
@@ -93,8 +93,8 @@ __global__ __launch_bounds__(kFlagThreads) void flag_kernel(
       const size_t base = ((size_t)a * L + l) * layer_chunks + (size_t)beta * chunks;
 #pragma unroll
       for (int q = 0; q < KC; ++q) {
-        B.k[q] = ak[base + cidx[q]];
-        B.v[q] = av[base + cidx[q]];
+        B.k[q] = ld16_nt(ak + base + cidx[q]);
+        B.v[q] = ld16_nt(av + base + cidx[q]);
       }
     };
     auto compare = [&](const Blk& B, int j, bool live) {
@@ -194,6 +194,17 @@ __global__ __launch_bounds__(kScanThreads) void offsets_kernel(const int32_t* __
   }
 }
 
+#ifndef TDX_CP_NT_STORES
+#define TDX_CP_NT_STORES 0
+#endif
+__device__ __forceinline__ void cp_store(const u32x4& v, u32x4* p) {
+#if TDX_CP_NT_STORES
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
+
 __global__ __launch_bounds__(kThreads) void copy_kernel(
     const u32x4* __restrict__ ak, const u32x4* __restrict__ av, const uint8_t* __restrict__ flags,
     const int32_t* __restrict__ rank, const int32_t* __restrict__ off, int nb, int chunks,
@@ -210,8 +221,8 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(
     const size_t src = (r * nb + beta) * (size_t)chunks;
     const size_t dst = (size_t)slot * chunks;
     for (int c = tid; c < chunks; c += kThreads) {
-      __builtin_nontemporal_store(ak[src + c], dk + dst + c);
-      __builtin_nontemporal_store(av[src + c], dv + dst + c);
+      cp_store(ld16_nt(ak + src + c), dk + dst + c);
+      cp_store(ld16_nt(av + src + c), dv + dst + c);
     }
   }
 }

@@ -27,7 +27,7 @@ constexpr int kItems = 2;        // (token, head) rows per lane per batch
 #define TDX_RR_TARGET_WG 16384
 #endif
 #ifndef TDX_RR_NT_STORES
-#define TDX_RR_NT_STORES 1
+#define TDX_RR_NT_STORES 0
 #endif
 
 template <typename E>
@@ -109,8 +109,8 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(
         for (int k = 0; k < kItems; ++k) {
           const int r = rb + row_base + k * RPP;
           if (r < nrows) {
-            lo_[k] = ld16(src + (size_t)r * D + e0);
-            hi_[k] = ld16(src + (size_t)r * D + HALF + e0);
+            lo_[k] = ld16_nt(src + (size_t)r * D + e0);
+            hi_[k] = ld16_nt(src + (size_t)r * D + HALF + e0);
           }
         }
       };

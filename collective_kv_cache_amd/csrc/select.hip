@@ -85,8 +85,8 @@ __global__ __launch_bounds__(kDevThreads) void deviation_kernel(
 #pragma unroll
       for (int k = 0; k < KCH; ++k) {
         const int c = min(lane + k * kWave, cpr - 1);
-        a[u][k] = ld16(kr + (size_t)i * kr_agent_stride + (size_t)tc * rowE + c * VEC);
-        b[u][k] = ld16(kx + ((size_t)i * T + tc) * rowE + c * VEC);
+        a[u][k] = ld16_nt(kr + (size_t)i * kr_agent_stride + (size_t)tc * rowE + c * VEC);
+        b[u][k] = ld16_nt(kx + ((size_t)i * T + tc) * rowE + c * VEC);
       }
     }
 #pragma unroll
