@@ -27,6 +27,9 @@ FLAGS = [
     # MFMA accumulators in ordinary VGPRs: the online-softmax rescale then
     # multiplies them in place instead of copying them out of and back into AGPRs
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # keep a single-lane atomic a single-lane atomic: the optimizer's rewrite
+    # uses the returned value at once, which waits for every load in flight
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

@@ -43,18 +43,14 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
 constexpr int kTile = 16;
-#ifndef TDX_AG_TPS
-#define TDX_AG_TPS 128
+#ifndef TDX_ST_TW
+#define TDX_ST_TW 64
 #endif
-#ifndef TDX_AG_NW
-#define TDX_AG_NW 4
+#ifndef TDX_ST_PD
+#define TDX_ST_PD 3
 #endif
-#ifndef TDX_AG_PD
-#define TDX_AG_PD 3
-#endif
-constexpr int kTilesPerSplit = TDX_AG_TPS;  // agent_kernel: tiles per workgroup
+constexpr int kTilesPerSplit = TDX_ST_TW;  // stream kernel: tiles per task (one partial record)
 constexpr int kShThreads = 256;     // shared_kernel: 4 waves, one 16-row tile each
 constexpr int kShWaves = kShThreads / kWave;
 constexpr int kRowsPerGroup = 16 * kShWaves;
@@ -216,8 +212,10 @@ struct AttnArgs {
   uint16_t* qrot;            // fused: [N][L][B][Hq][D] bf16 rotated queries
   uint16_t* qplain;          // [N][L][Hq][D] bf16 queries
   float* part;               // [N][L][Hq][S][D+4]: m, l, -, -, O[D]
+  unsigned char* ws_base;    // the workspace (task list, per-diff-entry cos/sin rows)
   int N, L, T, B, Hkv, Hq;
-  int SP;                    // agent-kernel record slots
+  long long dcap;            // fused: diff entries covered by the per-entry cos/sin rows
+  int SP;                    // stream-kernel record slots
   int SG;                    // shared-kernel record slots (after SP)
   int S;                     // SP + SG
   int AGS, NAG, TPG;         // shared kernel: agents per group, groups, tiles per split
@@ -525,27 +523,46 @@ __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(TDX_
   }
 }
 
-// ---- agent_kernel: private history + own diff blocks (or dense shared) ---------
+// ---- stream_kernel: every agent's own tiles, persistent waves -------------------
 //
-// Each wave walks a contiguous run of 16-token tiles through a PD-stage
-// register pipeline: while tile u is used, the K and V rows of tiles
-// u+1 .. u+PD-1 are in flight in VGPRs.  The query operand is the agent's
-// plain query, loaded once: the agent's own diff blocks are canonical keys, so
-// their rows are rotated to the agent's offsets in registers, each lane by the
-// shift of the shared block that holds its row (K' = R(Delta(i,b)) K, rounded
-// to bf16 like a materialised cache; cos/sin from the round's table, kept in
-// LDS when it fits).  K feeds the MFMA straight from registers; V is written
-// to a wave-private bf16 LDS tile and read back transposed
-// (ds_read_b64_tr_b16) as the PV operand.
+// The agent-private work is a stream of 16-token tiles per (agent, layer, KV
+// head): the agent's private history, then its own diff blocks (fused) or its
+// materialised shared cache (dense comparator).  stream_plan_kernel cuts
+// every (agent, layer) row into tasks of at most kTilesPerSplit tiles, each of
+// which becomes one partial softmax record per query row.  The waves of
+// stream_kernel stay resident and take (task, KV head) pairs in turn;
+// each wave runs ONE PD-stage register pipeline across task boundaries, so the
+// first tiles and the query of the next task are in flight while the current
+// task drains, and no workgroup start-up or combine step sits between tasks.
+// A task runs for at least PD-1 steps (shorter ones are padded with masked
+// steps), so the load side is never more than one task ahead.
+//
+// Per tile: K and V rows arrive in registers (16-byte non-temporal loads, a
+// quarter-wave per 256-byte row), go to wave-private LDS tiles, and come back
+// as MFMA operands: K as the A operand of S^T = K Q^T, V transposed
+// (ds_read_b64_tr_b16).  The query operand is the agent's plain query.  A
+// diff block holds canonical keys: its rows are rotated to the agent's
+// offsets in registers by the shift of the shared block that holds them
+// (K' = R(Delta(i,b)) K, rounded to bf16 like a materialised cache), with the
+// block's cos/sin row prepared per diff entry by diff_tab_kernel.
 
-template <typename E, int D>
+template <typename E, int D, int MODE>
 struct Stage {
-  static constexpr int KD = D / 32;                       // 16-byte bf16 chunks of K/Q per lane
-  static constexpr int KL = KD * (int)sizeof(E) / 2;       // K loads per lane
-  static constexpr int NV = kTile * D * (int)sizeof(E) / 16 / kWave;  // V loads per lane
-  u32x4 k[KL];
+  static constexpr int KD = D / 32;                                   // 16-byte bf16 chunks of K/Q per lane
+  static constexpr int NV = kTile * D * (int)sizeof(E) / 16 / kWave;  // K or V loads per lane
+  u32x4 k[NV];
   u32x4 v[NV];
+  float2 cs;  // fused: this lane's (cos, sin) pair of the diff entry's cos/sin row
+  int2 info;  // fused: (beta, shared block b) of the diff entry; ~b when the block straddles
 };
+
+// K tile of one wave in LDS, stored as loaded: [16 rows][CPR 16-byte chunks],
+// chunk ch of row t at position ch ^ t (t < 16 <= CPR), so that the row-wise
+// writes and the column reads of the MFMA operand spread over the banks.
+template <int CPR>
+__device__ __forceinline__ int klds_off(int t, int ch) {
+  return (t * CPR + (ch ^ t)) * 16;
+}
 
 // V tile of one wave in LDS: [16 rows][D] bf16, 16-byte chunk ch of row t
 // stored at chunk position ch ^ (t % (D/8)) so that row-wise writes and the
@@ -556,148 +573,273 @@ __device__ __forceinline__ int vlds_off(int t, int ch) {
   return (t * C + (ch ^ (t % C))) * 16;
 }
 
-#ifndef TDX_AG_NTK
-#define TDX_AG_NTK 0
+// One task of the agent stream: tiles [t0, t0 + cnt) of row r = i * L + l,
+// run once per KV head.
+struct __attribute__((aligned(32))) StreamTask {
+  int32_t r;     // (agent, layer) row
+  int32_t s;     // split index: the partial-record slot
+  int32_t t0;    // first tile (0 = the agent's first private tile)
+  int32_t cnt;   // tiles, >= 1
+  int32_t ntp;   // private tiles of the agent
+  int32_t P;     // private tokens of the agent
+  int32_t prow;  // first private row of the agent in layer l: l * Ptot + priv_off[i]
+  int32_t e0;    // first diff entry of the row (fused)
+};
+
+constexpr int kPlanThreads = 1024;
+#ifndef TDX_ST_NW
+#define TDX_ST_NW 4
 #endif
-#ifndef TDX_AG_NTV
-#define TDX_AG_NTV 1
+#ifndef TDX_ST_WPE
+#define TDX_ST_WPE 2
 #endif
-template <typename E>
-__device__ __forceinline__ u32x4 ag_ldk(const E* p) {
-#if TDX_AG_NTK
-  return ld16_nt(p);
-#else
-  return ld16(p);
-#endif
-}
-template <typename E>
-__device__ __forceinline__ u32x4 ag_ldv(const E* p) {
-#if TDX_AG_NTV
-  return ld16_nt(p);
-#else
-  return ld16(p);
-#endif
+constexpr int kStreamNW = TDX_ST_NW;  // waves per stream workgroup
+
+// Task order: every row's full splits first (row order), then the shorter
+// remainders, so that the last tasks taken are the small ones.
+// ctl[0] = task count.
+template <int MODE>
+__global__ __launch_bounds__(kPlanThreads) void stream_plan_kernel(AttnArgs a, StreamTask* __restrict__ tasks,
+                                                                   int32_t* __restrict__ ctl) {
+  constexpr int W = kPlanThreads / kWave;
+  __shared__ int wsum[W];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int rows = a.N * a.L;
+  const int nb = a.T / kTile;
+  const int ptot = a.priv_off[a.N];
+  int carry = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int base = 0; base < rows; base += kPlanThreads) {
+      const int r = base + tid;
+      StreamTask t{};
+      int nt = 0;
+      if (r < rows) {
+        const int i = r / a.L, l = r % a.L;
+        const int p0 = a.priv_off[i];
+        t.P = a.priv_off[i + 1] - p0;
+        t.ntp = (t.P + kTile - 1) / kTile;
+        t.prow = l * ptot + p0;
+        int nx = nb;
+        if (MODE == FUSED) {
+          t.e0 = a.diff_off[r];
+          nx = min(max(a.diff_off[r + 1] - t.e0, 0), nb);
+        }
+        nt = t.ntp + nx;
+        t.r = r;
+      }
+      // at most SP splits per row (tiles past them, which a max_priv below
+      // the longest history would leave, are not attended)
+      const int nfull = min(nt / kTilesPerSplit, a.SP);
+      const int rem = nfull < a.SP ? nt - nfull * kTilesPerSplit : 0;
+      const int n = pass == 0 ? nfull : (rem > 0 ? 1 : 0);
+      int x = n;  // inclusive wave scan, then the workgroup's exclusive prefix
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(x, o, kWave);
+        if (lane >= o) x += y;
+      }
+      if (lane == kWave - 1) wsum[wave] = x;
+      __syncthreads();
+      int pre = carry, all = carry;
+      for (int w = 0; w < W; ++w) {
+        if (w < wave) pre += wsum[w];
+        all += wsum[w];
+      }
+      pre += x - n;
+      for (int j = 0; j < n; ++j) {
+        const int s = pass == 0 ? j : nfull;
+        t.s = s;
+        t.t0 = s * kTilesPerSplit;
+        t.cnt = pass == 0 ? kTilesPerSplit : rem;
+        tasks[pre + j] = t;
+      }
+      carry = all;
+      __syncthreads();
+    }
+  }
+  if (tid == 0) ctl[0] = carry;
 }
 
-constexpr int kMaxLdsTabBlocks = 64;  // cos/sin table of up to 64 shared blocks in LDS
+// Per diff entry e of row r = i * L + l: info[e] = (beta, b) with b the shared
+// block holding the entry's first token (~b when the 16 tokens span more than
+// one block), and cs[e][0 .. D/2) = the (cos, sin) row of Delta(i, b).  One
+// workgroup per row, one wave per entry; the lanes test 64 blocks at a time.
+constexpr int kDiffTabThreads = 256;
+__global__ __launch_bounds__(kDiffTabThreads) void diff_tab_kernel(const int32_t* __restrict__ diff_off,
+                                                                   const int32_t* __restrict__ diff_idx,
+                                                                   const int32_t* __restrict__ blk_start,
+                                                                   const float2* __restrict__ tab, int L, int B,
+                                                                   int nb, int half, long long cap,
+                                                                   float2* __restrict__ cs, int2* __restrict__ info) {
+  const int r = blockIdx.x;
+  const int i = r / L;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int e0 = diff_off[r];
+  const int e1 = e0 + min(max(diff_off[r + 1] - e0, 0), nb);
+  for (int e = e0 + wave; e < e1; e += kDiffTabThreads / kWave) {
+    if (e < 0 || e >= cap) break;  // uniform
+    const int t0 = diff_idx[e] * kTile;
+    // b = the largest block with blk_start[b] <= t0 (empty blocks skipped)
+    int b = 0;
+    for (int c = 0; c < B; c += kWave) {
+      const int x = c + lane;
+      const uint64_t m = __ballot(x < B && blk_start[x] <= t0);
+      if (m != 0) b = c + 63 - __clzll(m);
+      if (m != ~0ull) break;  // the first block past t0 is in this chunk
+    }
+    const bool straddle = blk_start[b + 1] < t0 + kTile;
+    if (lane == 0) info[e] = make_int2(t0 / kTile, straddle ? ~b : b);
+    for (int x = lane; x < half; x += kWave) cs[(size_t)e * half + x] = tab[((size_t)i * B + b) * half + x];
+  }
+}
 
-// TAB_LDS: the agent's cos/sin table sits in LDS (B <= kMaxLdsTabBlocks),
-// else diff tiles read it from the workspace.
-#ifndef TDX_AG_WPE
-#define TDX_AG_WPE 2
-#endif
-template <typename E, int D, int MODE, int NW, int PD, bool TAB_LDS>
-__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(TDX_AG_WPE))) void agent_kernel(
-    AttnArgs a) {
-  using St = Stage<E, D>;
+template <typename E, int D, int MODE, int PD>
+__global__ __launch_bounds__(kStreamNW * kWave) __attribute__((amdgpu_waves_per_eu(TDX_ST_WPE))) void stream_kernel(
+    AttnArgs a, const StreamTask* __restrict__ tasks, const int32_t* __restrict__ ctl, const float2* __restrict__ dcs,
+    const int2* __restrict__ dinfo) {
+  using St = Stage<E, D, MODE>;
   constexpr int KD = St::KD;
   constexpr int DT = D / 16;
   constexpr int HALF = D / 2;
-  constexpr int NT = NW * kWave;
   constexpr int RB = D * (int)sizeof(E);  // K/V row bytes of one head
   constexpr int CPR = RB / 16;            // 16-byte chunks per K/V row
+  constexpr int KB = kTile * RB;          // K tile bytes (as stored)
   constexpr int VB = kTile * D * 2;       // bf16 V tile bytes
+  constexpr int CB = MODE == FUSED ? HALF * 8 : 0;  // cos/sin row of a diff entry
   extern __shared__ __align__(16) unsigned char smem[];
-  const size_t vbytes = (size_t)NW * VB;
-  const size_t cbytes = (size_t)NW * 16 * (D + 2) * 4;
-  int32_t* tbeta = reinterpret_cast<int32_t*>(smem + (vbytes > cbytes ? vbytes : cbytes));  // [TPS]
-  int32_t* sblk = tbeta + kTilesPerSplit;                                                    // [B+1]
-  float2* stab = reinterpret_cast<float2*>(sblk + ((a.B + 2) & ~1));                        // [B][HALF]
 
-  const int i = blockIdx.x;
-  const int s = blockIdx.y;
-  const int l = blockIdx.z / a.Hkv;
-  const int h = blockIdx.z % a.Hkv;
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform per wave
   const int q4 = lane / 16, c16 = lane % 16;
   const int g = a.Hq / a.Hkv;
+  const int Hkv = a.Hkv;
+  const int nht = ctl[0] * Hkv;  // (task, head) pairs
+  const int gw = blockIdx.x * kStreamNW + wave;
+  if (gw >= nht) return;  // wave-uniform; the kernel has no workgroup barrier
 
-  const size_t ptot = (size_t)a.priv_off[a.N];  // private rows per layer
-  const int p0 = a.priv_off[i];
-  const int P = a.priv_off[i + 1] - p0;
-  const int ntp = (P + kTile - 1) / kTile;
-  int e0 = 0, nx;
-  if (MODE == FUSED) {
-    const int r = i * a.L + l;
-    e0 = a.diff_off[r];
-    nx = a.diff_off[r + 1] - e0;
-  } else {
-    nx = a.T / kTile;
+  unsigned char* kl = smem + (size_t)wave * (KB + VB + CB);  // this wave's K tile
+  unsigned char* vl = kl + KB;                               // V tile
+  float2* csl = reinterpret_cast<float2*>(vl + VB);          // cos/sin row
+  const size_t rowHD = (size_t)Hkv * D;
+  const size_t rowbytes = rowHD * sizeof(E);
+  const unsigned char* pkb = static_cast<const unsigned char*>(a.pk);
+  const unsigned char* pvb = static_cast<const unsigned char*>(a.pv);
+
+  // Per-lane byte offsets inside a tile: 16-byte chunk p = 64 v + lane is
+  // row p / CPR, chunk p % CPR.  A tile's loads are a uniform base plus these.
+  uint32_t loff[St::NV], lcol[St::NV];
+#pragma unroll
+  for (int v = 0; v < St::NV; ++v) {
+    const int p = v * kWave + lane;
+    lcol[v] = (uint32_t)(p % CPR) * 16u;
+    loff[v] = (uint32_t)(p / CPR) * (uint32_t)rowbytes + lcol[v];
   }
-  const int ntiles = ntp + nx;
-  const int tbeg = s * kTilesPerSplit;
-  if (tbeg >= ntiles) return;  // uniform: this agent needs fewer splits
-  const int tend = min(tbeg + kTilesPerSplit, ntiles);
+  auto steps = [](const StreamTask& t) { return max(t.cnt, PD - 1); };
+  // the query rows of (agent, layer, KV head) as the B operand: row min(c16, g-1),
+  // elements 32k + 8*q4 .. +7 (rows >= g repeat row g-1; their logits are unused)
+  auto load_q = [&](const StreamTask& t, int h, u32x4* qv) {
+    const uint16_t* qp = a.qplain + ((size_t)t.r * a.Hq + (size_t)h * g + min(c16, g - 1)) * D;
+#pragma unroll
+    for (int k = 0; k < KD; ++k) qv[k] = ld16(qp + 32 * k + 8 * q4);
+  };
+  // Wave gw takes the (task, head) pairs gw, gw + NWV, gw + 2 NWV, ...: the
+  // waves of a workgroup work on neighbouring KV heads of the same rows.
+  const int NWV = gridDim.x * kStreamNW;
 
-  // the agent's plain query rows (bf16): row min(c16, g-1), elements 32k + 8*q4
-  const int qrow = min(c16, g - 1);  // rows >= g repeat row g-1 (unused columns)
-  const uint16_t* qp = a.qplain + (((size_t)i * a.L + l) * a.Hq + (size_t)h * g + qrow) * D;
+  // ---- load side: (task, head) lk, its descriptor LT, step lu; the next
+  // pair nk and its descriptor ND
+  int lk = gw, lh = gw % Hkv, lu = 0;
+  StreamTask LT = tasks[gw / Hkv];
+  u32x4 qn[KD];
+  load_q(LT, lh, qn);
+  int nk = gw + NWV;
+  StreamTask ND = LT;
+  if (nk < nht) ND = tasks[nk / Hkv];
+  bool ldone = false;
+
+  // ---- compute side: (task, head) pk of descriptor PT at step pu; the first
+  // PD-1 steps only fill the pipeline
+  int pk = 0, ph = 0, pu = -(PD - 1);
+  StreamTask PT = LT;
   u32x4 qop[KD];
 #pragma unroll
-  for (int k = 0; k < KD; ++k) qop[k] = ld16(qp + 32 * k + 8 * q4);
-
-  if (MODE == FUSED) {
-    for (int b = tid; b <= a.B; b += NT) sblk[b] = a.blk_start[b];
-    for (int u = tbeg + ntp + tid - ntp; u < tend; u += NT)
-      if (u >= ntp) tbeta[u - tbeg] = a.diff_idx[e0 + u - ntp];
-    if (TAB_LDS) {
-      const float2* gt = a.tab + (size_t)i * a.B * HALF;
-      for (int x = tid; x < a.B * HALF; x += NT) stab[x] = gt[x];
-    }
-  }
-  __syncthreads();
-
+  for (int k = 0; k < KD; ++k) qop[k] = u32x4{0, 0, 0, 0};
   RowState<D> st;
   st.init();
-  const size_t rowHD = (size_t)a.Hkv * D;
-  const size_t rowbytes = rowHD * sizeof(E);
-  const unsigned char* pkb = reinterpret_cast<const unsigned char*>(
-      static_cast<const E*>(a.pk) + ((size_t)l * ptot + p0) * rowHD + (size_t)h * D);
-  const unsigned char* pvb = reinterpret_cast<const unsigned char*>(
-      static_cast<const E*>(a.pv) + ((size_t)l * ptot + p0) * rowHD + (size_t)h * D);
-  unsigned char* vl = smem + (size_t)wave * VB;  // this wave's V tile
-  const float2* tabrow = TAB_LDS ? stab : a.tab + (size_t)i * a.B * HALF;
 
-  // Issue the loads of tile u into stage S (the same count on every path).
-  auto load = [&](int u, St& S) {
+  auto load = [&](St& S) {
+    if (lu == steps(LT) && !ldone) {  // next task (uniform)
+      if (nk < nht) {
+        lk = nk;
+        lh = lk % Hkv;
+        LT = ND;
+        lu = 0;
+        load_q(LT, lh, qn);
+        nk = lk + NWV;
+        if (nk < nht) ND = tasks[nk / Hkv];
+      } else {
+        ldone = true;  // no more work: keep re-reading the last tile (masked)
+        lk = nht;
+      }
+    }
+    const int su = min(lu, steps(LT) - 1);
+    const int u = LT.t0 + min(su, LT.cnt - 1);  // tile of the row (uniform)
     const unsigned char* kb;
     const unsigned char* vb;
     int rmax = kTile - 1;  // rows past the end of a partial tile re-read its last row
-    if (u < ntp) {
-      kb = pkb + (size_t)u * kTile * rowbytes;
-      vb = pvb + (size_t)u * kTile * rowbytes;
-      rmax = min(kTile - 1, P - 1 - u * kTile);
+    size_t e = 0;
+    if (u < LT.ntp) {
+      const size_t o = (((size_t)LT.prow + (size_t)u * kTile) * rowHD + (size_t)lh * D) * sizeof(E);
+      kb = pkb + o;
+      vb = pvb + o;
+      rmax = min(kTile - 1, LT.P - 1 - u * kTile);
     } else if (MODE == FUSED) {
-      const size_t o = ((size_t)(e0 + u - ntp) * kTile * rowHD + (size_t)h * D) * sizeof(E);
+      e = (size_t)(LT.e0 + u - LT.ntp);
+      const size_t o = (e * kTile * rowHD + (size_t)lh * D) * sizeof(E);
       kb = static_cast<const unsigned char*>(a.dk) + o;
       vb = static_cast<const unsigned char*>(a.dv) + o;
     } else {
-      const size_t o = ((((size_t)i * a.L + l) * a.T + (size_t)(u - ntp) * kTile) * rowHD + (size_t)h * D) * sizeof(E);
+      const size_t o = (((size_t)LT.r * a.T + (size_t)(u - LT.ntp) * kTile) * rowHD + (size_t)lh * D) * sizeof(E);
       kb = static_cast<const unsigned char*>(a.sk) + o;
       vb = static_cast<const unsigned char*>(a.sv) + o;
     }
-    // K: row c16, elements 32k + 8*q4 .. +7
-    const unsigned char* kr = kb + (size_t)min(c16, rmax) * rowbytes;
-#pragma unroll
-    for (int k = 0; k < St::KL; ++k)
-      S.k[k] = ag_ldk(kr + (sizeof(E) == 2 ? (32 * k + 8 * q4) * 2 : (32 * (k / 2) + 8 * q4 + 4 * (k % 2)) * 4));
-    // V: 16-byte chunk p = 64 v + lane of the tile = row p / CPR, chunk p % CPR
+    // min(row, rmax) * rowbytes + column = min(loff, rmax * rowbytes + column)
+    const uint32_t rlim = (uint32_t)rmax * (uint32_t)rowbytes;
 #pragma unroll
     for (int v = 0; v < St::NV; ++v) {
-      const int p = v * kWave + lane;
-      S.v[v] = ag_ldv(vb + (size_t)min(p / CPR, rmax) * rowbytes + (p % CPR) * 16);
+      const uint32_t o = min(loff[v], rlim + lcol[v]);
+      S.k[v] = ld16_nt(kb + o);
+      S.v[v] = ld16_nt(vb + o);
+    }
+    if (MODE == FUSED) {  // a private tile reads entry 0 (unused)
+      const size_t ec = e < (size_t)a.dcap ? e : 0;
+      S.cs = dcs[ec * HALF + (lane % HALF)];
+      S.info = dinfo[ec];  // uniform address: a scalar load
+    }
+    if (!ldone) ++lu;
+  };
+
+  // compute side, before the step's loads: a new task starts with the load
+  // side's current one (the load side is at most PD-2 tiles ahead and a task
+  // has at least PD-1 steps)
+  auto begin = [&]() {
+    if (pu == 0) {
+      PT = LT;
+      pk = lk;
+      ph = lh;
+#pragma unroll
+      for (int k = 0; k < KD; ++k) qop[k] = qn[k];
     }
   };
 
-  // live = false: a pipeline fill/drain step; every score is masked, so the
-  // stage contents (zeros, or a re-read of the last tile) add nothing
-  auto process = [&](St& S, int u, bool live) {
-    // V rows -> bf16 LDS tile (a wave's LDS operations run in order, so the
-    // previous tile's transposed reads have completed before these writes)
+  auto process = [&](St& S) {
+    const bool live = pk < nht && pu >= 0 && pu < PT.cnt;
+    const int u = PT.t0 + min(max(pu, 0), PT.cnt - 1);
+    // K rows -> LDS as loaded, V rows -> bf16 LDS tile (a wave's LDS
+    // operations run in order, so the previous tile's reads are done)
 #pragma unroll
     for (int v = 0; v < St::NV; ++v) {
       const int p = v * kWave + lane;
+      *reinterpret_cast<u32x4*>(kl + klds_off<CPR>(p / CPR, p % CPR)) = S.k[v];
       if constexpr (sizeof(E) == 2) {
         *reinterpret_cast<u32x4*>(vl + vlds_off<D>(p / CPR, p % CPR)) = S.v[v];
       } else {
@@ -708,41 +850,71 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(TDX_
         *reinterpret_cast<uint2*>(vl + vlds_off<D>(t, c4 / 2) + (c4 % 2) * 8) = w;
       }
     }
+    const bool rot = MODE == FUSED && u >= PT.ntp;  // the agent's own block (wave-uniform)
+    if (MODE == FUSED && lane < HALF) csl[lane] = S.cs;
     wave_sync();
-    // K chunks as floats: x[k][j] = K[row c16][32k + 8*q4 + j]
-    float x[KD][8];
+    // K operand of the QK product: kop[k] = K[row c16][32k + 8*q4 .. +7] as bf16
+    u32x4 kop[KD];
+    if constexpr (sizeof(E) == 2) {
 #pragma unroll
-    for (int k = 0; k < KD; ++k) {
-      if constexpr (sizeof(E) == 2) {
-        Fmt<uint16_t>::unpack(S.k[k], x[k]);
-      } else {
-        Fmt<float>::unpack(S.k[2 * k], x[k]);
-        Fmt<float>::unpack(S.k[2 * k + 1], x[k] + 4);
-      }
+      for (int k = 0; k < KD; ++k) kop[k] = *reinterpret_cast<const u32x4*>(kl + klds_off<CPR>(c16, 4 * k + q4));
     }
-    if (MODE == FUSED && u >= ntp) {
-      // the agent's own block: rotate this lane's key row by the shift of the
-      // shared block holding it; pairs (e, e + D/2) are chunks k and k + KD/2
-      const int t = tbeta[u - tbeg] * kTile + c16;
-      const int b = block_of(sblk, a.B, t);
-      const float2* cs = tabrow + (size_t)b * HALF;
+    if (sizeof(E) == 4 || rot) {
+      float x[KD][8];
 #pragma unroll
-      for (int k = 0; k < KD / 2; ++k)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float2 c = cs[32 * k + 8 * q4 + j];
-          const float lo = x[k][j], hi = x[k + KD / 2][j];
-          x[k][j] = lo * c.x - hi * c.y;
-          x[k + KD / 2][j] = hi * c.x + lo * c.y;
+      for (int k = 0; k < KD; ++k) {
+        if constexpr (sizeof(E) == 2) {
+          Fmt<uint16_t>::unpack(kop[k], x[k]);
+        } else {
+          Fmt<float>::unpack(*reinterpret_cast<const u32x4*>(kl + klds_off<CPR>(c16, 8 * k + 2 * q4)), x[k]);
+          Fmt<float>::unpack(*reinterpret_cast<const u32x4*>(kl + klds_off<CPR>(c16, 8 * k + 2 * q4 + 1)), x[k] + 4);
         }
+      }
+      // rotate this lane's key row by the shift of the shared block holding
+      // it; pairs (e, e + D/2) are chunks k and k + KD/2
+      auto rotate = [&](auto row) {
+#pragma unroll
+        for (int k = 0; k < KD / 2; ++k) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int ce = 2 * (32 * k + 8 * q4 + j);  // (cos, sin) of element 32k + 8*q4 + j
+            const float cc = row[ce], sn = row[ce + 1];
+            const float lo = x[k][j], hi = x[k + KD / 2][j];
+            x[k][j] = lo * cc - hi * sn;
+            x[k + KD / 2][j] = hi * cc + lo * sn;
+          }
+          kop[k] = Fmt<uint16_t>::pack(x[k]);
+          kop[k + KD / 2] = Fmt<uint16_t>::pack(x[k + KD / 2]);
+        }
+      };
+      if (rot && S.info.y >= 0) {
+        // the whole tile lies in one shared block: its cos/sin row in LDS
+        typedef __attribute__((address_space(3))) const float lds_float;
+        rotate((lds_float*)csl);
+      } else if (rot) {
+        // rows in several shared blocks: each row's own block, from the round's table
+        const int t = S.info.x * kTile + c16;
+        int lo = 0, hi = a.B - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (a.blk_start[mid] <= t) lo = mid; else hi = mid - 1;
+        }
+        typedef __attribute__((address_space(1))) const float global_float;
+        rotate((global_float*)(a.tab + ((size_t)(PT.r / a.L) * a.B + lo) * HALF));
+      } else {
+#pragma unroll
+        for (int k = 0; k < KD; ++k) kop[k] = Fmt<uint16_t>::pack(x[k]);
+      }
     }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < KD; ++k) acc = mfma32(Fmt<uint16_t>::pack(x[k]), qop[k], acc);
+    for (int k = 0; k < KD; ++k) acc = mfma32(kop[k], qop[k], acc);
+    // rows >= lim of the tile are masked (lim = 16 for a full tile, less for
+    // the last private tile, 0 for a fill, pad or drain step)
+    const int lim = !live ? 0 : (u < PT.ntp ? min(kTile, PT.P - u * kTile) : kTile);
     float z[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      z[j] = live && (u >= ntp || u * kTile + 4 * q4 + j < P) ? acc[j] * a.scale_log2 : -INFINITY;
+    for (int j = 0; j < 4; ++j) z[j] = 4 * q4 + j < lim ? acc[j] * a.scale_log2 : -INFINITY;
     // PV operand: va[dt][j] = V[token 4*q4 + j][dim 16*dt + c16]; this lane
     // addresses row 4*q4 + c16/4, dims 16*dt + 4*(c16%4)
     i16x4 va[DT];
@@ -751,66 +923,41 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(TDX_
     for (int dt = 0; dt < DT; ++dt)
       va[dt] = ld_tr16(vl + vlds_off<D>(vrow, 2 * dt + ((c16 & 3) >> 1)) + (c16 & 1) * 8);
     softmax_pv<D>(st, z, va);
+    // advance; at the end of a task write its record and start afresh
+    if (pu < 0) {
+      ++pu;
+    } else if (++pu == steps(PT)) {
+      if (pk < nht) {
+        float lsum = st.l;
+        lsum += __shfl_xor(lsum, 16, kWave);
+        lsum += __shfl_xor(lsum, 32, kWave);
+        if (c16 < g) {
+          float* rec = a.part + (((size_t)PT.r * a.Hq + (size_t)ph * g + c16) * a.S + PT.s) * (D + 4);
+          write_record<D>(rec, st, lsum, q4, c16);
+        }
+      }
+      st.init();
+      pu = 0;
+    }
   };
 
-  // each wave walks a contiguous run of tiles; PD-1 tiles are always in
-  // flight.  Step k of the unrolled body always loads into S[(k+PD-1) % PD]
-  // and uses S[k], with no branch around either: the pipeline fills in the
-  // first pass (masked steps over zeroed stages) and drains in the last one
-  // (masked steps over re-reads of the last tile).  Every stage then lives in
-  // the same registers on every pass and the hardware wait before a stage is
-  // used leaves the PD-1 younger tiles in flight.
-  const int span = (tend - tbeg + NW - 1) / NW;
-  const int ubeg = tbeg + wave * span;
-  const int uend = min(ubeg + span, tend);
-  if (ubeg < uend) {
-    St S[PD] = {};  // zeros for the fill steps
-    for (int u0 = ubeg - (PD - 1); u0 < uend; u0 += PD) {
+  // PD-stage register pipeline: step k of the unrolled body loads into
+  // S[(k+PD-1) % PD] and uses S[k], with no branch around either, so every
+  // stage lives in the same registers on every pass and the wait before a
+  // stage is used leaves the PD-1 younger tiles in flight.  The loop runs
+  // until the compute side has passed its last task (masked steps after it).
+  St S[PD] = {};
+  // the first query loads complete here, once: otherwise the compiler's wait
+  // counting sees them outstanding at the top of the loop
+  __builtin_amdgcn_s_waitcnt(0);
+  do {
 #pragma unroll
-      for (int k = 0; k < PD; ++k) {
-        const int u = u0 + k;  // tile used in this step (wave-uniform)
-        load(min(u + PD - 1, uend - 1), S[(k + PD - 1) % PD]);
-        process(S[k], min(max(u, ubeg), uend - 1), u >= ubeg && u < uend);
-      }
+    for (int k = 0; k < PD; ++k) {
+      begin();
+      load(S[(k + PD - 1) % PD]);
+      process(S[k]);
     }
-  }
-
-  // ---- combine the waves (LDS aliases the V tiles)
-  __syncthreads();
-  float* cm = reinterpret_cast<float*>(smem);  // [NW][16] max
-  float* cl = cm + NW * 16;                     // [NW][16] sum
-  float* co = cl + NW * 16;                     // [NW][16][D]
-  float lsum = st.l;
-  lsum += __shfl_xor(lsum, 16, kWave);
-  lsum += __shfl_xor(lsum, 32, kWave);
-  if (q4 == 0) {
-    cm[wave * 16 + c16] = st.m;
-    cl[wave * 16 + c16] = lsum;
-  }
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-    *reinterpret_cast<f32x4*>(co + ((size_t)wave * 16 + c16) * D + dt * 16 + 4 * q4) = st.o[dt];
-  __syncthreads();
-  const size_t rec = D + 4;
-  for (int x = tid; x < g * D; x += NT) {
-    const int r = x / D, d = x % D;
-    float mm = -INFINITY;
-    for (int w = 0; w < NW; ++w) mm = fmaxf(mm, cm[w * 16 + r]);
-    float o = 0.f, ls = 0.f;
-    if (mm != -INFINITY) {
-      for (int w = 0; w < NW; ++w) {
-        const float f = exp2f(cm[w * 16 + r] - mm);
-        o += f * co[((size_t)w * 16 + r) * D + d];
-        ls += f * cl[w * 16 + r];
-      }
-    }
-    float* dst = a.part + ((((size_t)i * a.L + l) * a.Hq + (size_t)h * g + r) * a.S + s) * rec;
-    dst[4 + d] = o;
-    if (d == 0) {
-      dst[0] = mm;
-      dst[1] = ls;
-    }
-  }
+  } while (pk < nht);
 }
 
 // bf16 copy of the queries (the MFMA operand form): qplain[i][l][hq][D]
@@ -831,7 +978,8 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, E* __restrict__ 
   const int i = (int)(row / ((size_t)a.L * a.Hq));
   const int l = (int)((row / a.Hq) % a.L);
   const int P = a.priv_off[i + 1] - a.priv_off[i];
-  const int nx = (MODE == FUSED) ? a.diff_off[i * a.L + l + 1] - a.diff_off[i * a.L + l] : a.T / kTile;
+  const int nx = (MODE == FUSED) ? min(max(a.diff_off[i * a.L + l + 1] - a.diff_off[i * a.L + l], 0), a.T / kTile)
+                                  : a.T / kTile;
   const int nt = (P + kTile - 1) / kTile + nx;
   const int nsp = min((nt + kTilesPerSplit - 1) / kTilesPerSplit, a.SP);
   const size_t rec = D + 4;
@@ -957,7 +1105,8 @@ __global__ __launch_bounds__(kThreads) void restore_dense_kernel(
 
 struct Plan {
   int SP, SG, AGS, NAG, TPG, n_sh_wg;
-  size_t part_bytes, tab_off, qrot_off, qplain_off, total;
+  long long dcap;
+  size_t part_bytes, tab_off, qrot_off, qplain_off, task_off, ctl_off, dcs_off, dinfo_off, total;
 };
 
 Plan make_plan(const Dims& d, int max_priv, bool fused) {
@@ -980,29 +1129,30 @@ Plan make_plan(const Dims& d, int max_priv, bool fused) {
     p.SG = (nb + p.TPG - 1) / p.TPG;
     p.n_sh_wg = p.NAG * p.SG * d.L * d.Hkv;
   }
+  // a valid diff record has at most T/16 entries per (agent, layer) row
+  p.dcap = fused ? (long long)d.N * d.L * nb : 0;
+  if (p.dcap < 1) p.dcap = 1;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   p.part_bytes = (size_t)d.N * d.L * d.Hq * (p.SP + p.SG) * (d.D + 4) * 4;
   p.tab_off = up(p.part_bytes);
   p.qrot_off = p.tab_off + (fused ? up((size_t)d.N * d.B * (d.D / 2) * 8) : 0);
   p.qplain_off = p.qrot_off + (fused ? up((size_t)d.N * d.L * d.B * d.Hq * d.D * 2) : 0);
-  p.total = p.qplain_off + up((size_t)d.N * d.L * d.Hq * d.D * 2);
+  p.task_off = p.qplain_off + up((size_t)d.N * d.L * d.Hq * d.D * 2);
+  p.ctl_off = p.task_off + up((size_t)d.N * d.L * p.SP * sizeof(StreamTask));
+  p.dcs_off = p.ctl_off + 256;
+  p.dinfo_off = p.dcs_off + (fused ? up((size_t)p.dcap * (d.D / 2) * 8) : 0);
+  p.total = p.dinfo_off + (fused ? up((size_t)p.dcap * 8) : 0);
   return p;
 }
 
-template <int D, int NW>
-size_t agent_lds(int B, bool fused, bool tab_lds) {
-  const size_t vbytes = (size_t)NW * kTile * D * 2;
-  const size_t cbytes = (size_t)NW * 16 * (D + 2) * 4;
-  return (vbytes > cbytes ? vbytes : cbytes) + (size_t)kTilesPerSplit * 4 + (size_t)((B + 2) & ~1) * 4 +
-         (fused && tab_lds ? (size_t)B * (D / 2) * 8 : 0);
-}
-
-// waves per workgroup / register stages of agent_kernel: PD stages keep PD-1
-// tiles in flight per wave; fp32 rows of 128 dims take twice the registers
+// register stages of stream_kernel: PD stages keep PD-1 tiles in flight per
+// wave; fp32 rows of 128 dims take twice the registers
 template <typename E, int D>
-struct AgentCfg {
-  static constexpr int NW = TDX_AG_NW;
-  static constexpr int PD = (sizeof(E) == 4 && D == 128) ? 2 : TDX_AG_PD;
+struct StreamCfg {
+  static constexpr int PD = (sizeof(E) == 4 && D == 128) ? 2 : TDX_ST_PD;
+  static constexpr size_t lds(bool fused) {
+    return (size_t)kStreamNW * (kTile * D * sizeof(E) + kTile * D * 2 + (fused ? D / 2 * 8 : 0));
+  }
 };
 
 size_t shared_lds(int D, int B, const Plan& p) {
@@ -1018,6 +1168,7 @@ hipError_t launch_attn_t(const Dims& d, AttnArgs a, const Plan& p, E* out, hipSt
   a.NAG = p.NAG;
   a.TPG = p.TPG;
   a.n_sh_wg = p.n_sh_wg;
+  a.dcap = p.dcap;
   hipError_t e;
   if (MODE == FUSED) {
     const size_t nq = (size_t)d.N * d.L * d.B * d.Hq * (D / 16);
@@ -1038,15 +1189,24 @@ hipError_t launch_attn_t(const Dims& d, AttnArgs a, const Plan& p, E* out, hipSt
                        a.qplain);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  constexpr int NW = AgentCfg<E, D>::NW, PD = AgentCfg<E, D>::PD;
-  const bool tab_lds = d.B <= kMaxLdsTabBlocks;
-  const size_t lds = agent_lds<D, NW>(d.B, MODE == FUSED, tab_lds);
-  if (lds > 160 * 1024) return hipErrorInvalidValue;
-  const dim3 agrid(d.N, p.SP, d.L * d.Hkv);
-  if (tab_lds)
-    hipLaunchKernelGGL((agent_kernel<E, D, MODE, NW, PD, true>), agrid, dim3(NW * kWave), lds, s, a);
-  else
-    hipLaunchKernelGGL((agent_kernel<E, D, MODE, NW, PD, false>), agrid, dim3(NW * kWave), lds, s, a);
+  constexpr int PD = StreamCfg<E, D>::PD;
+  const size_t lds = StreamCfg<E, D>::lds(MODE == FUSED);
+  auto kern = stream_kernel<E, D, MODE, PD>;
+  int dev = 0, ncu = 0, per_cu = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern),
+                                                         kStreamNW * kWave, lds)) != hipSuccess)
+    return e;
+  if (per_cu < 1) return hipErrorInvalidConfiguration;
+  const int grid = ncu * per_cu;  // resident workgroups; each wave takes every NWV-th (task, head)
+  StreamTask* tasks = reinterpret_cast<StreamTask*>(a.ws_base + p.task_off);
+  int32_t* ctl = reinterpret_cast<int32_t*>(a.ws_base + p.ctl_off);  // task count
+  const float2* dcs = reinterpret_cast<const float2*>(a.ws_base + p.dcs_off);
+  const int2* dinfo = reinterpret_cast<const int2*>(a.ws_base + p.dinfo_off);
+  hipLaunchKernelGGL((stream_plan_kernel<MODE>), dim3(1), dim3(kPlanThreads), 0, s, a, tasks, ctl);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kStreamNW * kWave), lds, s, a, tasks, ctl, dcs, dinfo);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t rows = (size_t)d.N * d.L * d.Hq;
   const int rpb = 256 / kWave;
@@ -1072,6 +1232,7 @@ AttnArgs common_args(const Dims& d, const void* q, const int32_t* priv_off, cons
   a.pk = pk;
   a.pv = pv;
   a.part = static_cast<float*>(ws);
+  a.ws_base = static_cast<unsigned char*>(ws);
   a.N = d.N;
   a.L = d.L;
   a.T = d.T;
@@ -1113,6 +1274,13 @@ hipError_t launch_restore_attn(const Dims& d, const tdx_layout& lay, const void*
                      d.N, d.B, d.D, d.theta, tab);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (d.N * d.L > 0) {
+    hipLaunchKernelGGL(diff_tab_kernel, dim3(d.N * d.L), dim3(kDiffTabThreads), 0, s, diff_off, diff_idx, lay.blk_start,
+                       tab, d.L, d.B, d.T / kTile, d.D / 2, (long long)p.dcap,
+                       reinterpret_cast<float2*>(static_cast<unsigned char*>(ws) + p.dcs_off),
+                       reinterpret_cast<int2*>(static_cast<unsigned char*>(ws) + p.dinfo_off));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   return dispatch_attn<FUSED>(d, a, p, out, s);
 }
 
