@@ -6,11 +6,12 @@
 // (indices, values), one record per Mirror per layer.
 //
 // Kernels (all deterministic, no atomics on the data path):
-//  flag_kernel    one workgroup per (block beta, layer l, chunk slice): the
-//                 Master block's K and V sit in registers (16-byte chunks per
-//                 lane); every Mirror block is streamed once through a register
-//                 pipeline and compared bit for bit.  Optionally writes the
-//                 dense Master copy from the same registers.
+//  flag_kernel    resident workgroups over the (block beta, layer l, chunk
+//                 slice) items: per item the Master block's K and V are held
+//                 in registers (16-byte chunks per lane) and every Mirror
+//                 block is streamed once through a register pipeline that
+//                 runs on across items, and compared bit for bit.  Optionally
+//                 writes the dense Master copy from the same registers.
 //  rows_kernel    one workgroup per CSR row (agent, layer): OR of the slices'
 //                 flags, count of flagged blocks and each block's rank inside
 //                 its row.
@@ -27,77 +28,92 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kFlagThreads = 1024;
 constexpr int kCopyChunk = 8;
+constexpr int kCopyUnroll = 8;
 constexpr int kScanThreads = 1024;
 constexpr int kMaxAgents = 1024;
 
-// One workgroup per (block beta, layer l, chunk slice cs): the slice's
-// 16-byte chunks of the Master block sit in registers (KC per thread and
-// tensor) and the Mirrors' blocks stream through a PD-stage register
-// pipeline: while Mirror j is compared, Mirrors j+1 .. j+PD-1 are in flight.
-// The unrolled body has no branch around a load, so the wait before each
-// compare leaves the younger Mirrors' loads outstanding.  A wave that sees a
-// difference marks the Mirror in LDS; the marks become the slice's flags.
+// Persistent: workgroup g takes the items w = g, g + G, ... of the (block beta,
+// layer l, chunk slice cs) grid, beta fastest.  Per item it streams N blocks:
+// the Master's block first, then every Mirror's, through one PD-stage
+// register pipeline that runs on across items (each thread holds KC 16-byte
+// chunks of K and of V per stage).  The Master's chunks are kept aside and
+// every Mirror chunk is compared with them bit for bit; a wave that sees a
+// difference marks the Mirror in LDS (two mark buffers, by item parity), and
+// after the item's last block one barrier publishes the marks as the item's
+// flags.  The unrolled body has no branch around a load, so the wait before
+// a block is used leaves the younger blocks' loads outstanding.
 template <int KC, int PD>
 __global__ __launch_bounds__(kFlagThreads) void flag_kernel(
     const u32x4* __restrict__ ak, const u32x4* __restrict__ av,
-    const int32_t* __restrict__ master_p, int N, int L, int nb, int chunks,
+    const int32_t* __restrict__ master_p, int N, int L, int nb, int chunks, int nslices,
     uint8_t* __restrict__ flags, u32x4* __restrict__ mk_out, u32x4* __restrict__ mv_out) {
-  __shared__ uint8_t mark[kMaxAgents];
-  const int beta = blockIdx.x;
-  const int l = blockIdx.y;
-  const int cs = blockIdx.z;
+  __shared__ uint8_t mark[2][kMaxAgents];
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
+  const int G = gridDim.x;
+  const int nitems = nb * L * nslices;
   const int m = master_p[0];
-  uint8_t* fl = flags + (size_t)cs * N * L * nb;
+  const size_t slice_flags = (size_t)N * L * nb;
   if (m < 0 || m >= N) {  // invalid Master: no reads; offsets_kernel reports nnz = -1
-    for (int i = tid; i < N; i += kFlagThreads) fl[((size_t)i * L + l) * nb + beta] = 0;
+    for (int w = blockIdx.x; w < nitems; w += G) {
+      const int beta = w % nb, l = (w / nb) % L, cs = w / (nb * L);
+      for (int i = tid; i < N; i += kFlagThreads) flags[cs * slice_flags + ((size_t)i * L + l) * nb + beta] = 0;
+    }
     return;
   }
-  for (int i = tid; i < N; i += kFlagThreads) mark[i] = 0;
-  // this thread's chunks c0 + tid + 1024 j of the slice; lanes past the block
-  // end re-read its last chunk (the compare then sees equal data)
-  const int c0 = cs * KC * kFlagThreads;
-  int cidx[KC];
-#pragma unroll
-  for (int j = 0; j < KC; ++j) cidx[j] = min(c0 + tid + j * kFlagThreads, chunks - 1);
-  // chunk offset of (agent a, layer l, block beta): ((a*L + l)*nb + beta)*chunks
+  const int nw = (nitems - (int)blockIdx.x + G - 1) / G;  // this workgroup's items
+  if (nw <= 0) return;
+  for (int i = tid; i < 2 * kMaxAgents; i += kFlagThreads) (&mark[0][0])[i] = 0;
+  __syncthreads();
   const size_t layer_chunks = (size_t)nb * chunks;
-  const size_t mbase = ((size_t)m * L + l) * layer_chunks + (size_t)beta * chunks;
+  struct Blk {
+    u32x4 k[KC], v[KC];
+  };
+  // block p of the stream = item p / N, agent slot p % N (slot 0 = the Master,
+  // slot j > 0 = Mirror j - 1 = agent j - 1 + (j - 1 >= m)); lanes past the
+  // block end re-read its last chunk (the compare then sees equal data)
+  const long long nblk = (long long)nw * N;
+  auto load = [&](long long p, Blk& B) {
+    p = p < nblk ? p : nblk - 1;
+    const int w = (int)blockIdx.x + (int)(p / N) * G;
+    const int j = (int)(p % N);
+    const int a = j == 0 ? m : (j - 1) + (j - 1 >= m);
+    const int beta = w % nb, l = (w / nb) % L, cs = w / (nb * L);
+    const size_t base = ((size_t)a * L + l) * layer_chunks + (size_t)beta * chunks;
+    const int c0 = cs * KC * kFlagThreads;
+#pragma unroll
+    for (int q = 0; q < KC; ++q) {
+      const int c = min(c0 + tid + q * kFlagThreads, chunks - 1);
+      B.k[q] = ld16_nt(ak + base + c);
+      B.v[q] = ld16_nt(av + base + c);
+    }
+  };
   u32x4 mkr[KC], mvr[KC];
 #pragma unroll
-  for (int j = 0; j < KC; ++j) {
-    mkr[j] = ld16_nt(ak + mbase + cidx[j]);
-    mvr[j] = ld16_nt(av + mbase + cidx[j]);
-  }
-  if (mk_out != nullptr) {
-    const size_t obase = (size_t)l * layer_chunks + (size_t)beta * chunks;
-#pragma unroll
-    for (int j = 0; j < KC; ++j) {
-      const int c = c0 + tid + j * kFlagThreads;
-      if (c < chunks) {
-        __builtin_nontemporal_store(mkr[j], mk_out + obase + c);
-        __builtin_nontemporal_store(mvr[j], mv_out + obase + c);
-      }
-    }
-  }
-  __syncthreads();  // marks cleared
-  const int nm = N - 1;  // Mirror j is agent j + (j >= m)
-  if (nm > 0) {
-    struct Blk {
-      u32x4 k[KC], v[KC];
-    };
-    Blk S[PD] = {};
-    auto load = [&](int j, Blk& B) {
-      const int a = j + (j >= m);
-      const size_t base = ((size_t)a * L + l) * layer_chunks + (size_t)beta * chunks;
+  for (int q = 0; q < KC; ++q) mkr[q] = mvr[q] = u32x4{0, 0, 0, 0};
+  auto use = [&](long long p, const Blk& B, bool live) {
+    const int wi = (int)(p / N);
+    const int j = (int)(p % N);
+    if (j == 0) {  // the Master's block (uniform)
 #pragma unroll
       for (int q = 0; q < KC; ++q) {
-        B.k[q] = ld16_nt(ak + base + cidx[q]);
-        B.v[q] = ld16_nt(av + base + cidx[q]);
+        mkr[q] = B.k[q];
+        mvr[q] = B.v[q];
       }
-    };
-    auto compare = [&](const Blk& B, int j, bool live) {
+      if (mk_out != nullptr && live) {
+        const int w = (int)blockIdx.x + wi * G;
+        const int beta = w % nb, l = (w / nb) % L, cs = w / (nb * L);
+        const size_t obase = (size_t)l * layer_chunks + (size_t)beta * chunks;
+#pragma unroll
+        for (int q = 0; q < KC; ++q) {
+          const int c = cs * KC * kFlagThreads + tid + q * kFlagThreads;
+          if (c < chunks) {
+            __builtin_nontemporal_store(B.k[q], mk_out + obase + c);
+            __builtin_nontemporal_store(B.v[q], mv_out + obase + c);
+          }
+        }
+      }
+    } else {
       uint32_t acc = 0;
 #pragma unroll
       for (int q = 0; q < KC; ++q) {
@@ -105,19 +121,28 @@ __global__ __launch_bounds__(kFlagThreads) void flag_kernel(
         const u32x4 xv = B.v[q] ^ mvr[q];
         acc |= xk[0] | xk[1] | xk[2] | xk[3] | xv[0] | xv[1] | xv[2] | xv[3];
       }
-      if (__builtin_amdgcn_ballot_w64(live && acc != 0) != 0 && lane == 0) mark[j + (j >= m)] = 1;
-    };
-    for (int j0 = -(PD - 1); j0 < nm; j0 += PD) {
-#pragma unroll
-      for (int k = 0; k < PD; ++k) {
-        const int j = j0 + k;  // Mirror compared in this step (wave-uniform)
-        load(min(j + PD - 1, nm - 1), S[(k + PD - 1) % PD]);
-        compare(S[k], j, j >= 0 && j < nm);
+      const int a = (j - 1) + (j - 1 >= m);
+      if (__builtin_amdgcn_ballot_w64(live && acc != 0) != 0 && lane == 0) mark[wi & 1][a] = 1;
+    }
+    if (j == N - 1 && live) {  // the item's last block (uniform): publish its flags
+      __syncthreads();
+      const int w = (int)blockIdx.x + wi * G;
+      const int beta = w % nb, l = (w / nb) % L, cs = w / (nb * L);
+      for (int i = tid; i < N; i += kFlagThreads) {
+        flags[cs * slice_flags + ((size_t)i * L + l) * nb + beta] = mark[wi & 1][i];
+        mark[wi & 1][i] = 0;  // item wi + 2 reuses the buffer after item wi + 1's barrier
       }
     }
+  };
+  Blk S[PD] = {};
+  for (long long p0 = -(PD - 1); p0 < nblk; p0 += PD) {
+#pragma unroll
+    for (int k = 0; k < PD; ++k) {
+      const long long p = p0 + k;  // block used in this step (workgroup-uniform)
+      load(p + PD - 1, S[(k + PD - 1) % PD]);
+      use(p < 0 ? 0 : p, S[k], p >= 0 && p < nblk);
+    }
   }
-  __syncthreads();
-  for (int i = tid; i < N; i += kFlagThreads) fl[((size_t)i * L + l) * nb + beta] = mark[i];
 }
 
 __device__ __forceinline__ int lanemask_count(uint64_t m, int lane) {
@@ -220,9 +245,23 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(
     if (tid == 0) diff_idx[slot] = beta;
     const size_t src = (r * nb + beta) * (size_t)chunks;
     const size_t dst = (size_t)slot * chunks;
-    for (int c = tid; c < chunks; c += kThreads) {
-      cp_store(ld16_nt(ak + src + c), dk + dst + c);
-      cp_store(ld16_nt(av + src + c), dv + dst + c);
+    // kCopyUnroll chunks of K and of V per thread in flight, then their stores
+    for (int c0 = tid; c0 < chunks; c0 += kThreads * kCopyUnroll) {
+      u32x4 xk[kCopyUnroll], xv[kCopyUnroll];
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u) {
+        const int c = min(c0 + u * kThreads, chunks - 1);
+        xk[u] = ld16_nt(ak + src + c);
+        xv[u] = ld16_nt(av + src + c);
+      }
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u) {
+        const int c = c0 + u * kThreads;
+        if (c < chunks) {
+          cp_store(xk[u], dk + dst + c);
+          cp_store(xv[u], dv + dst + c);
+        }
+      }
     }
   }
 }
@@ -273,14 +312,24 @@ hipError_t launch_encode(const Dims& d, const int32_t* master, const void* ak, c
   u32x4* mv4 = static_cast<u32x4*>(mv_out);
   {
     const int ns = flag_slices(d);
-    dim3 grid(nb, d.L, ns);
-    if (flag_kc(d) == 1)
-      hipLaunchKernelGGL((flag_kernel<1, 8>), grid, dim3(kFlagThreads), 0, s, k4, v4, master, d.N, d.L, nb,
-                         chunks, flags, mk4, mv4);
-    else
-      hipLaunchKernelGGL((flag_kernel<2, 4>), grid, dim3(kFlagThreads), 0, s, k4, v4, master, d.N, d.L, nb,
-                         chunks, flags, mk4, mv4);
-    hipError_t e = hipGetLastError();
+    const int nitems = nb * d.L * ns;
+    hipError_t e;
+    int dev = 0, ncu = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    auto launch_flag = [&](auto kern) -> hipError_t {
+      int per_cu = 0;
+      hipError_t e2 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern),
+                                                                    kFlagThreads, 0);
+      if (e2 != hipSuccess) return e2;
+      int grid = ncu * (per_cu < 1 ? 1 : per_cu);  // resident workgroups
+      if (grid > nitems) grid = nitems;
+      if (grid < 1) grid = 1;
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(kFlagThreads), 0, s, k4, v4, master, d.N, d.L, nb, chunks, ns,
+                         flags, mk4, mv4);
+      return hipGetLastError();
+    };
+    e = flag_kc(d) == 1 ? launch_flag(flag_kernel<1, 8>) : launch_flag(flag_kernel<2, 4>);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(rows_kernel, dim3(rows), dim3(kThreads), 0, s, flags, nb, ns, (size_t)rows * nb, rank,
                        count);
