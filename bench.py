@@ -37,6 +37,14 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, "
+                         "both with --calib-copy) into HBM bytes per entry point and record them in "
+                         "profiles/traffic.json; runs no GPU work")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_STATS_CSV", "BENCH_LOG"),
+                    help="summarise a rocprofv3 --kernel-trace --stats run of this script: per-kernel "
+                         "average durations and each entry point's sum next to the HIP-event stage times "
+                         "of the run's JSON line; runs no GPU work")
     return ap.parse_args()
 
 
@@ -72,6 +80,101 @@ def recorded_traffic(entry: str, workload: str):
     if not r or r.get("workload") != workload or r.get("src_sha256") != source_hash():
         return None
     return int(r["fetch_bytes"]) + int(r["write_bytes"])
+
+
+# kernels of each timed entry point (one call of the entry point launches each
+# of them once); the dense comparator's kernels run outside the step
+ENTRY_KERNELS = {
+    "tdx_rerotate": ("rerotate_kernel",),
+    "tdx_select_important": ("deviation_kernel", "select_kernel"),
+    "tdx_diff_encode": ("flag_kernel", "rows_kernel", "offsets_kernel", "copy_kernel"),
+    "tdx_restore_attn": ("rope_table_kernel", "diff_tab_kernel", "qrot_kernel", "shared_kernel",
+                         "qplain_kernel", "stream_plan_kernel<0>", "stream_kernel<unsigned short, 128, 0",
+                         "stream_kernel<float, 128, 0", "stream_kernel<unsigned short, 64, 0",
+                         "stream_kernel<float, 64, 0", "merge_kernel<unsigned short, 128, 0>",
+                         "merge_kernel<float, 128, 0>", "merge_kernel<unsigned short, 64, 0>",
+                         "merge_kernel<float, 64, 0>"),
+}
+
+
+def _short_kernel(name: str) -> str:
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0].replace("tdx::", "")
+
+
+def _entry_of(kernel: str):
+    for entry, pats in ENTRY_KERNELS.items():
+        if any(kernel.startswith(p) for p in pats):
+            return entry
+    return None
+
+
+def pmc_summary(fetch_csv: str, write_csv: str, workload: str):
+    """HBM bytes per dispatch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB),
+    scaled by what the same counters read for the 1 GiB calibration copy."""
+    import csv
+    from collections import defaultdict
+
+    def per_kernel(path, counter):
+        vals = defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                vals[_short_kernel(r["Kernel_Name"])].append(float(r["Counter_Value"]) * 1024.0)
+        return vals
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    gib = float(1 << 30)
+    # the calibration copy: a copy kernel whose every dispatch wrote ~1 GiB
+    calib = [k for k, v in write.items() if "copy" in k.lower() and v and all(abs(x - gib) < 0.05 * gib for x in v)]
+    if not calib:
+        raise SystemExit("no 1 GiB calibration copy found: run the --pmc passes with --calib-copy")
+    ck = calib[0]
+    f_scale = gib / (sum(fetch[ck]) / len(fetch[ck]))
+    w_scale = gib / (sum(write[ck]) / len(write[ck]))
+    print(f"calibration ({ck}): FETCH_SIZE x {f_scale:.3f}, WRITE_SIZE x {w_scale:.3f}")
+    print(f"{'kernel (per dispatch, mean)':62s} {'read_MB':>10s} {'written_MB':>11s}")
+    rec = {}
+    for k in sorted(set(fetch) | set(write)):
+        e = _entry_of(k)
+        if e is None:
+            continue
+        fb = f_scale * sum(fetch.get(k, [0])) / max(1, len(fetch.get(k, [0])))
+        wb = w_scale * sum(write.get(k, [0])) / max(1, len(write.get(k, [0])))
+        print(f"{k[:62]:62s} {fb / 1e6:10.1f} {wb / 1e6:11.1f}")
+        r = rec.setdefault(e, {"workload": workload, "fetch_bytes": 0, "write_bytes": 0,
+                               "src_sha256": source_hash(), "fetch_scale": round(f_scale, 4),
+                               "write_scale": round(w_scale, 4)})
+        r["fetch_bytes"] += int(fb)
+        r["write_bytes"] += int(wb)
+    for e, r in rec.items():
+        print(f"{e:24s} read {r['fetch_bytes'] / 1e9:7.3f} GB  written {r['write_bytes'] / 1e9:7.3f} GB")
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print("recorded in", os.path.relpath(TRAFFIC_FILE, ROOT))
+
+
+def trace_summary(stats_csv: str, bench_log: str):
+    """Per-kernel average durations of a rocprofv3 --kernel-trace --stats run
+    and each entry point's sum next to the run's HIP-event stage times."""
+    import csv
+
+    rows = list(csv.DictReader(open(stats_csv)))
+    print(f"{'kernel':60s} {'calls':>6s} {'avg_us':>10s} {'total_us':>11s}")
+    avg = {}
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        k = _short_kernel(r["Name"])
+        avg[k] = float(r["AverageNs"]) / 1e3
+        print(f"{k[:60]:60s} {int(r['Calls']):6d} {avg[k]:10.1f} {float(r['TotalDurationNs']) / 1e3:11.1f}")
+    line = None
+    for ln in open(bench_log):
+        if ln.startswith("{"):
+            line = json.loads(ln)
+    stage_of = {v: k for k, v in ENTRY.items()}
+    print("\nentry point = sum of its kernels' averages (rocprofv3) vs the HIP-event time of the stage:")
+    for e in ENTRY_KERNELS:
+        us = sum(v for k, v in avg.items() if _entry_of(k) == e)
+        ev = line["stages"][stage_of[e]]["ms"] * 1e3 if line else float("nan")
+        print(f"  {e:26s} {us:9.1f} us   bench {ev:9.1f} us")
 
 
 def stage_bytes(cfg, lay, nnz_total, k):
@@ -175,6 +278,12 @@ def cpu_baseline(cfg, lay, pct, n_sample=8):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary, args.config)
+        return
+    if args.trace_summary:
+        trace_summary(*args.trace_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the collective reuse path here runs on a single "
               "MI355X (run with --gpus 1)", file=sys.stderr)

@@ -19,9 +19,15 @@ namespace tdx {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTileTok = 16;
+#ifndef TDX_RR_TILE
+#define TDX_RR_TILE 16
+#endif
+constexpr int kTileTok = TDX_RR_TILE;  // canonical tokens per workgroup
 constexpr int kAgentChunk = 32;  // agents whose cos/sin sit in LDS at once
-constexpr int kItems = 2;        // (token, head) rows per lane per batch
+#ifndef TDX_RR_ITEMS
+#define TDX_RR_ITEMS 2
+#endif
+constexpr int kItems = TDX_RR_ITEMS;  // (token, head) rows per lane per batch
 
 #ifndef TDX_RR_TARGET_WG
 #define TDX_RR_TARGET_WG 16384
@@ -39,6 +45,14 @@ __device__ __forceinline__ void st_out(E* p, const u32x4& v) {
 #endif
 }
 
+// Column of element e in an agent's cos/sin row in LDS: each lane reads the
+// VEC pairs of its chunk, and the groups of VEC pairs are padded by 2 pairs so
+// that the lanes' 16-byte reads of neighbouring groups fall in different banks.
+template <int VEC>
+__device__ __forceinline__ int tab_col(int e) {
+  return e + (e / VEC) * 2;
+}
+
 // One workgroup: canonical tokens [t0, t0+16) for layers [l0, l0+lpg).  The
 // (layer, batch) steps run in sequence and the next step's input is loaded
 // while the current one is written out for every agent.
@@ -51,9 +65,10 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(
   constexpr int HALF = D / 2;
   constexpr int G = HALF / VEC;       // lanes per (token, head) row
   constexpr int RPP = kThreads / G;   // rows covered by the workgroup per item
+  constexpr int TROW = HALF + 2 * G;  // padded cos/sin row of one agent (float2)
   extern __shared__ __align__(16) unsigned char smem[];
   float2* tab = reinterpret_cast<float2*>(smem);                      // [kAgentChunk][HALF]
-  double* invf = reinterpret_cast<double*>(tab + kAgentChunk * HALF);  // [HALF]
+  double* invf = reinterpret_cast<double*>(tab + kAgentChunk * TROW);  // [HALF]
   int32_t* sblk = reinterpret_cast<int32_t*>(invf + HALF);            // [B+1]
 
   const int tid = threadIdx.x;
@@ -96,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(
         const double delta = (double)(dst_pos[(size_t)(a0 + a) * B + b] - sp);
         double sn, cs;
         sincos(delta * invf[e], &sn, &cs);
-        tab[x] = make_float2((float)cs, (float)sn);
+        tab[a * TROW + tab_col<VEC>(e)] = make_float2((float)cs, (float)sn);
       }
       __syncthreads();
       // step = (layer, batch of rows)
@@ -123,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(
           float cs[VEC], sn[VEC];
 #pragma unroll
           for (int j = 0; j < VEC; ++j) {
-            const float2 v = tab[a * HALF + e0 + j];
+            const float2 v = tab[a * TROW + tab_col<VEC>(e0 + j)];
             cs[j] = v.x;
             sn[j] = v.y;
           }
@@ -170,7 +185,8 @@ hipError_t launch_t(const Dims& d, const tdx_layout& lay, const void* kc, void* 
   const int apg = (d.N + asplit - 1) / asplit;
   asplit = (d.N + apg - 1) / apg;
   dim3 grid(tiles, groups, asplit);
-  const size_t lds = (size_t)kAgentChunk * (D / 2) * 8 + (D / 2) * 8 + (size_t)(d.B + 1) * 4;
+  const size_t lds = (size_t)kAgentChunk * (D / 2 + 2 * (D / 2 / Fmt<E>::VEC)) * 8 + (D / 2) * 8 +
+                     (size_t)(d.B + 1) * 4;
   hipLaunchKernelGGL((rerotate_kernel<E, D>), grid, dim3(kThreads), lds, s,
                      static_cast<const E*>(kc), static_cast<E*>(out), lay.blk_start,
                      lay.src_pos, lay.dst_pos, d.N, d.B, d.T, d.L, d.Hkv, lpg, apg, d.theta);
