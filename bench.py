@@ -116,21 +116,26 @@ def pmc_summary(fetch_csv: str, write_csv: str, workload: str):
     from collections import defaultdict
 
     def per_kernel(path, counter):
-        vals = defaultdict(list)
+        vals, by_id = defaultdict(list), {}
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] == counter:
-                vals[_short_kernel(r["Kernel_Name"])].append(float(r["Counter_Value"]) * 1024.0)
-        return vals
+                k = _short_kernel(r["Kernel_Name"])
+                vals[k].append(float(r["Counter_Value"]) * 1024.0)
+                by_id[r["Dispatch_Id"]] = (k, float(r["Counter_Value"]) * 1024.0)
+        return vals, by_id
 
-    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    (fetch, fetch_id), (write, write_id) = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
     gib = float(1 << 30)
-    # the calibration copy: a copy kernel whose every dispatch wrote ~1 GiB
-    calib = [k for k, v in write.items() if "copy" in k.lower() and v and all(abs(x - gib) < 0.05 * gib for x in v)]
+    # the calibration copies: copy dispatches that wrote ~1 GiB; the two runs
+    # launch the same dispatches in the same order, so the fetch run's
+    # dispatches of the same ids are the same copies
+    calib = [i for i, (k, v) in write_id.items() if "copy" in k.lower() and abs(v - gib) < 0.05 * gib]
+    calib = [i for i in calib if i in fetch_id and "copy" in fetch_id[i][0].lower()]
     if not calib:
         raise SystemExit("no 1 GiB calibration copy found: run the --pmc passes with --calib-copy")
-    ck = calib[0]
-    f_scale = gib / (sum(fetch[ck]) / len(fetch[ck]))
-    w_scale = gib / (sum(write[ck]) / len(write[ck]))
+    ck = write_id[calib[0]][0]
+    f_scale = gib / (sum(fetch_id[i][1] for i in calib) / len(calib))
+    w_scale = gib / (sum(write_id[i][1] for i in calib) / len(calib))
     print(f"calibration ({ck}): FETCH_SIZE x {f_scale:.3f}, WRITE_SIZE x {w_scale:.3f}")
     print(f"{'kernel (per dispatch, mean)':62s} {'read_MB':>10s} {'written_MB':>11s}")
     rec = {}
