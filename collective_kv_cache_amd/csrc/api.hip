@@ -262,6 +262,75 @@ int tdx_restore_attn(const tdx_shape* shape, const tdx_layout* layout, const voi
   GUARD_END
 }
 
+// The GPU can read p: device memory or registered (pinned) host memory.
+bool gpu_readable(const void* p) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error of an unregistered pointer
+    return false;
+  }
+  return at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeHost || at.type == hipMemoryTypeManaged;
+}
+
+size_t tdx_restore_transfer_workspace(const tdx_shape* shape, const tdx_layout* layout, int32_t n_req,
+                                      int32_t layer_begin, int32_t layer_end) {
+  tdx::Dims d{};
+  if (check_shape(shape, &d) != TDX_OK || check_layout(layout, &d, false) != TDX_OK) return 0;
+  if (n_req < 1 || layer_begin < 0 || layer_end <= layer_begin || layer_end > d.L) return 0;
+  return tdx::transfer_ws_bytes(d, n_req, layer_end - layer_begin);
+}
+
+int tdx_restore_transfer(const tdx_shape* shape, const tdx_layout* layout, const void* master_k,
+                         const void* master_v, const int32_t* diff_off, const int32_t* diff_idx,
+                         const void* diff_k, const void* diff_v, const int32_t* agents, int32_t n_req,
+                         int32_t layer_begin, int32_t layer_end, void* k_out, void* v_out, void* ws,
+                         size_t ws_bytes, void* stream) {
+  GUARD_BEGIN
+  tdx::Dims d{};
+  int rc;
+  if ((rc = check_shape(shape, &d)) != TDX_OK) return rc;
+  if ((rc = check_layout(layout, &d, true)) != TDX_OK) return rc;
+  REQ(d.T % TDX_DIFF_BLOCK == 0, TDX_EINVAL, "n_tokens %d is not a multiple of 16", d.T);
+  REQ(n_req >= 1, TDX_EINVAL, "n_req %d < 1", n_req);
+  REQ(layer_begin >= 0 && layer_begin < layer_end && layer_end <= d.L, TDX_EINVAL,
+      "layer range [%d, %d) is not inside [0, %d)", layer_begin, layer_end, d.L);
+  REQ((long long)n_req * (layer_end - layer_begin) <= (1LL << 31) - 1, TDX_EUNSUPPORTED, "too many rows");
+  REQ_PTR(master_k);
+  REQ_PTR(master_v);
+  REQ_PTR4(diff_off);
+  REQ(diff_idx != nullptr && diff_k != nullptr && diff_v != nullptr, TDX_EINVAL, "diff arrays are null");
+  REQ(aligned16(diff_k) && aligned16(diff_v), TDX_EINVAL, "diff_k/diff_v not 16-byte aligned");
+  REQ_PTR4(agents);
+  REQ_PTR(k_out);
+  REQ_PTR(v_out);
+  const size_t need = tdx::transfer_ws_bytes(d, n_req, layer_end - layer_begin);
+  REQ(ws != nullptr && aligned16(ws) && ws_bytes >= need, TDX_EWORKSPACE, "workspace of %zu bytes < %zu", ws_bytes, need);
+  REQ(gpu_readable(master_k) && gpu_readable(master_v) && gpu_readable(diff_off) && gpu_readable(diff_idx) &&
+          gpu_readable(diff_k) && gpu_readable(diff_v),
+      TDX_EINVAL, "Master and diff record must be device memory or pinned host memory");
+  tdx::TransferArgs t{};
+  t.mk = master_k;
+  t.mv = master_v;
+  t.diff_off = diff_off;
+  t.diff_idx = diff_idx;
+  t.dk = diff_k;
+  t.dv = diff_v;
+  t.agents = agents;
+  t.n_req = n_req;
+  t.l0 = layer_begin;
+  t.l1 = layer_end;
+  t.blk_start = layout->blk_start;
+  t.src_pos = layout->src_pos;
+  t.dst_pos = layout->dst_pos;
+  t.k_out = k_out;
+  t.v_out = v_out;
+  t.ws = ws;
+  hipError_t e = tdx::launch_transfer(d, t, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tdx_restore_transfer launch");
+  return ok();
+  GUARD_END
+}
+
 int tdx_restore_dense(const tdx_shape* shape, const tdx_layout* layout, const void* master_k,
                       const void* master_v, const int32_t* master_sel, int64_t master_stride,
                       const int32_t* diff_off, const int32_t* diff_idx,

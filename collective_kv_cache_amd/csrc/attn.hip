@@ -1032,8 +1032,8 @@ __global__ __launch_bounds__(kThreads) void restore_dense_kernel(
   constexpr int G = HALF / VEC;
   constexpr int RPP = kThreads / G;
   __shared__ float2 tab[kMaxTileBlocks * HALF];
-  __shared__ int s_b0, s_nb;
-  __shared__ int32_t sb[kMaxTileBlocks + 1];
+  __shared__ int s_nb;
+  __shared__ int32_t sst[kMaxTileBlocks], sid[kMaxTileBlocks];  // non-empty blocks of the tile
   const int beta = blockIdx.x;
   const int i = blockIdx.y;
   const int tid = threadIdx.x;
@@ -1042,22 +1042,27 @@ __global__ __launch_bounds__(kThreads) void restore_dense_kernel(
   mk += moff;
   mv += moff;
   if (tid == 0) {
+    // the non-empty shared blocks holding tokens of [t0, t0 + 16): the one
+    // holding t0, then those starting inside the tile (at most 16 in all)
     int lo = 0, hi = B - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (blk_start[mid] <= t0) lo = mid; else hi = mid - 1;
     }
-    int nbk = 0;
-    for (int b = lo; b < B && blk_start[b] < t0 + kTile; ++b) ++nbk;
-    s_b0 = lo;
-    s_nb = nbk;
+    int n = 0;
+    for (int b = lo; b < B && blk_start[b] < t0 + kTile && n < kMaxTileBlocks; ++b)
+      if (blk_start[b + 1] > blk_start[b]) {
+        sst[n] = blk_start[b];
+        sid[n] = b;
+        ++n;
+      }
+    s_nb = n;
   }
   __syncthreads();
-  const int b0 = s_b0, nbk = s_nb;
-  for (int x = tid; x <= nbk; x += kThreads) sb[x] = blk_start[b0 + x];
+  const int nbk = s_nb;
   for (int x = tid; x < nbk * HALF; x += kThreads) {
     const int bb = x / HALF, e = x % HALF;
-    const double delta = (double)(dst_pos[(size_t)i * B + b0 + bb] - src_pos[b0 + bb]);
+    const double delta = (double)(dst_pos[(size_t)i * B + sid[bb]] - src_pos[sid[bb]]);
     double sn, cs;
     sincos(delta * rope_inv_freq(theta, e, D), &sn, &cs);
     tab[x] = make_float2((float)cs, (float)sn);
@@ -1082,7 +1087,7 @@ __global__ __launch_bounds__(kThreads) void restore_dense_kernel(
     for (int row = row0; row < nrows; row += RPP) {
       const int tok = t0 + row / Hkv;
       int bb = 0;
-      while (bb + 1 < nbk && sb[bb + 1] <= tok) ++bb;
+      while (bb + 1 < nbk && sst[bb + 1] <= tok) ++bb;
       const size_t off = (size_t)row * D + e0;
       float x[VEC], y[VEC], ox[VEC], oy[VEC];
       Fmt<E>::unpack(ld16(ks + off), x);

@@ -156,4 +156,26 @@ hipError_t launch_dense_attn(const Dims& d, const void* q, const int32_t* priv_o
                              const void* pk, const void* pv, int max_priv, const void* kd,
                              const void* vd, float scale, void* out, void* ws, hipStream_t s);
 
+// Transfer-path restore: Master and diff records readable by the GPU
+// (pinned host storage or device memory), requested agents, layer range.
+struct TransferArgs {
+  const void* mk;
+  const void* mv;
+  const int32_t* diff_off;
+  const int32_t* diff_idx;
+  const void* dk;
+  const void* dv;
+  const int32_t* agents;  // device [n_req]
+  int n_req, l0, l1;
+  const int32_t* blk_start;
+  const int32_t* src_pos;
+  const int32_t* dst_pos;
+  void* k_out;  // [n_req][L][T][Hkv][D]
+  void* v_out;
+  void* ws;
+};
+size_t transfer_tab_off(const Dims& d, int n_req, int nl);
+size_t transfer_ws_bytes(const Dims& d, int n_req, int nl);
+hipError_t launch_transfer(const Dims& d, const TransferArgs& t, hipStream_t s);
+
 }  // namespace tdx

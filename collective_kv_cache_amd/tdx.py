@@ -72,6 +72,9 @@ _SIGS = {
     "tdx_restore_dense": (ctypes.c_int, [_PS, _PL, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "tdx_decode_attn_dense_workspace": (_SZ, [_PS, _PL, _I32]),
     "tdx_decode_attn_dense": (ctypes.c_int, [_PS, _PL, _P, _P, _P, _P, _I32, _P, _P, _F, _P, _P, _SZ, _P]),
+    "tdx_restore_transfer_workspace": (_SZ, [_PS, _PL, _I32, _I32, _I32]),
+    "tdx_restore_transfer": (ctypes.c_int, [_PS, _PL, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P,
+                                            _P, _SZ, _P]),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -355,6 +358,58 @@ def restore_dense(shape: Shape, lay: RoundLayout, master_k: torch.Tensor, master
         _ptr(diff.idx), _ptr(diff.k), _ptr(diff.v), _ptr(k_dense), _ptr(v_dense), _stream()),
         "tdx_restore_dense")
     return k_dense, v_dense
+
+
+def restore_transfer_workspace(shape: Shape, lay: RoundLayout, n_req: int, layer_begin: int,
+                               layer_end: int) -> int:
+    s, l = shape.c(), lay.c()
+    return int(lib().tdx_restore_transfer_workspace(ctypes.byref(s), ctypes.byref(l), int(n_req),
+                                                    int(layer_begin), int(layer_end)))
+
+
+def _host_or_device(t: torch.Tensor, name: str, dtype, shape_, dev_):
+    """A tensor on the round's device, or a pinned host tensor."""
+    if t.device.type == "cpu":
+        if not t.is_pinned():
+            raise ValueError(f"{name} is in pageable host memory; pin it (pin_memory) or move it to the GPU")
+        _need(t, name, dtype, shape_)
+    else:
+        _need(t, name, dtype, shape_, dev_)
+
+
+def restore_transfer(shape: Shape, lay: RoundLayout, master_k: torch.Tensor, master_v: torch.Tensor,
+                     diff_off: torch.Tensor, diff_idx: torch.Tensor, diff_k: torch.Tensor,
+                     diff_v: torch.Tensor, agents: torch.Tensor, layer_begin: int = 0,
+                     layer_end: Optional[int] = None, k_out: Optional[torch.Tensor] = None,
+                     v_out: Optional[torch.Tensor] = None, ws=None):
+    """Transfer-path restore: the requested agents' KV rebuilt layer by layer
+    from a Master and diff record that may sit in pinned host memory.  Writes
+    layers [layer_begin, layer_end) of k_out / v_out [n_req][L][T][Hkv][D]."""
+    N, L, T, H, D = lay.n_agents, shape.n_layers, lay.n_tokens, shape.n_kv_heads, shape.head_dim
+    dev_ = lay.device
+    layer_end = L if layer_end is None else int(layer_end)
+    _need(agents, "agents", torch.int32, None, dev_)
+    n_req = agents.numel()
+    for t, name in ((master_k, "master_k"), (master_v, "master_v")):
+        _host_or_device(t, name, shape.dtype, (L, T, H, D), dev_)
+    _host_or_device(diff_off, "diff_off", torch.int32, (N * L + 1,), dev_)
+    _host_or_device(diff_idx, "diff_idx", torch.int32, None, dev_)
+    for t, name in ((diff_k, "diff_k"), (diff_v, "diff_v")):
+        _host_or_device(t, name, shape.dtype, (diff_idx.shape[0], DIFF_BLOCK, H, D), dev_)
+    if k_out is None:
+        k_out = torch.empty((n_req, L, T, H, D), dtype=shape.dtype, device=dev_)
+    if v_out is None:
+        v_out = torch.empty((n_req, L, T, H, D), dtype=shape.dtype, device=dev_)
+    _need(k_out, "k_out", shape.dtype, (n_req, L, T, H, D), dev_)
+    _need(v_out, "v_out", shape.dtype, (n_req, L, T, H, D), dev_)
+    if ws is None:
+        ws = _ws(restore_transfer_workspace(shape, lay, n_req, layer_begin, layer_end), dev_)
+    s, l = shape.c(), lay.c()
+    _check(lib().tdx_restore_transfer(
+        ctypes.byref(s), ctypes.byref(l), _ptr(master_k), _ptr(master_v), _ptr(diff_off), _ptr(diff_idx),
+        _ptr(diff_k), _ptr(diff_v), _ptr(agents), n_req, int(layer_begin), int(layer_end), _ptr(k_out),
+        _ptr(v_out), _ptr(ws), ws.numel(), _stream()), "tdx_restore_transfer")
+    return k_out, v_out
 
 
 def decode_attn_dense_workspace(shape: Shape, lay: RoundLayout, max_priv: int) -> int:

@@ -24,10 +24,13 @@
  *                         "Fused Diff Restore"; blog §4.4).
  *   tdx_restore_dense +   the dense comparator: materialise every agent's
  *   tdx_decode_attn_dense cache, then attend (notes §3d, §7b).
+ *   tdx_restore_transfer  the transfer-path restore: Mirrors rebuilt layer by
+ *                         layer from a Master and diff records kept in host
+ *                         storage (notes §3d Algorithm 1; blog §4.4).
  *
  * Conventions shared by every call
- *  - Tensor arguments are DEVICE pointers to dense row-major arrays owned by
- *    the caller; the library allocates and frees nothing and keeps no state
+ *  - Tensor arguments are DEVICE pointers (tdx_restore_transfer also takes
+ *    pinned host storage) to dense row-major arrays owned by the caller; the library allocates and frees nothing and keeps no state
  *    apart from a thread-local error string.  Scratch memory is passed as
  *    (ws, ws_bytes), sized by the matching tdx_*_workspace() query.
  *  - Element type of K, V, q and outputs is shape->dtype (fp32 or bf16 bit
@@ -190,6 +193,40 @@ int tdx_restore_attn(const tdx_shape *shape, const tdx_layout *layout,
                      void *out, void *ws, size_t ws_bytes, void *stream);
 size_t tdx_restore_attn_workspace(const tdx_shape *shape, const tdx_layout *layout,
                                   int32_t max_priv);
+
+/* ---- transfer-path restore (Mirrors rebuilt from host storage) -------------
+ * The pages' restore path (notes Summary "Method" and §3d Algorithm 1 "Fused
+ * Diff Restore"; blog §4.4): the Master and the Mirrors' diff records live in
+ * storage outside the GPU and an agent's KV is rebuilt layer by layer on the
+ * way in, merged block by block and RoPE-recovered, with no dense Mirror in
+ * between.  For every requested agent a = agents[j] and layer l in
+ * [layer_begin, layer_end):
+ *   k_out[j][l][t] = round(R(Delta(a, b(t))) K~_a[l][t]),  v_out[j][l][t] = V~_a[l][t]
+ * with K~_a / V~_a the Master patched with agent a's diff rows (the same rows
+ * tdx_restore_dense writes for agent a).  Layers outside the range are not
+ * written.  The kernels read the Master and the diff record directly where
+ * they are, so they may sit in pinned host memory (hipHostMalloc, or a
+ * pinned torch tensor: the reads then cross PCIe, once per block for all
+ * requested agents) or in device memory; pageable host memory is rejected
+ * with TDX_EINVAL.
+ *   master_k/v       [L][T][Hkv][D] (T % 16 == 0), host-pinned or device
+ *   diff_off / diff_idx / diff_k / diff_v  as written by tdx_diff_encode,
+ *                    host-pinned or device
+ *   agents           device int32 [n_req], each in [0, N) (values outside are
+ *                    clamped to it); n_req >= 1
+ *   k_out/v_out      device [n_req][L][T][Hkv][D]
+ *   ws               tdx_restore_transfer_workspace(shape, layout, n_req,
+ *                    layer_begin, layer_end) bytes (device) */
+int tdx_restore_transfer(const tdx_shape *shape, const tdx_layout *layout,
+                         const void *master_k, const void *master_v,
+                         const int32_t *diff_off, const int32_t *diff_idx,
+                         const void *diff_k, const void *diff_v,
+                         const int32_t *agents, int32_t n_req,
+                         int32_t layer_begin, int32_t layer_end,
+                         void *k_out, void *v_out, void *ws, size_t ws_bytes,
+                         void *stream);
+size_t tdx_restore_transfer_workspace(const tdx_shape *shape, const tdx_layout *layout,
+                                      int32_t n_req, int32_t layer_begin, int32_t layer_end);
 
 /* ---- a6: dense comparator --------------------------------------------------
  * tdx_restore_dense writes every agent's full cache:

@@ -160,3 +160,26 @@ def test_restore_rejects_bad_arguments():
     assert _restore(msel=FAKE, mstride=12) == tdx.TDX_EINVAL
     assert _restore_dense(msel=FAKE, mstride=12) == tdx.TDX_EINVAL
     assert _restore_dense(msel=ctypes.c_void_p(0x10001)) == tdx.TDX_EINVAL
+
+
+def _transfer(T=64, n_req=2, l0=0, l1=2, ws_bytes=1 << 30, agents=FAKE, mk=FAKE):
+    s, l = _shape(), _layout(n_tokens=T)
+    return tdx.lib().tdx_restore_transfer(ctypes.byref(s), ctypes.byref(l), mk, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                          agents, n_req, l0, l1, FAKE, FAKE, FAKE, ws_bytes, None)
+
+
+def test_transfer_rejects_bad_arguments():
+    # every check here fails before the pointers are inspected or anything is enqueued
+    assert _transfer(T=40) == tdx.TDX_EINVAL          # not a multiple of 16
+    assert _transfer(n_req=0) == tdx.TDX_EINVAL
+    assert _transfer(l0=1, l1=1) == tdx.TDX_EINVAL    # empty layer range
+    assert _transfer(l0=-1) == tdx.TDX_EINVAL
+    assert _transfer(l1=3) == tdx.TDX_EINVAL          # past n_layers = 2
+    assert _transfer(agents=ctypes.c_void_p(0x10002)) == tdx.TDX_EINVAL
+    assert _transfer(mk=None) == tdx.TDX_EINVAL
+    assert _transfer(ws_bytes=0) == tdx.TDX_EWORKSPACE
+    s, l = _shape(), _layout(n_tokens=64)
+    w1 = tdx.lib().tdx_restore_transfer_workspace(ctypes.byref(s), ctypes.byref(l), 1, 0, 1)
+    w2 = tdx.lib().tdx_restore_transfer_workspace(ctypes.byref(s), ctypes.byref(l), 3, 0, 2)
+    assert 0 < w1 < w2
+    assert tdx.lib().tdx_restore_transfer_workspace(ctypes.byref(s), ctypes.byref(l), 1, 0, 3) == 0

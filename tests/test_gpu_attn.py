@@ -13,56 +13,9 @@ from collective_kv_cache_amd import tdx
 from workload import (CONFIGS, make_layout, cached_kv, agent_caches, queries, private_kv,
                       to_numpy_bits)
 
-from gpu_common import DEV, assert_close, dlayout, host, shape_of
+from gpu_common import DEV, Round, assert_close, dlayout, host, shape_of
 
 pytestmark = pytest.mark.gpu
-
-
-class Round:
-    """One generated round, on the host and on the device."""
-
-    def __init__(self, cfg, lay, master=1, blocks=None, device_gen="cpu"):
-        self.cfg, self.lay, self.master = cfg, lay, master
-        kc, vc = cached_kv(cfg, lay, device=device_gen)
-        ak, av = agent_caches(cfg, lay, kc, vc, master, blocks=blocks)
-        q = queries(cfg, device=device_gen)
-        pk, pv = private_kv(cfg, lay, device=device_gen)
-        self.dev = dict(kc=kc.to(DEV), vc=vc.to(DEV), ak=ak.to(DEV), av=av.to(DEV), q=q.to(DEV),
-                        pk=pk.to(DEV), pv=pv.to(DEV),
-                        po=torch.as_tensor(lay.priv_off, device=DEV))
-        self.host = dict(kc=kc, vc=vc, ak=ak, av=av, q=q, pk=pk, pv=pv)
-        self.shape = shape_of(cfg)
-        self.dl = dlayout(lay)
-        self.max_priv = int(lay.priv_len.max())
-        self.scale = 1.0 / math.sqrt(cfg.head_dim)
-
-    def gpu_encode(self):
-        d = self.dev
-        m = torch.tensor([self.master], dtype=torch.int32, device=DEV)
-        return tdx.diff_encode(self.shape, self.dl, m, d["ak"], d["av"])
-
-    def gpu_fused(self, ds):
-        d = self.dev
-        return tdx.restore_attn(self.shape, self.dl, d["q"], d["po"], d["pk"], d["pv"], self.max_priv,
-                                ds.master_k, ds.master_v, ds)
-
-    def gpu_dense(self, ds):
-        d = self.dev
-        kd, vd = tdx.restore_dense(self.shape, self.dl, ds.master_k, ds.master_v, ds)
-        out = tdx.decode_attn_dense(self.shape, self.dl, d["q"], d["po"], d["pk"], d["pv"],
-                                    self.max_priv, kd, vd)
-        return kd, vd, out
-
-    def oracle_full(self):
-        h = {k: to_numpy_bits(v) for k, v in self.host.items()}
-        lay = self.lay
-        off, idx, dk, dv = O.diff_encode(h["ak"], h["av"], self.master)
-        args = (lay.blk_start, lay.src_pos, lay.dst_pos, self.cfg.theta)
-        fused = O.restore_attn(h["q"], lay.priv_off, h["pk"], h["pv"], h["kc"], h["vc"], off, idx, dk, dv,
-                               *args, self.scale)
-        kd, vd = O.restore_dense(h["kc"], h["vc"], off, idx, dk, dv, *args)
-        dense = O.decode_attn_dense(h["q"], lay.priv_off, h["pk"], h["pv"], kd, vd, self.scale)
-        return fused, kd, vd, dense
 
 
 @pytest.mark.parametrize("name,kw", [
