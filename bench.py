@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--config", default="qwen14b_round")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-transfer", action="store_true",
+                    help="skip the transfer-path restore measurement (Master and diffs in pinned host memory)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -281,6 +283,115 @@ def cpu_baseline(cfg, lay, pct, n_sample=8):
     }
 
 
+PCIE_H2D_GBS = 64.0  # PCIe 5.0 x16, one direction, nominal
+
+
+def transfer_path(cfg, lay, shape, dl, ds, nnz, master_k, master_v, q, pk, pv, reps=3):
+    """The transfer-path restore of the same round with the Master and the
+    diff record in pinned host memory (outside the timed step):
+      - every agent's KV for every layer in one call: bytes over PCIe / time;
+      - one Mirror, layer by layer (the pages' per-Mirror per-layer latency);
+      - the same Mirror's layers restored on one stream while decode attention
+        over the layers already restored runs on another (pipelined), against
+        the two run back to back on one stream."""
+    import numpy as np
+    import torch
+    from collective_kv_cache_amd import tdx
+
+    dev = "cuda"
+    N, L, T, H, Hq, D = cfg.n_agents, cfg.n_layers, lay.n_tokens, cfg.n_kv_heads, cfg.n_q_heads, cfg.head_dim
+    kt = H * D * cfg.elem_bytes
+    torch.cuda.synchronize()
+    mk_h, mv_h = master_k.cpu().pin_memory(), master_v.cpu().pin_memory()
+    off_h, idx_h = ds.off.cpu().pin_memory(), ds.idx[:max(nnz, 1)].cpu().pin_memory()
+    dk_h, dv_h = ds.k[:max(nnz, 1)].cpu().pin_memory(), ds.v[:max(nnz, 1)].cpu().pin_memory()
+    counts = np.diff(off_h.numpy().astype(np.int64)).reshape(N, L)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, n=reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    # every agent, every layer
+    ag = torch.arange(N, dtype=torch.int32, device=dev)
+    k_all = torch.empty((N, L, T, H, D), dtype=cfg.torch_dtype, device=dev)
+    v_all = torch.empty_like(k_all)
+    ws_all = torch.empty(tdx.restore_transfer_workspace(shape, dl, N, 0, L), dtype=torch.uint8, device=dev)
+    ms_all = timed(lambda: tdx.restore_transfer(shape, dl, mk_h, mv_h, off_h, idx_h, dk_h, dv_h, ag, 0, L,
+                                                k_all, v_all, ws_all))
+    pcie_all = L * T * 2 * kt + int(counts.sum()) * (16 * 2 * kt + 4) + 4 * (N * L + 1)
+    del k_all, v_all
+    # one Mirror (the one with the most diff blocks), layer by layer
+    mir = int(np.argmax(counts.sum(axis=1)))
+    a1 = torch.tensor([mir], dtype=torch.int32, device=dev)
+    k1 = torch.empty((1, L, T, H, D), dtype=cfg.torch_dtype, device=dev)
+    v1 = torch.empty_like(k1)
+    ws1 = torch.empty(tdx.restore_transfer_workspace(shape, dl, 1, 0, 1), dtype=torch.uint8, device=dev)
+    restore_l = lambda l: tdx.restore_transfer(shape, dl, mk_h, mv_h, off_h, idx_h, dk_h, dv_h, a1, l, l + 1,
+                                               k1, v1, ws1)
+    ms_layers = timed(lambda: [restore_l(l) for l in range(L)])
+    pcie_mirror = L * T * 2 * kt + int(counts[mir].sum()) * (16 * 2 * kt + 4)
+    # decode attention of that Mirror over each restored layer (one agent, one layer per call)
+    shape1 = tdx.Shape(1, H, Hq, D, cfg.torch_dtype, cfg.theta)
+    dl1 = tdx.RoundLayout(lay.blk_start, lay.src_pos, lay.dst_pos[mir:mir + 1], dev)
+    p0, p1 = int(lay.priv_off[mir]), int(lay.priv_off[mir + 1])
+    po1 = torch.tensor([0, p1 - p0], dtype=torch.int32, device=dev)
+    out1 = torch.empty((1, 1, Hq, D), dtype=cfg.torch_dtype, device=dev)
+    ws_a = torch.empty(max(tdx.decode_attn_dense_workspace(shape1, dl1, max(p1 - p0, 1)), 16), dtype=torch.uint8,
+                       device=dev)
+    pk1 = [pk[l:l + 1, p0:p1] if p1 > p0 else pk[l:l + 1, :1] for l in range(L)]
+    pv1 = [pv[l:l + 1, p0:p1] if p1 > p0 else pv[l:l + 1, :1] for l in range(L)]
+    attn_l = lambda l: tdx.decode_attn_dense(shape1, dl1, q[mir:mir + 1, l:l + 1], po1, pk1[l], pv1[l], p1 - p0,
+                                             k1[:, l:l + 1], v1[:, l:l + 1], out=out1, ws=ws_a)
+
+    def serial():
+        for l in range(L):
+            restore_l(l)
+            attn_l(l)
+
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    done = [torch.cuda.Event() for _ in range(L)]
+
+    def pipelined():
+        cur = torch.cuda.current_stream()
+        sa.wait_stream(cur)
+        sb.wait_stream(cur)
+        for l in range(L):
+            with torch.cuda.stream(sa):
+                restore_l(l)
+                done[l].record(sa)
+            with torch.cuda.stream(sb):
+                sb.wait_event(done[l])
+                attn_l(l)
+        cur.wait_stream(sa)
+        cur.wait_stream(sb)
+
+    ms_serial = timed(serial)
+    ms_pipe = timed(pipelined)
+    attn_ms = timed(lambda: [attn_l(l) for l in range(L)])
+    return {
+        "source": "pinned host memory (Master + diff record), read by the restore kernel over PCIe",
+        "all_agents_ms": round(ms_all, 3),
+        "all_agents_pcie_GB": round(pcie_all / 1e9, 4),
+        "all_agents_GBps": round(pcie_all / (ms_all * 1e-3) / 1e9, 2),
+        "frac_pcie_peak": round(pcie_all / (ms_all * 1e-3) / 1e9 / PCIE_H2D_GBS, 4),
+        "dense_pcie_GB_avoided": round(N * L * T * 2 * kt / 1e9, 3),
+        "mirror": mir,
+        "ms_per_mirror_per_layer": round(ms_layers / L, 4),
+        "mirror_GBps": round(pcie_mirror / (ms_layers * 1e-3) / 1e9, 2),
+        "mirror_restore_then_attend_serial_ms": round(ms_serial, 3),
+        "mirror_restore_attend_pipelined_ms": round(ms_pipe, 3),
+        "mirror_attend_only_ms": round(attn_ms, 3),
+    }
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -407,6 +518,10 @@ def main():
                  "max_abs_fused_minus_dense": diff}
         del kd, vd
 
+    transfer = None
+    if not args.no_transfer:
+        transfer = transfer_path(cfg, lay, shape, dl, ds, nnz, ak[master], av[master], q, pk, pv)
+
     byts = stage_bytes(cfg, lay, nnz, k)
     stage_rep = {}
     for name in stages:
@@ -447,6 +562,7 @@ def main():
         "collective_reuse_agent_tokens_per_s": agent_tokens / (reuse_ms * 1e-3),
         "stages": stage_rep,
         "dense_comparator": dense,
+        "transfer_restore": transfer,
         "compression": compression(counts, master, T, H, D, cfg.elem_bytes, lay.priv_len, L),
         "cpu_baseline": None,
     }
