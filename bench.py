@@ -90,7 +90,7 @@ ENTRY_KERNELS = {
     "tdx_rerotate": ("rerotate_kernel",),
     "tdx_select_important": ("deviation_kernel", "select_kernel"),
     "tdx_diff_encode": ("flag_kernel", "rows_kernel", "offsets_kernel", "copy_kernel"),
-    "tdx_restore_attn": ("rope_table_kernel", "diff_tab_kernel", "qrot_kernel", "shared_kernel",
+    "tdx_restore_attn": ("rope_table_kernel", "diff_tab_kernel", "shared_kernel",
                          "qplain_kernel", "stream_plan_kernel<0>", "stream_kernel<unsigned short, 128, 0",
                          "stream_kernel<float, 128, 0", "stream_kernel<unsigned short, 64, 0",
                          "stream_kernel<float, 64, 0", "merge_kernel<unsigned short, 128, 0>",

@@ -153,45 +153,6 @@ __global__ __launch_bounds__(256) void rope_table_kernel(const int32_t* __restri
   }
 }
 
-// ---- rotated queries: qrot[((i*L + l)*B + b)*Hq + hq][D] = bf16(R(-Delta(i,b)) q[i][l][hq])
-// RoPE recovery on the query side: q . R(Delta) k = (R(-Delta) q) . k, so the
-// canonical Master/diff key rows can be used as they are stored.  One thread
-// per (agent, layer, block, query head, 8 lower-half dims).
-
-template <typename E, int D>
-__global__ __launch_bounds__(256) void qrot_kernel(const E* __restrict__ q, const float2* __restrict__ tab,
-                                                   int N, int L, int B, int Hq,
-                                                   uint16_t* __restrict__ qrot) {
-  constexpr int HALF = D / 2;
-  constexpr int C = HALF / 8;  // 8-dim chunks of the lower half
-  const size_t n = (size_t)N * L * B * Hq * C;
-  for (size_t x = blockIdx.x * (size_t)blockDim.x + threadIdx.x; x < n;
-       x += (size_t)gridDim.x * blockDim.x) {
-    const int c = (int)(x % C);
-    size_t r = x / C;
-    const int hq = (int)(r % Hq);
-    r /= Hq;
-    const int b = (int)(r % B);
-    r /= B;
-    const int l = (int)(r % L);
-    const int i = (int)(r / L);
-    const E* qr = q + (((size_t)i * L + l) * Hq + hq) * D;
-    float lo[8], hi[8], olo[8], ohi[8];
-    load8<E>(qr + 8 * c, lo);
-    load8<E>(qr + HALF + 8 * c, hi);
-    const float2* cs = tab + ((size_t)i * B + b) * HALF + 8 * c;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      // R(-phi): (x, y) -> (x cos + y sin, y cos - x sin)
-      olo[j] = lo[j] * cs[j].x + hi[j] * cs[j].y;
-      ohi[j] = hi[j] * cs[j].x - lo[j] * cs[j].y;
-    }
-    uint16_t* o = qrot + ((((size_t)i * L + l) * B + b) * Hq + hq) * D;
-    st16(o + 8 * c, Fmt<uint16_t>::pack(olo));
-    st16(o + HALF + 8 * c, Fmt<uint16_t>::pack(ohi));
-  }
-}
-
 // ---- shared state ----------------------------------------------------------------
 
 struct AttnArgs {
@@ -209,8 +170,7 @@ struct AttnArgs {
   const void* dv;
   const int32_t* blk_start;  // [B+1]
   const float2* tab;         // fused: [N][B][D/2] cos/sin of each shift
-  uint16_t* qrot;            // fused: [N][L][B][Hq][D] bf16 rotated queries
-  uint16_t* qplain;          // [N][L][Hq][D] bf16 queries
+  const uint16_t* qplain;    // [N][L][Hq][D] bf16 queries (the input itself when it is bf16)
   float* part;               // [N][L][Hq][S][D+4]: m, l, -, -, O[D]
   unsigned char* ws_base;    // the workspace (task list, per-diff-entry cos/sin rows)
   int N, L, T, B, Hkv, Hq;
@@ -315,8 +275,10 @@ __device__ __forceinline__ void write_record(float* rec, const RowState<D>& st, 
 // ---- shared_kernel: Master tiles staged once, all agents' query rows ------------
 //
 // One workgroup per (agent group, Master split, layer, KV head).  The split's
-// tiles are taken shared block by shared block: the wave's 16 rotated query
-// rows R(-Delta(i,b)) q are loaded once per block, and the block's tiles
+// tiles are taken shared block by shared block: the wave's 16 query rows are
+// rotated once per block, R(-Delta(i,b)) q, which is RoPE recovery moved to
+// the query side (q . R(Delta) k = (R(-Delta) q) . k), so the Master's
+// canonical key rows are used as they are stored; the block's tiles
 // stream through a PD-stage register pipeline (each thread's chunks of the
 // tile's K and V rows), the tile in use sitting in one of two LDS buffers.
 // Step n: issue the loads of tile n+PD-1, use tile n, store tile n+1 into the
@@ -362,6 +324,7 @@ __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(TDX_
   using St = ShStage<E, D>;
   constexpr int KD = D / 32;
   constexpr int DT = D / 16;
+  constexpr int HALF = D / 2;
   constexpr int VS = D + 8;  // padded LDS row stride (bf16)
   constexpr int CH = St::CH;
   constexpr int CPT = St::CPT;
@@ -429,8 +392,8 @@ __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(TDX_
   const size_t moff = master_offset(a.msel, a.mstride, a.N);
   const E* mk = static_cast<const E*>(a.sk) + moff + (size_t)l * a.T * rowHD + (size_t)h * D;
   const E* mv = static_cast<const E*>(a.sv) + moff + (size_t)l * a.T * rowHD + (size_t)h * D;
-  const uint16_t* qbase = a.qrot + (((size_t)agent * a.L + l) * a.B) * a.Hq * D + (size_t)hq * D;
-  const size_t qblk = (size_t)a.Hq * D;  // qrot stride between shared blocks
+  const E* qrow = static_cast<const E*>(a.q) + (((size_t)agent * a.L + l) * a.Hq + hq) * D;
+  const float2* tabrow = a.tab + (size_t)agent * a.B * HALF;
 
   auto load = [&](int tile, St& S) {
 #pragma unroll
@@ -470,11 +433,32 @@ __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(TDX_
     const int ta = max(b0, bs / kTile), tb = min(b1, (be + kTile - 1) / kTile);
     if (be <= bs || ta >= tb) continue;  // empty block (uniform)
     const int nt = tb - ta;
-    u32x4 qr[KD];  // rotated query rows for block b
+    // the lane's query elements 32k + 8*q4 .. +7 rotated by -Delta(agent, b)
+    // in fp32 and rounded to bf16; element e < D/2 pairs with e + D/2, which
+    // sits in chunk k + KD/2 of the same lane
+    u32x4 qr[KD];
     {
-      const uint16_t* qs = qbase + (size_t)b * qblk;
+      const float2* cs = tabrow + (size_t)b * HALF;
+      // fp32 rows are read again for every block rather than held across
+      // blocks (32 more registers than the kernel's budget allows)
+      const E* qp = qrow;
+      if constexpr (sizeof(E) == 4) asm volatile("" : "+v"(qp));
 #pragma unroll
-      for (int k = 0; k < KD; ++k) qr[k] = ld16(qs + 32 * k + 8 * q4);
+      for (int k = 0; k < KD / 2; ++k) {
+        const int e0 = 32 * k + 8 * q4;
+        float lo[8], hi[8], olo[8], ohi[8];
+        load8<E>(qp + e0, lo);
+        load8<E>(qp + HALF + e0, hi);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float2 c = cs[e0 + j];
+          // R(-phi): (x, y) -> (x cos + y sin, y cos - x sin)
+          olo[j] = lo[j] * c.x + hi[j] * c.y;
+          ohi[j] = hi[j] * c.x - lo[j] * c.y;
+        }
+        qr[k] = Fmt<uint16_t>::pack(olo);
+        qr[k + KD / 2] = Fmt<uint16_t>::pack(ohi);
+      }
     }
     // use tile ta + n (buffer buf)
     auto compute = [&](int n, bool live, int buf) {
@@ -1111,7 +1095,7 @@ __global__ __launch_bounds__(kThreads) void restore_dense_kernel(
 struct Plan {
   int SP, SG, AGS, NAG, TPG, n_sh_wg;
   long long dcap;
-  size_t part_bytes, tab_off, qrot_off, qplain_off, task_off, ctl_off, dcs_off, dinfo_off, total;
+  size_t part_bytes, tab_off, qplain_off, task_off, ctl_off, dcs_off, dinfo_off, total;
 };
 
 Plan make_plan(const Dims& d, int max_priv, bool fused) {
@@ -1140,9 +1124,9 @@ Plan make_plan(const Dims& d, int max_priv, bool fused) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   p.part_bytes = (size_t)d.N * d.L * d.Hq * (p.SP + p.SG) * (d.D + 4) * 4;
   p.tab_off = up(p.part_bytes);
-  p.qrot_off = p.tab_off + (fused ? up((size_t)d.N * d.B * (d.D / 2) * 8) : 0);
-  p.qplain_off = p.qrot_off + (fused ? up((size_t)d.N * d.L * d.B * d.Hq * d.D * 2) : 0);
-  p.task_off = p.qplain_off + up((size_t)d.N * d.L * d.Hq * d.D * 2);
+  p.qplain_off = p.tab_off + (fused ? up((size_t)d.N * d.B * (d.D / 2) * 8) : 0);
+  // bf16 queries are read in place; fp32 ones get a bf16 copy
+  p.task_off = p.qplain_off + (d.dtype == TDX_BF16 ? 0 : up((size_t)d.N * d.L * d.Hq * d.D * 2));
   p.ctl_off = p.task_off + up((size_t)d.N * d.L * p.SP * sizeof(StreamTask));
   p.dcs_off = p.ctl_off + 256;
   p.dinfo_off = p.dcs_off + (fused ? up((size_t)p.dcap * (d.D / 2) * 8) : 0);
@@ -1176,23 +1160,21 @@ hipError_t launch_attn_t(const Dims& d, AttnArgs a, const Plan& p, E* out, hipSt
   a.dcap = p.dcap;
   hipError_t e;
   if (MODE == FUSED) {
-    const size_t nq = (size_t)d.N * d.L * d.B * d.Hq * (D / 16);
-    const int qblocks = (int)((nq + 255) / 256 < 8192 ? (nq + 255) / 256 : 8192);
-    hipLaunchKernelGGL((qrot_kernel<E, D>), dim3(qblocks), dim3(256), 0, s,
-                       static_cast<const E*>(a.q), a.tab, d.N, d.L, d.B, d.Hq, a.qrot);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     const size_t lds = shared_lds(D, d.B, p);
     if (lds > 64 * 1024) return hipErrorInvalidValue;
     const int grid = (p.n_sh_wg + 7) / 8 * 8;
     hipLaunchKernelGGL((shared_kernel<E, D, TDX_SH_PD>), dim3(grid), dim3(kShThreads), lds, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  {
+  if constexpr (sizeof(E) == 2) {
+    a.qplain = static_cast<const uint16_t*>(a.q);  // already the operand form
+  } else {
+    uint16_t* qp = reinterpret_cast<uint16_t*>(a.ws_base + p.qplain_off);
     const size_t nq = (size_t)d.N * d.L * d.Hq * D / 8;
     const int qblocks = (int)((nq + 255) / 256 < 4096 ? (nq + 255) / 256 : 4096);
-    hipLaunchKernelGGL((qplain_kernel<E, D>), dim3(qblocks), dim3(256), 0, s, static_cast<const E*>(a.q), nq,
-                       a.qplain);
+    hipLaunchKernelGGL((qplain_kernel<E, D>), dim3(qblocks), dim3(256), 0, s, static_cast<const E*>(a.q), nq, qp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    a.qplain = qp;
   }
   constexpr int PD = StreamCfg<E, D>::PD;
   const size_t lds = StreamCfg<E, D>::lds(MODE == FUSED);
@@ -1271,8 +1253,6 @@ hipError_t launch_restore_attn(const Dims& d, const tdx_layout& lay, const void*
   a.blk_start = lay.blk_start;
   float2* tab = reinterpret_cast<float2*>(static_cast<unsigned char*>(ws) + p.tab_off);
   a.tab = tab;
-  a.qrot = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(ws) + p.qrot_off);
-  a.qplain = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(ws) + p.qplain_off);
   const size_t n = (size_t)d.N * d.B * (d.D / 2);
   const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
   hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(256), 0, s, lay.src_pos, lay.dst_pos,
@@ -1316,7 +1296,6 @@ hipError_t launch_dense_attn(const Dims& d, const void* q, const int32_t* priv_o
   AttnArgs a = common_args(d, q, priv_off, pk, pv, scale, ws);
   a.sk = kd;
   a.sv = vd;
-  a.qplain = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(ws) + p.qplain_off);
   return dispatch_attn<DENSE>(d, a, p, out, s);
 }
 
