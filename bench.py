@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-transfer", action="store_true",
                     help="skip the transfer-path restore measurement (Master and diffs in pinned host memory)")
+    ap.add_argument("--no-serial", action="store_true",
+                    help="skip the serial per-agent comparator (one-agent re-rotation and selection per agent)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -392,6 +394,34 @@ def transfer_path(cfg, lay, shape, dl, ds, nnz, master_k, master_v, q, pk, pv, r
     }
 
 
+def serial_path(shape, lay, kc, kx, k, check_layer, kr, steps, warmup, collective_ms):
+    """N one-agent launches of re-rotation and selection (the per-request
+    path) against the collective round's one launch of each."""
+    import torch
+
+    from collective_kv_cache_amd.serial import SerialReuse
+
+    ser = SerialReuse(shape, lay.blk_start, lay.src_pos, lay.dst_pos, k, kr.device)
+    kr_s = torch.empty_like(kr)
+    for _ in range(warmup):
+        ser.run(kc, kx, check_layer, kr_s)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        ser.run(kc, kx, check_layer, kr_s)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    same = bool(torch.equal(kr_s.view(torch.int16) if kr.dtype == torch.bfloat16 else kr_s.view(torch.int32),
+                            kr.view(torch.int16) if kr.dtype == torch.bfloat16 else kr.view(torch.int32)))
+    del kr_s
+    return {"ms": round(ms, 4), "launches": 2 * lay.n_agents, "collective_ms": round(collective_ms, 4),
+            "serial_over_collective": round(ms / collective_ms, 3),
+            "rerotate_bit_identical": same,
+            "note": "kernel time only; the pages' 2.57x includes model recompute"}
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -518,6 +548,12 @@ def main():
                  "max_abs_fused_minus_dense": diff}
         del kd, vd
 
+    # ---- serial per-agent reuse (the per-request fallback) on the same inputs
+    serial = None
+    if not args.no_serial:
+        serial = serial_path(shape1, lay, kc, kx, k, cfg.check_layer, kr, args.steps,
+                             max(1, args.warmup), stage_ms["rerotate"] + stage_ms["select"])
+
     transfer = None
     if not args.no_transfer:
         transfer = transfer_path(cfg, lay, shape, dl, ds, nnz, ak[master], av[master], q, pk, pv)
@@ -562,6 +598,7 @@ def main():
         "collective_reuse_agent_tokens_per_s": agent_tokens / (reuse_ms * 1e-3),
         "stages": stage_rep,
         "dense_comparator": dense,
+        "serial_per_agent": serial,
         "transfer_restore": transfer,
         "compression": compression(counts, master, T, H, D, cfg.elem_bytes, lay.priv_len, L),
         "cpu_baseline": None,
