@@ -90,6 +90,14 @@ int check_layout(const tdx_layout* lay, tdx::Dims* d, bool need_pos) {
 
 }  // namespace
 
+namespace tdx {
+// error reporting for the host-only entry points compiled in other files
+int report(int code, const char* msg) {
+  if (code == TDX_OK) return ok();
+  return fail(code, "%s", msg);
+}
+}  // namespace tdx
+
 extern "C" {
 
 int tdx_version(void) { return TDX_VERSION; }

@@ -75,6 +75,12 @@ _SIGS = {
     "tdx_restore_transfer_workspace": (_SZ, [_PS, _PL, _I32, _I32, _I32]),
     "tdx_restore_transfer": (ctypes.c_int, [_PS, _PL, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P,
                                             _P, _SZ, _P]),
+    "tdx_round_plan_build": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P, ctypes.POINTER(_P)]),
+    "tdx_round_plan_n_groups": (ctypes.c_int, [_P]),
+    "tdx_round_plan_group_dims": (ctypes.c_int, [_P, _I32, _P, _P, _P]),
+    "tdx_round_plan_group": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _P]),
+    "tdx_round_plan_request": (ctypes.c_int, [_P, _I32, _P, _P]),
+    "tdx_round_plan_free": (None, [_P]),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -441,3 +447,56 @@ def decode_attn_dense(shape: Shape, lay: RoundLayout, q: torch.Tensor, priv_off:
         int(max_priv), _ptr(k_dense), _ptr(v_dense), scale, _ptr(out), _ptr(ws), ws.numel(),
         _stream()), "tdx_decode_attn_dense")
     return out
+
+
+def _np_ptr(a: Optional[np.ndarray]):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def round_plan(requests, sep_token: int, min_share: int = 0, slots=None) -> dict:
+    """Shared blocks, groups and per-group layouts of one round, from the
+    requests' token IDs (host only; ``tdx_round_plan_*``).
+
+    requests: sequence of int token-ID sequences; slots: optional sequence of
+    (begin, end) slot ranges, one per request.  Returns dict(groups=[dict(
+    agents, seg_ids, blk_start, src_pos, dst_pos [N][B], priv_len)],
+    request_group, token_maps) with int32 NumPy arrays.
+    """
+    reqs = [np.ascontiguousarray(np.asarray(r, dtype=np.int32).reshape(-1)) for r in requests]
+    R = len(reqs)
+    off = np.zeros(R + 1, dtype=np.int64)
+    off[1:] = np.cumsum([r.size for r in reqs])
+    tokens = np.ascontiguousarray(np.concatenate(reqs) if R else np.zeros(0, np.int32), dtype=np.int32)
+    sb = se = None
+    if slots is not None:
+        sl = np.asarray(slots, dtype=np.int64).reshape(R, 2)
+        sb, se = np.ascontiguousarray(sl[:, 0]), np.ascontiguousarray(sl[:, 1])
+    h = ctypes.c_void_p()
+    _check(lib().tdx_round_plan_build(_np_ptr(tokens) if tokens.size else None, _np_ptr(off), R, int(sep_token),
+                                      int(min_share), _np_ptr(sb), _np_ptr(se), ctypes.byref(h)),
+           "tdx_round_plan_build")
+    try:
+        ng = lib().tdx_round_plan_n_groups(h)
+        groups = []
+        for g in range(ng):
+            n, b, t = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+            _check(lib().tdx_round_plan_group_dims(h, g, ctypes.byref(n), ctypes.byref(b), ctypes.byref(t)),
+                   "tdx_round_plan_group_dims")
+            N, B = n.value, b.value
+            a = dict(agents=np.zeros(N, np.int32), seg_ids=np.zeros(B, np.int32),
+                     blk_start=np.zeros(B + 1, np.int32), src_pos=np.zeros(B, np.int32),
+                     dst_pos=np.zeros((N, B), np.int32), priv_len=np.zeros(N, np.int32))
+            _check(lib().tdx_round_plan_group(h, g, *(_np_ptr(a[k]) for k in (
+                "agents", "seg_ids", "blk_start", "src_pos", "dst_pos", "priv_len"))), "tdx_round_plan_group")
+            groups.append(a)
+        request_group = np.zeros(R, np.int32)
+        maps = []
+        for r in range(R):
+            g = ctypes.c_int32()
+            m = np.zeros(reqs[r].size, np.int32)
+            _check(lib().tdx_round_plan_request(h, r, ctypes.byref(g), _np_ptr(m)), "tdx_round_plan_request")
+            request_group[r] = g.value
+            maps.append(m)
+    finally:
+        lib().tdx_round_plan_free(h)
+    return dict(groups=groups, request_group=request_group, token_maps=maps)

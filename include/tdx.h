@@ -27,6 +27,9 @@
  *   tdx_restore_transfer  the transfer-path restore: Mirrors rebuilt layer by
  *                         layer from a Master and diff records kept in host
  *                         storage (notes §3d Algorithm 1; blog §4.4).
+ *   tdx_round_plan_*      host side: shared blocks, groups and their layouts
+ *                         derived from the requests' token IDs (notes §4
+ *                         Round-Aware Prompt Interface, §5 "Scheduling").
  *
  * Conventions shared by every call
  *  - Tensor arguments are DEVICE pointers (tdx_restore_transfer also takes
@@ -250,6 +253,64 @@ int tdx_decode_attn_dense(const tdx_shape *shape, const tdx_layout *layout,
                           void *ws, size_t ws_bytes, void *stream);
 size_t tdx_decode_attn_dense_workspace(const tdx_shape *shape, const tdx_layout *layout,
                                        int32_t max_priv);
+
+/* ---- round structure from token IDs (host only) -----------------------------
+ * The step before the collective calls: find the blocks that the requests of
+ * one round share and derive, per group of compatible requests, the
+ * tdx_layout arrays.  TokenDance notes §4 "Key Innovations" (Round-Aware
+ * Prompt Interface: a reserved separator token marks logical block
+ * boundaries and the runtime hashes segment content, not positions), §2a
+ * (data flow: prompt assembly with separators, segment hashing, grouping of
+ * compatible requests), §5 "Scheduling" (a group needs the same cached span
+ * and disjoint slot mappings; other requests fall back to per-request reuse);
+ * blog §4.1 (the separator).
+ *
+ * Definitions:
+ *  - a segment is a maximal run of tokens != sep_token in one request;
+ *    separators belong to no segment (they are private tokens);
+ *  - segments with equal token sequences are one block (exact comparison;
+ *    the hash only indexes candidates).  Block IDs are dense, numbered in
+ *    order of first appearance (requests in order, segments in order);
+ *  - a block is shared when at least min_share distinct requests hold it
+ *    (min_share <= 0: every request).  In one request only the first
+ *    occurrence is the shared copy; repeats are private;
+ *  - requests holding the same set of shared blocks form one group, unless
+ *    slot ranges are given: a request then joins the first group of its set
+ *    (groups numbered by first member) none of whose members' half-open
+ *    ranges [slot_begin, slot_end) intersects its own, else a new group;
+ *  - a group's blocks are ordered as they first appear in its first member:
+ *    blk_start is the prefix sum of their lengths, src_pos[b] = blk_start[b]
+ *    (the cached K of a block sits at its canonical position), dst_pos[i][b]
+ *    is the offset of block b's shared copy in member i, priv_len[i] = the
+ *    member's length - T.  A group of one request is the per-request case.
+ *
+ * All pointers are HOST pointers.  tokens [req_off[n_req]] int32 (request r
+ * is tokens[req_off[r] .. req_off[r+1])), req_off [n_req+1] non-decreasing
+ * int64; slot_begin/slot_end [n_req] int64 or both NULL.  On success *plan
+ * owns the result until tdx_round_plan_free.  Errors: TDX_EINVAL (null or
+ * inconsistent arguments, a request or shared region over INT32_MAX tokens;
+ * *plan is then NULL), TDX_EINTERNAL (out of host memory).  The encode and
+ * restore calls further need T % 16 == 0, which a derived layout need not
+ * meet. */
+typedef struct tdx_round_plan tdx_round_plan;
+int tdx_round_plan_build(const int32_t *tokens, const int64_t *req_off, int32_t n_req, int32_t sep_token,
+                         int32_t min_share, const int64_t *slot_begin, const int64_t *slot_end,
+                         tdx_round_plan **plan);
+/* number of groups (>= 1), or TDX_EINVAL for a NULL plan */
+int tdx_round_plan_n_groups(const tdx_round_plan *plan);
+/* N, B and T of group g; any output may be NULL */
+int tdx_round_plan_group_dims(const tdx_round_plan *plan, int32_t group, int32_t *n_agents,
+                              int32_t *n_blocks, int32_t *n_tokens);
+/* group g's members (request indices, ascending) [N], block IDs [B],
+ * blk_start [B+1], src_pos [B], dst_pos [N*B] (member-major), priv_len [N];
+ * any output may be NULL */
+int tdx_round_plan_group(const tdx_round_plan *plan, int32_t group, int32_t *agents, int32_t *seg_ids,
+                         int32_t *blk_start, int32_t *src_pos, int32_t *dst_pos, int32_t *priv_len);
+/* request r's group, and its token map [req_off[r+1] - req_off[r]]: the
+ * canonical index of each token in its group's shared region, -1 for a
+ * private token; either output may be NULL */
+int tdx_round_plan_request(const tdx_round_plan *plan, int32_t request, int32_t *group, int32_t *token_map);
+void tdx_round_plan_free(tdx_round_plan *plan);
 
 /* ---- utilities -------------------------------------------------------------*/
 const char *tdx_strerror(int code); /* static text for a return code */

@@ -7,3 +7,4 @@ must fail loudly when its compiled library is missing.
 """
 
 from .tdx_oracle import *  # noqa: F401,F403
+from .round_oracle import round_plan, segments  # noqa: F401
