@@ -270,6 +270,154 @@ int tdx_restore_attn(const tdx_shape* shape, const tdx_layout* layout, const voi
   GUARD_END
 }
 
+// ---- paged KV layout ----------------------------------------------------------
+
+namespace {
+// A paged view: pools 16-byte aligned (v_pool only where needed), page table
+// 4-byte aligned, n_pages >= 1, row stride >= the pages a row needs when
+// there is more than one row.
+int check_paged(const tdx_paged_kv* p, const char* what, bool need_v, int64_t rows, int64_t per_row,
+                tdx::PageMap* m) {
+  REQ(p != nullptr, TDX_EINVAL, "%s is null", what);
+  REQ(p->k_pool != nullptr && aligned16(p->k_pool), TDX_EINVAL, "%s.k_pool is null or not 16-byte aligned", what);
+  if (need_v)
+    REQ(p->v_pool != nullptr && aligned16(p->v_pool), TDX_EINVAL, "%s.v_pool is null or not 16-byte aligned",
+        what);
+  REQ(p->n_pages >= 1, TDX_EINVAL, "%s.n_pages < 1", what);
+  REQ(p->pages != nullptr && aligned4(p->pages), TDX_EINVAL, "%s.pages is null or not 4-byte aligned", what);
+  REQ(rows <= 1 || p->stride >= per_row, TDX_EINVAL, "%s.stride %lld < %lld pages per row", what,
+      (long long)p->stride, (long long)per_row);
+  *m = tdx::PageMap{p->pages, (long long)p->stride, (long long)p->n_pages};
+  return TDX_OK;
+}
+}  // namespace
+
+int tdx_rerotate_paged(const tdx_shape* shape, const tdx_layout* layout, const tdx_paged_kv* cached,
+                       const tdx_paged_kv* out, void* stream) {
+  GUARD_BEGIN
+  tdx::Dims d{};
+  int rc;
+  if ((rc = check_shape(shape, &d)) != TDX_OK) return rc;
+  if ((rc = check_layout(layout, &d, true)) != TDX_OK) return rc;
+  const int64_t np = (d.T + TDX_DIFF_BLOCK - 1) / TDX_DIFF_BLOCK;
+  tdx::PageMap pin{}, pout{};
+  if ((rc = check_paged(cached, "cached", false, 1, np, &pin)) != TDX_OK) return rc;
+  if ((rc = check_paged(out, "out", false, d.N, np, &pout)) != TDX_OK) return rc;
+  hipError_t e = tdx::launch_rerotate_paged(d, *layout, cached->k_pool, pin, out->k_pool, pout,
+                                            static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tdx_rerotate_paged launch");
+  return ok();
+  GUARD_END
+}
+
+int tdx_select_important_paged(const tdx_shape* shape, const tdx_layout* layout, int32_t check_layer,
+                               const tdx_paged_kv* k_reuse, const void* k_recomp, int32_t k, float* dev,
+                               float* score, float* agent_dev, int32_t* selected, int32_t* master, void* ws,
+                               size_t ws_bytes, void* stream) {
+  GUARD_BEGIN
+  tdx::Dims d{};
+  int rc;
+  if ((rc = check_shape(shape, &d)) != TDX_OK) return rc;
+  if ((rc = check_layout(layout, &d, false)) != TDX_OK) return rc;
+  REQ(check_layer >= 0 && check_layer < d.L, TDX_EINVAL, "check_layer %d outside [0, %d)", check_layer, d.L);
+  REQ(k >= 1 && k <= d.T, TDX_EINVAL, "k %d outside [1, %d]", k, d.T);
+  tdx::PageMap pm{};
+  if ((rc = check_paged(k_reuse, "k_reuse", false, d.N, (d.T + TDX_DIFF_BLOCK - 1) / TDX_DIFF_BLOCK, &pm)) !=
+      TDX_OK)
+    return rc;
+  REQ_PTR(k_recomp);
+  REQ_PTR4(dev);
+  REQ_PTR4(score);
+  REQ_PTR4(agent_dev);
+  REQ_PTR4(selected);
+  REQ_PTR4(master);
+  const size_t need = tdx::select_ws_bytes(d);
+  REQ(ws != nullptr && aligned16(ws) && ws_bytes >= need, TDX_EWORKSPACE,
+      "workspace needs %zu bytes (16-byte aligned), got %zu", need, ws_bytes);
+  hipError_t e = tdx::launch_select_paged(d, check_layer, k_reuse->k_pool, pm, k_recomp, k, dev, score, agent_dev,
+                                          selected, master, ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tdx_select_important_paged launch");
+  return ok();
+  GUARD_END
+}
+
+int tdx_diff_encode_paged(const tdx_shape* shape, const tdx_layout* layout, const int32_t* master,
+                          const tdx_paged_kv* agents, int64_t cap_blocks, int32_t* diff_off, int32_t* diff_idx,
+                          int32_t* diff_page, void* diff_k, void* diff_v, int64_t* nnz, void* ws, size_t ws_bytes,
+                          void* stream) {
+  GUARD_BEGIN
+  tdx::Dims d{};
+  int rc;
+  if ((rc = check_shape(shape, &d)) != TDX_OK) return rc;
+  if ((rc = check_layout(layout, &d, false)) != TDX_OK) return rc;
+  REQ(d.T % TDX_DIFF_BLOCK == 0, TDX_EINVAL, "n_tokens %d is not a multiple of 16", d.T);
+  REQ(cap_blocks >= 0, TDX_EINVAL, "cap_blocks < 0");
+  REQ((int64_t)d.N * d.L <= INT32_MAX, TDX_EUNSUPPORTED, "too many CSR rows");
+  REQ_PTR4(master);
+  tdx::PageMap pm{};
+  if ((rc = check_paged(agents, "agents", true, d.N, d.T / TDX_DIFF_BLOCK, &pm)) != TDX_OK) return rc;
+  REQ_PTR4(diff_off);
+  REQ((reinterpret_cast<uintptr_t>(nnz) & 7u) == 0 && nnz != nullptr, TDX_EINVAL, "nnz is null or not 8-byte aligned");
+  REQ((diff_k == nullptr) == (diff_v == nullptr), TDX_EINVAL, "diff_k and diff_v must both be set or both be NULL");
+  if (cap_blocks > 0) {
+    REQ_PTR4(diff_idx);
+    REQ_PTR4(diff_page);
+    if (diff_k != nullptr) {
+      REQ_PTR(diff_k);
+      REQ_PTR(diff_v);
+    }
+  }
+  const size_t need = tdx::encode_ws_bytes(d);
+  REQ(ws != nullptr && aligned16(ws) && ws_bytes >= need, TDX_EWORKSPACE,
+      "workspace needs %zu bytes (16-byte aligned), got %zu", need, ws_bytes);
+  hipError_t e = tdx::launch_encode_paged(d, master, agents->k_pool, agents->v_pool, pm, cap_blocks, diff_off,
+                                          diff_idx, diff_page, diff_k, diff_v, nnz, ws,
+                                          static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tdx_diff_encode_paged launch");
+  return ok();
+  GUARD_END
+}
+
+int tdx_restore_attn_paged(const tdx_shape* shape, const tdx_layout* layout, const void* q,
+                           const int32_t* priv_off, const tdx_paged_kv* priv, int32_t max_priv,
+                           const tdx_paged_kv* agents, const int32_t* master_sel, const int32_t* diff_off,
+                           const int32_t* diff_idx, const int32_t* diff_page, float scale, void* out, void* ws,
+                           size_t ws_bytes, void* stream) {
+  GUARD_BEGIN
+  tdx::Dims d{};
+  int rc;
+  if ((rc = check_shape(shape, &d)) != TDX_OK) return rc;
+  if ((rc = check_layout(layout, &d, true)) != TDX_OK) return rc;
+  REQ(d.T % TDX_DIFF_BLOCK == 0, TDX_EINVAL, "n_tokens %d is not a multiple of 16", d.T);
+  REQ(d.Hq / d.Hkv <= 16, TDX_EUNSUPPORTED, "more than 16 query heads per KV head");
+  REQ(max_priv >= 0, TDX_EINVAL, "max_priv < 0");
+  REQ(scale > 0.0f, TDX_EINVAL, "scale must be > 0");
+  REQ_PTR(q);
+  REQ_PTR4(priv_off);
+  tdx::PageMap ppm{nullptr, 0, 1}, apm{};
+  if (max_priv > 0 &&
+      (rc = check_paged(priv, "priv", true, d.N, (max_priv + TDX_DIFF_BLOCK - 1) / TDX_DIFF_BLOCK, &ppm)) != TDX_OK)
+    return rc;
+  if ((rc = check_paged(agents, "agents", true, d.N, d.T / TDX_DIFF_BLOCK, &apm)) != TDX_OK) return rc;
+  REQ(master_sel == nullptr || aligned4(master_sel), TDX_EINVAL, "master_sel not 4-byte aligned");
+  REQ_PTR4(diff_off);
+  // diff arrays may be empty (all rows empty) but must then still be valid
+  // pointers to zero-length storage; they are only read through diff_off.
+  REQ(diff_idx != nullptr && diff_page != nullptr, TDX_EINVAL, "diff arrays are null");
+  REQ_PTR(out);
+  const size_t need = tdx::restore_attn_ws_bytes(d, max_priv);
+  REQ(ws != nullptr && aligned16(ws) && ws_bytes >= need, TDX_EWORKSPACE,
+      "workspace needs %zu bytes (16-byte aligned), got %zu", need, ws_bytes);
+  const void* pk = max_priv > 0 ? priv->k_pool : agents->k_pool;  // not read when max_priv = 0
+  const void* pv = max_priv > 0 ? priv->v_pool : agents->v_pool;
+  hipError_t e = tdx::launch_restore_attn_paged(d, *layout, q, priv_off, pk, pv, ppm, max_priv, agents->k_pool,
+                                                agents->v_pool, apm, master_sel, diff_off, diff_idx, diff_page,
+                                                scale, out, ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tdx_restore_attn_paged launch");
+  return ok();
+  GUARD_END
+}
+
 // The GPU can read p: device memory or registered (pinned) host memory.
 bool gpu_readable(const void* p) {
   hipPointerAttribute_t at{};

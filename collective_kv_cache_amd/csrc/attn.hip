@@ -181,6 +181,12 @@ struct AttnArgs {
   int AGS, NAG, TPG;         // shared kernel: agents per group, groups, tiles per split
   int n_sh_wg;               // shared kernel: real workgroups (grid is padded to 8)
   float scale_log2;
+  // paged (fused): sk/sv, dk/dv are the agents' K/V pools and pk/pv the
+  // private pools; the Master's pages are row *msel of mpm, the diff entries'
+  // pages dpm[0][e], agent i's private pages row i of ppm
+  PageMap mpm, dpm, ppm;
+  int pmax;  // >= 0: an agent's private tokens are capped at pmax (paged: a
+             // page-table row holds ceil(pmax/16) pages); -1: no cap
 };
 
 template <int D>
@@ -319,7 +325,7 @@ __device__ __forceinline__ u32x4 sh_ld(const E* p) {
 #ifndef TDX_SH_WPE
 #define TDX_SH_WPE 3
 #endif
-template <typename E, int D, int PD>
+template <typename E, int D, int PD, bool PAGED>
 __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(TDX_SH_WPE))) void shared_kernel(AttnArgs a) {
   using St = ShStage<E, D>;
   constexpr int KD = D / 32;
@@ -389,19 +395,24 @@ __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(TDX_
   st.init();
 
   const size_t rowHD = (size_t)a.Hkv * D;
-  const size_t moff = master_offset(a.msel, a.mstride, a.N);
-  const E* mk = static_cast<const E*>(a.sk) + moff + (size_t)l * a.T * rowHD + (size_t)h * D;
-  const E* mv = static_cast<const E*>(a.sv) + moff + (size_t)l * a.T * rowHD + (size_t)h * D;
+  // contiguous: Master token t at mk + t * rowHD; paged: at page
+  // mpm[mrow][t / 16], row t % 16 of layer l
+  const size_t moff = PAGED ? 0 : master_offset(a.msel, a.mstride, a.N) + (size_t)l * a.T * rowHD;
+  const E* mk = static_cast<const E*>(a.sk) + moff + (size_t)h * D;
+  const E* mv = static_cast<const E*>(a.sv) + moff + (size_t)h * D;
+  const int mrow = (PAGED && a.msel != nullptr) ? min(max(a.msel[0], 0), a.N - 1) : 0;
   const E* qrow = static_cast<const E*>(a.q) + (((size_t)agent * a.L + l) * a.Hq + hq) * D;
   const float2* tabrow = a.tab + (size_t)agent * a.B * HALF;
 
   auto load = [&](int tile, St& S) {
+    const size_t trow = PAGED ? ((size_t)l * a.mpm.n_pages + page_at(a.mpm, mrow, tile)) * kTile
+                              : (size_t)tile * kTile;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int idx = tid + c * kShThreads;
       const int tensor = idx / (kTile * CH);
       const int rem = idx % (kTile * CH);
-      const E* src = (tensor ? mv : mk) + (size_t)(tile * kTile + rem / CH) * rowHD + (rem % CH) * 8;
+      const E* src = (tensor ? mv : mk) + (trow + rem / CH) * rowHD + (rem % CH) * 8;
 #pragma unroll
       for (int p = 0; p < LPC; ++p) S.kv[c * LPC + p] = sh_ld(src + p * (8 / LPC));
     }
@@ -601,6 +612,7 @@ __global__ __launch_bounds__(kPlanThreads) void stream_plan_kernel(AttnArgs a, S
         const int i = r / a.L, l = r % a.L;
         const int p0 = a.priv_off[i];
         t.P = a.priv_off[i + 1] - p0;
+        if (a.pmax >= 0) t.P = min(t.P, a.pmax);
         t.ntp = (t.P + kTile - 1) / kTile;
         t.prow = l * ptot + p0;
         int nx = nb;
@@ -676,7 +688,7 @@ __global__ __launch_bounds__(kDiffTabThreads) void diff_tab_kernel(const int32_t
   }
 }
 
-template <typename E, int D, int MODE, int PD>
+template <typename E, int D, int MODE, int PD, bool PAGED>
 __global__ __launch_bounds__(kStreamNW * kWave) __attribute__((amdgpu_waves_per_eu(TDX_ST_WPE))) void stream_kernel(
     AttnArgs a, const StreamTask* __restrict__ tasks, const int32_t* __restrict__ ctl, const float2* __restrict__ dcs,
     const int2* __restrict__ dinfo) {
@@ -772,13 +784,17 @@ __global__ __launch_bounds__(kStreamNW * kWave) __attribute__((amdgpu_waves_per_
     int rmax = kTile - 1;  // rows past the end of a partial tile re-read its last row
     size_t e = 0;
     if (u < LT.ntp) {
-      const size_t o = (((size_t)LT.prow + (size_t)u * kTile) * rowHD + (size_t)lh * D) * sizeof(E);
+      const size_t prow = PAGED ? ((size_t)(LT.r % a.L) * a.ppm.n_pages + page_at(a.ppm, LT.r / a.L, u)) * kTile
+                                : (size_t)LT.prow + (size_t)u * kTile;
+      const size_t o = (prow * rowHD + (size_t)lh * D) * sizeof(E);
       kb = pkb + o;
       vb = pvb + o;
       rmax = min(kTile - 1, LT.P - 1 - u * kTile);
     } else if (MODE == FUSED) {
       e = (size_t)(LT.e0 + u - LT.ntp);
-      const size_t o = (e * kTile * rowHD + (size_t)lh * D) * sizeof(E);
+      const size_t drow = PAGED ? ((size_t)(LT.r % a.L) * a.dpm.n_pages + page_at(a.dpm, 0, (long long)e)) * kTile
+                                : e * kTile;
+      const size_t o = (drow * rowHD + (size_t)lh * D) * sizeof(E);
       kb = static_cast<const unsigned char*>(a.dk) + o;
       vb = static_cast<const unsigned char*>(a.dv) + o;
     } else {
@@ -961,7 +977,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, E* __restrict__ 
   if (row >= (size_t)a.N * a.L * a.Hq) return;
   const int i = (int)(row / ((size_t)a.L * a.Hq));
   const int l = (int)((row / a.Hq) % a.L);
-  const int P = a.priv_off[i + 1] - a.priv_off[i];
+  const int P = a.pmax >= 0 ? min(a.priv_off[i + 1] - a.priv_off[i], a.pmax) : a.priv_off[i + 1] - a.priv_off[i];
   const int nx = (MODE == FUSED) ? min(max(a.diff_off[i * a.L + l + 1] - a.diff_off[i * a.L + l], 0), a.T / kTile)
                                   : a.T / kTile;
   const int nt = (P + kTile - 1) / kTile + nx;
@@ -1148,8 +1164,9 @@ size_t shared_lds(int D, int B, const Plan& p) {
   return (size_t)4 * kTile * (D + 8) * 2 + (size_t)(B + 1) * 4 + (size_t)p.AGS * p.TPG;
 }
 
-template <typename E, int D, int MODE>
+template <typename E, int D, int MODE, bool PAGED>
 hipError_t launch_attn_t(const Dims& d, AttnArgs a, const Plan& p, E* out, hipStream_t s) {
+  static_assert(!PAGED || MODE == FUSED, "paged caches: fused path only");
   a.SP = p.SP;
   a.SG = p.SG;
   a.S = p.SP + p.SG;
@@ -1163,7 +1180,7 @@ hipError_t launch_attn_t(const Dims& d, AttnArgs a, const Plan& p, E* out, hipSt
     const size_t lds = shared_lds(D, d.B, p);
     if (lds > 64 * 1024) return hipErrorInvalidValue;
     const int grid = (p.n_sh_wg + 7) / 8 * 8;
-    hipLaunchKernelGGL((shared_kernel<E, D, TDX_SH_PD>), dim3(grid), dim3(kShThreads), lds, s, a);
+    hipLaunchKernelGGL((shared_kernel<E, D, TDX_SH_PD, PAGED>), dim3(grid), dim3(kShThreads), lds, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if constexpr (sizeof(E) == 2) {
@@ -1178,7 +1195,7 @@ hipError_t launch_attn_t(const Dims& d, AttnArgs a, const Plan& p, E* out, hipSt
   }
   constexpr int PD = StreamCfg<E, D>::PD;
   const size_t lds = StreamCfg<E, D>::lds(MODE == FUSED);
-  auto kern = stream_kernel<E, D, MODE, PD>;
+  auto kern = stream_kernel<E, D, MODE, PD, PAGED>;
   int dev = 0, ncu = 0, per_cu = 0;
   if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
   if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
@@ -1202,13 +1219,13 @@ hipError_t launch_attn_t(const Dims& d, AttnArgs a, const Plan& p, E* out, hipSt
   return hipGetLastError();
 }
 
-template <int MODE>
+template <int MODE, bool PAGED = false>
 hipError_t dispatch_attn(const Dims& d, AttnArgs a, const Plan& p, void* out, hipStream_t s) {
   if (d.dtype == TDX_BF16)
-    return d.D == 128 ? launch_attn_t<uint16_t, 128, MODE>(d, a, p, static_cast<uint16_t*>(out), s)
-                      : launch_attn_t<uint16_t, 64, MODE>(d, a, p, static_cast<uint16_t*>(out), s);
-  return d.D == 128 ? launch_attn_t<float, 128, MODE>(d, a, p, static_cast<float*>(out), s)
-                    : launch_attn_t<float, 64, MODE>(d, a, p, static_cast<float*>(out), s);
+    return d.D == 128 ? launch_attn_t<uint16_t, 128, MODE, PAGED>(d, a, p, static_cast<uint16_t*>(out), s)
+                      : launch_attn_t<uint16_t, 64, MODE, PAGED>(d, a, p, static_cast<uint16_t*>(out), s);
+  return d.D == 128 ? launch_attn_t<float, 128, MODE, PAGED>(d, a, p, static_cast<float*>(out), s)
+                    : launch_attn_t<float, 64, MODE, PAGED>(d, a, p, static_cast<float*>(out), s);
 }
 
 AttnArgs common_args(const Dims& d, const void* q, const int32_t* priv_off, const void* pk,
@@ -1227,6 +1244,7 @@ AttnArgs common_args(const Dims& d, const void* q, const int32_t* priv_off, cons
   a.Hkv = d.Hkv;
   a.Hq = d.Hq;
   a.scale_log2 = scale * kLog2e;
+  a.pmax = -1;
   return a;
 }
 
@@ -1235,21 +1253,14 @@ AttnArgs common_args(const Dims& d, const void* q, const int32_t* priv_off, cons
 size_t restore_attn_ws_bytes(const Dims& d, int max_priv) { return make_plan(d, max_priv, true).total; }
 size_t dense_attn_ws_bytes(const Dims& d, int max_priv) { return make_plan(d, max_priv, false).total; }
 
-hipError_t launch_restore_attn(const Dims& d, const tdx_layout& lay, const void* q,
-                               const int32_t* priv_off, const void* pk, const void* pv,
-                               int max_priv, const MasterRef& master,
-                               const int32_t* diff_off, const int32_t* diff_idx, const void* dk,
-                               const void* dv, float scale, void* out, void* ws, hipStream_t s) {
+namespace {
+// Query side (cos/sin table, per-diff-entry rows), then the fused kernels.
+template <bool PAGED>
+hipError_t restore_attn_t(const Dims& d, const tdx_layout& lay, AttnArgs a, const int32_t* diff_off,
+                          const int32_t* diff_idx, int max_priv, void* out, void* ws, hipStream_t s) {
   const Plan p = make_plan(d, max_priv, true);
-  AttnArgs a = common_args(d, q, priv_off, pk, pv, scale, ws);
-  a.sk = master.k;
-  a.sv = master.v;
-  a.msel = master.sel;
-  a.mstride = master.stride;
   a.diff_off = diff_off;
   a.diff_idx = diff_idx;
-  a.dk = dk;
-  a.dv = dv;
   a.blk_start = lay.blk_start;
   float2* tab = reinterpret_cast<float2*>(static_cast<unsigned char*>(ws) + p.tab_off);
   a.tab = tab;
@@ -1266,7 +1277,41 @@ hipError_t launch_restore_attn(const Dims& d, const tdx_layout& lay, const void*
                        reinterpret_cast<int2*>(static_cast<unsigned char*>(ws) + p.dinfo_off));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  return dispatch_attn<FUSED>(d, a, p, out, s);
+  return dispatch_attn<FUSED, PAGED>(d, a, p, out, s);
+}
+}  // namespace
+
+hipError_t launch_restore_attn(const Dims& d, const tdx_layout& lay, const void* q,
+                               const int32_t* priv_off, const void* pk, const void* pv,
+                               int max_priv, const MasterRef& master,
+                               const int32_t* diff_off, const int32_t* diff_idx, const void* dk,
+                               const void* dv, float scale, void* out, void* ws, hipStream_t s) {
+  AttnArgs a = common_args(d, q, priv_off, pk, pv, scale, ws);
+  a.sk = master.k;
+  a.sv = master.v;
+  a.msel = master.sel;
+  a.mstride = master.stride;
+  a.dk = dk;
+  a.dv = dv;
+  return restore_attn_t<false>(d, lay, a, diff_off, diff_idx, max_priv, out, ws, s);
+}
+
+hipError_t launch_restore_attn_paged(const Dims& d, const tdx_layout& lay, const void* q, const int32_t* priv_off,
+                                     const void* pk_pool, const void* pv_pool, const PageMap& ppm, int max_priv,
+                                     const void* ak_pool, const void* av_pool, const PageMap& apm,
+                                     const int32_t* master_sel, const int32_t* diff_off, const int32_t* diff_idx,
+                                     const int32_t* diff_page, float scale, void* out, void* ws, hipStream_t s) {
+  AttnArgs a = common_args(d, q, priv_off, pk_pool, pv_pool, scale, ws);
+  a.sk = ak_pool;  // the Master's pages and the diff entries' pages are agents' pages
+  a.sv = av_pool;
+  a.dk = ak_pool;
+  a.dv = av_pool;
+  a.msel = master_sel;
+  a.mpm = apm;
+  a.dpm = PageMap{diff_page, 0, apm.n_pages};
+  a.ppm = ppm;
+  a.pmax = max_priv;  // the page tables hold no private page past it
+  return restore_attn_t<true>(d, lay, a, diff_off, diff_idx, max_priv, out, ws, s);
 }
 
 hipError_t launch_restore_dense(const Dims& d, const tdx_layout& lay, const MasterRef& master,

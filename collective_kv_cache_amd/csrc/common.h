@@ -97,6 +97,20 @@ __device__ __forceinline__ void st16_nt(E* p, const u32x4& v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
+// A paged KV pool: page p of layer l holds 16 token rows of Hkv*D elements
+// at pool + (l * n_pages + p) * 16 * Hkv * D; row r of the page table starts
+// at pages + r * stride.  Page IDs outside [0, n_pages) are clamped, so a bad
+// table reads or writes a wrong page of the pool but never outside it.
+struct PageMap {
+  const int32_t* pages;
+  long long stride;
+  long long n_pages;
+};
+__device__ __forceinline__ long long page_at(const PageMap& m, long long row, long long j) {
+  const long long p = m.pages[row * m.stride + j];
+  return p < 0 ? 0 : (p >= m.n_pages ? m.n_pages - 1 : p);
+}
+
 // RoPE inverse frequency theta^(-2e/D) in double precision.
 __device__ __forceinline__ double rope_inv_freq(double theta, int e, int D) {
   return pow(theta, -2.0 * (double)e / (double)D);
@@ -116,6 +130,9 @@ struct Dims {
 
 hipError_t launch_rerotate(const Dims& d, const tdx_layout& lay, const void* kc, void* out,
                            hipStream_t s);
+// paged: cached K in pages cin (row 0), agent i's output in pages cout row i
+hipError_t launch_rerotate_paged(const Dims& d, const tdx_layout& lay, const void* kc, const PageMap& cin,
+                                 void* out, const PageMap& cout, hipStream_t s);
 
 size_t select_ws_bytes(const Dims& d);
 hipError_t launch_select(const Dims& d, const tdx_layout& lay, int check_layer,
@@ -123,11 +140,23 @@ hipError_t launch_select(const Dims& d, const tdx_layout& lay, int check_layer,
                          float* score, float* agent_dev, int32_t* selected, int32_t* master,
                          void* ws, hipStream_t s);
 
+// paged: agent i's reused K at the check layer in pages pm row i of the pool
+hipError_t launch_select_paged(const Dims& d, int check_layer, const void* kr_pool, const PageMap& pm,
+                               const void* k_recomp, int k, float* dev, float* score, float* agent_dev,
+                               int32_t* selected, int32_t* master, void* ws, hipStream_t s);
+
 size_t encode_ws_bytes(const Dims& d);
 hipError_t launch_encode(const Dims& d, const int32_t* master, const void* ak, const void* av,
                          int64_t cap, int32_t* diff_off, int32_t* diff_idx, void* diff_k,
                          void* diff_v, int64_t* nnz, void* mk_out, void* mv_out, void* ws,
                          hipStream_t s);
+
+// paged: agent a's block beta is page pm[a][beta] of the K and V pools; the
+// record holds each entry's page (diff_page) and, when diff_k is set, copies
+hipError_t launch_encode_paged(const Dims& d, const int32_t* master, const void* k_pool, const void* v_pool,
+                               const PageMap& pm, int64_t cap, int32_t* diff_off, int32_t* diff_idx,
+                               int32_t* diff_page, void* diff_k, void* diff_v, int64_t* nnz, void* ws,
+                               hipStream_t s);
 
 size_t restore_attn_ws_bytes(const Dims& d, int max_priv);
 // The Master's cache: k/v + m * stride elements, m = *sel clamped to [0, N)
@@ -145,6 +174,15 @@ hipError_t launch_restore_attn(const Dims& d, const tdx_layout& lay, const void*
                                const int32_t* diff_off, const int32_t* diff_idx,
                                const void* dk, const void* dv, float scale, void* out, void* ws,
                                hipStream_t s);
+
+// paged: agent i's private history in pages ppm row i of the private pools;
+// the Master (agent *master_sel) and the diff blocks in pages of the agents'
+// pools (the Master's row of apm; entry e's page diff_page[e])
+hipError_t launch_restore_attn_paged(const Dims& d, const tdx_layout& lay, const void* q, const int32_t* priv_off,
+                                     const void* pk_pool, const void* pv_pool, const PageMap& ppm, int max_priv,
+                                     const void* ak_pool, const void* av_pool, const PageMap& apm,
+                                     const int32_t* master_sel, const int32_t* diff_off, const int32_t* diff_idx,
+                                     const int32_t* diff_page, float scale, void* out, void* ws, hipStream_t s);
 
 hipError_t launch_restore_dense(const Dims& d, const tdx_layout& lay, const MasterRef& master,
                                 const int32_t* diff_off,

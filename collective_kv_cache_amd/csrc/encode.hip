@@ -42,11 +42,14 @@ constexpr int kMaxAgents = 1024;
 // after the item's last block one barrier publishes the marks as the item's
 // flags.  The unrolled body has no branch around a load, so the wait before
 // a block is used leaves the younger blocks' loads outstanding.
-template <int KC, int PD>
+//
+// PAGED: agent a's block beta of layer l is page pm[a][beta] of the K and V
+// pools (ak, av), whose pages hold `chunks` 16-byte chunks each.
+template <int KC, int PD, bool PAGED>
 __global__ __launch_bounds__(kFlagThreads) void flag_kernel(
     const u32x4* __restrict__ ak, const u32x4* __restrict__ av,
     const int32_t* __restrict__ master_p, int N, int L, int nb, int chunks, int nslices,
-    uint8_t* __restrict__ flags, u32x4* __restrict__ mk_out, u32x4* __restrict__ mv_out) {
+    uint8_t* __restrict__ flags, u32x4* __restrict__ mk_out, u32x4* __restrict__ mv_out, PageMap pm) {
   __shared__ uint8_t mark[2][kMaxAgents];
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -79,7 +82,8 @@ __global__ __launch_bounds__(kFlagThreads) void flag_kernel(
     const int j = (int)(p % N);
     const int a = j == 0 ? m : (j - 1) + (j - 1 >= m);
     const int beta = w % nb, l = (w / nb) % L, cs = w / (nb * L);
-    const size_t base = ((size_t)a * L + l) * layer_chunks + (size_t)beta * chunks;
+    const size_t base = PAGED ? ((size_t)l * pm.n_pages + page_at(pm, a, beta)) * chunks
+                              : ((size_t)a * L + l) * layer_chunks + (size_t)beta * chunks;
     const int c0 = cs * KC * kFlagThreads;
 #pragma unroll
     for (int q = 0; q < KC; ++q) {
@@ -230,10 +234,14 @@ __device__ __forceinline__ void cp_store(const u32x4& v, u32x4* p) {
 #endif
 }
 
+// PAGED: the Mirror's block is page pm[a][beta] (row r = a * L + l); its page
+// ID goes to diff_page[slot], and the values are copied only when dk is set.
+template <bool PAGED>
 __global__ __launch_bounds__(kThreads) void copy_kernel(
     const u32x4* __restrict__ ak, const u32x4* __restrict__ av, const uint8_t* __restrict__ flags,
     const int32_t* __restrict__ rank, const int32_t* __restrict__ off, int nb, int chunks,
-    int64_t cap, int32_t* __restrict__ diff_idx, u32x4* __restrict__ dk, u32x4* __restrict__ dv) {
+    int64_t cap, int32_t* __restrict__ diff_idx, u32x4* __restrict__ dk, u32x4* __restrict__ dv,
+    PageMap pm, int L, int32_t* __restrict__ diff_page) {
   const size_t r = blockIdx.y;
   const int b0 = blockIdx.x * kCopyChunk;
   const int tid = threadIdx.x;
@@ -242,8 +250,14 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(
     if (!flags[r * nb + beta]) continue;  // uniform
     const int64_t slot = row_off + rank[r * nb + beta];
     if (slot >= cap) continue;
+    size_t src = (r * nb + beta) * (size_t)chunks;
+    if constexpr (PAGED) {
+      const long long pg = page_at(pm, (long long)(r / L), beta);
+      src = ((size_t)(r % L) * pm.n_pages + pg) * chunks;
+      if (tid == 0) diff_page[slot] = (int32_t)pg;
+    }
     if (tid == 0) diff_idx[slot] = beta;
-    const size_t src = (r * nb + beta) * (size_t)chunks;
+    if (dk == nullptr) continue;  // paged record without value copies (uniform)
     const size_t dst = (size_t)slot * chunks;
     // kCopyUnroll chunks of K and of V per thread in flight, then their stores
     for (int c0 = tid; c0 < chunks; c0 += kThreads * kCopyUnroll) {
@@ -295,10 +309,11 @@ WsLayout ws_layout(const Dims& d) {
 
 size_t encode_ws_bytes(const Dims& d) { return ws_layout(d).total; }
 
-hipError_t launch_encode(const Dims& d, const int32_t* master, const void* ak, const void* av,
-                         int64_t cap, int32_t* diff_off, int32_t* diff_idx, void* diff_k,
-                         void* diff_v, int64_t* nnz, void* mk_out, void* mv_out, void* ws,
-                         hipStream_t s) {
+namespace {
+template <bool PAGED>
+hipError_t encode_t(const Dims& d, const int32_t* master, const void* ak, const void* av, const PageMap& pm,
+                    int64_t cap, int32_t* diff_off, int32_t* diff_idx, int32_t* diff_page, void* diff_k,
+                    void* diff_v, int64_t* nnz, void* mk_out, void* mv_out, void* ws, hipStream_t s) {
   const int nb = d.T / kBlock;
   const int chunks = block_chunks(d);
   const int rows = d.N * d.L;
@@ -326,10 +341,10 @@ hipError_t launch_encode(const Dims& d, const int32_t* master, const void* ak, c
       if (grid > nitems) grid = nitems;
       if (grid < 1) grid = 1;
       hipLaunchKernelGGL(kern, dim3(grid), dim3(kFlagThreads), 0, s, k4, v4, master, d.N, d.L, nb, chunks, ns,
-                         flags, mk4, mv4);
+                         flags, mk4, mv4, pm);
       return hipGetLastError();
     };
-    e = flag_kc(d) == 1 ? launch_flag(flag_kernel<1, 8>) : launch_flag(flag_kernel<2, 4>);
+    e = flag_kc(d) == 1 ? launch_flag(flag_kernel<1, 8, PAGED>) : launch_flag(flag_kernel<2, 4, PAGED>);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(rows_kernel, dim3(rows), dim3(kThreads), 0, s, flags, nb, ns, (size_t)rows * nb, rank,
                        count);
@@ -340,10 +355,28 @@ hipError_t launch_encode(const Dims& d, const int32_t* master, const void* ak, c
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 cgrid((nb + kCopyChunk - 1) / kCopyChunk, rows);
-  hipLaunchKernelGGL(copy_kernel, cgrid, dim3(kThreads), 0, s, k4, v4, flags, rank, diff_off, nb,
-                     chunks, cap, diff_idx, static_cast<u32x4*>(diff_k),
-                     static_cast<u32x4*>(diff_v));
+  hipLaunchKernelGGL((copy_kernel<PAGED>), cgrid, dim3(kThreads), 0, s, k4, v4, flags, rank, diff_off, nb,
+                     chunks, cap, diff_idx, static_cast<u32x4*>(diff_k), static_cast<u32x4*>(diff_v), pm, d.L,
+                     diff_page);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_encode(const Dims& d, const int32_t* master, const void* ak, const void* av,
+                         int64_t cap, int32_t* diff_off, int32_t* diff_idx, void* diff_k,
+                         void* diff_v, int64_t* nnz, void* mk_out, void* mv_out, void* ws,
+                         hipStream_t s) {
+  const PageMap none{nullptr, 0, 1};
+  return encode_t<false>(d, master, ak, av, none, cap, diff_off, diff_idx, nullptr, diff_k, diff_v, nnz, mk_out,
+                         mv_out, ws, s);
+}
+
+hipError_t launch_encode_paged(const Dims& d, const int32_t* master, const void* k_pool, const void* v_pool,
+                               const PageMap& pm, int64_t cap, int32_t* diff_off, int32_t* diff_idx,
+                               int32_t* diff_page, void* diff_k, void* diff_v, int64_t* nnz, void* ws,
+                               hipStream_t s) {
+  return encode_t<true>(d, master, k_pool, v_pool, pm, cap, diff_off, diff_idx, diff_page, diff_k, diff_v, nnz,
+                        nullptr, nullptr, ws, s);
 }
 
 }  // namespace tdx

@@ -56,11 +56,16 @@ __device__ __forceinline__ int tab_col(int e) {
 // One workgroup: canonical tokens [t0, t0+16) for layers [l0, l0+lpg).  The
 // (layer, batch) steps run in sequence and the next step's input is loaded
 // while the current one is written out for every agent.
-template <typename E, int D>
+//
+// PAGED: the cached K and every agent's output live in 16-token pages of
+// pools (a workgroup's tile is one page); pin row 0 lists the cached K's
+// pages, pout row i agent i's pages, both in canonical token order.
+template <typename E, int D, bool PAGED>
 __global__ __launch_bounds__(kThreads) void rerotate_kernel(
     const E* __restrict__ kc, E* __restrict__ out, const int32_t* __restrict__ blk_start,
     const int32_t* __restrict__ src_pos, const int32_t* __restrict__ dst_pos, int N, int B,
-    int T, int L, int Hkv, int lpg, int apg, double theta) {
+    int T, int L, int Hkv, int lpg, int apg, double theta, PageMap pin, PageMap pout) {
+  static_assert(!PAGED || kTileTok == kBlock, "a paged tile is one page");
   constexpr int VEC = Fmt<E>::VEC;
   constexpr int HALF = D / 2;
   constexpr int G = HALF / VEC;       // lanes per (token, head) row
@@ -69,7 +74,8 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(
   extern __shared__ __align__(16) unsigned char smem[];
   float2* tab = reinterpret_cast<float2*>(smem);                      // [kAgentChunk][HALF]
   double* invf = reinterpret_cast<double*>(tab + kAgentChunk * TROW);  // [HALF]
-  int32_t* sblk = reinterpret_cast<int32_t*>(invf + HALF);            // [B+1]
+  long long* opage = reinterpret_cast<long long*>(invf + HALF);        // [kAgentChunk] (paged)
+  int32_t* sblk = reinterpret_cast<int32_t*>(opage + kAgentChunk);     // [B+1]
 
   const int tid = threadIdx.x;
   const int t0 = blockIdx.x * kTileTok;
@@ -94,6 +100,8 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(
   const int e0 = (tid % G) * VEC;
   const int row_base = tid / G;
   const size_t rowD = (size_t)Hkv * D;
+  const int pj = t0 / kBlock;                         // paged: the tile's page column
+  const long long ipage = PAGED ? page_at(pin, 0, pj) : 0;
 
   for (int b = lo; b < B && sblk[b] < t1; ++b) {
     const int ta = max(t0, sblk[b]);
@@ -113,13 +121,16 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(
         sincos(delta * invf[e], &sn, &cs);
         tab[a * TROW + tab_col<VEC>(e)] = make_float2((float)cs, (float)sn);
       }
+      if constexpr (PAGED)
+        for (int a = tid; a < na; a += kThreads) opage[a] = page_at(pout, a0 + a, pj);
       __syncthreads();
       // step = (layer, batch of rows)
       u32x4 xl[kItems], xh[kItems], nl[kItems], nh[kItems];
       auto load_step = [&](int step, u32x4* lo_, u32x4* hi_) {
         const int l = l0 + step / nbatch;
         const int rb = (step % nbatch) * RPP * kItems;
-        const E* src = kc + ((size_t)l * T + ta) * rowD;
+        const E* src = PAGED ? kc + (((size_t)l * pin.n_pages + ipage) * kBlock + (ta - t0)) * rowD
+                             : kc + ((size_t)l * T + ta) * rowD;
 #pragma unroll
         for (int k = 0; k < kItems; ++k) {
           const int r = rb + row_base + k * RPP;
@@ -142,7 +153,8 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(
             cs[j] = v.x;
             sn[j] = v.y;
           }
-          E* dst = out + ((size_t)(a0 + a) * L + l) * (size_t)T * rowD + (size_t)ta * rowD;
+          E* dst = PAGED ? out + (((size_t)l * pout.n_pages + opage[a]) * kBlock + (ta - t0)) * rowD
+                         : out + ((size_t)(a0 + a) * L + l) * (size_t)T * rowD + (size_t)ta * rowD;
 #pragma unroll
           for (int k = 0; k < kItems; ++k) {
             const int r = rb + row_base + k * RPP;
@@ -170,9 +182,9 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(
   }
 }
 
-template <typename E, int D>
-hipError_t launch_t(const Dims& d, const tdx_layout& lay, const void* kc, void* out,
-                    hipStream_t s) {
+template <typename E, int D, bool PAGED>
+hipError_t launch_t(const Dims& d, const tdx_layout& lay, const void* kc, void* out, const PageMap& pin,
+                    const PageMap& pout, hipStream_t s) {
   const int tiles = (d.T + kTileTok - 1) / kTileTok;
   // enough workgroups to fill 256 CUs several times over: layers split
   // first (>= 1 layer each), then agents
@@ -186,23 +198,35 @@ hipError_t launch_t(const Dims& d, const tdx_layout& lay, const void* kc, void* 
   asplit = (d.N + apg - 1) / apg;
   dim3 grid(tiles, groups, asplit);
   const size_t lds = (size_t)kAgentChunk * (D / 2 + 2 * (D / 2 / Fmt<E>::VEC)) * 8 + (D / 2) * 8 +
-                     (size_t)(d.B + 1) * 4;
-  hipLaunchKernelGGL((rerotate_kernel<E, D>), grid, dim3(kThreads), lds, s,
+                     (size_t)kAgentChunk * 8 + (size_t)(d.B + 1) * 4;
+  hipLaunchKernelGGL((rerotate_kernel<E, D, PAGED>), grid, dim3(kThreads), lds, s,
                      static_cast<const E*>(kc), static_cast<E*>(out), lay.blk_start,
-                     lay.src_pos, lay.dst_pos, d.N, d.B, d.T, d.L, d.Hkv, lpg, apg, d.theta);
+                     lay.src_pos, lay.dst_pos, d.N, d.B, d.T, d.L, d.Hkv, lpg, apg, d.theta, pin, pout);
   return hipGetLastError();
+}
+
+template <bool PAGED>
+hipError_t dispatch(const Dims& d, const tdx_layout& lay, const void* kc, void* out, const PageMap& pin,
+                    const PageMap& pout, hipStream_t s) {
+  if (d.dtype == TDX_BF16) {
+    return d.D == 128 ? launch_t<uint16_t, 128, PAGED>(d, lay, kc, out, pin, pout, s)
+                      : launch_t<uint16_t, 64, PAGED>(d, lay, kc, out, pin, pout, s);
+  }
+  return d.D == 128 ? launch_t<float, 128, PAGED>(d, lay, kc, out, pin, pout, s)
+                    : launch_t<float, 64, PAGED>(d, lay, kc, out, pin, pout, s);
 }
 
 }  // namespace
 
 hipError_t launch_rerotate(const Dims& d, const tdx_layout& lay, const void* kc, void* out,
                            hipStream_t s) {
-  if (d.dtype == TDX_BF16) {
-    return d.D == 128 ? launch_t<uint16_t, 128>(d, lay, kc, out, s)
-                      : launch_t<uint16_t, 64>(d, lay, kc, out, s);
-  }
-  return d.D == 128 ? launch_t<float, 128>(d, lay, kc, out, s)
-                    : launch_t<float, 64>(d, lay, kc, out, s);
+  const PageMap none{nullptr, 0, 1};
+  return dispatch<false>(d, lay, kc, out, none, none, s);
+}
+
+hipError_t launch_rerotate_paged(const Dims& d, const tdx_layout& lay, const void* kc, const PageMap& cin,
+                                 void* out, const PageMap& cout, hipStream_t s) {
+  return dispatch<true>(d, lay, kc, out, cin, cout, s);
 }
 
 }  // namespace tdx

@@ -56,11 +56,14 @@ __device__ __forceinline__ float group_sum(float v) {
 // AU in flight together), square-sum each lane's elements in fp32,
 // sum each head's lanes with DPP, take the head norms and add the heads.
 // KCH = 16-byte chunks per lane per row (row = Hkv * D elements).
-template <typename E, int D, int KCH, int AU>
+//
+// PAGED: the reused K lives in 16-token pages of a pool; agent i's token t is
+// row t % 16 of page pm[i][t / 16] at layer pl (kr is the pool).
+template <typename E, int D, int KCH, int AU, bool PAGED>
 __global__ __launch_bounds__(kDevThreads) void deviation_kernel(
     const E* __restrict__ kr, const E* __restrict__ kx, int N, int T, int Hkv,
     size_t kr_agent_stride, float* __restrict__ dev, float* __restrict__ score,
-    double* __restrict__ part) {
+    double* __restrict__ part, PageMap pm, long long pl) {
   constexpr int VEC = Fmt<E>::VEC;
   constexpr int G = D / VEC;  // lanes per head
   static_assert(G == 8 || G == 16 || G == 32, "lanes per head");
@@ -85,7 +88,9 @@ __global__ __launch_bounds__(kDevThreads) void deviation_kernel(
 #pragma unroll
       for (int k = 0; k < KCH; ++k) {
         const int c = min(lane + k * kWave, cpr - 1);
-        a[u][k] = ld16_nt(kr + (size_t)i * kr_agent_stride + (size_t)tc * rowE + c * VEC);
+        const size_t ra = PAGED ? ((size_t)(pl * pm.n_pages + page_at(pm, i, tc / kBlock)) * kBlock + tc % kBlock) * rowE
+                                : (size_t)i * kr_agent_stride + (size_t)tc * rowE;
+        a[u][k] = ld16_nt(kr + ra + c * VEC);
         b[u][k] = ld16_nt(kx + ((size_t)i * T + tc) * rowE + c * VEC);
       }
     }
@@ -271,12 +276,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   }
 }
 
-template <typename E, int D, int KCH>
-hipError_t launch_dev(const Dims& d, int check_layer, const void* kr, const void* kx,
+template <typename E, int D, int KCH, bool PAGED>
+hipError_t launch_dev(const Dims& d, int check_layer, const void* kr, const PageMap& pm, const void* kx,
                       float* dev, float* score, double* part, int nparts, hipStream_t s) {
   const size_t rowE = (size_t)d.Hkv * d.D;
   const size_t stride = (size_t)d.L * d.T * rowE;
-  const E* krl = static_cast<const E*>(kr) + (size_t)check_layer * d.T * rowE;
+  const E* krl = PAGED ? static_cast<const E*>(kr) : static_cast<const E*>(kr) + (size_t)check_layer * d.T * rowE;
   // agents in flight per wave: the group size that wastes the fewest re-reads
   // of the last agent (ties to the larger group)
   int best = 8;
@@ -286,9 +291,9 @@ hipError_t launch_dev(const Dims& d, int check_layer, const void* kr, const void
     if (waste < bw) best = au;
   }
 #define TDX_DEV(AU)                                                                      \
-  hipLaunchKernelGGL((deviation_kernel<E, D, KCH, AU>), dim3(nparts), dim3(kDevThreads), \
+  hipLaunchKernelGGL((deviation_kernel<E, D, KCH, AU, PAGED>), dim3(nparts), dim3(kDevThreads), \
                      kDevWaves * d.N * sizeof(double), s, krl, static_cast<const E*>(kx), d.N, \
-                     d.T, d.Hkv, stride, dev, score, part)
+                     d.T, d.Hkv, stride, dev, score, part, pm, (long long)check_layer)
   if (best == 8) TDX_DEV(8);
   else if (best == 5) TDX_DEV(5);
   else TDX_DEV(4);
@@ -296,19 +301,20 @@ hipError_t launch_dev(const Dims& d, int check_layer, const void* kr, const void
   return hipGetLastError();
 }
 
-template <typename E, int D>
-hipError_t launch_dev_d(const Dims& d, int check_layer, const void* kr, const void* kx,
+template <typename E, int D, bool PAGED>
+hipError_t launch_dev_d(const Dims& d, int check_layer, const void* kr, const PageMap& pm, const void* kx,
                         float* dev, float* score, double* part, int nparts, hipStream_t s) {
   const int cpr = d.Hkv * D / Fmt<E>::VEC;
   const int kch = (cpr + kWave - 1) / kWave;
   switch (kch) {
-    case 1: return launch_dev<E, D, 1>(d, check_layer, kr, kx, dev, score, part, nparts, s);
-    case 2: return launch_dev<E, D, 2>(d, check_layer, kr, kx, dev, score, part, nparts, s);
+    case 1: return launch_dev<E, D, 1, PAGED>(d, check_layer, kr, pm, kx, dev, score, part, nparts, s);
+    case 2: return launch_dev<E, D, 2, PAGED>(d, check_layer, kr, pm, kx, dev, score, part, nparts, s);
     case 3:
-    case 4: return launch_dev<E, D, 4>(d, check_layer, kr, kx, dev, score, part, nparts, s);
+    case 4: return launch_dev<E, D, 4, PAGED>(d, check_layer, kr, pm, kx, dev, score, part, nparts, s);
     default: return hipErrorInvalidValue;
   }
 }
+
 
 }  // namespace
 
@@ -318,26 +324,45 @@ size_t select_ws_bytes(const Dims& d) {
   return (size_t)dev_parts(d) * d.N * sizeof(double);
 }
 
-hipError_t launch_select(const Dims& d, const tdx_layout& lay, int check_layer,
-                         const void* k_reuse, const void* k_recomp, int k, float* dev,
-                         float* score, float* agent_dev, int32_t* selected, int32_t* master,
-                         void* ws, hipStream_t s) {
-  (void)lay;
+namespace {
+template <bool PAGED>
+hipError_t select_t(const Dims& d, int check_layer, const void* k_reuse, const PageMap& pm, const void* k_recomp,
+                    int k, float* dev, float* score, float* agent_dev, int32_t* selected, int32_t* master,
+                    void* ws, hipStream_t s) {
   if (d.N > kMaxAgents) return hipErrorInvalidValue;
   const int nparts = dev_parts(d);
   double* part = static_cast<double*>(ws);
   hipError_t e;
   if (d.dtype == TDX_BF16)
-    e = d.D == 128 ? launch_dev_d<uint16_t, 128>(d, check_layer, k_reuse, k_recomp, dev, score, part, nparts, s)
-                   : launch_dev_d<uint16_t, 64>(d, check_layer, k_reuse, k_recomp, dev, score, part, nparts, s);
+    e = d.D == 128
+            ? launch_dev_d<uint16_t, 128, PAGED>(d, check_layer, k_reuse, pm, k_recomp, dev, score, part, nparts, s)
+            : launch_dev_d<uint16_t, 64, PAGED>(d, check_layer, k_reuse, pm, k_recomp, dev, score, part, nparts, s);
   else
-    e = d.D == 128 ? launch_dev_d<float, 128>(d, check_layer, k_reuse, k_recomp, dev, score, part, nparts, s)
-                   : launch_dev_d<float, 64>(d, check_layer, k_reuse, k_recomp, dev, score, part, nparts, s);
+    e = d.D == 128
+            ? launch_dev_d<float, 128, PAGED>(d, check_layer, k_reuse, pm, k_recomp, dev, score, part, nparts, s)
+            : launch_dev_d<float, 64, PAGED>(d, check_layer, k_reuse, pm, k_recomp, dev, score, part, nparts, s);
   if (e != hipSuccess) return e;
   const size_t lds = d.T <= kSelLdsKeys ? (size_t)d.T * sizeof(uint32_t) : 0;
   hipLaunchKernelGGL(select_kernel, dim3(1), dim3(kSelThreads), lds, s, score, part, nparts, d.N,
                      d.T, k, agent_dev, selected, master);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_select(const Dims& d, const tdx_layout& lay, int check_layer,
+                         const void* k_reuse, const void* k_recomp, int k, float* dev,
+                         float* score, float* agent_dev, int32_t* selected, int32_t* master,
+                         void* ws, hipStream_t s) {
+  (void)lay;
+  const PageMap none{nullptr, 0, 1};
+  return select_t<false>(d, check_layer, k_reuse, none, k_recomp, k, dev, score, agent_dev, selected, master, ws,
+                         s);
+}
+
+hipError_t launch_select_paged(const Dims& d, int check_layer, const void* kr_pool, const PageMap& pm,
+                               const void* k_recomp, int k, float* dev, float* score, float* agent_dev,
+                               int32_t* selected, int32_t* master, void* ws, hipStream_t s) {
+  return select_t<true>(d, check_layer, kr_pool, pm, k_recomp, k, dev, score, agent_dev, selected, master, ws, s);
 }
 
 }  // namespace tdx

@@ -48,6 +48,11 @@ class CLayout(ctypes.Structure):
                 ("src_pos", ctypes.c_void_p), ("dst_pos", ctypes.c_void_p)]
 
 
+class CPagedKV(ctypes.Structure):
+    _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p), ("n_pages", ctypes.c_int64),
+                ("pages", ctypes.c_void_p), ("stride", ctypes.c_int64)]
+
+
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
@@ -75,6 +80,13 @@ _SIGS = {
     "tdx_restore_transfer_workspace": (_SZ, [_PS, _PL, _I32, _I32, _I32]),
     "tdx_restore_transfer": (ctypes.c_int, [_PS, _PL, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P,
                                             _P, _SZ, _P]),
+    "tdx_rerotate_paged": (ctypes.c_int, [_PS, _PL, ctypes.POINTER(CPagedKV), ctypes.POINTER(CPagedKV), _P]),
+    "tdx_select_important_paged": (ctypes.c_int, [_PS, _PL, _I32, ctypes.POINTER(CPagedKV), _P, _I32, _P, _P, _P,
+                                                  _P, _P, _P, _SZ, _P]),
+    "tdx_diff_encode_paged": (ctypes.c_int, [_PS, _PL, _P, ctypes.POINTER(CPagedKV), _I64, _P, _P, _P, _P, _P, _P,
+                                             _P, _SZ, _P]),
+    "tdx_restore_attn_paged": (ctypes.c_int, [_PS, _PL, _P, _P, ctypes.POINTER(CPagedKV), _I32,
+                                              ctypes.POINTER(CPagedKV), _P, _P, _P, _P, _F, _P, _P, _SZ, _P]),
     "tdx_round_plan_build": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P, ctypes.POINTER(_P)]),
     "tdx_round_plan_n_groups": (ctypes.c_int, [_P]),
     "tdx_round_plan_group_dims": (ctypes.c_int, [_P, _I32, _P, _P, _P]),
@@ -446,6 +458,156 @@ def decode_attn_dense(shape: Shape, lay: RoundLayout, q: torch.Tensor, priv_off:
         ctypes.byref(s), ctypes.byref(l), _ptr(q), _ptr(priv_off), _ptr(priv_k), _ptr(priv_v),
         int(max_priv), _ptr(k_dense), _ptr(v_dense), scale, _ptr(out), _ptr(ws), ws.numel(),
         _stream()), "tdx_decode_attn_dense")
+    return out
+
+
+# ---- paged KV layout -------------------------------------------------------------
+
+class PagedKV:
+    """A paged view of K (and V) rows: pools [L][n_pages][16][Hkv][D] and a
+    device int32 page table [rows][stride] (row r = one sequence's pages in
+    token order)."""
+
+    def __init__(self, k_pool: torch.Tensor, v_pool: Optional[torch.Tensor], pages: torch.Tensor):
+        if k_pool.dim() != 5 or k_pool.shape[2] != DIFF_BLOCK:
+            raise ValueError("a pool is [L][n_pages][16][Hkv][D]")
+        _need(k_pool, "k_pool")
+        if v_pool is not None:
+            _need(v_pool, "v_pool", k_pool.dtype, tuple(k_pool.shape), k_pool.device)
+        if pages.dim() != 2:
+            raise ValueError("pages is [rows][stride]")
+        _need(pages, "pages", torch.int32, None, k_pool.device)
+        self.k_pool, self.v_pool, self.pages = k_pool, v_pool, pages
+        self._c = CPagedKV(k_pool.data_ptr(), None if v_pool is None else v_pool.data_ptr(), int(k_pool.shape[1]),
+                           pages.data_ptr(), int(pages.shape[1]))
+
+    def check(self, shape: Shape, rows: int, per_row: int, device):
+        L, H, D = shape.n_layers, shape.n_kv_heads, shape.head_dim
+        if self.k_pool.dtype != shape.dtype or self.k_pool.shape[0] != L or tuple(self.k_pool.shape[3:]) != (H, D):
+            raise ValueError(f"pool must be [{L}][n_pages][16][{H}][{D}] of {shape.dtype}")
+        if self.pages.shape[0] < rows or self.pages.shape[1] < per_row:
+            raise ValueError(f"page table must cover {rows} rows of {per_row} pages")
+        if _norm(self.k_pool.device) != _norm(device):
+            raise ValueError("pool on the wrong device")
+
+    def c(self):
+        return ctypes.byref(self._c)
+
+
+def _pages(n: int) -> int:
+    return (int(n) + DIFF_BLOCK - 1) // DIFF_BLOCK
+
+
+def rerotate_paged(shape: Shape, lay: RoundLayout, cached: PagedKV, out: PagedKV) -> None:
+    """a1 over pages: agent i's re-rotated K into the pages of ``out`` row i."""
+    cached.check(shape, 1, _pages(lay.n_tokens), lay.device)
+    out.check(shape, lay.n_agents, _pages(lay.n_tokens), lay.device)
+    s, l = shape.c(), lay.c()
+    _check(lib().tdx_rerotate_paged(ctypes.byref(s), ctypes.byref(l), cached.c(), out.c(), _stream()),
+           "tdx_rerotate_paged")
+
+
+def select_important_paged(shape: Shape, lay: RoundLayout, k_reuse: PagedKV, k_recomp: torch.Tensor, k: int,
+                           check_layer: int = 0, out: Optional[dict] = None, ws=None) -> dict:
+    """a2 + a3 with agent i's re-rotated K in the pages of ``k_reuse`` row i."""
+    N, T, H, D = lay.n_agents, lay.n_tokens, shape.n_kv_heads, shape.head_dim
+    dev_ = lay.device
+    k_reuse.check(shape, N, _pages(T), dev_)
+    _need(k_recomp, "k_recomp", shape.dtype, (N, T, H, D), dev_)
+    if out is None:
+        out = dict(dev=torch.empty((N, T), dtype=torch.float32, device=dev_),
+                   score=torch.empty((T,), dtype=torch.float32, device=dev_),
+                   agent_dev=torch.empty((N,), dtype=torch.float32, device=dev_),
+                   selected=torch.empty((max(int(k), 1),), dtype=torch.int32, device=dev_),
+                   master=torch.empty((1,), dtype=torch.int32, device=dev_))
+    if ws is None:
+        ws = _ws(select_workspace(shape, lay), dev_)
+    s, l = shape.c(), lay.c()
+    _check(lib().tdx_select_important_paged(
+        ctypes.byref(s), ctypes.byref(l), int(check_layer), k_reuse.c(), _ptr(k_recomp), int(k), _ptr(out["dev"]),
+        _ptr(out["score"]), _ptr(out["agent_dev"]), _ptr(out["selected"]), _ptr(out["master"]), _ptr(ws),
+        ws.numel(), _stream()), "tdx_select_important_paged")
+    return out
+
+
+class PagedDiff:
+    """A paged diff record: CSR offsets and block indices, the Mirror's page
+    of every entry, and optional value copies."""
+
+    def __init__(self, off, idx, page, k, v, nnz, cap):
+        self.off, self.idx, self.page, self.k, self.v = off, idx, page, k, v
+        self.nnz_dev = nnz
+        self.cap = cap
+
+    def nnz(self) -> int:
+        return int(self.nnz_dev.item())
+
+
+def diff_encode_paged(shape: Shape, lay: RoundLayout, master: torch.Tensor, agents: PagedKV,
+                      cap_blocks: Optional[int] = None, copy_values: bool = False, check: bool = True,
+                      out: Optional[PagedDiff] = None, ws=None) -> PagedDiff:
+    """a4 over pages: each entry names the Mirror's own page of the block."""
+    N, L, T, H, D = lay.n_agents, shape.n_layers, lay.n_tokens, shape.n_kv_heads, shape.head_dim
+    dev_ = lay.device
+    _need(master, "master", torch.int32, (1,), dev_)
+    agents.check(shape, N, T // DIFF_BLOCK, dev_)
+    if agents.v_pool is None:
+        raise ValueError("agents needs a V pool")
+    if out is None:
+        cap = (N - 1) * L * (T // DIFF_BLOCK) if cap_blocks is None else int(cap_blocks)
+        c1 = max(cap, 1)
+        out = PagedDiff(torch.empty((N * L + 1,), dtype=torch.int32, device=dev_),
+                        torch.empty((c1,), dtype=torch.int32, device=dev_),
+                        torch.empty((c1,), dtype=torch.int32, device=dev_),
+                        torch.empty((c1, DIFF_BLOCK, H, D), dtype=shape.dtype, device=dev_) if copy_values else None,
+                        torch.empty((c1, DIFF_BLOCK, H, D), dtype=shape.dtype, device=dev_) if copy_values else None,
+                        torch.empty((1,), dtype=torch.int64, device=dev_), cap)
+    if ws is None:
+        ws = _ws(encode_workspace(shape, lay), dev_)
+    s, l = shape.c(), lay.c()
+    _check(lib().tdx_diff_encode_paged(
+        ctypes.byref(s), ctypes.byref(l), _ptr(master), agents.c(), int(out.cap), _ptr(out.off), _ptr(out.idx),
+        _ptr(out.page), _ptr(out.k), _ptr(out.v), _ptr(out.nnz_dev), _ptr(ws), ws.numel(), _stream()),
+        "tdx_diff_encode_paged")
+    if check:
+        n = out.nnz()
+        if n < 0:
+            raise TdxError(TDX_EINVAL, "tdx_diff_encode_paged", "the Master index is outside [0, N)")
+        if n > out.cap:
+            raise TdxError(TDX_EINVAL, "tdx_diff_encode_paged", f"{n} diff blocks exceed capacity {out.cap}")
+    return out
+
+
+def restore_attn_paged(shape: Shape, lay: RoundLayout, q: torch.Tensor, priv_off: torch.Tensor,
+                       priv: Optional[PagedKV], max_priv: int, agents: PagedKV, master_sel: Optional[torch.Tensor],
+                       diff: PagedDiff, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                       ws=None) -> torch.Tensor:
+    """a5 over pages: private history from ``priv`` row i, the Master as row
+    ``master_sel[0]`` of ``agents``, diff values from the pages ``diff.page``."""
+    N, L, T, Hq, D = lay.n_agents, shape.n_layers, lay.n_tokens, shape.n_q_heads, shape.head_dim
+    dev_ = lay.device
+    _need(q, "q", shape.dtype, (N, L, Hq, D), dev_)
+    _need(priv_off, "priv_off", torch.int32, (N + 1,), dev_)
+    if max_priv > 0:
+        if priv is None or priv.v_pool is None:
+            raise ValueError("priv needs K and V pools")
+        priv.check(shape, N, _pages(max_priv), dev_)
+    agents.check(shape, N, T // DIFF_BLOCK, dev_)
+    if agents.v_pool is None:
+        raise ValueError("agents needs a V pool")
+    if master_sel is not None:
+        _need(master_sel, "master_sel", torch.int32, (1,), dev_)
+    if out is None:
+        out = torch.empty((N, L, Hq, D), dtype=shape.dtype, device=dev_)
+    _need(out, "out", shape.dtype, (N, L, Hq, D), dev_)
+    if ws is None:
+        ws = _ws(restore_attn_workspace(shape, lay, max_priv), dev_)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    s, l = shape.c(), lay.c()
+    _check(lib().tdx_restore_attn_paged(
+        ctypes.byref(s), ctypes.byref(l), _ptr(q), _ptr(priv_off), priv.c() if priv is not None else None,
+        int(max_priv), agents.c(), _ptr(master_sel), _ptr(diff.off), _ptr(diff.idx), _ptr(diff.page), scale,
+        _ptr(out), _ptr(ws), ws.numel(), _stream()), "tdx_restore_attn_paged")
     return out
 
 

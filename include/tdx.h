@@ -27,6 +27,8 @@
  *   tdx_restore_transfer  the transfer-path restore: Mirrors rebuilt layer by
  *                         layer from a Master and diff records kept in host
  *                         storage (notes §3d Algorithm 1; blog §4.4).
+ *   tdx_*_paged           the four collective calls over a paged KV pool
+ *                         (16-token pages + page tables; notes §3c, §3d).
  *   tdx_round_plan_*      host side: shared blocks, groups and their layouts
  *                         derived from the requests' token IDs (notes §4
  *                         Round-Aware Prompt Interface, §5 "Scheduling").
@@ -253,6 +255,65 @@ int tdx_decode_attn_dense(const tdx_shape *shape, const tdx_layout *layout,
                           void *ws, size_t ws_bytes, void *stream);
 size_t tdx_decode_attn_dense_workspace(const tdx_shape *shape, const tdx_layout *layout,
                                        int32_t max_priv);
+
+/* ---- paged KV layout ---------------------------------------------------------
+ * The four collective calls over caches kept in a serving KV pool: 16-token
+ * pages plus page tables instead of contiguous canonical arrays (notes §3c A4
+ * and §3d: 16/32-token pages, diff indices aligned to page boundaries, the
+ * fused restore's dependence on the paged KV slot map; §5 "Scheduling":
+ * memory management inherits paged attention).  Every sequence keeps its
+ * tokens in the order the contiguous calls use (a canonical shared region is
+ * ceil(T/16) pages, page j holding canonical tokens 16j .. 16j+15), so a
+ * 16-token diff block is exactly one page.
+ *
+ * A pool holds n_layers x n_pages pages: page p of layer l is the 16 x Hkv x D
+ * elements at pool + (l * n_pages + p) * 16 * Hkv * D (shape->dtype), the same
+ * page ID in every layer.  Row r of a page table lists one sequence's pages
+ * at pages + r * stride.  Page IDs are read on the device; IDs outside
+ * [0, n_pages) are clamped, so a bad table can read or write a wrong page of
+ * the pool but never memory outside it.  Output pages of different sequences
+ * must be distinct; input and output pools may be the same allocation. */
+typedef struct {
+  void *k_pool;          /* K pool, 16-byte aligned */
+  void *v_pool;          /* V pool, same layout; NULL where the call reads only K */
+  int64_t n_pages;       /* pages per layer in each pool, >= 1 */
+  const int32_t *pages;  /* device page table, 4-byte aligned */
+  int64_t stride;        /* entries between consecutive rows (>= a row's pages when rows > 1) */
+} tdx_paged_kv;
+
+/* a1 paged: out row i's pages receive agent i's re-rotated K, as
+ * tdx_rerotate writes k_out[i]; cached row 0 lists the cached K's pages.  A
+ * partial last page (T % 16 != 0) is written only up to T. */
+int tdx_rerotate_paged(const tdx_shape *shape, const tdx_layout *layout, const tdx_paged_kv *cached,
+                       const tdx_paged_kv *out, void *stream);
+/* a2 + a3 paged: agent i's re-rotated K at check_layer is row i of k_reuse;
+ * everything else as tdx_select_important (same workspace size). */
+int tdx_select_important_paged(const tdx_shape *shape, const tdx_layout *layout, int32_t check_layer,
+                               const tdx_paged_kv *k_reuse, const void *k_recomp, int32_t k, float *dev,
+                               float *score, float *agent_dev, int32_t *selected, int32_t *master, void *ws,
+                               size_t ws_bytes, void *stream);
+/* a4 paged: agent i's canonical K/V (T/16 pages, K and V pools under one
+ * table) is row i of agents.  The record is diff_off and diff_idx as in
+ * tdx_diff_encode plus diff_page[e], the Mirror's own page holding entry e's
+ * block: the values stay in the pool (the Mirror's other pages can be
+ * released).  When diff_k/diff_v are set, the values are also copied there as
+ * in tdx_diff_encode.  Same workspace size as tdx_diff_encode. */
+int tdx_diff_encode_paged(const tdx_shape *shape, const tdx_layout *layout, const int32_t *master,
+                          const tdx_paged_kv *agents, int64_t cap_blocks, int32_t *diff_off, int32_t *diff_idx,
+                          int32_t *diff_page, void *diff_k, void *diff_v, int64_t *nnz, void *ws, size_t ws_bytes,
+                          void *stream);
+/* a5 paged: as tdx_restore_attn with agent i's private history in row i of
+ * priv (ceil(max_priv/16) entries per row, lengths from priv_off, history
+ * past max_priv never read; unused when max_priv = 0),
+ * the Master as row *master_sel of agents (row 0 when master_sel is NULL; the
+ * selector is clamped to [0, N)) and diff entry e's values in page
+ * diff_page[e] of the agents' pools.  Same workspace size as
+ * tdx_restore_attn. */
+int tdx_restore_attn_paged(const tdx_shape *shape, const tdx_layout *layout, const void *q,
+                           const int32_t *priv_off, const tdx_paged_kv *priv, int32_t max_priv,
+                           const tdx_paged_kv *agents, const int32_t *master_sel, const int32_t *diff_off,
+                           const int32_t *diff_idx, const int32_t *diff_page, float scale, void *out, void *ws,
+                           size_t ws_bytes, void *stream);
 
 /* ---- round structure from token IDs (host only) -----------------------------
  * The step before the collective calls: find the blocks that the requests of

@@ -8,3 +8,4 @@ must fail loudly when its compiled library is missing.
 
 from .tdx_oracle import *  # noqa: F401,F403
 from .round_oracle import round_plan, segments  # noqa: F401
+from . import paged_oracle as paged  # noqa: F401
