@@ -39,6 +39,8 @@ def parse():
                     help="skip the transfer-path restore measurement (Master and diffs in pinned host memory)")
     ap.add_argument("--no-serial", action="store_true",
                     help="skip the serial per-agent comparator (one-agent re-rotation and selection per agent)")
+    ap.add_argument("--no-paged", action="store_true",
+                    help="skip the paged-layout measurement (the four calls over 16-token pages)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -107,6 +109,8 @@ def _short_kernel(name: str) -> str:
 
 
 def _entry_of(kernel: str):
+    if kernel.rstrip().endswith("true>"):
+        return None  # a paged-layout variant: not part of the timed step
     for entry, pats in ENTRY_KERNELS.items():
         if any(kernel.startswith(p) for p in pats):
             return entry
@@ -394,6 +398,108 @@ def transfer_path(cfg, lay, shape, dl, ds, nnz, master_k, master_v, q, pk, pv, r
     }
 
 
+def _to_pool(seqs, gen):
+    """Per-sequence [L][n][Hkv][D] device tensors -> (pool [L][P][16][Hkv][D],
+    page table [rows][stride]) with the pages in a seeded random order."""
+    import torch
+
+    L, _, H, D = seqs[0].shape
+    dev = seqs[0].device
+    npg = [(s.shape[1] + 15) // 16 for s in seqs]
+    n_pages = max(sum(npg), 1)
+    perm = torch.randperm(n_pages, generator=gen).to(dev)
+    pool = torch.zeros((L, n_pages, 16, H, D), dtype=seqs[0].dtype, device=dev)
+    stride = max(max(npg), 1)
+    pages = torch.zeros((len(seqs), stride), dtype=torch.int32, device=dev)
+    k = 0
+    for r, s in enumerate(seqs):
+        n, ids = s.shape[1], perm[k:k + npg[r]]
+        k += npg[r]
+        pages[r, :npg[r]] = ids.to(torch.int32)
+        full = n // 16
+        if full:
+            pool[:, ids[:full]] = s[:, :full * 16].reshape(L, full, 16, H, D)
+        if n > full * 16:
+            pool[:, ids[-1], :n - full * 16] = s[:, full * 16:]
+    return pool, pages
+
+
+def paged_path(cfg, lay, shape, shape1, dl, kc, kr, kx, k, msel, ak, av, q, po, pk, pv, max_priv, out_ref,
+               steps, warmup, stage_ms, nnz):
+    """The four calls over 16-token pages (shuffled page order), timed like the
+    step's stages, with the same algorithmic bytes (the paged record holds a
+    page ID per entry instead of a value copy)."""
+    import torch
+
+    from collective_kv_cache_amd import tdx
+
+    N, L, T, H, D, Hq = cfg.n_agents, cfg.n_layers, lay.n_tokens, cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads
+    gen = torch.Generator(device="cpu").manual_seed(0)
+    cpool, cpages = _to_pool([kc], gen)
+    rpool, rpages = _to_pool([kr[i] for i in range(N)], gen)
+    kpool, apages = _to_pool([ak[i] for i in range(N)], gen)
+    vpool = torch.empty_like(kpool)
+    nbp = T // 16
+    for i in range(N):  # the V pool under the same table
+        vpool[:, apages[i].long()] = av[i].reshape(L, nbp, 16, H, D)
+    pof = lay.priv_off
+    ppk, ppages = _to_pool([pk[:, pof[i]:pof[i + 1]] for i in range(N)], gen)
+    ppv = torch.empty_like(ppk)
+    for i in range(N):
+        n = int(pof[i + 1] - pof[i])
+        full = n // 16
+        ids = ppages[i, :(n + 15) // 16].long()
+        if full:
+            ppv[:, ids[:full]] = pv[:, pof[i]:pof[i] + full * 16].reshape(L, full, 16, H, D)
+        if n > full * 16:
+            ppv[:, ids[-1], :n - full * 16] = pv[:, pof[i] + full * 16:pof[i + 1]]
+    cached = tdx.PagedKV(cpool, None, cpages)
+    rview = tdx.PagedKV(rpool, None, rpages)
+    agents = tdx.PagedKV(kpool, vpool, apages)
+    priv = tdx.PagedKV(ppk, ppv, ppages)
+    sel = tdx.select_important_paged(shape1, dl, rview, kx, k, cfg.check_layer)
+    cap = int(math.ceil(0.35 * (N - 1) * L * nbp))
+    pd = tdx.diff_encode_paged(shape, dl, msel, agents, cap_blocks=cap)
+    out = tdx.restore_attn_paged(shape, dl, q, po, priv, max_priv, agents, msel, pd)
+    ws_s = torch.empty(max(tdx.select_workspace(shape1, dl), 16), dtype=torch.uint8, device=kc.device)
+    ws_e = torch.empty(max(tdx.encode_workspace(shape, dl), 16), dtype=torch.uint8, device=kc.device)
+    ws_a = torch.empty(max(tdx.restore_attn_workspace(shape, dl, max_priv), 16), dtype=torch.uint8,
+                       device=kc.device)
+    calls = {
+        "rerotate": lambda: tdx.rerotate_paged(shape, dl, cached, rview),
+        "select": lambda: tdx.select_important_paged(shape1, dl, rview, kx, k, cfg.check_layer, out=sel, ws=ws_s),
+        "encode": lambda: tdx.diff_encode_paged(shape, dl, msel, agents, out=pd, check=False, ws=ws_e),
+        "restore_attn": lambda: tdx.restore_attn_paged(shape, dl, q, po, priv, max_priv, agents, msel, pd, out=out,
+                                                       ws=ws_a),
+    }
+    byts = stage_bytes(cfg, lay, nnz, k)
+    kv = 2 * H * D * cfg.elem_bytes
+    byts["encode"] = N * L * T * kv + nnz * 8 + 4 * (N * L + 1)  # index + page ID per entry
+    res = {}
+    for name, fn in calls.items():
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        gbs = byts[name] / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 4), "alg_GB": round(byts[name] / 1e9, 4), "GBps": round(gbs, 1),
+                     "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                     "paged_over_contiguous": round(ms / stage_ms[name], 3)}
+    bits = (lambda t: t.view(torch.int16)) if out.dtype == torch.bfloat16 else (lambda t: t.view(torch.int32))
+    res["nnz_equal"] = pd.nnz() == nnz
+    res["restore_bit_identical"] = bool(torch.equal(bits(out), bits(out_ref)))
+    res["layout"] = "16-token pages in a seeded random order; the diff record names pages (no value copies)"
+    del cpool, rpool, kpool, vpool, ppk, ppv
+    torch.cuda.empty_cache()
+    return res
+
+
 def serial_path(shape, lay, kc, kx, k, check_layer, kr, steps, warmup, collective_ms):
     """N one-agent launches of re-rotation and selection (the per-request
     path) against the collective round's one launch of each."""
@@ -554,6 +660,11 @@ def main():
         serial = serial_path(shape1, lay, kc, kx, k, cfg.check_layer, kr, args.steps,
                              max(1, args.warmup), stage_ms["rerotate"] + stage_ms["select"])
 
+    paged = None
+    if not args.no_paged:
+        paged = paged_path(cfg, lay, shape, shape1, dl, kc, kr, kx, k, sel["master"], ak, av, q, po, pk, pv,
+                           max_priv, out, args.steps, max(1, args.warmup), stage_ms, nnz)
+
     transfer = None
     if not args.no_transfer:
         transfer = transfer_path(cfg, lay, shape, dl, ds, nnz, ak[master], av[master], q, pk, pv)
@@ -599,6 +710,7 @@ def main():
         "stages": stage_rep,
         "dense_comparator": dense,
         "serial_per_agent": serial,
+        "paged_layout": paged,
         "transfer_restore": transfer,
         "compression": compression(counts, master, T, H, D, cfg.elem_bytes, lay.priv_len, L),
         "cpu_baseline": None,
