@@ -39,11 +39,14 @@ def parse():
                     help="skip the transfer-path restore measurement (Master and diffs in pinned host memory)")
     ap.add_argument("--no-serial", action="store_true",
                     help="skip the serial per-agent comparator (one-agent re-rotation and selection per agent)")
+    ap.add_argument("--sq-summary", nargs=2, metavar=("SQ_CSV", "KERNEL_STATS_CSV"),
+                    help="summarise a rocprofv3 --pmc run of SQ counters (MFMA/VALU/LDS use per kernel) "
+                         "with a kernel-trace run's durations; runs no GPU work")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the paged-layout measurement (the four calls over 16-token pages)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
-    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+    ap.add_argument("--pmc-summary", nargs="+", metavar="CSV",
                     help="summarise two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, "
                          "both with --calib-copy) into HBM bytes per entry point and record them in "
                          "profiles/traffic.json; runs no GPU work")
@@ -117,7 +120,7 @@ def _entry_of(kernel: str):
     return None
 
 
-def pmc_summary(fetch_csv: str, write_csv: str, workload: str):
+def pmc_summary(fetch_csv: str, write_csv: str, workload: str, bench_log: str = None):
     """HBM bytes per dispatch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB),
     scaled by what the same counters read for the 1 GiB calibration copy."""
     import csv
@@ -164,6 +167,47 @@ def pmc_summary(fetch_csv: str, write_csv: str, workload: str):
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1)
     print("recorded in", os.path.relpath(TRAFFIC_FILE, ROOT))
+    if bench_log:
+        line = None
+        for ln in open(bench_log):
+            if ln.startswith("{"):
+                line = json.loads(ln)
+        if line:
+            stage_of = {v: k for k, v in ENTRY.items()}
+            print("\nentry point (per call): counted HBM bytes vs the algorithmic bytes bench.py uses:")
+            for e, r in rec.items():
+                cnt = (r["fetch_bytes"] + r["write_bytes"]) / 1e9
+                alg = line["stages"][stage_of[e]]["alg_GB"]
+                print(f"  {e:24s} counted {cnt:7.3f} GB   algorithmic {alg:7.3f} GB   ratio {cnt / alg:.3f}")
+
+
+def sq_summary(sq_csv: str, stats_csv: str):
+    """MFMA / VALU / LDS use per kernel from a rocprofv3 --pmc run of SQ
+    counters, with each kernel's average duration from a kernel-trace run:
+    MFMA% = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x kernel cycles at 2.4 GHz),
+    MFMA GFLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512."""
+    import csv
+    from collections import defaultdict
+
+    acc, disp = defaultdict(lambda: defaultdict(float)), defaultdict(set)
+    for r in csv.DictReader(open(sq_csv)):
+        k = _short_kernel(r["Kernel_Name"])
+        acc[k][r["Counter_Name"]] += float(r["Counter_Value"])
+        disp[k].add(r["Dispatch_Id"])
+    us = {_short_kernel(r["Name"]): float(r["AverageNs"]) / 1e3 for r in csv.DictReader(open(stats_csv))}
+    print(f"{'kernel':46s} {'us':>8s} {'MFMA%':>7s} {'MFMA_GF':>8s} {'TFLOP/s':>8s} {'VALU_inst':>10s} "
+          f"{'MFMA_inst':>10s} {'LDS_inst':>9s}")
+    for k in sorted(acc, key=lambda k: -us.get(k, 0.0)):
+        if _entry_of(k) is None or k not in us:
+            continue
+        n = len(disp[k])
+        c = {name: v / n for name, v in acc[k].items()}
+        t = us[k]
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (1024 * t * 2400.0)
+        gf = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512 / 1e9
+        print(f"{k[:46]:46s} {t:8.1f} {100 * busy:6.1f}% {gf:8.1f} {gf / t * 1e3:8.1f} "
+              f"{c.get('SQ_INSTS_VALU', 0.0):10.3g} {c.get('SQ_INSTS_MFMA', 0.0):10.3g} "
+              f"{c.get('SQ_INSTS_LDS', 0.0):9.3g}")
 
 
 def trace_summary(stats_csv: str, bench_log: str):
@@ -531,10 +575,15 @@ def serial_path(shape, lay, kc, kx, k, check_layer, kr, steps, warmup, collectiv
 def main():
     args = parse()
     if args.pmc_summary:
-        pmc_summary(*args.pmc_summary, args.config)
+        if len(args.pmc_summary) not in (2, 3):
+            raise SystemExit("--pmc-summary FETCH_CSV WRITE_CSV [BENCH_LOG]")
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.config, *args.pmc_summary[2:])
         return
     if args.trace_summary:
         trace_summary(*args.trace_summary)
+        return
+    if args.sq_summary:
+        sq_summary(*args.sq_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the collective reuse path here runs on a single "
