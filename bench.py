@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--sq-summary", nargs=2, metavar=("SQ_CSV", "KERNEL_STATS_CSV"),
                     help="summarise a rocprofv3 --pmc run of SQ counters (MFMA/VALU/LDS use per kernel) "
                          "with a kernel-trace run's durations; runs no GPU work")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay of the step")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the paged-layout measurement (the four calls over 16-token pages)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -544,6 +546,38 @@ def paged_path(cfg, lay, shape, shape1, dl, kc, kr, kx, k, msel, ak, av, q, po, 
     return res
 
 
+def graph_step(step, steps, warmup, eager_ms, out):
+    """One step captured in a HIP graph (outputs and workspaces preallocated,
+    no allocation or memset inside the calls) and replayed."""
+    import torch
+
+    ref = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(warmup):
+        g.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    bits = (lambda t: t.view(torch.int16)) if out.dtype == torch.bfloat16 else (lambda t: t.view(torch.int32))
+    same = bool(torch.equal(bits(out), bits(ref)))
+    del g
+    return {"ms_per_step": round(ms, 4), "eager_ms_per_step": round(eager_ms, 4),
+            "graph_over_eager": round(ms / eager_ms, 4), "restore_bit_identical": same}
+
+
 def serial_path(shape, lay, kc, kx, k, check_layer, kr, steps, warmup, collective_ms):
     """N one-agent launches of re-rotation and selection (the per-request
     path) against the collective round's one launch of each."""
@@ -703,6 +737,11 @@ def main():
                  "max_abs_fused_minus_dense": diff}
         del kd, vd
 
+    # ---- the same step captured once in a HIP graph and replayed
+    graph = None
+    if not args.no_graph:
+        graph = graph_step(step, args.steps, max(1, args.warmup), ms_step, out)
+
     # ---- serial per-agent reuse (the per-request fallback) on the same inputs
     serial = None
     if not args.no_serial:
@@ -758,6 +797,7 @@ def main():
         "collective_reuse_agent_tokens_per_s": agent_tokens / (reuse_ms * 1e-3),
         "stages": stage_rep,
         "dense_comparator": dense,
+        "graph_replay": graph,
         "serial_per_agent": serial,
         "paged_layout": paged,
         "transfer_restore": transfer,
