@@ -38,7 +38,8 @@ def to_pool(seqs, extra, seed, dtype=None):
     npg = [math.ceil(s.shape[1] / PAGE) for s in seqs]
     n_pages = sum(npg) + extra
     perm = torch.randperm(n_pages, generator=g)
-    pool = torch.randn((L, n_pages, PAGE, H, D), generator=g).to(dtype).to(DEV)
+    gd = torch.Generator(device=DEV).manual_seed(seed)
+    pool = torch.randn((L, n_pages, PAGE, H, D), generator=gd, device=DEV).to(dtype)
     stride = max(max(npg), 1) + 2
     pages = torch.full((len(seqs), stride), UNUSED, dtype=torch.int32)
     k = 0
@@ -208,3 +209,63 @@ def test_restore_attn_paged_without_private_history():
     got = tdx.restore_attn_paged(r.shape, r.dl, d["q"], d["po"], None, 0, agents, m, pd)
     torch.cuda.synchronize()
     assert_close(host(got), r.oracle_full()[0], "paged restore, no private history")
+
+
+def test_full_size_14b_paged_matches_contiguous():
+    # the 14B round at full size in the benchmark's launch configuration: every
+    # paged call gives the contiguous call's bits; sampled restore outputs are
+    # checked one by one against the oracle
+    cfg = CONFIGS["qwen14b_round"]
+    lay = make_layout(cfg)
+    master = 4
+    r = Round(cfg, lay, master=master, device_gen=DEV)
+    d = r.dev
+    shape, dl = r.shape, r.dl
+    N, L, T = cfg.n_agents, cfg.n_layers, lay.n_tokens
+    m = torch.tensor([master], dtype=torch.int32, device=DEV)
+    # a1
+    kr = tdx.rerotate(shape, dl, d["kc"])
+    cpool, cpages = to_pool([d["kc"]], 3, 21)
+    zero = torch.zeros_like(kr[0])
+    opool, opages = to_pool([zero] * N, 3, 22)  # zero pages: the call must write every one
+    del zero
+    tdx.rerotate_paged(shape, dl, tdx.PagedKV(cpool, None, cpages), tdx.PagedKV(opool, None, opages))
+    for i in range(N):
+        assert torch.equal(bits(gather(opool, opages, i, T).contiguous()), bits(kr[i])), i
+    # a2 + a3 at the check layer
+    kx = recomputed_k(cfg, lay, kr[:, 0].contiguous())
+    k = O.topk_count(cfg.pct, T)
+    col = tdx.select_important(shape, dl, kr, kx, k)
+    got = tdx.select_important_paged(shape, dl, tdx.PagedKV(opool, None, opages), kx, k)
+    for key in ("dev", "score", "agent_dev", "selected", "master"):
+        assert torch.equal(got[key], col[key]), key
+    del cpool, opool, kr
+    torch.cuda.empty_cache()
+    # a4 + a5
+    ds = tdx.diff_encode(shape, dl, m, d["ak"], d["av"], master_copy=False)
+    out = tdx.restore_attn(shape, dl, d["q"], d["po"], d["pk"], d["pv"], r.max_priv, d["ak"], d["av"], ds,
+                           master_sel=m)
+    kpool, pages = to_pool([d["ak"][i] for i in range(N)], 4, 23)
+    vpool, _ = to_pool([d["av"][i] for i in range(N)], 4, 23)
+    po = lay.priv_off
+    pkpool, ppages = to_pool([d["pk"][:, po[i]:po[i + 1]] for i in range(N)], 2, 24)
+    pvpool, _ = to_pool([d["pv"][:, po[i]:po[i + 1]] for i in range(N)], 2, 24)
+    agents = tdx.PagedKV(kpool, vpool, pages)
+    pd = tdx.diff_encode_paged(shape, dl, m, agents)
+    n = pd.nnz()
+    assert n == ds.nnz() and torch.equal(pd.off, ds.off) and torch.equal(pd.idx[:n], ds.idx[:n])
+    pout = tdx.restore_attn_paged(shape, dl, d["q"], d["po"], tdx.PagedKV(pkpool, pvpool, ppages), r.max_priv,
+                                  agents, m, pd)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(pout), bits(out))
+    for i, l in ((0, 0), (master, 17), (N - 1, L - 1)):
+        p0, p1 = int(po[i]), int(po[i + 1])
+        mk, mv = to_numpy_bits(d["ak"][master, l]), to_numpy_bits(d["av"][master, l])
+        _, idx, dk, dv = O.diff_encode(np.stack([mk, to_numpy_bits(d["ak"][i, l])])[:, None],
+                                       np.stack([mv, to_numpy_bits(d["av"][i, l])])[:, None], 0)
+        ref = O.restore_attn_one(to_numpy_bits(d["q"][i, l]), to_numpy_bits(d["pk"][l, p0:p1]),
+                                 to_numpy_bits(d["pv"][l, p0:p1]), mk, mv, idx, dk, dv,
+                                 lay.blk_start, lay.src_pos, lay.dst_pos[i], cfg.theta, r.scale)
+        assert_close(to_numpy_bits(pout[i, l]), O.narrow(ref, np.uint16), f"paged full i={i} l={l}")
+    del kpool, vpool, pkpool, pvpool, r, ds, pd
+    torch.cuda.empty_cache()
