@@ -552,11 +552,13 @@ struct Stage {
 };
 
 // K tile of one wave in LDS, stored as loaded: [16 rows][CPR 16-byte chunks],
-// chunk ch of row t at position ch ^ t (t < 16 <= CPR), so that the row-wise
-// writes and the column reads of the MFMA operand spread over the banks.
+// chunk ch of row t at position ch ^ (t % CPR) (CPR a power of two, so the
+// position stays inside the row), so that the row-wise writes and the column
+// reads of the MFMA operand spread over the banks.
 template <int CPR>
 __device__ __forceinline__ int klds_off(int t, int ch) {
-  return (t * CPR + (ch ^ t)) * 16;
+  static_assert((CPR & (CPR - 1)) == 0, "chunks per row: a power of two");
+  return (t * CPR + (ch ^ (t % CPR))) * 16;
 }
 
 // V tile of one wave in LDS: [16 rows][D] bf16, 16-byte chunk ch of row t
