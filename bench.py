@@ -704,8 +704,9 @@ def main():
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
-    stage_ms = {name: float(np.mean([evs[s][j].elapsed_time(evs[s][j + 1]) for s in range(args.steps)]))
-                for j, name in enumerate(stages)}
+    stage_all = {name: [evs[s][j].elapsed_time(evs[s][j + 1]) for s in range(args.steps)]
+                 for j, name in enumerate(stages)}
+    stage_ms = {name: float(np.mean(v)) for name, v in stage_all.items()}
     if ds.nnz() != nnz or nnz > cap:
         raise RuntimeError("diff encode changed between steps or overflowed")
 
@@ -761,7 +762,8 @@ def main():
     stage_rep = {}
     for name in stages:
         gbs = byts[name] / (stage_ms[name] * 1e-3) / 1e9
-        stage_rep[name] = {"ms": round(stage_ms[name], 4), "alg_GB": round(byts[name] / 1e9, 4),
+        stage_rep[name] = {"ms": round(stage_ms[name], 4), "ms_median": round(float(np.median(stage_all[name])), 4),
+                           "ms_min": round(float(np.min(stage_all[name])), 4), "alg_GB": round(byts[name] / 1e9, 4),
                            "GBps": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
     if dense is not None:
         gbs = byts["dense"] / (dense["ms"] * 1e-3) / 1e9
