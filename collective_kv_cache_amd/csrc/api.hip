@@ -81,6 +81,24 @@ int check_layout(const tdx_layout* lay, tdx::Dims* d, bool need_pos) {
   return TDX_OK;
 }
 
+// A paged view: pools 16-byte aligned (v_pool only where needed), page table
+// 4-byte aligned, n_pages >= 1, row stride >= the pages a row needs when
+// there is more than one row.
+int check_paged(const tdx_paged_kv* p, const char* what, bool need_v, int64_t rows, int64_t per_row,
+                tdx::PageMap* m) {
+  REQ(p != nullptr, TDX_EINVAL, "%s is null", what);
+  REQ(p->k_pool != nullptr && aligned16(p->k_pool), TDX_EINVAL, "%s.k_pool is null or not 16-byte aligned", what);
+  if (need_v)
+    REQ(p->v_pool != nullptr && aligned16(p->v_pool), TDX_EINVAL, "%s.v_pool is null or not 16-byte aligned",
+        what);
+  REQ(p->n_pages >= 1, TDX_EINVAL, "%s.n_pages < 1", what);
+  REQ(p->pages != nullptr && aligned4(p->pages), TDX_EINVAL, "%s.pages is null or not 4-byte aligned", what);
+  REQ(rows <= 1 || p->stride >= per_row, TDX_EINVAL, "%s.stride %lld < %lld pages per row", what,
+      (long long)p->stride, (long long)per_row);
+  *m = tdx::PageMap{p->pages, (long long)p->stride, (long long)p->n_pages};
+  return TDX_OK;
+}
+
 #define GUARD_BEGIN try {
 #define GUARD_END                                                   \
   }                                                                 \
@@ -272,25 +290,6 @@ int tdx_restore_attn(const tdx_shape* shape, const tdx_layout* layout, const voi
 
 // ---- paged KV layout ----------------------------------------------------------
 
-namespace {
-// A paged view: pools 16-byte aligned (v_pool only where needed), page table
-// 4-byte aligned, n_pages >= 1, row stride >= the pages a row needs when
-// there is more than one row.
-int check_paged(const tdx_paged_kv* p, const char* what, bool need_v, int64_t rows, int64_t per_row,
-                tdx::PageMap* m) {
-  REQ(p != nullptr, TDX_EINVAL, "%s is null", what);
-  REQ(p->k_pool != nullptr && aligned16(p->k_pool), TDX_EINVAL, "%s.k_pool is null or not 16-byte aligned", what);
-  if (need_v)
-    REQ(p->v_pool != nullptr && aligned16(p->v_pool), TDX_EINVAL, "%s.v_pool is null or not 16-byte aligned",
-        what);
-  REQ(p->n_pages >= 1, TDX_EINVAL, "%s.n_pages < 1", what);
-  REQ(p->pages != nullptr && aligned4(p->pages), TDX_EINVAL, "%s.pages is null or not 4-byte aligned", what);
-  REQ(rows <= 1 || p->stride >= per_row, TDX_EINVAL, "%s.stride %lld < %lld pages per row", what,
-      (long long)p->stride, (long long)per_row);
-  *m = tdx::PageMap{p->pages, (long long)p->stride, (long long)p->n_pages};
-  return TDX_OK;
-}
-}  // namespace
 
 int tdx_rerotate_paged(const tdx_shape* shape, const tdx_layout* layout, const tdx_paged_kv* cached,
                        const tdx_paged_kv* out, void* stream) {

@@ -183,3 +183,38 @@ def test_transfer_rejects_bad_arguments():
     w2 = tdx.lib().tdx_restore_transfer_workspace(ctypes.byref(s), ctypes.byref(l), 3, 0, 2)
     assert 0 < w1 < w2
     assert tdx.lib().tdx_restore_transfer_workspace(ctypes.byref(s), ctypes.byref(l), 1, 0, 3) == 0
+
+
+def _paged(k_pool=FAKE, v_pool=FAKE, n_pages=8, pages=0x50000, stride=4):
+    return tdx.CPagedKV(k_pool, v_pool, n_pages, pages, stride)
+
+
+def test_paged_calls_reject_bad_arguments():
+    s, l = _shape(), _layout(n_tokens=64)  # N = 3 rows of 4 pages
+    L = tdx.lib()
+
+    def rer(cached, out):
+        return L.tdx_rerotate_paged(ctypes.byref(s), ctypes.byref(l), ctypes.byref(cached) if cached else None,
+                                    ctypes.byref(out) if out else None, None)
+    assert rer(None, _paged()) == tdx.TDX_EINVAL
+    assert rer(_paged(k_pool=None), _paged()) == tdx.TDX_EINVAL
+    assert rer(_paged(), _paged(n_pages=0)) == tdx.TDX_EINVAL
+    assert rer(_paged(), _paged(stride=3)) == tdx.TDX_EINVAL        # 3 rows need >= 4 pages each
+    assert rer(_paged(), _paged(pages=0x50002)) == tdx.TDX_EINVAL   # page table not 4-byte aligned
+    assert rer(_paged(), _paged(k_pool=ctypes.c_void_p(0x10008))) == tdx.TDX_EINVAL
+    assert "stride" in L.tdx_last_error().decode() or "aligned" in L.tdx_last_error().decode()
+
+    def enc(agents, diff_k=None, diff_v=None, ws_bytes=1 << 30):
+        return L.tdx_diff_encode_paged(ctypes.byref(s), ctypes.byref(l), FAKE, ctypes.byref(agents), 10, FAKE,
+                                       FAKE, FAKE, diff_k, diff_v, FAKE, FAKE, ws_bytes, None)
+    assert enc(_paged(v_pool=None)) == tdx.TDX_EINVAL                # encode compares V too
+    assert enc(_paged(), diff_k=FAKE) == tdx.TDX_EINVAL              # value copies: both or neither
+    assert enc(_paged(), ws_bytes=0) == tdx.TDX_EWORKSPACE
+
+    def att(priv, max_priv, agents):
+        return L.tdx_restore_attn_paged(ctypes.byref(s), ctypes.byref(l), FAKE, FAKE,
+                                        ctypes.byref(priv) if priv else None, max_priv, ctypes.byref(agents), None,
+                                        FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE, 1 << 30, None)
+    assert att(None, 10, _paged()) == tdx.TDX_EINVAL                 # private history needs its pools
+    assert att(_paged(stride=0), 40, _paged()) == tdx.TDX_EINVAL     # 40 tokens = 3 pages per row
+    assert att(_paged(), 10, _paged(v_pool=None)) == tdx.TDX_EINVAL
