@@ -17,9 +17,11 @@
 //                 its row.
 //  offsets_kernel one workgroup: exclusive scan of the row counts -> row
 //                 offsets and the true total nnz.
-//  copy_kernel    one workgroup per (row, 8-block chunk): writes the ascending
-//                 block indices and copies the Mirror's K/V blocks; entries at
-//                 or past the capacity are skipped.
+//  index_kernel   one workgroup per CSR row: the ascending block indices
+//                 (and, paged, the Mirror's page) into their slots; entries at
+//                 or past the capacity are dropped.
+//  copy_kernel    slot-major: each workgroup copies the Mirror's K/V blocks of
+//                 a few consecutive CSR entries.
 #include "common.h"
 
 namespace tdx {
@@ -27,7 +29,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kFlagThreads = 1024;
-constexpr int kCopyChunk = 8;
+constexpr int kCopySlots = 2;       // diff entries per copy workgroup step
+constexpr int kCopyMaxWg = 65536;  // copy grid (grid-stride beyond)
 constexpr int kCopyUnroll = 8;
 constexpr int kScanThreads = 1024;
 constexpr int kMaxAgents = 1024;
@@ -234,32 +237,53 @@ __device__ __forceinline__ void cp_store(const u32x4& v, u32x4* p) {
 #endif
 }
 
-// PAGED: the Mirror's block is page pm[a][beta] (row r = a * L + l); its page
-// ID goes to diff_page[slot], and the values are copied only when dk is set.
+// One workgroup per CSR row (agent, layer): the ascending block indices of the
+// row's flagged blocks into their slots (entries at or past the capacity are
+// dropped).  PAGED: also each entry's page, the Mirror's page pm[a][beta].
 template <bool PAGED>
-__global__ __launch_bounds__(kThreads) void copy_kernel(
-    const u32x4* __restrict__ ak, const u32x4* __restrict__ av, const uint8_t* __restrict__ flags,
-    const int32_t* __restrict__ rank, const int32_t* __restrict__ off, int nb, int chunks,
-    int64_t cap, int32_t* __restrict__ diff_idx, u32x4* __restrict__ dk, u32x4* __restrict__ dv,
-    PageMap pm, int L, int32_t* __restrict__ diff_page) {
-  const size_t r = blockIdx.y;
-  const int b0 = blockIdx.x * kCopyChunk;
-  const int tid = threadIdx.x;
+__global__ __launch_bounds__(kThreads) void index_kernel(const uint8_t* __restrict__ flags,
+                                                         const int32_t* __restrict__ rank,
+                                                         const int32_t* __restrict__ off, int nb, int64_t cap,
+                                                         int32_t* __restrict__ diff_idx, PageMap pm, int L,
+                                                         int32_t* __restrict__ diff_page) {
+  const size_t r = blockIdx.x;
   const int64_t row_off = off[r];
-  for (int beta = b0; beta < min(b0 + kCopyChunk, nb); ++beta) {
-    if (!flags[r * nb + beta]) continue;  // uniform
+  for (int beta = threadIdx.x; beta < nb; beta += kThreads) {
+    if (!flags[r * nb + beta]) continue;
     const int64_t slot = row_off + rank[r * nb + beta];
     if (slot >= cap) continue;
-    size_t src = (r * nb + beta) * (size_t)chunks;
-    if constexpr (PAGED) {
-      const long long pg = page_at(pm, (long long)(r / L), beta);
-      src = ((size_t)(r % L) * pm.n_pages + pg) * chunks;
-      if (tid == 0) diff_page[slot] = (int32_t)pg;
-    }
-    if (tid == 0) diff_idx[slot] = beta;
-    if (dk == nullptr) continue;  // paged record without value copies (uniform)
-    const size_t dst = (size_t)slot * chunks;
-    // kCopyUnroll chunks of K and of V per thread in flight, then their stores
+    diff_idx[slot] = beta;
+    if constexpr (PAGED) diff_page[slot] = (int32_t)page_at(pm, (long long)(r / L), beta);
+  }
+}
+
+// Slot-major value copy: workgroup w copies CSR entries [w*S, w*S + S), then
+// the groups of S a grid further on (of the min(nnz, cap) written entries),
+// from the Mirrors' caches, kCopyUnroll chunks of K and of V per thread in
+// flight.  An entry's row is found by walking the
+// row offsets from a binary search at the workgroup's first entry; its block
+// index comes from diff_idx (index_kernel).  PAGED: the source is the entry's
+// page of the pools.
+template <bool PAGED>
+__global__ __launch_bounds__(kThreads) void copy_kernel(
+    const u32x4* __restrict__ ak, const u32x4* __restrict__ av, const int32_t* __restrict__ off, int rows, int nb,
+    int chunks, int64_t cap, const int32_t* __restrict__ diff_idx, const int32_t* __restrict__ diff_page,
+    u32x4* __restrict__ dk, u32x4* __restrict__ dv, long long n_pages, int L) {
+  const int tid = threadIdx.x;
+  const int64_t total = min((int64_t)off[rows], cap);
+  for (int64_t e0 = (int64_t)blockIdx.x * kCopySlots; e0 < total; e0 += (int64_t)gridDim.x * kCopySlots) {
+  const int64_t e1 = min(e0 + kCopySlots, total);
+  int lo = 0, hi = rows - 1;  // the row of e0: largest r with off[r] <= e0
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= e0) lo = mid; else hi = mid - 1;
+  }
+  int r = lo;
+  for (int64_t e = e0; e < e1; ++e) {
+    while (off[r + 1] <= e) ++r;  // uniform
+    const size_t src = PAGED ? ((size_t)(r % L) * (size_t)n_pages + (size_t)diff_page[e]) * chunks
+                             : ((size_t)r * nb + (size_t)diff_idx[e]) * chunks;
+    const size_t dst = (size_t)e * chunks;
     for (int c0 = tid; c0 < chunks; c0 += kThreads * kCopyUnroll) {
       u32x4 xk[kCopyUnroll], xv[kCopyUnroll];
 #pragma unroll
@@ -277,6 +301,7 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(
         }
       }
     }
+  }
   }
 }
 
@@ -354,10 +379,15 @@ hipError_t encode_t(const Dims& d, const int32_t* master, const void* ak, const 
                      master, d.N);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 cgrid((nb + kCopyChunk - 1) / kCopyChunk, rows);
-  hipLaunchKernelGGL((copy_kernel<PAGED>), cgrid, dim3(kThreads), 0, s, k4, v4, flags, rank, diff_off, nb,
-                     chunks, cap, diff_idx, static_cast<u32x4*>(diff_k), static_cast<u32x4*>(diff_v), pm, d.L,
-                     diff_page);
+  hipLaunchKernelGGL((index_kernel<PAGED>), dim3(rows), dim3(kThreads), 0, s, flags, rank, diff_off, nb, cap,
+                     diff_idx, pm, d.L, diff_page);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (diff_k == nullptr || cap <= 0) return hipSuccess;  // a paged record without value copies
+  // every written entry has a slot below cap; surplus workgroups exit at once
+  const int64_t cwg = min((cap + kCopySlots - 1) / kCopySlots, (int64_t)kCopyMaxWg);
+  hipLaunchKernelGGL((copy_kernel<PAGED>), dim3((unsigned)cwg), dim3(kThreads), 0, s, k4, v4, diff_off, rows, nb,
+                     chunks, cap, diff_idx, diff_page, static_cast<u32x4*>(diff_k), static_cast<u32x4*>(diff_v),
+                     (long long)pm.n_pages, d.L);
   return hipGetLastError();
 }
 }  // namespace
