@@ -13,6 +13,14 @@ layer).  Each paged operation is defined as the contiguous operation applied
 to the sequences gathered out of their pages; a paged diff record names, per
 entry, the Mirror's own page of the block instead of holding a copy.  Page
 IDs outside [0, n_pages) are clamped to the nearest valid page.
+
+Pins (tests/test_oracle_paged.py): an identity page table reduces gather to a
+reshape of the pool; scatter/gather round trips leave untouched pages and the
+unused rows of a partial page as they were; clamping of out-of-range IDs;
+the paged re-rotation on shuffled pages equals the contiguous definition;
+every diff entry's page holds the entry's values; the paged
+restore-attention on shuffled pages equals the contiguous oracle on the
+original arrays.  No function here is "parity unpinned".
 """
 
 from __future__ import annotations

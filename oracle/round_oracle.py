@@ -45,6 +45,13 @@ Readings where the pages leave a step open:
   copy in member i, ``priv_len[i]`` the member's other tokens.
 * ``token_map[r][p]`` is the canonical index of token p of request r in its
   group's shared region, or -1 for a private token.
+
+Pins (tests/test_round_plan.py): four hand-worked rounds with literal expected
+layouts (slot splits, min_share, a private repeat, leading and doubled
+separators), separator edge cases, and brute-force restatements of every rule
+above on seeded random rounds (itertools.groupby runs, holder counts, content
+at every dst_pos, first occurrences, token maps, priv_len, slot
+disjointness, greedy placement).  No function here is "parity unpinned".
 """
 
 from __future__ import annotations
