@@ -435,12 +435,16 @@ size_t tdx_restore_transfer_workspace(const tdx_shape* shape, const tdx_layout* 
   return tdx::transfer_ws_bytes(d, n_req, layer_end - layer_begin);
 }
 
-int tdx_restore_transfer(const tdx_shape* shape, const tdx_layout* layout, const void* master_k,
-                         const void* master_v, const int32_t* diff_off, const int32_t* diff_idx,
-                         const void* diff_k, const void* diff_v, const int32_t* agents, int32_t n_req,
-                         int32_t layer_begin, int32_t layer_end, void* k_out, void* v_out, void* ws,
-                         size_t ws_bytes, void* stream) {
-  GUARD_BEGIN
+}  // extern "C"
+
+namespace {
+// Shared by the dense-output and paged-output transfer restores: out_paged
+// null = dense k_out/v_out [n_req][L][T][Hkv][D].
+int restore_transfer_impl(const char* what, const tdx_shape* shape, const tdx_layout* layout, const void* master_k,
+                          const void* master_v, const int32_t* diff_off, const int32_t* diff_idx,
+                          const void* diff_k, const void* diff_v, const int32_t* agents, int32_t n_req,
+                          int32_t layer_begin, int32_t layer_end, void* k_out, void* v_out,
+                          const tdx_paged_kv* out_paged, void* ws, size_t ws_bytes, void* stream) {
   tdx::Dims d{};
   int rc;
   if ((rc = check_shape(shape, &d)) != TDX_OK) return rc;
@@ -456,8 +460,15 @@ int tdx_restore_transfer(const tdx_shape* shape, const tdx_layout* layout, const
   REQ(diff_idx != nullptr && diff_k != nullptr && diff_v != nullptr, TDX_EINVAL, "diff arrays are null");
   REQ(aligned16(diff_k) && aligned16(diff_v), TDX_EINVAL, "diff_k/diff_v not 16-byte aligned");
   REQ_PTR4(agents);
-  REQ_PTR(k_out);
-  REQ_PTR(v_out);
+  tdx::PageMap opm{nullptr, 0, 1};
+  if (out_paged != nullptr) {
+    if ((rc = check_paged(out_paged, "out", true, n_req, d.T / TDX_DIFF_BLOCK, &opm)) != TDX_OK) return rc;
+    k_out = out_paged->k_pool;
+    v_out = out_paged->v_pool;
+  } else {
+    REQ_PTR(k_out);
+    REQ_PTR(v_out);
+  }
   const size_t need = tdx::transfer_ws_bytes(d, n_req, layer_end - layer_begin);
   REQ(ws != nullptr && aligned16(ws) && ws_bytes >= need, TDX_EWORKSPACE, "workspace of %zu bytes < %zu", ws_bytes, need);
   REQ(gpu_readable(master_k) && gpu_readable(master_v) && gpu_readable(diff_off) && gpu_readable(diff_idx) &&
@@ -480,9 +491,37 @@ int tdx_restore_transfer(const tdx_shape* shape, const tdx_layout* layout, const
   t.k_out = k_out;
   t.v_out = v_out;
   t.ws = ws;
+  t.out_pages = opm;
   hipError_t e = tdx::launch_transfer(d, t, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "tdx_restore_transfer launch");
+  if (e != hipSuccess) return hip_fail(e, what);
   return ok();
+}
+}  // namespace
+
+extern "C" {
+
+int tdx_restore_transfer(const tdx_shape* shape, const tdx_layout* layout, const void* master_k,
+                         const void* master_v, const int32_t* diff_off, const int32_t* diff_idx,
+                         const void* diff_k, const void* diff_v, const int32_t* agents, int32_t n_req,
+                         int32_t layer_begin, int32_t layer_end, void* k_out, void* v_out, void* ws,
+                         size_t ws_bytes, void* stream) {
+  GUARD_BEGIN
+  return restore_transfer_impl("tdx_restore_transfer launch", shape, layout, master_k, master_v, diff_off, diff_idx,
+                               diff_k, diff_v, agents, n_req, layer_begin, layer_end, k_out, v_out, nullptr, ws,
+                               ws_bytes, stream);
+  GUARD_END
+}
+
+int tdx_restore_transfer_paged(const tdx_shape* shape, const tdx_layout* layout, const void* master_k,
+                               const void* master_v, const int32_t* diff_off, const int32_t* diff_idx,
+                               const void* diff_k, const void* diff_v, const int32_t* agents, int32_t n_req,
+                               int32_t layer_begin, int32_t layer_end, const tdx_paged_kv* out, void* ws,
+                               size_t ws_bytes, void* stream) {
+  GUARD_BEGIN
+  REQ(out != nullptr, TDX_EINVAL, "out is null");
+  return restore_transfer_impl("tdx_restore_transfer_paged launch", shape, layout, master_k, master_v, diff_off,
+                               diff_idx, diff_k, diff_v, agents, n_req, layer_begin, layer_end, nullptr, nullptr,
+                               out, ws, ws_bytes, stream);
   GUARD_END
 }
 

@@ -208,9 +208,10 @@ struct TransferArgs {
   const int32_t* blk_start;
   const int32_t* src_pos;
   const int32_t* dst_pos;
-  void* k_out;  // [n_req][L][T][Hkv][D]
+  void* k_out;  // [n_req][L][T][Hkv][D], or the output pools when out_pages is set
   void* v_out;
   void* ws;
+  PageMap out_pages;  // pages: null for the dense output; row j = requested agent j's T/16 pages
 };
 size_t transfer_tab_off(const Dims& d, int n_req, int nl);
 size_t transfer_ws_bytes(const Dims& d, int n_req, int nl);

@@ -75,13 +75,14 @@ __global__ __launch_bounds__(kThreads) void transfer_tab_kernel(const int32_t* _
 
 // Rows of one (block, layer): (token, head) row = 16-byte chunks at dims
 // [e0, e0 + VEC) and [e0 + D/2, e0 + D/2 + VEC), G lanes per row, RPP rows per
-// pass, NP passes cover the tile's 16 * Hkv rows.
-template <typename E, int D, int NP>
+// pass, NP passes cover the tile's 16 * Hkv rows.  PAGED: requested agent
+// j's tile is page opm[j][beta] of the output pools (16 rows of layer l).
+template <typename E, int D, int NP, bool PAGED>
 __global__ __launch_bounds__(kThreads) void transfer_kernel(
     const E* __restrict__ mk, const E* __restrict__ mv, const int32_t* __restrict__ slot,
     const E* __restrict__ dk, const E* __restrict__ dv, const float2* __restrict__ tab,
     const int32_t* __restrict__ blk_start, int n_req, int B, int T, int L, int l0, int nl, int Hkv,
-    E* __restrict__ k_out, E* __restrict__ v_out) {
+    E* __restrict__ k_out, E* __restrict__ v_out, PageMap opm) {
   constexpr int VEC = Fmt<E>::VEC;
   constexpr int HALF = D / 2;
   constexpr int G = HALF / VEC;
@@ -139,8 +140,10 @@ __global__ __launch_bounds__(kThreads) void transfer_kernel(
   for (int j = 0; j < n_req; ++j) {
     const int e = slot[((size_t)j * nl + ll) * nb + beta];  // uniform
     const float2* cs_j = tab + (size_t)j * B * HALF;
-    E* ko = k_out + (((size_t)j * L + l) * T + t0) * rowHD;
-    E* vo = v_out + (((size_t)j * L + l) * T + t0) * rowHD;
+    const size_t orow = PAGED ? ((size_t)l * opm.n_pages + page_at(opm, j, beta)) * kTile
+                              : ((size_t)j * L + l) * T + t0;
+    E* ko = k_out + orow * rowHD;
+    E* vo = v_out + orow * rowHD;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const int row = row0 + p * RPP;
@@ -172,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void transfer_kernel(
   }
 }
 
-template <typename E, int D>
+template <typename E, int D, bool PAGED>
 hipError_t launch_t(const Dims& d, const TransferArgs& t, hipStream_t s) {
   constexpr int G = D / 2 / Fmt<E>::VEC;
   constexpr int RPP = kThreads / G;
@@ -192,10 +195,11 @@ hipError_t launch_t(const Dims& d, const TransferArgs& t, hipStream_t s) {
   const int rows = kTile * d.Hkv;
   const dim3 grid(nb, nl);
 #define TDX_TR(NP)                                                                                         \
-  hipLaunchKernelGGL((transfer_kernel<E, D, NP>), grid, dim3(kThreads), 0, s, static_cast<const E*>(t.mk), \
-                     static_cast<const E*>(t.mv), slot, static_cast<const E*>(t.dk),                       \
-                     static_cast<const E*>(t.dv), tab, t.blk_start, t.n_req, d.B, d.T, d.L, t.l0, nl,       \
-                     d.Hkv, static_cast<E*>(t.k_out), static_cast<E*>(t.v_out))
+  hipLaunchKernelGGL((transfer_kernel<E, D, NP, PAGED>), grid, dim3(kThreads), 0, s,                       \
+                     static_cast<const E*>(t.mk), static_cast<const E*>(t.mv), slot,                       \
+                     static_cast<const E*>(t.dk), static_cast<const E*>(t.dv), tab, t.blk_start, t.n_req,  \
+                     d.B, d.T, d.L, t.l0, nl, d.Hkv, static_cast<E*>(t.k_out), static_cast<E*>(t.v_out),   \
+                     t.out_pages)
   if (rows <= RPP) TDX_TR(1);
   else if (rows <= 2 * RPP) TDX_TR(2);
   else if (rows <= 4 * RPP) TDX_TR(4);
@@ -216,10 +220,17 @@ size_t transfer_ws_bytes(const Dims& d, int n_req, int nl) {
   return transfer_tab_off(d, n_req, nl) + (size_t)n_req * d.B * (d.D / 2) * 8;
 }
 
-hipError_t launch_transfer(const Dims& d, const TransferArgs& t, hipStream_t s) {
+namespace {
+template <bool PAGED>
+hipError_t transfer_t(const Dims& d, const TransferArgs& t, hipStream_t s) {
   if (d.dtype == TDX_BF16)
-    return d.D == 128 ? launch_t<uint16_t, 128>(d, t, s) : launch_t<uint16_t, 64>(d, t, s);
-  return d.D == 128 ? launch_t<float, 128>(d, t, s) : launch_t<float, 64>(d, t, s);
+    return d.D == 128 ? launch_t<uint16_t, 128, PAGED>(d, t, s) : launch_t<uint16_t, 64, PAGED>(d, t, s);
+  return d.D == 128 ? launch_t<float, 128, PAGED>(d, t, s) : launch_t<float, 64, PAGED>(d, t, s);
+}
+}  // namespace
+
+hipError_t launch_transfer(const Dims& d, const TransferArgs& t, hipStream_t s) {
+  return t.out_pages.pages != nullptr ? transfer_t<true>(d, t, s) : transfer_t<false>(d, t, s);
 }
 
 }  // namespace tdx

@@ -87,6 +87,8 @@ _SIGS = {
                                              _P, _SZ, _P]),
     "tdx_restore_attn_paged": (ctypes.c_int, [_PS, _PL, _P, _P, ctypes.POINTER(CPagedKV), _I32,
                                               ctypes.POINTER(CPagedKV), _P, _P, _P, _P, _F, _P, _P, _SZ, _P]),
+    "tdx_restore_transfer_paged": (ctypes.c_int, [_PS, _PL, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
+                                                  ctypes.POINTER(CPagedKV), _P, _SZ, _P]),
     "tdx_round_plan_build": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P, ctypes.POINTER(_P)]),
     "tdx_round_plan_n_groups": (ctypes.c_int, [_P]),
     "tdx_round_plan_group_dims": (ctypes.c_int, [_P, _I32, _P, _P, _P]),
@@ -662,3 +664,32 @@ def round_plan(requests, sep_token: int, min_share: int = 0, slots=None) -> dict
     finally:
         lib().tdx_round_plan_free(h)
     return dict(groups=groups, request_group=request_group, token_maps=maps)
+
+
+def restore_transfer_paged(shape: Shape, lay: RoundLayout, master_k: torch.Tensor, master_v: torch.Tensor,
+                           diff_off: torch.Tensor, diff_idx: torch.Tensor, diff_k: torch.Tensor,
+                           diff_v: torch.Tensor, agents: torch.Tensor, out: PagedKV, layer_begin: int = 0,
+                           layer_end: Optional[int] = None, ws=None) -> None:
+    """NEXT-1 into pages: requested agent j's rebuilt K/V (layers
+    [layer_begin, layer_end)) into the pages of ``out`` row j.  Sources as for
+    ``restore_transfer`` (device memory or pinned host memory)."""
+    L, T, H, D = shape.n_layers, lay.n_tokens, shape.n_kv_heads, shape.head_dim
+    dev_ = lay.device
+    l1 = L if layer_end is None else int(layer_end)
+    _need(agents, "agents", torch.int32, None, dev_)
+    n_req = agents.numel()
+    for name, t, dt, shp in (("master_k", master_k, shape.dtype, (L, T, H, D)),
+                             ("master_v", master_v, shape.dtype, (L, T, H, D)),
+                             ("diff_off", diff_off, torch.int32, None), ("diff_idx", diff_idx, torch.int32, None),
+                             ("diff_k", diff_k, shape.dtype, None), ("diff_v", diff_v, shape.dtype, None)):
+        _host_or_device(t, name, dt, shp, dev_)
+    out.check(shape, n_req, T // DIFF_BLOCK, dev_)
+    if out.v_pool is None:
+        raise ValueError("out needs a V pool")
+    if ws is None:
+        ws = _ws(restore_transfer_workspace(shape, lay, n_req, layer_begin, l1), dev_)
+    s, l = shape.c(), lay.c()
+    _check(lib().tdx_restore_transfer_paged(
+        ctypes.byref(s), ctypes.byref(l), _ptr(master_k), _ptr(master_v), _ptr(diff_off), _ptr(diff_idx),
+        _ptr(diff_k), _ptr(diff_v), _ptr(agents), n_req, int(layer_begin), l1, out.c(), _ptr(ws), ws.numel(),
+        _stream()), "tdx_restore_transfer_paged")

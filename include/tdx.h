@@ -315,6 +315,18 @@ int tdx_restore_attn_paged(const tdx_shape *shape, const tdx_layout *layout, con
                            const int32_t *diff_idx, const int32_t *diff_page, float scale, void *out, void *ws,
                            size_t ws_bytes, void *stream);
 
+/* NEXT-1 over pages: as tdx_restore_transfer, with requested agent j's
+ * rebuilt K (re-rotated) and V written into the pages of row j of out (T/16
+ * entries per row, canonical order, both pools) instead of a dense array:
+ * the Master chunk and the diff blocks go straight into the paged KV of the
+ * agent (notes §2a stage table, "Fused restore"; §3d).  Pages not listed in
+ * the rows, and layers outside [layer_begin, layer_end), are not written. */
+int tdx_restore_transfer_paged(const tdx_shape *shape, const tdx_layout *layout, const void *master_k,
+                               const void *master_v, const int32_t *diff_off, const int32_t *diff_idx,
+                               const void *diff_k, const void *diff_v, const int32_t *agents, int32_t n_req,
+                               int32_t layer_begin, int32_t layer_end, const tdx_paged_kv *out, void *ws,
+                               size_t ws_bytes, void *stream);
+
 /* ---- round structure from token IDs (host only) -----------------------------
  * The step before the collective calls: find the blocks that the requests of
  * one round share and derive, per group of compatible requests, the

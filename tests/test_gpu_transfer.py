@@ -145,3 +145,41 @@ def test_pageable_host_memory_is_rejected():
                                         p(v_out), p(ws), ws.numel(), None)
     assert rc == tdx.TDX_EINVAL
     assert b"pinned" in tdx.lib().tdx_last_error()
+
+
+@pytest.mark.parametrize("name,kw,agents,lr", [
+    ("tiny", {}, [2, 0], (0, 1)),
+    ("qwen7b_round", dict(n_layers=3, n_agents=4), [3, 1, 1], (1, 3)),
+])
+def test_transfer_restore_into_pages(name, kw, agents, lr):
+    # the requested agents' rebuilt K/V go straight into their pages: the same
+    # bits as the dense output, pages of other rows and layers outside the
+    # range untouched
+    from test_gpu_paged import bits, gather, to_pool
+    cfg = CONFIGS[name].scaled(**kw)
+    lay = make_layout(cfg)
+    r = Round(cfg, lay, master=1)
+    ds = r.gpu_encode()
+    H, D, L, T = cfg.n_kv_heads, cfg.head_dim, cfg.n_layers, lay.n_tokens
+    ag = torch.tensor(agents, dtype=torch.int32, device=DEV)
+    rec = record_on_host(ds)
+    k_out = sentinel_like((len(agents), L, T, H, D), cfg.torch_dtype)
+    v_out = sentinel_like((len(agents), L, T, H, D), cfg.torch_dtype)
+    tdx.restore_transfer(r.shape, r.dl, *rec, ag, lr[0], lr[1], k_out, v_out)
+    filler = torch.zeros((L, T, H, D), dtype=cfg.torch_dtype, device=DEV)
+    kpool, pages = to_pool([filler] * len(agents), 5, 41)
+    vpool, _ = to_pool([filler] * len(agents), 5, 41)
+    kbefore, vbefore = kpool.clone(), vpool.clone()
+    tdx.restore_transfer_paged(r.shape, r.dl, *rec, ag, tdx.PagedKV(kpool, vpool, pages), lr[0], lr[1])
+    torch.cuda.synchronize()
+    owned = torch.zeros(kpool.shape[1], dtype=torch.bool, device=DEV)
+    for j in range(len(agents)):
+        gk, gv = gather(kpool, pages, j, T), gather(vpool, pages, j, T)
+        assert torch.equal(bits(gk[lr[0]:lr[1]].contiguous()), bits(k_out[j, lr[0]:lr[1]].contiguous())), j
+        assert torch.equal(bits(gv[lr[0]:lr[1]].contiguous()), bits(v_out[j, lr[0]:lr[1]].contiguous())), j
+        owned[pages[j, :T // 16].long()] = True
+    outside = [l for l in range(L) if not lr[0] <= l < lr[1]]
+    for pool, before in ((kpool, kbefore), (vpool, vbefore)):
+        assert torch.equal(bits(pool[:, ~owned]), bits(before[:, ~owned]))  # other pages untouched
+        if outside:
+            assert torch.equal(bits(pool[outside]), bits(before[outside]))  # layers outside the range
