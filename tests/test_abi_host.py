@@ -218,3 +218,17 @@ def test_paged_calls_reject_bad_arguments():
     assert att(None, 10, _paged()) == tdx.TDX_EINVAL                 # private history needs its pools
     assert att(_paged(stride=0), 40, _paged()) == tdx.TDX_EINVAL     # 40 tokens = 3 pages per row
     assert att(_paged(), 10, _paged(v_pool=None)) == tdx.TDX_EINVAL
+
+
+def test_paged_transfer_rejects_bad_arguments():
+    s, l = _shape(), _layout(n_tokens=64)
+    L = tdx.lib()
+
+    def tr(out, n_req=2):
+        return L.tdx_restore_transfer_paged(ctypes.byref(s), ctypes.byref(l), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                            FAKE, n_req, 0, 2, ctypes.byref(out) if out else None, FAKE, 1 << 30,
+                                            None)
+    assert tr(None) == tdx.TDX_EINVAL
+    assert tr(_paged(v_pool=None)) == tdx.TDX_EINVAL   # K and V are both written
+    assert tr(_paged(stride=3)) == tdx.TDX_EINVAL      # 2 rows of 4 pages
+    assert tr(_paged(), n_req=0) == tdx.TDX_EINVAL
