@@ -269,3 +269,36 @@ def test_full_size_14b_paged_matches_contiguous():
         assert_close(to_numpy_bits(pout[i, l]), O.narrow(ref, np.uint16), f"paged full i={i} l={l}")
     del kpool, vpool, pkpool, pvpool, r, ds, pd
     torch.cuda.empty_cache()
+
+
+def test_out_of_range_page_ids_are_clamped():
+    # page IDs below 0 or past the pool read (and write) the nearest valid
+    # page, as the paged oracle defines; nothing outside the pool is touched
+    cfg = CONFIGS["tiny"].scaled(n_layers=2)
+    lay = make_layout(cfg)
+    r = Round(cfg, lay, master=0)
+    d = r.dev
+    N, L, T = cfg.n_agents, cfg.n_layers, lay.n_tokens
+    npg = T // PAGE
+    kc = d["kc"]
+    # tile j lives in page j, the last tile in the pool's last page (npg + 1);
+    # the table names the first tile's page as -7 and the last one's past the end
+    n_pages = npg + 2
+    cpool = torch.randn((L, n_pages, PAGE, cfg.n_kv_heads, cfg.head_dim), device=DEV).to(kc.dtype)
+    tiles = kc.reshape(L, npg, PAGE, cfg.n_kv_heads, cfg.head_dim)
+    cpool[:, :npg - 1] = tiles[:, :npg - 1]
+    cpool[:, n_pages - 1] = tiles[:, npg - 1]
+    row = list(range(npg))
+    row[0], row[npg - 1] = -7, n_pages + 100
+    cp = torch.tensor([row], dtype=torch.int32, device=DEV)
+    kr = tdx.rerotate(r.shape, r.dl, kc)
+    opool, opages = to_pool([torch.zeros_like(kc)] * N, 2, 52)
+    tdx.rerotate_paged(r.shape, r.dl, tdx.PagedKV(cpool, None, cp), tdx.PagedKV(opool, None, opages))
+    torch.cuda.synchronize()
+    ref = O.paged.rerotate_paged(to_numpy_bits(cpool.cpu()), row, to_numpy_bits(torch.zeros_like(opool).cpu()),
+                                 host(opages), lay.blk_start, lay.src_pos, lay.dst_pos, cfg.theta)
+    for i in range(N):
+        got = gather(opool, opages, i, T)
+        want = O.paged.gather(ref, host(opages)[i], T)
+        assert_close(host(got), want, f"clamped rerotate agent {i}", atol=1e-5, rtol=1e-5)
+        assert torch.equal(got, kr[i])  # the clamped IDs point at the right tiles
