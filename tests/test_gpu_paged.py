@@ -114,6 +114,14 @@ def test_rerotate_paged_partial_last_page():
         assert torch.equal(gather(opool, opages, i, T), kr[i])
         last = int(opages[i, T // PAGE])
         assert torch.equal(opool[:, last, T % PAGE:], before[:, last, T % PAGE:])
+    # selection reads the same partial pages: the contiguous call's bits
+    kx = kr[:, 1].clone()
+    kx[:, ::3] += 0.05
+    col = tdx.select_important(shape, dl, kr, kx, 9, check_layer=1)
+    got = tdx.select_important_paged(shape, dl, tdx.PagedKV(opool, None, opages), kx, 9, check_layer=1)
+    torch.cuda.synchronize()
+    for key in ("dev", "score", "agent_dev", "selected", "master"):
+        assert torch.equal(got[key], col[key]), key
 
 
 @pytest.mark.parametrize("name,kw", CASES)
