@@ -14,8 +14,8 @@
 //                    per-workgroup agent partials for the Master total.
 //  select_kernel     one 1024-thread workgroup: fixed-order agent totals and
 //                    argmin, 4-pass 8-bit radix select of the k-th largest
-//                    fp32 score bit pattern, then an ordered ballot compaction
-//                    that takes ties in ascending token order.
+//                    fp32 score bit pattern, then an ordered compaction by one
+//                    scan that takes ties in ascending token order.
 #include "common.h"
 
 namespace tdx {
@@ -134,84 +134,115 @@ __global__ __launch_bounds__(kDevThreads) void deviation_kernel(
   }
 }
 
-// Inclusive wave prefix of a predicate via ballot; returns count of set lanes
-// strictly below this lane and writes the wave total.
-__device__ __forceinline__ int wave_rank(bool p, int lane, int* total) {
-  const uint64_t m = __ballot(p);
-  *total = __popcll(m);
-  return __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+// Exclusive prefix over the wave of two counters at once (the lanes below this
+// one) and the two wave totals.
+__device__ __forceinline__ void wave_excl2(uint32_t a, uint32_t b, int lane, uint32_t* ea, uint32_t* eb,
+                                           uint32_t* ta, uint32_t* tb) {
+  uint32_t ia = a, ib = b;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t va = __shfl_up(ia, o, kWave);
+    const uint32_t vb = __shfl_up(ib, o, kWave);
+    if (lane >= o) {
+      ia += va;
+      ib += vb;
+    }
+  }
+  *ea = ia - a;
+  *eb = ib - b;
+  *ta = __builtin_amdgcn_readlane(ia, kWave - 1);
+  *tb = __builtin_amdgcn_readlane(ib, kWave - 1);
 }
 
+// IN_LDS: the scores fit in LDS (T <= kSelLdsKeys) and are read from there;
+// else from global memory.  A compile-time choice, so every key read has one
+// address space (a pointer that may be either makes each read wait for all
+// outstanding loads).
+template <bool IN_LDS>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ score, const double* __restrict__ part, int nparts, int N, int T,
     int k, float* __restrict__ agent_dev, int32_t* __restrict__ selected,
     int32_t* __restrict__ master) {
   constexpr int W = kSelThreads / kWave;
-  extern __shared__ uint32_t s_key_dyn[];  // [T] score bits, when they fit
+  constexpr int KPT = kSelLdsKeys / kSelThreads;  // keys per thread when the scores fit in LDS
+  constexpr int PB = 16;                          // partial sums in flight per thread
+  extern __shared__ uint32_t s_key_dyn[];  // [kSelLdsKeys] score bits, when they fit
   __shared__ float s_adev[kMaxAgents];
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[2][256];  // radix histograms, alternating between passes
   __shared__ uint32_t s_prefix, s_need;
-  __shared__ int s_wcnt[2][W];
+  __shared__ uint32_t s_wtot[2][W];
   __shared__ double s_at[kSelThreads];  // [S][N] slice sums
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
-  // the scores (>= 0, so their fp32 bit patterns order like the values) are
-  // read from LDS when the launch gave room for them, else from global memory
-  const bool in_lds = T <= kSelLdsKeys;
-  const uint32_t* key = in_lds ? s_key_dyn : reinterpret_cast<const uint32_t*>(score);
-  if (in_lds)
-    for (int t = tid; t < T; t += kSelThreads) s_key_dyn[t] = __float_as_uint(score[t]);
+  // the scores (>= 0, so their fp32 bit patterns order like the values)
+  constexpr bool in_lds = IN_LDS;
+  const uint32_t* sbits = reinterpret_cast<const uint32_t*>(score);
+  const uint32_t* key = in_lds ? s_key_dyn : sbits;
 
-  // ---- agent totals and Master.  Thread (slice j, agent i) = tid sums the
-  // partials p = j, j + S, ... of agent i (S = 1024 / N slices, consecutive
-  // threads read consecutive agents); agent i then adds its S slice sums in
-  // slice order, so the order of every addition is fixed.
-  {
-    const int S = kSelThreads / N;  // N <= 1024
-    const int i = tid % N, j = tid / N;
-    if (j < S) {
-      double acc = 0.0;
-#pragma unroll 4
-      for (int p = j; p < nparts; p += S) acc += part[(size_t)p * N + i];
-      s_at[j * N + i] = acc;
-    }
-    __syncthreads();
-    for (int a = tid; a < N; a += kSelThreads) {
-      double tot = 0.0;
-      for (int q = 0; q < S; ++q) tot += s_at[q * N + a];
-      const float v = (float)tot;
-      agent_dev[a] = v;
-      s_adev[a] = v;
-    }
+  // ---- loads.  The scores go to LDS; this thread's first PB partial sums
+  // are issued right after them and stay in flight through the selection,
+  // which does not need them (the agent totals and the Master come last).
+  // Thread (slice j, agent i) sums the partials p = j, j + S, ... of agent i
+  // in that order (S = 1024 / N slices); agent i then adds its S slice sums
+  // in slice order, so the order of every addition is fixed.
+  uint32_t kreg[KPT];
+  if constexpr (in_lds) {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) kreg[u] = sbits[min(tid + u * kSelThreads, T - 1)];
   }
+  const int S = kSelThreads / N;  // N <= 1024
+  const int ai = tid % N, sj = tid / N;
+  double pv[PB];
+#pragma unroll
+  for (int u = 0; u < PB; ++u) pv[u] = part[(size_t)min(sj + u * S, nparts - 1) * N + ai];
+  if constexpr (in_lds) {
+    // the launch gives room for kSelLdsKeys keys: slots past T get copies of
+    // the last score and are never read (no branch around the stores, so the
+    // partial sums issued after the scores stay in flight)
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) s_key_dyn[tid + u * kSelThreads] = kreg[u];
+  }
+  for (int x = tid; x < 2 * 256; x += kSelThreads) hist[x / 256][x % 256] = 0;
   __syncthreads();
-  if (tid == 0) {
-    int best = 0;
-    for (int i = 1; i < N; ++i)
-      if (s_adev[i] < s_adev[best]) best = i;
-    master[0] = best;
-  }
 
   // ---- radix select of the k-th largest key, 8 bits per pass from the top
   uint32_t prefix = 0, mask = 0, need = (uint32_t)k;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    for (int x = tid; x < 256; x += kSelThreads) hist[x] = 0;
-    __syncthreads();
-    for (int t = tid; t < T; t += kSelThreads) {
-      const uint32_t u = key[t];
-      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+    uint32_t* h = hist[pass & 1];
+    for (int base = 0; base < T; base += kSelThreads) {
+      const int t = base + tid;
+      const uint32_t u = key[min(t, T - 1)];
+      bool pend = t < T && (u & mask) == prefix;
+      const uint32_t dg = (u >> shift) & 255u;
+      if (pass == 0) {
+        // most scores share one of a few top bytes: one atomic per distinct
+        // digit of the wave instead of one per lane on the same bin
+        uint64_t act = __ballot(pend);
+        while (act) {
+          const int ld = __builtin_ctzll(act);
+          const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)dg, ld);
+          const uint64_t m = __ballot(pend && dg == d0);
+          if (lane == ld) atomicAdd(&h[d0], (uint32_t)__popcll(m));
+          pend = pend && dg != d0;
+          act &= ~m;
+        }
+      } else if (pend) {
+        atomicAdd(&h[dg], 1u);
+      }
     }
     __syncthreads();
     if (wave == 0) {
-      // lane owns digits 4*lane .. 4*lane+3; keys above this lane's digits =
-      // exclusive suffix sum over the higher lanes (shuffle scan, 6 steps)
-      uint32_t h[4], own = 0;
+      // lane owns digits 4*lane .. 4*lane+3 (read, then cleared for the pass
+      // after next); keys above this lane's digits = exclusive suffix sum over
+      // the higher lanes (shuffle scan, 6 steps)
+      uint32_t hv[4], own = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        h[q] = hist[4 * lane + q];
-        own += h[q];
+        hv[q] = h[4 * lane + q];
+        h[4 * lane + q] = 0;
+        own += hv[q];
       }
       uint32_t incl = own;  // inclusive suffix sum: lanes >= lane
 #pragma unroll
@@ -220,16 +251,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         if (lane + o < kWave) incl += v;
       }
       uint32_t run = incl - own;  // lanes > lane
-      // digit d crosses when run + sum_{q > d} h[q] < need <= ... + h[d]
+      // digit d crosses when run + sum_{q > d} hv[q] < need <= ... + hv[d]
       int found = -1;
       uint32_t need_in = 0;
 #pragma unroll
       for (int q = 3; q >= 0; --q) {
-        if (found < 0 && run < need && need <= run + h[q]) {
+        if (found < 0 && run < need && need <= run + hv[q]) {
           found = 4 * lane + q;
           need_in = need - run;
         }
-        run += h[q];
+        run += hv[q];
       }
       if (found >= 0) {  // exactly one lane
         s_prefix = prefix | ((uint32_t)found << shift);
@@ -242,37 +273,93 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     mask |= 255u << shift;
   }
 
-  // ---- ordered compaction: every key > thr, and the first `need` keys == thr
+  // ---- ordered compaction in one scan.  Thread j owns the contiguous run of
+  // tokens [j*C, j*C + C).  Every key above the threshold is selected, and
+  // the first `need` keys equal to it in token order; so a selected token's
+  // slot is (keys above before it) + min(keys equal before it, need), and one
+  // exclusive scan of the two per-run counts places every token.
   const uint32_t thr = prefix;
-  int carry_eq = 0, carry_sel = 0;
-  for (int base = 0; base < T; base += kSelThreads) {
-    const int t = base + tid;
-    const bool valid = t < T;
-    const uint32_t u = valid ? key[t] : 0u;
-    const bool gt = valid && u > thr;
-    const bool eq = valid && u == thr;
-    int tot_eq, tot_sel;
-    const int r_eq = wave_rank(eq, lane, &tot_eq);
-    if (lane == 0) s_wcnt[0][wave] = tot_eq;
-    __syncthreads();
-    int pre_eq = carry_eq, all_eq = carry_eq;
-    for (int w = 0; w < W; ++w) {
-      if (w < wave) pre_eq += s_wcnt[0][w];
-      all_eq += s_wcnt[0][w];
+  const int C = (T + kSelThreads - 1) / kSelThreads;
+  const int t0 = min(tid * C, T), t1 = min(t0 + C, T);
+  uint32_t ngt = 0, neq = 0;
+  for (int t = t0; t < t1; ++t) {
+    const uint32_t u = key[t];
+    ngt += u > thr;
+    neq += u == thr;
+  }
+  uint32_t egt, eeq, wgt, weq;
+  wave_excl2(ngt, neq, lane, &egt, &eeq, &wgt, &weq);
+  if (lane == 0) {
+    s_wtot[0][wave] = wgt;
+    s_wtot[1][wave] = weq;
+  }
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) {
+    egt += s_wtot[0][w];
+    eeq += s_wtot[1][w];
+  }
+  for (int t = t0; t < t1; ++t) {
+    const uint32_t u = key[t];
+    if (u > thr) {
+      const uint32_t pos = egt + min(eeq, need);
+      if (pos < (uint32_t)k) selected[pos] = t;
+      ++egt;
+    } else if (u == thr) {
+      if (eeq < need && egt + eeq < (uint32_t)k) selected[egt + eeq] = t;
+      ++eeq;
     }
-    const bool sel = gt || (eq && (uint32_t)(pre_eq + r_eq) < need);
-    const int r_sel = wave_rank(sel, lane, &tot_sel);
-    if (lane == 0) s_wcnt[1][wave] = tot_sel;
-    __syncthreads();
-    int pre_sel = carry_sel, all_sel = carry_sel;
-    for (int w = 0; w < W; ++w) {
-      if (w < wave) pre_sel += s_wcnt[1][w];
-      all_sel += s_wcnt[1][w];
+  }
+
+  // ---- agent totals (the partial sums loaded at the start, then any further
+  // batches), then the Master
+  if (sj < S) {
+    double acc = 0.0;
+#pragma unroll
+    for (int u = 0; u < PB; ++u)
+      if (sj + u * S < nparts) acc += pv[u];
+    for (int p0 = sj + PB * S; p0 < nparts; p0 += PB * S) {
+      double v[PB];
+#pragma unroll
+      for (int u = 0; u < PB; ++u) v[u] = part[(size_t)min(p0 + u * S, nparts - 1) * N + ai];
+#pragma unroll
+      for (int u = 0; u < PB; ++u)
+        if (p0 + u * S < nparts) acc += v[u];
     }
-    if (sel && pre_sel + r_sel < k) selected[pre_sel + r_sel] = t;
-    carry_eq = all_eq;
-    carry_sel = all_sel;
-    __syncthreads();
+    s_at[sj * N + ai] = acc;
+  }
+  __syncthreads();
+  for (int a = tid; a < N; a += kSelThreads) {
+    double tot = 0.0;
+    for (int q = 0; q < S; ++q) tot += s_at[q * N + a];
+    const float v = (float)tot;
+    agent_dev[a] = v;
+    s_adev[a] = v;
+  }
+  __syncthreads();
+
+  // ---- Master: argmin over the fp32 totals, ties to the lower index (each
+  // lane scans its agents in ascending order, then a butterfly that prefers
+  // the lower index on equal values)
+  if (wave == 0) {
+    float bv = lane < N ? s_adev[lane] : INFINITY;
+    int bi = lane < N ? lane : 0x7fffffff;
+    for (int a = lane + kWave; a < N; a += kWave) {
+      const float v = s_adev[a];
+      if (v < bv) {
+        bv = v;
+        bi = a;
+      }
+    }
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, kWave);
+      const int oi = __shfl_xor(bi, o, kWave);
+      if (ov < bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (lane == 0) master[0] = bi;
   }
 }
 
@@ -342,9 +429,13 @@ hipError_t select_t(const Dims& d, int check_layer, const void* k_reuse, const P
             ? launch_dev_d<float, 128, PAGED>(d, check_layer, k_reuse, pm, k_recomp, dev, score, part, nparts, s)
             : launch_dev_d<float, 64, PAGED>(d, check_layer, k_reuse, pm, k_recomp, dev, score, part, nparts, s);
   if (e != hipSuccess) return e;
-  const size_t lds = d.T <= kSelLdsKeys ? (size_t)d.T * sizeof(uint32_t) : 0;
-  hipLaunchKernelGGL(select_kernel, dim3(1), dim3(kSelThreads), lds, s, score, part, nparts, d.N,
-                     d.T, k, agent_dev, selected, master);
+  const size_t lds = d.T <= kSelLdsKeys ? (size_t)kSelLdsKeys * sizeof(uint32_t) : 0;
+  if (d.T <= kSelLdsKeys)
+    hipLaunchKernelGGL(select_kernel<true>, dim3(1), dim3(kSelThreads), lds, s, score, part, nparts, d.N,
+                       d.T, k, agent_dev, selected, master);
+  else
+    hipLaunchKernelGGL(select_kernel<false>, dim3(1), dim3(kSelThreads), lds, s, score, part, nparts, d.N,
+                       d.T, k, agent_dev, selected, master);
   return hipGetLastError();
 }
 }  // namespace

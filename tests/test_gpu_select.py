@@ -111,3 +111,44 @@ def test_select_deterministic():
     torch.cuda.synchronize()
     for key in a:
         assert torch.equal(a[key].view(torch.int32), b[key].view(torch.int32)), key
+
+
+# a round longer than the selection's LDS buffer (12288 scores): the scores
+# are read from global memory in every pass
+LONG = CONFIGS["tiny"].scaled(name="tiny_long", n_blocks=40, blk_len=(512, 512))
+
+
+def test_select_long_round_reads_scores_from_global_memory():
+    lay = make_layout(LONG)
+    assert lay.n_tokens > 12288
+    kr = reuse_stand_in(LONG, lay)
+    kx = recomputed_k(LONG, lay, kr)
+    k = O.topk_count(LONG.pct, lay.n_tokens)
+    sel, m, sel_ref, m_ref = _check(LONG, lay, kr, kx, k)
+    assert sel.tolist() == sel_ref.tolist()
+    assert m == m_ref
+
+
+def _tied_round(cfg, lay):
+    """Reused K all zero; recomputed K = 1.0 on every 7th token and 0.5 on
+    every 3rd of the others, so scores take three exact values and the 0.5
+    band is one long run of ties spread over the whole round."""
+    T = lay.n_tokens
+    kr = torch.zeros((cfg.n_agents, T, cfg.n_kv_heads, cfg.head_dim), dtype=cfg.torch_dtype)
+    kx = kr.clone()
+    hi = np.arange(0, T, 7)
+    lo = np.setdiff1d(np.arange(0, T, 3), hi)
+    kx[:, torch.as_tensor(hi)] = 1.0
+    kx[:, torch.as_tensor(lo)] = 0.5
+    return kr, kx, hi, lo
+
+
+@pytest.mark.parametrize("cfg", [CONFIGS["qwen7b_check"], LONG], ids=["qwen7b_check", "tiny_long"])
+def test_select_ties_at_the_threshold_take_the_lowest_tokens(cfg):
+    lay = make_layout(cfg)
+    kr, kx, hi, lo = _tied_round(cfg, lay)
+    k = len(hi) + len(lo) // 2 + 1
+    sel, _, sel_ref, _ = _check(cfg, lay, kr, kx, k)
+    want = np.sort(np.concatenate([hi, lo[:k - len(hi)]]))
+    assert sel_ref.tolist() == want.tolist()
+    assert sel.tolist() == want.tolist()
