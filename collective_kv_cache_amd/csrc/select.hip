@@ -154,11 +154,11 @@ __device__ __forceinline__ void wave_excl2(uint32_t a, uint32_t b, int lane, uin
   *tb = __builtin_amdgcn_readlane(ib, kWave - 1);
 }
 
-// IN_LDS: the scores fit in LDS (T <= kSelLdsKeys) and are read from there;
-// else from global memory.  A compile-time choice, so every key read has one
-// address space (a pointer that may be either makes each read wait for all
+// KEYS_IN_LDS = 1: the scores fit in LDS (T <= kSelLdsKeys) and are read from
+// there; 0: from global memory.  A compile-time choice, so every key read has
+// one address space (a pointer that may be either makes each read wait for all
 // outstanding loads).
-template <bool IN_LDS>
+template <int KEYS_IN_LDS>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ score, const double* __restrict__ part, int nparts, int N, int T,
     int k, float* __restrict__ agent_dev, int32_t* __restrict__ selected,
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const int lane = tid % kWave;
   const int wave = tid / kWave;
   // the scores (>= 0, so their fp32 bit patterns order like the values)
-  constexpr bool in_lds = IN_LDS;
+  constexpr bool in_lds = KEYS_IN_LDS != 0;
   const uint32_t* sbits = reinterpret_cast<const uint32_t*>(score);
   const uint32_t* key = in_lds ? s_key_dyn : sbits;
 
@@ -431,10 +431,10 @@ hipError_t select_t(const Dims& d, int check_layer, const void* k_reuse, const P
   if (e != hipSuccess) return e;
   const size_t lds = d.T <= kSelLdsKeys ? (size_t)kSelLdsKeys * sizeof(uint32_t) : 0;
   if (d.T <= kSelLdsKeys)
-    hipLaunchKernelGGL(select_kernel<true>, dim3(1), dim3(kSelThreads), lds, s, score, part, nparts, d.N,
+    hipLaunchKernelGGL(select_kernel<1>, dim3(1), dim3(kSelThreads), lds, s, score, part, nparts, d.N,
                        d.T, k, agent_dev, selected, master);
   else
-    hipLaunchKernelGGL(select_kernel<false>, dim3(1), dim3(kSelThreads), lds, s, score, part, nparts, d.N,
+    hipLaunchKernelGGL(select_kernel<0>, dim3(1), dim3(kSelThreads), lds, s, score, part, nparts, d.N,
                        d.T, k, agent_dev, selected, master);
   return hipGetLastError();
 }
