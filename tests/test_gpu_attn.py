@@ -87,11 +87,13 @@ def test_zero_and_all_diff_blocks(which):
     assert_close(fused, o_fused, f"fused {which}")
 
 
-def test_full_size_14b_sampled():
-    # 14B round at full size in the benchmark's launch configuration; sampled
-    # (agent, layer) outputs are computed one by one by the oracle from host
-    # copies of the generated inputs and the oracle's own diff rows.
-    cfg = CONFIGS["qwen14b_round"]
+@pytest.mark.parametrize("name", ["qwen14b_round", "qwen7b_scaleout"])
+def test_full_size_sampled(name):
+    # full-size rounds in the benchmark's launch configuration (the 64-agent
+    # round's caches pass 2^32 elements); sampled (agent, layer) outputs are
+    # computed one by one by the oracle from host copies of the generated
+    # inputs and the oracle's own diff rows.
+    cfg = CONFIGS[name]
     lay = make_layout(cfg)
     master = 2
     r = Round(cfg, lay, master=master, device_gen=DEV)
@@ -101,7 +103,8 @@ def test_full_size_14b_sampled():
     torch.cuda.synchronize()
     d = r.dev
     scale = r.scale
-    for i, l in ((0, 0), (master, 11), (5, 30), (cfg.n_agents - 1, cfg.n_layers - 1)):
+    L = cfg.n_layers
+    for i, l in ((0, 0), (master, 11), (5, L - 5), (cfg.n_agents - 1, L - 1)):
         p0, p1 = int(lay.priv_off[i]), int(lay.priv_off[i + 1])
         mk, mv = to_numpy_bits(d["kc"][l]), to_numpy_bits(d["vc"][l])
         _, idx, dk, dv = O.diff_encode(np.stack([mk, to_numpy_bits(d["ak"][i, l])])[:, None],

@@ -91,11 +91,13 @@ def test_encode_capacity_overflow_reports_true_total():
                         ak.to(DEV), av.to(DEV), cap_blocks=cap, check=True)
 
 
-def test_encode_full_size_planted_rows_and_samples():
-    # 14B round at full size, drawn in HBM; every row must equal the planted
-    # block set (a property that holds at any size) and sampled rows must be
-    # bit-exact against the oracle.
-    cfg = CONFIGS["qwen14b_round"]
+@pytest.mark.parametrize("name", ["qwen14b_round", "qwen7b_scaleout"])
+def test_encode_full_size_planted_rows_and_samples(name):
+    # full-size rounds (the 64-agent caches hold over 2^32 elements each),
+    # drawn in HBM; every row must equal the planted block set (a property
+    # that holds at any size) and sampled rows must be bit-exact against the
+    # oracle.
+    cfg = CONFIGS[name]
     lay = make_layout(cfg)
     kc, vc = cached_kv(cfg, lay, device=DEV)
     master = 4
@@ -111,7 +113,7 @@ def test_encode_full_size_planted_rows_and_samples():
         for l in range(L):
             r = i * L + l
             assert idx[off[r]:off[r + 1]].tolist() == want, (i, l)
-    for i, l in ((0, 0), (7, 23), (cfg.n_agents - 1, L - 1)):
+    for i, l in ((0, 0), (7, 23), (cfg.n_agents // 2, L // 2), (cfg.n_agents - 1, L - 1)):
         pk = torch.stack([ak[master, l:l + 1], ak[i, l:l + 1]])
         pv = torch.stack([av[master, l:l + 1], av[i, l:l + 1]])
         ref = O.diff_encode(to_numpy_bits(pk), to_numpy_bits(pv), 0)

@@ -61,11 +61,13 @@ def test_rerotate_zero_shift_is_bitwise_copy_bf16():
         np.testing.assert_array_equal(got[i], to_numpy_bits(kc))
 
 
-def test_rerotate_full_size_sampled():
-    # 14B round at full size (10 agents x 48 layers x 4912 tokens x 8 heads):
-    # sampled (agent, layer, token) rows against the oracle, in the same launch
-    # configuration the benchmark times.
-    cfg = CONFIGS["qwen14b_round"]
+@pytest.mark.parametrize("name", ["qwen14b_round", "qwen7b_scaleout"])
+def test_rerotate_full_size_sampled(name):
+    # full-size rounds (14B: 10 agents x 48 layers x 4912 tokens x 8 heads;
+    # 64 agents x 28 layers x ~5.5K tokens x 4 heads, whose output passes 2^32
+    # elements): sampled (agent, layer, token) rows against the oracle, in the
+    # same launch configuration the benchmark times.
+    cfg = CONFIGS[name]
     lay = make_layout(cfg)
     kc, _ = cached_kv(cfg, lay, device=DEV)
     out = tdx.rerotate(shape_of(cfg), dlayout(lay), kc)

@@ -10,7 +10,7 @@ import torch
 
 import oracle as O
 from collective_kv_cache_amd import tdx
-from workload import CONFIGS, make_layout, reuse_stand_in, recomputed_k, to_numpy_bits
+from workload import CONFIGS, make_layout, cached_kv, reuse_stand_in, recomputed_k, to_numpy_bits
 
 from gpu_common import (DEV, assert_master, assert_scores, assert_selection, dlayout, host,
                         shape_of)
@@ -152,3 +152,28 @@ def test_select_ties_at_the_threshold_take_the_lowest_tokens(cfg):
     want = np.sort(np.concatenate([hi, lo[:k - len(hi)]]))
     assert sel_ref.tolist() == want.tolist()
     assert sel.tolist() == want.tolist()
+
+
+@pytest.mark.parametrize("name", ["qwen14b_round", "qwen7b_scaleout"])
+def test_select_full_size_last_layer_of_the_rerotated_round(name):
+    # the benchmark's inputs at full size: the re-rotated K of every layer
+    # (64 agents: over 2^32 elements), with the check layer the last one, so
+    # the agents' rows sit at the far end of the tensor
+    cfg = CONFIGS[name]
+    lay = make_layout(cfg)
+    kc, _ = cached_kv(cfg, lay, device=DEV)
+    kr = tdx.rerotate(shape_of(cfg), dlayout(lay), kc)
+    cl = cfg.n_layers - 1
+    kx = recomputed_k(cfg, lay, kr[:, cl].contiguous())
+    k = O.topk_count(cfg.pct, lay.n_tokens)
+    out = tdx.select_important(shape_of(cfg), dlayout(lay), kr, kx, k, check_layer=cl)
+    torch.cuda.synchronize()
+    d, s, a = O.deviation(to_numpy_bits(kr[:, cl]), to_numpy_bits(kx))
+    s32, a32 = s.astype(np.float32), a.astype(np.float32)
+    assert_scores(host(out["dev"]), d.astype(np.float32), "dev")
+    assert_scores(host(out["score"]), s32, "score")
+    assert_scores(host(out["agent_dev"]), a32, "agent_dev")
+    assert_selection(host(out["selected"]), s32, k)
+    assert_master(int(host(out["master"])[0]), a32)
+    del kr, kx, kc, out
+    torch.cuda.empty_cache()
