@@ -986,21 +986,43 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, E* __restrict__ 
   const int nsp = min((nt + kTilesPerSplit - 1) / kTilesPerSplit, a.SP);
   const size_t rec = D + 4;
   const float* pr = a.part + row * a.S * rec;
+  // the row's records: its nsp agent splits, then the Master splits [SP, S)
+  // (slots [nsp, SP) belong to no task of this row); record j of that list
+  const int nu = nsp + (a.S - a.SP);
+  auto rec_of = [&](int j) { return (size_t)(j < nsp ? j : a.SP + (j - nsp)) * rec; };
+  // the row maximum: lane j reads record j's m (up to 64 records at once)
   float mm = -INFINITY;
-  for (int s = 0; s < a.S; ++s) {
-    if (s >= nsp && s < a.SP) continue;
-    mm = fmaxf(mm, pr[s * rec]);
+  for (int j0 = 0; j0 < nu; j0 += kWave) {
+    const int j = j0 + lane;
+    const float ms = pr[rec_of(min(j, nu - 1))];
+    mm = fmaxf(mm, j < nu ? ms : -INFINITY);
   }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) mm = fmaxf(mm, __shfl_xor(mm, o, kWave));
+  // rescale and add the records in list order, MG records' loads in flight at
+  // a time
   constexpr int PER = D / kWave;
+  constexpr int MG = 8;
   float o[PER] = {};
   float ls = 0.f;
-  for (int s = 0; s < a.S; ++s) {
-    if (s >= nsp && s < a.SP) continue;
-    const float ms = pr[s * rec];
-    const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - mm);
-    ls += f * pr[s * rec + 1];
+  for (int j0 = 0; j0 < nu; j0 += MG) {
+    float mv[MG], lv[MG], ov[MG][PER];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) o[k] += f * pr[s * rec + 4 + lane + k * kWave];
+    for (int j = 0; j < MG; ++j) {
+      const float* r = pr + rec_of(min(j0 + j, nu - 1));
+      mv[j] = r[0];
+      lv[j] = r[1];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) ov[j][k] = r[4 + lane + k * kWave];
+    }
+#pragma unroll
+    for (int j = 0; j < MG; ++j) {
+      if (j0 + j >= nu) break;
+      const float f = (mv[j] == -INFINITY) ? 0.f : exp2f(mv[j] - mm);
+      ls += f * lv[j];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) o[k] += f * ov[j][k];
+    }
   }
   const float inv = ls > 0.f ? 1.0f / ls : 0.f;
 #pragma unroll

@@ -12,7 +12,9 @@
 // agents in double precision into LDS once, then streams: every lane holds the
 // 16-byte chunk at dims [e0, e0+VEC) and its rotate-half partner at
 // [e0+D/2, e0+D/2+VEC) in registers and emits both rotated chunks for every
-// agent with 16-byte non-temporal stores.
+// agent with 16-byte stores.  Loads and stores are plain: non-temporal stores
+// were slower, and plain loads of the cached K slightly faster than
+// non-temporal ones amid the write stream.
 #include "common.h"
 
 namespace tdx {
@@ -135,8 +137,8 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(
         for (int k = 0; k < kItems; ++k) {
           const int r = rb + row_base + k * RPP;
           if (r < nrows) {
-            lo_[k] = ld16_nt(src + (size_t)r * D + e0);
-            hi_[k] = ld16_nt(src + (size_t)r * D + HALF + e0);
+            lo_[k] = ld16(src + (size_t)r * D + e0);
+            hi_[k] = ld16(src + (size_t)r * D + HALF + e0);
           }
         }
       };
