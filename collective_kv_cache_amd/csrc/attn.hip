@@ -288,9 +288,10 @@ __device__ __forceinline__ void write_record(float* rec, const RowState<D>& st, 
 // stream through a PD-stage register pipeline (each thread's chunks of the
 // tile's K and V rows), the tile in use sitting in one of two LDS buffers.
 // Step n: issue the loads of tile n+PD-1, use tile n, store tile n+1 into the
-// other buffer, barrier.  No branch surrounds a load or a use inside a
-// block, so the wait before a stage leaves the younger tiles in flight; fill
-// and drain steps run masked.  A tile that straddles two shared blocks is
+// other buffer, barrier.  No branch surrounds a load or a store of a stage
+// inside a block, so the wait before a stage leaves the younger tiles in
+// flight; fill steps skip the dot products, and a block stops after its
+// last tile.  A tile that straddles two shared blocks is
 // used once for each, with the other block's rows masked.
 
 #ifndef TDX_SH_PD
@@ -494,13 +495,17 @@ __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(TDX_
       gather_v<D>(vt, VS, q4, c16, va);
       softmax_pv<D>(st, z, va);
     };
+    // the PD-1 fill steps only load and stage; the block ends at its last
+    // tile (compute reads LDS and registers only, so the branch around it
+    // leaves the loads' waits as they are)
     St S[PD] = {};
     for (int n0 = -(PD - 1); n0 < nt; n0 += PD) {
 #pragma unroll
       for (int k = 0; k < PD; ++k) {
         const int n = n0 + k;  // tile ta + n used in this step (workgroup-uniform)
+        if (n >= nt) break;
         load(ta + min(n + PD - 1, nt - 1), S[(k + PD - 1) % PD]);
-        compute(n, n >= 0 && n < nt, n & 1);
+        if (n >= 0) compute(n, true, n & 1);
         store(S[(k + 1) % PD], (n + 1) & 1);
         __syncthreads();
       }
