@@ -370,20 +370,27 @@ hipError_t launch_dev(const Dims& d, int check_layer, const void* kr, const Page
   const size_t stride = (size_t)d.L * d.T * rowE;
   const E* krl = PAGED ? static_cast<const E*>(kr) : static_cast<const E*>(kr) + (size_t)check_layer * d.T * rowE;
   // agents in flight per wave: the group size that wastes the fewest re-reads
-  // of the last agent (ties to the larger group)
-  int best = 8;
-  for (int au : {8, 5, 4}) {
-    const int waste = (d.N + au - 1) / au * au - d.N;
-    const int bw = (d.N + best - 1) / best * best - d.N;
-    if (waste < bw) best = au;
+  // of the last agent (ties to the larger group); rows of 8 chunks per lane
+  // (fp32, 16 heads x 128) keep 2 agents in flight, within the register file
+  int best = KCH >= 8 ? 2 : 8;
+  if (KCH < 8) {
+    for (int au : {8, 5, 4}) {
+      const int waste = (d.N + au - 1) / au * au - d.N;
+      const int bw = (d.N + best - 1) / best * best - d.N;
+      if (waste < bw) best = au;
+    }
   }
 #define TDX_DEV(AU)                                                                      \
   hipLaunchKernelGGL((deviation_kernel<E, D, KCH, AU, PAGED>), dim3(nparts), dim3(kDevThreads), \
                      kDevWaves * d.N * sizeof(double), s, krl, static_cast<const E*>(kx), d.N, \
                      d.T, d.Hkv, stride, dev, score, part, pm, (long long)check_layer)
-  if (best == 8) TDX_DEV(8);
-  else if (best == 5) TDX_DEV(5);
-  else TDX_DEV(4);
+  if constexpr (KCH >= 8) {
+    TDX_DEV(2);
+  } else {
+    if (best == 8) TDX_DEV(8);
+    else if (best == 5) TDX_DEV(5);
+    else TDX_DEV(4);
+  }
 #undef TDX_DEV
   return hipGetLastError();
 }
@@ -398,7 +405,11 @@ hipError_t launch_dev_d(const Dims& d, int check_layer, const void* kr, const Pa
     case 2: return launch_dev<E, D, 2, PAGED>(d, check_layer, kr, pm, kx, dev, score, part, nparts, s);
     case 3:
     case 4: return launch_dev<E, D, 4, PAGED>(d, check_layer, kr, pm, kx, dev, score, part, nparts, s);
-    default: return hipErrorInvalidValue;
+    case 5:
+    case 6:
+    case 7:
+    case 8: return launch_dev<E, D, 8, PAGED>(d, check_layer, kr, pm, kx, dev, score, part, nparts, s);
+    default: return hipErrorInvalidValue;  // rows past 16 heads x 128 fp32 are rejected before
   }
 }
 

@@ -1,0 +1,94 @@
+"""Seeded random round shapes through every stage, against the oracle (GPU).
+
+The named workloads fix one shape each.  Here each seed draws a small round:
+1-12 agents, 1-8 KV heads, GQA groups of 1-8 query heads, 64- or 128-dim
+heads, fp32 or bf16, 1-3 layers, 1-6 shared blocks of 16-192 tokens,
+private histories of 0-300 tokens, RoPE base 1e4 or 1e6, and a random
+Master.  Re-rotation, selection (stage-wise on identical inputs), encode,
+fused restore-attention and the dense comparator are each checked against
+the oracle to the usual bar: bit-exact indices and diff values, the band
+rule for the selected set and the Master, and the stated tolerances for
+floating-point outputs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from collective_kv_cache_amd import tdx
+from workload import CONFIGS, make_layout, recomputed_k, reuse_stand_in, to_numpy_bits
+
+from gpu_common import (DEV, Round, assert_close, assert_master, assert_scores, assert_selection, dlayout,
+                        host, shape_of)
+
+pytestmark = pytest.mark.gpu
+
+# seeds with one field forced: a single agent, no private history, and 16
+# KV heads of 128 dims (the largest supported, where encode splits each
+# block's compare into two chunk slices)
+FORCED = {12: dict(n_agents=1), 13: dict(priv=("uniform", 0, 0)),
+          14: dict(n_kv_heads=16, n_q_heads=32, head_dim=128)}
+SEEDS = list(range(12)) + sorted(FORCED)
+
+
+def draw(seed):
+    rng = np.random.default_rng(np.random.SeedSequence([2024, seed]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 3, 5, 7, 8]))
+    lo = int(rng.integers(1, 13))
+    hi = int(rng.integers(lo, 13))
+    plo = int(rng.integers(0, 301))
+    phi = int(rng.integers(plo, 301))
+    cfg = CONFIGS["tiny"].scaled(
+        name=f"random{seed}", seed=1000 + seed, n_agents=int(rng.integers(1, 13)),
+        n_layers=int(rng.integers(1, 4)), n_kv_heads=hkv, n_q_heads=g * hkv,
+        head_dim=int(rng.choice([64, 128])), dtype=str(rng.choice(["f32", "bf16"])),
+        theta=float(rng.choice([1e4, 1e6])), n_blocks=int(rng.integers(1, 7)),
+        blk_len=(16 * lo, 16 * hi), priv=("uniform", plo, phi), mirror_frac=(0.1, 0.3))
+    cfg = cfg.scaled(**FORCED.get(seed, {}))
+    master = int(rng.integers(0, cfg.n_agents))
+    return cfg, master
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_round(seed):
+    cfg, master = draw(seed)
+    lay = make_layout(cfg)
+    what = (f"seed={seed} N={cfg.n_agents} L={cfg.n_layers} Hkv={cfg.n_kv_heads} Hq={cfg.n_q_heads} "
+            f"D={cfg.head_dim} {cfg.dtype} T={lay.n_tokens} B={cfg.n_blocks}")
+    fp32 = cfg.dtype == "f32"
+    r = Round(cfg, lay, master=master)
+    # a1
+    kr = host(tdx.rerotate(r.shape, r.dl, r.dev["kc"]))
+    ref = O.rerotate(to_numpy_bits(r.host["kc"]), lay.blk_start, lay.src_pos, lay.dst_pos, cfg.theta)
+    assert_close(kr, ref, f"rerotate {what}", **(dict(atol=1e-5, rtol=1e-5) if fp32 else {}))
+    # a2 + a3 on identical inputs
+    kin = reuse_stand_in(cfg, lay)
+    kx = recomputed_k(cfg, lay, kin)
+    k = O.topk_count(cfg.pct, lay.n_tokens)
+    out = tdx.select_important(shape_of(cfg, 1), dlayout(lay), kin.unsqueeze(1).contiguous().to(DEV),
+                               kx.to(DEV), k)
+    torch.cuda.synchronize()
+    d, s, a = O.deviation(to_numpy_bits(kin), to_numpy_bits(kx))
+    assert_scores(host(out["dev"]), d.astype(np.float32), f"dev {what}")
+    assert_scores(host(out["score"]), s.astype(np.float32), f"score {what}")
+    assert_selection(host(out["selected"]), s.astype(np.float32), k)
+    assert_master(int(host(out["master"])[0]), a.astype(np.float32))
+    # a4
+    ds = r.gpu_encode()
+    h = {key: to_numpy_bits(v) for key, v in r.host.items()}
+    off, idx, dk, dv = O.diff_encode(h["ak"], h["av"], master)
+    n = int(off[-1])
+    assert ds.nnz() == n, what
+    np.testing.assert_array_equal(host(ds.off), off, err_msg=what)
+    np.testing.assert_array_equal(host(ds.idx)[:n], idx, err_msg=what)
+    np.testing.assert_array_equal(to_numpy_bits(ds.k[:n]), dk, err_msg=what)
+    np.testing.assert_array_equal(to_numpy_bits(ds.v[:n]), dv, err_msg=what)
+    # a5 and a6
+    fused = host(r.gpu_fused(ds))
+    kd, vd, dense = r.gpu_dense(ds)
+    o_fused, o_kd, o_vd, o_dense = r.oracle_full()
+    assert_close(fused, o_fused, f"fused {what}")
+    assert_close(host(dense), o_dense, f"dense {what}")
+    np.testing.assert_array_equal(host(vd), o_vd, err_msg=what)
