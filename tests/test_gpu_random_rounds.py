@@ -1,7 +1,7 @@
 """Seeded random round shapes through every stage, against the oracle (GPU).
 
 The named workloads fix one shape each.  Here each seed draws a small round:
-1-12 agents, 1-8 KV heads, GQA groups of 1-8 query heads, 64- or 128-dim
+1-12 agents (40-80 in three forced seeds), 1-8 KV heads, GQA groups of 1-8 query heads, 64- or 128-dim
 heads, fp32 or bf16, 1-3 layers, 1-6 shared blocks of 16-192 tokens,
 private histories of 0-300 tokens, RoPE base 1e4 or 1e6, and a random
 Master.  Re-rotation, selection (stage-wise on identical inputs), encode,
@@ -24,11 +24,17 @@ from gpu_common import (DEV, Round, assert_close, assert_master, assert_scores, 
 
 pytestmark = pytest.mark.gpu
 
-# seeds with one field forced: a single agent, no private history, and 16
-# KV heads of 128 dims (the largest supported, where encode splits each
-# block's compare into two chunk slices)
+# seeds with fields forced: a single agent, no private history, 16 KV heads
+# of 128 dims (the largest supported, where encode splits each block's
+# compare into chunk slices), and rounds of 40-80 agents
 FORCED = {12: dict(n_agents=1), 13: dict(priv=("uniform", 0, 0)),
-          14: dict(n_kv_heads=16, n_q_heads=32, head_dim=128)}
+          14: dict(n_kv_heads=16, n_q_heads=32, head_dim=128),
+          # more agents than one re-rotation workgroup holds (32) and several
+          # agent groups per Master tile
+          15: dict(n_agents=40, n_layers=2, n_kv_heads=2, n_q_heads=14, n_blocks=8, blk_len=(64, 256)),
+          16: dict(n_agents=64, n_layers=1, n_kv_heads=4, n_q_heads=20, n_blocks=10, blk_len=(32, 192)),
+          17: dict(n_agents=80, n_layers=2, n_kv_heads=1, n_q_heads=1, head_dim=64, n_blocks=4,
+                   blk_len=(128, 320))}
 SEEDS = list(range(12)) + sorted(FORCED)
 
 
@@ -92,3 +98,50 @@ def test_random_round(seed):
     assert_close(fused, o_fused, f"fused {what}")
     assert_close(host(dense), o_dense, f"dense {what}")
     np.testing.assert_array_equal(host(vd), o_vd, err_msg=what)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_round_paged_matches_contiguous(seed):
+    # the four paged calls over pools with shuffled pages give the contiguous
+    # calls' bits on the same random round
+    from test_gpu_paged import bits, gather, to_pool
+    cfg, master = draw(seed)
+    lay = make_layout(cfg)
+    r = Round(cfg, lay, master=master)
+    d = r.dev
+    N, L, T = cfg.n_agents, cfg.n_layers, lay.n_tokens
+    what = f"seed={seed}"
+    kc = d["kc"]
+    kr = tdx.rerotate(r.shape, r.dl, kc)
+    cpool, cpages = to_pool([kc], 3, 100 + seed)
+    opool, opages = to_pool([torch.zeros_like(kc)] * N, 5, 200 + seed)
+    tdx.rerotate_paged(r.shape, r.dl, tdx.PagedKV(cpool, None, cpages), tdx.PagedKV(opool, None, opages))
+    torch.cuda.synchronize()
+    for i in range(N):
+        assert torch.equal(bits(gather(opool, opages, i, T).contiguous()), bits(kr[i])), what
+    check = L - 1
+    kx = recomputed_k(cfg, lay, kr[:, check].contiguous())
+    k = O.topk_count(cfg.pct, T)
+    col = tdx.select_important(r.shape, r.dl, kr, kx, k, check)
+    got = tdx.select_important_paged(r.shape, r.dl, tdx.PagedKV(opool, None, opages), kx, k, check)
+    torch.cuda.synchronize()
+    for key in ("dev", "score", "agent_dev", "selected", "master"):
+        assert torch.equal(got[key], col[key]), (key, what)
+    m = torch.tensor([master], dtype=torch.int32, device=DEV)
+    ds = tdx.diff_encode(r.shape, r.dl, m, d["ak"], d["av"], master_copy=False)
+    restored = tdx.restore_attn(r.shape, r.dl, d["q"], d["po"], d["pk"], d["pv"], r.max_priv, d["ak"], d["av"], ds,
+                                master_sel=m)
+    kpool, pages = to_pool([d["ak"][i] for i in range(N)], 4, 300 + seed)
+    vpool, _ = to_pool([d["av"][i] for i in range(N)], 4, 300 + seed)
+    po = lay.priv_off
+    pkpool, ppages = to_pool([d["pk"][:, po[i]:po[i + 1]] for i in range(N)], 3, 400 + seed)
+    pvpool, _ = to_pool([d["pv"][:, po[i]:po[i + 1]] for i in range(N)], 3, 400 + seed)
+    agents = tdx.PagedKV(kpool, vpool, pages)
+    pd = tdx.diff_encode_paged(r.shape, r.dl, m, agents)
+    n = ds.nnz()
+    assert pd.nnz() == n, what
+    assert torch.equal(pd.off, ds.off) and torch.equal(pd.idx[:n], ds.idx[:n]), what
+    got = tdx.restore_attn_paged(r.shape, r.dl, d["q"], d["po"], tdx.PagedKV(pkpool, pvpool, ppages), r.max_priv,
+                                 agents, m, pd)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(got), bits(restored)), what
