@@ -119,9 +119,10 @@ __global__ __launch_bounds__(kThreads) void transfer_kernel(
   const int nrows = kTile * Hkv;
   const size_t rowHD = (size_t)Hkv * D;
   const size_t tile_off = ((size_t)l * T + t0) * rowHD;
-  // this thread's rows of the Master tile: row0 + p * RPP, p < NP (all rows
-  // of the tile are covered when NP * RPP >= 16 * Hkv)
-  const int row0 = tid / G;
+  // this thread's rows of the Master tile: row0 + p * RPP, p < NP, from the
+  // workgroup's first row NP * RPP * blockIdx.z (the workgroups along z
+  // cover all 16 * Hkv rows of the tile)
+  const int row0 = (int)blockIdx.z * NP * RPP + tid / G;
   u32x4 mkl[NP], mkh[NP], mvl[NP], mvh[NP];
   int bb[NP];
 #pragma unroll
@@ -193,7 +194,10 @@ hipError_t launch_t(const Dims& d, const TransferArgs& t, hipStream_t s) {
                      d.N, t.n_req, d.B, D, d.theta, tab);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int rows = kTile * d.Hkv;
-  const dim3 grid(nb, nl);
+  // rows per workgroup: up to 8 per thread; more rows (fp32, 16 heads x
+  // 128) go to further workgroups along z
+  const int nz = (rows + 8 * RPP - 1) / (8 * RPP);
+  const dim3 grid(nb, nl, nz);
 #define TDX_TR(NP)                                                                                         \
   hipLaunchKernelGGL((transfer_kernel<E, D, NP, PAGED>), grid, dim3(kThreads), 0, s,                       \
                      static_cast<const E*>(t.mk), static_cast<const E*>(t.mv), slot,                       \
@@ -203,8 +207,7 @@ hipError_t launch_t(const Dims& d, const TransferArgs& t, hipStream_t s) {
   if (rows <= RPP) TDX_TR(1);
   else if (rows <= 2 * RPP) TDX_TR(2);
   else if (rows <= 4 * RPP) TDX_TR(4);
-  else if (rows <= 8 * RPP) TDX_TR(8);
-  else return hipErrorInvalidValue;
+  else TDX_TR(8);
 #undef TDX_TR
   return hipGetLastError();
 }

@@ -145,3 +145,25 @@ def test_random_round_paged_matches_contiguous(seed):
                                  agents, m, pd)
     torch.cuda.synchronize()
     assert torch.equal(bits(got), bits(restored)), what
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_round_transfer_restore(seed):
+    # a random subset of agents (repeats allowed) and a random layer range,
+    # rebuilt from the Master and the diff record in pinned host memory,
+    # against the oracle's dense restore; layers outside the range untouched
+    from test_gpu_transfer import check_agents, record_on_host, sentinel_like
+    cfg, master = draw(seed)
+    lay = make_layout(cfg)
+    r = Round(cfg, lay, master=master)
+    ds = r.gpu_encode()
+    rng = np.random.default_rng(np.random.SeedSequence([4096, seed]))
+    N, L, T, H, D = cfg.n_agents, cfg.n_layers, lay.n_tokens, cfg.n_kv_heads, cfg.head_dim
+    agents = [int(a) for a in rng.integers(0, N, size=int(rng.integers(1, min(N, 6) + 1)))]
+    l0 = int(rng.integers(0, L))
+    l1 = int(rng.integers(l0 + 1, L + 1))
+    ag = torch.tensor(agents, dtype=torch.int32, device=DEV)
+    k_out = sentinel_like((len(agents), L, T, H, D), cfg.torch_dtype)
+    v_out = sentinel_like((len(agents), L, T, H, D), cfg.torch_dtype)
+    tdx.restore_transfer(r.shape, r.dl, *record_on_host(ds), ag, l0, l1, k_out, v_out)
+    check_agents(r, k_out, v_out, agents, l0, l1)
