@@ -167,3 +167,42 @@ def test_random_round_transfer_restore(seed):
     v_out = sentinel_like((len(agents), L, T, H, D), cfg.torch_dtype)
     tdx.restore_transfer(r.shape, r.dl, *record_on_host(ds), ag, l0, l1, k_out, v_out)
     check_agents(r, k_out, v_out, agents, l0, l1)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_ragged_rerotate_and_select(seed):
+    # shared blocks of any length (re-rotation and selection work per token,
+    # so T need not be a multiple of 16), shifts of either sign
+    rng = np.random.default_rng(np.random.SeedSequence([8192, seed]))
+    N = int(rng.integers(1, 20))
+    H = int(rng.choice([1, 2, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    dtype = torch.float32 if rng.integers(2) else torch.bfloat16
+    B = int(rng.integers(1, 9))
+    lens = rng.integers(1, 140, size=B)
+    blk_start = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(blk_start[-1])
+    src_pos = blk_start[:-1].copy()
+    dst_pos = rng.integers(-3000, 9000, size=(N, B)).astype(np.int32)
+    theta = float(rng.choice([1e4, 1e6]))
+    shape = tdx.Shape(1, H, H, D, dtype, theta)
+    dl = tdx.RoundLayout(blk_start, src_pos, dst_pos, DEV)
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    kc = torch.randn((1, T, H, D), generator=g).to(dtype)
+    kr = host(tdx.rerotate(shape, dl, kc.to(DEV)))
+    ref = O.rerotate(to_numpy_bits(kc), blk_start, src_pos, dst_pos, theta)
+    assert_close(kr, ref, f"ragged rerotate seed={seed} T={T}",
+                 **(dict(atol=1e-5, rtol=1e-5) if dtype == torch.float32 else {}))
+    # selection on an independent reused K and noise on a random 15% of tokens
+    kin = torch.randn((N, T, H, D), generator=g).to(dtype)
+    kx = kin.clone()
+    for i in range(N):
+        tok = torch.as_tensor(rng.choice(T, max(1, T * 15 // 100), replace=False))
+        kx[i, tok] = (kin[i, tok].float() + 0.05 * torch.randn((len(tok), H, D), generator=g)).to(dtype)
+    k = O.topk_count(15, T)
+    out = tdx.select_important(shape, dl, kin.unsqueeze(1).contiguous().to(DEV), kx.to(DEV), k)
+    torch.cuda.synchronize()
+    d, s, a = O.deviation(to_numpy_bits(kin), to_numpy_bits(kx))
+    assert_scores(host(out["dev"]), d.astype(np.float32), f"ragged dev seed={seed}")
+    assert_selection(host(out["selected"]), s.astype(np.float32), k)
+    assert_master(int(host(out["master"])[0]), a.astype(np.float32))
