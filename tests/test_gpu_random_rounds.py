@@ -151,7 +151,8 @@ def test_random_round_paged_matches_contiguous(seed):
 def test_random_round_transfer_restore(seed):
     # a random subset of agents (repeats allowed) and a random layer range,
     # rebuilt from the Master and the diff record in pinned host memory,
-    # against the oracle's dense restore; layers outside the range untouched
+    # against the oracle's dense restore (layers outside the range
+    # untouched), and into pages (the same bits)
     from test_gpu_transfer import check_agents, record_on_host, sentinel_like
     cfg, master = draw(seed)
     lay = make_layout(cfg)
@@ -165,8 +166,20 @@ def test_random_round_transfer_restore(seed):
     ag = torch.tensor(agents, dtype=torch.int32, device=DEV)
     k_out = sentinel_like((len(agents), L, T, H, D), cfg.torch_dtype)
     v_out = sentinel_like((len(agents), L, T, H, D), cfg.torch_dtype)
-    tdx.restore_transfer(r.shape, r.dl, *record_on_host(ds), ag, l0, l1, k_out, v_out)
+    rec = record_on_host(ds)
+    tdx.restore_transfer(r.shape, r.dl, *rec, ag, l0, l1, k_out, v_out)
     check_agents(r, k_out, v_out, agents, l0, l1)
+    # the same agents rebuilt straight into pages: the dense output's bits
+    from test_gpu_paged import bits, gather, to_pool
+    filler = torch.zeros((L, T, H, D), dtype=cfg.torch_dtype, device=DEV)
+    kpool, pages = to_pool([filler] * len(agents), 3, 500 + seed)
+    vpool, _ = to_pool([filler] * len(agents), 3, 500 + seed)
+    tdx.restore_transfer_paged(r.shape, r.dl, *rec, ag, tdx.PagedKV(kpool, vpool, pages), l0, l1)
+    torch.cuda.synchronize()
+    for j in range(len(agents)):
+        gk, gv = gather(kpool, pages, j, T), gather(vpool, pages, j, T)
+        assert torch.equal(bits(gk[l0:l1].contiguous()), bits(k_out[j, l0:l1].contiguous())), (seed, j)
+        assert torch.equal(bits(gv[l0:l1].contiguous()), bits(v_out[j, l0:l1].contiguous())), (seed, j)
 
 
 @pytest.mark.parametrize("seed", range(6))
