@@ -219,3 +219,28 @@ def test_random_ragged_rerotate_and_select(seed):
     assert_scores(host(out["dev"]), d.astype(np.float32), f"ragged dev seed={seed}")
     assert_selection(host(out["selected"]), s.astype(np.float32), k)
     assert_master(int(host(out["master"])[0]), a.astype(np.float32))
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_round_serial_path(seed):
+    # the per-agent path: its re-rotations are the collective output's bits,
+    # agent by agent, and each agent's own selection matches the oracle run
+    # on that agent alone
+    from collective_kv_cache_amd.serial import SerialReuse
+    cfg, _ = draw(seed)
+    lay = make_layout(cfg)
+    r = Round(cfg, lay, master=0)
+    kc = r.dev["kc"]
+    kr = tdx.rerotate(r.shape, r.dl, kc)
+    kx = recomputed_k(cfg, lay, kr[:, 0].contiguous())
+    k = O.topk_count(cfg.pct, lay.n_tokens)
+    ser = SerialReuse(r.shape, lay.blk_start, lay.src_pos, lay.dst_pos, k, DEV)
+    kr_s, outs = ser.run(kc, kx, check_layer=0)
+    torch.cuda.synchronize()
+    view = torch.int16 if kr.dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(kr_s.view(view), kr.view(view)), seed
+    krh, kxh = to_numpy_bits(kr[:, 0]), to_numpy_bits(kx)
+    for i in range(cfg.n_agents):
+        d, s, a = O.deviation(krh[i:i + 1], kxh[i:i + 1])
+        assert_scores(host(outs[i]["score"]), s.astype(np.float32), f"serial score seed={seed} agent={i}")
+        assert_selection(host(outs[i]["selected"]), s.astype(np.float32), k)
