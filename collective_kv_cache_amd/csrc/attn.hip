@@ -185,8 +185,8 @@ struct AttnArgs {
   // private pools; the Master's pages are row *msel of mpm, the diff entries'
   // pages dpm[0][e], agent i's private pages row i of ppm
   PageMap mpm, dpm, ppm;
-  int pmax;  // >= 0: an agent's private tokens are capped at pmax (paged: a
-             // page-table row holds ceil(pmax/16) pages); -1: no cap
+  int pmax;  // an agent's private tokens are capped at pmax (= max_priv;
+             // paged: a page-table row holds ceil(pmax/16) pages)
 };
 
 template <int D>
@@ -619,7 +619,7 @@ __global__ __launch_bounds__(kPlanThreads) void stream_plan_kernel(AttnArgs a, S
         const int i = r / a.L, l = r % a.L;
         const int p0 = a.priv_off[i];
         t.P = a.priv_off[i + 1] - p0;
-        if (a.pmax >= 0) t.P = min(t.P, a.pmax);
+        t.P = min(t.P, a.pmax);
         t.ntp = (t.P + kTile - 1) / kTile;
         t.prow = l * ptot + p0;
         int nx = nb;
@@ -984,7 +984,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, E* __restrict__ 
   if (row >= (size_t)a.N * a.L * a.Hq) return;
   const int i = (int)(row / ((size_t)a.L * a.Hq));
   const int l = (int)((row / a.Hq) % a.L);
-  const int P = a.pmax >= 0 ? min(a.priv_off[i + 1] - a.priv_off[i], a.pmax) : a.priv_off[i + 1] - a.priv_off[i];
+  const int P = min(a.priv_off[i + 1] - a.priv_off[i], a.pmax);
   const int nx = (MODE == FUSED) ? min(max(a.diff_off[i * a.L + l + 1] - a.diff_off[i * a.L + l], 0), a.T / kTile)
                                   : a.T / kTile;
   const int nt = (P + kTile - 1) / kTile + nx;
@@ -1063,6 +1063,7 @@ __global__ __launch_bounds__(kThreads) void restore_dense_kernel(
   __shared__ float2 tab[kMaxTileBlocks * HALF];
   __shared__ int s_nb;
   __shared__ int32_t sst[kMaxTileBlocks], sid[kMaxTileBlocks];  // non-empty blocks of the tile
+  __shared__ int32_t szero[kMaxTileBlocks];                       // the block's shift is 0
   const int beta = blockIdx.x;
   const int i = blockIdx.y;
   const int tid = threadIdx.x;
@@ -1083,6 +1084,7 @@ __global__ __launch_bounds__(kThreads) void restore_dense_kernel(
       if (blk_start[b + 1] > blk_start[b]) {
         sst[n] = blk_start[b];
         sid[n] = b;
+        szero[n] = dst_pos[(size_t)i * B + b] == src_pos[b];
         ++n;
       }
     s_nb = n;
@@ -1118,17 +1120,23 @@ __global__ __launch_bounds__(kThreads) void restore_dense_kernel(
       int bb = 0;
       while (bb + 1 < nbk && sst[bb + 1] <= tok) ++bb;
       const size_t off = (size_t)row * D + e0;
-      float x[VEC], y[VEC], ox[VEC], oy[VEC];
-      Fmt<E>::unpack(ld16(ks + off), x);
-      Fmt<E>::unpack(ld16(ks + off + HALF), y);
+      const u32x4 rl = ld16(ks + off), rh = ld16(ks + off + HALF);
+      if (szero[bb]) {  // R(0) is the identity: the stored bits as they are
+        st16_nt(ko + off, rl);
+        st16_nt(ko + off + HALF, rh);
+      } else {
+        float x[VEC], y[VEC], ox[VEC], oy[VEC];
+        Fmt<E>::unpack(rl, x);
+        Fmt<E>::unpack(rh, y);
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) {
-        const float2 cs = tab[bb * HALF + e0 + j];
-        ox[j] = x[j] * cs.x - y[j] * cs.y;
-        oy[j] = y[j] * cs.x + x[j] * cs.y;
+        for (int j = 0; j < VEC; ++j) {
+          const float2 cs = tab[bb * HALF + e0 + j];
+          ox[j] = x[j] * cs.x - y[j] * cs.y;
+          oy[j] = y[j] * cs.x + x[j] * cs.y;
+        }
+        st16_nt(ko + off, Fmt<E>::pack(ox));
+        st16_nt(ko + off + HALF, Fmt<E>::pack(oy));
       }
-      st16_nt(ko + off, Fmt<E>::pack(ox));
-      st16_nt(ko + off + HALF, Fmt<E>::pack(oy));
       st16_nt(vo + off, ld16(vs + off));
       st16_nt(vo + off + HALF, ld16(vs + off + HALF));
     }
@@ -1258,7 +1266,7 @@ hipError_t dispatch_attn(const Dims& d, AttnArgs a, const Plan& p, void* out, hi
 }
 
 AttnArgs common_args(const Dims& d, const void* q, const int32_t* priv_off, const void* pk,
-                     const void* pv, float scale, void* ws) {
+                     const void* pv, int max_priv, float scale, void* ws) {
   AttnArgs a{};
   a.q = q;
   a.priv_off = priv_off;
@@ -1273,7 +1281,10 @@ AttnArgs common_args(const Dims& d, const void* q, const int32_t* priv_off, cons
   a.Hkv = d.Hkv;
   a.Hq = d.Hq;
   a.scale_log2 = scale * kLog2e;
-  a.pmax = -1;
+  // private histories are capped at max_priv: the splits are sized for it,
+  // so a history past it can only lose its own tail, never the diff tiles
+  // that follow it (paged: a page-table row holds no private page past it)
+  a.pmax = max_priv;
   return a;
 }
 
@@ -1315,7 +1326,7 @@ hipError_t launch_restore_attn(const Dims& d, const tdx_layout& lay, const void*
                                int max_priv, const MasterRef& master,
                                const int32_t* diff_off, const int32_t* diff_idx, const void* dk,
                                const void* dv, float scale, void* out, void* ws, hipStream_t s) {
-  AttnArgs a = common_args(d, q, priv_off, pk, pv, scale, ws);
+  AttnArgs a = common_args(d, q, priv_off, pk, pv, max_priv, scale, ws);
   a.sk = master.k;
   a.sv = master.v;
   a.msel = master.sel;
@@ -1330,7 +1341,7 @@ hipError_t launch_restore_attn_paged(const Dims& d, const tdx_layout& lay, const
                                      const void* ak_pool, const void* av_pool, const PageMap& apm,
                                      const int32_t* master_sel, const int32_t* diff_off, const int32_t* diff_idx,
                                      const int32_t* diff_page, float scale, void* out, void* ws, hipStream_t s) {
-  AttnArgs a = common_args(d, q, priv_off, pk_pool, pv_pool, scale, ws);
+  AttnArgs a = common_args(d, q, priv_off, pk_pool, pv_pool, max_priv, scale, ws);
   a.sk = ak_pool;  // the Master's pages and the diff entries' pages are agents' pages
   a.sv = av_pool;
   a.dk = ak_pool;
@@ -1339,7 +1350,6 @@ hipError_t launch_restore_attn_paged(const Dims& d, const tdx_layout& lay, const
   a.mpm = apm;
   a.dpm = PageMap{diff_page, 0, apm.n_pages};
   a.ppm = ppm;
-  a.pmax = max_priv;  // the page tables hold no private page past it
   return restore_attn_t<true>(d, lay, a, diff_off, diff_idx, max_priv, out, ws, s);
 }
 
@@ -1367,7 +1377,7 @@ hipError_t launch_dense_attn(const Dims& d, const void* q, const int32_t* priv_o
                              const void* pk, const void* pv, int max_priv, const void* kd,
                              const void* vd, float scale, void* out, void* ws, hipStream_t s) {
   const Plan p = make_plan(d, max_priv, false);
-  AttnArgs a = common_args(d, q, priv_off, pk, pv, scale, ws);
+  AttnArgs a = common_args(d, q, priv_off, pk, pv, max_priv, scale, ws);
   a.sk = kd;
   a.sv = vd;
   return dispatch_attn<DENSE>(d, a, p, out, s);

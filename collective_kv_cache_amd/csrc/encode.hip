@@ -16,7 +16,9 @@
 //                 flags, count of flagged blocks and each block's rank inside
 //                 its row.
 //  offsets_kernel one workgroup: exclusive scan of the row counts -> row
-//                 offsets and the true total nnz.
+//                 offsets (clamped to the capacity, so a record whose blocks
+//                 overflow it still names only written entries) and the true
+//                 total nnz.
 //  index_kernel   one workgroup per CSR row: the ascending block indices
 //                 (and, paged, the Mirror's page) into their slots; entries at
 //                 or past the capacity are dropped.
@@ -190,8 +192,14 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(uint8_t* __restrict__ fl
   if (tid == 0) count[r] = carry;
 }
 
+// Row offsets are written as min(true offset, cap): entries past the
+// capacity are never written (index_kernel, copy_kernel), and with clamped
+// offsets no row of the record reaches one of them, so every consumer that
+// reads entries [off[r], off[r+1]) stays inside the written entries.  nnz
+// keeps the true total, which tells the caller that the record is truncated.
 __global__ __launch_bounds__(kScanThreads) void offsets_kernel(const int32_t* __restrict__ count,
-                                                               int rows, int32_t* __restrict__ off,
+                                                               int rows, int64_t cap,
+                                                               int32_t* __restrict__ off,
                                                                int64_t* __restrict__ nnz,
                                                                const int32_t* __restrict__ master_p,
                                                                int N) {
@@ -215,12 +223,12 @@ __global__ __launch_bounds__(kScanThreads) void offsets_kernel(const int32_t* __
       if (w < wave) pre += wsum[w];
       all += wsum[w];
     }
-    if (r < rows) off[r] = (int32_t)(pre + x - v);
+    if (r < rows) off[r] = (int32_t)min(pre + x - v, (long long)cap);
     carry = all;
     __syncthreads();
   }
   if (tid == 0) {
-    off[rows] = (int32_t)carry;
+    off[rows] = (int32_t)min(carry, (long long)cap);
     const int m = master_p[0];
     nnz[0] = (m < 0 || m >= N) ? -1 : carry;
   }
@@ -375,7 +383,7 @@ hipError_t encode_t(const Dims& d, const int32_t* master, const void* ak, const 
                        count);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(kScanThreads), 0, s, count, rows, diff_off, nnz,
+  hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(kScanThreads), 0, s, count, rows, cap, diff_off, nnz,
                      master, d.N);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -77,7 +77,8 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(
   float2* tab = reinterpret_cast<float2*>(smem);                      // [kAgentChunk][HALF]
   double* invf = reinterpret_cast<double*>(tab + kAgentChunk * TROW);  // [HALF]
   long long* opage = reinterpret_cast<long long*>(invf + HALF);        // [kAgentChunk] (paged)
-  int32_t* sblk = reinterpret_cast<int32_t*>(opage + kAgentChunk);     // [B+1]
+  int32_t* szero = reinterpret_cast<int32_t*>(opage + kAgentChunk);    // [kAgentChunk] Delta == 0
+  int32_t* sblk = szero + kAgentChunk;                                 // [B+1]
 
   const int tid = threadIdx.x;
   const int t0 = blockIdx.x * kTileTok;
@@ -123,8 +124,10 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(
         sincos(delta * invf[e], &sn, &cs);
         tab[a * TROW + tab_col<VEC>(e)] = make_float2((float)cs, (float)sn);
       }
-      if constexpr (PAGED)
-        for (int a = tid; a < na; a += kThreads) opage[a] = page_at(pout, a0 + a, pj);
+      for (int a = tid; a < na; a += kThreads) {
+        if constexpr (PAGED) opage[a] = page_at(pout, a0 + a, pj);
+        szero[a] = dst_pos[(size_t)(a0 + a) * B + b] == sp;
+      }
       __syncthreads();
       // step = (layer, batch of rows)
       u32x4 xl[kItems], xh[kItems], nl[kItems], nh[kItems];
@@ -148,6 +151,22 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(
         const int l = l0 + step / nbatch;
         const int rb = (step % nbatch) * RPP * kItems;
         for (int a = 0; a < na; ++a) {
+          // R(0) is the identity: a zero shift stores the cached bits as
+          // they are (signed zeros and non-finite values included), which
+          // x*1 - y*0 would not (workgroup-uniform branch)
+          if (szero[a]) {
+            E* dst = PAGED ? out + (((size_t)l * pout.n_pages + opage[a]) * kBlock + (ta - t0)) * rowD
+                           : out + ((size_t)(a0 + a) * L + l) * (size_t)T * rowD + (size_t)ta * rowD;
+#pragma unroll
+            for (int k = 0; k < kItems; ++k) {
+              const int r = rb + row_base + k * RPP;
+              if (r < nrows) {
+                st_out(dst + (size_t)r * D + e0, xl[k]);
+                st_out(dst + (size_t)r * D + HALF + e0, xh[k]);
+              }
+            }
+            continue;
+          }
           float cs[VEC], sn[VEC];
 #pragma unroll
           for (int j = 0; j < VEC; ++j) {
@@ -200,7 +219,7 @@ hipError_t launch_t(const Dims& d, const tdx_layout& lay, const void* kc, void* 
   asplit = (d.N + apg - 1) / apg;
   dim3 grid(tiles, groups, asplit);
   const size_t lds = (size_t)kAgentChunk * (D / 2 + 2 * (D / 2 / Fmt<E>::VEC)) * 8 + (D / 2) * 8 +
-                     (size_t)kAgentChunk * 8 + (size_t)(d.B + 1) * 4;
+                     (size_t)kAgentChunk * 8 + (size_t)kAgentChunk * 4 + (size_t)(d.B + 1) * 4;
   hipLaunchKernelGGL((rerotate_kernel<E, D, PAGED>), grid, dim3(kThreads), lds, s,
                      static_cast<const E*>(kc), static_cast<E*>(out), lay.blk_start,
                      lay.src_pos, lay.dst_pos, d.N, d.B, d.T, d.L, d.Hkv, lpg, apg, d.theta, pin, pout);

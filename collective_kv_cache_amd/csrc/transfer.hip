@@ -81,7 +81,8 @@ template <typename E, int D, int NP, bool PAGED>
 __global__ __launch_bounds__(kThreads) void transfer_kernel(
     const E* __restrict__ mk, const E* __restrict__ mv, const int32_t* __restrict__ slot,
     const E* __restrict__ dk, const E* __restrict__ dv, const float2* __restrict__ tab,
-    const int32_t* __restrict__ blk_start, int n_req, int B, int T, int L, int l0, int nl, int Hkv,
+    const int32_t* __restrict__ blk_start, const int32_t* __restrict__ agents, const int32_t* __restrict__ src_pos,
+    const int32_t* __restrict__ dst_pos, int N, int n_req, int B, int T, int L, int l0, int nl, int Hkv,
     E* __restrict__ k_out, E* __restrict__ v_out, PageMap opm) {
   constexpr int VEC = Fmt<E>::VEC;
   constexpr int HALF = D / 2;
@@ -141,6 +142,7 @@ __global__ __launch_bounds__(kThreads) void transfer_kernel(
   for (int j = 0; j < n_req; ++j) {
     const int e = slot[((size_t)j * nl + ll) * nb + beta];  // uniform
     const float2* cs_j = tab + (size_t)j * B * HALF;
+    const int32_t* dst_j = dst_pos + (size_t)min(max(agents[j], 0), N - 1) * B;
     const size_t orow = PAGED ? ((size_t)l * opm.n_pages + page_at(opm, j, beta)) * kTile
                               : ((size_t)j * L + l) * T + t0;
     E* ko = k_out + orow * rowHD;
@@ -157,19 +159,24 @@ __global__ __launch_bounds__(kThreads) void transfer_kernel(
         yl = ld16_nt(dv + off);
         yh = ld16_nt(dv + off + HALF);
       }
-      float x[VEC], y[VEC], ox[VEC], oy[VEC];
-      Fmt<E>::unpack(xl, x);
-      Fmt<E>::unpack(xh, y);
-      const float2* cs = cs_j + (size_t)bb[p] * HALF + e0;
-#pragma unroll
-      for (int q = 0; q < VEC; ++q) {
-        const float2 c = cs[q];
-        ox[q] = x[q] * c.x - y[q] * c.y;
-        oy[q] = y[q] * c.x + x[q] * c.y;
-      }
       const size_t o = (size_t)row * D + e0;
-      st16(ko + o, Fmt<E>::pack(ox));
-      st16(ko + o + HALF, Fmt<E>::pack(oy));
+      if (dst_j[bb[p]] == src_pos[bb[p]]) {  // R(0) is the identity: the stored bits as they are
+        st16(ko + o, xl);
+        st16(ko + o + HALF, xh);
+      } else {
+        float x[VEC], y[VEC], ox[VEC], oy[VEC];
+        Fmt<E>::unpack(xl, x);
+        Fmt<E>::unpack(xh, y);
+        const float2* cs = cs_j + (size_t)bb[p] * HALF + e0;
+#pragma unroll
+        for (int q = 0; q < VEC; ++q) {
+          const float2 c = cs[q];
+          ox[q] = x[q] * c.x - y[q] * c.y;
+          oy[q] = y[q] * c.x + x[q] * c.y;
+        }
+        st16(ko + o, Fmt<E>::pack(ox));
+        st16(ko + o + HALF, Fmt<E>::pack(oy));
+      }
       st16(vo + o, yl);
       st16(vo + o + HALF, yh);
     }
@@ -201,9 +208,9 @@ hipError_t launch_t(const Dims& d, const TransferArgs& t, hipStream_t s) {
 #define TDX_TR(NP)                                                                                         \
   hipLaunchKernelGGL((transfer_kernel<E, D, NP, PAGED>), grid, dim3(kThreads), 0, s,                       \
                      static_cast<const E*>(t.mk), static_cast<const E*>(t.mv), slot,                       \
-                     static_cast<const E*>(t.dk), static_cast<const E*>(t.dv), tab, t.blk_start, t.n_req,  \
-                     d.B, d.T, d.L, t.l0, nl, d.Hkv, static_cast<E*>(t.k_out), static_cast<E*>(t.v_out),   \
-                     t.out_pages)
+                     static_cast<const E*>(t.dk), static_cast<const E*>(t.dv), tab, t.blk_start, t.agents, \
+                     t.src_pos, t.dst_pos, d.N, t.n_req, d.B, d.T, d.L, t.l0, nl, d.Hkv,                   \
+                     static_cast<E*>(t.k_out), static_cast<E*>(t.v_out), t.out_pages)
   if (rows <= RPP) TDX_TR(1);
   else if (rows <= 2 * RPP) TDX_TR(2);
   else if (rows <= 4 * RPP) TDX_TR(4);

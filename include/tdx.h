@@ -35,8 +35,9 @@
  *
  * Conventions shared by every call
  *  - Tensor arguments are DEVICE pointers (tdx_restore_transfer also takes
- *    pinned host storage) to dense row-major arrays owned by the caller; the library allocates and frees nothing and keeps no state
- *    apart from a thread-local error string.  Scratch memory is passed as
+ *    pinned host storage) to dense row-major arrays owned by the caller; the
+ *    library allocates and frees nothing and keeps no state apart from a
+ *    thread-local error string.  Scratch memory is passed as
  *    (ws, ws_bytes), sized by the matching tdx_*_workspace() query.
  *  - Element type of K, V, q and outputs is shape->dtype (fp32 or bf16 bit
  *    patterns).  All tensor pointers must be 16-byte aligned.
@@ -135,6 +136,7 @@ int tdx_select_important(const tdx_shape *shape, const tdx_layout *layout,
                          int32_t *master, void *ws, size_t ws_bytes,
                          void *stream);
 size_t tdx_select_workspace(const tdx_shape *shape, const tdx_layout *layout);
+
 /* ceil(pct * n_tokens / 100) in integer arithmetic, clamped to [1, n_tokens];
  * returns 0 when n_tokens < 1 or pct is outside [0, 100]. */
 int32_t tdx_topk_count(int32_t pct, int32_t n_tokens);
@@ -149,12 +151,17 @@ int32_t tdx_topk_count(int32_t pct, int32_t n_tokens);
  *   master      [1] device int32 (e.g. tdx_select_important output)
  *   agents_k/v  [N][L][T][Hkv][D] canonical-frame caches; T % 16 == 0
  *   cap_blocks  capacity of diff_idx / diff_k / diff_v in blocks (>= 0)
- *   diff_off    [N*L+1] int32, row offsets (always written in full)
+ *   diff_off    [N*L+1] int32, row offsets, always written in full and
+ *               clamped to cap_blocks (diff_off[r] = min(true offset, cap))
  *   diff_idx    [cap] int32, ascending block indices within each row
  *   diff_k/v    [cap][16][Hkv][D]
  *   nnz         [1] int64: the true total; when it exceeds cap_blocks the
  *               entries at positions >= cap_blocks are not written, which the
- *               caller detects by reading nnz (a device-side condition).
+ *               caller detects by reading nnz (a device-side condition).  The
+ *               clamped offsets name written entries only, so an overflowed
+ *               record is still safe to pass to the restore calls (no read
+ *               past the capacity); it is incomplete: the dropped blocks of
+ *               a Mirror restore as the Master's.
  *               nnz = -1 (and every row empty) when *master is not in [0, N).
  *   master_k_out/master_v_out  [L][T][Hkv][D] dense copy of the Master, or
  *               NULL to skip. */
@@ -172,11 +179,12 @@ size_t tdx_diff_encode_workspace(const tdx_shape *shape, const tdx_layout *layou
  * canonical token t is R(Delta(i, b(t))) applied to K~_i[l][t], and K~_i / V~_i
  * are the Master patched with agent i's diff rows.  The patch and the RoPE
  * recovery happen tile by tile inside the attention kernel; no dense Mirror
- * is written (notes §3d "dense materialization zero times", §4; blog §4.4).
+ * is written (notes §3d, §4; blog §4.4).
  *   q          [N][L][Hq][D]
  *   priv_off   [N+1] device int32 offsets into the private arrays
  *   priv_k/v   [L][P_total][Hkv][D], agent i owns rows priv_off[i]..priv_off[i+1]
- *   max_priv   host scalar >= max_i (priv_off[i+1] - priv_off[i])
+ *   max_priv   host scalar >= max_i (priv_off[i+1] - priv_off[i]); a longer
+ *              history is attended only up to its first max_priv tokens
  *   master_k/v the Master's cache, [L][T][Hkv][D] (T % 16 == 0), found at
  *              master_k + m * master_stride elements (same for v), where
  *              m = *master_sel (device int32, clamped to [0, N)) or m = 0 when
@@ -208,7 +216,7 @@ size_t tdx_restore_attn_workspace(const tdx_shape *shape, const tdx_layout *layo
  * [layer_begin, layer_end):
  *   k_out[j][l][t] = round(R(Delta(a, b(t))) K~_a[l][t]),  v_out[j][l][t] = V~_a[l][t]
  * with K~_a / V~_a the Master patched with agent a's diff rows (the same rows
- * tdx_restore_dense writes for agent a).  Layers outside the range are not
+ * tdx_restore_dense writes for agent a; a zero shift copies the bits).  Layers outside the range are not
  * written.  The kernels read the Master and the diff record directly where
  * they are, so they may sit in pinned host memory (hipHostMalloc, or a
  * pinned torch tensor: the reads then cross PCIe, once per block for all
@@ -236,7 +244,9 @@ size_t tdx_restore_transfer_workspace(const tdx_shape *shape, const tdx_layout *
 /* ---- a6: dense comparator --------------------------------------------------
  * tdx_restore_dense writes every agent's full cache:
  *   k_dense[i][l][t] = round(R(Delta(i, b(t))) K~_i[l][t]), v_dense[i][l][t] = V~_i[l][t]
- * ([N][L][T][Hkv][D] each; inputs as for tdx_restore_attn).
+ * ([N][L][T][Hkv][D] each; inputs as for tdx_restore_attn).  R(0) is the
+ * identity: the K rows of a block with Delta = 0 are copied bit for bit (as
+ * in tdx_rerotate and tdx_restore_transfer).
  * tdx_decode_attn_dense then runs plain decode attention of agent i over its
  * private keys followed by k_dense[i] / v_dense[i] (outputs as tdx_restore_attn).
  * Together they are the dense restore-then-attend path the fused restore is

@@ -18,7 +18,9 @@ Pins (tests/test_oracle_paged.py): an identity page table reduces gather to a
 reshape of the pool; scatter/gather round trips leave untouched pages and the
 unused rows of a partial page as they were; clamping of out-of-range IDs;
 the paged re-rotation on shuffled pages equals the contiguous definition;
-every diff entry's page holds the entry's values; the paged
+the paged deviation on shuffled pages (one clamped ID) equals the contiguous
+deviation of the original arrays at the check layer; every diff entry's page
+holds the entry's values; the paged
 restore-attention on shuffled pages equals the contiguous oracle on the
 original arrays.  No function here is "parity unpinned".
 """

@@ -107,14 +107,21 @@ def rope_inv_freq(head_dim: int, theta: float) -> np.ndarray:
 def rope_rotate(x: np.ndarray, pos, theta: float) -> np.ndarray:
     """Rotate float64 vectors x[..., D] by positions ``pos`` (broadcast over
     the leading axes of x): pair (x_e, x_{e+D/2}) at angle pos * inv_freq_e
-    becomes (x_e cos - x_{e+D/2} sin, x_{e+D/2} cos + x_e sin)."""
+    becomes (x_e cos - x_{e+D/2} sin, x_{e+D/2} cos + x_e sin).
+
+    R(0) is the identity, so a vector at position 0 is returned exactly as
+    given: its signed zeros and non-finite entries included, which the
+    products x*1 - y*0 would turn into +0 or NaN."""
     x = np.asarray(x, dtype=np.float64)
     D = x.shape[-1]
     half = D // 2
-    ang = np.asarray(pos, dtype=np.float64)[..., None] * rope_inv_freq(D, theta)
+    p = np.asarray(pos, dtype=np.float64)
+    ang = p[..., None] * rope_inv_freq(D, theta)
     c, s = np.cos(ang), np.sin(ang)
     lo, hi = x[..., :half], x[..., half:]
-    return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
+    with np.errstate(invalid="ignore"):
+        out = np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
+    return np.where((p == 0)[..., None], x, out)
 
 
 # ---------------------------------------------------------------------------

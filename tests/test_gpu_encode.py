@@ -9,7 +9,7 @@ import oracle as O
 from collective_kv_cache_amd import tdx
 from workload import CONFIGS, make_layout, cached_kv, agent_caches, mirror_blocks, to_numpy_bits
 
-from gpu_common import DEV, dlayout, host, shape_of
+from gpu_common import DEV, Round, assert_close, dlayout, host, shape_of
 
 pytestmark = pytest.mark.gpu
 
@@ -24,7 +24,9 @@ def _compare(ds, ref, L, cap=None):
     off, idx, dk, dv = ref
     nnz = ds.nnz()
     assert nnz == int(off[-1])
-    np.testing.assert_array_equal(host(ds.off).astype(np.int64), off)
+    # row offsets are clamped to the capacity; nnz keeps the true total
+    want_off = off if cap is None else np.minimum(off, cap)
+    np.testing.assert_array_equal(host(ds.off).astype(np.int64), want_off)
     n = nnz if cap is None else min(nnz, cap)
     np.testing.assert_array_equal(host(ds.idx)[:n], idx[:n])
     np.testing.assert_array_equal(host(ds.k)[:n], dk[:n])
@@ -89,6 +91,41 @@ def test_encode_capacity_overflow_reports_true_total():
     with pytest.raises(tdx.TdxError):
         tdx.diff_encode(shape_of(cfg), dlayout(lay), torch.tensor([3], dtype=torch.int32, device=DEV),
                         ak.to(DEV), av.to(DEV), cap_blocks=cap, check=True)
+
+
+def test_overflowed_record_restores_as_truncated():
+    # a record whose blocks overflow the capacity names only written entries
+    # (offsets clamped), so the fused and dense restores and the transfer
+    # restore read inside it; their outputs equal the oracle run on the
+    # truncated record (the first cap entries, offsets min(off, cap))
+    import math
+
+    cfg = CONFIGS["qwen7b_round"].scaled(n_layers=2, n_agents=5)
+    lay = make_layout(cfg)
+    r = Round(cfg, lay, master=2)
+    h = {k: to_numpy_bits(v) for k, v in r.host.items()}
+    off, idx, dk, dv = O.diff_encode(h["ak"], h["av"], 2)
+    cap = int(off[-1]) // 2
+    m = torch.tensor([2], dtype=torch.int32, device=DEV)
+    ds = tdx.diff_encode(r.shape, r.dl, m, r.dev["ak"], r.dev["av"], cap_blocks=cap, check=False)
+    assert ds.nnz() == int(off[-1]) > cap
+    toff = np.minimum(off, cap)
+    np.testing.assert_array_equal(host(ds.off).astype(np.int64), toff)
+    d = r.dev
+    fused = tdx.restore_attn(r.shape, r.dl, d["q"], d["po"], d["pk"], d["pv"], r.max_priv, ds.master_k,
+                             ds.master_v, ds)
+    kd, vd = tdx.restore_dense(r.shape, r.dl, ds.master_k, ds.master_v, ds)
+    ag = torch.arange(cfg.n_agents, dtype=torch.int32, device=DEV)
+    ko, vo = tdx.restore_transfer(r.shape, r.dl, ds.master_k, ds.master_v, ds.off, ds.idx, ds.k, ds.v, ag)
+    args = (lay.blk_start, lay.src_pos, lay.dst_pos, cfg.theta)
+    ref = O.restore_attn(h["q"], lay.priv_off, h["pk"], h["pv"], h["kc"], h["vc"], toff, idx[:cap], dk[:cap],
+                         dv[:cap], *args, 1.0 / math.sqrt(cfg.head_dim))
+    rkd, rvd = O.restore_dense(h["kc"], h["vc"], toff, idx[:cap], dk[:cap], dv[:cap], *args)
+    assert_close(host(fused), ref, "fused restore of a truncated record")
+    assert_close(host(kd), rkd, "dense K of a truncated record")
+    np.testing.assert_array_equal(host(vd), rvd)
+    np.testing.assert_array_equal(host(ko), host(kd))
+    np.testing.assert_array_equal(host(vo), rvd)
 
 
 @pytest.mark.parametrize("name", ["qwen14b_round", "qwen7b_scaleout"])

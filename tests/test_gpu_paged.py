@@ -18,7 +18,8 @@ import oracle as O
 from collective_kv_cache_amd import tdx
 from workload import CONFIGS, make_layout, recomputed_k, to_numpy_bits
 
-from gpu_common import DEV, Round, assert_close, dlayout, host, shape_of
+from gpu_common import (DEV, Round, assert_close, assert_master, assert_scores, assert_selection, dlayout, host,
+                        shape_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -140,6 +141,12 @@ def test_select_paged(name, kw):
     torch.cuda.synchronize()
     for key in ("dev", "score", "agent_dev", "selected", "master"):
         assert torch.equal(got[key], col[key]), key
+    # and the paged oracle (the sequences gathered out of their pages)
+    d_ref, s_ref, a_ref = O.paged.deviation_paged(to_numpy_bits(pool), host(pages), check, to_numpy_bits(kx), T)
+    assert_scores(host(got["dev"]), d_ref.astype(np.float32), "paged dev")
+    assert_scores(host(got["score"]), s_ref.astype(np.float32), "paged score")
+    assert_selection(host(got["selected"]), s_ref.astype(np.float32), k)
+    assert_master(int(host(got["master"])[0]), a_ref.astype(np.float32))
 
 
 @pytest.mark.parametrize("name,kw", CASES + [("qwen7b_scaleout", dict(n_layers=1, n_agents=6, n_blocks=8))])

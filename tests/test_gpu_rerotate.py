@@ -93,3 +93,41 @@ def test_rerotate_deterministic():
     b = tdx.rerotate(shape_of(cfg), dlayout(lay), kc)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_zero_shift_keeps_special_values(dtype):
+    # R(0) is the identity: re-rotation, the dense restore and the transfer
+    # restore store a zero-shift block's bits as they are, also -0 elements
+    # with a negative rotate-half partner and infinite elements (x*1 - y*0
+    # would give +0 and NaN); agent 0 has zero shifts, the others do not
+    cfg = CONFIGS["tiny"].scaled(dtype=dtype, n_layers=2)
+    lay = make_layout(cfg)
+    N, L, T, H, D = cfg.n_agents, cfg.n_layers, lay.n_tokens, cfg.n_kv_heads, cfg.head_dim
+    dst = lay.dst_pos.copy()
+    dst[0] = lay.src_pos
+    dl = tdx.RoundLayout(lay.blk_start, lay.src_pos, dst, DEV)
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn((L, T, H, D), generator=g)
+    x[..., 0] = -0.0
+    x[..., D // 2] = -1.5
+    x[0, 3, 1, 5] = float("inf")
+    x[1, 20, 0, 6] = float("-inf")
+    kc = x.to(cfg.torch_dtype).to(DEV)
+    vc = torch.randn((L, T, H, D), generator=g).to(cfg.torch_dtype).to(DEV)
+    bits = (lambda t: t.view(torch.int16)) if dtype == "bf16" else (lambda t: t.view(torch.int32))
+    shape = shape_of(cfg)
+    kr = tdx.rerotate(shape, dl, kc)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(kr[0]), bits(kc))
+    # a round whose agents all hold the Master: an empty record
+    ak = kc.unsqueeze(0).repeat(N, 1, 1, 1, 1).contiguous()
+    av = vc.unsqueeze(0).repeat(N, 1, 1, 1, 1).contiguous()
+    ds = tdx.diff_encode(shape, dl, torch.zeros(1, dtype=torch.int32, device=DEV), ak, av)
+    assert ds.nnz() == 0
+    kd, vd = tdx.restore_dense(shape, dl, ds.master_k, ds.master_v, ds)
+    ko, vo = tdx.restore_transfer(shape, dl, ds.master_k, ds.master_v, ds.off, ds.idx, ds.k, ds.v,
+                                  torch.zeros(1, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(bits(kd[0]), bits(kc)) and torch.equal(bits(vd[0]), bits(vc))
+    assert torch.equal(bits(ko[0]), bits(kc)) and torch.equal(bits(vo[0]), bits(vc))

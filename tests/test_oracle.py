@@ -182,6 +182,34 @@ def test_rerotate_zero_shift_is_bitwise_copy(dt):
         np.testing.assert_array_equal(out[i].view(np.uint8), kc.view(np.uint8))
 
 
+@pytest.mark.parametrize("dt", [np.uint16, np.float32])
+def test_zero_shift_keeps_signed_zeros_and_infinities(dt):
+    # R(0) is the identity: a zero-shift block is its stored bits, also where
+    # the element is -0 with a negative rotate-half partner (x*1 - y*0 would
+    # give +0) or the partner is infinite (y*0 would give NaN); blocks with a
+    # non-zero shift of the same round are rotated as usual
+    rng = np.random.default_rng(61)
+    bs, src, dst = _layout([16, 16], [0, 16], [[0, 16], [5, 16]])
+    x = rng.standard_normal((1, 32, 2, 8))
+    x[0, :, :, 0] = -0.0
+    x[0, :, :, 4] = -1.5  # partner of dim 0
+    x[0, 3, 1, 5] = np.inf
+    x[0, 20, 0, 6] = -np.inf
+    kc = O.narrow(x, dt)
+    out = O.rerotate(kc, bs, src, dst, 1e4)
+    np.testing.assert_array_equal(out[0].view(np.uint8), kc.view(np.uint8))  # agent 0: zero shifts
+    np.testing.assert_array_equal(out[1, :, 16:].view(np.uint8), kc[:, 16:].view(np.uint8))
+    # the non-zero shift of agent 1's first block rotates it (the infinite
+    # element spreads to its pair partner)
+    moved = O.widen(out[1, 0, :16])
+    assert np.mean(out[1, :, :16] != kc[:, :16]) > 0.5 and np.isinf(moved[3, 1, [1, 5]]).all()
+    # the dense restore of a round without diffs is the same copy
+    kd, vd = O.restore_dense(kc, kc, np.zeros(3, np.int64), np.zeros(0, np.int32),
+                             np.zeros((0, 16, 2, 8), kc.dtype), np.zeros((0, 16, 2, 8), kc.dtype),
+                             bs, src, np.asarray([[0, 16]], np.int32), 1e4)
+    np.testing.assert_array_equal(kd[0].view(np.uint8), kc.view(np.uint8))
+
+
 def test_rerotate_there_and_back_bf16():
     rng = np.random.default_rng(7)
     bs, src, dst = _layout([64], [0], [[5000]])

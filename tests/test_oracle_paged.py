@@ -4,6 +4,7 @@ A paged call is the contiguous call on the sequences gathered out of their
 pages.  Pinned here by: the identity page table reducing to a reshape of the
 pool, scatter/gather round trips, permutation invariance of the whole
 restore-attention against the contiguous oracle on the original arrays, the
+paged deviation against the contiguous deviation at the check layer, the
 content of every diff entry's page, untouched pages staying untouched, and
 clamping of out-of-range page IDs.
 """
@@ -47,6 +48,38 @@ def test_out_of_range_ids_are_clamped():
     pool = _pool(rng, 1, 4, 1, 8)
     np.testing.assert_array_equal(P.gather(pool, [-3, 99], 32),
                                   np.concatenate([pool[:, 0], pool[:, 3]], axis=1))
+
+
+def test_deviation_paged_reads_each_agents_pages_at_the_check_layer():
+    # three agents' reused K (two layers, 40 tokens: a partial last page) laid
+    # into shuffled pages of one pool by plain indexing, one used entry out of
+    # range (it clamps to the last page, which holds that page's rows); the
+    # paged deviation equals the contiguous one on the original arrays at the
+    # check layer.  A wrong layer, agent row, page or in-page row changes it.
+    rng = np.random.default_rng(31)
+    N, L, T, H, D = 3, 2, 40, 2, 8
+    npg = 3
+    n_pages = N * npg + 2
+    kr = O.f64_to_bf16(rng.standard_normal((N, L, T, H, D)))
+    kx = O.f64_to_bf16(rng.standard_normal((N, T, H, D)))
+    pool = O.f64_to_bf16(rng.standard_normal((L, n_pages, 16, H, D)))
+    perm = rng.permutation(n_pages - 1)  # page n_pages - 1 is placed by hand
+    pages = np.full((N, npg + 1), -7, np.int64)  # the spare column is never read
+    k = 0
+    for i in range(N):
+        for j in range(npg):
+            pid = n_pages - 1 if (i, j) == (1, 2) else int(perm[k])
+            k += (i, j) != (1, 2)
+            pages[i, j] = n_pages + 5 if (i, j) == (1, 2) else pid
+            n = min(16, T - 16 * j)
+            pool[:, pid, :n] = kr[i, :, 16 * j:16 * j + n]
+    for check in (0, 1):
+        got = P.deviation_paged(pool, pages, check, kx, T)
+        want = O.deviation(kr[:, check], kx)
+        for g, w in zip(got, want):
+            np.testing.assert_array_equal(g, w)
+    # the other layer's deviation is a different answer (the pin can fail)
+    assert not np.array_equal(P.deviation_paged(pool, pages, 0, kx, T)[0], O.deviation(kr[:, 1], kx)[0])
 
 
 def _round(rng, N=3, L=2, H=2, D=8, lens=(16, 32, 16)):
