@@ -3,9 +3,15 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "common.h"
+
+// Scratch of tdx_select_important_noalloc: one copy per GPU, resident until
+// the process ends.  In host code this name is only a stand-in for the
+// device symbol; its device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[TDX_SELECT_SCRATCH_BYTES];
 
 namespace {
 
@@ -163,12 +169,14 @@ size_t tdx_select_workspace(const tdx_shape* shape, const tdx_layout* layout) {
   return tdx::select_ws_bytes(d);
 }
 
-int tdx_select_important(const tdx_shape* shape, const tdx_layout* layout, int32_t check_layer,
-                         const void* k_reuse, const void* k_recomp, int32_t k, float* dev,
-                         float* score, float* agent_dev, int32_t* selected, int32_t* master,
-                         void* ws, size_t ws_bytes, void* stream) {
-  GUARD_BEGIN
-  tdx::Dims d{};
+}  // extern "C"
+
+namespace {
+// Argument checks shared by tdx_select_important and its no-allocation variant.
+int check_select(const tdx_shape* shape, const tdx_layout* layout, int32_t check_layer, const void* k_reuse,
+                 const void* k_recomp, int32_t k, const float* dev, const float* score, const float* agent_dev,
+                 const int32_t* selected, const int32_t* master, tdx::Dims* dd) {
+  tdx::Dims& d = *dd;
   int rc;
   if ((rc = check_shape(shape, &d)) != TDX_OK) return rc;
   if ((rc = check_layout(layout, &d, false)) != TDX_OK) return rc;
@@ -181,6 +189,68 @@ int tdx_select_important(const tdx_shape* shape, const tdx_layout* layout, int32
   REQ_PTR4(agent_dev);
   REQ_PTR4(selected);
   REQ_PTR4(master);
+  return TDX_OK;
+}
+
+// Device address of `scratch` on the calling thread's current device, looked
+// up once per device (the symbol's address differs from GPU to GPU).
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+int scratch_on_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  REQ(dev >= 0 && dev < kMaxScratchDevices, TDX_EUNSUPPORTED, "device %d beyond the %d the scratch table serves", dev,
+      kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    REQ(p != nullptr && aligned16(p), TDX_EINTERNAL, "scratch address %p is null or unaligned", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TDX_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int tdx_select_important_noalloc(const tdx_shape* shape, const tdx_layout* layout, int32_t check_layer,
+                                 const void* k_reuse, const void* k_recomp, int32_t k, float* dev, float* score,
+                                 float* agent_dev, int32_t* selected, int32_t* master, void* stream) {
+  GUARD_BEGIN
+  tdx::Dims d{};
+  int rc;
+  if ((rc = check_select(shape, layout, check_layer, k_reuse, k_recomp, k, dev, score, agent_dev, selected, master,
+                         &d)) != TDX_OK)
+    return rc;
+  const size_t need = tdx::select_ws_bytes(d);
+  REQ(need <= (size_t)TDX_SELECT_SCRATCH_BYTES, TDX_EUNSUPPORTED,
+      "the round needs %zu bytes of scratch, more than the static %zu (N * ceil(T/4) * 8 bytes)", need,
+      (size_t)TDX_SELECT_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((rc = scratch_on_current_device(&ws)) != TDX_OK) return rc;
+  hipError_t e = tdx::launch_select(d, *layout, check_layer, k_reuse, k_recomp, k, dev, score, agent_dev, selected,
+                                    master, ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tdx_select_important_noalloc launch");
+  return ok();
+  GUARD_END
+}
+
+int tdx_select_important(const tdx_shape* shape, const tdx_layout* layout, int32_t check_layer,
+                         const void* k_reuse, const void* k_recomp, int32_t k, float* dev,
+                         float* score, float* agent_dev, int32_t* selected, int32_t* master,
+                         void* ws, size_t ws_bytes, void* stream) {
+  GUARD_BEGIN
+  tdx::Dims d{};
+  int rc;
+  if ((rc = check_select(shape, layout, check_layer, k_reuse, k_recomp, k, dev, score, agent_dev, selected, master,
+                         &d)) != TDX_OK)
+    return rc;
   const size_t need = tdx::select_ws_bytes(d);
   REQ(ws != nullptr && aligned16(ws) && ws_bytes >= need, TDX_EWORKSPACE,
       "workspace needs %zu bytes (16-byte aligned), got %zu", need, ws_bytes);

@@ -69,6 +69,7 @@ _SIGS = {
     "tdx_rerotate": (ctypes.c_int, [_PS, _PL, _P, _P, _P]),
     "tdx_select_workspace": (_SZ, [_PS, _PL]),
     "tdx_select_important": (ctypes.c_int, [_PS, _PL, _I32, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "tdx_select_important_noalloc": (ctypes.c_int, [_PS, _PL, _I32, _P, _P, _I32, _P, _P, _P, _P, _P, _P]),
     "tdx_diff_encode_workspace": (_SZ, [_PS, _PL]),
     "tdx_diff_encode": (ctypes.c_int, [_PS, _PL, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "tdx_restore_attn_workspace": (_SZ, [_PS, _PL, _I32]),
@@ -245,6 +246,35 @@ def select_important(shape: Shape, lay: RoundLayout, k_reuse: torch.Tensor, k_re
         ctypes.byref(s), ctypes.byref(l), int(check_layer), _ptr(k_reuse), _ptr(k_recomp), int(k),
         _ptr(out["dev"]), _ptr(out["score"]), _ptr(out["agent_dev"]), _ptr(out["selected"]),
         _ptr(out["master"]), _ptr(ws), ws.numel(), _stream()), "tdx_select_important")
+    return out
+
+
+SELECT_SCRATCH_BYTES = 4 << 20  # TDX_SELECT_SCRATCH_BYTES
+
+
+def select_important_noalloc(shape: Shape, lay: RoundLayout, k_reuse: torch.Tensor, k_recomp: torch.Tensor,
+                             k: int, check_layer: int = 0, out: Optional[dict] = None) -> dict:
+    """a2 + a3 without a workspace argument: the library's static scratch
+    array of the current device serves it (``tdx_select_important_noalloc``).
+    Outputs as :func:`select_important`; with ``out`` given, nothing is
+    allocated on this call."""
+    N, L, T, H, D = lay.n_agents, shape.n_layers, lay.n_tokens, shape.n_kv_heads, shape.head_dim
+    dev_ = lay.device
+    _need(k_reuse, "k_reuse", shape.dtype, (N, L, T, H, D), dev_)
+    _need(k_recomp, "k_recomp", shape.dtype, (N, T, H, D), dev_)
+    if out is None:
+        out = dict(
+            dev=torch.empty((N, T), dtype=torch.float32, device=dev_),
+            score=torch.empty((T,), dtype=torch.float32, device=dev_),
+            agent_dev=torch.empty((N,), dtype=torch.float32, device=dev_),
+            selected=torch.empty((max(int(k), 1),), dtype=torch.int32, device=dev_),
+            master=torch.empty((1,), dtype=torch.int32, device=dev_),
+        )
+    s, l = shape.c(), lay.c()
+    _check(lib().tdx_select_important_noalloc(
+        ctypes.byref(s), ctypes.byref(l), int(check_layer), _ptr(k_reuse), _ptr(k_recomp), int(k),
+        _ptr(out["dev"]), _ptr(out["score"]), _ptr(out["agent_dev"]), _ptr(out["selected"]),
+        _ptr(out["master"]), _stream()), "tdx_select_important_noalloc")
     return out
 
 

@@ -37,7 +37,8 @@
  *  - Tensor arguments are DEVICE pointers (tdx_restore_transfer also takes
  *    pinned host storage) to dense row-major arrays owned by the caller; the
  *    library allocates and frees nothing and keeps no state apart from a
- *    thread-local error string.  Scratch memory is passed as
+ *    thread-local error string and the static scratch array of
+ *    tdx_select_important_noalloc.  Scratch memory is passed as
  *    (ws, ws_bytes), sized by the matching tdx_*_workspace() query.
  *  - Element type of K, V, q and outputs is shape->dtype (fp32 or bf16 bit
  *    patterns).  All tensor pointers must be 16-byte aligned.
@@ -137,6 +138,28 @@ int tdx_select_important(const tdx_shape *shape, const tdx_layout *layout,
                          void *stream);
 size_t tdx_select_workspace(const tdx_shape *shape, const tdx_layout *layout);
 
+/* tdx_select_important for callers that cannot allocate device memory: code
+ * under HIP graph capture, serving loops and harnesses that forbid hipMalloc.
+ * Same arguments, outputs and checks as tdx_select_important minus the
+ * workspace: the scratch (tdx_select_workspace bytes) is a static device
+ * array of TDX_SELECT_SCRATCH_BYTES inside the library, one per GPU, held
+ * until the process ends.  The call allocates nothing; it uses the array of
+ * the calling thread's current device (stream must belong to that device).
+ *  - A round whose workspace exceeds TDX_SELECT_SCRATCH_BYTES is rejected
+ *    with TDX_EUNSUPPORTED before anything is enqueued.
+ *  - The first call on a device looks the array's address up once (a HIP
+ *    runtime query, no allocation); a failure returns TDX_EHIP.
+ *  - Every call on one GPU shares that GPU's array: calls that overlap on
+ *    one GPU (two streams, two threads) race and must be serialised by the
+ *    caller.  Nothing in the array needs to start at zero; each call
+ *    overwrites what it reads. */
+#define TDX_SELECT_SCRATCH_BYTES (4u << 20) /* 4 MiB: N * ceil(T / 4) * 8 bytes */
+int tdx_select_important_noalloc(const tdx_shape *shape, const tdx_layout *layout,
+                                 int32_t check_layer, const void *k_reuse,
+                                 const void *k_recomp, int32_t k, float *dev,
+                                 float *score, float *agent_dev,
+                                 int32_t *selected, int32_t *master,
+                                 void *stream);
 /* ceil(pct * n_tokens / 100) in integer arithmetic, clamped to [1, n_tokens];
  * returns 0 when n_tokens < 1 or pct is outside [0, 100]. */
 int32_t tdx_topk_count(int32_t pct, int32_t n_tokens);

@@ -232,3 +232,17 @@ def test_paged_transfer_rejects_bad_arguments():
     assert tr(_paged(v_pool=None)) == tdx.TDX_EINVAL   # K and V are both written
     assert tr(_paged(stride=3)) == tdx.TDX_EINVAL      # 2 rows of 4 pages
     assert tr(_paged(), n_req=0) == tdx.TDX_EINVAL
+
+
+def test_noalloc_select_rejects_rounds_beyond_its_scratch():
+    # N * ceil(T/4) * 8 bytes above TDX_SELECT_SCRATCH_BYTES: refused before
+    # anything reaches the HIP runtime (aligned fake pointers, never read)
+    big = _layout(n_agents=1024, n_blocks=4, n_tokens=8192)
+    rc = tdx.lib().tdx_select_important_noalloc(ctypes.byref(_shape(n_layers=1)), ctypes.byref(big), 0, FAKE, FAKE,
+                                                10, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert rc == tdx.TDX_EUNSUPPORTED
+    assert b"scratch" in tdx.lib().tdx_last_error()
+    # and the shared argument checks run first
+    rc = tdx.lib().tdx_select_important_noalloc(ctypes.byref(_shape(n_layers=1)), ctypes.byref(big), 1, FAKE, FAKE,
+                                                10, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert rc == tdx.TDX_EINVAL
