@@ -11,7 +11,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["api.hip", "rerotate.hip", "select.hip", "encode.hip", "attn.hip", "transfer.hip", "round.cpp"]
+SOURCES = ["api.hip", "rerotate.hip", "select.hip", "encode.hip", "attn.hip", "attn_f32.hip", "transfer.hip",
+           "round.cpp"]
 LIB = os.path.join(HERE, "libtdx.so")
 
 FLAGS = [

@@ -32,8 +32,10 @@
 // query row), online softmax with rows in lanes, O^T += V^T P^T with
 // v_mfma_f32_16x16x16_bf16.  The dense comparator's attention is agent_kernel
 // reading the materialised caches instead of diff records.
-// Operands are bf16 (fp32 K/V/q are rounded to bf16 for the MFMA); softmax,
-// accumulation and the merge run in fp32.
+// These kernels serve bf16 caches: the operands are the stored bf16 values
+// (and bf16 softmax weights), softmax, accumulation and the merge run in
+// fp32.  fp32 caches take the fp32 vector-unit kernels of attn_f32.hip,
+// which round nothing to bf16.
 #include "common.h"
 
 namespace tdx {
@@ -57,39 +59,11 @@ constexpr int kRowsPerGroup = 16 * kShWaves;
 constexpr int kMaxSharedTiles = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
-enum Mode { FUSED = 0, DENSE = 1 };
 
 // ---- bf16 operand helpers ---------------------------------------------------
 
-// 8 consecutive elements -> 8 floats
-template <typename E>
-__device__ __forceinline__ void load8(const E* p, float* x);
-template <>
-__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float* x) {
-  Fmt<uint16_t>::unpack(ld16(p), x);
-}
-template <>
-__device__ __forceinline__ void load8<float>(const float* p, float* x) {
-  Fmt<float>::unpack(ld16(p), x);
-  Fmt<float>::unpack(ld16(p + 4), x + 4);
-}
-
-// 8 consecutive elements as packed bf16 (4 dwords); bf16 input is passed through
-template <typename E>
-__device__ __forceinline__ u32x4 load8_bf16(const E* p);
-template <>
-__device__ __forceinline__ u32x4 load8_bf16<uint16_t>(const uint16_t* p) {
-  return ld16(p);
-}
-template <>
-__device__ __forceinline__ u32x4 load8_bf16<float>(const float* p) {
-  float x[8];
-  load8<float>(p, x);
-  u32x4 v;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) v[k] = pack_bf16(x[2 * k], x[2 * k + 1]);
-  return v;
-}
+// 8 consecutive bf16 elements -> 8 floats
+__device__ __forceinline__ void load8(const uint16_t* p, float* x) { Fmt<uint16_t>::unpack(ld16(p), x); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
   bf16x8 r;
@@ -114,13 +88,6 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
-// Element offset of the Master's cache: (*sel clamped to [0, N)) * stride,
-// 0 without a selector.
-__device__ __forceinline__ size_t master_offset(const int32_t* sel, long long stride, int N) {
-  if (sel == nullptr) return 0;
-  const int m = min(max(sel[0], 0), N - 1);
-  return (size_t)m * (size_t)stride;
-}
 
 // Largest b in [0, B) with blk[b] <= t (the block holding token t; skips
 // empty blocks).  blk is an LDS copy of blk_start.
@@ -170,7 +137,7 @@ struct AttnArgs {
   const void* dv;
   const int32_t* blk_start;  // [B+1]
   const float2* tab;         // fused: [N][B][D/2] cos/sin of each shift
-  const uint16_t* qplain;    // [N][L][Hq][D] bf16 queries (the input itself when it is bf16)
+  const uint16_t* qplain;    // [N][L][Hq][D] bf16 queries (the input q)
   float* part;               // [N][L][Hq][S][D+4]: m, l, -, -, O[D]
   unsigned char* ws_base;    // the workspace (task list, per-diff-entry cos/sin rows)
   int N, L, T, B, Hkv, Hq;
@@ -336,6 +303,7 @@ __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(TDX_
   constexpr int CH = St::CH;
   constexpr int CPT = St::CPT;
   constexpr int LPC = St::LPC;
+  static_assert(sizeof(E) == 2, "bf16 caches (fp32 ones take the fp32 kernel)");
   static_assert(2 * kTile * CH % kShThreads == 0, "tile chunks per thread");
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* kbuf = reinterpret_cast<uint16_t*>(smem);  // [2][16][VS]
@@ -425,17 +393,7 @@ __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(TDX_
       const int tensor = idx / (kTile * CH);
       const int rem = idx % (kTile * CH);
       uint16_t* dst = (tensor ? vbuf : kbuf) + (buf * kTile + rem / CH) * VS + (rem % CH) * 8;
-      u32x4 v;
-      if constexpr (sizeof(E) == 2) {
-        v = S.kv[c];
-      } else {
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          v[2 * p] = pack_bf16(__uint_as_float(S.kv[2 * c + p][0]), __uint_as_float(S.kv[2 * c + p][1]));
-          v[2 * p + 1] = pack_bf16(__uint_as_float(S.kv[2 * c + p][2]), __uint_as_float(S.kv[2 * c + p][3]));
-        }
-      }
-      *reinterpret_cast<u32x4*>(dst) = v;
+      *reinterpret_cast<u32x4*>(dst) = S.kv[c];
     }
   };
 
@@ -451,16 +409,12 @@ __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(TDX_
     u32x4 qr[KD];
     {
       const float2* cs = tabrow + (size_t)b * HALF;
-      // fp32 rows are read again for every block rather than held across
-      // blocks (32 more registers than the kernel's budget allows)
-      const E* qp = qrow;
-      if constexpr (sizeof(E) == 4) asm volatile("" : "+v"(qp));
 #pragma unroll
       for (int k = 0; k < KD / 2; ++k) {
         const int e0 = 32 * k + 8 * q4;
         float lo[8], hi[8], olo[8], ohi[8];
-        load8<E>(qp + e0, lo);
-        load8<E>(qp + HALF + e0, hi);
+        load8(qrow + e0, lo);
+        load8(qrow + HALF + e0, hi);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float2 c = cs[e0 + j];
@@ -699,6 +653,7 @@ template <typename E, int D, int MODE, int PD, bool PAGED>
 __global__ __launch_bounds__(kStreamNW * kWave) __attribute__((amdgpu_waves_per_eu(TDX_ST_WPE))) void stream_kernel(
     AttnArgs a, const StreamTask* __restrict__ tasks, const int32_t* __restrict__ ctl, const float2* __restrict__ dcs,
     const int2* __restrict__ dinfo) {
+  static_assert(sizeof(E) == 2, "bf16 caches (fp32 ones take the fp32 kernel)");
   using St = Stage<E, D, MODE>;
   constexpr int KD = St::KD;
   constexpr int DT = D / 16;
@@ -847,36 +802,19 @@ __global__ __launch_bounds__(kStreamNW * kWave) __attribute__((amdgpu_waves_per_
     for (int v = 0; v < St::NV; ++v) {
       const int p = v * kWave + lane;
       *reinterpret_cast<u32x4*>(kl + klds_off<CPR>(p / CPR, p % CPR)) = S.k[v];
-      if constexpr (sizeof(E) == 2) {
-        *reinterpret_cast<u32x4*>(vl + vlds_off<D>(p / CPR, p % CPR)) = S.v[v];
-      } else {
-        const int t = p / CPR, c4 = p % CPR;  // fp32 chunk = dims 4*c4 .. +3
-        uint2 w;
-        w.x = pack_bf16(__uint_as_float(S.v[v][0]), __uint_as_float(S.v[v][1]));
-        w.y = pack_bf16(__uint_as_float(S.v[v][2]), __uint_as_float(S.v[v][3]));
-        *reinterpret_cast<uint2*>(vl + vlds_off<D>(t, c4 / 2) + (c4 % 2) * 8) = w;
-      }
+      *reinterpret_cast<u32x4*>(vl + vlds_off<D>(p / CPR, p % CPR)) = S.v[v];
     }
     const bool rot = MODE == FUSED && u >= PT.ntp;  // the agent's own block (wave-uniform)
     if (MODE == FUSED && lane < HALF) csl[lane] = S.cs;
     wave_sync();
     // K operand of the QK product: kop[k] = K[row c16][32k + 8*q4 .. +7] as bf16
     u32x4 kop[KD];
-    if constexpr (sizeof(E) == 2) {
 #pragma unroll
-      for (int k = 0; k < KD; ++k) kop[k] = *reinterpret_cast<const u32x4*>(kl + klds_off<CPR>(c16, 4 * k + q4));
-    }
-    if (sizeof(E) == 4 || rot) {
+    for (int k = 0; k < KD; ++k) kop[k] = *reinterpret_cast<const u32x4*>(kl + klds_off<CPR>(c16, 4 * k + q4));
+    if (rot) {
       float x[KD][8];
 #pragma unroll
-      for (int k = 0; k < KD; ++k) {
-        if constexpr (sizeof(E) == 2) {
-          Fmt<uint16_t>::unpack(kop[k], x[k]);
-        } else {
-          Fmt<float>::unpack(*reinterpret_cast<const u32x4*>(kl + klds_off<CPR>(c16, 8 * k + 2 * q4)), x[k]);
-          Fmt<float>::unpack(*reinterpret_cast<const u32x4*>(kl + klds_off<CPR>(c16, 8 * k + 2 * q4 + 1)), x[k] + 4);
-        }
-      }
+      for (int k = 0; k < KD; ++k) Fmt<uint16_t>::unpack(kop[k], x[k]);
       // rotate this lane's key row by the shift of the shared block holding
       // it; pairs (e, e + D/2) are chunks k and k + KD/2
       auto rotate = [&](auto row) {
@@ -894,11 +832,11 @@ __global__ __launch_bounds__(kStreamNW * kWave) __attribute__((amdgpu_waves_per_
           kop[k + KD / 2] = Fmt<uint16_t>::pack(x[k + KD / 2]);
         }
       };
-      if (rot && S.info.y >= 0) {
+      if (S.info.y >= 0) {
         // the whole tile lies in one shared block: its cos/sin row in LDS
         typedef __attribute__((address_space(3))) const float lds_float;
         rotate((lds_float*)csl);
-      } else if (rot) {
+      } else {
         // rows in several shared blocks: each row's own block, from the round's table
         const int t = S.info.x * kTile + c16;
         int lo = 0, hi = a.B - 1;
@@ -908,9 +846,6 @@ __global__ __launch_bounds__(kStreamNW * kWave) __attribute__((amdgpu_waves_per_
         }
         typedef __attribute__((address_space(1))) const float global_float;
         rotate((global_float*)(a.tab + ((size_t)(PT.r / a.L) * a.B + lo) * HALF));
-      } else {
-#pragma unroll
-        for (int k = 0; k < KD; ++k) kop[k] = Fmt<uint16_t>::pack(x[k]);
       }
     }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -965,14 +900,6 @@ __global__ __launch_bounds__(kStreamNW * kWave) __attribute__((amdgpu_waves_per_
       process(S[k]);
     }
   } while (pk < nht);
-}
-
-// bf16 copy of the queries (the MFMA operand form): qplain[i][l][hq][D]
-template <typename E, int D>
-__global__ __launch_bounds__(256) void qplain_kernel(const E* __restrict__ q, size_t n8,
-                                                     uint16_t* __restrict__ out) {
-  for (size_t x = blockIdx.x * (size_t)blockDim.x + threadIdx.x; x < n8; x += (size_t)gridDim.x * blockDim.x)
-    st16(out + 8 * x, load8_bf16<E>(q + 8 * x));
 }
 
 // One wave per output row (agent, layer, query head): combine the agent
@@ -1032,12 +959,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, E* __restrict__ 
   const float inv = ls > 0.f ? 1.0f / ls : 0.f;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    const float v = o[k] * inv;
-    if constexpr (sizeof(E) == 2) {
-      out[row * D + lane + k * kWave] = (uint16_t)f32_to_bf16(v);
-    } else {
-      out[row * D + lane + k * kWave] = v;
-    }
+    out[row * D + lane + k * kWave] = (uint16_t)f32_to_bf16(o[k] * inv);
   }
 }
 
@@ -1148,7 +1070,7 @@ __global__ __launch_bounds__(kThreads) void restore_dense_kernel(
 struct Plan {
   int SP, SG, AGS, NAG, TPG, n_sh_wg;
   long long dcap;
-  size_t part_bytes, tab_off, qplain_off, task_off, ctl_off, dcs_off, dinfo_off, total;
+  size_t part_bytes, tab_off, task_off, ctl_off, dcs_off, dinfo_off, total;
 };
 
 Plan make_plan(const Dims& d, int max_priv, bool fused) {
@@ -1177,9 +1099,7 @@ Plan make_plan(const Dims& d, int max_priv, bool fused) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   p.part_bytes = (size_t)d.N * d.L * d.Hq * (p.SP + p.SG) * (d.D + 4) * 4;
   p.tab_off = up(p.part_bytes);
-  p.qplain_off = p.tab_off + (fused ? up((size_t)d.N * d.B * (d.D / 2) * 8) : 0);
-  // bf16 queries are read in place; fp32 ones get a bf16 copy
-  p.task_off = p.qplain_off + (d.dtype == TDX_BF16 ? 0 : up((size_t)d.N * d.L * d.Hq * d.D * 2));
+  p.task_off = p.tab_off + (fused ? up((size_t)d.N * d.B * (d.D / 2) * 8) : 0);
   p.ctl_off = p.task_off + up((size_t)d.N * d.L * p.SP * sizeof(StreamTask));
   p.dcs_off = p.ctl_off + 256;
   p.dinfo_off = p.dcs_off + (fused ? up((size_t)p.dcap * (d.D / 2) * 8) : 0);
@@ -1187,11 +1107,10 @@ Plan make_plan(const Dims& d, int max_priv, bool fused) {
   return p;
 }
 
-// register stages of stream_kernel: PD stages keep PD-1 tiles in flight per
-// wave; fp32 rows of 128 dims take twice the registers
+// register stages of stream_kernel: PD stages keep PD-1 tiles in flight per wave
 template <typename E, int D>
 struct StreamCfg {
-  static constexpr int PD = (sizeof(E) == 4 && D == 128) ? 2 : TDX_ST_PD;
+  static constexpr int PD = TDX_ST_PD;
   static constexpr size_t lds(bool fused) {
     return (size_t)kStreamNW * (kTile * D * sizeof(E) + kTile * D * 2 + (fused ? D / 2 * 8 : 0));
   }
@@ -1220,16 +1139,7 @@ hipError_t launch_attn_t(const Dims& d, AttnArgs a, const Plan& p, E* out, hipSt
     hipLaunchKernelGGL((shared_kernel<E, D, TDX_SH_PD, PAGED>), dim3(grid), dim3(kShThreads), lds, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if constexpr (sizeof(E) == 2) {
-    a.qplain = static_cast<const uint16_t*>(a.q);  // already the operand form
-  } else {
-    uint16_t* qp = reinterpret_cast<uint16_t*>(a.ws_base + p.qplain_off);
-    const size_t nq = (size_t)d.N * d.L * d.Hq * D / 8;
-    const int qblocks = (int)((nq + 255) / 256 < 4096 ? (nq + 255) / 256 : 4096);
-    hipLaunchKernelGGL((qplain_kernel<E, D>), dim3(qblocks), dim3(256), 0, s, static_cast<const E*>(a.q), nq, qp);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    a.qplain = qp;
-  }
+  a.qplain = static_cast<const uint16_t*>(a.q);  // bf16 queries are the MFMA operand as stored
   constexpr int PD = StreamCfg<E, D>::PD;
   const size_t lds = StreamCfg<E, D>::lds(MODE == FUSED);
   auto kern = stream_kernel<E, D, MODE, PD, PAGED>;
@@ -1256,13 +1166,12 @@ hipError_t launch_attn_t(const Dims& d, AttnArgs a, const Plan& p, E* out, hipSt
   return hipGetLastError();
 }
 
+// bf16 caches (fp32 ones take launch_attn_f32 before reaching here)
 template <int MODE, bool PAGED = false>
 hipError_t dispatch_attn(const Dims& d, AttnArgs a, const Plan& p, void* out, hipStream_t s) {
-  if (d.dtype == TDX_BF16)
-    return d.D == 128 ? launch_attn_t<uint16_t, 128, MODE, PAGED>(d, a, p, static_cast<uint16_t*>(out), s)
-                      : launch_attn_t<uint16_t, 64, MODE, PAGED>(d, a, p, static_cast<uint16_t*>(out), s);
-  return d.D == 128 ? launch_attn_t<float, 128, MODE, PAGED>(d, a, p, static_cast<float*>(out), s)
-                    : launch_attn_t<float, 64, MODE, PAGED>(d, a, p, static_cast<float*>(out), s);
+  if (d.dtype != TDX_BF16) return hipErrorInvalidValue;
+  return d.D == 128 ? launch_attn_t<uint16_t, 128, MODE, PAGED>(d, a, p, static_cast<uint16_t*>(out), s)
+                    : launch_attn_t<uint16_t, 64, MODE, PAGED>(d, a, p, static_cast<uint16_t*>(out), s);
 }
 
 AttnArgs common_args(const Dims& d, const void* q, const int32_t* priv_off, const void* pk,
@@ -1290,8 +1199,32 @@ AttnArgs common_args(const Dims& d, const void* q, const int32_t* priv_off, cons
 
 }  // namespace
 
-size_t restore_attn_ws_bytes(const Dims& d, int max_priv) { return make_plan(d, max_priv, true).total; }
-size_t dense_attn_ws_bytes(const Dims& d, int max_priv) { return make_plan(d, max_priv, false).total; }
+size_t restore_attn_ws_bytes(const Dims& d, int max_priv) {
+  return d.dtype == TDX_F32 ? f32_attn_ws_bytes(d, max_priv, true) : make_plan(d, max_priv, true).total;
+}
+size_t dense_attn_ws_bytes(const Dims& d, int max_priv) {
+  return d.dtype == TDX_F32 ? f32_attn_ws_bytes(d, max_priv, false) : make_plan(d, max_priv, false).total;
+}
+
+namespace {
+// fp32 caches take the fp32 vector-unit path (attn_f32.hip)
+F32AttnArgs f32_args(const Dims& d, const tdx_layout* lay, const void* q, const int32_t* priv_off, const void* pk,
+                     const void* pv, float scale, void* out) {
+  F32AttnArgs a{};
+  a.q = static_cast<const float*>(q);
+  a.priv_off = priv_off;
+  a.pk = static_cast<const float*>(pk);
+  a.pv = static_cast<const float*>(pv);
+  if (lay != nullptr) {
+    a.blk_start = lay->blk_start;
+    a.src_pos = lay->src_pos;
+    a.dst_pos = lay->dst_pos;
+  }
+  a.scale_log2 = scale * kLog2e;
+  a.out = static_cast<float*>(out);
+  return a;
+}
+}  // namespace
 
 namespace {
 // Query side (cos/sin table, per-diff-entry rows), then the fused kernels.
@@ -1326,6 +1259,18 @@ hipError_t launch_restore_attn(const Dims& d, const tdx_layout& lay, const void*
                                int max_priv, const MasterRef& master,
                                const int32_t* diff_off, const int32_t* diff_idx, const void* dk,
                                const void* dv, float scale, void* out, void* ws, hipStream_t s) {
+  if (d.dtype == TDX_F32) {
+    F32AttnArgs f = f32_args(d, &lay, q, priv_off, pk, pv, scale, out);
+    f.sk = static_cast<const float*>(master.k);
+    f.sv = static_cast<const float*>(master.v);
+    f.msel = master.sel;
+    f.mstride = master.stride;
+    f.diff_off = diff_off;
+    f.diff_idx = diff_idx;
+    f.dk = static_cast<const float*>(dk);
+    f.dv = static_cast<const float*>(dv);
+    return launch_attn_f32(d, FUSED, false, f, max_priv, ws, s);
+  }
   AttnArgs a = common_args(d, q, priv_off, pk, pv, max_priv, scale, ws);
   a.sk = master.k;
   a.sv = master.v;
@@ -1341,6 +1286,18 @@ hipError_t launch_restore_attn_paged(const Dims& d, const tdx_layout& lay, const
                                      const void* ak_pool, const void* av_pool, const PageMap& apm,
                                      const int32_t* master_sel, const int32_t* diff_off, const int32_t* diff_idx,
                                      const int32_t* diff_page, float scale, void* out, void* ws, hipStream_t s) {
+  if (d.dtype == TDX_F32) {
+    F32AttnArgs f = f32_args(d, &lay, q, priv_off, pk_pool, pv_pool, scale, out);
+    f.sk = f.dk = static_cast<const float*>(ak_pool);  // Master and diff pages are agents' pages
+    f.sv = f.dv = static_cast<const float*>(av_pool);
+    f.msel = master_sel;
+    f.mpm = apm;
+    f.dpm = PageMap{diff_page, 0, apm.n_pages};
+    f.ppm = ppm;
+    f.diff_off = diff_off;
+    f.diff_idx = diff_idx;
+    return launch_attn_f32(d, FUSED, true, f, max_priv, ws, s);
+  }
   AttnArgs a = common_args(d, q, priv_off, pk_pool, pv_pool, max_priv, scale, ws);
   a.sk = ak_pool;  // the Master's pages and the diff entries' pages are agents' pages
   a.sv = av_pool;
@@ -1376,6 +1333,12 @@ hipError_t launch_restore_dense(const Dims& d, const tdx_layout& lay, const Mast
 hipError_t launch_dense_attn(const Dims& d, const void* q, const int32_t* priv_off,
                              const void* pk, const void* pv, int max_priv, const void* kd,
                              const void* vd, float scale, void* out, void* ws, hipStream_t s) {
+  if (d.dtype == TDX_F32) {
+    F32AttnArgs f = f32_args(d, nullptr, q, priv_off, pk, pv, scale, out);
+    f.sk = static_cast<const float*>(kd);
+    f.sv = static_cast<const float*>(vd);
+    return launch_attn_f32(d, DENSE, false, f, max_priv, ws, s);
+  }
   const Plan p = make_plan(d, max_priv, false);
   AttnArgs a = common_args(d, q, priv_off, pk, pv, max_priv, scale, ws);
   a.sk = kd;

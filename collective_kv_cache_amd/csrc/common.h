@@ -116,6 +116,18 @@ __device__ __forceinline__ double rope_inv_freq(double theta, int e, int D) {
   return pow(theta, -2.0 * (double)e / (double)D);
 }
 
+// Element offset of the Master's cache: (*sel clamped to [0, N)) * stride,
+// 0 without a selector.
+__device__ __forceinline__ size_t master_offset(const int32_t* sel, long long stride, int N) {
+  if (sel == nullptr) return 0;
+  const int m = min(max(sel[0], 0), N - 1);
+  return (size_t)m * (size_t)stride;
+}
+
+// Restore-attention modes: FUSED = the Master patched with diff records
+// tile by tile; DENSE = the comparator's attention over materialised caches.
+enum AttnMode { FUSED = 0, DENSE = 1 };
+
 }  // namespace tdx
 
 // ---- internal launchers (implemented per kernel file, called by api.hip) ----
@@ -193,6 +205,39 @@ size_t dense_attn_ws_bytes(const Dims& d, int max_priv);
 hipError_t launch_dense_attn(const Dims& d, const void* q, const int32_t* priv_off,
                              const void* pk, const void* pv, int max_priv, const void* kd,
                              const void* vd, float scale, void* out, void* ws, hipStream_t s);
+
+// fp32 caches: restore-attention on the fp32 vector units (attn_f32.hip).
+// Pointers as in the bf16 path; sk/sv = the Master (or, with msel, every
+// agent's cache at stride mstride) for FUSED, the dense caches
+// [N][L][T][Hkv][D] for DENSE; paged (FUSED only): sk/sv/dk/dv are the
+// agents' pools and pk/pv the private pools, mapped by mpm / dpm / ppm.
+struct F32AttnArgs {
+  const float* q;  // [N][L][Hq][D]
+  const int32_t* priv_off;
+  const float* pk;
+  const float* pv;
+  const float* sk;
+  const float* sv;
+  const int32_t* msel;
+  long long mstride;
+  const int32_t* diff_off;
+  const int32_t* diff_idx;
+  const float* dk;
+  const float* dv;
+  const int32_t* blk_start;
+  const int32_t* src_pos;
+  const int32_t* dst_pos;
+  PageMap mpm, dpm, ppm;
+  float scale_log2;  // softmax scale * log2(e)
+  float* out;        // [N][L][Hq][D]
+  // set by launch_attn_f32
+  const float2* tab;
+  float* part;
+  int N, L, T, B, Hkv, Hq, pmax;
+};
+size_t f32_attn_ws_bytes(const Dims& d, int max_priv, bool fused);
+hipError_t launch_attn_f32(const Dims& d, int mode, bool paged, F32AttnArgs a, int max_priv, void* ws,
+                           hipStream_t s);
 
 // Transfer-path restore: Master and diff records readable by the GPU
 // (pinned host storage or device memory), requested agents, layer range.
