@@ -87,21 +87,25 @@ def test_zero_and_all_diff_blocks(which):
     assert_close(fused, o_fused, f"fused {which}")
 
 
-@pytest.mark.parametrize("name", ["qwen14b_round", "qwen7b_scaleout"])
+@pytest.mark.parametrize("name", ["qwen7b_round", "qwen14b_round", "qwen7b_scaleout"])
 def test_full_size_sampled(name):
-    # full-size rounds in the benchmark's launch configuration (the 64-agent
-    # round's caches pass 2^32 elements); sampled (agent, layer) outputs are
-    # computed one by one by the oracle from host copies of the generated
-    # inputs and the oracle's own diff rows.
+    # full-size rounds in the benchmark's launch configuration (no Master
+    # copy: the restore reads the Master in place through the device-side
+    # selector; the 64-agent round's caches pass 2^32 elements); sampled
+    # (agent, layer) outputs are computed one by one by the oracle from host
+    # copies of the generated inputs and the oracle's own diff rows.
     cfg = CONFIGS[name]
     lay = make_layout(cfg)
     master = 2
     r = Round(cfg, lay, master=master, device_gen=DEV)
-    ds = r.gpu_encode()
-    fused = r.gpu_fused(ds)
-    kd, vd, dense = r.gpu_dense(ds)
-    torch.cuda.synchronize()
     d = r.dev
+    m = torch.tensor([master], dtype=torch.int32, device=DEV)
+    ds = tdx.diff_encode(r.shape, r.dl, m, d["ak"], d["av"], master_copy=False)
+    fused = tdx.restore_attn(r.shape, r.dl, d["q"], d["po"], d["pk"], d["pv"], r.max_priv, d["ak"], d["av"], ds,
+                             master_sel=m)
+    kd, vd = tdx.restore_dense(r.shape, r.dl, d["ak"], d["av"], ds, master_sel=m)
+    dense = tdx.decode_attn_dense(r.shape, r.dl, d["q"], d["po"], d["pk"], d["pv"], r.max_priv, kd, vd)
+    torch.cuda.synchronize()
     scale = r.scale
     L = cfg.n_layers
     for i, l in ((0, 0), (master, 11), (5, L - 5), (cfg.n_agents - 1, L - 1)):

@@ -128,7 +128,7 @@ def test_overflowed_record_restores_as_truncated():
     np.testing.assert_array_equal(host(vo), rvd)
 
 
-@pytest.mark.parametrize("name", ["qwen14b_round", "qwen7b_scaleout"])
+@pytest.mark.parametrize("name", ["qwen7b_round", "qwen14b_round", "qwen7b_scaleout"])
 def test_encode_full_size_planted_rows_and_samples(name):
     # full-size rounds (the 64-agent caches hold over 2^32 elements each),
     # drawn in HBM; every row must equal the planted block set (a property

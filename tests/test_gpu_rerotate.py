@@ -61,9 +61,9 @@ def test_rerotate_zero_shift_is_bitwise_copy_bf16():
         np.testing.assert_array_equal(got[i], to_numpy_bits(kc))
 
 
-@pytest.mark.parametrize("name", ["qwen14b_round", "qwen7b_scaleout"])
+@pytest.mark.parametrize("name", ["qwen7b_round", "qwen14b_round", "qwen7b_scaleout"])
 def test_rerotate_full_size_sampled(name):
-    # full-size rounds (14B: 10 agents x 48 layers x 4912 tokens x 8 heads;
+    # full-size rounds (7B: 10 agents x 28 layers; 14B: 10 agents x 48 layers x 4912 tokens x 8 heads;
     # 64 agents x 28 layers x ~5.5K tokens x 4 heads, whose output passes 2^32
     # elements): sampled (agent, layer, token) rows against the oracle, in the
     # same launch configuration the benchmark times.

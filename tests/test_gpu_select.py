@@ -154,7 +154,7 @@ def test_select_ties_at_the_threshold_take_the_lowest_tokens(cfg):
     assert sel.tolist() == want.tolist()
 
 
-@pytest.mark.parametrize("name", ["qwen14b_round", "qwen7b_scaleout"])
+@pytest.mark.parametrize("name", ["qwen7b_round", "qwen14b_round", "qwen7b_scaleout"])
 def test_select_full_size_last_layer_of_the_rerotated_round(name):
     # the benchmark's inputs at full size: the re-rotated K of every layer
     # (64 agents: over 2^32 elements), with the check layer the last one, so

@@ -183,3 +183,38 @@ def test_transfer_restore_into_pages(name, kw, agents, lr):
         assert torch.equal(bits(pool[:, ~owned]), bits(before[:, ~owned]))  # other pages untouched
         if outside:
             assert torch.equal(bits(pool[outside]), bits(before[outside]))  # layers outside the range
+
+
+@pytest.mark.parametrize("name", ["qwen7b_round", "qwen14b_round"])
+def test_transfer_full_size_sampled(name):
+    # full-size rounds as the benchmark runs them: the Master and the diff
+    # record in pinned host memory, every agent and layer restored in one
+    # call.  A restored row is the agent's own canonical row (the record is
+    # lossless) rotated to its offsets, so sampled rows are checked against
+    # the oracle's re-rotation of those rows (K) and bit for bit (V).
+    cfg = CONFIGS[name]
+    lay = make_layout(cfg)
+    master = 3
+    r = Round(cfg, lay, master=master, device_gen=DEV)
+    d = r.dev
+    m = torch.tensor([master], dtype=torch.int32, device=DEV)
+    ds = tdx.diff_encode(r.shape, r.dl, m, d["ak"], d["av"], master_copy=False)
+    torch.cuda.synchronize()
+    n = ds.nnz()
+    rec = (pinned(d["ak"][master]), pinned(d["av"][master]), pinned(ds.off), pinned(ds.idx[:max(n, 1)]),
+           pinned(ds.k[:max(n, 1)]), pinned(ds.v[:max(n, 1)]))
+    ag = torch.arange(cfg.n_agents, dtype=torch.int32, device=DEV)
+    ko, vo = tdx.restore_transfer(r.shape, r.dl, *rec, ag)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    toks = np.unique(np.concatenate([rng.choice(lay.n_tokens, 24, replace=False), lay.blk_start[:-1],
+                                     [lay.n_tokens - 1]]))
+    tt = torch.as_tensor(toks, device=DEV)
+    L = cfg.n_layers
+    for a, l in ((0, 0), (master, 7), (4, L - 3), (cfg.n_agents - 1, L - 1)):
+        own_k = to_numpy_bits(d["ak"][a, l, tt])
+        ref = O.rerotate_tokens(own_k, toks, a, lay.blk_start, lay.src_pos, lay.dst_pos, cfg.theta)
+        assert_close(to_numpy_bits(ko[a, l, tt]), ref, f"transfer K full a={a} l={l}")
+        np.testing.assert_array_equal(to_numpy_bits(vo[a, l, tt]), to_numpy_bits(d["av"][a, l, tt]))
+    del ko, vo, r, ds
+    torch.cuda.empty_cache()
