@@ -34,6 +34,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="qwen14b_round")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="time only --config (not the 7B round, 14B round and 64-agent round beside it)")
+    ap.add_argument("--no-per-config-cpu", action="store_true",
+                    help="skip the oracle timings of the per-config workloads other than --config")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="do not write the 1 GiB scratch between timed steps")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-transfer", action="store_true",
                     help="skip the transfer-path restore measurement (Master and diffs in pinned host memory)")
@@ -100,11 +106,9 @@ ENTRY_KERNELS = {
     "tdx_select_important": ("deviation_kernel", "select_kernel"),
     "tdx_diff_encode": ("flag_kernel", "rows_kernel", "offsets_kernel", "index_kernel", "copy_kernel"),
     "tdx_restore_attn": ("rope_table_kernel", "diff_tab_kernel", "shared_kernel",
-                         "qplain_kernel", "stream_plan_kernel<0>", "stream_kernel<unsigned short, 128, 0",
-                         "stream_kernel<float, 128, 0", "stream_kernel<unsigned short, 64, 0",
-                         "stream_kernel<float, 64, 0", "merge_kernel<unsigned short, 128, 0>",
-                         "merge_kernel<float, 128, 0>", "merge_kernel<unsigned short, 64, 0>",
-                         "merge_kernel<float, 64, 0>"),
+                         "stream_plan_kernel<0>", "stream_kernel<unsigned short, 128, 0",
+                         "stream_kernel<unsigned short, 64, 0", "merge_kernel<unsigned short, 128, 0>",
+                         "merge_kernel<unsigned short, 64, 0>"),
 }
 
 
@@ -282,57 +286,164 @@ def compression(counts, master, T, H, D, eb, priv_len, L):
     }
 
 
-def cpu_baseline(cfg, lay, pct, n_sample=8):
-    """The oracle on a bounded sample: the first ``n_sample`` layers of the same
-    round (drawn on the host), all agents; the round's layers are iid, so the
-    whole-round time is the per-layer time x L (select runs once per round)."""
-    import numpy as np
-    import oracle as O
-    from threadpoolctl import threadpool_limits
-    from workload import (cached_kv, agent_caches, queries, private_kv, recomputed_k,
-                          to_numpy_bits, from_numpy_bits)
+# ---- the oracle on the host (cpu_baseline) ----------------------------------
+# The oracle runs in a pool of worker processes created before this process
+# makes its first GPU call (spawned interpreters, one torch / BLAS thread
+# each).  A round's layers are independent, so each worker takes whole layers:
+# it draws the layer's inputs on the host (same shapes and structure as the
+# GPU round) and times the oracle's stages on them.
 
-    ns = min(n_sample, cfg.n_layers)
-    c1 = cfg.scaled(n_layers=ns)
-    kc, vc = cached_kv(c1, lay)
-    q = queries(c1)
-    pk, pv = private_kv(c1, lay)
-    hk, hv, hq, hpk, hpv = (to_numpy_bits(x) for x in (kc, vc, q, pk, pv))
+POOL_MAX = 16  # the host's CPU share on a one-GPU machine
+
+
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def make_oracle_pool():
+    """(pool, size): spawned workers, sized to the affinity mask capped at POOL_MAX."""
+    import multiprocessing as mp
+
+    n = max(1, min(len(os.sched_getaffinity(0)), POOL_MAX))
+    return mp.get_context("spawn").Pool(n, initializer=_oracle_worker_init), n
+
+
+def _oracle_worker_init():
+    os.environ["OMP_NUM_THREADS"] = "1"
+    import torch
+
+    torch.set_num_threads(1)
+
+
+def _oracle_select(name: str):
+    """Check layer: the oracle's re-rotation of it (input preparation), then
+    the timed deviation, top-k and Master."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+    from workload import CONFIGS, cached_kv, from_numpy_bits, make_layout, recomputed_k, to_numpy_bits
+
+    cfg = CONFIGS[name]
+    lay = make_layout(cfg)
     with threadpool_limits(limits=1):
+        kc, _ = cached_kv(cfg, lay, layers=[cfg.check_layer])
+        kr = O.rerotate(to_numpy_bits(kc), lay.blk_start, lay.src_pos, lay.dst_pos, cfg.theta)[:, 0]
+        kx = to_numpy_bits(recomputed_k(cfg, lay, from_numpy_bits(kr)))
         t0 = time.perf_counter()
-        kr = O.rerotate(hk, lay.blk_start, lay.src_pos, lay.dst_pos, cfg.theta)
-        t1 = time.perf_counter()
-        kx = to_numpy_bits(recomputed_k(c1, lay, from_numpy_bits(kr[:, 0])))
-        t2 = time.perf_counter()
-        _, s, a = O.deviation(kr[:, 0], kx)
-        k = O.topk_count(pct, lay.n_tokens)
-        O.select_important(s.astype(np.float32), k)
+        _, s, a = O.deviation(kr, kx)
+        O.select_important(s.astype(np.float32), O.topk_count(cfg.pct, lay.n_tokens))
         m = O.choose_master(a.astype(np.float32))
+        t1 = time.perf_counter()
+    return m, t1 - t0
+
+
+def _oracle_layer(name: str, layer: int, master: int):
+    """One layer of the round: draw its inputs, then time the oracle's
+    re-rotation, diff encode and restore-attention of that layer."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+    from workload import (CONFIGS, agent_caches, cached_kv, make_layout, private_kv, queries,
+                          to_numpy_bits)
+
+    cfg = CONFIGS[name]
+    lay = make_layout(cfg)
+    g0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        kc, vc = cached_kv(cfg, lay, layers=[layer])
+        q = to_numpy_bits(queries(cfg)[:, layer:layer + 1])
+        pk, pv = (to_numpy_bits(x) for x in private_kv(cfg, lay, layers=[layer]))
+        ak, av = (to_numpy_bits(x) for x in agent_caches(cfg, lay, kc, vc, master))
+        hk, hv = to_numpy_bits(kc), to_numpy_bits(vc)
+        t0 = time.perf_counter()
+        O.rerotate(hk, lay.blk_start, lay.src_pos, lay.dst_pos, cfg.theta)
+        t1 = time.perf_counter()
+        off, idx, dk, dv = O.diff_encode(ak, av, master)
+        t2 = time.perf_counter()
+        O.restore_attn(q, lay.priv_off, pk, pv, hk, hv, off, idx, dk, dv, lay.blk_start, lay.src_pos,
+                       lay.dst_pos, cfg.theta, 1.0 / math.sqrt(cfg.head_dim))
         t3 = time.perf_counter()
-        ak, av = agent_caches(c1, lay, kc, vc, m)
-        hak, hav = to_numpy_bits(ak), to_numpy_bits(av)
-        t4 = time.perf_counter()
-        off, idx, dk, dv = O.diff_encode(hak, hav, m)
-        t5 = time.perf_counter()
-        O.restore_attn(hq, lay.priv_off, hpk, hpv, hk, hv, off, idx, dk, dv, lay.blk_start,
-                       lay.src_pos, lay.dst_pos, cfg.theta, 1.0 / math.sqrt(cfg.head_dim))
-        t6 = time.perf_counter()
+    return {"pid": os.getpid(), "layer": layer, "draw": t0 - g0, "rerotate": t1 - t0, "encode": t2 - t1,
+            "restore_attn": t3 - t2}
+
+
+def cpu_baseline(pool, n_pool: int, name: str, layers=None):
+    """The oracle's round time on the host's cores: the check-layer selection,
+    then the round's layers spread over the pool.  value = N*T agent-tokens /
+    (selection + the largest per-process sum of the layers' oracle stage
+    times); drawing the inputs is not counted.  ``layers``: a bounded sample
+    of the round's layers (the per-layer stages then scale by L / len)."""
+    from collections import defaultdict
+
+    from workload import CONFIGS, make_layout
+
+    cfg = CONFIGS[name]
+    lay = make_layout(cfg)
     L = cfg.n_layers
-    f = L / ns
-    per_round = ((t1 - t0) + (t5 - t4) + (t6 - t5)) * f + (t3 - t2)
+    layers = list(range(L)) if layers is None else list(layers)
+    w0 = time.perf_counter()
+    master, t_sel = pool.apply(_oracle_select, (name,))
+    res = pool.starmap(_oracle_layer, [(name, l, master) for l in layers], chunksize=1)
+    wall = time.perf_counter() - w0
+    per_proc = defaultdict(float)
+    for r in res:
+        per_proc[r["pid"]] += r["rerotate"] + r["encode"] + r["restore_attn"]
+    f = L / len(layers)
+    stage = {k: sum(r[k] for r in res) * f for k in ("rerotate", "encode", "restore_attn")}
+    if len(layers) == L:
+        layers_s = max(per_proc.values())  # measured: the busiest process's oracle time
+    else:
+        # a sample: the whole round's oracle time spread over the pool, but no
+        # less than one layer's
+        layers_s = max(sum(stage.values()) / n_pool,
+                       max(r["rerotate"] + r["encode"] + r["restore_attn"] for r in res))
+    round_s = t_sel + layers_s
+    sample = (f"every layer of the {name} round ({L} layers, {cfg.n_agents} agents, {lay.n_tokens} shared "
+              f"tokens, the same shapes and structure as the GPU round, drawn on the host)"
+              if len(layers) == L else
+              f"layers {layers[0]}..{layers[-1]} of the {L} of the {name} round ({cfg.n_agents} agents, "
+              f"{lay.n_tokens} shared tokens); the round's oracle time is their stage times x {L}/{len(layers)} "
+              f"spread evenly over the {n_pool} processes")
     return {
-        "value": cfg.n_agents * lay.n_tokens / per_round,
+        "value": cfg.n_agents * lay.n_tokens / round_s,
         "unit": "agent-tokens/s",
-        "cores": 1,
+        "cores": len(per_proc) if len(layers) == L else n_pool,
         "kind": "oracle",
-        "sample": (f"layers 0..{ns - 1} of the {cfg.name} round on the host (all {cfg.n_agents} "
-                   f"agents, {lay.n_tokens} shared tokens, the same private histories), one thread; "
-                   f"per-layer stages x {L}/{ns} + one select; measured "
-                   f"{t6 - t0 - (t2 - t1) - (t4 - t3):.1f} s of oracle time"),
-        "stage_s_per_layer": {"rerotate": (t1 - t0) / ns, "select_once": t3 - t2,
-                              "encode": (t5 - t4) / ns, "restore_attn": (t6 - t5) / ns},
-        "cpu": platform.processor() or platform.machine(),
+        "sample": (sample + (f"; layers spread over {len(per_proc)} worker processes, one thread each; round "
+                             f"time = check-layer selection + the largest per-process sum of its layers' oracle "
+                             f"stage times" if len(layers) == L else "") + "; drawing the inputs is not counted"),
+        "cpu": cpu_model(),
+        "round_s": round(round_s, 3),
+        "oracle_cpu_s": round(t_sel + sum(stage.values()), 2),
+        "stage_cpu_s": {"select": round(t_sel, 3), **{k: round(v, 2) for k, v in stage.items()}},
+        "wall_s": round(wall, 2),
     }
+
+
+def time_calls(fn, steps, warmup, flush):
+    """Mean ms of fn() over ``steps`` calls, each after ``flush`` and timed by
+    its own HIP events (the flush falls outside them)."""
+    import torch
+
+    for _ in range(warmup):
+        flush()
+        fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        flush()
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps
 
 
 PCIE_H2D_GBS = 64.0  # PCIe 5.0 x16, one direction, nominal
@@ -343,9 +454,9 @@ def transfer_path(cfg, lay, shape, dl, ds, nnz, master_k, master_v, q, pk, pv, r
     diff record in pinned host memory (outside the timed step):
       - every agent's KV for every layer in one call: bytes over PCIe / time;
       - one Mirror, layer by layer (the pages' per-Mirror per-layer latency);
-      - the same Mirror's layers restored on one stream while decode attention
-        over the layers already restored runs on another (pipelined), against
-        the two run back to back on one stream."""
+      - decode attention of that Mirror over each restored layer, the only
+        work a restore on a second stream could hide (its share of the
+        restore time bounds what overlap can gain)."""
     import numpy as np
     import torch
     from collective_kv_cache_amd import tdx
@@ -390,7 +501,8 @@ def transfer_path(cfg, lay, shape, dl, ds, nnz, master_k, master_v, q, pk, pv, r
                                                k1, v1, ws1)
     ms_layers = timed(lambda: [restore_l(l) for l in range(L)])
     pcie_mirror = L * T * 2 * kt + int(counts[mir].sum()) * (16 * 2 * kt + 4)
-    # decode attention of that Mirror over each restored layer (one agent, one layer per call)
+    # decode attention of that Mirror over each restored layer (one agent, one
+    # layer per call): the work a second stream could overlap with the restore
     shape1 = tdx.Shape(1, H, Hq, D, cfg.torch_dtype, cfg.theta)
     dl1 = tdx.RoundLayout(lay.blk_start, lay.src_pos, lay.dst_pos[mir:mir + 1], dev)
     p0, p1 = int(lay.priv_off[mir]), int(lay.priv_off[mir + 1])
@@ -402,31 +514,6 @@ def transfer_path(cfg, lay, shape, dl, ds, nnz, master_k, master_v, q, pk, pv, r
     pv1 = [pv[l:l + 1, p0:p1] if p1 > p0 else pv[l:l + 1, :1] for l in range(L)]
     attn_l = lambda l: tdx.decode_attn_dense(shape1, dl1, q[mir:mir + 1, l:l + 1], po1, pk1[l], pv1[l], p1 - p0,
                                              k1[:, l:l + 1], v1[:, l:l + 1], out=out1, ws=ws_a)
-
-    def serial():
-        for l in range(L):
-            restore_l(l)
-            attn_l(l)
-
-    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
-    done = [torch.cuda.Event() for _ in range(L)]
-
-    def pipelined():
-        cur = torch.cuda.current_stream()
-        sa.wait_stream(cur)
-        sb.wait_stream(cur)
-        for l in range(L):
-            with torch.cuda.stream(sa):
-                restore_l(l)
-                done[l].record(sa)
-            with torch.cuda.stream(sb):
-                sb.wait_event(done[l])
-                attn_l(l)
-        cur.wait_stream(sa)
-        cur.wait_stream(sb)
-
-    ms_serial = timed(serial)
-    ms_pipe = timed(pipelined)
     attn_ms = timed(lambda: [attn_l(l) for l in range(L)])
     return {
         "source": "pinned host memory (Master + diff record), read by the restore kernel over PCIe",
@@ -438,9 +525,8 @@ def transfer_path(cfg, lay, shape, dl, ds, nnz, master_k, master_v, q, pk, pv, r
         "mirror": mir,
         "ms_per_mirror_per_layer": round(ms_layers / L, 4),
         "mirror_GBps": round(pcie_mirror / (ms_layers * 1e-3) / 1e9, 2),
-        "mirror_restore_then_attend_serial_ms": round(ms_serial, 3),
-        "mirror_restore_attend_pipelined_ms": round(ms_pipe, 3),
-        "mirror_attend_only_ms": round(attn_ms, 3),
+        "mirror_attend_ms_per_layer": round(attn_ms / L, 4),
+        "attend_over_restore": round(attn_ms / ms_layers, 4),
     }
 
 
@@ -471,7 +557,7 @@ def _to_pool(seqs, gen):
 
 
 def paged_path(cfg, lay, shape, shape1, dl, kc, kr, kx, k, msel, ak, av, q, po, pk, pv, max_priv, out_ref,
-               steps, warmup, stage_ms, nnz):
+               steps, warmup, stage_ms, nnz, flush):
     """The four calls over 16-token pages (shuffled page order), timed like the
     step's stages, with the same algorithmic bytes (the paged record holds a
     page ID per entry instead of a value copy)."""
@@ -523,16 +609,7 @@ def paged_path(cfg, lay, shape, shape1, dl, kc, kr, kx, k, msel, ak, av, q, po, 
     byts["encode"] = N * L * T * kv + nnz * 8 + 4 * (N * L + 1)  # index + page ID per entry
     res = {}
     for name, fn in calls.items():
-        for _ in range(warmup):
-            fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(steps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
+        ms = time_calls(fn, steps, warmup, flush)
         gbs = byts[name] / (ms * 1e-3) / 1e9
         res[name] = {"ms": round(ms, 4), "alg_GB": round(byts[name] / 1e9, 4), "GBps": round(gbs, 1),
                      "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
@@ -546,7 +623,7 @@ def paged_path(cfg, lay, shape, shape1, dl, kc, kr, kx, k, msel, ak, av, q, po, 
     return res
 
 
-def graph_step(step, steps, warmup, eager_ms, out):
+def graph_step(step, steps, warmup, eager_ms, out, flush):
     """One step captured in a HIP graph (outputs and workspaces preallocated,
     no allocation or memset inside the calls) and replayed."""
     import torch
@@ -561,16 +638,7 @@ def graph_step(step, steps, warmup, eager_ms, out):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         step()
-    for _ in range(warmup):
-        g.replay()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(steps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms = time_calls(g.replay, steps, warmup, flush)
     bits = (lambda t: t.view(torch.int16)) if out.dtype == torch.bfloat16 else (lambda t: t.view(torch.int32))
     same = bool(torch.equal(bits(out), bits(ref)))
     del g
@@ -578,7 +646,7 @@ def graph_step(step, steps, warmup, eager_ms, out):
             "graph_over_eager": round(ms / eager_ms, 4), "restore_bit_identical": same}
 
 
-def serial_path(shape, lay, kc, kx, k, check_layer, kr, steps, warmup, collective_ms):
+def serial_path(shape, lay, kc, kx, k, check_layer, kr, steps, warmup, collective_ms, flush):
     """N one-agent launches of re-rotation and selection (the per-request
     path) against the collective round's one launch of each."""
     import torch
@@ -587,16 +655,7 @@ def serial_path(shape, lay, kc, kx, k, check_layer, kr, steps, warmup, collectiv
 
     ser = SerialReuse(shape, lay.blk_start, lay.src_pos, lay.dst_pos, k, kr.device)
     kr_s = torch.empty_like(kr)
-    for _ in range(warmup):
-        ser.run(kc, kx, check_layer, kr_s)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(steps):
-        ser.run(kc, kx, check_layer, kr_s)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms = time_calls(lambda: ser.run(kc, kx, check_layer, kr_s), steps, warmup, flush)
     same = bool(torch.equal(kr_s.view(torch.int16) if kr.dtype == torch.bfloat16 else kr_s.view(torch.int32),
                             kr.view(torch.int16) if kr.dtype == torch.bfloat16 else kr.view(torch.int32)))
     del kr_s
@@ -606,24 +665,15 @@ def serial_path(shape, lay, kc, kx, k, check_layer, kr, steps, warmup, collectiv
             "note": "kernel time only; the pages' 2.57x includes model recompute"}
 
 
-def main():
-    args = parse()
-    if args.pmc_summary:
-        if len(args.pmc_summary) not in (2, 3):
-            raise SystemExit("--pmc-summary FETCH_CSV WRITE_CSV [BENCH_LOG]")
-        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.config, *args.pmc_summary[2:])
-        return
-    if args.trace_summary:
-        trace_summary(*args.trace_summary)
-        return
-    if args.sq_summary:
-        sq_summary(*args.sq_summary)
-        return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the collective reuse path here runs on a single "
-              "MI355X (run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
+FLUSH_BYTES = 1 << 30  # written between timed steps: more than the 256 MB last-level cache holds
 
+
+def measure(name, args, legs: bool, flush):
+    """One round of workload ``name`` in HBM: warm-up, then ``args.steps``
+    timed steps, each after a MALL flush and bracketed by its own HIP events
+    (the flush falls outside them).  With ``legs``, the graph replay, serial,
+    paged and transfer legs follow; the dense comparator runs unless
+    --no-dense."""
     import numpy as np
     import torch
 
@@ -632,7 +682,7 @@ def main():
                           recomputed_k)
 
     dev = "cuda"
-    cfg = CONFIGS[args.config]
+    cfg = CONFIGS[name]
     lay = make_layout(cfg)
     N, L, T, H, Hq, D = cfg.n_agents, cfg.n_layers, lay.n_tokens, cfg.n_kv_heads, cfg.n_q_heads, cfg.head_dim
     shape = tdx.Shape(L, H, Hq, D, cfg.torch_dtype, cfg.theta)
@@ -681,6 +731,140 @@ def main():
                          master_sel=sel["master"])
         mark(4)
 
+    def timed_steps(fn, steps, nev):
+        """fn(events) per step; a flush before each step, outside its events."""
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for s_ in range(steps):
+            flush()
+            fn(evs[s_])
+        torch.cuda.synchronize()
+        return evs
+
+    for _ in range(args.warmup):
+        flush()
+        step()
+    evs = timed_steps(step, args.steps, 5)
+    per_step = [evs[s_][0].elapsed_time(evs[s_][4]) for s_ in range(args.steps)]
+    ms_step = float(np.mean(per_step))
+    stage_all = {nm: [evs[s_][j].elapsed_time(evs[s_][j + 1]) for s_ in range(args.steps)]
+                 for j, nm in enumerate(stages)}
+    stage_ms = {nm: float(np.mean(v)) for nm, v in stage_all.items()}
+    if ds.nnz() != nnz or nnz > cap:
+        raise RuntimeError("diff encode changed between steps or overflowed")
+
+    # ---- dense comparator on the same round (outside the step)
+    byts = stage_bytes(cfg, lay, nnz, k)
+    dense = None
+    if not args.no_dense:
+        kd = torch.empty((N, L, T, H, D), dtype=cfg.torch_dtype, device=dev)
+        vd = torch.empty_like(kd)
+        outd = torch.empty_like(out)
+        ws_d = torch.empty(max(tdx.decode_attn_dense_workspace(shape, dl, max_priv), 16), dtype=torch.uint8,
+                           device=dev)
+
+        def dense_step(ev):
+            ev[0].record()
+            tdx.restore_dense(shape, dl, ak, av, ds, kd, vd, master_sel=sel["master"])
+            ev[1].record()
+            tdx.decode_attn_dense(shape, dl, q, po, pk, pv, max_priv, kd, vd, out=outd, ws=ws_d)
+            ev[2].record()
+
+        for _ in range(max(1, args.warmup)):
+            flush()
+            dense_step([torch.cuda.Event(enable_timing=True) for _ in range(3)])
+        devs = timed_steps(dense_step, args.steps, 3)
+        dense_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in devs]))
+        restore_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in devs]))
+        diff = (outd.float() - out.float()).abs().max().item()
+        gbs = byts["dense"] / (dense_ms * 1e-3) / 1e9
+        dense = {"ms": round(dense_ms, 4), "restore_ms": round(restore_ms, 4),
+                 "attend_ms": round(dense_ms - restore_ms, 4), "fused_ms": round(stage_ms["restore_attn"], 4),
+                 "speedup_fused_vs_dense": round(dense_ms / stage_ms["restore_attn"], 3),
+                 "alg_bytes_dense_over_fused": round(byts["dense"] / byts["restore_attn"], 3),
+                 "max_abs_fused_minus_dense": diff, "alg_GB": round(byts["dense"] / 1e9, 3),
+                 "GBps": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        del kd, vd, outd
+
+    graph = serial = paged = transfer = None
+    if legs and not args.no_graph:
+        graph = graph_step(step, args.steps, max(1, args.warmup), ms_step, out, flush)
+    if legs and not args.no_serial:
+        serial = serial_path(shape1, lay, kc, kx, k, cfg.check_layer, kr, args.steps,
+                             max(1, args.warmup), stage_ms["rerotate"] + stage_ms["select"], flush)
+    if legs and not args.no_paged:
+        paged = paged_path(cfg, lay, shape, shape1, dl, kc, kr, kx, k, sel["master"], ak, av, q, po, pk, pv,
+                           max_priv, out, args.steps, max(1, args.warmup), stage_ms, nnz, flush)
+    if legs and not args.no_transfer:
+        transfer = transfer_path(cfg, lay, shape, dl, ds, nnz, ak[master], av[master], q, pk, pv)
+
+    stage_rep = {}
+    for nm in stages:
+        gbs = byts[nm] / (stage_ms[nm] * 1e-3) / 1e9
+        stage_rep[nm] = {"ms": round(stage_ms[nm], 4), "ms_median": round(float(np.median(stage_all[nm])), 4),
+                         "ms_min": round(float(np.min(stage_all[nm])), 4), "alg_GB": round(byts[nm] / 1e9, 4),
+                         "GBps": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    res = {
+        "cfg": cfg, "lay": lay, "k": k, "nnz": nnz, "master": master, "ms_step": ms_step,
+        "stage_ms": stage_ms, "stages": stage_rep, "bytes": byts, "dense": dense, "graph": graph,
+        "serial": serial, "paged": paged, "transfer": transfer,
+        "compression": compression(counts, master, T, H, D, cfg.elem_bytes, lay.priv_len, L),
+    }
+    del kc, vc, q, pk, pv, kr, kx, ak, av, ds, out, ws_sel, ws_enc, ws_att
+    torch.cuda.empty_cache()
+    return res
+
+
+def config_summary(r):
+    """The per-workload entry of the JSON line."""
+    cfg, lay = r["cfg"], r["lay"]
+    N, T = cfg.n_agents, lay.n_tokens
+    return {
+        "n_agents": N, "n_layers": cfg.n_layers, "n_kv_heads": cfg.n_kv_heads, "shared_tokens": T,
+        "private_tokens_total": int(lay.priv_len.sum()), "diff_blocks": r["nnz"],
+        "ms_per_step": round(r["ms_step"], 4),
+        "agent_tokens_per_s": N * T / (r["ms_step"] * 1e-3),
+        "stages": {k: {f: v[f] for f in ("ms", "ms_median", "GBps", "frac_hbm_peak")} for k, v in r["stages"].items()},
+        "dense_comparator": None if r["dense"] is None else {
+            f: r["dense"][f] for f in ("ms", "speedup_fused_vs_dense", "alg_bytes_dense_over_fused", "frac_hbm_peak")},
+    }
+
+
+PER_CONFIG = ("qwen7b_round", "qwen14b_round", "qwen7b_scaleout")
+# bounded oracle samples for the per-workload CPU figures (the 64-agent round's
+# full oracle pass takes several CPU-minutes)
+CPU_SAMPLE_LAYERS = {"qwen7b_scaleout": range(0, 4)}
+
+
+def main():
+    args = parse()
+    if args.pmc_summary:
+        if len(args.pmc_summary) not in (2, 3):
+            raise SystemExit("--pmc-summary FETCH_CSV WRITE_CSV [BENCH_LOG]")
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.config, *args.pmc_summary[2:])
+        return
+    if args.trace_summary:
+        trace_summary(*args.trace_summary)
+        return
+    if args.sq_summary:
+        sq_summary(*args.sq_summary)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the collective reuse path here runs on a single "
+              "MI355X (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    # the oracle's worker processes start before this process touches the GPU
+    pool = n_pool = None
+    if not args.no_cpu_baseline:
+        pool, n_pool = make_oracle_pool()
+
+    import torch
+
+    dev = "cuda"
+    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flush = flush_buf.zero_ if not args.no_flush else (lambda: None)
+
     if args.calib_copy:
         # a plain copy of known size (1 GiB read + 1 GiB written) for scaling
         # the FETCH_SIZE / WRITE_SIZE counters of a rocprofv3 --pmc run
@@ -690,87 +874,20 @@ def main():
             cdst.copy_(csrc)
         torch.cuda.synchronize()
         del csrc, cdst
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for s in range(args.steps):
-        step(evs[s])
-    t_end.record()
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_step = total_ms / args.steps
-    stage_all = {name: [evs[s][j].elapsed_time(evs[s][j + 1]) for s in range(args.steps)]
-                 for j, name in enumerate(stages)}
-    stage_ms = {name: float(np.mean(v)) for name, v in stage_all.items()}
-    if ds.nnz() != nnz or nnz > cap:
-        raise RuntimeError("diff encode changed between steps or overflowed")
 
-    # ---- dense comparator on the same round (outside the step)
-    dense = None
-    if not args.no_dense:
-        kd = torch.empty((N, L, T, H, D), dtype=cfg.torch_dtype, device=dev)
-        vd = torch.empty_like(kd)
-        outd = torch.empty_like(out)
-        ws_d = torch.empty(max(tdx.decode_attn_dense_workspace(shape, dl, max_priv), 16), dtype=torch.uint8, device=dev)
+    main_r = measure(args.config, args, legs=True, flush=flush)
+    per_config = {args.config: config_summary(main_r)}
+    for nm in ([] if args.no_per_config else [c for c in PER_CONFIG if c != args.config]):
+        per_config[nm] = config_summary(measure(nm, args, legs=False, flush=flush))
 
-        def dense_step():
-            tdx.restore_dense(shape, dl, ak, av, ds, kd, vd, master_sel=sel["master"])
-            tdx.decode_attn_dense(shape, dl, q, po, pk, pv, max_priv, kd, vd, out=outd, ws=ws_d)
-
-        for _ in range(max(1, args.warmup)):
-            dense_step()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(args.steps):
-            dense_step()
-        e1.record()
-        torch.cuda.synchronize()
-        dense_ms = e0.elapsed_time(e1) / args.steps
-        diff = (outd.float() - out.float()).abs().max().item()
-        dense = {"ms": dense_ms, "fused_ms": stage_ms["restore_attn"],
-                 "speedup_fused_vs_dense": dense_ms / stage_ms["restore_attn"],
-                 "max_abs_fused_minus_dense": diff}
-        del kd, vd
-
-    # ---- the same step captured once in a HIP graph and replayed
-    graph = None
-    if not args.no_graph:
-        graph = graph_step(step, args.steps, max(1, args.warmup), ms_step, out)
-
-    # ---- serial per-agent reuse (the per-request fallback) on the same inputs
-    serial = None
-    if not args.no_serial:
-        serial = serial_path(shape1, lay, kc, kx, k, cfg.check_layer, kr, args.steps,
-                             max(1, args.warmup), stage_ms["rerotate"] + stage_ms["select"])
-
-    paged = None
-    if not args.no_paged:
-        paged = paged_path(cfg, lay, shape, shape1, dl, kc, kr, kx, k, sel["master"], ak, av, q, po, pk, pv,
-                           max_priv, out, args.steps, max(1, args.warmup), stage_ms, nnz)
-
-    transfer = None
-    if not args.no_transfer:
-        transfer = transfer_path(cfg, lay, shape, dl, ds, nnz, ak[master], av[master], q, pk, pv)
-
-    byts = stage_bytes(cfg, lay, nnz, k)
-    stage_rep = {}
-    for name in stages:
-        gbs = byts[name] / (stage_ms[name] * 1e-3) / 1e9
-        stage_rep[name] = {"ms": round(stage_ms[name], 4), "ms_median": round(float(np.median(stage_all[name])), 4),
-                           "ms_min": round(float(np.min(stage_all[name])), 4), "alg_GB": round(byts[name] / 1e9, 4),
-                           "GBps": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
-    if dense is not None:
-        gbs = byts["dense"] / (dense["ms"] * 1e-3) / 1e9
-        dense.update({"alg_GB": round(byts["dense"] / 1e9, 3), "GBps": round(gbs, 1)})
+    cfg, lay = main_r["cfg"], main_r["lay"]
+    N, L, T, H, Hq, D = cfg.n_agents, cfg.n_layers, lay.n_tokens, cfg.n_kv_heads, cfg.n_q_heads, cfg.head_dim
+    stage_ms, stage_rep, byts = main_r["stage_ms"], main_r["stages"], main_r["bytes"]
+    stages = list(stage_rep)
     dom = max(stages, key=lambda n: stage_ms[n])
     reuse_ms = stage_ms["rerotate"] + stage_ms["select"]
     agent_tokens = N * T
+    ms_step = main_r["ms_step"]
     res = {
         "metric": "collective reuse agent-tokens/s; fused restore-attn GB/s (% of HBM peak)",
         "value": agent_tokens / (ms_step * 1e-3),
@@ -786,8 +903,11 @@ def main():
         "data": "synthetic (seeded N(0,1) K/V/q, generated in HBM)",
         "config": {"workload": cfg.name, "n_agents": N, "n_layers": L, "n_kv_heads": H,
                    "n_q_heads": Hq, "head_dim": D, "shared_tokens": T,
-                   "private_tokens_total": int(lay.priv_len.sum()), "select_k": k,
-                   "diff_blocks": nnz, "master": master, "parallelism": "single GPU"},
+                   "private_tokens_total": int(lay.priv_len.sum()), "select_k": main_r["k"],
+                   "diff_blocks": main_r["nnz"], "master": main_r["master"], "parallelism": "single GPU"},
+        "timing": (f"each step timed by its own HIP events on the launch stream; a {FLUSH_BYTES >> 30} GiB "
+                   f"scratch write before every step (outside its events) flushes the last-level cache"
+                   if not args.no_flush else "steps timed by HIP events, no cache flush"),
         "roofline": {"bound": "hbm", "kernel": ENTRY[dom], "stage": dom,
                      "achieved": round(stage_rep[dom]["GBps"], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -798,17 +918,28 @@ def main():
                                "frac_hbm_peak": stage_rep["restore_attn"]["frac_hbm_peak"]},
         "collective_reuse_agent_tokens_per_s": agent_tokens / (reuse_ms * 1e-3),
         "stages": stage_rep,
-        "dense_comparator": dense,
-        "graph_replay": graph,
-        "serial_per_agent": serial,
-        "paged_layout": paged,
-        "transfer_restore": transfer,
-        "compression": compression(counts, master, T, H, D, cfg.elem_bytes, lay.priv_len, L),
+        "per_config": per_config,
+        "dense_comparator": main_r["dense"],
+        "graph_replay": main_r["graph"],
+        "serial_per_agent": main_r["serial"],
+        "paged_layout": main_r["paged"],
+        "transfer_restore": main_r["transfer"],
+        "compression": main_r["compression"],
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, lay, cfg.pct)
+    if pool is not None:
+        res["cpu_baseline"] = cpu_baseline(pool, n_pool, cfg.name)
         res["gpu_vs_oracle"] = res["value"] / res["cpu_baseline"]["value"]
+        for nm, pc in per_config.items():
+            if nm == cfg.name:
+                pc["cpu_oracle"] = {f: res["cpu_baseline"][f] for f in ("value", "cores", "round_s")}
+            elif not args.no_per_config_cpu:
+                cb = cpu_baseline(pool, n_pool, nm, CPU_SAMPLE_LAYERS.get(nm))
+                pc["cpu_oracle"] = {f: cb[f] for f in ("value", "cores", "round_s", "sample")}
+            if "cpu_oracle" in pc:
+                pc["gpu_vs_oracle"] = pc["agent_tokens_per_s"] / pc["cpu_oracle"]["value"]
+        pool.close()
+        pool.join()
     print(json.dumps(res), flush=True)
 
 

@@ -236,12 +236,14 @@ def queries(cfg: Config, device="cpu") -> torch.Tensor:
                    cfg, device, 0, _S_Q)
 
 
-def private_kv(cfg: Config, lay: Layout, device="cpu"):
-    """Private-history K/V, [L][sum P_i][Hkv][D] each, agents concatenated."""
+def private_kv(cfg: Config, lay: Layout, device="cpu", layers: Optional[Sequence[int]] = None):
+    """Private-history K/V, [L][sum P_i][Hkv][D] each, agents concatenated
+    (``layers``: only those layers, each drawn as in the whole round)."""
+    layers = range(cfg.n_layers) if layers is None else layers
     ptot = int(lay.priv_len.sum())
     shape = (ptot, cfg.n_kv_heads, cfg.head_dim)
-    k = torch.stack([_normal(shape, cfg, device, l, _S_PRIV_K) for l in range(cfg.n_layers)])
-    v = torch.stack([_normal(shape, cfg, device, l, _S_PRIV_V) for l in range(cfg.n_layers)])
+    k = torch.stack([_normal(shape, cfg, device, l, _S_PRIV_K) for l in layers])
+    v = torch.stack([_normal(shape, cfg, device, l, _S_PRIV_V) for l in layers])
     return k, v
 
 
