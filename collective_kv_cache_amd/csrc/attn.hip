@@ -181,38 +181,44 @@ __device__ __forceinline__ i16x4 ld_tr16(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
 }
 
-// The PV operand of one tile from row-major LDS V [16][VS] (bf16):
-// va[dt][j] = V[token 4*q4 + j][dim 16*dt + c16].
-template <int D>
-__device__ __forceinline__ void gather_v(const uint16_t* vt, int VS, int q4, int c16, i16x4* va) {
-  constexpr int DT = D / 16;
-  const uint16_t* base = vt + (4 * q4 + (c16 >> 2)) * VS + 4 * (c16 & 3);
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) va[dt] = ld_tr16(base + 16 * dt);
+// Maximum over the four lanes that hold one query row (lanes l, l ^ 16,
+// l ^ 32, l ^ 48): two row swaps on the VALU (v_permlane16_swap,
+// v_permlane32_swap), each followed by a max of the two halves.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float row_max4(float x) {
+  u32x2 r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+
+// The running reference m of a row may lag its true maximum by up to
+// kRescaleLag (log2 units): weights exp2(z - m) then stay below
+// 2^kRescaleLag, and O and l are rescaled only when some row of the wave
+// passes its reference by more than that.  O / l is the same quotient
+// whichever reference is used, and the records carry their reference.
+constexpr float kRescaleLag = 8.0f;
 
 // Online softmax + PV for one tile.  z: the 4 logits (log2 domain) of the
 // lane's row at tokens 4*q4 .. 4*q4+3 (-inf = masked).  While a row has no
-// valid key, mnew = -inf: 0 is used as the reference so every exp2 is of -inf
-// (-> 0) and nothing turns into NaN; the path stays wave-uniform around the
-// MFMAs.
+// valid key its reference is -inf and 0 is used in its place, so every
+// weight is exp2(-inf) = 0 and nothing turns into NaN; the path stays
+// wave-uniform around the MFMAs.
 template <int D>
 __device__ __forceinline__ void softmax_pv(RowState<D>& st, const float z[4], const i16x4* va) {
   constexpr int DT = D / 16;
-  float tmax = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-  const float mnew = fmaxf(st.m, tmax);
-  const float mref = (mnew == -INFINITY) ? 0.0f : mnew;
-  // O and l are rescaled only when some row's maximum grew; otherwise every
-  // lane's factor is exactly 1 (or 0 * 0 for a row with no key yet) and the
-  // wave skips the multiplies as a whole
-  float alpha = 1.0f;
-  const bool grow = __builtin_amdgcn_ballot_w64(mnew > st.m) != 0;
-  if (grow) alpha = __builtin_amdgcn_exp2f(st.m - mref);
-  st.m = mnew;
-  // weights in (0, 1]: v_exp_f32, then one v_cvt_pk_bf16_f32 (round to
-  // nearest even) per pair; the sum uses the same rounded weights
+  const float tmax = row_max4(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+  if (__builtin_amdgcn_ballot_w64(tmax > st.m + kRescaleLag) != 0) {
+    const float mnew = fmaxf(st.m, tmax);
+    const float alpha = st.m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(st.m - mnew);
+    st.m = mnew;
+    st.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) st.o[dt] *= alpha;
+  }
+  const float mref = st.m == -INFINITY ? 0.0f : st.m;
+  // weights in (0, 2^kRescaleLag]: v_exp_f32, then one v_cvt_pk_bf16_f32
+  // (round to nearest even) per pair; the sum uses the same rounded weights
   const uint32_t w01 = pack_bf16(__builtin_amdgcn_exp2f(z[0] - mref), __builtin_amdgcn_exp2f(z[1] - mref));
   const uint32_t w23 = pack_bf16(__builtin_amdgcn_exp2f(z[2] - mref), __builtin_amdgcn_exp2f(z[3] - mref));
   const float psum = (__uint_as_float(w01 << 16) + __uint_as_float(w01 & 0xffff0000u)) +
@@ -222,11 +228,7 @@ __device__ __forceinline__ void softmax_pv(RowState<D>& st, const float z[4], co
   pb[1] = (short)(w01 >> 16);
   pb[2] = (short)(w23 & 0xffffu);
   pb[3] = (short)(w23 >> 16);
-  st.l = st.l * alpha + psum;
-  if (grow) {
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) st.o[dt] *= alpha;
-  }
+  st.l += psum;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) st.o[dt] = mfma16(va[dt], pb, st.o[dt]);
 }
@@ -248,68 +250,116 @@ __device__ __forceinline__ void write_record(float* rec, const RowState<D>& st, 
 // ---- shared_kernel: Master tiles staged once, all agents' query rows ------------
 //
 // One workgroup per (agent group, Master split, layer, KV head).  The split's
-// tiles are taken shared block by shared block: the wave's 16 query rows are
-// rotated once per block, R(-Delta(i,b)) q, which is RoPE recovery moved to
+// 16-token Master tiles arrive in a ring of NB LDS slots through direct
+// global-to-LDS loads (global_load_lds_dwordx4): each wave's load instruction
+// moves 1 KB of a tile (4 rows of 128 dims or 8 of 64) straight into the
+// slot, so NB-2 tiles stay in flight per workgroup without holding any in
+// registers.  A slot keeps K and V rows unpadded, 16-byte chunk ch of row t
+// at position ch ^ (t % chunks per row): each lane picks the global chunk
+// that belongs at its LDS position, which spreads the MFMA operand reads
+// over the banks.
+//
+// Step n (tile n of the split): wait until this wave has at most the loads
+// of tiles n+1 .. n+NB-2 outstanding, barrier (tile n is in LDS and every
+// wave is done with tile n-1), issue the loads of tile n+NB-1 into tile
+// n-1's slot, then use tile n.  Loads past the split's last tile re-read it
+// into the freed slot, so every step issues the same number of loads and
+// one wait count serves all steps.
+//
+// The wave's 16 query rows (agents stacked into one MFMA tile) are rotated
+// once per shared block, R(-Delta(i,b)) q, which is RoPE recovery moved to
 // the query side (q . R(Delta) k = (R(-Delta) q) . k), so the Master's
-// canonical key rows are used as they are stored; the block's tiles
-// stream through a PD-stage register pipeline (each thread's chunks of the
-// tile's K and V rows), the tile in use sitting in one of two LDS buffers.
-// Step n: issue the loads of tile n+PD-1, use tile n, store tile n+1 into the
-// other buffer, barrier.  No branch surrounds a load or a store of a stage
-// inside a block, so the wait before a stage leaves the younger tiles in
-// flight; fill steps skip the dot products, and a block stops after its
-// last tile.  A tile that straddles two shared blocks is
-// used once for each, with the other block's rows masked.
+// canonical key rows are used as stored.  A tile that straddles shared
+// blocks is used once for each, with the other blocks' rows masked; rows of
+// an agent whose diff record holds the tile are masked here (the stream
+// kernel attends that agent's own rows).
 
-#ifndef TDX_SH_PD
-#define TDX_SH_PD 4
+#ifndef TDX_SH_NB
+#define TDX_SH_NB 6
 #endif
 #ifndef TDX_SH_TARGET_WG
 #define TDX_SH_TARGET_WG 1024
 #endif
 
-template <typename E, int D>
-struct ShStage {
-  static constexpr int CH = D / 8;                         // 8-element chunks per row
-  static constexpr int CPT = 2 * kTile * CH / kShThreads;  // chunks per thread (K then V)
-  static constexpr int LPC = (int)sizeof(E) / 2;           // 16-byte loads per chunk
-  u32x4 kv[CPT * LPC];
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One Master tile slot: [K rows][V rows], 16 rows of RB bytes each.
+template <int D>
+struct ShTile {
+  static constexpr int RB = D * 2;                         // bytes of one bf16 row of a head
+  static constexpr int CPR = RB / 16;                      // 16-byte chunks per row
+  static constexpr int BYTES = 2 * kTile * RB;             // K and V
+  static constexpr int RPI = 1024 / RB;                    // rows per wave load instruction
+  static constexpr int IPT = kTile * RB / 1024;            // load instructions per tensor
+  static constexpr int LPT = BYTES / (kShThreads * 16);    // loads per thread per tile
+  static_assert(LPT * kShWaves == 2 * IPT, "every wave issues the same loads");
 };
 
-// Master tiles are read by every agent group of a (layer, head, split); a
-// plain load lets the groups that run together on one XCD share its L2 lines.
-#ifndef TDX_SH_NT
-#define TDX_SH_NT 0
-#endif
-template <typename E>
-__device__ __forceinline__ u32x4 sh_ld(const E* p) {
-#if TDX_SH_NT
-  return ld16_nt(p);
-#else
-  return ld16(p);
-#endif
+__device__ __forceinline__ int sh_swz(int t, int ch, int cpr) { return ch ^ (t % cpr); }
+
+// ds_read_b64_tr_b16 (as ld_tr16) issued as inline asm: the compiler cannot
+// tell a ring slot being read from the slot the pending global-to-LDS loads
+// write, and would otherwise wait for every one of them before a transposed
+// read.  The caller waits for the results with lds_wait.
+__device__ __forceinline__ i16x4 ld_tr16_nowait(const void* p) {
+  i16x4 r;
+  const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+  return r;
 }
+__device__ __forceinline__ u32x4 ld_b128_nowait(const void* p) {
+  u32x4 r;
+  const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+  return r;
+}
+// Wait until at most N of this wave's LDS reads are outstanding (LDS reads
+// complete in order); the operands tie the K operand read before them.
+template <int N, int KD>
+__device__ __forceinline__ void lds_wait_k(u32x4 (&k)[KD]) {
+  static_assert(KD == 2 || KD == 4, "K chunks");
+  if constexpr (KD == 4)
+    asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(k[0]), "+v"(k[1]), "+v"(k[2]), "+v"(k[3]) : "n"(N));
+  else
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(k[0]), "+v"(k[1]) : "n"(N));
+}
+// Wait for this wave's LDS reads; the operands tie the values read by
+// ld_tr16_nowait to this point, so no use of them is scheduled before it.
+template <int N>
+__device__ __forceinline__ void lds_wait(i16x4 (&v)[N]) {
+  static_assert(N == 4 || N == 8, "dim tiles");
+  if constexpr (N == 8)
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]));
+  else
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
+}
+
+// s_waitcnt immediate (gfx9 layout): vmcnt <= V, lgkmcnt 0, expcnt not waited
+template <int V>
+struct VmWait {
+  static_assert(V >= 0 && V < 64, "vmcnt range");
+  static constexpr int imm = (V & 15) | (7 << 4) | ((V >> 4) << 14);
+};
 
 #ifndef TDX_SH_WPE
 #define TDX_SH_WPE 3
 #endif
-template <typename E, int D, int PD, bool PAGED>
+template <typename E, int D, int NB, bool PAGED>
 __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(TDX_SH_WPE))) void shared_kernel(AttnArgs a) {
-  using St = ShStage<E, D>;
+  using Tl = ShTile<D>;
   constexpr int KD = D / 32;
   constexpr int DT = D / 16;
   constexpr int HALF = D / 2;
-  constexpr int VS = D + 8;  // padded LDS row stride (bf16)
-  constexpr int CH = St::CH;
-  constexpr int CPT = St::CPT;
-  constexpr int LPC = St::LPC;
+  constexpr int RB = Tl::RB;
+  constexpr int CPR = Tl::CPR;
   static_assert(sizeof(E) == 2, "bf16 caches (fp32 ones take the fp32 kernel)");
-  static_assert(2 * kTile * CH % kShThreads == 0, "tile chunks per thread");
+  static_assert(NB >= 3, "ring slots");
   extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t* kbuf = reinterpret_cast<uint16_t*>(smem);  // [2][16][VS]
-  uint16_t* vbuf = kbuf + 2 * kTile * VS;              // [2][16][VS]
-  int32_t* sblk = reinterpret_cast<int32_t*>(vbuf + 2 * kTile * VS);  // [B+1]
-  uint8_t* dflag = reinterpret_cast<uint8_t*>(sblk + a.B + 1);        // [AGS][TPG]
+  unsigned char* ring = smem;                                            // [NB][BYTES]
+  int32_t* sblk = reinterpret_cast<int32_t*>(smem + NB * Tl::BYTES);     // [B+1]
+  const int NW = (a.TPG + 31) / 32;                                      // flag words per agent
+  uint32_t* dbits = reinterpret_cast<uint32_t*>(sblk + a.B + 1);         // [AGS][NW]
 
   // Hardware deals workgroups round-robin to the 8 XCDs; give each XCD a
   // contiguous run of logical ids so that the agent groups sharing a Master
@@ -336,20 +386,17 @@ __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(TDX_
   const int q4 = lane / 16, c16 = lane % 16;
 
   for (int x = tid; x <= a.B; x += kShThreads) sblk[x] = a.blk_start[x];
-  for (int x = tid; x < a.AGS * a.TPG; x += kShThreads) dflag[x] = 0;
-  // zeroed tile buffers: the first fill steps read them under a full mask
-  for (int x = tid; x < 4 * kTile * VS / 8; x += kShThreads)
-    reinterpret_cast<u32x4*>(kbuf)[x] = u32x4{0, 0, 0, 0};
+  for (int x = tid; x < a.AGS * NW; x += kShThreads) dbits[x] = 0;
   __syncthreads();
-  // flag (agent, tile) pairs whose block is in the agent's diff row: those
-  // rows take the tile from the agent's own record (agent_kernel); read after
-  // the pipeline's first barrier
+  // flag (agent, tile) pairs whose block is in the agent's diff row, one bit
+  // per tile: those rows take the tile from the agent's own record (stream
+  // kernel)
   for (int al = wave; al < na; al += kShWaves) {
     const int r = (a0 + al) * a.L + l;
     const int e1 = a.diff_off[r + 1];
     for (int e = a.diff_off[r] + lane; e < e1; e += kWave) {
       const int beta = a.diff_idx[e];
-      if (beta >= b0 && beta < b1) dflag[al * a.TPG + (beta - b0)] = 1;
+      if (beta >= b0 && beta < b1) atomicOr(&dbits[al * NW + ((beta - b0) >> 5)], 1u << ((beta - b0) & 31));
     }
   }
 
@@ -373,98 +420,130 @@ __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(TDX_
   const E* qrow = static_cast<const E*>(a.q) + (((size_t)agent * a.L + l) * a.Hq + hq) * D;
   const float2* tabrow = a.tab + (size_t)agent * a.B * HALF;
 
-  auto load = [&](int tile, St& S) {
-    const size_t trow = PAGED ? ((size_t)l * a.mpm.n_pages + page_at(a.mpm, mrow, tile)) * kTile
-                              : (size_t)tile * kTile;
+  // the lane's query elements 32k + 8*q4 .. +7 (element e < D/2 pairs with
+  // e + D/2, which sits in chunk k + KD/2 of the same lane)
+  u32x4 qraw[KD];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + c * kShThreads;
-      const int tensor = idx / (kTile * CH);
-      const int rem = idx % (kTile * CH);
-      const E* src = (tensor ? mv : mk) + (trow + rem / CH) * rowHD + (rem % CH) * 8;
+  for (int k = 0; k < KD; ++k) qraw[k] = ld16(qrow + 32 * k + 8 * q4);
+  // rotated by -Delta(agent, b) in fp32 and rounded to bf16
+  u32x4 qr[KD];
+  auto rotate = [&](int b) {
+    const float2* cs = tabrow + (size_t)b * HALF;
 #pragma unroll
-      for (int p = 0; p < LPC; ++p) S.kv[c * LPC + p] = sh_ld(src + p * (8 / LPC));
+    for (int k = 0; k < KD / 2; ++k) {
+      const int e0 = 32 * k + 8 * q4;
+      float lo[8], hi[8], olo[8], ohi[8];
+      Fmt<uint16_t>::unpack(qraw[k], lo);
+      Fmt<uint16_t>::unpack(qraw[k + KD / 2], hi);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float2 c = cs[e0 + j];
+        // R(-phi): (x, y) -> (x cos + y sin, y cos - x sin)
+        olo[j] = lo[j] * c.x + hi[j] * c.y;
+        ohi[j] = hi[j] * c.x - lo[j] * c.y;
+      }
+      qr[k] = Fmt<uint16_t>::pack(olo);
+      qr[k + KD / 2] = Fmt<uint16_t>::pack(ohi);
     }
   };
-  auto store = [&](const St& S, int buf) {
+  __syncthreads();
+  int b = block_of(sblk, a.B, b0 * kTile);  // the block of the split's first token
+  int bs = sblk[b], be = sblk[b + 1];       // its tokens [bs, be)
+  if (has_rows) rotate(b);
+  // everything above is complete before the ring's loads start, so that the
+  // ring's wait counts see only its own loads
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // this thread's loads of tile u into slot s (tiles past the split re-read its last)
+  auto issue = [&](int u, int s) {
+    const int tile = min(u, b1 - 1);
+    const size_t trow = PAGED ? ((size_t)l * a.mpm.n_pages + page_at(a.mpm, mrow, tile)) * kTile
+                              : (size_t)tile * kTile;
+    unsigned char* slot = ring + s * Tl::BYTES;
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + c * kShThreads;
-      const int tensor = idx / (kTile * CH);
-      const int rem = idx % (kTile * CH);
-      uint16_t* dst = (tensor ? vbuf : kbuf) + (buf * kTile + rem / CH) * VS + (rem % CH) * 8;
-      *reinterpret_cast<u32x4*>(dst) = S.kv[c];
+    for (int p = 0; p < Tl::LPT; ++p) {
+      const int inst = wave * Tl::LPT + p;  // K instructions first, then V
+      const int tensor = inst / Tl::IPT;
+      const int r0 = (inst % Tl::IPT) * Tl::RPI;
+      const int t = r0 + lane / CPR, pos = lane % CPR;
+      const E* src = (tensor ? mv : mk) + (trow + t) * rowHD + sh_swz(t, pos, CPR) * 8;
+      __builtin_amdgcn_global_load_lds((void*)src, (lds_void_t*)(slot + tensor * kTile * RB + r0 * RB), 16, 0, 0);
     }
   };
 
-  // shared blocks that intersect this split's tiles, one after the other
-  for (int b = block_of(sblk, a.B, b0 * kTile); b < a.B && sblk[b] < b1 * kTile; ++b) {
-    const int bs = sblk[b], be = sblk[b + 1];
-    const int ta = max(b0, bs / kTile), tb = min(b1, (be + kTile - 1) / kTile);
-    if (be <= bs || ta >= tb) continue;  // empty block (uniform)
-    const int nt = tb - ta;
-    // the lane's query elements 32k + 8*q4 .. +7 rotated by -Delta(agent, b)
-    // in fp32 and rounded to bf16; element e < D/2 pairs with e + D/2, which
-    // sits in chunk k + KD/2 of the same lane
-    u32x4 qr[KD];
-    {
-      const float2* cs = tabrow + (size_t)b * HALF;
+  // use tokens [t_lo, t_hi) of tile u (in slot s) with the current rotation;
+  // fw: the lane's agent's diff-flag word of the tile
+  auto compute = [&](int u, int s, int t_lo, int t_hi, uint32_t fw) {
+    const unsigned char* kt = ring + s * Tl::BYTES;
+    const unsigned char* vt = kt + kTile * RB;
+    // the K and V operands of the tile in one round trip: K first, then V,
+    // whose latency the QK products cover
+    u32x4 kop[KD];
 #pragma unroll
-      for (int k = 0; k < KD / 2; ++k) {
-        const int e0 = 32 * k + 8 * q4;
-        float lo[8], hi[8], olo[8], ohi[8];
-        load8(qrow + e0, lo);
-        load8(qrow + HALF + e0, hi);
+    for (int k = 0; k < KD; ++k) kop[k] = ld_b128_nowait(kt + c16 * RB + sh_swz(c16, 4 * k + q4, CPR) * 16);
+    // PV operand: va[dt][j] = V[token 4*q4 + j][dim 16*dt + c16]; this lane
+    // addresses row 4*q4 + c16/4, dims 16*dt + 4*(c16%4)
+    i16x4 va[DT];
+    const int vrow = 4 * q4 + (c16 >> 2);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float2 c = cs[e0 + j];
-          // R(-phi): (x, y) -> (x cos + y sin, y cos - x sin)
-          olo[j] = lo[j] * c.x + hi[j] * c.y;
-          ohi[j] = hi[j] * c.x - lo[j] * c.y;
-        }
-        qr[k] = Fmt<uint16_t>::pack(olo);
-        qr[k + KD / 2] = Fmt<uint16_t>::pack(ohi);
-      }
-    }
-    // use tile ta + n (buffer buf)
-    auto compute = [&](int n, bool live, int buf) {
-      if (!has_rows) return;  // wave-uniform; no loads or barriers inside
-      const uint16_t* kt = kbuf + buf * kTile * VS;
-      const uint16_t* vt = vbuf + buf * kTile * VS;
-      u32x4 kop[KD];
+    for (int dt = 0; dt < DT; ++dt)
+      va[dt] = ld_tr16_nowait(vt + vrow * RB + sh_swz(vrow, 2 * dt + ((c16 & 3) >> 1), CPR) * 16 + (c16 & 1) * 8);
+    lds_wait_k<DT>(kop);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < KD; ++k) kop[k] = *reinterpret_cast<const u32x4*>(kt + c16 * VS + 32 * k + 8 * q4);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < KD; ++k) acc = mfma32(kop[k], qr[k], acc);
+    const bool on = valid && !((fw >> ((u - b0) & 31)) & 1u);
+    float z[4];
+    if (t_lo == u * kTile && t_hi == u * kTile + kTile) {  // the whole tile (uniform)
+      const float bias = on ? 0.0f : -INFINITY;
 #pragma unroll
-      for (int k = 0; k < KD; ++k) acc = mfma32(kop[k], qr[k], acc);
-      const int tile = ta + min(max(n, 0), nt - 1);
-      const bool on = live && valid && !dflag[(agent - a0) * a.TPG + (tile - b0)];
-      float z[4];
+      for (int j = 0; j < 4; ++j) z[j] = fmaf(acc[j], a.scale_log2, bias);
+    } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int tt = tile * kTile + 4 * q4 + j;
-        z[j] = (on && tt >= bs && tt < be) ? acc[j] * a.scale_log2 : -INFINITY;
+        const int tt = u * kTile + 4 * q4 + j;
+        z[j] = (on && tt >= t_lo && tt < t_hi) ? acc[j] * a.scale_log2 : -INFINITY;
       }
-      i16x4 va[DT];
-      gather_v<D>(vt, VS, q4, c16, va);
-      softmax_pv<D>(st, z, va);
-    };
-    // the PD-1 fill steps only load and stage; the block ends at its last
-    // tile (compute reads LDS and registers only, so the branch around it
-    // leaves the loads' waits as they are)
-    St S[PD] = {};
-    for (int n0 = -(PD - 1); n0 < nt; n0 += PD) {
+    }
+    lds_wait(va);
+    softmax_pv<D>(st, z, va);
+  };
+
+  const int nt = b1 - b0;
+  uint32_t fw = 0;  // the lane's agent's diff flags of the current 32 tiles
 #pragma unroll
-      for (int k = 0; k < PD; ++k) {
-        const int n = n0 + k;  // tile ta + n used in this step (workgroup-uniform)
-        if (n >= nt) break;
-        load(ta + min(n + PD - 1, nt - 1), S[(k + PD - 1) % PD]);
-        if (n >= 0) compute(n, true, n & 1);
-        store(S[(k + 1) % PD], (n + 1) & 1);
-        __syncthreads();
+  for (int s = 0; s < NB - 1; ++s) issue(b0 + s, s);
+  for (int n = 0; n < nt; ++n) {
+    // tile n is in LDS once this wave's loads of it are done (the NB-2
+    // younger tiles may stay in flight) and every wave has passed the barrier
+    __builtin_amdgcn_s_waitcnt(VmWait<Tl::LPT * (NB - 2)>::imm);
+    asm volatile("s_barrier" ::: "memory");
+    issue(b0 + n + NB - 1, (n + NB - 1) % NB);
+    if (has_rows) {  // wave-uniform: no loads or barriers inside
+      const int u = b0 + n, t0 = u * kTile, t1 = t0 + kTile;
+      if (((u - b0) & 31) == 0) fw = dbits[(agent - a0) * NW + ((u - b0) >> 5)];
+      if (be <= t0) {  // the block ended before this tile: the one holding t0
+        do {
+          ++b;
+          be = sblk[b + 1];
+        } while (be <= t0);
+        bs = sblk[b];
+        rotate(b);
+      }
+      for (;;) {
+        compute(u, n % NB, max(bs, t0), min(be, t1), fw);
+        if (be >= t1) break;
+        bs = be;  // the tile goes on in the next non-empty block
+        do {
+          ++b;
+          be = sblk[b + 1];
+        } while (be <= bs);
+        rotate(b);
       }
     }
   }
+  // no load may still write this workgroup's LDS once it exits
+  __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
 
   if (has_rows) {
     float lsum = st.l;
@@ -1116,8 +1195,10 @@ struct StreamCfg {
   }
 };
 
-size_t shared_lds(int D, int B, const Plan& p) {
-  return (size_t)4 * kTile * (D + 8) * 2 + (size_t)(B + 1) * 4 + (size_t)p.AGS * p.TPG;
+// the Master-tile kernel's LDS: its tile ring of nb slots, blk_start, the
+// diff flags (one bit per agent and tile)
+size_t shared_lds(int D, int B, const Plan& p, int nb) {
+  return (size_t)nb * 2 * kTile * D * 2 + (size_t)(B + 1) * 4 + (size_t)p.AGS * ((p.TPG + 31) / 32) * 4;
 }
 
 template <typename E, int D, int MODE, bool PAGED>
@@ -1133,10 +1214,17 @@ hipError_t launch_attn_t(const Dims& d, AttnArgs a, const Plan& p, E* out, hipSt
   a.dcap = p.dcap;
   hipError_t e;
   if (MODE == FUSED) {
-    const size_t lds = shared_lds(D, d.B, p);
-    if (lds > 64 * 1024) return hipErrorInvalidValue;
+    // a ring of TDX_SH_NB slots, or of 3 when blk_start and the diff flags
+    // leave too little of the 64 KB
     const int grid = (p.n_sh_wg + 7) / 8 * 8;
-    hipLaunchKernelGGL((shared_kernel<E, D, TDX_SH_PD, PAGED>), dim3(grid), dim3(kShThreads), lds, s, a);
+    const size_t lds = shared_lds(D, d.B, p, TDX_SH_NB);
+    if (lds <= 64 * 1024) {
+      hipLaunchKernelGGL((shared_kernel<E, D, TDX_SH_NB, PAGED>), dim3(grid), dim3(kShThreads), lds, s, a);
+    } else {
+      const size_t lds3 = shared_lds(D, d.B, p, 3);
+      if (lds3 > 64 * 1024) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((shared_kernel<E, D, 3, PAGED>), dim3(grid), dim3(kShThreads), lds3, s, a);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   a.qplain = static_cast<const uint16_t*>(a.q);  // bf16 queries are the MFMA operand as stored

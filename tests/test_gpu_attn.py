@@ -175,3 +175,18 @@ def test_master_selector_is_clamped():
 
     np.testing.assert_array_equal(run(-7), run(0))
     np.testing.assert_array_equal(run(N + 3), run(N - 1))
+
+
+def test_4096_shared_blocks_small_tile_ring():
+    # 4096 shared blocks of 16 tokens (the library's block limit): the Master-
+    # tile kernel's copy of blk_start fills 16 KB of LDS, so it runs with its
+    # smallest tile ring; every tile starts a new block (a rotation per tile)
+    cfg = CONFIGS["qwen7b_round"].scaled(n_agents=2, n_layers=1, n_kv_heads=1, n_q_heads=2, n_blocks=4096,
+                                         blk_len=(16, 16), priv=("uniform", 0, 40))
+    lay = make_layout(cfg)
+    assert lay.n_tokens == 65536
+    r = Round(cfg, lay, master=1)
+    ds = r.gpu_encode()
+    fused = host(r.gpu_fused(ds))
+    o_fused, _, _, _ = r.oracle_full()
+    assert_close(fused, o_fused, "fused, 4096 blocks")
