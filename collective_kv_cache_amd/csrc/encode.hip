@@ -74,51 +74,71 @@ __global__ __launch_bounds__(kFlagThreads) void flag_kernel(
   for (int i = tid; i < 2 * kMaxAgents; i += kFlagThreads) (&mark[0][0])[i] = 0;
   __syncthreads();
   const size_t layer_chunks = (size_t)nb * chunks;
+  const size_t agent_chunks = (size_t)L * layer_chunks;
   struct Blk {
     u32x4 k[KC], v[KC];
   };
-  // block p of the stream = item p / N, agent slot p % N (slot 0 = the Master,
-  // slot j > 0 = Mirror j - 1 = agent j - 1 + (j - 1 >= m)); lanes past the
-  // block end re-read its last chunk (the compare then sees equal data)
+  // Position in the block stream: block p = item p / N (w = blockIdx.x + G *
+  // (p / N), beta = w % nb, l = (w / nb) % L, slice cs = w / (nb * L)), agent
+  // slot j = p % N (slot 0 = the Master, slot j > 0 = Mirror j - 1 = agent
+  // j - 1 + (j - 1 >= m)).  Advanced one block at a time: the divisions run
+  // once per item, not per block.
+  struct Cursor {
+    int j, wi, beta, l, cs;
+    size_t item;  // chunk offset of the item's block in a cache (layer l, block beta)
+    __device__ void set_item(int w, int nb_, int L_, size_t lchunks, int chunks_) {
+      beta = w % nb_;
+      l = (w / nb_) % L_;
+      cs = w / (nb_ * L_);
+      item = (size_t)l * lchunks + (size_t)beta * chunks_;
+    }
+  };
+  const int b0w = (int)blockIdx.x;
+  Cursor lc{0, 0, 0, 0, 0, 0}, uc{0, 0, 0, 0, 0, 0};
+  lc.set_item(b0w, nb, L, layer_chunks, chunks);
+  uc = lc;
   const long long nblk = (long long)nw * N;
-  auto load = [&](long long p, Blk& B) {
-    p = p < nblk ? p : nblk - 1;
-    const int w = (int)blockIdx.x + (int)(p / N) * G;
-    const int j = (int)(p % N);
-    const int a = j == 0 ? m : (j - 1) + (j - 1 >= m);
-    const int beta = w % nb, l = (w / nb) % L, cs = w / (nb * L);
-    const size_t base = PAGED ? ((size_t)l * pm.n_pages + page_at(pm, a, beta)) * chunks
-                              : ((size_t)a * L + l) * layer_chunks + (size_t)beta * chunks;
-    const int c0 = cs * KC * kFlagThreads;
+  long long lp = 0;  // blocks loaded
+  auto advance = [&](Cursor& c) {
+    if (++c.j == N) {
+      c.j = 0;
+      ++c.wi;
+      c.set_item(b0w + c.wi * G, nb, L, layer_chunks, chunks);
+    }
+  };
+  // the next block of the stream; past the end the last block is re-read
+  // (its compare is not used)
+  auto load = [&](Blk& B) {
+    const int a = lc.j == 0 ? m : (lc.j - 1) + (lc.j - 1 >= m);
+    const size_t base = PAGED ? ((size_t)lc.l * pm.n_pages + page_at(pm, a, lc.beta)) * chunks
+                              : (size_t)a * agent_chunks + lc.item;
+    const int c0 = lc.cs * KC * kFlagThreads;
 #pragma unroll
     for (int q = 0; q < KC; ++q) {
       const int c = min(c0 + tid + q * kFlagThreads, chunks - 1);
       B.k[q] = ld16_nt(ak + base + c);
       B.v[q] = ld16_nt(av + base + c);
     }
+    if (++lp < nblk) advance(lc);
   };
   u32x4 mkr[KC], mvr[KC];
 #pragma unroll
   for (int q = 0; q < KC; ++q) mkr[q] = mvr[q] = u32x4{0, 0, 0, 0};
-  auto use = [&](long long p, const Blk& B, bool live) {
-    const int wi = (int)(p / N);
-    const int j = (int)(p % N);
+  auto use = [&](const Blk& B) {
+    const int j = uc.j;
     if (j == 0) {  // the Master's block (uniform)
 #pragma unroll
       for (int q = 0; q < KC; ++q) {
         mkr[q] = B.k[q];
         mvr[q] = B.v[q];
       }
-      if (mk_out != nullptr && live) {
-        const int w = (int)blockIdx.x + wi * G;
-        const int beta = w % nb, l = (w / nb) % L, cs = w / (nb * L);
-        const size_t obase = (size_t)l * layer_chunks + (size_t)beta * chunks;
+      if (mk_out != nullptr) {
 #pragma unroll
         for (int q = 0; q < KC; ++q) {
-          const int c = cs * KC * kFlagThreads + tid + q * kFlagThreads;
+          const int c = uc.cs * KC * kFlagThreads + tid + q * kFlagThreads;
           if (c < chunks) {
-            __builtin_nontemporal_store(B.k[q], mk_out + obase + c);
-            __builtin_nontemporal_store(B.v[q], mv_out + obase + c);
+            __builtin_nontemporal_store(B.k[q], mk_out + uc.item + c);
+            __builtin_nontemporal_store(B.v[q], mv_out + uc.item + c);
           }
         }
       }
@@ -131,25 +151,30 @@ __global__ __launch_bounds__(kFlagThreads) void flag_kernel(
         acc |= xk[0] | xk[1] | xk[2] | xk[3] | xv[0] | xv[1] | xv[2] | xv[3];
       }
       const int a = (j - 1) + (j - 1 >= m);
-      if (__builtin_amdgcn_ballot_w64(live && acc != 0) != 0 && lane == 0) mark[wi & 1][a] = 1;
+      if (__builtin_amdgcn_ballot_w64(acc != 0) != 0 && lane == 0) mark[uc.wi & 1][a] = 1;
     }
-    if (j == N - 1 && live) {  // the item's last block (uniform): publish its flags
+    if (j == N - 1) {  // the item's last block (uniform): publish its flags
       __syncthreads();
-      const int w = (int)blockIdx.x + wi * G;
-      const int beta = w % nb, l = (w / nb) % L, cs = w / (nb * L);
       for (int i = tid; i < N; i += kFlagThreads) {
-        flags[cs * slice_flags + ((size_t)i * L + l) * nb + beta] = mark[wi & 1][i];
-        mark[wi & 1][i] = 0;  // item wi + 2 reuses the buffer after item wi + 1's barrier
+        flags[uc.cs * slice_flags + ((size_t)i * L + uc.l) * nb + uc.beta] = mark[uc.wi & 1][i];
+        mark[uc.wi & 1][i] = 0;  // item wi + 2 reuses the buffer after item wi + 1's barrier
       }
     }
+    advance(uc);
   };
+  // PD-stage register pipeline: the first PD-1 blocks are loaded ahead, then
+  // each step loads one block and uses the oldest.  The unrolled body has no
+  // branch around a load, so the wait before a block is used leaves the
+  // younger blocks' loads outstanding.
   Blk S[PD] = {};
-  for (long long p0 = -(PD - 1); p0 < nblk; p0 += PD) {
+#pragma unroll
+  for (int k = 0; k < PD - 1; ++k) load(S[k]);
+  for (long long p0 = 0; p0 < nblk; p0 += PD) {
 #pragma unroll
     for (int k = 0; k < PD; ++k) {
-      const long long p = p0 + k;  // block used in this step (workgroup-uniform)
-      load(p + PD - 1, S[(k + PD - 1) % PD]);
-      use(p < 0 ? 0 : p, S[k], p >= 0 && p < nblk);
+      if (p0 + k >= nblk) break;  // uniform; the stream's last step
+      load(S[(k + PD - 1) % PD]);
+      use(S[k]);
     }
   }
 }
