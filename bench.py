@@ -104,7 +104,7 @@ def recorded_traffic(entry: str, workload: str):
 ENTRY_KERNELS = {
     "tdx_rerotate": ("rerotate_kernel",),
     "tdx_select_important": ("deviation_kernel", "select_kernel"),
-    "tdx_diff_encode": ("flag_kernel", "rows_kernel", "offsets_kernel", "index_kernel", "copy_kernel"),
+    "tdx_diff_encode": ("flag_kernel", "rows_kernel", "offsets_kernel", "place_kernel"),
     "tdx_restore_attn": ("rope_table_kernel", "diff_tab_kernel", "shared_kernel",
                          "stream_plan_kernel<0>", "stream_kernel<unsigned short, 128, 0",
                          "stream_kernel<unsigned short, 64, 0", "merge_kernel<unsigned short, 128, 0>",
@@ -214,6 +214,18 @@ def sq_summary(sq_csv: str, stats_csv: str):
         print(f"{k[:46]:46s} {t:8.1f} {100 * busy:6.1f}% {gf:8.1f} {gf / t * 1e3:8.1f} "
               f"{c.get('SQ_INSTS_VALU', 0.0):10.3g} {c.get('SQ_INSTS_MFMA', 0.0):10.3g} "
               f"{c.get('SQ_INSTS_LDS', 0.0):9.3g}")
+    # any other counters of the run, per dispatch, for the same kernels
+    shown = {"SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+             "SQ_INSTS_LDS"}
+    extra = sorted({n for k in acc for n in acc[k]} - shown)
+    if extra:
+        print("\nother counters, per dispatch:")
+        print(f"{'kernel':46s} " + " ".join(f"{n[3:][:22]:>22s}" for n in extra))
+        for k in sorted(acc, key=lambda k: -us.get(k, 0.0)):
+            if _entry_of(k) is None or k not in us:
+                continue
+            n = len(disp[k])
+            print(f"{k[:46]:46s} " + " ".join(f"{acc[k].get(x, 0.0) / n:22.4g}" for x in extra))
 
 
 def trace_summary(stats_csv: str, bench_log: str):
