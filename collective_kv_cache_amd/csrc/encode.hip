@@ -19,13 +19,11 @@
 //                 offsets (clamped to the capacity, so a record whose blocks
 //                 overflow it still names only written entries) and the true
 //                 total nnz.
-//  place_kernel   one workgroup per (CSR row, group of E consecutive
-//                 entries of the row): the entries' block indices
+//  place_kernel   one workgroup per (CSR row, group of kPlaceEntries
+//                 consecutive entries of the row): the entries' block indices
 //                 (and, paged, the Mirror's pages) into their slots and,
 //                 with values, the Mirror's K/V blocks copied into them;
 //                 entries at or past the capacity are dropped.
-#include <algorithm>
-
 #include "common.h"
 
 namespace tdx {
@@ -33,8 +31,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kFlagThreads = 1024;
-constexpr int kPlaceMaxEntries = 16;  // CSR entries per place_kernel workgroup, at most
-constexpr int kPlaceGrid = 65536;     // place_kernel grid size aimed at
+constexpr int kPlaceEntries = 4;  // CSR entries per place_kernel workgroup
 constexpr int kCopyUnroll = 8;
 constexpr int kScanThreads = 1024;
 constexpr int kMaxAgents = 1024;
@@ -272,10 +269,9 @@ __device__ __forceinline__ void cp_store(const u32x4& v, u32x4* p) {
 #endif
 }
 
-// Workgroup (r, p): the flagged blocks of CSR row r (agent, layer) whose
-// in-row ranks are [p*E, p*E + E), E <= kPlaceMaxEntries (sized so that the
-// grid, whose workgroups past a row's count exit at once, stays near
-// kPlaceGrid).  Their slots are the
+// Workgroup r*G + p: the flagged blocks of CSR row r (agent, layer) whose
+// in-row ranks are [p*E, p*E + E), E = kPlaceEntries (a row has G = nb / E
+// groups; workgroups past a row's count exit at once).  Their slots are the
 // row offset plus the rank; slots at or past the capacity are dropped (with
 // clamped offsets every consumer reads only written slots).  Each slot gets
 // its block index (PAGED: also the Mirror's page pm[a][beta]) and, when
@@ -286,10 +282,13 @@ __global__ __launch_bounds__(kThreads) void place_kernel(
     const uint8_t* __restrict__ flags, const int32_t* __restrict__ rank, const int32_t* __restrict__ count,
     const int32_t* __restrict__ off, int nb, int64_t cap, int32_t* __restrict__ diff_idx,
     int32_t* __restrict__ diff_page, PageMap pm, int L, const u32x4* __restrict__ ak,
-    const u32x4* __restrict__ av, u32x4* __restrict__ dk, u32x4* __restrict__ dv, int chunks, int E) {
-  __shared__ size_t s_src[kPlaceMaxEntries];
-  const size_t r = blockIdx.x;
-  const int first = blockIdx.y * E;
+    const u32x4* __restrict__ av, u32x4* __restrict__ dk, u32x4* __restrict__ dv, int chunks, int G) {
+  constexpr int E = kPlaceEntries;
+  __shared__ size_t s_src[E];
+  // G groups per row, the group index fastest: consecutive workgroups place
+  // consecutive slots (sequential writes, neighbouring reads)
+  const size_t r = blockIdx.x / G;
+  const int first = (int)(blockIdx.x % G) * E;
   const int cnt = count[r];
   if (first >= cnt) return;  // uniform
   const int64_t slot0 = (int64_t)off[r] + first;
@@ -409,13 +408,10 @@ hipError_t encode_t(const Dims& d, const int32_t* master, const void* ak, const 
   if (e != hipSuccess) return e;
   if (cap <= 0) return hipSuccess;  // no slot to place
   // a row has at most nb entries; workgroups past a row's count exit at once
-  const long long cells = (long long)rows * nb;
-  const int E = (int)std::min<long long>(std::max<long long>((cells + kPlaceGrid - 1) / kPlaceGrid, 2),
-                                         kPlaceMaxEntries);
-  const dim3 pgrid((unsigned)rows, (unsigned)((nb + E - 1) / E));
-  hipLaunchKernelGGL((place_kernel<PAGED>), pgrid, dim3(kThreads), 0, s, flags, rank, count, diff_off, nb, cap,
-                     diff_idx, diff_page, pm, d.L, k4, v4, static_cast<u32x4*>(diff_k), static_cast<u32x4*>(diff_v),
-                     chunks, E);
+  const int G = (nb + kPlaceEntries - 1) / kPlaceEntries;
+  hipLaunchKernelGGL((place_kernel<PAGED>), dim3((unsigned)((long long)rows * G)), dim3(kThreads), 0, s, flags, rank,
+                     count, diff_off, nb, cap, diff_idx, diff_page, pm, d.L, k4, v4, static_cast<u32x4*>(diff_k),
+                     static_cast<u32x4*>(diff_v), chunks, G);
   return hipGetLastError();
 }
 }  // namespace
