@@ -6,32 +6,41 @@
 // dense comparator (restore every agent's cache, then attend) is what the
 // fused path is measured against (notes §3d, §7b).
 //
-// Fused path = two kernels writing split-K partials, then one merge:
+// Fused path = set-up kernels, two kernels writing split-K partial records,
+// then one merge:
 //
-//  shared_kernel  one workgroup per (agent group, shared split, layer, KV
-//                 head).  Each 16-token Master tile (= one diff block) is
-//                 staged ONCE in LDS (ping-pong buffers: the next tile's
-//                 loads are in flight while this one is used) and serves the
-//                 query rows of every agent of the group: the agents' GQA
-//                 query groups are stacked into 16-row MFMA tiles, two per
-//                 wave.  RoPE is recovered on the query side,
-//                 q . R(Delta) k = (R(-Delta) q) . k, with Q' = R(-Delta(i,b))
-//                 per row from a double-precision cos/sin table, so one
-//                 canonical Master tile serves all agents.  Rows of an agent
-//                 whose diff record holds the tile are masked here.
-//  agent_kernel   one workgroup per (agent, split, layer, KV head): the
-//                 agent's private history followed by its own diff blocks
-//                 (the "patch": K/V straight from the diff record, Q' rotated
-//                 by the block's Delta).  4 waves stride over 16-token tiles;
-//                 the next tile's loads are issued before the current tile is
-//                 used; V goes through wave-private LDS.
-//  merge_kernel   combines the partials of every (agent, layer, query head).
+//  rope_table_kernel   cos/sin(Delta(i,b) * theta^(-2e/D)) in double, stored
+//                      as fp32 pairs [N][B][D/2].
+//  diff_tab_kernel     per diff entry: its shared block and that block's
+//                      cos/sin row (a block straddling two shared blocks is
+//                      marked, and its rows take their own rows).
+//  shared_kernel       one workgroup per (agent group, Master split, layer,
+//                      KV head).  Each 16-token Master tile (= one diff
+//                      block) arrives ONCE in an LDS ring through direct
+//                      global-to-LDS loads and serves the query rows of every
+//                      agent of the group, the agents' GQA query groups
+//                      stacked into one 16-row MFMA tile per wave.  RoPE is
+//                      recovered on the query side, q . R(Delta) k =
+//                      (R(-Delta) q) . k, so one canonical Master tile serves
+//                      all agents.  Rows of an agent whose diff record holds
+//                      the tile are masked here.
+//  stream_plan_kernel  cuts every (agent, layer) row into tasks of at most
+//                      kTilesPerSplit tiles.
+//  stream_kernel       persistent waves over (task, KV head) pairs: the
+//                      agent's private history followed by its own diff
+//                      blocks (K/V straight from the diff record, the keys
+//                      rotated by their block's Delta in registers), through
+//                      one register pipeline that runs across tasks; K and V
+//                      go through wave-private LDS into the MFMA operands.
+//  merge_kernel        combines the records of every (agent, layer, query
+//                      head).
 //
-// Per tile: S^T = K Q'^T with v_mfma_f32_16x16x32_bf16 (K rows in the A
+// Per tile: S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (K rows in the A
 // operand, query rows in B, so each lane ends up holding 4 logits of ONE
 // query row), online softmax with rows in lanes, O^T += V^T P^T with
-// v_mfma_f32_16x16x16_bf16.  The dense comparator's attention is agent_kernel
-// reading the materialised caches instead of diff records.
+// v_mfma_f32_16x16x16_bf16.  The dense comparator is restore_dense_kernel
+// (every agent's cache materialised) followed by stream_kernel reading the
+// materialised caches instead of diff records.
 // These kernels serve bf16 caches: the operands are the stored bf16 values
 // (and bf16 softmax weights), softmax, accumulation and the merge run in
 // fp32.  fp32 caches take the fp32 vector-unit kernels of attn_f32.hip,
