@@ -230,7 +230,7 @@ int tdx_select_important_noalloc(const tdx_shape* shape, const tdx_layout* layou
     return rc;
   const size_t need = tdx::select_ws_bytes(d);
   REQ(need <= (size_t)TDX_SELECT_SCRATCH_BYTES, TDX_EUNSUPPORTED,
-      "the round needs %zu bytes of scratch, more than the static %zu (N * ceil(T/4) * 8 bytes)", need,
+      "the round needs %zu bytes of scratch, more than the static %zu (N * ceil(T/8) * 8 bytes)", need,
       (size_t)TDX_SELECT_SCRATCH_BYTES);
   void* ws = nullptr;
   if ((rc = scratch_on_current_device(&ws)) != TDX_OK) return rc;

@@ -21,9 +21,12 @@
 namespace tdx {
 namespace {
 
-constexpr int kDevThreads = 256;
-constexpr int kDevWaves = kDevThreads / kWave;
-constexpr int kTokPerWg = kDevWaves;  // one token per wave
+// deviation_kernel workgroups: 8 waves (one token each) when every token's
+// wave can be resident at once, else 4.  With 8, a workgroup reads 8
+// consecutive rows of every agent and the selection sums half as many
+// per-workgroup partials (64 agents: 692 instead of 1384 rows of N doubles).
+constexpr int kDevMaxThreads = 512;
+constexpr int kDevMinWaves = 4;
 constexpr int kSelThreads = 1024;
 constexpr int kMaxAgents = 1024;
 constexpr int kSelLdsKeys = 12288;  // scores kept in LDS up to this many tokens
@@ -60,23 +63,24 @@ __device__ __forceinline__ float group_sum(float v) {
 // PAGED: the reused K lives in 16-token pages of a pool; agent i's token t is
 // row t % 16 of page pm[i][t / 16] at layer pl (kr is the pool).
 template <typename E, int D, int KCH, int AU, bool PAGED>
-__global__ __launch_bounds__(kDevThreads) void deviation_kernel(
+__global__ __launch_bounds__(kDevMaxThreads) void deviation_kernel(
     const E* __restrict__ kr, const E* __restrict__ kx, int N, int T, int Hkv,
     size_t kr_agent_stride, float* __restrict__ dev, float* __restrict__ score,
     double* __restrict__ part, PageMap pm, long long pl) {
   constexpr int VEC = Fmt<E>::VEC;
   constexpr int G = D / VEC;  // lanes per head
   static_assert(G == 8 || G == 16 || G == 32, "lanes per head");
-  extern __shared__ double wsum_dyn[];  // [kDevWaves][N] per-wave agent sums
+  extern __shared__ float wsum_dyn[];  // [waves][N] the wave's token's deviation per agent
+  const int nw = blockDim.x / kWave;   // waves = tokens per workgroup
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int rowE = Hkv * D;
   const int cpr = rowE / VEC;  // chunks per row
-  double* wsum = wsum_dyn + (size_t)wave * N;
-  for (int i = lane; i < N; i += kWave) wsum[i] = 0.0;
+  float* wsum = wsum_dyn + (size_t)wave * N;
+  for (int i = lane; i < N; i += kWave) wsum[i] = 0.0f;
   __syncthreads();
 
-  const int t = blockIdx.x * kTokPerWg + wave;
+  const int t = blockIdx.x * nw + wave;
   const bool live = t < T;  // uniform within the wave
   const int tc = live ? t : T - 1;
   double s_t = 0.0;
@@ -120,16 +124,16 @@ __global__ __launch_bounds__(kDevThreads) void deviation_kernel(
         s_t += (double)d_it;
         if (lane == 0 && live) {
           dev[(size_t)i * T + t] = d_it;
-          wsum[i] += (double)d_it;
+          wsum[i] = d_it;
         }
       }
     }
   }
   if (lane == 0 && live) score[t] = (float)s_t;
   __syncthreads();
-  for (int i = threadIdx.x; i < N; i += kDevThreads) {
+  for (int i = threadIdx.x; i < N; i += blockDim.x) {
     double acc = 0.0;
-    for (int w = 0; w < kDevWaves; ++w) acc += wsum_dyn[(size_t)w * N + i];
+    for (int w = 0; w < nw; ++w) acc += (double)wsum_dyn[(size_t)w * N + i];
     part[(size_t)blockIdx.x * N + i] = acc;
   }
 }
@@ -365,39 +369,56 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 
 template <typename E, int D, int KCH, bool PAGED>
 hipError_t launch_dev(const Dims& d, int check_layer, const void* kr, const PageMap& pm, const void* kx,
-                      float* dev, float* score, double* part, int nparts, hipStream_t s) {
+                      float* dev, float* score, double* part, int* nparts, hipStream_t s) {
   const size_t rowE = (size_t)d.Hkv * d.D;
   const size_t stride = (size_t)d.L * d.T * rowE;
   const E* krl = PAGED ? static_cast<const E*>(kr) : static_cast<const E*>(kr) + (size_t)check_layer * d.T * rowE;
   // agents in flight per wave: the group size that wastes the fewest re-reads
-  // of the last agent (ties to the larger group); rows of 8 chunks per lane
-  // (fp32, 16 heads x 128) keep 2 agents in flight, within the register file
-  int best = KCH >= 8 ? 2 : 8;
+  // of the last agent (ties to the larger group), within the 256 registers a
+  // wave of a 512-thread workgroup has: rows of 3-4 chunks per lane keep at
+  // most 5 agents in flight, rows of 8 chunks (fp32, 16 heads x 128) 2
+  int best = KCH >= 8 ? 2 : (KCH >= 4 ? 5 : 8);
   if (KCH < 8) {
     for (int au : {8, 5, 4}) {
+      if (KCH >= 4 && au > 5) continue;
       const int waste = (d.N + au - 1) / au * au - d.N;
       const int bw = (d.N + best - 1) / best * best - d.N;
       if (waste < bw) best = au;
     }
   }
-#define TDX_DEV(AU)                                                                      \
-  hipLaunchKernelGGL((deviation_kernel<E, D, KCH, AU, PAGED>), dim3(nparts), dim3(kDevThreads), \
-                     kDevWaves * d.N * sizeof(double), s, krl, static_cast<const E*>(kx), d.N, \
-                     d.T, d.Hkv, stride, dev, score, part, pm, (long long)check_layer)
+  // 8-wave workgroups when the GPU holds every token's wave at once, else 4
+  auto launch = [&](auto kern) -> hipError_t {
+    int dv = 0, ncu = 0, per_cu = 0, waves = kDevMinWaves;
+    hipError_t e;
+    if ((e = hipGetDevice(&dv)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dv)) != hipSuccess) return e;
+    const int big = kDevMaxThreads / kWave;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern),
+                                                           kDevMaxThreads, big * d.N * sizeof(float))) != hipSuccess)
+      return e;
+    if ((long long)per_cu * ncu * big >= d.T) waves = big;
+    *nparts = (d.T + waves - 1) / waves;
+    hipLaunchKernelGGL(kern, dim3(*nparts), dim3(waves * kWave), waves * d.N * sizeof(float), s, krl,
+                       static_cast<const E*>(kx), d.N, d.T, d.Hkv, stride, dev, score, part, pm, (long long)check_layer);
+    return hipGetLastError();
+  };
+#define TDX_DEV(AU) return launch(deviation_kernel<E, D, KCH, AU, PAGED>)
   if constexpr (KCH >= 8) {
     TDX_DEV(2);
+  } else if constexpr (KCH >= 4) {
+    if (best == 5) TDX_DEV(5);
+    else TDX_DEV(4);
   } else {
     if (best == 8) TDX_DEV(8);
     else if (best == 5) TDX_DEV(5);
     else TDX_DEV(4);
   }
 #undef TDX_DEV
-  return hipGetLastError();
 }
 
 template <typename E, int D, bool PAGED>
 hipError_t launch_dev_d(const Dims& d, int check_layer, const void* kr, const PageMap& pm, const void* kx,
-                        float* dev, float* score, double* part, int nparts, hipStream_t s) {
+                        float* dev, float* score, double* part, int* nparts, hipStream_t s) {
   const int cpr = d.Hkv * D / Fmt<E>::VEC;
   const int kch = (cpr + kWave - 1) / kWave;
   switch (kch) {
@@ -416,7 +437,8 @@ hipError_t launch_dev_d(const Dims& d, int check_layer, const void* kr, const Pa
 
 }  // namespace
 
-static int dev_parts(const Dims& d) { return (d.T + kTokPerWg - 1) / kTokPerWg; }
+// partials of the deviation pass: one row per workgroup of at least 4 tokens
+static int dev_parts(const Dims& d) { return (d.T + kDevMinWaves - 1) / kDevMinWaves; }
 
 size_t select_ws_bytes(const Dims& d) {
   return (size_t)dev_parts(d) * d.N * sizeof(double);
@@ -428,17 +450,17 @@ hipError_t select_t(const Dims& d, int check_layer, const void* k_reuse, const P
                     int k, float* dev, float* score, float* agent_dev, int32_t* selected, int32_t* master,
                     void* ws, hipStream_t s) {
   if (d.N > kMaxAgents) return hipErrorInvalidValue;
-  const int nparts = dev_parts(d);
+  int nparts = dev_parts(d);
   double* part = static_cast<double*>(ws);
   hipError_t e;
   if (d.dtype == TDX_BF16)
     e = d.D == 128
-            ? launch_dev_d<uint16_t, 128, PAGED>(d, check_layer, k_reuse, pm, k_recomp, dev, score, part, nparts, s)
-            : launch_dev_d<uint16_t, 64, PAGED>(d, check_layer, k_reuse, pm, k_recomp, dev, score, part, nparts, s);
+            ? launch_dev_d<uint16_t, 128, PAGED>(d, check_layer, k_reuse, pm, k_recomp, dev, score, part, &nparts, s)
+            : launch_dev_d<uint16_t, 64, PAGED>(d, check_layer, k_reuse, pm, k_recomp, dev, score, part, &nparts, s);
   else
     e = d.D == 128
-            ? launch_dev_d<float, 128, PAGED>(d, check_layer, k_reuse, pm, k_recomp, dev, score, part, nparts, s)
-            : launch_dev_d<float, 64, PAGED>(d, check_layer, k_reuse, pm, k_recomp, dev, score, part, nparts, s);
+            ? launch_dev_d<float, 128, PAGED>(d, check_layer, k_reuse, pm, k_recomp, dev, score, part, &nparts, s)
+            : launch_dev_d<float, 64, PAGED>(d, check_layer, k_reuse, pm, k_recomp, dev, score, part, &nparts, s);
   if (e != hipSuccess) return e;
   const size_t lds = d.T <= kSelLdsKeys ? (size_t)kSelLdsKeys * sizeof(uint32_t) : 0;
   if (d.T <= kSelLdsKeys)

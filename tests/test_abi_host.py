@@ -235,7 +235,7 @@ def test_paged_transfer_rejects_bad_arguments():
 
 
 def test_noalloc_select_rejects_rounds_beyond_its_scratch():
-    # N * ceil(T/4) * 8 bytes above TDX_SELECT_SCRATCH_BYTES: refused before
+    # N * ceil(T/8) * 8 bytes above TDX_SELECT_SCRATCH_BYTES: refused before
     # anything reaches the HIP runtime (aligned fake pointers, never read)
     big = _layout(n_agents=1024, n_blocks=4, n_tokens=8192)
     rc = tdx.lib().tdx_select_important_noalloc(ctypes.byref(_shape(n_layers=1)), ctypes.byref(big), 0, FAKE, FAKE,
