@@ -56,7 +56,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kTile = 16;
 #ifndef TDX_ST_TW
-#define TDX_ST_TW 64
+#define TDX_ST_TW 48
 #endif
 #ifndef TDX_ST_PD
 #define TDX_ST_PD 3
@@ -647,61 +647,92 @@ __global__ __launch_bounds__(kPlanThreads) void stream_plan_kernel(AttnArgs a, S
                                                                    int32_t* __restrict__ ctl) {
   constexpr int W = kPlanThreads / kWave;
   __shared__ int wsum[W];
+  __shared__ int rcur[kTilesPerSplit];  // remainder tasks: per size, the next slot
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int rows = a.N * a.L;
   const int nb = a.T / kTile;
   const int ptot = a.priv_off[a.N];
-  int carry = 0;
-  for (int pass = 0; pass < 2; ++pass) {
-    for (int base = 0; base < rows; base += kPlanThreads) {
-      const int r = base + tid;
-      StreamTask t{};
-      int nt = 0;
-      if (r < rows) {
-        const int i = r / a.L, l = r % a.L;
-        const int p0 = a.priv_off[i];
-        t.P = a.priv_off[i + 1] - p0;
-        t.P = min(t.P, a.pmax);
-        t.ntp = (t.P + kTile - 1) / kTile;
-        t.prow = l * ptot + p0;
-        int nx = nb;
-        if (MODE == FUSED) {
-          t.e0 = a.diff_off[r];
-          nx = min(max(a.diff_off[r + 1] - t.e0, 0), nb);
-        }
-        nt = t.ntp + nx;
-        t.r = r;
-      }
-      // at most SP splits per row (tiles past them, which a max_priv below
-      // the longest history would leave, are not attended)
-      const int nfull = min(nt / kTilesPerSplit, a.SP);
-      const int rem = nfull < a.SP ? nt - nfull * kTilesPerSplit : 0;
-      const int n = pass == 0 ? nfull : (rem > 0 ? 1 : 0);
-      int x = n;  // inclusive wave scan, then the workgroup's exclusive prefix
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int y = __shfl_up(x, o, kWave);
-        if (lane >= o) x += y;
-      }
-      if (lane == kWave - 1) wsum[wave] = x;
-      __syncthreads();
-      int pre = carry, all = carry;
-      for (int w = 0; w < W; ++w) {
-        if (w < wave) pre += wsum[w];
-        all += wsum[w];
-      }
-      pre += x - n;
-      for (int j = 0; j < n; ++j) {
-        const int s = pass == 0 ? j : nfull;
-        t.s = s;
-        t.t0 = s * kTilesPerSplit;
-        t.cnt = pass == 0 ? kTilesPerSplit : rem;
-        tasks[pre + j] = t;
-      }
-      carry = all;
-      __syncthreads();
+  for (int x = tid; x < kTilesPerSplit; x += kPlanThreads) rcur[x] = 0;
+  __syncthreads();
+  // row r's task fields and its tile count
+  auto row_task = [&](int r, StreamTask& t) {
+    const int i = r / a.L, l = r % a.L;
+    const int p0 = a.priv_off[i];
+    t.P = a.priv_off[i + 1] - p0;
+    t.P = min(t.P, a.pmax);
+    t.ntp = (t.P + kTile - 1) / kTile;
+    t.prow = l * ptot + p0;
+    int nx = nb;
+    if (MODE == FUSED) {
+      t.e0 = a.diff_off[r];
+      nx = min(max(a.diff_off[r + 1] - t.e0, 0), nb);
     }
+    t.r = r;
+    return t.ntp + nx;
+  };
+  // at most SP splits per row (tiles past them, which a max_priv below the
+  // longest history would leave, are not attended)
+  auto split = [&](int nt, int* nfull, int* rem) {
+    *nfull = min(nt / kTilesPerSplit, a.SP);
+    *rem = *nfull < a.SP ? nt - *nfull * kTilesPerSplit : 0;
+  };
+  // pass 0: the full tasks, in row order; counts the remainders per size
+  int carry = 0;
+  for (int base = 0; base < rows; base += kPlanThreads) {
+    const int r = base + tid;
+    StreamTask t{};
+    int nfull = 0, rem = 0;
+    if (r < rows) split(row_task(r, t), &nfull, &rem);
+    if (rem > 0) atomicAdd(&rcur[rem], 1);
+    const int n = nfull;
+    int x = n;  // inclusive wave scan, then the workgroup's exclusive prefix
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(x, o, kWave);
+      if (lane >= o) x += y;
+    }
+    if (lane == kWave - 1) wsum[wave] = x;
+    __syncthreads();
+    int pre = carry, all = carry;
+    for (int w = 0; w < W; ++w) {
+      if (w < wave) pre += wsum[w];
+      all += wsum[w];
+    }
+    pre += x - n;
+    for (int j = 0; j < n; ++j) {
+      t.s = j;
+      t.t0 = j * kTilesPerSplit;
+      t.cnt = kTilesPerSplit;
+      tasks[pre + j] = t;
+    }
+    carry = all;
+    __syncthreads();
   }
-  if (tid == 0) ctl[0] = carry;
+  // remainder tasks after the full ones, largest first: the waves take tasks
+  // round-robin, so the ones still finishing a full task get the smallest
+  // remainders (the order of equal sizes does not matter: every task writes
+  // its own record)
+  if (tid == 0) {
+    int c = carry;
+    for (int sz = kTilesPerSplit - 1; sz >= 1; --sz) {
+      const int n = rcur[sz];
+      rcur[sz] = c;
+      c += n;
+    }
+    ctl[0] = c;
+  }
+  __syncthreads();
+  for (int base = 0; base < rows; base += kPlanThreads) {
+    const int r = base + tid;
+    if (r >= rows) continue;
+    StreamTask t{};
+    int nfull = 0, rem = 0;
+    split(row_task(r, t), &nfull, &rem);
+    if (rem == 0) continue;
+    t.s = nfull;
+    t.t0 = nfull * kTilesPerSplit;
+    t.cnt = rem;
+    tasks[atomicAdd(&rcur[rem], 1)] = t;
+  }
 }
 
 // Per diff entry e of row r = i * L + l: info[e] = (beta, b) with b the shared
