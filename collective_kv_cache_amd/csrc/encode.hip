@@ -19,11 +19,11 @@
 //                 offsets (clamped to the capacity, so a record whose blocks
 //                 overflow it still names only written entries) and the true
 //                 total nnz.
-//  place_kernel   one workgroup per (CSR row, group of kPlaceEntries
-//                 consecutive entries of the row): the entries' block indices
-//                 (and, paged, the Mirror's pages) into their slots and,
-//                 with values, the Mirror's K/V blocks copied into them;
-//                 entries at or past the capacity are dropped.
+//  index_kernel   one workgroup per CSR row: the ascending block indices
+//                 (and, paged, the Mirror's page) into their slots; entries at
+//                 or past the capacity are dropped.
+//  copy_kernel    slot-major: each workgroup copies the Mirror's K/V blocks of
+//                 a few consecutive CSR entries.
 #include "common.h"
 
 namespace tdx {
@@ -31,7 +31,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kFlagThreads = 1024;
-constexpr int kPlaceEntries = 4;  // CSR entries per place_kernel workgroup
+constexpr int kCopySlots = 2;       // diff entries per copy workgroup step
+constexpr int kCopyMaxWg = 65536;  // copy grid (grid-stride beyond)
 constexpr int kCopyUnroll = 8;
 constexpr int kScanThreads = 1024;
 constexpr int kMaxAgents = 1024;
@@ -184,7 +185,7 @@ __device__ __forceinline__ int lanemask_count(uint64_t m, int lane) {
 
 // In-row exclusive ranks of the flagged blocks and the row count.  With
 // several chunk slices the block flag is the OR of the slices' flags; it is
-// stored back into slice 0 for place_kernel.
+// stored back into slice 0 for copy_kernel.
 __global__ __launch_bounds__(kThreads) void rows_kernel(uint8_t* __restrict__ flags, int nb,
                                                         int nslices, size_t slice_stride,
                                                         int32_t* __restrict__ rank,
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(uint8_t* __restrict__ fl
 }
 
 // Row offsets are written as min(true offset, cap): entries past the
-// capacity are never written (place_kernel), and with clamped
+// capacity are never written (index_kernel, copy_kernel), and with clamped
 // offsets no row of the record reaches one of them, so every consumer that
 // reads entries [off[r], off[r+1]) stays inside the written entries.  nnz
 // keeps the true total, which tells the caller that the record is truncated.
@@ -269,66 +270,71 @@ __device__ __forceinline__ void cp_store(const u32x4& v, u32x4* p) {
 #endif
 }
 
-// Workgroup r*G + p: the flagged blocks of CSR row r (agent, layer) whose
-// in-row ranks are [p*E, p*E + E), E = kPlaceEntries (a row has G = nb / E
-// groups; workgroups past a row's count exit at once).  Their slots are the
-// row offset plus the rank; slots at or past the capacity are dropped (with
-// clamped offsets every consumer reads only written slots).  Each slot gets
-// its block index (PAGED: also the Mirror's page pm[a][beta]) and, when
-// values are requested (dk set), the block's K and V chunks, copied from the
-// Mirror's cache kCopyUnroll chunks of each per thread in flight.
+// One workgroup per CSR row (agent, layer): the ascending block indices of the
+// row's flagged blocks into their slots (entries at or past the capacity are
+// dropped).  PAGED: also each entry's page, the Mirror's page pm[a][beta].
 template <bool PAGED>
-__global__ __launch_bounds__(kThreads) void place_kernel(
-    const uint8_t* __restrict__ flags, const int32_t* __restrict__ rank, const int32_t* __restrict__ count,
-    const int32_t* __restrict__ off, int nb, int64_t cap, int32_t* __restrict__ diff_idx,
-    int32_t* __restrict__ diff_page, PageMap pm, int L, const u32x4* __restrict__ ak,
-    const u32x4* __restrict__ av, u32x4* __restrict__ dk, u32x4* __restrict__ dv, int chunks, int G) {
-  constexpr int E = kPlaceEntries;
-  __shared__ size_t s_src[E];
-  // G groups per row, the group index fastest: consecutive workgroups place
-  // consecutive slots (sequential writes, neighbouring reads)
-  const size_t r = blockIdx.x / G;
-  const int first = (int)(blockIdx.x % G) * E;
-  const int cnt = count[r];
-  if (first >= cnt) return;  // uniform
-  const int64_t slot0 = (int64_t)off[r] + first;
-  const int n = (int)max((int64_t)0, min((int64_t)min(E, cnt - first), cap - slot0));
-  if (n == 0) return;
+__global__ __launch_bounds__(kThreads) void index_kernel(const uint8_t* __restrict__ flags,
+                                                         const int32_t* __restrict__ rank,
+                                                         const int32_t* __restrict__ off, int nb, int64_t cap,
+                                                         int32_t* __restrict__ diff_idx, PageMap pm, int L,
+                                                         int32_t* __restrict__ diff_page) {
+  const size_t r = blockIdx.x;
+  const int64_t row_off = off[r];
   for (int beta = threadIdx.x; beta < nb; beta += kThreads) {
     if (!flags[r * nb + beta]) continue;
-    const int k = rank[r * nb + beta] - first;
-    if (k < 0 || k >= n) continue;
-    diff_idx[slot0 + k] = beta;
-    long long page = 0;
-    if constexpr (PAGED) {
-      page = page_at(pm, (long long)(r / L), beta);
-      diff_page[slot0 + k] = (int32_t)page;
-    }
-    s_src[k] = PAGED ? ((size_t)(r % L) * (size_t)pm.n_pages + (size_t)page) * chunks
-                     : ((size_t)r * nb + beta) * chunks;
+    const int64_t slot = row_off + rank[r * nb + beta];
+    if (slot >= cap) continue;
+    diff_idx[slot] = beta;
+    if constexpr (PAGED) diff_page[slot] = (int32_t)page_at(pm, (long long)(r / L), beta);
   }
-  if (dk == nullptr) return;  // uniform: a paged record without value copies
-  __syncthreads();
-  const size_t dst0 = (size_t)slot0 * chunks;
-  const int total = n * chunks;  // the entries' chunks, entry-major
-  for (int f0 = threadIdx.x; f0 < total; f0 += kThreads * kCopyUnroll) {
-    u32x4 xk[kCopyUnroll], xv[kCopyUnroll];
+}
+
+// Slot-major value copy: workgroup w copies CSR entries [w*S, w*S + S), then
+// the groups of S a grid further on (of the min(nnz, cap) written entries),
+// from the Mirrors' caches, kCopyUnroll chunks of K and of V per thread in
+// flight.  An entry's row is found by walking the
+// row offsets from a binary search at the workgroup's first entry; its block
+// index comes from diff_idx (index_kernel).  PAGED: the source is the entry's
+// page of the pools.
+template <bool PAGED>
+__global__ __launch_bounds__(kThreads) void copy_kernel(
+    const u32x4* __restrict__ ak, const u32x4* __restrict__ av, const int32_t* __restrict__ off, int rows, int nb,
+    int chunks, int64_t cap, const int32_t* __restrict__ diff_idx, const int32_t* __restrict__ diff_page,
+    u32x4* __restrict__ dk, u32x4* __restrict__ dv, long long n_pages, int L) {
+  const int tid = threadIdx.x;
+  const int64_t total = min((int64_t)off[rows], cap);
+  for (int64_t e0 = (int64_t)blockIdx.x * kCopySlots; e0 < total; e0 += (int64_t)gridDim.x * kCopySlots) {
+  const int64_t e1 = min(e0 + kCopySlots, total);
+  int lo = 0, hi = rows - 1;  // the row of e0: largest r with off[r] <= e0
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= e0) lo = mid; else hi = mid - 1;
+  }
+  int r = lo;
+  for (int64_t e = e0; e < e1; ++e) {
+    while (off[r + 1] <= e) ++r;  // uniform
+    const size_t src = PAGED ? ((size_t)(r % L) * (size_t)n_pages + (size_t)diff_page[e]) * chunks
+                             : ((size_t)r * nb + (size_t)diff_idx[e]) * chunks;
+    const size_t dst = (size_t)e * chunks;
+    for (int c0 = tid; c0 < chunks; c0 += kThreads * kCopyUnroll) {
+      u32x4 xk[kCopyUnroll], xv[kCopyUnroll];
 #pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) {
-      const int f = min(f0 + u * kThreads, total - 1);
-      const int j = f / chunks;
-      const size_t src = s_src[j] + (f - j * chunks);
-      xk[u] = ld16_nt(ak + src);
-      xv[u] = ld16_nt(av + src);
-    }
+      for (int u = 0; u < kCopyUnroll; ++u) {
+        const int c = min(c0 + u * kThreads, chunks - 1);
+        xk[u] = ld16_nt(ak + src + c);
+        xv[u] = ld16_nt(av + src + c);
+      }
 #pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) {
-      const int f = f0 + u * kThreads;
-      if (f < total) {
-        cp_store(xk[u], dk + dst0 + f);
-        cp_store(xv[u], dv + dst0 + f);
+      for (int u = 0; u < kCopyUnroll; ++u) {
+        const int c = c0 + u * kThreads;
+        if (c < chunks) {
+          cp_store(xk[u], dk + dst + c);
+          cp_store(xv[u], dv + dst + c);
+        }
       }
     }
+  }
   }
 }
 
@@ -406,12 +412,15 @@ hipError_t encode_t(const Dims& d, const int32_t* master, const void* ak, const 
                      master, d.N);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (cap <= 0) return hipSuccess;  // no slot to place
-  // a row has at most nb entries; workgroups past a row's count exit at once
-  const int G = (nb + kPlaceEntries - 1) / kPlaceEntries;
-  hipLaunchKernelGGL((place_kernel<PAGED>), dim3((unsigned)((long long)rows * G)), dim3(kThreads), 0, s, flags, rank,
-                     count, diff_off, nb, cap, diff_idx, diff_page, pm, d.L, k4, v4, static_cast<u32x4*>(diff_k),
-                     static_cast<u32x4*>(diff_v), chunks, G);
+  hipLaunchKernelGGL((index_kernel<PAGED>), dim3(rows), dim3(kThreads), 0, s, flags, rank, diff_off, nb, cap,
+                     diff_idx, pm, d.L, diff_page);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (diff_k == nullptr || cap <= 0) return hipSuccess;  // a paged record without value copies
+  // every written entry has a slot below cap; surplus workgroups exit at once
+  const int64_t cwg = min((cap + kCopySlots - 1) / kCopySlots, (int64_t)kCopyMaxWg);
+  hipLaunchKernelGGL((copy_kernel<PAGED>), dim3((unsigned)cwg), dim3(kThreads), 0, s, k4, v4, diff_off, rows, nb,
+                     chunks, cap, diff_idx, diff_page, static_cast<u32x4*>(diff_k), static_cast<u32x4*>(diff_v),
+                     (long long)pm.n_pages, d.L);
   return hipGetLastError();
 }
 }  // namespace
