@@ -24,9 +24,11 @@
 //                      (R(-Delta) q) . k, so one canonical Master tile serves
 //                      all agents.  Rows of an agent whose diff record holds
 //                      the tile are masked here.
-//  stream_plan_kernel  cuts every (agent, layer) row into tasks of at most
-//                      kTilesPerSplit tiles.
-//  stream_kernel       persistent waves over (task, KV head) pairs: the
+//  stream_plan_kernel  lays the (agent, layer) rows' tiles end to end and
+//                      cuts them into one equal piece per stream-kernel
+//                      slot (a wave per KV head); a piece is one task per
+//                      row it touches.
+//  stream_kernel       persistent waves, each running its slot's tasks: the
 //                      agent's private history followed by its own diff
 //                      blocks (K/V straight from the diff record, the keys
 //                      rotated by their block's Delta in registers), through
@@ -45,6 +47,9 @@
 // (and bf16 softmax weights), softmax, accumulation and the merge run in
 // fp32.  fp32 caches take the fp32 vector-unit kernels of attn_f32.hip,
 // which round nothing to bf16.
+#include <algorithm>
+#include <utility>
+
 #include "common.h"
 
 namespace tdx {
@@ -194,11 +199,27 @@ __device__ __forceinline__ i16x4 ld_tr16(const void* p) {
 // l ^ 32, l ^ 48): two row swaps on the VALU (v_permlane16_swap,
 // v_permlane32_swap), each followed by a max of the two halves.
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Maxima of logits, which are finite or -inf and never NaN, as single
+// v_max_f32 / v_max3_f32 instructions: fmaxf would first quiet possible
+// signalling NaNs in each operand with an extra v_max of the value with
+// itself.  The operands are VALU or permlane results, never MFMA results.
+__device__ __forceinline__ float max_nn(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3_nn(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ float row_max4(float x) {
   u32x2 r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  x = max_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
   r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // The running reference m of a row may lag its true maximum by up to
@@ -216,7 +237,7 @@ constexpr float kRescaleLag = 8.0f;
 template <int D>
 __device__ __forceinline__ void softmax_pv(RowState<D>& st, const float z[4], const i16x4* va) {
   constexpr int DT = D / 16;
-  const float tmax = row_max4(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+  const float tmax = row_max4(max_nn(max3_nn(z[0], z[1], z[2]), z[3]));
   if (__builtin_amdgcn_ballot_w64(tmax > st.m + kRescaleLag) != 0) {
     const float mnew = fmaxf(st.m, tmax);
     const float alpha = st.m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(st.m - mnew);
@@ -261,12 +282,15 @@ __device__ __forceinline__ void write_record(float* rec, const RowState<D>& st, 
 // One workgroup per (agent group, Master split, layer, KV head).  The split's
 // 16-token Master tiles arrive in a ring of NB LDS slots through direct
 // global-to-LDS loads (global_load_lds_dwordx4): each wave's load instruction
-// moves 1 KB of a tile (4 rows of 128 dims or 8 of 64) straight into the
-// slot, so NB-2 tiles stay in flight per workgroup without holding any in
-// registers.  A slot keeps K and V rows unpadded, 16-byte chunk ch of row t
-// at position ch ^ (t % chunks per row): each lane picks the global chunk
-// that belongs at its LDS position, which spreads the MFMA operand reads
-// over the banks.
+// moves 1 KB of a tile, RPI whole rows (4 rows of 128 dims or 8 of 64),
+// straight into the slot, so NB-2 tiles stay in flight per workgroup without
+// holding any in registers.  Within its 1 KB, the 16-byte chunks of those
+// rows are placed in the order the MFMA operands are read back (ShTile), so
+// that a lane's K chunks of successive 32-dim steps, and its V elements of
+// successive 16-dim slices, sit at fixed distances from its first one: the
+// operand reads take one base address per tile and immediate offsets, and
+// 16 consecutive lanes of a read touch 16 distinct 16-byte (K) or 8-byte (V)
+// units of one 256-byte or 128-byte span.
 //
 // Step n (tile n of the split): wait until this wave has at most the loads
 // of tiles n+1 .. n+NB-2 outstanding, barrier (tile n is in LDS and every
@@ -292,7 +316,14 @@ __device__ __forceinline__ void write_record(float* rec, const RowState<D>& st, 
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// One Master tile slot: [K rows][V rows], 16 rows of RB bytes each.
+// One Master tile slot: [K rows][V rows], 16 rows of RB bytes each.  Load
+// instruction g of a tensor fills bytes [1024 g, 1024 g + 1024) of the
+// tensor's half with rows RPI*g + i, i < RPI.  There, 16-byte chunk c of row
+// RPI*g + i is at 16-byte unit
+//   K: (c / 4) * 4*RPI + i + RPI * ((c % 4) ^ g)
+//   V: (c / 2) * 2*RPI + 2*i + (c % 2)
+// so the K chunk 4k + q of a row is k * KSTEP bytes past chunk q, and the V
+// chunks of 16-dim slice dt are dt * VSTEP bytes past those of slice 0.
 template <int D>
 struct ShTile {
   static constexpr int RB = D * 2;                         // bytes of one bf16 row of a head
@@ -301,26 +332,49 @@ struct ShTile {
   static constexpr int RPI = 1024 / RB;                    // rows per wave load instruction
   static constexpr int IPT = kTile * RB / 1024;            // load instructions per tensor
   static constexpr int LPT = BYTES / (kShThreads * 16);    // loads per thread per tile
+  static constexpr int KSTEP = 4 * RPI * 16;               // bytes between a lane's K chunks of consecutive 32-dim steps
+  static constexpr int VSTEP = 2 * RPI * 16;               // bytes between a lane's V reads of consecutive 16-dim slices
   static_assert(LPT * kShWaves == 2 * IPT, "every wave issues the same loads");
+  static_assert(CPR % 4 == 0 && IPT <= 4, "K chunk groups, XOR of the instruction index into 2 bits");
+  // byte offset of K chunk c of tile row r / of V chunk c of tile row r within the tensor's half
+  __device__ static constexpr int kbyte(int r, int c) {
+    return ((r / RPI) * 64 + (c / 4) * 4 * RPI + r % RPI + RPI * ((c % 4) ^ (r / RPI))) * 16;
+  }
+  __device__ static constexpr int vbyte(int r, int c) {
+    return ((r / RPI) * 64 + (c / 2) * 2 * RPI + 2 * (r % RPI) + c % 2) * 16;
+  }
 };
 
-__device__ __forceinline__ int sh_swz(int t, int ch, int cpr) { return ch ^ (t % cpr); }
-
-// ds_read_b64_tr_b16 (as ld_tr16) issued as inline asm: the compiler cannot
-// tell a ring slot being read from the slot the pending global-to-LDS loads
-// write, and would otherwise wait for every one of them before a transposed
-// read.  The caller waits for the results with lds_wait.
-__device__ __forceinline__ i16x4 ld_tr16_nowait(const void* p) {
+// ds_read_b64_tr_b16 (as ld_tr16) and ds_read_b128 issued as inline asm, at
+// address p + OFF (OFF in the instruction's offset field): the compiler
+// cannot tell a ring slot being read from the slot the pending global-to-LDS
+// loads write, and would otherwise wait for every one of them before each
+// read.  The caller waits for the results with lds_wait / lds_wait_k.
+template <int OFF>
+__device__ __forceinline__ i16x4 ld_tr16_nowait(uint32_t p) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field");
   i16x4 r;
-  const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(p), "n"(OFF) : "memory");
   return r;
 }
-__device__ __forceinline__ u32x4 ld_b128_nowait(const void* p) {
+template <int OFF>
+__device__ __forceinline__ u32x4 ld_b128_nowait(uint32_t p) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field");
   u32x4 r;
-  const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(p), "n"(OFF) : "memory");
   return r;
+}
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 // Wait until at most N of this wave's LDS reads are outstanding (LDS reads
 // complete in order); the operands tie the K operand read before them.
@@ -361,7 +415,6 @@ __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(TDX_
   constexpr int DT = D / 16;
   constexpr int HALF = D / 2;
   constexpr int RB = Tl::RB;
-  constexpr int CPR = Tl::CPR;
   static_assert(sizeof(E) == 2, "bf16 caches (fp32 ones take the fp32 kernel)");
   static_assert(NB >= 3, "ring slots");
   extern __shared__ __align__(16) unsigned char smem[];
@@ -463,40 +516,60 @@ __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(TDX_
   // ring's wait counts see only its own loads
   __builtin_amdgcn_s_waitcnt(0);
 
+  // This thread's share of a tile's loads: load p is instruction
+  // wave * LPT + p (K instructions first, then V), and the lane's 16-byte
+  // chunk is the one its position in the instruction's 1 KB holds (ShTile);
+  // loff[p] is that chunk's byte offset from the tile's first row.
+  uint32_t loff[Tl::LPT];
+#pragma unroll
+  for (int p = 0; p < Tl::LPT; ++p) {
+    const int inst = wave * Tl::LPT + p;
+    const int g = inst % Tl::IPT;
+    int r, c;
+    if (inst < Tl::IPT) {  // K: lane = (c / 4) * 4*RPI + i + RPI * ((c % 4) ^ g)
+      r = g * Tl::RPI + lane % Tl::RPI;
+      c = (lane / (4 * Tl::RPI)) * 4 + (((lane % (4 * Tl::RPI)) / Tl::RPI) ^ g);
+    } else {  // V: lane = (c / 2) * 2*RPI + 2*i + c % 2
+      r = g * Tl::RPI + (lane % (2 * Tl::RPI)) / 2;
+      c = (lane / (2 * Tl::RPI)) * 2 + lane % 2;
+    }
+    loff[p] = (uint32_t)(((size_t)r * rowHD + (size_t)c * 8) * sizeof(E));
+  }
+
   // this thread's loads of tile u into slot s (tiles past the split re-read its last)
   auto issue = [&](int u, int s) {
     const int tile = min(u, b1 - 1);
     const size_t trow = PAGED ? ((size_t)l * a.mpm.n_pages + page_at(a.mpm, mrow, tile)) * kTile
                               : (size_t)tile * kTile;
+    const unsigned char* kb = reinterpret_cast<const unsigned char*>(mk + trow * rowHD);
+    const unsigned char* vb = reinterpret_cast<const unsigned char*>(mv + trow * rowHD);
     unsigned char* slot = ring + s * Tl::BYTES;
 #pragma unroll
     for (int p = 0; p < Tl::LPT; ++p) {
-      const int inst = wave * Tl::LPT + p;  // K instructions first, then V
-      const int tensor = inst / Tl::IPT;
-      const int r0 = (inst % Tl::IPT) * Tl::RPI;
-      const int t = r0 + lane / CPR, pos = lane % CPR;
-      const E* src = (tensor ? mv : mk) + (trow + t) * rowHD + sh_swz(t, pos, CPR) * 8;
-      __builtin_amdgcn_global_load_lds((void*)src, (lds_void_t*)(slot + tensor * kTile * RB + r0 * RB), 16, 0, 0);
+      const int inst = wave * Tl::LPT + p;
+      const int tensor = inst / Tl::IPT, g = inst % Tl::IPT;
+      __builtin_amdgcn_global_load_lds((void*)((tensor ? vb : kb) + loff[p]),
+                                       (lds_void_t*)(slot + tensor * kTile * RB + g * 1024), 16, 0, 0);
     }
   };
 
   // use tokens [t_lo, t_hi) of tile u (in slot s) with the current rotation;
   // fw: the lane's agent's diff-flag word of the tile
+  // The lane's operand addresses within a slot: K chunk q4 of row c16 (the
+  // chunk of step k is k * KSTEP further); for the PV operand, va[dt][j] =
+  // V[token 4*q4 + j][dim 16*dt + c16], the lane addresses row 4*q4 + c16/4
+  // at dims 16*dt + 4*(c16%4) (slice dt is dt * VSTEP further).
+  const uint32_t koff = Tl::kbyte(c16, q4);
+  const uint32_t voff = kTile * RB + Tl::vbyte(4 * q4 + (c16 >> 2), (c16 & 3) >> 1) + (c16 & 1) * 8;
   auto compute = [&](int u, int s, int t_lo, int t_hi, uint32_t fw) {
-    const unsigned char* kt = ring + s * Tl::BYTES;
-    const unsigned char* vt = kt + kTile * RB;
+    const uint32_t slot = lds_addr(ring + s * Tl::BYTES);
+    const uint32_t ka = slot + koff, vaddr = slot + voff;
     // the K and V operands of the tile in one round trip: K first, then V,
     // whose latency the QK products cover
     u32x4 kop[KD];
-#pragma unroll
-    for (int k = 0; k < KD; ++k) kop[k] = ld_b128_nowait(kt + c16 * RB + sh_swz(c16, 4 * k + q4, CPR) * 16);
-    // PV operand: va[dt][j] = V[token 4*q4 + j][dim 16*dt + c16]; this lane
-    // addresses row 4*q4 + c16/4, dims 16*dt + 4*(c16%4)
+    static_for<KD>([&](auto k) { kop[decltype(k)::value] = ld_b128_nowait<decltype(k)::value * Tl::KSTEP>(ka); });
     i16x4 va[DT];
-    const int vrow = 4 * q4 + (c16 >> 2);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      va[dt] = ld_tr16_nowait(vt + vrow * RB + sh_swz(vrow, 2 * dt + ((c16 & 3) >> 1), CPR) * 16 + (c16 & 1) * 8);
+    static_for<DT>([&](auto dt) { va[decltype(dt)::value] = ld_tr16_nowait<decltype(dt)::value * Tl::VSTEP>(vaddr); });
     lds_wait_k<DT>(kop);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -569,10 +642,11 @@ __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(TDX_
 //
 // The agent-private work is a stream of 16-token tiles per (agent, layer, KV
 // head): the agent's private history, then its own diff blocks (fused) or its
-// materialised shared cache (dense comparator).  stream_plan_kernel cuts
-// every (agent, layer) row into tasks of at most kTilesPerSplit tiles, each of
-// which becomes one partial softmax record per query row.  The waves of
-// stream_kernel stay resident and take (task, KV head) pairs in turn;
+// materialised shared cache (dense comparator).  stream_plan_kernel gives
+// every slot of Hkv waves (one per KV head) an equal share of all rows' tiles
+// as a run of tasks, each task one row's part of the share and one partial
+// softmax record per query row.  The waves of stream_kernel stay resident and
+// run their slot's tasks in turn;
 // each wave runs ONE PD-stage register pipeline across task boundaries, so the
 // first tiles and the query of the next task are in flight while the current
 // task drains, and no workgroup start-up or combine step sits between tasks.
@@ -639,21 +713,31 @@ constexpr int kPlanThreads = 1024;
 #endif
 constexpr int kStreamNW = TDX_ST_NW;  // waves per stream workgroup
 
-// Task order: every row's full splits first (row order), then the shorter
-// remainders, so that the last tasks taken are the small ones.
-// ctl[0] = task count.
+// stream-kernel slots the plan can feed: a slot is one wave per KV head
+// working on the same tasks
+constexpr int kMaxSlots = 8192;
+
+// Task plan (one workgroup).  The (agent, layer) rows' tiles are laid end to
+// end in row order and cut into nslot equal pieces of
+// P = max(kTilesPerSplit, ceil(total / nslot)) tiles, one per slot; where a
+// piece crosses a row boundary it becomes one task per row.  Every wave then
+// runs at most P tiles whatever the mix of row lengths, and a row has at most
+// ceil(tiles / P) + 1 <= SP tasks (one partial record each).  Tasks are
+// stored slot by slot in row order.  Writes ctl[0] = tasks, ctl[1] = nslot,
+// ctl[2 + s] = first task of slot s (s <= nslot) and nrec[r] = tasks of row r.
 template <int MODE>
-__global__ __launch_bounds__(kPlanThreads) void stream_plan_kernel(AttnArgs a, StreamTask* __restrict__ tasks,
-                                                                   int32_t* __restrict__ ctl) {
+__global__ __launch_bounds__(kPlanThreads) void stream_plan_kernel(AttnArgs a, int nslot,
+                                                                   StreamTask* __restrict__ tasks,
+                                                                   int32_t* __restrict__ ctl,
+                                                                   int32_t* __restrict__ nrec) {
   constexpr int W = kPlanThreads / kWave;
-  __shared__ int wsum[W];
-  __shared__ int rcur[kTilesPerSplit];  // remainder tasks: per size, the next slot
+  __shared__ int wsum[2][W];
+  __shared__ int red[W];
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int rows = a.N * a.L;
   const int nb = a.T / kTile;
   const int ptot = a.priv_off[a.N];
-  for (int x = tid; x < kTilesPerSplit; x += kPlanThreads) rcur[x] = 0;
-  __syncthreads();
+  int32_t* slot_start = ctl + 2;
   // row r's task fields and its tile count
   auto row_task = [&](int r, StreamTask& t) {
     const int i = r / a.L, l = r % a.L;
@@ -670,68 +754,77 @@ __global__ __launch_bounds__(kPlanThreads) void stream_plan_kernel(AttnArgs a, S
     t.r = r;
     return t.ntp + nx;
   };
-  // at most SP splits per row (tiles past them, which a max_priv below the
-  // longest history would leave, are not attended)
-  auto split = [&](int nt, int* nfull, int* rem) {
-    *nfull = min(nt / kTilesPerSplit, a.SP);
-    *rem = *nfull < a.SP ? nt - *nfull * kTilesPerSplit : 0;
-  };
-  // pass 0: the full tasks, in row order; counts the remainders per size
-  int carry = 0;
-  for (int base = 0; base < rows; base += kPlanThreads) {
-    const int r = base + tid;
-    StreamTask t{};
-    int nfull = 0, rem = 0;
-    if (r < rows) split(row_task(r, t), &nfull, &rem);
-    if (rem > 0) atomicAdd(&rcur[rem], 1);
-    const int n = nfull;
-    int x = n;  // inclusive wave scan, then the workgroup's exclusive prefix
+  // inclusive wave scan of x
+  auto wave_scan = [&](int x) {
     for (int o = 1; o < kWave; o <<= 1) {
       const int y = __shfl_up(x, o, kWave);
       if (lane >= o) x += y;
     }
-    if (lane == kWave - 1) wsum[wave] = x;
-    __syncthreads();
-    int pre = carry, all = carry;
-    for (int w = 0; w < W; ++w) {
-      if (w < wave) pre += wsum[w];
-      all += wsum[w];
-    }
-    pre += x - n;
-    for (int j = 0; j < n; ++j) {
-      t.s = j;
-      t.t0 = j * kTilesPerSplit;
-      t.cnt = kTilesPerSplit;
-      tasks[pre + j] = t;
-    }
-    carry = all;
-    __syncthreads();
+    return x;
+  };
+
+  // pass 1: the total
+  int part = 0;
+  for (int r = tid; r < rows; r += kPlanThreads) {
+    StreamTask t{};
+    part += row_task(r, t);
   }
-  // remainder tasks after the full ones, largest first: the waves take tasks
-  // round-robin, so the ones still finishing a full task get the smallest
-  // remainders (the order of equal sizes does not matter: every task writes
-  // its own record)
-  if (tid == 0) {
-    int c = carry;
-    for (int sz = kTilesPerSplit - 1; sz >= 1; --sz) {
-      const int n = rcur[sz];
-      rcur[sz] = c;
-      c += n;
-    }
-    ctl[0] = c;
-  }
+  part = wave_scan(part);
+  if (lane == kWave - 1) red[wave] = part;
   __syncthreads();
+  int total = 0;
+  for (int w = 0; w < W; ++w) total += red[w];
+  const int P = max(kTilesPerSplit, (total + nslot - 1) / nslot);
+
+  // pass 2: each row's first tile position R0 and first task index, then its
+  // tasks: piece j covers slot R0 / P + j
+  int carry0 = 0, carry1 = 0;
   for (int base = 0; base < rows; base += kPlanThreads) {
     const int r = base + tid;
-    if (r >= rows) continue;
     StreamTask t{};
-    int nfull = 0, rem = 0;
-    split(row_task(r, t), &nfull, &rem);
-    if (rem == 0) continue;
-    t.s = nfull;
-    t.t0 = nfull * kTilesPerSplit;
-    t.cnt = rem;
-    tasks[atomicAdd(&rcur[rem], 1)] = t;
+    const int nt = r < rows ? row_task(r, t) : 0;
+    const int x0 = wave_scan(nt);
+    if (lane == kWave - 1) wsum[0][wave] = x0;
+    __syncthreads();
+    int pre0 = carry0, all0 = carry0;
+    for (int w = 0; w < W; ++w) {
+      if (w < wave) pre0 += wsum[0][w];
+      all0 += wsum[0][w];
+    }
+    const int R0 = pre0 + x0 - nt;
+    const int first = R0 / P;
+    const int np = nt > 0 ? (R0 + nt - 1) / P - first + 1 : 0;
+    const int x1 = wave_scan(np);
+    if (lane == kWave - 1) wsum[1][wave] = x1;
+    __syncthreads();
+    int pre1 = carry1, all1 = carry1;
+    for (int w = 0; w < W; ++w) {
+      if (w < wave) pre1 += wsum[1][w];
+      all1 += wsum[1][w];
+    }
+    pre1 += x1 - np;
+    if (r < rows) {
+      nrec[r] = np;
+      for (int j = 0; j < np; ++j) {
+        const int sl = first + j;
+        const int lo = max(R0, sl * P), hi = min(R0 + nt, (sl + 1) * P);
+        t.s = j;
+        t.t0 = lo - R0;
+        t.cnt = hi - lo;
+        tasks[pre1 + j] = t;
+        if (lo == sl * P) slot_start[sl] = pre1 + j;  // the slot's first task
+      }
+    }
+    carry0 = all0;
+    carry1 = all1;
+    __syncthreads();
+  }
+  // slots past the last piece have no tasks
+  const int used = (total + P - 1) / P;
+  for (int sl = used + tid; sl <= nslot; sl += kPlanThreads) slot_start[sl] = carry1;
+  if (tid == 0) {
+    ctl[0] = carry1;
+    ctl[1] = nslot;
   }
 }
 
@@ -789,9 +882,14 @@ __global__ __launch_bounds__(kStreamNW * kWave) __attribute__((amdgpu_waves_per_
   const int q4 = lane / 16, c16 = lane % 16;
   const int g = a.Hq / a.Hkv;
   const int Hkv = a.Hkv;
-  const int nht = ctl[0] * Hkv;  // (task, head) pairs
+  // Wave gw runs the tasks of slot gw / Hkv, [slot_start[s], slot_start[s + 1])
+  // (stream_plan_kernel), for KV head gw % Hkv: the waves of a workgroup
+  // work on neighbouring KV heads of the same rows.
   const int gw = blockIdx.x * kStreamNW + wave;
-  if (gw >= nht) return;  // wave-uniform; the kernel has no workgroup barrier
+  const int slot = gw / Hkv;
+  if (slot >= ctl[1]) return;  // wave-uniform; the kernel has no workgroup barrier
+  const int ts = ctl[2 + slot], te = ctl[3 + slot];
+  if (ts >= te) return;
 
   unsigned char* kl = smem + (size_t)wave * (KB + VB + CB);  // this wave's K tile
   unsigned char* vl = kl + KB;                               // V tile
@@ -818,24 +916,21 @@ __global__ __launch_bounds__(kStreamNW * kWave) __attribute__((amdgpu_waves_per_
 #pragma unroll
     for (int k = 0; k < KD; ++k) qv[k] = ld16(qp + 32 * k + 8 * q4);
   };
-  // Wave gw takes the (task, head) pairs gw, gw + NWV, gw + 2 NWV, ...: the
-  // waves of a workgroup work on neighbouring KV heads of the same rows.
-  const int NWV = gridDim.x * kStreamNW;
-
-  // ---- load side: (task, head) lk, its descriptor LT, step lu; the next
-  // pair nk and its descriptor ND
-  int lk = gw, lh = gw % Hkv, lu = 0;
-  StreamTask LT = tasks[gw / Hkv];
+  // ---- load side: task lk, its descriptor LT, step lu; the next task nk
+  // and its descriptor ND
+  const int lh = gw % Hkv;
+  int lk = ts, lu = 0;
+  StreamTask LT = tasks[lk];
   u32x4 qn[KD];
   load_q(LT, lh, qn);
-  int nk = gw + NWV;
+  int nk = lk + 1;
   StreamTask ND = LT;
-  if (nk < nht) ND = tasks[nk / Hkv];
+  if (nk < te) ND = tasks[nk];
   bool ldone = false;
 
-  // ---- compute side: (task, head) pk of descriptor PT at step pu; the first
-  // PD-1 steps only fill the pipeline
-  int pk = 0, ph = 0, pu = -(PD - 1);
+  // ---- compute side: task pk of descriptor PT at step pu; the first PD-1
+  // steps only fill the pipeline
+  int pk = ts, pu = -(PD - 1);
   StreamTask PT = LT;
   u32x4 qop[KD];
 #pragma unroll
@@ -845,17 +940,16 @@ __global__ __launch_bounds__(kStreamNW * kWave) __attribute__((amdgpu_waves_per_
 
   auto load = [&](St& S) {
     if (lu == steps(LT) && !ldone) {  // next task (uniform)
-      if (nk < nht) {
+      if (nk < te) {
         lk = nk;
-        lh = lk % Hkv;
         LT = ND;
         lu = 0;
         load_q(LT, lh, qn);
-        nk = lk + NWV;
-        if (nk < nht) ND = tasks[nk / Hkv];
+        nk = lk + 1;
+        if (nk < te) ND = tasks[nk];
       } else {
         ldone = true;  // no more work: keep re-reading the last tile (masked)
-        lk = nht;
+        lk = te;
       }
     }
     const int su = min(lu, steps(LT) - 1);
@@ -906,14 +1000,13 @@ __global__ __launch_bounds__(kStreamNW * kWave) __attribute__((amdgpu_waves_per_
     if (pu == 0) {
       PT = LT;
       pk = lk;
-      ph = lh;
 #pragma unroll
       for (int k = 0; k < KD; ++k) qop[k] = qn[k];
     }
   };
 
   auto process = [&](St& S) {
-    const bool live = pk < nht && pu >= 0 && pu < PT.cnt;
+    const bool live = pk < te && pu >= 0 && pu < PT.cnt;
     const int u = PT.t0 + min(max(pu, 0), PT.cnt - 1);
     // K rows -> LDS as loaded, V rows -> bf16 LDS tile (a wave's LDS
     // operations run in order, so the previous tile's reads are done)
@@ -988,12 +1081,12 @@ __global__ __launch_bounds__(kStreamNW * kWave) __attribute__((amdgpu_waves_per_
     if (pu < 0) {
       ++pu;
     } else if (++pu == steps(PT)) {
-      if (pk < nht) {
+      if (pk < te) {
         float lsum = st.l;
         lsum += __shfl_xor(lsum, 16, kWave);
         lsum += __shfl_xor(lsum, 32, kWave);
         if (c16 < g) {
-          float* rec = a.part + (((size_t)PT.r * a.Hq + (size_t)ph * g + c16) * a.S + PT.s) * (D + 4);
+          float* rec = a.part + (((size_t)PT.r * a.Hq + (size_t)lh * g + c16) * a.S + PT.s) * (D + 4);
           write_record<D>(rec, st, lsum, q4, c16);
         }
       }
@@ -1018,23 +1111,21 @@ __global__ __launch_bounds__(kStreamNW * kWave) __attribute__((amdgpu_waves_per_
       load(S[(k + PD - 1) % PD]);
       process(S[k]);
     }
-  } while (pk < nht);
+  } while (pk < te);
 }
 
-// One wave per output row (agent, layer, query head): combine the agent
-// kernel's splits [0, nsp) and the shared kernel's splits [SP, SP + SG).
+// One wave per output row (agent, layer, query head): combine the stream
+// kernel's records [0, nsp) of the row (nsp = nrec[agent * L + layer]) and
+// the shared kernel's splits [SP, SP + SG).
 template <typename E, int D, int MODE>
-__global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, E* __restrict__ out) {
+__global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, const int32_t* __restrict__ nrec,
+                                                     E* __restrict__ out) {
   const int lane = threadIdx.x % kWave;
   const size_t row = (size_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (row >= (size_t)a.N * a.L * a.Hq) return;
   const int i = (int)(row / ((size_t)a.L * a.Hq));
   const int l = (int)((row / a.Hq) % a.L);
-  const int P = min(a.priv_off[i + 1] - a.priv_off[i], a.pmax);
-  const int nx = (MODE == FUSED) ? min(max(a.diff_off[i * a.L + l + 1] - a.diff_off[i * a.L + l], 0), a.T / kTile)
-                                  : a.T / kTile;
-  const int nt = (P + kTile - 1) / kTile + nx;
-  const int nsp = min((nt + kTilesPerSplit - 1) / kTilesPerSplit, a.SP);
+  const int nsp = min(nrec[i * a.L + l], a.SP);
   const size_t rec = D + 4;
   const float* pr = a.part + row * a.S * rec;
   // the row's records: its nsp agent splits, then the Master splits [SP, S)
@@ -1189,14 +1280,17 @@ __global__ __launch_bounds__(kThreads) void restore_dense_kernel(
 struct Plan {
   int SP, SG, AGS, NAG, TPG, n_sh_wg;
   long long dcap;
-  size_t part_bytes, tab_off, task_off, ctl_off, dcs_off, dinfo_off, total;
+  size_t part_bytes, tab_off, task_off, ctl_off, nrec_off, dcs_off, dinfo_off, total;
 };
 
 Plan make_plan(const Dims& d, int max_priv, bool fused) {
   Plan p{};
   const int nb = d.T / kTile;
-  p.SP = ((max_priv + kTile - 1) / kTile + nb + kTilesPerSplit - 1) / kTilesPerSplit;
-  if (p.SP < 1) p.SP = 1;
+  // stream-kernel records per row: a row of at most SP0 * kTilesPerSplit
+  // tiles, cut into pieces of at least kTilesPerSplit tiles at arbitrary
+  // offsets, has at most SP0 + 1 of them
+  const int SP0 = ((max_priv + kTile - 1) / kTile + nb + kTilesPerSplit - 1) / kTilesPerSplit;
+  p.SP = (SP0 < 1 ? 1 : SP0) + 1;
   if (fused) {
     const int g = d.Hq / d.Hkv;
     p.AGS = kRowsPerGroup / g;
@@ -1220,7 +1314,8 @@ Plan make_plan(const Dims& d, int max_priv, bool fused) {
   p.tab_off = up(p.part_bytes);
   p.task_off = p.tab_off + (fused ? up((size_t)d.N * d.B * (d.D / 2) * 8) : 0);
   p.ctl_off = p.task_off + up((size_t)d.N * d.L * p.SP * sizeof(StreamTask));
-  p.dcs_off = p.ctl_off + 256;
+  p.nrec_off = p.ctl_off + up((size_t)(kMaxSlots + 3) * 4);
+  p.dcs_off = p.nrec_off + up((size_t)d.N * d.L * 4);
   p.dinfo_off = p.dcs_off + (fused ? up((size_t)p.dcap * (d.D / 2) * 8) : 0);
   p.total = p.dinfo_off + (fused ? up((size_t)p.dcap * 8) : 0);
   return p;
@@ -1278,19 +1373,23 @@ hipError_t launch_attn_t(const Dims& d, AttnArgs a, const Plan& p, E* out, hipSt
                                                          kStreamNW * kWave, lds)) != hipSuccess)
     return e;
   if (per_cu < 1) return hipErrorInvalidConfiguration;
-  const int grid = ncu * per_cu;  // resident workgroups; each wave takes every NWV-th (task, head)
+  // resident workgroups (at least one slot: one wave per KV head); slot s
+  // is waves s * Hkv .. s * Hkv + Hkv - 1
+  const int grid = std::max(ncu * per_cu, (d.Hkv + kStreamNW - 1) / kStreamNW);
+  const int nslot = std::min(grid * kStreamNW / d.Hkv, kMaxSlots);
   StreamTask* tasks = reinterpret_cast<StreamTask*>(a.ws_base + p.task_off);
-  int32_t* ctl = reinterpret_cast<int32_t*>(a.ws_base + p.ctl_off);  // task count
+  int32_t* ctl = reinterpret_cast<int32_t*>(a.ws_base + p.ctl_off);  // task count, slots, slot starts
+  int32_t* nrec = reinterpret_cast<int32_t*>(a.ws_base + p.nrec_off);
   const float2* dcs = reinterpret_cast<const float2*>(a.ws_base + p.dcs_off);
   const int2* dinfo = reinterpret_cast<const int2*>(a.ws_base + p.dinfo_off);
-  hipLaunchKernelGGL((stream_plan_kernel<MODE>), dim3(1), dim3(kPlanThreads), 0, s, a, tasks, ctl);
+  hipLaunchKernelGGL((stream_plan_kernel<MODE>), dim3(1), dim3(kPlanThreads), 0, s, a, nslot, tasks, ctl, nrec);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kStreamNW * kWave), lds, s, a, tasks, ctl, dcs, dinfo);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t rows = (size_t)d.N * d.L * d.Hq;
   const int rpb = 256 / kWave;
   hipLaunchKernelGGL((merge_kernel<E, D, MODE>), dim3((rows + rpb - 1) / rpb), dim3(256), 0, s, a,
-                     out);
+                     static_cast<const int32_t*>(nrec), out);
   return hipGetLastError();
 }
 
