@@ -259,8 +259,12 @@ __global__ __launch_bounds__(kScanThreads) void offsets_kernel(const int32_t* __
   }
 }
 
+// The diff values are written with non-temporal stores: the restore that
+// reads them next then finds no dirty lines of them in the last-level cache
+// to write back first (with plain stores a diff record that fits in the
+// cache is left there dirty in full).
 #ifndef TDX_CP_NT_STORES
-#define TDX_CP_NT_STORES 0
+#define TDX_CP_NT_STORES 1
 #endif
 __device__ __forceinline__ void cp_store(const u32x4& v, u32x4* p) {
 #if TDX_CP_NT_STORES
