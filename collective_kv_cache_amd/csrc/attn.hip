@@ -321,9 +321,13 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // tensor's half with rows RPI*g + i, i < RPI.  There, 16-byte chunk c of row
 // RPI*g + i is at 16-byte unit
 //   K: (c / 4) * 4*RPI + i + RPI * ((c % 4) ^ g)
-//   V: (c / 2) * 2*RPI + 2*i + (c % 2)
+//   V: ((c / 2) ^ VX(g)) * 2*RPI + 2*i + (c % 2),  VX(g) = g % 2 for 128 dims, else 0
 // so the K chunk 4k + q of a row is k * KSTEP bytes past chunk q, and the V
-// chunks of 16-dim slice dt are dt * VSTEP bytes past those of slice 0.
+// chunks of 16-dim slice dt are dt * VSTEP bytes past those of slice 0 for
+// even dt, and past slice 1's minus VSTEP for odd dt.  VX staggers the
+// 128-dim slices of consecutive row groups by 128 bytes: the lanes of one
+// transposed read that address rows 4 apart then hit different banks
+// (measured: half the LDS bank-conflict cycles of the unstaggered layout).
 template <int D>
 struct ShTile {
   static constexpr int RB = D * 2;                         // bytes of one bf16 row of a head
@@ -340,8 +344,9 @@ struct ShTile {
   __device__ static constexpr int kbyte(int r, int c) {
     return ((r / RPI) * 64 + (c / 4) * 4 * RPI + r % RPI + RPI * ((c % 4) ^ (r / RPI))) * 16;
   }
+  __device__ static constexpr int vx(int g) { return D == 128 ? g % 2 : 0; }
   __device__ static constexpr int vbyte(int r, int c) {
-    return ((r / RPI) * 64 + (c / 2) * 2 * RPI + 2 * (r % RPI) + c % 2) * 16;
+    return ((r / RPI) * 64 + ((c / 2) ^ vx(r / RPI)) * 2 * RPI + 2 * (r % RPI) + c % 2) * 16;
   }
 };
 
@@ -529,9 +534,9 @@ __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(TDX_
     if (inst < Tl::IPT) {  // K: lane = (c / 4) * 4*RPI + i + RPI * ((c % 4) ^ g)
       r = g * Tl::RPI + lane % Tl::RPI;
       c = (lane / (4 * Tl::RPI)) * 4 + (((lane % (4 * Tl::RPI)) / Tl::RPI) ^ g);
-    } else {  // V: lane = (c / 2) * 2*RPI + 2*i + c % 2
+    } else {  // V: lane = ((c / 2) ^ VX(g)) * 2*RPI + 2*i + c % 2
       r = g * Tl::RPI + (lane % (2 * Tl::RPI)) / 2;
-      c = (lane / (2 * Tl::RPI)) * 2 + lane % 2;
+      c = ((lane / (2 * Tl::RPI)) ^ Tl::vx(g)) * 2 + lane % 2;
     }
     loff[p] = (uint32_t)(((size_t)r * rowHD + (size_t)c * 8) * sizeof(E));
   }
@@ -558,18 +563,24 @@ __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(TDX_
   // The lane's operand addresses within a slot: K chunk q4 of row c16 (the
   // chunk of step k is k * KSTEP further); for the PV operand, va[dt][j] =
   // V[token 4*q4 + j][dim 16*dt + c16], the lane addresses row 4*q4 + c16/4
-  // at dims 16*dt + 4*(c16%4) (slice dt is dt * VSTEP further).
+  // at dims 16*dt + 4*(c16%4): slice dt is dt * VSTEP past voff0 (even dt)
+  // or voff1 (odd dt).
+  const int vrow = 4 * q4 + (c16 >> 2), vc = (c16 & 3) >> 1;
   const uint32_t koff = Tl::kbyte(c16, q4);
-  const uint32_t voff = kTile * RB + Tl::vbyte(4 * q4 + (c16 >> 2), (c16 & 3) >> 1) + (c16 & 1) * 8;
+  const uint32_t voff0 = kTile * RB + Tl::vbyte(vrow, vc) + (c16 & 1) * 8;
+  const uint32_t voff1 = kTile * RB + Tl::vbyte(vrow, 2 + vc) - Tl::VSTEP + (c16 & 1) * 8;
   auto compute = [&](int u, int s, int t_lo, int t_hi, uint32_t fw) {
     const uint32_t slot = lds_addr(ring + s * Tl::BYTES);
-    const uint32_t ka = slot + koff, vaddr = slot + voff;
+    const uint32_t ka = slot + koff, va0 = slot + voff0, va1 = slot + voff1;
     // the K and V operands of the tile in one round trip: K first, then V,
     // whose latency the QK products cover
     u32x4 kop[KD];
     static_for<KD>([&](auto k) { kop[decltype(k)::value] = ld_b128_nowait<decltype(k)::value * Tl::KSTEP>(ka); });
     i16x4 va[DT];
-    static_for<DT>([&](auto dt) { va[decltype(dt)::value] = ld_tr16_nowait<decltype(dt)::value * Tl::VSTEP>(vaddr); });
+    static_for<DT>([&](auto dt) {
+      constexpr int j = decltype(dt)::value;
+      va[j] = ld_tr16_nowait<j * Tl::VSTEP>(j % 2 ? va1 : va0);
+    });
     lds_wait_k<DT>(kop);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
