@@ -9,8 +9,13 @@
 // Fused path = set-up kernels, two kernels writing split-K partial records,
 // then one merge:
 //
-//  rope_table_kernel   cos/sin(Delta(i,b) * theta^(-2e/D)) in double, stored
-//                      as fp32 pairs [N][B][D/2].
+//  stream_plan_kernel  one launch, two roles: workgroup 0 lays the (agent,
+//                      layer) rows' tiles end to end and cuts them into one
+//                      equal piece per stream-kernel slot (a wave per KV
+//                      head), a piece being one task per row it touches; the
+//                      other workgroups fill the table
+//                      cos/sin(Delta(i,b) * theta^(-2e/D)), computed in
+//                      double and stored as fp32 pairs [N][B][D/2].
 //  diff_tab_kernel     per diff entry: its shared block and that block's
 //                      cos/sin row (a block straddling two shared blocks is
 //                      marked, and its rows take their own rows).
@@ -24,10 +29,6 @@
 //                      (R(-Delta) q) . k, so one canonical Master tile serves
 //                      all agents.  Rows of an agent whose diff record holds
 //                      the tile are masked here.
-//  stream_plan_kernel  lays the (agent, layer) rows' tiles end to end and
-//                      cuts them into one equal piece per stream-kernel
-//                      slot (a wave per KV head); a piece is one task per
-//                      row it touches.
 //  stream_kernel       persistent waves, each running its slot's tasks: the
 //                      agent's private history followed by its own diff
 //                      blocks (K/V straight from the diff record, the keys
@@ -116,14 +117,13 @@ __device__ __forceinline__ int block_of(const int32_t* blk, int B, int t) {
 
 // ---- RoPE table: tab[(i*B + b)*HALF + e] = (cos, sin)(Delta(i,b) * theta^(-2e/D))
 
-__global__ __launch_bounds__(256) void rope_table_kernel(const int32_t* __restrict__ src_pos,
-                                                         const int32_t* __restrict__ dst_pos,
-                                                         int N, int B, int D, double theta,
-                                                         float2* __restrict__ tab) {
+// entries x0, x0 + stride, ... of the table
+__device__ void rope_table_fill(const int32_t* __restrict__ src_pos, const int32_t* __restrict__ dst_pos,
+                                int N, int B, int D, double theta, float2* __restrict__ tab, size_t x0,
+                                size_t stride) {
   const int half = D / 2;
   const size_t n = (size_t)N * B * half;
-  for (size_t x = blockIdx.x * (size_t)blockDim.x + threadIdx.x; x < n;
-       x += (size_t)gridDim.x * blockDim.x) {
+  for (size_t x = x0; x < n; x += stride) {
     const int e = (int)(x % half);
     const size_t ib = x / half;
     const int b = (int)(ib % B);
@@ -151,10 +151,13 @@ struct AttnArgs {
   const void* dv;
   const int32_t* blk_start;  // [B+1]
   const float2* tab;         // fused: [N][B][D/2] cos/sin of each shift
+  const int32_t* src_pos;    // fused: [B] and [N][B], the shifts the table is filled from
+  const int32_t* dst_pos;
+  double theta;
   const uint16_t* qplain;    // [N][L][Hq][D] bf16 queries (the input q)
   float* part;               // [N][L][Hq][S][D+4]: m, l, -, -, O[D]
   unsigned char* ws_base;    // the workspace (task list, per-diff-entry cos/sin rows)
-  int N, L, T, B, Hkv, Hq;
+  int N, L, T, B, Hkv, Hq, D;
   long long dcap;            // fused: diff entries covered by the per-entry cos/sin rows
   int SP;                    // stream-kernel record slots
   int SG;                    // shared-kernel record slots (after SP)
@@ -736,11 +739,19 @@ constexpr int kMaxSlots = 8192;
 // ceil(tiles / P) + 1 <= SP tasks (one partial record each).  Tasks are
 // stored slot by slot in row order.  Writes ctl[0] = tasks, ctl[1] = nslot,
 // ctl[2 + s] = first task of slot s (s <= nslot) and nrec[r] = tasks of row r.
+// Workgroups 1 .. gridDim.x - 1 (fused path) fill the cos/sin table instead.
 template <int MODE>
 __global__ __launch_bounds__(kPlanThreads) void stream_plan_kernel(AttnArgs a, int nslot,
                                                                    StreamTask* __restrict__ tasks,
                                                                    int32_t* __restrict__ ctl,
                                                                    int32_t* __restrict__ nrec) {
+  if (blockIdx.x > 0) {  // workgroup-uniform
+    if (MODE == FUSED)
+      rope_table_fill(a.src_pos, a.dst_pos, a.N, a.B, a.D, a.theta, const_cast<float2*>(a.tab),
+                      (size_t)(blockIdx.x - 1) * kPlanThreads + threadIdx.x,
+                      (size_t)(gridDim.x - 1) * kPlanThreads);
+    return;
+  }
   constexpr int W = kPlanThreads / kWave;
   __shared__ int wsum[2][W];
   __shared__ int red[W];
@@ -1359,20 +1370,6 @@ hipError_t launch_attn_t(const Dims& d, AttnArgs a, const Plan& p, E* out, hipSt
   a.n_sh_wg = p.n_sh_wg;
   a.dcap = p.dcap;
   hipError_t e;
-  if (MODE == FUSED) {
-    // a ring of TDX_SH_NB slots, or of 3 when blk_start and the diff flags
-    // leave too little of the 64 KB
-    const int grid = (p.n_sh_wg + 7) / 8 * 8;
-    const size_t lds = shared_lds(D, d.B, p, TDX_SH_NB);
-    if (lds <= 64 * 1024) {
-      hipLaunchKernelGGL((shared_kernel<E, D, TDX_SH_NB, PAGED>), dim3(grid), dim3(kShThreads), lds, s, a);
-    } else {
-      const size_t lds3 = shared_lds(D, d.B, p, 3);
-      if (lds3 > 64 * 1024) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((shared_kernel<E, D, 3, PAGED>), dim3(grid), dim3(kShThreads), lds3, s, a);
-    }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
   a.qplain = static_cast<const uint16_t*>(a.q);  // bf16 queries are the MFMA operand as stored
   constexpr int PD = StreamCfg<E, D>::PD;
   const size_t lds = StreamCfg<E, D>::lds(MODE == FUSED);
@@ -1393,8 +1390,35 @@ hipError_t launch_attn_t(const Dims& d, AttnArgs a, const Plan& p, E* out, hipSt
   int32_t* nrec = reinterpret_cast<int32_t*>(a.ws_base + p.nrec_off);
   const float2* dcs = reinterpret_cast<const float2*>(a.ws_base + p.dcs_off);
   const int2* dinfo = reinterpret_cast<const int2*>(a.ws_base + p.dinfo_off);
-  hipLaunchKernelGGL((stream_plan_kernel<MODE>), dim3(1), dim3(kPlanThreads), 0, s, a, nslot, tasks, ctl, nrec);
+  // set-up: the task plan (workgroup 0) and, fused, the cos/sin table (the
+  // other workgroups) in one launch
+  int pgrid = 1;
+  if (MODE == FUSED) {
+    const size_t n = (size_t)d.N * d.B * (d.D / 2);
+    pgrid += (int)std::min<size_t>((n + kPlanThreads - 1) / kPlanThreads, 64);
+  }
+  hipLaunchKernelGGL((stream_plan_kernel<MODE>), dim3(pgrid), dim3(kPlanThreads), 0, s, a, nslot, tasks, ctl, nrec);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (MODE == FUSED) {
+    // per diff entry: its shared block and that block's cos/sin row
+    hipLaunchKernelGGL(diff_tab_kernel, dim3(d.N * d.L), dim3(kDiffTabThreads), 0, s, a.diff_off, a.diff_idx,
+                       a.blk_start, a.tab, d.L, d.B, d.T / kTile, d.D / 2, (long long)p.dcap,
+                       reinterpret_cast<float2*>(a.ws_base + p.dcs_off),
+                       reinterpret_cast<int2*>(a.ws_base + p.dinfo_off));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // a ring of TDX_SH_NB slots, or of 3 when blk_start and the diff flags
+    // leave too little of the 64 KB
+    const int sgrid = (p.n_sh_wg + 7) / 8 * 8;
+    const size_t slds = shared_lds(D, d.B, p, TDX_SH_NB);
+    if (slds <= 64 * 1024) {
+      hipLaunchKernelGGL((shared_kernel<E, D, TDX_SH_NB, PAGED>), dim3(sgrid), dim3(kShThreads), slds, s, a);
+    } else {
+      const size_t lds3 = shared_lds(D, d.B, p, 3);
+      if (lds3 > 64 * 1024) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((shared_kernel<E, D, 3, PAGED>), dim3(sgrid), dim3(kShThreads), lds3, s, a);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kStreamNW * kWave), lds, s, a, tasks, ctl, dcs, dinfo);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t rows = (size_t)d.N * d.L * d.Hq;
@@ -1427,6 +1451,7 @@ AttnArgs common_args(const Dims& d, const void* q, const int32_t* priv_off, cons
   a.B = d.B;
   a.Hkv = d.Hkv;
   a.Hq = d.Hq;
+  a.D = d.D;
   a.scale_log2 = scale * kLog2e;
   // private histories are capped at max_priv: the splits are sized for it,
   // so a history past it can only lose its own tail, never the diff tiles
@@ -1465,7 +1490,7 @@ F32AttnArgs f32_args(const Dims& d, const tdx_layout* lay, const void* q, const 
 }  // namespace
 
 namespace {
-// Query side (cos/sin table, per-diff-entry rows), then the fused kernels.
+// The fused restore: set-up (task plan and cos/sin table, per-diff-entry rows), then the attention kernels.
 template <bool PAGED>
 hipError_t restore_attn_t(const Dims& d, const tdx_layout& lay, AttnArgs a, const int32_t* diff_off,
                           const int32_t* diff_idx, int max_priv, void* out, void* ws, hipStream_t s) {
@@ -1473,21 +1498,10 @@ hipError_t restore_attn_t(const Dims& d, const tdx_layout& lay, AttnArgs a, cons
   a.diff_off = diff_off;
   a.diff_idx = diff_idx;
   a.blk_start = lay.blk_start;
-  float2* tab = reinterpret_cast<float2*>(static_cast<unsigned char*>(ws) + p.tab_off);
-  a.tab = tab;
-  const size_t n = (size_t)d.N * d.B * (d.D / 2);
-  const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
-  hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(256), 0, s, lay.src_pos, lay.dst_pos,
-                     d.N, d.B, d.D, d.theta, tab);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (d.N * d.L > 0) {
-    hipLaunchKernelGGL(diff_tab_kernel, dim3(d.N * d.L), dim3(kDiffTabThreads), 0, s, diff_off, diff_idx, lay.blk_start,
-                       tab, d.L, d.B, d.T / kTile, d.D / 2, (long long)p.dcap,
-                       reinterpret_cast<float2*>(static_cast<unsigned char*>(ws) + p.dcs_off),
-                       reinterpret_cast<int2*>(static_cast<unsigned char*>(ws) + p.dinfo_off));
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
+  a.tab = reinterpret_cast<float2*>(static_cast<unsigned char*>(ws) + p.tab_off);
+  a.src_pos = lay.src_pos;
+  a.dst_pos = lay.dst_pos;
+  a.theta = d.theta;
   return dispatch_attn<FUSED, PAGED>(d, a, p, out, s);
 }
 }  // namespace
