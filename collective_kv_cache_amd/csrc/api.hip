@@ -69,6 +69,18 @@ int check_shape(const tdx_shape* s, tdx::Dims* d) {
   return TDX_OK;
 }
 
+// The restore calls count every (agent, layer) row's tiles (its history up
+// to max_priv, then the shared tokens) in 32-bit integers.
+bool restore_tiles_fit(const tdx::Dims& d, int32_t max_priv) {
+  const long long per_row = ((long long)max_priv + TDX_DIFF_BLOCK - 1) / TDX_DIFF_BLOCK + d.T / TDX_DIFF_BLOCK;
+  return max_priv >= 0 && (long long)d.N * d.L * per_row <= 0x7fffffffLL;
+}
+int check_restore_tiles(const tdx::Dims& d, int32_t max_priv) {
+  REQ(restore_tiles_fit(d, max_priv), TDX_EUNSUPPORTED,
+      "n_agents * n_layers * (max_priv + n_tokens) / 16 exceeds 2^31 - 1 tiles");
+  return TDX_OK;
+}
+
 int check_layout(const tdx_layout* lay, tdx::Dims* d, bool need_pos) {
   REQ(lay != nullptr, TDX_EINVAL, "layout is null");
   REQ(lay->n_agents >= 1, TDX_EINVAL, "n_agents %d < 1", lay->n_agents);
@@ -309,7 +321,8 @@ int tdx_diff_encode(const tdx_shape* shape, const tdx_layout* layout, const int3
 
 size_t tdx_restore_attn_workspace(const tdx_shape* shape, const tdx_layout* layout, int32_t max_priv) {
   tdx::Dims d{};
-  if (check_shape(shape, &d) != TDX_OK || check_layout(layout, &d, false) != TDX_OK || max_priv < 0) return 0;
+  if (check_shape(shape, &d) != TDX_OK || check_layout(layout, &d, false) != TDX_OK || !restore_tiles_fit(d, max_priv))
+    return 0;
   return tdx::restore_attn_ws_bytes(d, max_priv);
 }
 
@@ -328,6 +341,7 @@ int tdx_restore_attn(const tdx_shape* shape, const tdx_layout* layout, const voi
   REQ(d.T % TDX_DIFF_BLOCK == 0, TDX_EINVAL, "n_tokens %d is not a multiple of 16", d.T);
   REQ(d.Hq / d.Hkv <= 16, TDX_EUNSUPPORTED, "more than 16 query heads per KV head");
   REQ(max_priv >= 0, TDX_EINVAL, "max_priv < 0");
+  if ((rc = check_restore_tiles(d, max_priv)) != TDX_OK) return rc;
   REQ(scale > 0.0f, TDX_EINVAL, "scale must be > 0");
   REQ_PTR(q);
   REQ_PTR4(priv_off);
@@ -460,6 +474,7 @@ int tdx_restore_attn_paged(const tdx_shape* shape, const tdx_layout* layout, con
   REQ(d.T % TDX_DIFF_BLOCK == 0, TDX_EINVAL, "n_tokens %d is not a multiple of 16", d.T);
   REQ(d.Hq / d.Hkv <= 16, TDX_EUNSUPPORTED, "more than 16 query heads per KV head");
   REQ(max_priv >= 0, TDX_EINVAL, "max_priv < 0");
+  if ((rc = check_restore_tiles(d, max_priv)) != TDX_OK) return rc;
   REQ(scale > 0.0f, TDX_EINVAL, "scale must be > 0");
   REQ_PTR(q);
   REQ_PTR4(priv_off);
@@ -627,7 +642,8 @@ int tdx_restore_dense(const tdx_shape* shape, const tdx_layout* layout, const vo
 size_t tdx_decode_attn_dense_workspace(const tdx_shape* shape, const tdx_layout* layout,
                                        int32_t max_priv) {
   tdx::Dims d{};
-  if (check_shape(shape, &d) != TDX_OK || check_layout(layout, &d, false) != TDX_OK || max_priv < 0) return 0;
+  if (check_shape(shape, &d) != TDX_OK || check_layout(layout, &d, false) != TDX_OK || !restore_tiles_fit(d, max_priv))
+    return 0;
   return tdx::dense_attn_ws_bytes(d, max_priv);
 }
 
@@ -643,6 +659,7 @@ int tdx_decode_attn_dense(const tdx_shape* shape, const tdx_layout* layout, cons
   REQ(d.T % TDX_DIFF_BLOCK == 0, TDX_EINVAL, "n_tokens %d is not a multiple of 16", d.T);
   REQ(d.Hq / d.Hkv <= 16, TDX_EUNSUPPORTED, "more than 16 query heads per KV head");
   REQ(max_priv >= 0, TDX_EINVAL, "max_priv < 0");
+  if ((rc = check_restore_tiles(d, max_priv)) != TDX_OK) return rc;
   REQ(scale > 0.0f, TDX_EINVAL, "scale must be > 0");
   REQ_PTR(q);
   REQ_PTR4(priv_off);

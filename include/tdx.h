@@ -218,7 +218,11 @@ size_t tdx_diff_encode_workspace(const tdx_shape *shape, const tdx_layout *layou
  *              keeps its own cache, notes Figure 8).
  *   diff_off / diff_idx / diff_k / diff_v  as written by tdx_diff_encode
  *   scale      softmax scale (> 0), usually 1/sqrt(D)
- *   out        [N][L][Hq][D] */
+ *   out        [N][L][Hq][D]
+ * Returns TDX_EUNSUPPORTED when N * L * (ceil(max_priv / 16) + T / 16), the
+ * number of 16-token tiles the call plans, exceeds 2^31 - 1 (the same bound
+ * holds for tdx_restore_attn_paged and tdx_decode_attn_dense, whose
+ * workspace queries then return 0). */
 int tdx_restore_attn(const tdx_shape *shape, const tdx_layout *layout,
                      const void *q, const int32_t *priv_off,
                      const void *priv_k, const void *priv_v, int32_t max_priv,

@@ -135,8 +135,8 @@ def test_encode_rejects_bad_arguments():
     assert _encode(ws_bytes=0) == tdx.TDX_EWORKSPACE
 
 
-def _restore(T=64, scale=0.1, max_priv=10, ws_bytes=1 << 30, hq=28, msel=None, mstride=0):
-    s, l = _shape(n_q_heads=hq), _layout(n_tokens=T)
+def _restore(T=64, scale=0.1, max_priv=10, ws_bytes=1 << 30, hq=28, msel=None, mstride=0, L=2):
+    s, l = _shape(n_q_heads=hq, n_layers=L), _layout(n_tokens=T)
     return tdx.lib().tdx_restore_attn(ctypes.byref(s), ctypes.byref(l), FAKE, FAKE, FAKE, FAKE, max_priv,
                                       FAKE, FAKE, msel, mstride, FAKE, FAKE, FAKE, FAKE,
                                       ctypes.c_float(scale), FAKE, FAKE, ws_bytes, None)
@@ -154,6 +154,13 @@ def test_restore_rejects_bad_arguments():
     assert _restore(max_priv=-1) == tdx.TDX_EINVAL
     assert _restore(ws_bytes=0) == tdx.TDX_EWORKSPACE
     assert _restore(hq=4 * 17) == tdx.TDX_EUNSUPPORTED  # 17 query heads per KV head
+    # the tiles the call plans, N * L * (ceil(max_priv / 16) + T / 16), must fit in 31 bits
+    # (3 agents x 8 layers x 134217728 tiles here; 2 layers would still fit)
+    assert _restore(max_priv=2**31 - 1, L=8) == tdx.TDX_EUNSUPPORTED
+    assert "tiles" in tdx.lib().tdx_last_error().decode()
+    s, l = _shape(n_layers=8), _layout(n_tokens=64)
+    assert tdx.lib().tdx_restore_attn_workspace(ctypes.byref(s), ctypes.byref(l), 2**31 - 1) == 0
+    assert tdx.lib().tdx_decode_attn_dense_workspace(ctypes.byref(s), ctypes.byref(l), 2**31 - 1) == 0
     # the Master selector: aligned pointer, stride >= 0 keeping 16-byte alignment (bf16: % 8)
     assert _restore(msel=ctypes.c_void_p(0x10002)) == tdx.TDX_EINVAL
     assert _restore(msel=FAKE, mstride=-8) == tdx.TDX_EINVAL
