@@ -23,6 +23,13 @@ pytestmark = pytest.mark.gpu
     ("qwen7b_round", dict(n_layers=2, n_agents=4)),
     ("qwen14b_round", dict(n_layers=1, n_agents=3)),
     ("qwen7b_scaleout", dict(n_layers=1, n_agents=6, n_blocks=8)),
+    # agent groups of the Master-tile kernel (64 query rows) that end in a
+    # remainder: 7 query heads per KV head, 10 agents = 9 + 1 and
+    # 19 agents = 9 + 9 + 1; 64-dim bf16 heads with 14 query heads per KV
+    # head, 5 agents = 4 + 1
+    ("qwen7b_round", dict(n_layers=1, n_agents=10)),
+    ("qwen7b_scaleout", dict(n_layers=1, n_agents=19, n_blocks=8)),
+    ("tiny", dict(dtype="bf16", n_q_heads=28, n_agents=5, priv=("fixed", (37, 90, 15, 0, 5)))),
 ])
 def test_fused_and_dense_match_oracle(name, kw):
     cfg = CONFIGS[name].scaled(**kw)
