@@ -16,11 +16,11 @@
 //                      other workgroups fill the table
 //                      cos/sin(Delta(i,b) * theta^(-2e/D)), computed in
 //                      double and stored as fp32 pairs [N][B][D/2].
-//  diff_tab_kernel     per diff entry: its shared block and that block's
-//                      cos/sin row (a block straddling two shared blocks is
-//                      marked, and its rows take their own rows).
-//  shared_kernel       one workgroup per (agent group, Master split, layer,
-//                      KV head).  Each 16-token Master tile (= one diff
+//  shared_kernel       first, one wave per (agent, layer) row: per diff entry,
+//                      its shared block and that block's cos/sin row (a
+//                      block straddling two shared blocks is marked, and its
+//                      rows take their own rows); then one workgroup per
+//                      (agent group, Master split, layer, KV head).  Each 16-token Master tile (= one diff
 //                      block) arrives ONCE in an LDS ring through direct
 //                      global-to-LDS loads and serves the query rows of every
 //                      agent of the group, the agents' GQA query groups
@@ -164,6 +164,10 @@ struct AttnArgs {
   int S;                     // SP + SG
   int AGS, NAG, TPG;         // shared kernel: agents per group, groups, tiles per split
   int n_sh_wg;               // shared kernel: real workgroups (grid is padded to 8)
+  int n_dt_wg;               // fused: workgroups in front of the shared kernel's that prepare the
+                             // per-diff-entry rows (a multiple of 8)
+  float2* dcs;               // fused: [dcap][D/2] per-diff-entry cos/sin rows (written by those)
+  int2* dinfo;               // fused: [dcap] per-diff-entry (beta, shared block)
   float scale_log2;
   // paged (fused): sk/sv, dk/dv are the agents' K/V pools and pk/pv the
   // private pools; the Master's pages are row *msel of mpm, the diff entries'
@@ -416,6 +420,56 @@ struct VmWait {
 #ifndef TDX_SH_WPE
 #define TDX_SH_WPE 3
 #endif
+
+// Per diff entry e of row r = i * L + l: dinfo[e] = (beta, b) with b the
+// shared block holding the entry's first token (~b when the 16 tokens span
+// more than one block), and dcs[e][0 .. D/2) = the (cos, sin) row of
+// Delta(i, b) from the round's table.  One wave per row: lane j searches the
+// block starts for entries j, j + 64, ... of the row (all lanes at once),
+// then the wave copies the entries' rows, eight independent reads in flight
+// per lane.  Entries at or past dcap are left out.
+__device__ void diff_tab_row(const AttnArgs& a, int r, int lane) {
+  const int half = a.D / 2;
+  const int nb = a.T / kTile;
+  const int i = r / a.L;
+  const int e0 = a.diff_off[r];
+  if (e0 < 0) return;  // uniform
+  const long long n = std::min<long long>(std::min(std::max(a.diff_off[r + 1] - e0, 0), nb), a.dcap - e0);
+  for (int c = 0; c < n; c += kWave) {
+    const int m = (int)std::min<long long>(kWave, n - c);  // entries of this chunk
+    int b = 0;
+    if (lane < m) {
+      const int e = e0 + c + lane;
+      const int t0 = a.diff_idx[e] * kTile;
+      // b = the largest block with blk_start[b] <= t0 (empty blocks skipped)
+      int lo = 0, hi = a.B - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.blk_start[mid] <= t0) lo = mid; else hi = mid - 1;
+      }
+      b = lo;
+      const bool straddle = a.blk_start[b + 1] < t0 + kTile;
+      a.dinfo[e] = make_int2(t0 / kTile, straddle ? ~b : b);
+    }
+    // the m rows of half (cos, sin) pairs, element f = j * half + x
+    const int tot = m * half;
+    for (int f0 = 0; f0 < tot; f0 += 8 * kWave) {
+      float2 v[8];
+      int fj[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int f = std::min(f0 + u * kWave + lane, tot - 1);
+        const int j = f / half;
+        const int bj = __shfl(b, j, kWave);
+        v[u] = a.tab[((size_t)i * a.B + bj) * half + f % half];
+        fj[u] = f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (f0 + u * kWave + lane < tot) a.dcs[(size_t)(e0 + c) * half + fj[u]] = v[u];
+    }
+  }
+}
 template <typename E, int D, int NB, bool PAGED>
 __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(TDX_SH_WPE))) void shared_kernel(AttnArgs a) {
   using Tl = ShTile<D>;
@@ -431,11 +485,19 @@ __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(TDX_
   const int NW = (a.TPG + 31) / 32;                                      // flag words per agent
   uint32_t* dbits = reinterpret_cast<uint32_t*>(sblk + a.B + 1);         // [AGS][NW]
 
+  // The first n_dt_wg workgroups (fused) prepare the per-diff-entry rows
+  // that the stream kernel reads, one row per wave; they run before the
+  // Master-tile workgroups and touch no LDS.
+  if ((int)blockIdx.x < a.n_dt_wg) {
+    const int r = (int)blockIdx.x * kShWaves + (int)threadIdx.x / kWave;
+    if (r < a.N * a.L) diff_tab_row(a, r, (int)threadIdx.x % kWave);
+    return;
+  }
   // Hardware deals workgroups round-robin to the 8 XCDs; give each XCD a
   // contiguous run of logical ids so that the agent groups sharing a Master
   // tile run on the same XCD (one L2) at the same time.
-  const int nwg = gridDim.x;  // a multiple of 8
-  const int w = blockIdx.x;
+  const int nwg = gridDim.x - a.n_dt_wg;  // a multiple of 8, as is n_dt_wg
+  const int w = blockIdx.x - a.n_dt_wg;
   const int logical = (w % 8) * (nwg / 8) + w / 8;
   if (logical >= a.n_sh_wg) return;
   const int ag = logical % a.NAG;
@@ -674,7 +736,8 @@ __global__ __launch_bounds__(kShThreads) __attribute__((amdgpu_waves_per_eu(TDX_
 // diff block holds canonical keys: its rows are rotated to the agent's
 // offsets in registers by the shift of the shared block that holds them
 // (K' = R(Delta(i,b)) K, rounded to bf16 like a materialised cache), with the
-// block's cos/sin row prepared per diff entry by diff_tab_kernel.
+// block's cos/sin row prepared per diff entry (diff_tab_row) in the
+// Master-tile launch.
 
 template <typename E, int D, int MODE>
 struct Stage {
@@ -847,39 +910,6 @@ __global__ __launch_bounds__(kPlanThreads) void stream_plan_kernel(AttnArgs a, i
   if (tid == 0) {
     ctl[0] = carry1;
     ctl[1] = nslot;
-  }
-}
-
-// Per diff entry e of row r = i * L + l: info[e] = (beta, b) with b the shared
-// block holding the entry's first token (~b when the 16 tokens span more than
-// one block), and cs[e][0 .. D/2) = the (cos, sin) row of Delta(i, b).  One
-// workgroup per row, one wave per entry; the lanes test 64 blocks at a time.
-constexpr int kDiffTabThreads = 256;
-__global__ __launch_bounds__(kDiffTabThreads) void diff_tab_kernel(const int32_t* __restrict__ diff_off,
-                                                                   const int32_t* __restrict__ diff_idx,
-                                                                   const int32_t* __restrict__ blk_start,
-                                                                   const float2* __restrict__ tab, int L, int B,
-                                                                   int nb, int half, long long cap,
-                                                                   float2* __restrict__ cs, int2* __restrict__ info) {
-  const int r = blockIdx.x;
-  const int i = r / L;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int e0 = diff_off[r];
-  const int e1 = e0 + min(max(diff_off[r + 1] - e0, 0), nb);
-  for (int e = e0 + wave; e < e1; e += kDiffTabThreads / kWave) {
-    if (e < 0 || e >= cap) break;  // uniform
-    const int t0 = diff_idx[e] * kTile;
-    // b = the largest block with blk_start[b] <= t0 (empty blocks skipped)
-    int b = 0;
-    for (int c = 0; c < B; c += kWave) {
-      const int x = c + lane;
-      const uint64_t m = __ballot(x < B && blk_start[x] <= t0);
-      if (m != 0) b = c + 63 - __clzll(m);
-      if (m != ~0ull) break;  // the first block past t0 is in this chunk
-    }
-    const bool straddle = blk_start[b + 1] < t0 + kTile;
-    if (lane == 0) info[e] = make_int2(t0 / kTile, straddle ? ~b : b);
-    for (int x = lane; x < half; x += kWave) cs[(size_t)e * half + x] = tab[((size_t)i * B + b) * half + x];
   }
 }
 
@@ -1400,15 +1430,15 @@ hipError_t launch_attn_t(const Dims& d, AttnArgs a, const Plan& p, E* out, hipSt
   hipLaunchKernelGGL((stream_plan_kernel<MODE>), dim3(pgrid), dim3(kPlanThreads), 0, s, a, nslot, tasks, ctl, nrec);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (MODE == FUSED) {
-    // per diff entry: its shared block and that block's cos/sin row
-    hipLaunchKernelGGL(diff_tab_kernel, dim3(d.N * d.L), dim3(kDiffTabThreads), 0, s, a.diff_off, a.diff_idx,
-                       a.blk_start, a.tab, d.L, d.B, d.T / kTile, d.D / 2, (long long)p.dcap,
-                       reinterpret_cast<float2*>(a.ws_base + p.dcs_off),
-                       reinterpret_cast<int2*>(a.ws_base + p.dinfo_off));
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // in front of the Master-tile workgroups: per diff entry, its shared
+    // block and that block's cos/sin row (one (agent, layer) row per wave)
+    a.dcs = reinterpret_cast<float2*>(a.ws_base + p.dcs_off);
+    a.dinfo = reinterpret_cast<int2*>(a.ws_base + p.dinfo_off);
+    a.n_dt_wg = (d.N * d.L + kShWaves - 1) / kShWaves;
+    a.n_dt_wg = (a.n_dt_wg + 7) / 8 * 8;
     // a ring of TDX_SH_NB slots, or of 3 when blk_start and the diff flags
     // leave too little of the 64 KB
-    const int sgrid = (p.n_sh_wg + 7) / 8 * 8;
+    const int sgrid = a.n_dt_wg + (p.n_sh_wg + 7) / 8 * 8;
     const size_t slds = shared_lds(D, d.B, p, TDX_SH_NB);
     if (slds <= 64 * 1024) {
       hipLaunchKernelGGL((shared_kernel<E, D, TDX_SH_NB, PAGED>), dim3(sgrid), dim3(kShThreads), slds, s, a);

@@ -18,10 +18,13 @@
 //  offsets_kernel one workgroup: exclusive scan of the row counts -> row
 //                 offsets (clamped to the capacity, so a record whose blocks
 //                 overflow it still names only written entries) and the true
-//                 total nnz.
-//  index_kernel   one workgroup per CSR row: the ascending block indices
-//                 (and, paged, the Mirror's page) into their slots; entries at
-//                 or past the capacity are dropped.
+//                 total nnz.  Launched only for rounds of more than 4096
+//                 rows; smaller rounds have index_kernel do it per row.
+//  index_kernel   one workgroup per CSR row: the row offset (the sum of the
+//                 earlier rows' counts, on rounds of at most 4096 rows), then
+//                 the ascending block indices (and, paged, the Mirror's page)
+//                 into their slots; entries at or past the capacity are
+//                 dropped.
 //  copy_kernel    slot-major: each workgroup copies the Mirror's K/V blocks of
 //                 a few consecutive CSR entries.
 #include "common.h"
@@ -62,7 +65,7 @@ __global__ __launch_bounds__(kFlagThreads) void flag_kernel(
   const int nitems = nb * L * nslices;
   const int m = master_p[0];
   const size_t slice_flags = (size_t)N * L * nb;
-  if (m < 0 || m >= N) {  // invalid Master: no reads; offsets_kernel reports nnz = -1
+  if (m < 0 || m >= N) {  // invalid Master: no reads; nnz is reported as -1
     for (int w = blockIdx.x; w < nitems; w += G) {
       const int beta = w % nb, l = (w / nb) % L, cs = w / (nb * L);
       for (int i = tid; i < N; i += kFlagThreads) flags[cs * slice_flags + ((size_t)i * L + l) * nb + beta] = 0;
@@ -277,14 +280,46 @@ __device__ __forceinline__ void cp_store(const u32x4& v, u32x4* p) {
 // One workgroup per CSR row (agent, layer): the ascending block indices of the
 // row's flagged blocks into their slots (entries at or past the capacity are
 // dropped).  PAGED: also each entry's page, the Mirror's page pm[a][beta].
-template <bool PAGED>
+// With OWN_OFF (rounds of at most kOwnOffRows rows) the workgroup first sums
+// the earlier rows' counts itself and writes its row offset as
+// offsets_kernel would (the last row also the end offset and nnz), so no
+// separate scan launch is needed; larger rounds read the offsets that
+// offsets_kernel wrote.
+constexpr int kOwnOffRows = 4096;
+template <bool PAGED, bool OWN_OFF>
 __global__ __launch_bounds__(kThreads) void index_kernel(const uint8_t* __restrict__ flags,
                                                          const int32_t* __restrict__ rank,
-                                                         const int32_t* __restrict__ off, int nb, int64_t cap,
-                                                         int32_t* __restrict__ diff_idx, PageMap pm, int L,
-                                                         int32_t* __restrict__ diff_page) {
+                                                         const int32_t* __restrict__ count, int rows,
+                                                         int32_t* __restrict__ off, int64_t* __restrict__ nnz,
+                                                         const int32_t* __restrict__ master_p, int N, int nb,
+                                                         int64_t cap, int32_t* __restrict__ diff_idx, PageMap pm,
+                                                         int L, int32_t* __restrict__ diff_page) {
   const size_t r = blockIdx.x;
-  const int64_t row_off = off[r];
+  int64_t row_off;
+  if constexpr (OWN_OFF) {
+    constexpr int W = kThreads / kWave;
+    __shared__ long long wsum[W];
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    long long x = 0;
+    for (size_t j = tid; j < r; j += kThreads) x += count[j];
+    for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+    if (lane == 0) wsum[wave] = x;
+    __syncthreads();
+    long long pre = 0;
+    for (int w = 0; w < W; ++w) pre += wsum[w];
+    row_off = min(pre, (long long)cap);
+    if (tid == 0) {
+      off[r] = (int32_t)row_off;
+      if ((int)r == rows - 1) {
+        const long long total = pre + count[r];
+        off[rows] = (int32_t)min(total, (long long)cap);
+        const int m = master_p[0];
+        nnz[0] = (m < 0 || m >= N) ? -1 : total;
+      }
+    }
+  } else {
+    row_off = off[r];
+  }
   for (int beta = threadIdx.x; beta < nb; beta += kThreads) {
     if (!flags[r * nb + beta]) continue;
     const int64_t slot = row_off + rank[r * nb + beta];
@@ -412,12 +447,17 @@ hipError_t encode_t(const Dims& d, const int32_t* master, const void* ak, const 
                        count);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(kScanThreads), 0, s, count, rows, cap, diff_off, nnz,
-                     master, d.N);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((index_kernel<PAGED>), dim3(rows), dim3(kThreads), 0, s, flags, rank, diff_off, nb, cap,
-                     diff_idx, pm, d.L, diff_page);
+  hipError_t e;
+  if (rows <= kOwnOffRows) {
+    hipLaunchKernelGGL((index_kernel<PAGED, true>), dim3(rows), dim3(kThreads), 0, s, flags, rank, count, rows,
+                       diff_off, nnz, master, d.N, nb, cap, diff_idx, pm, d.L, diff_page);
+  } else {
+    hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(kScanThreads), 0, s, count, rows, cap, diff_off, nnz,
+                       master, d.N);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((index_kernel<PAGED, false>), dim3(rows), dim3(kThreads), 0, s, flags, rank, count, rows,
+                       diff_off, nnz, master, d.N, nb, cap, diff_idx, pm, d.L, diff_page);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (diff_k == nullptr || cap <= 0) return hipSuccess;  // a paged record without value copies
   // every written entry has a slot below cap; surplus workgroups exit at once

@@ -93,6 +93,21 @@ def test_encode_capacity_overflow_reports_true_total():
                         ak.to(DEV), av.to(DEV), cap_blocks=cap, check=True)
 
 
+@pytest.mark.parametrize("capped", [False, True])
+def test_encode_more_than_4096_rows(capped):
+    # 700 agents x 6 layers = 4200 CSR rows: past 4096 rows the row offsets
+    # come from one workgroup's scan of the row counts instead of each row's
+    # own sum of the earlier counts; both clamp the offsets to the capacity
+    cfg = CONFIGS["tiny"].scaled(n_agents=700, n_layers=6, n_blocks=3, blk_len=(16, 32), priv=("uniform", 0, 40))
+    lay = make_layout(cfg)
+    kc, vc = cached_kv(cfg, lay)
+    ak, av = agent_caches(cfg, lay, kc, vc, 5)
+    ref = O.diff_encode(to_numpy_bits(ak), to_numpy_bits(av), 5)
+    cap = int(ref[0][-1]) // 2 if capped else None
+    ds = _encode(cfg, lay, ak, av, 5, cap=cap)
+    _compare(ds, ref, 6, cap=cap)
+
+
 def test_overflowed_record_restores_as_truncated():
     # a record whose blocks overflow the capacity names only written entries
     # (offsets clamped), so the fused and dense restores and the transfer
