@@ -12,10 +12,12 @@
 //                    the per-head norm and add the heads.  The wave sums its
 //                    token over agents in index order (score) and writes
 //                    per-workgroup agent partials for the Master total.
-//  select_kernel     one 1024-thread workgroup: fixed-order agent totals and
-//                    argmin, 4-pass 8-bit radix select of the k-th largest
-//                    fp32 score bit pattern, then an ordered compaction by one
-//                    scan that takes ties in ascending token order.
+//  select_kernel     two 1024-thread workgroups side by side: one runs an 8-bit
+//                    radix select of the k-th largest fp32 score bit pattern
+//                    (at most 4 passes, fewer once the k-th key's bin is taken
+//                    whole), then an ordered compaction by one scan that takes
+//                    ties in ascending token order; the other sums the agent
+//                    totals in a fixed order and takes their argmin.
 #include "common.h"
 
 namespace tdx {
@@ -158,59 +160,45 @@ __device__ __forceinline__ void wave_excl2(uint32_t a, uint32_t b, int lane, uin
   *tb = __builtin_amdgcn_readlane(ib, kWave - 1);
 }
 
+// Workgroup 0 of select_kernel: the k largest scores (ties to the lower
+// token), written in ascending token order.
+//
 // KEYS_IN_LDS = 1: the scores fit in LDS (T <= kSelLdsKeys) and are read from
 // there; 0: from global memory.  A compile-time choice, so every key read has
 // one address space (a pointer that may be either makes each read wait for all
 // outstanding loads).
 template <int KEYS_IN_LDS>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(
-    const float* __restrict__ score, const double* __restrict__ part, int nparts, int N, int T,
-    int k, float* __restrict__ agent_dev, int32_t* __restrict__ selected,
-    int32_t* __restrict__ master) {
+__device__ __forceinline__ void topk_role(const float* __restrict__ score, int T, int k,
+                                          int32_t* __restrict__ selected, uint32_t* s_key) {
   constexpr int W = kSelThreads / kWave;
   constexpr int KPT = kSelLdsKeys / kSelThreads;  // keys per thread when the scores fit in LDS
-  constexpr int PB = 16;                          // partial sums in flight per thread
-  extern __shared__ uint32_t s_key_dyn[];  // [kSelLdsKeys] score bits, when they fit
-  __shared__ float s_adev[kMaxAgents];
   __shared__ uint32_t hist[2][256];  // radix histograms, alternating between passes
-  __shared__ uint32_t s_prefix, s_need;
+  __shared__ uint32_t s_prefix, s_need, s_done;
   __shared__ uint32_t s_wtot[2][W];
-  __shared__ double s_at[kSelThreads];  // [S][N] slice sums
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
   // the scores (>= 0, so their fp32 bit patterns order like the values)
   constexpr bool in_lds = KEYS_IN_LDS != 0;
   const uint32_t* sbits = reinterpret_cast<const uint32_t*>(score);
-  const uint32_t* key = in_lds ? s_key_dyn : sbits;
-
-  // ---- loads.  The scores go to LDS; this thread's first PB partial sums
-  // are issued right after them and stay in flight through the selection,
-  // which does not need them (the agent totals and the Master come last).
-  // Thread (slice j, agent i) sums the partials p = j, j + S, ... of agent i
-  // in that order (S = 1024 / N slices); agent i then adds its S slice sums
-  // in slice order, so the order of every addition is fixed.
-  uint32_t kreg[KPT];
-  if constexpr (in_lds) {
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) kreg[u] = sbits[min(tid + u * kSelThreads, T - 1)];
-  }
-  const int S = kSelThreads / N;  // N <= 1024
-  const int ai = tid % N, sj = tid / N;
-  double pv[PB];
-#pragma unroll
-  for (int u = 0; u < PB; ++u) pv[u] = part[(size_t)min(sj + u * S, nparts - 1) * N + ai];
+  const uint32_t* key = in_lds ? s_key : sbits;
   if constexpr (in_lds) {
     // the launch gives room for kSelLdsKeys keys: slots past T get copies of
-    // the last score and are never read (no branch around the stores, so the
-    // partial sums issued after the scores stay in flight)
+    // the last score and are never read
+    uint32_t kreg[KPT];
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) s_key_dyn[tid + u * kSelThreads] = kreg[u];
+    for (int u = 0; u < KPT; ++u) kreg[u] = sbits[min(tid + u * kSelThreads, T - 1)];
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) s_key[tid + u * kSelThreads] = kreg[u];
   }
   for (int x = tid; x < 2 * 256; x += kSelThreads) hist[x / 256][x % 256] = 0;
   __syncthreads();
 
-  // ---- radix select of the k-th largest key, 8 bits per pass from the top
+  // ---- radix select of the k-th largest key, 8 bits per pass from the top.
+  // A pass narrows the keys to those sharing the k-th largest key's leading
+  // bits (prefix under mask); `need` of them still belong to the set.  Once
+  // the k-th key's bin holds exactly `need` keys, every key of the bin
+  // belongs to the set and the remaining passes are skipped.
   uint32_t prefix = 0, mask = 0, need = (uint32_t)k;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
@@ -257,37 +245,43 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       uint32_t run = incl - own;  // lanes > lane
       // digit d crosses when run + sum_{q > d} hv[q] < need <= ... + hv[d]
       int found = -1;
-      uint32_t need_in = 0;
+      uint32_t need_in = 0, cnt = 0;
 #pragma unroll
       for (int q = 3; q >= 0; --q) {
         if (found < 0 && run < need && need <= run + hv[q]) {
           found = 4 * lane + q;
           need_in = need - run;
+          cnt = hv[q];
         }
         run += hv[q];
       }
       if (found >= 0) {  // exactly one lane
         s_prefix = prefix | ((uint32_t)found << shift);
         s_need = need_in;
+        s_done = need_in == cnt;
       }
     }
     __syncthreads();
     prefix = s_prefix;
     need = s_need;
     mask |= 255u << shift;
+    if (s_done) break;  // uniform: read after the barrier by every thread
   }
 
   // ---- ordered compaction in one scan.  Thread j owns the contiguous run of
-  // tokens [j*C, j*C + C).  Every key above the threshold is selected, and
-  // the first `need` keys equal to it in token order; so a selected token's
-  // slot is (keys above before it) + min(keys equal before it, need), and one
-  // exclusive scan of the two per-run counts places every token.
+  // tokens [j*C, j*C + C).  A key whose leading bits (under mask) exceed the
+  // prefix is selected, and the first `need` keys whose leading bits equal it
+  // in token order; so a selected token's slot is (keys above before it) +
+  // min(keys equal before it, need), and one exclusive scan of the two
+  // per-run counts places every token.  With all bits resolved these are the
+  // keys above the k-th and the lowest tokens tied with it; after an early
+  // stop every key of the k-th key's bin is selected.
   const uint32_t thr = prefix;
   const int C = (T + kSelThreads - 1) / kSelThreads;
   const int t0 = min(tid * C, T), t1 = min(t0 + C, T);
   uint32_t ngt = 0, neq = 0;
   for (int t = t0; t < t1; ++t) {
-    const uint32_t u = key[t];
+    const uint32_t u = key[t] & mask;
     ngt += u > thr;
     neq += u == thr;
   }
@@ -303,7 +297,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     eeq += s_wtot[1][w];
   }
   for (int t = t0; t < t1; ++t) {
-    const uint32_t u = key[t];
+    const uint32_t u = key[t] & mask;
     if (u > thr) {
       const uint32_t pos = egt + min(eeq, need);
       if (pos < (uint32_t)k) selected[pos] = t;
@@ -313,15 +307,29 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       ++eeq;
     }
   }
+}
 
-  // ---- agent totals (the partial sums loaded at the start, then any further
-  // batches), then the Master
+// Workgroup 1 of select_kernel: agent totals D_i = sum over the deviation
+// pass's per-workgroup partials, then the Master (argmin, ties to the lower
+// index).  Thread (slice j, agent i) sums the partials p = j, j + S, ... of
+// agent i in that order (S = 1024 / N slices); agent i's S slice sums are then
+// added by one wave (lane l takes slices l, l + 64, ... in order, then a fixed
+// butterfly) when there are 8 or more, else by one thread in slice order, so
+// the order of every addition is fixed.
+__device__ __forceinline__ void totals_role(const double* __restrict__ part, int nparts, int N,
+                                            float* __restrict__ agent_dev, int32_t* __restrict__ master) {
+  constexpr int W = kSelThreads / kWave;
+  constexpr int PB = 32;  // partial sums in flight per thread
+  __shared__ float s_adev[kMaxAgents];
+  __shared__ double s_at[kSelThreads];  // [S][N] slice sums
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  const int S = kSelThreads / N;  // N <= 1024
+  const int ai = tid % N, sj = tid / N;
   if (sj < S) {
     double acc = 0.0;
-#pragma unroll
-    for (int u = 0; u < PB; ++u)
-      if (sj + u * S < nparts) acc += pv[u];
-    for (int p0 = sj + PB * S; p0 < nparts; p0 += PB * S) {
+    for (int p0 = sj; p0 < nparts; p0 += PB * S) {
       double v[PB];
 #pragma unroll
       for (int u = 0; u < PB; ++u) v[u] = part[(size_t)min(p0 + u * S, nparts - 1) * N + ai];
@@ -332,12 +340,23 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     s_at[sj * N + ai] = acc;
   }
   __syncthreads();
-  for (int a = tid; a < N; a += kSelThreads) {
-    double tot = 0.0;
-    for (int q = 0; q < S; ++q) tot += s_at[q * N + a];
-    const float v = (float)tot;
-    agent_dev[a] = v;
-    s_adev[a] = v;
+  if (S >= 8) {
+    for (int a = wave; a < N; a += W) {
+      double v = 0.0;
+      for (int q = lane; q < S; q += kWave) v += s_at[q * N + a];
+      v = wave_sum_xor(v, kWave);
+      if (lane == 0) {
+        agent_dev[a] = (float)v;
+        s_adev[a] = (float)v;
+      }
+    }
+  } else {
+    for (int a = tid; a < N; a += kSelThreads) {
+      double tot = 0.0;
+      for (int q = 0; q < S; ++q) tot += s_at[q * N + a];
+      agent_dev[a] = (float)tot;
+      s_adev[a] = (float)tot;
+    }
   }
   __syncthreads();
 
@@ -365,6 +384,20 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     }
     if (lane == 0) master[0] = bi;
   }
+}
+
+// Two workgroups of 1024 threads that run side by side: workgroup 0 selects
+// the important set, workgroup 1 sums the agent totals and picks the Master.
+template <int KEYS_IN_LDS>
+__global__ __launch_bounds__(kSelThreads) void select_kernel(
+    const float* __restrict__ score, const double* __restrict__ part, int nparts, int N, int T,
+    int k, float* __restrict__ agent_dev, int32_t* __restrict__ selected,
+    int32_t* __restrict__ master) {
+  extern __shared__ uint32_t s_key_dyn[];  // [kSelLdsKeys] score bits, when they fit
+  if (blockIdx.x == 0)
+    topk_role<KEYS_IN_LDS>(score, T, k, selected, s_key_dyn);
+  else
+    totals_role(part, nparts, N, agent_dev, master);
 }
 
 template <typename E, int D, int KCH, bool PAGED>
@@ -464,10 +497,10 @@ hipError_t select_t(const Dims& d, int check_layer, const void* k_reuse, const P
   if (e != hipSuccess) return e;
   const size_t lds = d.T <= kSelLdsKeys ? (size_t)kSelLdsKeys * sizeof(uint32_t) : 0;
   if (d.T <= kSelLdsKeys)
-    hipLaunchKernelGGL(select_kernel<1>, dim3(1), dim3(kSelThreads), lds, s, score, part, nparts, d.N,
+    hipLaunchKernelGGL(select_kernel<1>, dim3(2), dim3(kSelThreads), lds, s, score, part, nparts, d.N,
                        d.T, k, agent_dev, selected, master);
   else
-    hipLaunchKernelGGL(select_kernel<0>, dim3(1), dim3(kSelThreads), lds, s, score, part, nparts, d.N,
+    hipLaunchKernelGGL(select_kernel<0>, dim3(2), dim3(kSelThreads), lds, s, score, part, nparts, d.N,
                        d.T, k, agent_dev, selected, master);
   return hipGetLastError();
 }
