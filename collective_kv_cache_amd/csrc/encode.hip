@@ -329,6 +329,76 @@ __global__ __launch_bounds__(kThreads) void index_kernel(const uint8_t* __restri
   }
 }
 
+// index_kernel without the rows_kernel launch in front of it, for rounds
+// whose flags have one chunk slice and whose flag array is small
+// (rows * nb <= kRowsInIndexFlags): workgroup r sums the flags of the rows
+// before it itself (the flags are 0/1 bytes, so a popcount of each 16-byte
+// chunk counts them), writes its row offset (the last row also the end
+// offset and nnz) and then ranks its own row's flags in ascending block order
+// while it writes their indices.  Same outputs as rows_kernel + index_kernel.
+constexpr long long kRowsInIndexFlags = 256 * 1024;
+template <bool PAGED>
+__global__ __launch_bounds__(kThreads) void index_rows_kernel(const uint8_t* __restrict__ flags, int rows,
+                                                              int32_t* __restrict__ off, int64_t* __restrict__ nnz,
+                                                              const int32_t* __restrict__ master_p, int N, int nb,
+                                                              int64_t cap, int32_t* __restrict__ diff_idx,
+                                                              PageMap pm, int L, int32_t* __restrict__ diff_page) {
+  constexpr int W = kThreads / kWave;
+  __shared__ int wsum[W];
+  __shared__ int wcnt[W];
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  // flagged blocks of rows [0, r): bytes [0, r * nb) of the flag array
+  const long long nbytes = (long long)r * nb;
+  const long long n16 = nbytes / 16;
+  const u32x4* f4 = reinterpret_cast<const u32x4*>(flags);
+  int x = 0;
+  for (long long j = tid; j < n16; j += kThreads) {
+    const u32x4 v = f4[j];
+    x += __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
+  }
+  if (n16 * 16 + tid < nbytes) x += flags[n16 * 16 + tid] != 0;  // < 16 tail bytes
+  for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+  if (lane == 0) wsum[wave] = x;
+  __syncthreads();
+  long long pre = 0;
+  for (int w = 0; w < W; ++w) pre += wsum[w];
+  const int64_t row_off = min(pre, (long long)cap);
+  // own row: in-row exclusive ranks by ballots, indices into their slots
+  const uint8_t* fr = flags + nbytes;
+  int carry = 0;
+  for (int base = 0; base < nb; base += kThreads) {
+    const int beta = base + tid;
+    const bool f = beta < nb && fr[beta] != 0;
+    const uint64_t m = __ballot(f);
+    if (lane == 0) wcnt[wave] = __popcll(m);
+    __syncthreads();
+    int rk = carry, all = carry;
+    for (int w = 0; w < W; ++w) {
+      if (w < wave) rk += wcnt[w];
+      all += wcnt[w];
+    }
+    if (f) {
+      const int64_t slot = row_off + rk + lanemask_count(m, lane);
+      if (slot < cap) {
+        diff_idx[slot] = beta;
+        if constexpr (PAGED) diff_page[slot] = (int32_t)page_at(pm, (long long)(r / L), beta);
+      }
+    }
+    carry = all;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    off[r] = (int32_t)row_off;
+    if (r == rows - 1) {
+      const long long total = pre + carry;
+      off[rows] = (int32_t)min(total, (long long)cap);
+      const int m = master_p[0];
+      nnz[0] = (m < 0 || m >= N) ? -1 : total;
+    }
+  }
+}
+
 // Slot-major value copy: workgroup w copies CSR entries [w*S, w*S + S), then
 // the groups of S a grid further on (of the min(nnz, cap) written entries),
 // from the Mirrors' caches, kCopyUnroll chunks of K and of V per thread in
@@ -443,12 +513,19 @@ hipError_t encode_t(const Dims& d, const int32_t* master, const void* ak, const 
     };
     e = flag_kc(d) == 1 ? launch_flag(flag_kernel<1, 8, PAGED>) : launch_flag(flag_kernel<2, 4, PAGED>);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(rows_kernel, dim3(rows), dim3(kThreads), 0, s, flags, nb, ns, (size_t)rows * nb, rank,
-                       count);
+    if (ns == 1 && (long long)rows * nb <= kRowsInIndexFlags) {
+      hipLaunchKernelGGL((index_rows_kernel<PAGED>), dim3(rows), dim3(kThreads), 0, s, flags, rows, diff_off, nnz,
+                         master, d.N, nb, cap, diff_idx, pm, d.L, diff_page);
+    } else {
+      hipLaunchKernelGGL(rows_kernel, dim3(rows), dim3(kThreads), 0, s, flags, nb, ns, (size_t)rows * nb, rank,
+                         count);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipError_t e;
-  if (rows <= kOwnOffRows) {
+  if (flag_slices(d) == 1 && (long long)rows * nb <= kRowsInIndexFlags) {
+    // index_rows_kernel has written the offsets, nnz and indices
+  } else if (rows <= kOwnOffRows) {
     hipLaunchKernelGGL((index_kernel<PAGED, true>), dim3(rows), dim3(kThreads), 0, s, flags, rank, count, rows,
                        diff_off, nnz, master, d.N, nb, cap, diff_idx, pm, d.L, diff_page);
   } else {
