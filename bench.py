@@ -66,6 +66,57 @@ def parse():
 
 
 CSRC = os.path.join(ROOT, "collective_kv_cache_amd", "csrc")
+
+
+# hipEventDisableSystemFence: the event skips the system-scope fence (an L2
+# writeback and invalidate) when it is recorded.  The HIP runtime documents
+# the flag for events used only for timing; with default events each
+# stage boundary also pays for that fence (~1.5-2.5 us per stage here).
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+class HipEvent:
+    """A timing event on the HIP runtime that torch loaded, created with
+    hipEventDisableSystemFence, recorded on torch's current stream (the stream
+    the library's kernels are launched on).  Same use as torch.cuda.Event:
+    record(), then elapsed_time(later_event) in ms after a synchronize."""
+    _lib = None
+
+    def __init__(self):
+        import ctypes
+        import torch
+
+        if HipEvent._lib is None:
+            # the runtime torch already loaded (dlopen of the same path returns it)
+            lib = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            HipEvent._lib = lib
+        self._ct = ctypes
+        self._h = ctypes.c_void_p()
+        rc = HipEvent._lib.hipEventCreateWithFlags(ctypes.byref(self._h), HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self):
+        import torch
+
+        rc = HipEvent._lib.hipEventRecord(self._h, self._ct.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end: "HipEvent") -> float:
+        ms = self._ct.c_float()
+        rc = HipEvent._lib.hipEventElapsedTime(self._ct.byref(ms), self._h, end._h)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if HipEvent._lib is not None and self._h:
+            HipEvent._lib.hipEventDestroy(self._h)
 # C-ABI entry point of each stage (one call per step; its kernels run back to back)
 ENTRY = {"rerotate": "tdx_rerotate", "select": "tdx_select_important", "encode": "tdx_diff_encode",
          "restore_attn": "tdx_restore_attn"}
@@ -447,7 +498,7 @@ def time_calls(fn, steps, warmup, flush):
     for _ in range(warmup):
         flush()
         fn()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    evs = [(HipEvent(), HipEvent()) for _ in range(steps)]
     torch.cuda.synchronize()
     for e0, e1 in evs:
         flush()
@@ -481,7 +532,7 @@ def transfer_path(cfg, lay, shape, dl, ds, nnz, master_k, master_v, q, pk, pv, r
     off_h, idx_h = ds.off.cpu().pin_memory(), ds.idx[:max(nnz, 1)].cpu().pin_memory()
     dk_h, dv_h = ds.k[:max(nnz, 1)].cpu().pin_memory(), ds.v[:max(nnz, 1)].cpu().pin_memory()
     counts = np.diff(off_h.numpy().astype(np.int64)).reshape(N, L)
-    ev = lambda: torch.cuda.Event(enable_timing=True)
+    ev = lambda: HipEvent()
 
     def timed(fn, n=reps):
         fn()
@@ -745,7 +796,7 @@ def measure(name, args, legs: bool, flush):
 
     def timed_steps(fn, steps, nev):
         """fn(events) per step; a flush before each step, outside its events."""
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
+        evs = [[HipEvent() for _ in range(nev)] for _ in range(steps)]
         torch.cuda.synchronize()
         for s_ in range(steps):
             flush()
@@ -784,7 +835,7 @@ def measure(name, args, legs: bool, flush):
 
         for _ in range(max(1, args.warmup)):
             flush()
-            dense_step([torch.cuda.Event(enable_timing=True) for _ in range(3)])
+            dense_step([HipEvent() for _ in range(3)])
         devs = timed_steps(dense_step, args.steps, 3)
         dense_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in devs]))
         restore_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in devs]))
@@ -926,7 +977,8 @@ def main():
                    "n_q_heads": Hq, "head_dim": D, "shared_tokens": T,
                    "private_tokens_total": int(lay.priv_len.sum()), "select_k": main_r["k"],
                    "diff_blocks": main_r["nnz"], "master": main_r["master"], "parallelism": "single GPU"},
-        "timing": (f"each step timed by its own HIP events on the launch stream; a {FLUSH_BYTES >> 30} GiB "
+        "timing": (f"each step timed by its own HIP events on the launch stream (created with "
+                   f"hipEventDisableSystemFence, so no event adds a cache writeback); a {FLUSH_BYTES >> 30} GiB "
                    f"scratch read before every step (outside its events) flushes the caches and leaves them clean"
                    if not args.no_flush else "steps timed by HIP events, no cache flush"),
         "roofline": {"bound": "hbm", "kernel": ENTRY[dom], "stage": dom,
