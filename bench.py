@@ -155,7 +155,8 @@ def recorded_traffic(entry: str, workload: str):
 ENTRY_KERNELS = {
     "tdx_rerotate": ("rerotate_kernel",),
     "tdx_select_important": ("deviation_kernel", "select_kernel"),
-    "tdx_diff_encode": ("flag_kernel", "rows_kernel", "offsets_kernel", "index_kernel", "copy_kernel"),
+    "tdx_diff_encode": ("flag_kernel", "rows_kernel", "offsets_kernel", "index_kernel", "index_rows_kernel",
+                        "copy_kernel"),
     "tdx_restore_attn": ("shared_kernel",
                          "stream_plan_kernel<0>", "stream_kernel<unsigned short, 128, 0",
                          "stream_kernel<unsigned short, 64, 0", "merge_kernel<unsigned short, 128, 0>",
