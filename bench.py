@@ -115,7 +115,9 @@ class HipEvent:
         return ms.value
 
     def __del__(self):
-        if HipEvent._lib is not None and self._h:
+        # at interpreter exit the runtime may already be torn down: leave the
+        # event to the process's end then
+        if HipEvent._lib is not None and self._h and not sys.is_finalizing():
             HipEvent._lib.hipEventDestroy(self._h)
 # C-ABI entry point of each stage (one call per step; its kernels run back to back)
 ENTRY = {"rerotate": "tdx_rerotate", "select": "tdx_select_important", "encode": "tdx_diff_encode",
