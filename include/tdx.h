@@ -153,7 +153,7 @@ size_t tdx_select_workspace(const tdx_shape *shape, const tdx_layout *layout);
  *    one GPU (two streams, two threads) race and must be serialised by the
  *    caller.  Nothing in the array needs to start at zero; each call
  *    overwrites what it reads. */
-#define TDX_SELECT_SCRATCH_BYTES (4u << 20) /* 4 MiB: N * ceil(T / 8) * 8 bytes */
+#define TDX_SELECT_SCRATCH_BYTES (4u << 20) /* 4 MiB: N * ceil(T / 4) * 8 bytes */
 int tdx_select_important_noalloc(const tdx_shape *shape, const tdx_layout *layout,
                                  int32_t check_layer, const void *k_reuse,
                                  const void *k_recomp, int32_t k, float *dev,
