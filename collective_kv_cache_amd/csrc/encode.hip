@@ -12,6 +12,12 @@
 //                 block is streamed once through a register pipeline that
 //                 runs on across items, and compared bit for bit.  Optionally
 //                 writes the dense Master copy from the same registers.
+//  index_rows_kernel  rounds with one chunk slice and at most 256K row-blocks:
+//                 one workgroup per CSR row (agent, layer) counts the flagged
+//                 blocks of the earlier rows itself (popcount of the flag
+//                 bytes), writes its row offset (and, last row, the end offset
+//                 and nnz) and ranks its own row while writing its indices;
+//                 it replaces the three kernels below.
 //  rows_kernel    one workgroup per CSR row (agent, layer): OR of the slices'
 //                 flags, count of flagged blocks and each block's rank inside
 //                 its row.
