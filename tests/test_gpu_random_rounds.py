@@ -1,6 +1,7 @@
 """Seeded random round shapes through every stage, against the oracle (GPU).
 
-The named workloads fix one shape each.  Here each seed draws a small round:
+The named workloads fix one shape each.  Here each seed draws a small round
+(and, from seed 18 on, also the number of positions to select):
 1-12 agents (40-80 in three forced seeds), 1-8 KV heads, GQA groups of 1-8 query heads, 64- or 128-dim
 heads, fp32 or bf16, 1-3 layers, 1-6 shared blocks of 16-192 tokens,
 private histories of 0-300 tokens, RoPE base 1e4 or 1e6, and a random
@@ -35,7 +36,10 @@ FORCED = {12: dict(n_agents=1), 13: dict(priv=("uniform", 0, 0)),
           16: dict(n_agents=64, n_layers=1, n_kv_heads=4, n_q_heads=20, n_blocks=10, blk_len=(32, 192)),
           17: dict(n_agents=80, n_layers=2, n_kv_heads=1, n_q_heads=1, head_dim=64, n_blocks=4,
                    blk_len=(128, 320))}
-SEEDS = list(range(12)) + sorted(FORCED)
+# seeds from 18 on also draw the selection's k uniformly from [1, T], so the
+# radix select stops at every pass (or runs all four) across the shapes
+K_DRAWN_FROM = 18
+SEEDS = list(range(12)) + sorted(FORCED) + list(range(K_DRAWN_FROM, K_DRAWN_FROM + 24))
 
 
 def draw(seed):
@@ -73,6 +77,9 @@ def test_random_round(seed):
     kin = reuse_stand_in(cfg, lay)
     kx = recomputed_k(cfg, lay, kin)
     k = O.topk_count(cfg.pct, lay.n_tokens)
+    if seed >= K_DRAWN_FROM:
+        k = int(np.random.default_rng([77, seed]).integers(1, lay.n_tokens + 1))
+        what += f" k={k}"
     out = tdx.select_important(shape_of(cfg, 1), dlayout(lay), kin.unsqueeze(1).contiguous().to(DEV),
                                kx.to(DEV), k)
     torch.cuda.synchronize()
