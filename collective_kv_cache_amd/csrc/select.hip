@@ -14,10 +14,12 @@
 //                    per-workgroup agent partials for the Master total.
 //  select_kernel     two 1024-thread workgroups side by side: one runs an 8-bit
 //                    radix select of the k-th largest fp32 score bit pattern
-//                    (at most 4 passes, fewer once the k-th key's bin is taken
-//                    whole), then an ordered compaction by one scan that takes
-//                    ties in ascending token order; the other sums the agent
-//                    totals in a fixed order and takes their argmin.
+//                    from the highest bit in which the non-zero scores differ
+//                    (no pass when the set takes every non-zero score, fewer
+//                    once the k-th key's bin is taken whole), then an ordered
+//                    compaction by one scan that takes ties in ascending token
+//                    order; the other sums the agent totals in a fixed order
+//                    and takes their argmin.
 #include "common.h"
 
 namespace tdx {
@@ -140,24 +142,52 @@ __global__ __launch_bounds__(kDevMaxThreads) void deviation_kernel(
   }
 }
 
+// DPP moves of a 32-bit value within rows of 16 lanes; lanes whose source
+// lies outside the row, or outside row_mask's rows, read 0.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Inclusive prefix sum over the wave's 64 lanes: a Hillis-Steele scan inside
+// each row of 16 (row_shr 1, 2, 4, 8), then row 1 and 3 add the last lane of
+// the row before (row_bcast:15) and rows 2 and 3 add lane 31 (row_bcast:31).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += dpp_u<0x111>(x);
+  x += dpp_u<0x112>(x);
+  x += dpp_u<0x114>(x);
+  x += dpp_u<0x118>(x);
+  x += dpp_u<0x142, 0xA>(x);
+  x += dpp_u<0x143, 0xC>(x);
+  return x;
+}
+
+// Wave-wide max, min or sum of a 32-bit value, the same in every lane: a DPP
+// butterfly inside each row of 16 (quad_perm [1,0,3,2], [2,3,0,1],
+// row_half_mirror, row_mirror), then the four rows' results by readlane.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, Op op) {
+  v = op(v, dpp_u<0xB1>(v));
+  v = op(v, dpp_u<0x4E>(v));
+  v = op(v, dpp_u<0x141>(v));
+  v = op(v, dpp_u<0x140>(v));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return op(op(r0, r1), op(r2, r3));
+}
+
 // Exclusive prefix over the wave of two counters at once (the lanes below this
 // one) and the two wave totals.
-__device__ __forceinline__ void wave_excl2(uint32_t a, uint32_t b, int lane, uint32_t* ea, uint32_t* eb,
-                                           uint32_t* ta, uint32_t* tb) {
-  uint32_t ia = a, ib = b;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t va = __shfl_up(ia, o, kWave);
-    const uint32_t vb = __shfl_up(ib, o, kWave);
-    if (lane >= o) {
-      ia += va;
-      ib += vb;
-    }
-  }
+__device__ __forceinline__ void wave_excl2(uint32_t a, uint32_t b, uint32_t* ea, uint32_t* eb, uint32_t* ta,
+                                           uint32_t* tb) {
+  const uint32_t ia = wave_incl_scan(a);
+  const uint32_t ib = wave_incl_scan(b);
   *ea = ia - a;
   *eb = ib - b;
-  *ta = __builtin_amdgcn_readlane(ia, kWave - 1);
-  *tb = __builtin_amdgcn_readlane(ib, kWave - 1);
+  *ta = (uint32_t)__builtin_amdgcn_readlane((int)ia, kWave - 1);
+  *tb = (uint32_t)__builtin_amdgcn_readlane((int)ib, kWave - 1);
 }
 
 // Workgroup 0 of select_kernel: the k largest scores (ties to the lower
@@ -175,6 +205,7 @@ __device__ __forceinline__ void topk_role(const float* __restrict__ score, int T
   __shared__ uint32_t hist[2][256];  // radix histograms, alternating between passes
   __shared__ uint32_t s_prefix, s_need, s_done;
   __shared__ uint32_t s_wtot[2][W];
+  __shared__ uint32_t s_wmax[W], s_wmin[W], s_wnz[W];
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
@@ -182,6 +213,17 @@ __device__ __forceinline__ void topk_role(const float* __restrict__ score, int T
   constexpr bool in_lds = KEYS_IN_LDS != 0;
   const uint32_t* sbits = reinterpret_cast<const uint32_t*>(score);
   const uint32_t* key = in_lds ? s_key : sbits;
+  // the largest key, the smallest non-zero key and the count of non-zero keys
+  uint32_t kmax = 0, kmin = 0xffffffffu, nz = 0;
+  auto take = [&](int t, uint32_t u) {
+    if (t < T) {
+      kmax = max(kmax, u);
+      if (u != 0) {
+        kmin = min(kmin, u);
+        ++nz;
+      }
+    }
+  };
   if constexpr (in_lds) {
     // the launch gives room for kSelLdsKeys keys: slots past T get copies of
     // the last score and are never read
@@ -189,46 +231,82 @@ __device__ __forceinline__ void topk_role(const float* __restrict__ score, int T
 #pragma unroll
     for (int u = 0; u < KPT; ++u) kreg[u] = sbits[min(tid + u * kSelThreads, T - 1)];
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) s_key[tid + u * kSelThreads] = kreg[u];
+    for (int u = 0; u < KPT; ++u) {
+      s_key[tid + u * kSelThreads] = kreg[u];
+      take(tid + u * kSelThreads, kreg[u]);
+    }
+  } else {
+    for (int t = tid; t < T; t += kSelThreads) take(t, sbits[t]);
+  }
+  kmax = wave_reduce(kmax, [](uint32_t x, uint32_t y) { return max(x, y); });
+  kmin = wave_reduce(kmin, [](uint32_t x, uint32_t y) { return min(x, y); });
+  nz = wave_reduce(nz, [](uint32_t x, uint32_t y) { return x + y; });
+  if (lane == 0) {
+    s_wmax[wave] = kmax;
+    s_wmin[wave] = kmin;
+    s_wnz[wave] = nz;
   }
   for (int x = tid; x < 2 * 256; x += kSelThreads) hist[x / 256][x % 256] = 0;
   __syncthreads();
+  kmax = 0;
+  kmin = 0xffffffffu;
+  nz = 0;
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    kmax = max(kmax, s_wmax[w]);
+    kmin = min(kmin, s_wmin[w]);
+    nz += s_wnz[w];
+  }
 
-  // ---- radix select of the k-th largest key, 8 bits per pass from the top.
-  // A pass narrows the keys to those sharing the k-th largest key's leading
-  // bits (prefix under mask); `need` of them still belong to the set.  Once
-  // the k-th key's bin holds exactly `need` keys, every key of the bin
-  // belongs to the set and the remaining passes are skipped.
-  uint32_t prefix = 0, mask = 0, need = (uint32_t)k;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
+  // ---- the k-th largest key by radix select, 8 bits per pass from the
+  // highest bit in which the non-zero keys differ (the bits above it are the
+  // same in all of them, and the zero keys rank below them).  A pass narrows
+  // the keys to those sharing the k-th largest key's leading bits (prefix
+  // under mask); `need` of them still belong to the set.  Once the k-th
+  // key's bin holds exactly `need` keys, every key of the bin belongs to the
+  // set and the remaining passes are skipped.  With k above the count of
+  // non-zero keys the threshold is 0: every non-zero key and the lowest
+  // k - nz zero keys; with all non-zero keys equal it is their value.
+  uint32_t prefix, mask = 0xffffffffu, need;
+  int hb = -1;  // highest differing bit of the non-zero keys, -1: no passes
+  if ((uint32_t)k > nz) {
+    prefix = 0;
+    need = (uint32_t)k - nz;
+  } else if (kmin == kmax) {
+    prefix = kmax;
+    need = (uint32_t)k;
+  } else {
+    hb = 31 - __builtin_clz(kmin ^ kmax);  // <= 30: the keys' sign bits are 0
+    mask = ~((2u << hb) - 1u);
+    prefix = kmax & mask;
+    need = (uint32_t)k;
+  }
+  // a pass's digit is bits [sh, sh + 8) with sh = max(hb - 7 - 8 pass, 0);
+  // when sh is clamped to 0 the digit also holds bits already resolved,
+  // which the keys still in play share, so it ranks them the same way
+  for (int pass = 0, sh = hb - 7; hb >= 0; ++pass, sh -= 8) {
+    const int s0 = max(sh, 0);
     uint32_t* h = hist[pass & 1];
     for (int base = 0; base < T; base += kSelThreads) {
       const int t = base + tid;
       const uint32_t u = key[min(t, T - 1)];
       bool pend = t < T && (u & mask) == prefix;
-      const uint32_t dg = (u >> shift) & 255u;
-      if (pass == 0) {
-        // most scores share one of a few top bytes: one atomic per distinct
-        // digit of the wave instead of one per lane on the same bin
-        uint64_t act = __ballot(pend);
-        while (act) {
-          const int ld = __builtin_ctzll(act);
-          const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)dg, ld);
-          const uint64_t m = __ballot(pend && dg == d0);
-          if (lane == ld) atomicAdd(&h[d0], (uint32_t)__popcll(m));
-          pend = pend && dg != d0;
-          act &= ~m;
-        }
-      } else if (pend) {
-        atomicAdd(&h[dg], 1u);
+      const uint32_t dg = (u >> s0) & 255u;
+      // the wave's first pending digit with one atomic for all its lanes
+      // (the common case of many equal digits), the others one per lane
+      const uint64_t act = __ballot(pend);
+      if (act) {
+        const int ld = __builtin_ctzll(act);
+        const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)dg, ld);
+        const uint64_t m = __ballot(pend && dg == d0);
+        if (lane == ld) atomicAdd(&h[d0], (uint32_t)__popcll(m));
+        if (pend && dg != d0) atomicAdd(&h[dg], 1u);
       }
     }
     __syncthreads();
     if (wave == 0) {
       // lane owns digits 4*lane .. 4*lane+3 (read, then cleared for the pass
-      // after next); keys above this lane's digits = exclusive suffix sum over
-      // the higher lanes (shuffle scan, 6 steps)
+      // after next)
       uint32_t hv[4], own = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -236,13 +314,10 @@ __device__ __forceinline__ void topk_role(const float* __restrict__ score, int T
         h[4 * lane + q] = 0;
         own += hv[q];
       }
-      uint32_t incl = own;  // inclusive suffix sum: lanes >= lane
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t v = __shfl_down(incl, o, kWave);
-        if (lane + o < kWave) incl += v;
-      }
-      uint32_t run = incl - own;  // lanes > lane
+      // keys in the digits of the lanes above this one: the wave total less
+      // the inclusive prefix sum up to this lane
+      const uint32_t pre = wave_incl_scan(own);
+      uint32_t run = (uint32_t)__builtin_amdgcn_readlane((int)pre, kWave - 1) - pre;  // lanes > lane
       // digit d crosses when run + sum_{q > d} hv[q] < need <= ... + hv[d]
       int found = -1;
       uint32_t need_in = 0, cnt = 0;
@@ -256,7 +331,7 @@ __device__ __forceinline__ void topk_role(const float* __restrict__ score, int T
         run += hv[q];
       }
       if (found >= 0) {  // exactly one lane
-        s_prefix = prefix | ((uint32_t)found << shift);
+        s_prefix = prefix | ((uint32_t)found << s0);
         s_need = need_in;
         s_done = need_in == cnt;
       }
@@ -264,8 +339,8 @@ __device__ __forceinline__ void topk_role(const float* __restrict__ score, int T
     __syncthreads();
     prefix = s_prefix;
     need = s_need;
-    mask |= 255u << shift;
-    if (s_done) break;  // uniform: read after the barrier by every thread
+    mask |= 255u << s0;
+    if (s_done || s0 == 0) break;  // uniform: read after the barrier by every thread
   }
 
   // ---- ordered compaction in one scan.  Thread j owns the contiguous run of
@@ -286,7 +361,7 @@ __device__ __forceinline__ void topk_role(const float* __restrict__ score, int T
     neq += u == thr;
   }
   uint32_t egt, eeq, wgt, weq;
-  wave_excl2(ngt, neq, lane, &egt, &eeq, &wgt, &weq);
+  wave_excl2(ngt, neq, &egt, &eeq, &wgt, &weq);
   if (lane == 0) {
     s_wtot[0][wave] = wgt;
     s_wtot[1][wave] = weq;
@@ -312,14 +387,15 @@ __device__ __forceinline__ void topk_role(const float* __restrict__ score, int T
 // Workgroup 1 of select_kernel: agent totals D_i = sum over the deviation
 // pass's per-workgroup partials, then the Master (argmin, ties to the lower
 // index).  Thread (slice j, agent i) sums the partials p = j, j + S, ... of
-// agent i in that order (S = 1024 / N slices); agent i's S slice sums are then
-// added by one wave (lane l takes slices l, l + 64, ... in order, then a fixed
-// butterfly) when there are 8 or more, else by one thread in slice order, so
-// the order of every addition is fixed.
+// agent i in that order (S = 1024 / N slices), PB loads in flight (PB at
+// least the thread's count where that fits, so one round trip serves it);
+// agent i's S slice sums are then added by one wave (lane l takes slices l,
+// l + 64, ... in order, then a fixed butterfly) when there are 8 or more,
+// else by one thread in slice order, so the order of every addition is fixed.
+template <int PB>
 __device__ __forceinline__ void totals_role(const double* __restrict__ part, int nparts, int N,
                                             float* __restrict__ agent_dev, int32_t* __restrict__ master) {
   constexpr int W = kSelThreads / kWave;
-  constexpr int PB = 32;  // partial sums in flight per thread
   __shared__ float s_adev[kMaxAgents];
   __shared__ double s_at[kSelThreads];  // [S][N] slice sums
   const int tid = threadIdx.x;
@@ -388,7 +464,7 @@ __device__ __forceinline__ void totals_role(const double* __restrict__ part, int
 
 // Two workgroups of 1024 threads that run side by side: workgroup 0 selects
 // the important set, workgroup 1 sums the agent totals and picks the Master.
-template <int KEYS_IN_LDS>
+template <int KEYS_IN_LDS, int PB>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ score, const double* __restrict__ part, int nparts, int N, int T,
     int k, float* __restrict__ agent_dev, int32_t* __restrict__ selected,
@@ -397,7 +473,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   if (blockIdx.x == 0)
     topk_role<KEYS_IN_LDS>(score, T, k, selected, s_key_dyn);
   else
-    totals_role(part, nparts, N, agent_dev, master);
+    totals_role<PB>(part, nparts, N, agent_dev, master);
 }
 
 template <typename E, int D, int KCH, bool PAGED>
@@ -496,12 +572,22 @@ hipError_t select_t(const Dims& d, int check_layer, const void* k_reuse, const P
             : launch_dev_d<float, 64, PAGED>(d, check_layer, k_reuse, pm, k_recomp, dev, score, part, &nparts, s);
   if (e != hipSuccess) return e;
   const size_t lds = d.T <= kSelLdsKeys ? (size_t)kSelLdsKeys * sizeof(uint32_t) : 0;
-  if (d.T <= kSelLdsKeys)
-    hipLaunchKernelGGL(select_kernel<1>, dim3(2), dim3(kSelThreads), lds, s, score, part, nparts, d.N,
-                       d.T, k, agent_dev, selected, master);
-  else
-    hipLaunchKernelGGL(select_kernel<0>, dim3(2), dim3(kSelThreads), lds, s, score, part, nparts, d.N,
-                       d.T, k, agent_dev, selected, master);
+  // partials per thread of the totals workgroup: the smallest batch of 8, 16
+  // or 32 loads that holds them, else batches of 32
+  const int per = (nparts + kSelThreads / d.N - 1) / (kSelThreads / d.N);
+  auto launch = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(2), dim3(kSelThreads), lds, s, score, part, nparts, d.N, d.T, k, agent_dev,
+                       selected, master);
+  };
+  if (d.T <= kSelLdsKeys) {
+    if (per <= 8) launch(select_kernel<1, 8>);
+    else if (per <= 16) launch(select_kernel<1, 16>);
+    else launch(select_kernel<1, 32>);
+  } else {
+    if (per <= 8) launch(select_kernel<0, 8>);
+    else if (per <= 16) launch(select_kernel<0, 16>);
+    else launch(select_kernel<0, 32>);
+  }
   return hipGetLastError();
 }
 }  // namespace
