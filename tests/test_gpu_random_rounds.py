@@ -35,7 +35,14 @@ FORCED = {12: dict(n_agents=1), 13: dict(priv=("uniform", 0, 0)),
           15: dict(n_agents=40, n_layers=2, n_kv_heads=2, n_q_heads=14, n_blocks=8, blk_len=(64, 256)),
           16: dict(n_agents=64, n_layers=1, n_kv_heads=4, n_q_heads=20, n_blocks=10, blk_len=(32, 192)),
           17: dict(n_agents=80, n_layers=2, n_kv_heads=1, n_q_heads=1, head_dim=64, n_blocks=4,
-                   blk_len=(128, 320))}
+                   blk_len=(128, 320)),
+          # a shared region of ~20K tokens (longer than the selection's LDS
+          # buffer, ~1280 tiles per Master split plan) and private histories of
+          # 8K-12K tokens (long stream-kernel rows)
+          90: dict(n_agents=4, n_layers=1, n_kv_heads=2, n_q_heads=6, head_dim=64, dtype="bf16",
+                   n_blocks=40, blk_len=(480, 512)),
+          91: dict(n_agents=3, n_layers=2, n_kv_heads=2, n_q_heads=4, head_dim=128, dtype="bf16",
+                   n_blocks=3, blk_len=(64, 256), priv=("uniform", 8000, 12000))}
 # seeds from 18 on also draw the selection's k uniformly from [1, T], so the
 # radix select stops at every pass (or runs all four) across the shapes
 K_DRAWN_FROM = 18
