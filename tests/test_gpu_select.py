@@ -177,3 +177,62 @@ def test_select_full_size_last_layer_of_the_rerotated_round(name):
     assert_master(int(host(out["master"])[0]), a32)
     del kr, kx, kc, out
     torch.cuda.empty_cache()
+
+
+def _planted(cfg, lay, vals):
+    """Reused K all zero; recomputed K = vals[t] in every element of token t
+    (all agents and heads), so token t's score is N * Hkv * |vals[t]| * sqrt(D)
+    and the scores' order is the order of |vals|."""
+    N, T = cfg.n_agents, lay.n_tokens
+    kr = torch.zeros((N, T, cfg.n_kv_heads, cfg.head_dim), dtype=cfg.torch_dtype)
+    kx = torch.as_tensor(np.asarray(vals, dtype=np.float32)).to(cfg.torch_dtype).view(1, T, 1, 1)
+    return kr, kx.expand(N, T, cfg.n_kv_heads, cfg.head_dim).contiguous()
+
+
+def test_select_k_above_the_nonzero_scores_takes_them_all_and_the_lowest_zero_tokens():
+    # a third of the tokens score > 0; k exceeds their count, so the set is
+    # every scored token plus the lowest-index tokens of score 0
+    cfg = CONFIGS["tiny"]
+    lay = make_layout(cfg)
+    T = lay.n_tokens
+    z = np.arange(T) % 3 == 1
+    vals = np.where(z, 1.0 + np.arange(T) / T, 0.0)
+    kr, kx = _planted(cfg, lay, vals)
+    k = int(z.sum()) + 5
+    sel, _, sel_ref, _ = _check(cfg, lay, kr, kx, k)
+    want = np.sort(np.concatenate([np.flatnonzero(z), np.flatnonzero(~z)[:5]]))
+    assert sel_ref.tolist() == want.tolist()
+    assert sel.tolist() == want.tolist()
+
+
+def test_select_equal_nonzero_scores_take_the_lowest_tokens():
+    # every scored token has the same score (and the rest score 0): the set
+    # is the lowest-index scored tokens
+    cfg = CONFIGS["tiny"]
+    lay = make_layout(cfg)
+    T = lay.n_tokens
+    z = np.arange(T) % 4 != 0
+    kr, kx = _planted(cfg, lay, np.where(z, 0.75, 0.0))
+    k = int(z.sum()) // 2
+    sel, _, sel_ref, _ = _check(cfg, lay, kr, kx, k)
+    want = np.flatnonzero(z)[:k]
+    assert sel_ref.tolist() == want.tolist()
+    assert sel.tolist() == want.tolist()
+
+
+@pytest.mark.parametrize("k_frac", [0.05, 0.5, 0.95])
+def test_select_scores_over_many_binades(k_frac):
+    # scores from ~1e-14 to ~1e10 (every exponent byte differs) in a shuffled
+    # order: the set is the tokens of the k largest planted values
+    cfg = CONFIGS["tiny"]
+    lay = make_layout(cfg)
+    T = lay.n_tokens
+    rng = np.random.default_rng(7)
+    mags = np.logspace(-15, 8, T)
+    vals = rng.permutation(mags)
+    kr, kx = _planted(cfg, lay, vals)
+    k = max(1, int(k_frac * T))
+    sel, _, sel_ref, _ = _check(cfg, lay, kr, kx, k)
+    want = np.sort(np.argsort(-vals, kind="stable")[:k])
+    assert sel_ref.tolist() == want.tolist()
+    assert sel.tolist() == want.tolist()
