@@ -12,6 +12,8 @@ rule for the selected set and the Master, and the stated tolerances for
 floating-point outputs.
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -47,6 +49,10 @@ FORCED = {12: dict(n_agents=1), 13: dict(priv=("uniform", 0, 0)),
 # radix select stops at every pass (or runs all four) across the shapes
 K_DRAWN_FROM = 18
 SEEDS = list(range(12)) + sorted(FORCED) + list(range(K_DRAWN_FROM, K_DRAWN_FROM + 24))
+# a wider sweep on request: TDX_RANDOM_SEEDS=LO:HI adds the plain seeds [LO, HI)
+if os.environ.get("TDX_RANDOM_SEEDS"):
+    _lo, _hi = (int(x) for x in os.environ["TDX_RANDOM_SEEDS"].split(":"))
+    SEEDS += [x for x in range(_lo, _hi) if x not in SEEDS]
 
 
 def draw(seed):
