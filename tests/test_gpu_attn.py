@@ -94,16 +94,19 @@ def test_zero_and_all_diff_blocks(which):
     assert_close(fused, o_fused, f"fused {which}")
 
 
-@pytest.mark.parametrize("name", ["qwen7b_round", "qwen14b_round", "qwen7b_scaleout"])
-def test_full_size_sampled(name):
+@pytest.mark.parametrize("name,seed,master", [("qwen7b_round", None, 2), ("qwen14b_round", None, 2),
+                                               ("qwen7b_scaleout", None, 2), ("qwen14b_round", 1, 7),
+                                               ("qwen7b_scaleout", 2, 40)])
+def test_full_size_sampled(name, seed, master):
     # full-size rounds in the benchmark's launch configuration (no Master
     # copy: the restore reads the Master in place through the device-side
     # selector; the 64-agent round's caches pass 2^32 elements); sampled
     # (agent, layer) outputs are computed one by one by the oracle from host
-    # copies of the generated inputs and the oracle's own diff rows.
-    cfg = CONFIGS[name]
+    # copies of the generated inputs and the oracle's own diff rows.  Two
+    # cases redraw the round (layout, data, diff blocks) from another seed
+    # with another Master.
+    cfg = CONFIGS[name] if seed is None else CONFIGS[name].scaled(seed=CONFIGS[name].seed + 100 * seed)
     lay = make_layout(cfg)
-    master = 2
     r = Round(cfg, lay, master=master, device_gen=DEV)
     d = r.dev
     m = torch.tensor([master], dtype=torch.int32, device=DEV)
