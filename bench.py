@@ -90,8 +90,18 @@ class HipEvent:
         import torch
 
         if HipEvent._lib is None:
-            # the runtime torch already loaded (dlopen of the same path returns it)
-            lib = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+            # the HIP runtime this process has loaded (torch's, which the
+            # library's kernels also run on); dlopen of its path returns it
+            path = None
+            try:
+                with open("/proc/self/maps") as f:
+                    for ln in f:
+                        if "libamdhip64.so" in ln:
+                            path = ln.split()[-1]
+                            break
+            except OSError:
+                pass
+            lib = ctypes.CDLL(path or os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
             lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
             lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
             lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
